@@ -1,0 +1,126 @@
+"""Physical forward models used by the oracle's own pins.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+``first_order_G`` writes the weak-object data model directly from the probe
+amplitude A(k) = a(k) exp(-i chi(k)); ``wave_optics_G`` is a brute-force
+simulation (shifted probe times object, far-field intensity, Fourier transform
+over probe positions) that pins the first-order model, and with it the sign,
+lobe, alias and tilt conventions of the transfer.
+
+Derivation of the first-order model (numpy's exp(-2 pi i) forward
+convention).  With object transmission 1 + c(r), c = A_l + i phi,
+c(r) = sum_K c^(K) exp(2 pi i K.r), the far field of the probe at r_p is
+Psi(k) = A(k) e^{-2 pi i k.r_p} + sum_K c^(K) A(k - K) e^{-2 pi i (k-K).r_p}.
+To first order in c, |Psi|^2 = a(k)^2 + sum_K c^(K) conj A(k) A(k-K)
+e^{2 pi i K.r_p} + c.c., and summing over the N x N probe positions with
+exp(-2 pi i q.r_p) keeps the fine frequencies K = q (mod N dq):
+    G(q, k) = N^2 a(k)^2 [q = 0]
+            + N^2 sum_{K = q} [ c^(K) conj A(k) A(k - K)
+                               + conj(c^(-K)) A(k) conj A(k + K) ].
+With c sampled on the u N fine grid, N^2 c^(K) = fft2(c)[K] / u^2.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .dsp_oracle import aperture, chi, scan_frequency_step, signed_index
+
+
+def probe_amplitude(ky, kx, optics):
+    """A(k) = a(k) exp(-i chi(k))."""
+    return aperture(np.hypot(ky, kx), optics) * np.exp(-1j * chi(ky, kx, optics))
+
+
+def fine_spectrum(field: np.ndarray, upsampling: int) -> np.ndarray:
+    """fft2(field) / u^2 of a (uN, uN) fine-grid field: the object-spectrum
+    value the data model multiplies at each fine frequency."""
+    return np.fft.fft2(field) / float(upsampling * upsampling)
+
+
+def first_order_G(k: np.ndarray, c_fine: np.ndarray, n_scan: int, step: float, upsampling: int,
+                  optics, include_dc: bool = True) -> np.ndarray:
+    """Noise-free first-order data (n_bf, N, N/2+1) complex128 for the complex
+    fine-grid object c = A_l + i phi (module docstring).  Every fine alias of
+    every stored frequency is summed (no alias rule applied)."""
+    n = n_scan
+    nf = upsampling * n
+    dq = scan_frequency_step(n, step)
+    F = np.fft.fft2(c_fine) / float(upsampling * upsampling)
+    ky, kx = k[:, 0], k[:, 1]
+    A0 = probe_amplitude(ky, kx, optics)
+    G = np.zeros((k.shape[0], n, n // 2 + 1), dtype=np.complex128)
+    half = nf // 2
+    for iy in range(n):
+        yh = int(signed_index(iy, n))
+        for ix in range(n // 2 + 1):
+            acc = np.zeros(k.shape[0], dtype=np.complex128)
+            for jy in range(-upsampling, upsampling + 1):
+                Ky = yh + jy * n
+                if Ky < -half or Ky >= half:
+                    continue
+                for jx in range(-upsampling, upsampling + 1):
+                    Kx = ix + jx * n
+                    if Kx < -half or Kx >= half:
+                        continue
+                    cK = F[Ky % nf, Kx % nf]
+                    cmK = F[(-Ky) % nf, (-Kx) % nf]
+                    Qy, Qx = Ky * dq, Kx * dq
+                    Am = probe_amplitude(ky - Qy, kx - Qx, optics)
+                    Ap = probe_amplitude(ky + Qy, kx + Qx, optics)
+                    acc += cK * np.conj(A0) * Am + np.conj(cmK) * A0 * np.conj(Ap)
+            G[:, iy, ix] = acc          # F already holds N^2 c^(K) = fft2(c)[K] / u^2
+            if include_dc and iy == 0 and ix == 0:
+                G[:, iy, ix] += n * n * np.abs(A0) ** 2
+    return G
+
+
+def band_limited_field(nf: int, rng: np.random.Generator, std: float = 1.0, cutoff: float = 1.0) -> np.ndarray:
+    """Real seeded field on an nf x nf grid whose spectrum is zero on the
+    Nyquist lines and beyond ``cutoff`` x Nyquist (so Fourier interpolation to
+    a finer grid is exact)."""
+    f = rng.standard_normal((nf, nf))
+    F = np.fft.fft2(f)
+    fy = np.fft.fftfreq(nf)[:, None] * nf
+    fx = np.fft.fftfreq(nf)[None, :] * nf
+    keep = (np.abs(fy) < nf // 2) & (np.abs(fx) < nf // 2) & (np.hypot(fy, fx) <= cutoff * nf / 2)
+    keep[0, 0] = False
+    f = np.real(np.fft.ifft2(F * keep))
+    return f * (std / f.std())
+
+
+def wave_optics_G(n_scan: int, step: float, m_sim: int, optics, c_fine: np.ndarray, upsampling: int):
+    """Brute-force data for object transmission exp(c), c = A_l + i phi.
+
+    The simulation grid spans the scan's field of view L = N s with m_sim
+    pixels per axis (pitch L / m_sim); its far-field pixels are the scan
+    frequencies themselves (spacing dq = 1/L), which serve as the detector.
+    The probe is ifft2(A(k)), shifted by whole simulation pixels to each of
+    the N x N scan positions; the object is the fine-grid field Fourier
+    interpolated onto the simulation grid.  Returns (k (m^2, 2) detector
+    vectors (1/A), G (m^2, N, N/2+1) complex128).
+    """
+    n = n_scan
+    m = m_sim
+    nf = upsampling * n
+    assert m % n == 0 and m >= 2 * nf
+    shift = m // n
+    L = n * step
+    f = np.fft.fftfreq(m, d=L / m)
+    KY, KX = np.meshgrid(f, f, indexing="ij")
+    psi = np.fft.ifft2(probe_amplitude(KY, KX, optics))
+    F = np.fft.fft2(c_fine)
+    Fs = np.zeros((m, m), dtype=np.complex128)
+    idx = signed_index(np.arange(nf), nf)
+    Fs[np.ix_(idx % m, idx % m)] = F
+    c_sim = np.fft.ifft2(Fs) * (m / nf) ** 2
+    obj = np.exp(c_sim)
+    I = np.empty((n, n, m, m))
+    for py in range(n):
+        for px in range(n):
+            ps = np.roll(psi, (py * shift, px * shift), axis=(0, 1))
+            I[py, px] = np.abs(np.fft.fft2(ps * obj)) ** 2
+    G = np.fft.rfft2(I, axes=(0, 1))                    # (n, n/2+1, m, m)
+    G = np.transpose(G, (2, 3, 0, 1)).reshape(m * m, n, n // 2 + 1)
+    k = np.stack([KY.ravel(), KX.ravel()], axis=1)
+    return k, G

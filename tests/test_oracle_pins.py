@@ -1,0 +1,545 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: numbers the
+pages print (tests/golden), textbook closed forms, a brute-force wave-optics
+simulation, explicit loops on tiny inputs, and algebraic identities.  Several
+tests plant a mistake in the oracle (monkeypatched, CPU only) to show that the
+pin would catch it.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import dsp_oracle as O
+from oracle import simulate as S
+from synthetic import LAMBDA_300KV, Optics, bf_pixels, workload
+
+LAM = LAMBDA_300KV
+ALPHA = 0.030
+
+
+def tiny_optics(det_step, soft=True):
+    return Optics(LAM, ALPHA, det_step, soft=soft, tilt=(2e-3, -1e-3),
+                  aberrations=[(1, 0, -50.0, 0.0), (1, 2, 20.0, math.radians(30)),
+                               (2, 1, 300.0, 0.4), (3, 0, 1e4, 0.0)])
+
+
+# ----------------------------------------------------------------------------
+# frequency set and aliases
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n", [4, 8, 32, 128, 512])
+def test_unique_set_covers_plane_once(n):
+    """U, its conjugates -U and the self-conjugate classes (DC and the Nyquist
+    lines) tile the full N x N frequency grid exactly once."""
+    U = O.unique_frequencies(n)
+    assert len(U) == n * (n - 2) // 2
+    cover = np.zeros((n, n), dtype=int)
+    for iy, ix in U:
+        cover[iy, ix] += 1
+        cover[(-iy) % n, (-ix) % n] += 1
+    # never solved: DC, the Nyquist row and the Nyquist column
+    cover[0, 0] += 1
+    cover[n // 2, :] += 1
+    cover[:, n // 2] += 1
+    cover[n // 2, n // 2] -= 1
+    assert np.all(cover == 1)
+
+
+def test_frequency_count_and_alias_histogram_match_pages(golden):
+    g = golden("frequency_counts_512.txt")
+    w = workload("c4")
+    q, counts, _ = O.alias_table(w.n_scan, w.step, w.upsampling, w.optics)
+    assert len(q) == int(g["n_frequencies"][0][0])
+    hist = O.alias_histogram(counts)
+    want = {int(a): int(b) for a, b in g["alias_count"]}
+    assert hist == want
+    chunks = sum(math.ceil(v / 128) for v in hist.values())
+    assert chunks == int(g["chunks_of_128"][0][0])
+
+
+def test_alias_histogram_rejects_rival_readings(golden):
+    """Plausible mistakes in the alias rule change the printed histogram."""
+    g = golden("frequency_counts_512.txt")
+    want = {int(a): int(b) for a, b in g["alias_count"]}
+    w = workload("c4")
+    # hard-aperture radius (no detector-step margin)
+    hard = w.optics.replace(soft=False)
+    _, c_hard, _ = O.alias_table(w.n_scan, w.step, w.upsampling, hard)
+    assert O.alias_histogram(c_hard) != want
+    # the rival frequency set "columns 1..N/2-1 and all rows" has the same
+    # size but a different histogram
+    n = w.n_scan
+    dq = O.scan_frequency_step(n, w.step)
+    R = O.alias_radius(w.optics)
+    rival = [len(O.aliases_of(iy, ix, n, 3, dq, R)) for iy in range(n) for ix in range(1, n // 2)]
+    assert len(rival) == 130560
+    assert O.alias_histogram(np.asarray(rival)) != want
+
+
+@pytest.mark.parametrize("u", [1, 2, 3])
+def test_alias_rule_bruteforce_tiny(u):
+    """Every fine frequency inside the overlap radius is reached exactly once:
+    as an alias of a solved frequency or as the conjugate of one (indices
+    modulo the fine grid, whose Nyquist lines are their own conjugates);
+    fine frequencies of the never-solved classes (DC, coarse Nyquist lines)
+    are never reached."""
+    n, step = 8, 0.5
+    opt = tiny_optics(0.125)
+    dq = O.scan_frequency_step(n, step)
+    R = O.alias_radius(opt)
+    q, counts, Ks = O.alias_table(n, step, u, opt)
+    nf = u * n
+    seen = {}
+    for (iy, ix), K in zip(q, Ks):
+        for ky, kx in K:
+            assert ((ky - O.signed_index(iy, n)) % n, (kx - ix) % n) == (0, 0)
+            assert (ky * ky + kx * kx) * dq * dq < R * R
+            for key in {(ky % nf, kx % nf), ((-ky) % nf, (-kx) % nf)}:
+                seen[key] = seen.get(key, 0) + 1
+    n_inside = 0
+    for ky in range(-nf // 2, nf // 2):
+        for kx in range(-nf // 2, nf // 2):
+            inside = (ky * ky + kx * kx) * dq * dq < R * R
+            cy, cx = ky % n, kx % n
+            never = (cy == 0 and cx == 0) or cy == n // 2 or cx == n // 2
+            hits = seen.get((ky % nf, kx % nf), 0)
+            if never:
+                assert hits == 0
+            elif inside:
+                assert hits == 1, (ky, kx)
+                n_inside += 1
+    assert n_inside > 0
+
+
+def test_band_count_matches_pages(golden):
+    g = golden("band_count_512.txt")
+    w = workload("c5")
+    m = O.band_mask(w.n_scan, w.step, (float(g["band_lo_invA"][0][0]), float(g["band_hi_invA"][0][0])))
+    assert int(m.sum()) == int(g["band_frequencies"][0][0])
+    nbf = int(g["bf_pixels"][0][0])
+    assert abs(m.sum() * nbf * 8 / 1e9 - float(g["g_band_read_GB"][0][0])) < 0.05
+    assert abs(w.n_scan * (w.n_scan // 2 + 1) * nbf * 8 / 1e9 - float(g["g_half_plane_GB"][0][0])) < 0.05
+
+
+def test_work_counts_match_pages(golden):
+    g = golden("magnitudes.txt")
+    w = workload("c4")
+    _, counts, _ = O.alias_table(w.n_scan, w.step, w.upsampling, w.optics)
+    pix, k = bf_pixels(w)
+    act = O.active_pixels(k, w.optics)
+    assert len(act) == 9298
+    pairs = len(act) * int(counts.sum())
+    assert abs(pairs / float(g["pixel_alias_pairs"][0][0]) - 1.0) < 0.05
+    assert abs(1.0 / w.optics.det_step / float(g["inverse_det_step_A"][0][0]) - 1.0) < 0.05
+    assert abs(len(act) * 512 * 257 * 8 / 1e9 - float(g["g_full_frame_GB"][0][0])) < 0.05
+
+
+# ----------------------------------------------------------------------------
+# optics closed forms
+# ----------------------------------------------------------------------------
+
+
+def test_chi_textbook_terms(golden):
+    """Defocus, astigmatism, coma and spherical aberration against their
+    textbook Cartesian forms; theta = lambda k + tau."""
+    rng = np.random.default_rng(3)
+    ky, kx = rng.uniform(-1.5, 1.5, size=(2, 50))
+    tau = (1.5e-3, -2.5e-3)
+    ty, tx = LAM * ky + tau[0], LAM * kx + tau[1]
+    t2 = tx * tx + ty * ty
+    base = Optics(LAM, ALPHA, 0.03, tilt=tau)
+    # defocus C10: pi C10 theta^2 / lambda
+    o = base.replace(aberrations=[(1, 0, 120.0, 0.0)])
+    assert np.allclose(O.chi(ky, kx, o), math.pi * 120.0 * t2 / LAM, rtol=1e-12, atol=1e-12)
+    # two-fold astigmatism C12 at angle p: (pi C12 / lambda)((tx^2 - ty^2) cos 2p + 2 tx ty sin 2p)
+    p = 0.7
+    o = base.replace(aberrations=[(1, 2, 40.0, p)])
+    want = math.pi * 40.0 / LAM * ((tx * tx - ty * ty) * math.cos(2 * p) + 2 * tx * ty * math.sin(2 * p))
+    assert np.allclose(O.chi(ky, kx, o), want, rtol=1e-10, atol=1e-12)
+    # coma C21 at angle p: (2 pi / 3 lambda) C21 t^2 (tx cos p + ty sin p)
+    o = base.replace(aberrations=[(2, 1, 500.0, p)])
+    want = 2 * math.pi / (3 * LAM) * 500.0 * t2 * (tx * math.cos(p) + ty * math.sin(p))
+    assert np.allclose(O.chi(ky, kx, o), want, rtol=1e-10, atol=1e-12)
+    # spherical C30: pi C30 theta^4 / (2 lambda)
+    o = base.replace(aberrations=[(3, 0, 1e4, 0.0)])
+    assert np.allclose(O.chi(ky, kx, o), math.pi * 1e4 * t2 * t2 / (2 * LAM), rtol=1e-12, atol=1e-12)
+    # scale: defocus of 100 A reaches ~14 rad at the 30 mrad edge ("about 13 rad")
+    o = Optics(LAM, ALPHA, 0.03, aberrations=[(1, 0, 100.0, 0.0)])
+    edge = float(O.chi(ALPHA / LAM, 0.0, o))
+    g = golden("magnitudes.txt")
+    assert 0.5 < edge / float(g["chi_edge_rad"][0][0]) < 2.0
+
+
+def test_chi_all_terms_rotate_with_their_angle():
+    """chi of term (n, m) at angle phi equals the m-fold rotation of the
+    same term at angle 0 (pins the cos(m (p - phi)) angle convention)."""
+    rng = np.random.default_rng(4)
+    ky, kx = rng.uniform(-1.2, 1.2, size=(2, 20))
+    for n, m in [(1, 2), (2, 1), (2, 3), (3, 2), (3, 4), (4, 1), (4, 3), (4, 5), (5, 2), (5, 4), (5, 6)]:
+        phi = 0.3
+        o1 = Optics(LAM, ALPHA, 0.03, aberrations=[(n, m, 1000.0, phi)])
+        o0 = Optics(LAM, ALPHA, 0.03, aberrations=[(n, m, 1000.0, 0.0)])
+        c, s = math.cos(-phi), math.sin(-phi)
+        # rotate k by -phi: term at angle phi equals term at 0 evaluated there
+        kyr, kxr = s * kx + c * ky, c * kx - s * ky
+        assert np.allclose(O.chi(ky, kx, o1), O.chi(kyr, kxr, o0), rtol=1e-9, atol=1e-9)
+
+
+def test_soft_aperture_edge():
+    o = Optics(LAM, ALPHA, 0.05, soft=True)
+    kc = ALPHA / LAM
+    assert O.aperture(kc, o) == pytest.approx(0.5)
+    assert O.aperture(kc - 0.025, o) == pytest.approx(1.0)
+    assert O.aperture(kc + 0.025, o) == pytest.approx(0.0, abs=1e-12)
+    assert O.aperture(kc + 0.0125, o) == pytest.approx(0.25)
+    # overlap radius = sum of the two support radii
+    assert O.alias_radius(o) == pytest.approx(2 * (kc + 0.025))
+
+
+# ----------------------------------------------------------------------------
+# physics of the transfer: brute-force wave optics
+# ----------------------------------------------------------------------------
+
+
+def _wave_optics_residual(sigma, opt, n=16, step=0.5, u=3, m=96, seed=5):
+    rng = np.random.default_rng(seed)
+    nf = u * n
+    fA = S.band_limited_field(nf, rng)
+    fP = S.band_limited_field(nf, rng)
+    c = sigma * (fA + 1j * fP)
+    k, G = S.wave_optics_G(n, step, m, opt, c, u)
+    act = O.active_pixels(k, opt)
+    dq = O.scan_frequency_step(n, step)
+    q, counts, Ks = O.alias_table(n, step, u, opt)
+    FA = S.fine_spectrum(c.real, u)
+    FP = S.fine_spectrum(c.imag, u)
+    num = den = 0.0
+    for (iy, ix), K in zip(q, Ks):
+        T = O.transfer(k[act], K * dq, opt, "complex")
+        x = np.concatenate([FA[K[:, 0] % nf, K[:, 1] % nf], FP[K[:, 0] % nf, K[:, 1] % nf]])
+        model = T @ x
+        num += np.sum(np.abs(G[act, iy, ix] - model) ** 2)
+        den += np.sum(np.abs(model) ** 2)
+    return math.sqrt(num / den), counts
+
+
+def test_transfer_matches_wave_optics():
+    """The first-order transfer (all alias, lobe, sign and tilt conventions)
+    reproduces a brute-force wave-optics simulation to O(sigma)."""
+    n, step = 16, 0.5
+    opt = tiny_optics(O.scan_frequency_step(n, step))
+    r1, counts = _wave_optics_residual(1e-3, opt)
+    r2, _ = _wave_optics_residual(5e-4, opt)
+    assert r1 < 1e-2
+    assert 0.4 < r2 / r1 < 0.6           # second-order remainder halves with sigma
+    assert len(set(counts.tolist())) > 1  # the tiny case exercises several alias counts
+
+
+def test_wave_optics_pin_catches_planted_mistakes(monkeypatch):
+    """A plausible convention error in the oracle makes the wave-optics pin
+    fail (planted on the CPU only)."""
+    n, step = 16, 0.5
+    opt = tiny_optics(O.scan_frequency_step(n, step))
+    true_lobes = O.lobes
+
+    def swapped(ky, kx, Qy, Qx, optics):
+        L, R = true_lobes(ky, kx, Qy, Qx, optics)
+        return R, L
+
+    monkeypatch.setattr(O, "lobes", swapped)
+    r_bad, _ = _wave_optics_residual(1e-3, opt)
+    monkeypatch.setattr(O, "lobes", true_lobes)
+    assert r_bad > 0.3
+
+    def no_tilt_shift(ky, kx, Qy, Qx, optics):
+        return true_lobes(ky, kx, Qy, Qx, optics.replace(tilt=(0.0, 0.0)))
+
+    monkeypatch.setattr(O, "lobes", no_tilt_shift)
+    r_bad, _ = _wave_optics_residual(1e-3, opt)
+    assert r_bad > 0.05
+
+
+def test_first_order_model_equals_transfer_sum():
+    """The physics-form first-order data (written from A(k)) equals
+    sum_Q T x over the oracle's aliases."""
+    n, step, u = 8, 0.5, 3
+    opt = tiny_optics(0.1)
+    rng = np.random.default_rng(9)
+    nf = u * n
+    c = 0.01 * (S.band_limited_field(nf, rng) + 1j * S.band_limited_field(nf, rng))
+    w = workload("c1")
+    _, k = bf_pixels(w)
+    k = k * 0.1 / w.optics.det_step  # spread over the aperture at this dk
+    act = O.active_pixels(k, opt)
+    G = S.first_order_G(k[act], c, n, step, u, opt, include_dc=False)
+    dq = O.scan_frequency_step(n, step)
+    q, _, Ks = O.alias_table(n, step, u, opt)
+    FA, FP = S.fine_spectrum(c.real, u), S.fine_spectrum(c.imag, u)
+    for (iy, ix), K in zip(q, Ks):
+        T = O.transfer(k[act], K * dq, opt, "complex")
+        x = np.concatenate([FA[K[:, 0] % nf, K[:, 1] % nf], FP[K[:, 0] % nf, K[:, 1] % nf]])
+        assert np.allclose(G[:, iy, ix], T @ x, rtol=1e-12, atol=1e-12 * np.abs(G).max())
+
+
+# ----------------------------------------------------------------------------
+# normal equations and solves
+# ----------------------------------------------------------------------------
+
+
+def _small_problem(method, u=2, n=8, seed=0, weights=True):
+    step = 0.5
+    opt = tiny_optics(0.12)
+    rng = np.random.default_rng(seed)
+    ang = rng.uniform(0, 2 * np.pi, 60)
+    rad = np.sqrt(rng.uniform(0, 1, 60)) * (ALPHA / LAM + 0.05)
+    k = np.stack([rad * np.sin(ang), rad * np.cos(ang)], axis=1)
+    act = O.active_pixels(k, opt)
+    k = k[act]
+    w = rng.uniform(0.5, 1.5, len(k)) if weights else np.ones(len(k))
+    q = O.unique_frequencies(n)
+    cols = [rng.standard_normal(len(k)) + 1j * rng.standard_normal(len(k)) for _ in q]
+    prep = O.prepare(q, cols, k, w, n, step, u, opt, method, smoothness=ALPHA / LAM)
+    return prep, k, w, cols, opt, n, step, u
+
+
+def test_gram_bruteforce_loops():
+    """Gram, right side and power by explicit Python loops over pixels and
+    unknowns, transfer entries from the lobe definitions one pixel at a time."""
+    prep, k, w, cols, opt, n, step, u = _small_problem("complex")
+    dq = O.scan_frequency_step(n, step)
+    kc = ALPHA / LAM
+
+    def amp(y, x):
+        return min(1.0, max(0.0, 0.5 + (kc - math.hypot(y, x)) / opt.det_step))
+
+    def phase(y, x):
+        ty, tx = LAM * y + opt.tilt[0], LAM * x + opt.tilt[1]
+        t, p = math.hypot(ty, tx), math.atan2(ty, tx)
+        return 2 * math.pi / LAM * sum(c * t ** (nn + 1) / (nn + 1) * math.cos(mm * (p - ph))
+                                        for nn, mm, c, ph in opt.aberrations)
+
+    for i in [0, 5, len(prep.q) - 1]:
+        K = prep.K[i]
+        A = K.shape[0]
+        T = np.zeros((len(k), 2 * A), dtype=complex)
+        for j, (y, x) in enumerate(k):
+            for m in range(A):
+                Qy, Qx = K[m, 0] * dq, K[m, 1] * dq
+                L = amp(y, x) * amp(y - Qy, x - Qx) * np.exp(1j * (phase(y, x) - phase(y - Qy, x - Qx)))
+                R = amp(y, x) * amp(y + Qy, x + Qx) * np.exp(-1j * (phase(y, x) - phase(y + Qy, x + Qx)))
+                T[j, m] = L + R
+                T[j, A + m] = 1j * (L - R)
+        d = 2 * A
+        M = np.zeros((d, d), dtype=complex)
+        r = np.zeros(d, dtype=complex)
+        P = 0.0
+        for j in range(len(k)):
+            for a in range(d):
+                r[a] += w[j] * np.conj(T[j, a]) * cols[i][j]
+                for b in range(d):
+                    M[a, b] += w[j] * np.conj(T[j, a]) * T[j, b]
+            P += w[j] * abs(cols[i][j]) ** 2
+        assert np.allclose(prep.M[i], M, rtol=1e-12, atol=1e-12 * abs(M).max())
+        assert np.allclose(prep.r[i], r, rtol=1e-12, atol=1e-12 * abs(r).max())
+        assert prep.P[i] == pytest.approx(P, rel=1e-13)
+
+
+def test_gram_hermitian_psd():
+    prep, *_ = _small_problem("complex", u=3)
+    for M, r, P in zip(prep.M, prep.r, prep.P):
+        assert np.abs(M - M.conj().T).max() <= 1e-15 * max(1.0, np.abs(M).max())
+        aug = np.block([[M, r[:, None]], [r.conj()[None, :], np.array([[P]])]])
+        ev = np.linalg.eigvalsh(aug)
+        assert ev.min() >= -1e-12 * ev.max()
+
+
+def test_eigenbasis_equals_direct_solve():
+    prep, *_ = _small_problem("phase", u=3)
+    for s in [1e-3, 1e-1, 3.0]:
+        xe = O.solve(prep, s, use_eigenbasis=True)
+        xd = O.solve(prep, s, use_eigenbasis=False)
+        for a, b in zip(xe, xd):
+            assert np.linalg.norm(a - b) <= 1e-11 * max(np.linalg.norm(b), 1e-300)
+    for lam in prep.lam:
+        assert np.all(np.diff(lam) >= 0)
+
+
+def test_complex_system_contains_phase_system():
+    pc, *_ = _small_problem("complex", u=3, seed=2)
+    pp, *_ = _small_problem("phase", u=3, seed=2)
+    for Mc, rc, Mp, rp, A in zip(pc.M, pc.r, pp.M, pp.r, pc.A):
+        assert np.allclose(Mc[A:, A:], Mp, rtol=0, atol=1e-15 * np.abs(Mc).max())
+        assert np.allclose(rc[A:], rp, rtol=0, atol=1e-15 * np.abs(rc).max())
+
+
+@pytest.mark.parametrize("method", ["phase", "complex"])
+def test_solution_minimizes_objective(method):
+    """x(lambda) minimizes sum_k w |g - T x|^2 + lambda scale sum p |x|^2,
+    evaluated by brute force; and the residual identity holds."""
+    prep, k, w, cols, opt, n, step, u = _small_problem(method, u=3, seed=4)
+    dq = O.scan_frequency_step(n, step)
+    strength = 0.05 if method == "phase" else (0.05, 0.02)
+    xs = O.solve(prep, strength)
+    rng = np.random.default_rng(1)
+    for i in [1, 7, 20]:
+        T = O.transfer(k, prep.K[i] * dq, opt, method)
+        g = cols[i]
+        A = prep.A[i]
+        if method == "phase":
+            reg = strength * prep.scale * prep.p[i]
+        else:
+            reg = prep.scale * np.concatenate([strength[0] * prep.p[i][:A], strength[1] * prep.p[i][A:]])
+
+        def J(x):
+            return np.sum(w * np.abs(g - T @ x) ** 2) + np.sum(reg * np.abs(x) ** 2)
+
+        x = xs[i]
+        j0 = J(x)
+        for _ in range(5):
+            d = rng.standard_normal(x.shape) + 1j * rng.standard_normal(x.shape)
+            d *= 1e-3 * np.linalg.norm(x) / np.linalg.norm(d)
+            assert J(x + d) > j0 and J(x - d) > j0
+        rho = np.sum(w * np.abs(g - T @ x) ** 2)
+        assert O.residual(prep.M[i], prep.r[i], prep.P[i], x) == pytest.approx(rho, rel=1e-10)
+
+
+def test_planted_transpose_breaks_minimality(monkeypatch):
+    """Using M^T instead of M in the solve is caught by the objective pin."""
+    prep, k, w, cols, opt, n, step, u = _small_problem("complex", u=3, seed=4)
+    prep.M = [M.T for M in prep.M]
+    xs = O.solve(prep, (0.05, 0.05))
+    dq = O.scan_frequency_step(n, step)
+    i = 7
+    T = O.transfer(k, prep.K[i] * dq, opt, "complex")
+    A = prep.A[i]
+    reg = prep.scale * 0.05 * np.concatenate([prep.p[i][:A], prep.p[i][A:]])
+    x_true = np.linalg.solve(T.conj().T @ (w[:, None] * T) + np.diag(reg), T.conj().T @ (w * cols[i]))
+    assert np.linalg.norm(xs[i] - x_true) > 1e-6 * np.linalg.norm(x_true)
+
+
+# ----------------------------------------------------------------------------
+# closed-form recovery and scatter
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("method", ["phase", "complex"])
+def test_noise_free_recovery_and_scatter(method):
+    """Noise-free first-order data from a known object: the prepared system
+    returns x = (M + mu D)^-1 M x_true and, as mu -> 0, x_true on every
+    well-conditioned frequency; the scatter places it at fft2(c)/u^2."""
+    n, step, u = 16, 0.5, 2
+    opt = tiny_optics(0.125)
+    rng = np.random.default_rng(11)
+    nf = u * n
+    phi = S.band_limited_field(nf, rng, std=0.05)
+    amp = S.band_limited_field(nf, rng, std=0.02) if method == "complex" else np.zeros_like(phi)
+    c = amp + 1j * phi
+    w = workload("c2")
+    _, k = bf_pixels(w)
+    act = O.active_pixels(k, opt)
+    k = k[act]
+    G = S.first_order_G(k, c, n, step, u, opt)
+    q = O.unique_frequencies(n)
+    cols = [G[:, iy, ix] for iy, ix in q]
+    wts = np.ones(len(k))
+    prep = O.prepare(q, cols, k, wts, n, step, u, opt, method, smoothness=ALPHA / LAM)
+    FA, FP = S.fine_spectrum(amp, u), S.fine_spectrum(phi, u)
+    tiny = 1e-10 if method == "phase" else (1e-10, 1e-10)
+    xs = O.solve(prep, tiny)
+    checked = 0
+    x_true_all = []
+    for i, K in enumerate(prep.K):
+        xt = FP[K[:, 0] % nf, K[:, 1] % nf]
+        if method == "complex":
+            xt = np.concatenate([FA[K[:, 0] % nf, K[:, 1] % nf], xt])
+        x_true_all.append(xt)
+        M = prep.M[i]
+        ev = np.linalg.eigvalsh(M)
+        if ev[0] > 1e-6 * ev[-1]:
+            assert np.linalg.norm(xs[i] - xt) <= 1e-6 * np.linalg.norm(xt) + 1e-12
+            checked += 1
+        # moderate strength: closed form of Tikhonov on exact data
+        s = 0.1 if method == "phase" else (0.1, 0.1)
+        xm = O.solve(prep, s)[i] if i < 3 else None
+        if xm is not None:
+            mu = 0.1 * prep.scale
+            want = np.linalg.solve(M + np.diag(mu * prep.p[i]), M @ xt)
+            assert np.allclose(xm, want, rtol=1e-9, atol=1e-12)
+    assert checked > 0.8 * len(prep.K)
+    ncomp = 2 if method == "complex" else 1
+    spec = O.scatter(prep.q, prep.K, x_true_all, n, u, ncomp)
+    want = [FA, FP] if method == "complex" else [FP]
+    for c_i in range(ncomp):
+        sp = spec[c_i]
+        ref = want[c_i][:, : nf // 2 + 1]
+        nz = sp != 0
+        assert np.allclose(sp[nz], ref[nz], rtol=1e-12, atol=1e-15)
+        # the fine real-field spectrum is recovered wherever an alias reaches it
+        assert nz.sum() > 0.5 * nz.size
+
+
+# ----------------------------------------------------------------------------
+# SSB sum and agreement
+# ----------------------------------------------------------------------------
+
+
+def test_ssb_equals_unregularized_prepare_at_u1():
+    """At one alias per frequency with no prior and zero strength, S/N is the
+    prepared solution."""
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    opt = w.optics
+    act = O.active_pixels(k, opt)
+    rng = np.random.default_rng(2)
+    q = O.unique_frequencies(w.n_scan)[::7]
+    cols = [rng.standard_normal(len(act)) + 1j * rng.standard_normal(len(act)) for _ in q]
+    wts = rng.uniform(0.5, 1.5, len(act))
+    prep = O.prepare(q, cols, k[act], wts, w.n_scan, w.step, 1, opt, "phase", smoothness=0.0)
+    Sv, Nv = O.ssb(q, cols, k[act], wts, w.n_scan, w.step, [opt])
+    n_ok = 0
+    for i in range(len(q)):
+        if Nv[0, i] > 1e-9 * Nv.max():
+            x = O.solve_direct(prep.M[i], prep.r[i], np.zeros(1))
+            assert abs(Sv[0, i] / Nv[0, i] - x[0]) <= 1e-12 * abs(x[0]) + 1e-15
+            n_ok += 1
+    assert n_ok > 0.5 * len(q)
+
+
+def test_agreement_is_maximal_at_true_optics():
+    """Noise-free single-alias data: the agreement peaks at the true defocus
+    and stays <= 1."""
+    n, step = 16, 0.5
+    opt = Optics(LAM, ALPHA, 0.1, soft=True, aberrations=[(1, 0, -60.0, 0.0), (3, 0, 1e4, 0.0)])
+    rng = np.random.default_rng(8)
+    phi = S.band_limited_field(n, rng, std=0.05, cutoff=0.6)
+    w = workload("c1")
+    _, k = bf_pixels(w)
+    k = k * 0.1 / w.optics.det_step
+    act = O.active_pixels(k, opt)
+    k = k[act]
+    G = S.first_order_G(k, 1j * phi, n, step, 1, opt)
+    wts = np.ones(len(k))
+    entries = np.argwhere(O.band_mask(n, step, (0.2, 0.9)))
+    cols = [G[:, iy, ix] for iy, ix in entries]
+    power = np.array([np.sum(wts * np.abs(g) ** 2) for g in cols])
+    shifts = [-20.0, -10.0, -5.0, 0.0, 5.0, 10.0, 20.0]
+    sets = [opt.replace(aberrations=[(1, 0, -60.0 + d, 0.0), (3, 0, 1e4, 0.0)]) for d in shifts]
+    Sv, Nv = O.ssb(entries, cols, k, wts, n, step, sets)
+    E = O.agreement(Sv, Nv, power)
+    assert np.argmax(E) == shifts.index(0.0)
+    assert E[shifts.index(0.0)] == pytest.approx(1.0, abs=1e-9)
+    assert np.all(np.diff(E[:4]) > 0) and np.all(np.diff(E[3:]) < 0)
+
+
+def test_bright_field_sum_linearity():
+    """Summing corrected G over pixels then one inverse FFT equals the mean of
+    per-pixel inverse FFTs ([P4] object-redraw identity)."""
+    rng = np.random.default_rng(0)
+    G = rng.standard_normal((5, 8, 8)) + 1j * rng.standard_normal((5, 8, 8))
+    corr = np.exp(1j * rng.uniform(0, 6.3, (5, 8, 8)))
+    a = np.fft.ifft2((G * corr).sum(axis=0)) / 5
+    b = np.mean([np.fft.ifft2(G[i] * corr[i]) for i in range(5)], axis=0)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
