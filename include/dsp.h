@@ -1,0 +1,234 @@
+/*
+ * dsp.h -- regularized direct (single-side-band) ptychography on MI355X.
+ *
+ * C ABI of libdsp.so.  Plain pointers and sizes only.  Every function returns
+ * a dsp_status; nothing throws across the ABI.  On error the outputs are
+ * unspecified, no handle is created, an existing handle is unchanged, and
+ * dsp_last_error() returns a message (thread-local).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Scan: square N x N (N even, >= 4), step s (A); scan-frequency step
+ * dq = 1 / (N s).  Measured data G(q, k) is the Hermitian half plane of the
+ * scan-space FFT of each bright-field pixel's intensity trace, complex64,
+ * layout [n_bf][N][N/2+1] (pixel-major, contiguous along the last axis),
+ * device memory ("Historical WebGPU G(q,k) memory experiment", section
+ * "Why herm is exactly lossless").  Stored row iy means signed frequency
+ * iy (iy < N/2) or iy - N.
+ *
+ * Bright-field pixel coordinates k are (k_y, k_x) in 1/A in the scan frame
+ * (detector rotation already applied), host double[n_bf][2].  Weights are
+ * host double[n_bf] (NULL: all 1).  Only pixels with non-zero aperture
+ * weight are used ("active" pixels).
+ *
+ * Optics: aberration phase in Krivanek polar notation,
+ *   chi(k) = (2 pi / lambda) sum C_nm t^(n+1) / (n+1) cos(m (p - phi_nm)),
+ *   theta = lambda k + tau, t = |theta|, p = atan2(theta_y, theta_x);
+ * probe amplitude A(k) = a(k) exp(-i chi(k)); soft aperture
+ * a = clamp(1/2 + (alpha/lambda - |k|) / dk, 0, 1), hard a = [|k| <= alpha/lambda]
+ * ("Tilt-corrected SSB on CUDA: fit and preview speed", section "Changes":
+ * the soft edge's denominator is the detector step).
+ *
+ * Weak-object transfer of object frequency Q at pixel k ("Where the 9 s of
+ * regularized preparation goes", section "Code path"; "Preparation in one
+ * kernel per alias count", section "What changed" 1-2):
+ *   L = a(k) a(k-Q) exp(+i [chi(k) - chi(k-Q)]),
+ *   R = a(k) a(k+Q) exp(-i [chi(k) - chi(k+Q)]),
+ *   T_phi = i (L - R) (phase), T_A = L + R (log-amplitude).
+ *
+ * Solved frequencies: stored (iy, ix) with ix < N/2, iy != N/2, excluding
+ * ix = 0 with signed row <= 0; row-major order; n_q = N (N - 2) / 2.  Aliases
+ * of q on the u-times finer grid: K = (iy_signed + j_y N, ix + j_x N) inside
+ * [-uN/2, uN/2)^2 with |K|^2 dq^2 < R^2, R = 2 alpha/lambda (+ dk when soft);
+ * order (j_y, j_x) ascending; A(q) = number of aliases (1..9).
+ *
+ * Asynchrony: validation and host geometry run synchronously in the call;
+ * kernels are enqueued on the caller's HIP stream (hipStream_t passed as
+ * void*, NULL = the null stream) and results are valid once that stream has
+ * passed the call's work.  Device inputs must stay alive and unchanged until
+ * then.  Launch or runtime failures return DSP_EDEVICE from the call (or the
+ * next call) with HIP's message.  NaN/Inf in G propagate unchecked.
+ *
+ * Thread safety: one handle per thread; distinct handles are independent.
+ * All device memory a handle owns lives on the device current at prepare.
+ */
+#ifndef DSP_H
+#define DSP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSP_OK = 0,
+    DSP_EINVAL = 1,        /* bad argument: NULL, size, range, layout */
+    DSP_EUNSUPPORTED = 2,  /* valid but not built: depth != 0, odd N, u > 4 */
+    DSP_EALIAS = 3,        /* an alias count above the compiled maximum */
+    DSP_ENOMEM = 4,        /* device or host allocation failed */
+    DSP_EDEVICE = 5        /* HIP runtime / launch failure */
+} dsp_status;
+
+typedef enum { DSP_PHASE = 0, DSP_COMPLEX = 1 } dsp_method;
+
+/* One Krivanek term C_{n,m} (A) at angle phi (rad); 1 <= n <= 5,
+ * 0 <= m <= n+1, n+1-m even. */
+typedef struct {
+    int n, m;
+    double c_A;
+    double phi_rad;
+} dsp_aberration;
+
+#define DSP_MAX_ABERRATIONS 16
+
+typedef struct {
+    double wavelength_A;     /* lambda */
+    double semiangle_rad;    /* alpha */
+    double det_step_invA;    /* dk: detector pixel pitch in the scan frame */
+    int soft_aperture;       /* 1: soft edge one pixel wide, 0: hard */
+    double tilt_rad[2];      /* (tau_y, tau_x) */
+    double depth_A;          /* must be 0 */
+    int n_aber;              /* <= DSP_MAX_ABERRATIONS */
+    dsp_aberration aber[DSP_MAX_ABERRATIONS];
+} dsp_optics;
+
+typedef struct {
+    int n_scan;              /* N: square N x N scan, even, >= 4 */
+    double step_A;           /* s */
+} dsp_scan;
+
+typedef struct {
+    dsp_method method;
+    int upsampling;          /* u in 1..4 */
+    double smoothness_invA;  /* prior p(Q) = (1 + |Q|^2/s^2)^2; <= 0: p = 1 */
+    int flags;               /* DSP_FLAG_* */
+} dsp_prepare_opts;
+
+#define DSP_FLAG_TIMING 1    /* record per-stage HIP events (read by dsp_info) */
+
+typedef struct dsp_handle dsp_handle;
+
+typedef struct {
+    int n_q;                 /* solved frequencies */
+    int a_max;               /* largest alias count */
+    int n_comp;              /* unknown components: 1 (phase), 2 (complex) */
+    int dim;                 /* slot dimension D = n_comp * a_max + 1 */
+    int n_bf, n_active_bf;
+    int method, upsampling, n_scan;
+    int n_tiles;             /* 4 x 16 frequency tiles of the Gram kernels */
+    int alias_hist[10];      /* alias_hist[A] = frequencies with A aliases */
+    double scale;            /* strength unit: sum of active weights */
+    double g_bytes;          /* algorithmic G bytes a prepare reads: n_q * n_active * 8 */
+    double lobes;            /* nonzero weak-object lobes a prepare evaluates */
+    double host_ms;          /* host geometry + upload enqueue of the last prepare */
+    double stage_ms[4];      /* with DSP_FLAG_TIMING: pixel terms, Gram, eigenbasis, total */
+} dsp_info_t;
+
+/*
+ * Prepare: per solved frequency, the weighted augmented Gram
+ * [T g]^H W [T g] (complex128) -> M = T^H W T, r = T^H W g, P = g^H W g,
+ * and, for DSP_PHASE, the eigenbasis of D^-1/2 M D^-1/2 (D = diag(p)), so any
+ * strength is a diagonal evaluation ("Where the 9 s of regularized
+ * preparation goes", section "Code path").  Complex unknowns are
+ * [A_l(Q_1..Q_A), phi(Q_1..Q_A)]; phase unknowns [phi(Q_1..Q_A)].
+ *
+ * G_c64_dev: device complex64 [n_bf][N][N/2+1], borrowed (not retained).
+ * bf_coords_host: double[n_bf][2]; weights_host: double[n_bf] or NULL.
+ * Host arrays are copied during the call.  *out receives a new handle that
+ * owns its device buffers (free with dsp_destroy).
+ */
+dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_host,
+                       const double *weights_host, const dsp_scan *scan, const dsp_optics *optics,
+                       const dsp_prepare_opts *opts, void *hip_stream, dsp_handle **out);
+
+/*
+ * Solve at S strengths.  Phase: strengths_host = double[S] (lambda);
+ * x = U (c / (Lambda + lambda scale)).  Complex: strengths_host =
+ * double[S][2] (lambda_A, lambda_phi); x = (M + scale diag(lambda_A p,
+ * lambda_phi p))^-1 r.  ("Where the 9 s ...", section "Code path": complex
+ * keeps the Gram and solves at each strength.)
+ * x_out_c128_dev: device complex128 [S][n_comp][n_q][a_max]; slot m >= A(q)
+ * is written 0.  resid_out_dev: device double[S][n_q] (weighted misfit
+ * sum_k w |g - T x|^2) or NULL.
+ */
+dsp_status dsp_solve(dsp_handle *h, const double *strengths_host, int S, void *x_out_c128_dev,
+                     double *resid_out_dev, void *hip_stream);
+
+/*
+ * Scatter packed solutions to the fine half plane: spec_out_c128_dev
+ * complex128 [S][n_comp][uN][uN/2+1]; alias K lands at (K_y mod uN, K_x)
+ * when K_x > 0 or (K_x = 0 and K_y >= 0), otherwise its conjugate lands at
+ * -K.  Entries no alias reaches are 0.
+ */
+dsp_status dsp_scatter(const dsp_handle *h, const void *x_packed_c128_dev, int S,
+                       void *spec_out_c128_dev, void *hip_stream);
+
+/*
+ * SSB / agreement pass over the stored entries (one alias per frequency,
+ * Q = q) for B optics sets, reading G once ("Tilt-corrected SSB on CUDA",
+ * section "Where the time went": one pass evaluates several parameter sets;
+ * "Historical WebGPU G(q,k) memory experiment", section "Object-redraw fast
+ * path": the corrected G summed over pixels in Fourier space).
+ *   Gamma = T_phi(q, k; set b); S_b(q) = sum_k w conj(Gamma) g;
+ *   N_b(q) = sum_k w |Gamma|^2;
+ *   E_b = sum_{band, N>0} |S_b|^2 / N_b / sum_{band} sum_k w |g|^2.
+ * sets_host: dsp_optics[B], 1 <= B <= 8; the aperture parameters (lambda,
+ * alpha, dk, soft) must be equal across sets.  band_invA: double[2] (f_lo,
+ * f_hi), inclusive on |q|, or NULL for every stored entry.
+ * S_out_c128_dev: complex128 [B][N][N/2+1] or NULL; norm_out_dev: double
+ * [B][N][N/2+1] or NULL (entries outside the band are 0);
+ * agreement_out_host: double[B] or NULL (non-NULL synchronizes the stream).
+ */
+dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host,
+                   const double *weights_host, const dsp_scan *scan, const dsp_optics *sets_host,
+                   int B, const double *band_invA, void *S_out_c128_dev, double *norm_out_dev,
+                   double *agreement_out_host, void *hip_stream);
+
+/* Sizes, histogram, timings of a prepared handle (synchronizes the timing
+ * events when DSP_FLAG_TIMING was set). */
+dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out);
+
+/*
+ * Parity export.  aug_out_c128_dev: complex128 [n_q][D][D], the Hermitian
+ * augmented system in slot coordinates: unknown (component c, alias m) at
+ * index c * a_max + m, g at index D - 1; rows/columns of absent aliases are 0.
+ * eig_out_dev: double [n_q][a_max] ascending eigenvalues (phase), or NULL.
+ */
+dsp_status dsp_export_system(const dsp_handle *h, void *aug_out_c128_dev, double *eig_out_dev,
+                             void *hip_stream);
+
+/* Host copies of the handle's alias table: q_host int32[n_q][2] (iy, ix),
+ * count_host int32[n_q], K_host int32[n_q][a_max][2] (0 past A(q)). */
+dsp_status dsp_alias_table(const dsp_handle *h, int32_t *q_host, int32_t *count_host, int32_t *K_host);
+
+void dsp_destroy(dsp_handle *h);
+const char *dsp_last_error(void);
+
+/* ---------------- host-only geometry (no device calls) ---------------- */
+
+/* n_q, a_max and alias histogram hist_out[10] (may be NULL) of a scan. */
+dsp_status dsp_geometry_counts(const dsp_scan *scan, const dsp_optics *optics, int upsampling,
+                               int *n_q, int *a_max, int32_t *hist_out);
+
+/* Solved frequencies and their aliases, same layout as dsp_alias_table
+ * (K_host sized n_q * a_max * 2 with a_max from dsp_geometry_counts). */
+dsp_status dsp_alias_geometry(const dsp_scan *scan, const dsp_optics *optics, int upsampling,
+                              int32_t *q_host, int32_t *count_host, int32_t *K_host);
+
+/* Active bright-field pixels (a(k) > 0), input order: idx_out int32[n_bf]. */
+dsp_status dsp_active_bf(const double *bf_coords_host, int n_bf, const dsp_optics *optics,
+                         int32_t *idx_out, int *n_active);
+
+/* Stored entries with f_lo <= |q| <= f_hi (the SSB band). */
+dsp_status dsp_band_count(const dsp_scan *scan, const double *band_invA, int *count);
+
+/* The library's chi(k) (its polynomial expansion of the Krivanek terms)
+ * evaluated on the host at n points k_host double[n][2]: chi_out double[n]. */
+dsp_status dsp_chi_host(const dsp_optics *optics, const double *k_host, int n, double *chi_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSP_H */

@@ -1,0 +1,899 @@
+// C ABI of libdsp: validation, host geometry, device buffers and launches.
+//
+// Host geometry (data-only, recomputed per call): the solved frequency list,
+// alias tables, 4 x 16 frequency tiles with their alias-slot unions, priors,
+// the active bright-field set and the aberration polynomial.  Pages: "Where
+// the 9 s of regularized preparation goes" (Code path: frequencies bucketed
+// by alias count; prior; gather) and "Preparation in one kernel per alias
+// count" (What changed 4: data-only layout computed once, kernels per optics).
+#include "../../include/dsp.h"
+#include "dsp_internal.hpp"
+#include "dsp_kernels.hpp"
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+using namespace dsp;
+
+namespace {
+
+thread_local std::string g_err;
+
+dsp_status fail(dsp_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+#define HIP_TRY(expr)                                                                     \
+    do {                                                                                  \
+        hipError_t e_ = (expr);                                                           \
+        if (e_ != hipSuccess)                                                             \
+            return fail(e_ == hipErrorOutOfMemory ? DSP_ENOMEM : DSP_EDEVICE, "%s: %s", #expr, \
+                        hipGetErrorString(e_));                                           \
+    } while (0)
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+
+dsp_status check_scan(const dsp_scan *scan) {
+    if (!scan) return fail(DSP_EINVAL, "scan is NULL");
+    if (scan->n_scan < 4) return fail(DSP_EINVAL, "n_scan must be >= 4 (got %d)", scan->n_scan);
+    if (scan->n_scan % 2) return fail(DSP_EUNSUPPORTED, "odd n_scan %d is not supported", scan->n_scan);
+    if (scan->n_scan > 8192) return fail(DSP_EUNSUPPORTED, "n_scan %d above 8192", scan->n_scan);
+    if (!(scan->step_A > 0.0) || !std::isfinite(scan->step_A)) return fail(DSP_EINVAL, "step_A must be > 0");
+    return DSP_OK;
+}
+
+dsp_status check_optics(const dsp_optics *o) {
+    if (!o) return fail(DSP_EINVAL, "optics is NULL");
+    if (!(o->wavelength_A > 0.0) || !std::isfinite(o->wavelength_A)) return fail(DSP_EINVAL, "wavelength must be > 0");
+    if (!(o->semiangle_rad > 0.0) || !std::isfinite(o->semiangle_rad)) return fail(DSP_EINVAL, "semiangle must be > 0");
+    if (!(o->det_step_invA > 0.0) || !std::isfinite(o->det_step_invA)) return fail(DSP_EINVAL, "det_step must be > 0");
+    if (o->soft_aperture != 0 && o->soft_aperture != 1) return fail(DSP_EINVAL, "soft_aperture must be 0 or 1");
+    if (o->depth_A != 0.0) return fail(DSP_EUNSUPPORTED, "depth terms are not built (depth_A must be 0)");
+    if (!std::isfinite(o->tilt_rad[0]) || !std::isfinite(o->tilt_rad[1])) return fail(DSP_EINVAL, "tilt not finite");
+    if (o->n_aber < 0 || o->n_aber > DSP_MAX_ABERRATIONS)
+        return fail(DSP_EINVAL, "n_aber %d outside [0, %d]", o->n_aber, DSP_MAX_ABERRATIONS);
+    for (int i = 0; i < o->n_aber; ++i) {
+        const dsp_aberration &a = o->aber[i];
+        if (a.n < 1 || a.n > 5 || a.m < 0 || a.m > a.n + 1 || ((a.n + 1 - a.m) & 1))
+            return fail(DSP_EINVAL, "aberration %d: (n, m) = (%d, %d) is not a Krivanek term of order 1..5", i, a.n, a.m);
+        if (!std::isfinite(a.c_A) || !std::isfinite(a.phi_rad)) return fail(DSP_EINVAL, "aberration %d not finite", i);
+    }
+    return DSP_OK;
+}
+
+dsp_status check_upsampling(int u) {
+    if (u < 1) return fail(DSP_EINVAL, "upsampling must be >= 1 (got %d)", u);
+    if (u > 4) return fail(DSP_EUNSUPPORTED, "upsampling %d above 4", u);
+    return DSP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// optics helpers
+// ---------------------------------------------------------------------------
+
+double binom(int n, int k) {
+    double r = 1.0;
+    for (int i = 1; i <= k; ++i) r = r * (n - k + i) / i;
+    return r;
+}
+
+// chi(theta) polynomial coefficients (rad) from the Krivanek terms:
+// t^(n+1) cos(m (p - phi)) = Re[exp(-i m phi) w^m] (w w*)^((n+1-m)/2),
+// w^m = sum_k C(m,k) i^k tx^(m-k) ty^k, (w w*)^h = sum_l C(h,l) tx^(2h-2l) ty^(2l).
+void chi_coefficients(const dsp_optics *o, double *coef) {
+    for (int i = 0; i < CHI_NCOEF; ++i) coef[i] = 0.0;
+    const double two_pi = 6.283185307179586476925286766559;
+    for (int t = 0; t < o->n_aber; ++t) {
+        const dsp_aberration &a = o->aber[t];
+        const int n = a.n, m = a.m, h = (n + 1 - m) / 2;
+        const double f = two_pi / o->wavelength_A * a.c_A / (n + 1);
+        const double cm = std::cos(m * a.phi_rad), sm = std::sin(m * a.phi_rad);
+        for (int k = 0; k <= m; ++k) {
+            // Re[(cm - i sm) i^k] = cm Re(i^k) + sm Im(i^k)
+            static const int re_ik[4] = {1, 0, -1, 0};
+            static const int im_ik[4] = {0, 1, 0, -1};
+            const double ck = binom(m, k) * (cm * re_ik[k & 3] + sm * im_ik[k & 3]);
+            if (ck == 0.0) continue;
+            for (int l = 0; l <= h; ++l) {
+                const int px = (m - k) + 2 * (h - l);
+                const int py = k + 2 * l;
+                coef[chi_off(py) + px] += f * ck * binom(h, l);
+            }
+        }
+    }
+}
+
+OpticsDev make_optics_dev(const dsp_optics *o) {
+    OpticsDev d;
+    d.lam = o->wavelength_A;
+    d.tau_y = o->tilt_rad[0];
+    d.tau_x = o->tilt_rad[1];
+    chi_coefficients(o, d.chi_c);
+    return d;
+}
+
+ApertureDev make_aperture_dev(const dsp_optics *o) {
+    ApertureDev a;
+    a.kc = o->semiangle_rad / o->wavelength_A;
+    a.inv_dk = 1.0 / o->det_step_invA;
+    a.soft = o->soft_aperture;
+    const double h = 0.5 * o->det_step_invA;
+    if (a.soft) {
+        const double rin = std::max(0.0, a.kc - h);
+        a.rin2 = rin * rin;
+        a.rout2 = (a.kc + h) * (a.kc + h);
+    } else {
+        a.rin2 = a.kc * a.kc;
+        a.rout2 = a.kc * a.kc;
+    }
+    return a;
+}
+
+// a(|k|) > 0, evaluated as the definition: clamp(1/2 + (kc - |k|)/dk, 0, 1).
+bool pixel_active(const dsp_optics *o, double ky, double kx) {
+    const double kabs = std::hypot(ky, kx);
+    const double kc = o->semiangle_rad / o->wavelength_A;
+    if (o->soft_aperture) {
+        double a = 0.5 + (kc - kabs) / o->det_step_invA;
+        a = std::min(1.0, std::max(0.0, a));
+        return a > 0.0;
+    }
+    return kabs <= kc;
+}
+
+double alias_radius(const dsp_optics *o) {
+    double r = (2.0 * o->semiangle_rad) / o->wavelength_A;
+    if (o->soft_aperture) r = r + o->det_step_invA;
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// frequency geometry
+// ---------------------------------------------------------------------------
+
+struct Geometry {
+    int N = 0, u = 0, n_q = 0, a_max = 0;
+    double dq = 0.0;
+    std::vector<int32_t> q;       // [n_q][2] stored (iy, ix)
+    std::vector<int32_t> count;   // [n_q]
+    std::vector<int32_t> K;       // [n_q][a_max][2]
+    std::vector<int32_t> jy, jx;  // [n_q][a_max] alias offsets
+    int hist[10] = {0};
+};
+
+dsp_status build_geometry(const dsp_scan *scan, const dsp_optics *o, int u, Geometry &g) {
+    const int N = scan->n_scan;
+    g.N = N;
+    g.u = u;
+    g.dq = 1.0 / (N * scan->step_A);
+    const double dq = g.dq;
+    const double R = alias_radius(o);
+    const int half = (u * N) / 2;
+    std::vector<int32_t> ktmp;
+    std::vector<int32_t> jtmp;
+    std::vector<int> cnt;
+    g.q.clear();
+    const int maxc = (2 * u + 1) * (2 * u + 1);
+    for (int iy = 0; iy < N; ++iy) {
+        if (iy == N / 2) continue;
+        const int yh = iy < N / 2 ? iy : iy - N;
+        for (int ix = 0; ix < N / 2; ++ix) {
+            if (ix == 0 && yh <= 0) continue;
+            g.q.push_back(iy);
+            g.q.push_back(ix);
+            int c = 0;
+            for (int jyy = -u; jyy <= u; ++jyy) {
+                const int ky = yh + jyy * N;
+                if (ky < -half || ky >= half) continue;
+                for (int jxx = -u; jxx <= u; ++jxx) {
+                    const int kx = ix + jxx * N;
+                    if (kx < -half || kx >= half) continue;
+                    const double k2 = (double)((long long)ky * ky + (long long)kx * kx);
+                    if (k2 * (dq * dq) < R * R) {
+                        ktmp.push_back(ky);
+                        ktmp.push_back(kx);
+                        jtmp.push_back(jyy);
+                        jtmp.push_back(jxx);
+                        ++c;
+                    }
+                }
+            }
+            (void)maxc;
+            cnt.push_back(c);
+        }
+    }
+    g.n_q = (int)cnt.size();
+    g.a_max = 0;
+    for (int c : cnt) g.a_max = std::max(g.a_max, c);
+    if (g.a_max > 9) return fail(DSP_EALIAS, "alias count %d above 9", g.a_max);
+    g.count.assign(cnt.begin(), cnt.end());
+    const int am = std::max(1, g.a_max);
+    g.K.assign((size_t)g.n_q * am * 2, 0);
+    g.jy.assign((size_t)g.n_q * am, 0);
+    g.jx.assign((size_t)g.n_q * am, 0);
+    size_t pos = 0;
+    for (int i = 0; i < g.n_q; ++i) {
+        for (int m = 0; m < cnt[i]; ++m, ++pos) {
+            g.K[((size_t)i * am + m) * 2] = ktmp[2 * pos];
+            g.K[((size_t)i * am + m) * 2 + 1] = ktmp[2 * pos + 1];
+            g.jy[(size_t)i * am + m] = jtmp[2 * pos];
+            g.jx[(size_t)i * am + m] = jtmp[2 * pos + 1];
+        }
+        g.hist[std::min(cnt[i], 9)]++;
+    }
+    return DSP_OK;
+}
+
+// Group the solved frequencies into 4 x 16 tiles (rows = signed row, cols =
+// ix) and collect each tile's sorted union of alias offsets.  A tile whose
+// union exceeds the kernels' slot maximum is split into sub-tiles with the
+// same origin and disjoint lane subsets (greedy over the lanes' alias sets).
+struct TileGroups {
+    std::vector<GramTile> tiles;      // grouped by nj, groups in ascending nj
+    std::vector<int> group_nj, group_off, group_n;
+};
+
+typedef std::vector<std::pair<int, int>> JSet;
+
+void finish_tile(GramTile &t, const JSet &js_in, const Geometry &g,
+                 std::map<int, std::vector<std::pair<long long, GramTile>>> &by_nj) {
+    const int am = std::max(1, g.a_max);
+    JSet js = js_in;
+    if (js.empty()) js.emplace_back(0, 0);   // no aliases anywhere: one inactive slot
+    t.nj = (int)js.size();
+    long long cost = 0;
+    for (int s = 0; s < t.nj; ++s) {
+        t.jy[s] = (int8_t)js[s].first;
+        t.jx[s] = (int8_t)js[s].second;
+    }
+    for (int l = 0; l < 64; ++l) {
+        const int qi = t.qidx[l];
+        t.mask[l] = 0;
+        if (qi < 0) continue;
+        cost += g.count[qi];
+        unsigned msk = 0;
+        for (int m = 0; m < g.count[qi]; ++m) {
+            const std::pair<int, int> j(g.jy[(size_t)qi * am + m], g.jx[(size_t)qi * am + m]);
+            const int s = (int)(std::lower_bound(js.begin(), js.end(), j) - js.begin());
+            msk |= 1u << s;
+        }
+        t.mask[l] = (uint16_t)msk;
+    }
+    by_nj[t.nj].emplace_back(-cost, t);
+}
+
+dsp_status build_gram_tiles(const Geometry &g, int max_nj, TileGroups &tg) {
+    const int N = g.N, am = std::max(1, g.a_max);
+    // index of each solved frequency by (iy, ix)
+    std::vector<int32_t> qidx((size_t)N * (N / 2), -1);
+    for (int i = 0; i < g.n_q; ++i) qidx[(size_t)g.q[2 * i] * (N / 2) + g.q[2 * i + 1]] = i;
+    std::map<int, std::vector<std::pair<long long, GramTile>>> by_nj;
+    for (int yh0 = -N / 2 + 1; yh0 <= N / 2 - 1; yh0 += TILE_Y) {
+        for (int ix0 = 0; ix0 < N / 2; ix0 += TILE_X) {
+            int lane_q[64];
+            JSet lane_js[64];
+            JSet uni;
+            int nvalid = 0;
+            for (int l = 0; l < 64; ++l) {
+                const int yh = yh0 + l / TILE_X, ix = ix0 + l % TILE_X;
+                lane_q[l] = -1;
+                if (yh > N / 2 - 1 || ix >= N / 2) continue;
+                const int iy = yh < 0 ? yh + N : yh;
+                const int qi = qidx[(size_t)iy * (N / 2) + ix];
+                if (qi < 0) continue;
+                lane_q[l] = qi;
+                ++nvalid;
+                for (int m = 0; m < g.count[qi]; ++m)
+                    lane_js[l].emplace_back(g.jy[(size_t)qi * am + m], g.jx[(size_t)qi * am + m]);
+                uni.insert(uni.end(), lane_js[l].begin(), lane_js[l].end());
+            }
+            if (nvalid == 0) continue;
+            std::sort(uni.begin(), uni.end());
+            uni.erase(std::unique(uni.begin(), uni.end()), uni.end());
+            GramTile base;
+            std::memset(&base, 0, sizeof base);
+            base.yh0 = yh0;
+            base.ix0 = ix0;
+            if ((int)uni.size() <= max_nj) {
+                for (int l = 0; l < 64; ++l) base.qidx[l] = lane_q[l];
+                finish_tile(base, uni, g, by_nj);
+                continue;
+            }
+            // split: each sub-tile takes lanes while its union stays within max_nj
+            bool taken[64] = {false};
+            int left = nvalid;
+            while (left > 0) {
+                GramTile t = base;
+                JSet js;
+                for (int l = 0; l < 64; ++l) t.qidx[l] = -1;
+                for (int l = 0; l < 64; ++l) {
+                    if (lane_q[l] < 0 || taken[l]) continue;
+                    JSet tryu = js;
+                    tryu.insert(tryu.end(), lane_js[l].begin(), lane_js[l].end());
+                    std::sort(tryu.begin(), tryu.end());
+                    tryu.erase(std::unique(tryu.begin(), tryu.end()), tryu.end());
+                    if ((int)tryu.size() > max_nj) continue;
+                    js.swap(tryu);
+                    t.qidx[l] = lane_q[l];
+                    taken[l] = true;
+                    --left;
+                }
+                if (js.empty() && left > 0) {
+                    // a single frequency above the maximum (checked by the caller)
+                    return fail(DSP_EALIAS, "a frequency needs more than %d alias slots", max_nj);
+                }
+                finish_tile(t, js, g, by_nj);
+            }
+        }
+    }
+    tg.tiles.clear();
+    tg.group_nj.clear();
+    tg.group_off.clear();
+    tg.group_n.clear();
+    for (auto &kv : by_nj) {
+        auto &v = kv.second;
+        std::stable_sort(v.begin(), v.end(), [](const std::pair<long long, GramTile> &a,
+                                                const std::pair<long long, GramTile> &b) { return a.first < b.first; });
+        tg.group_nj.push_back(kv.first);
+        tg.group_off.push_back((int)tg.tiles.size());
+        tg.group_n.push_back((int)v.size());
+        for (auto &p : v) tg.tiles.push_back(p.second);
+    }
+    return DSP_OK;
+}
+
+struct ActiveSet {
+    std::vector<int32_t> idx;
+    std::vector<PixelRec> pix;
+    double scale = 0.0;
+};
+
+dsp_status build_active(const double *k, const double *w, int n_bf, const dsp_optics *o, int N, ActiveSet &as) {
+    as.idx.clear();
+    as.pix.clear();
+    as.scale = 0.0;
+    const long long plane = (long long)N * (N / 2 + 1);
+    for (int i = 0; i < n_bf; ++i) {
+        const double ky = k[2 * i], kx = k[2 * i + 1];
+        if (!std::isfinite(ky) || !std::isfinite(kx)) return fail(DSP_EINVAL, "bf_coords[%d] not finite", i);
+        const double wi = w ? w[i] : 1.0;
+        if (!(wi >= 0.0) || !std::isfinite(wi)) return fail(DSP_EINVAL, "weights[%d] must be finite and >= 0", i);
+        if (!pixel_active(o, ky, kx)) continue;
+        PixelRec p;
+        std::memset(&p, 0, sizeof p);
+        p.ky = ky;
+        p.kx = kx;
+        p.w = wi;
+        p.goff = (long long)i * plane;
+        as.idx.push_back(i);
+        as.pix.push_back(p);
+        as.scale += wi;
+    }
+    return DSP_OK;
+}
+
+double now_ms() {
+    using namespace std::chrono;
+    return duration<double, std::milli>(steady_clock::now().time_since_epoch()).count();
+}
+
+template <class T>
+dsp_status dev_alloc(T **p, size_t n) {
+    *p = nullptr;
+    if (n == 0) n = 1;
+    HIP_TRY(hipMalloc((void **)p, n * sizeof(T)));
+    return DSP_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// handle
+// ---------------------------------------------------------------------------
+
+struct dsp_handle {
+    int device = 0;
+    int method = 0;
+    Geometry geo;
+    TileGroups tg;
+    ActiveSet act;
+    int n_bf = 0;
+    int D = 0, n_comp = 1;
+    double scale = 0.0;
+    double host_ms = 0.0;
+    // device
+    PixelRec *d_pix = nullptr;
+    GramTile *d_tiles = nullptr;
+    double2 *d_sys = nullptr;       // [n_q][tri_size(D)]
+    double *d_prior = nullptr;      // [n_q][a_max]
+    int32_t *d_count = nullptr;     // [n_q]
+    int32_t *d_K = nullptr;         // [n_q][a_max][2]
+    int32_t *d_bucket = nullptr;    // frequency lists by alias count
+    std::vector<int> bucket_off, bucket_n;   // per alias count 0..9
+    double *d_lam = nullptr;
+    double2 *d_U = nullptr;
+    double2 *d_c = nullptr;
+    bool timing = false;
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+
+    ~dsp_handle() {
+        hipSetDevice(device);
+        hipFree(d_pix);
+        hipFree(d_tiles);
+        hipFree(d_sys);
+        hipFree(d_prior);
+        hipFree(d_count);
+        hipFree(d_K);
+        hipFree(d_bucket);
+        hipFree(d_lam);
+        hipFree(d_U);
+        hipFree(d_c);
+        for (auto &e : ev)
+            if (e) hipEventDestroy(e);
+    }
+};
+
+extern "C" {
+
+const char *dsp_last_error(void) { return g_err.c_str(); }
+
+void dsp_destroy(dsp_handle *h) { delete h; }
+
+dsp_status dsp_geometry_counts(const dsp_scan *scan, const dsp_optics *optics, int upsampling, int *n_q, int *a_max,
+                               int32_t *hist_out) {
+    dsp_status st;
+    if ((st = check_scan(scan)) || (st = check_optics(optics)) || (st = check_upsampling(upsampling))) return st;
+    Geometry g;
+    if ((st = build_geometry(scan, optics, upsampling, g))) return st;
+    if (n_q) *n_q = g.n_q;
+    if (a_max) *a_max = g.a_max;
+    if (hist_out)
+        for (int i = 0; i < 10; ++i) hist_out[i] = g.hist[i];
+    return DSP_OK;
+}
+
+dsp_status dsp_alias_geometry(const dsp_scan *scan, const dsp_optics *optics, int upsampling, int32_t *q_host,
+                              int32_t *count_host, int32_t *K_host) {
+    dsp_status st;
+    if ((st = check_scan(scan)) || (st = check_optics(optics)) || (st = check_upsampling(upsampling))) return st;
+    Geometry g;
+    if ((st = build_geometry(scan, optics, upsampling, g))) return st;
+    if (q_host) std::memcpy(q_host, g.q.data(), g.q.size() * sizeof(int32_t));
+    if (count_host) std::memcpy(count_host, g.count.data(), g.count.size() * sizeof(int32_t));
+    if (K_host && g.a_max > 0) std::memcpy(K_host, g.K.data(), g.K.size() * sizeof(int32_t));
+    return DSP_OK;
+}
+
+dsp_status dsp_active_bf(const double *bf_coords_host, int n_bf, const dsp_optics *optics, int32_t *idx_out,
+                         int *n_active) {
+    dsp_status st;
+    if ((st = check_optics(optics))) return st;
+    if (n_bf < 0 || (n_bf > 0 && !bf_coords_host)) return fail(DSP_EINVAL, "bad bf_coords");
+    if (!n_active) return fail(DSP_EINVAL, "n_active is NULL");
+    int n = 0;
+    for (int i = 0; i < n_bf; ++i) {
+        if (pixel_active(optics, bf_coords_host[2 * i], bf_coords_host[2 * i + 1])) {
+            if (idx_out) idx_out[n] = i;
+            ++n;
+        }
+    }
+    *n_active = n;
+    return DSP_OK;
+}
+
+dsp_status dsp_band_count(const dsp_scan *scan, const double *band_invA, int *count) {
+    dsp_status st;
+    if ((st = check_scan(scan))) return st;
+    if (!count) return fail(DSP_EINVAL, "count is NULL");
+    const int N = scan->n_scan;
+    const double dq = 1.0 / (N * scan->step_A);
+    int c = 0;
+    for (int iy = 0; iy < N; ++iy) {
+        const int yh = iy < N / 2 ? iy : iy - N;
+        for (int ix = 0; ix <= N / 2; ++ix) {
+            const double f = std::hypot((double)yh * dq, (double)ix * dq);
+            if (!band_invA || (f >= band_invA[0] && f <= band_invA[1])) ++c;
+        }
+    }
+    *count = c;
+    return DSP_OK;
+}
+
+dsp_status dsp_chi_host(const dsp_optics *optics, const double *k_host, int n, double *chi_out) {
+    dsp_status st;
+    if ((st = check_optics(optics))) return st;
+    if (n < 0 || (n > 0 && (!k_host || !chi_out))) return fail(DSP_EINVAL, "bad arguments");
+    double c[CHI_NCOEF];
+    chi_coefficients(optics, c);
+    for (int i = 0; i < n; ++i) {
+        const double ty = optics->wavelength_A * k_host[2 * i] + optics->tilt_rad[0];
+        const double tx = optics->wavelength_A * k_host[2 * i + 1] + optics->tilt_rad[1];
+        chi_out[i] = chi_poly(c, tx, ty);
+    }
+    return DSP_OK;
+}
+
+dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
+                       const dsp_scan *scan, const dsp_optics *optics, const dsp_prepare_opts *opts, void *hip_stream,
+                       dsp_handle **out) {
+    const double t0 = now_ms();
+    dsp_status st;
+    if (!out) return fail(DSP_EINVAL, "out is NULL");
+    *out = nullptr;
+    if ((st = check_scan(scan)) || (st = check_optics(optics))) return st;
+    if (!opts) return fail(DSP_EINVAL, "opts is NULL");
+    if ((st = check_upsampling(opts->upsampling))) return st;
+    if (opts->method != DSP_PHASE && opts->method != DSP_COMPLEX) return fail(DSP_EINVAL, "unknown method %d", (int)opts->method);
+    if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
+    if (n_bf <= 0 || !bf_coords_host) return fail(DSP_EINVAL, "n_bf must be > 0 with bf_coords");
+    if (!std::isfinite(opts->smoothness_invA)) return fail(DSP_EINVAL, "smoothness not finite");
+    hipStream_t stream = (hipStream_t)hip_stream;
+
+    std::unique_ptr<dsp_handle> h(new dsp_handle());
+    h->method = opts->method;
+    h->n_bf = n_bf;
+    h->timing = (opts->flags & DSP_FLAG_TIMING) != 0;
+    if ((st = build_geometry(scan, optics, opts->upsampling, h->geo))) return st;
+    Geometry &g = h->geo;
+    const int max_nj = h->method == DSP_PHASE ? MAX_NJ_PHASE : MAX_NJ_COMPLEX;
+    const int max_a = h->method == DSP_PHASE ? MAX_A_PHASE : MAX_A_SOLVE_COMPLEX;
+    if (g.a_max > max_a) return fail(DSP_EALIAS, "alias count %d above the compiled maximum %d", g.a_max, max_a);
+    if ((st = build_gram_tiles(g, max_nj, h->tg))) return st;
+    if ((st = build_active(bf_coords_host, weights_host, n_bf, optics, g.N, h->act))) return st;
+    if (h->act.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
+    h->scale = h->act.scale;
+    HIP_TRY(hipGetDevice(&h->device));
+    h->n_comp = h->method == DSP_PHASE ? 1 : 2;
+    const int am = std::max(1, g.a_max);
+    h->D = h->n_comp * am + 1;
+
+    // prior per (frequency, alias)
+    std::vector<double> prior((size_t)g.n_q * am, 1.0);
+    const double sp = opts->smoothness_invA;
+    for (int i = 0; i < g.n_q; ++i)
+        for (int m = 0; m < g.count[i]; ++m) {
+            if (sp > 0.0) {
+                const double qy = (double)g.K[((size_t)i * am + m) * 2] * g.dq;
+                const double qx = (double)g.K[((size_t)i * am + m) * 2 + 1] * g.dq;
+                const double q2 = qy * qy + qx * qx;
+                const double b = 1.0 + q2 / (sp * sp);
+                prior[(size_t)i * am + m] = b * b;
+            }
+        }
+    // frequency lists by alias count
+    std::vector<int32_t> bucket;
+    h->bucket_off.assign(10, 0);
+    h->bucket_n.assign(10, 0);
+    for (int A = 0; A <= 9; ++A) {
+        h->bucket_off[A] = (int)bucket.size();
+        for (int i = 0; i < g.n_q; ++i)
+            if (g.count[i] == A) bucket.push_back(i);
+        h->bucket_n[A] = (int)bucket.size() - h->bucket_off[A];
+    }
+
+    // device buffers
+    const size_t n_sys = (size_t)g.n_q * tri_size(h->D);
+    if ((st = dev_alloc(&h->d_pix, h->act.pix.size())) || (st = dev_alloc(&h->d_tiles, h->tg.tiles.size())) ||
+        (st = dev_alloc(&h->d_sys, n_sys)) || (st = dev_alloc(&h->d_prior, prior.size())) ||
+        (st = dev_alloc(&h->d_count, g.count.size())) || (st = dev_alloc(&h->d_K, g.K.size())) ||
+        (st = dev_alloc(&h->d_bucket, bucket.size())))
+        return st;
+    if (h->method == DSP_PHASE) {
+        if ((st = dev_alloc(&h->d_lam, (size_t)g.n_q * am)) || (st = dev_alloc(&h->d_U, (size_t)g.n_q * am * am)) ||
+            (st = dev_alloc(&h->d_c, (size_t)g.n_q * am)))
+            return st;
+    }
+    HIP_TRY(hipMemcpyAsync(h->d_pix, h->act.pix.data(), h->act.pix.size() * sizeof(PixelRec), hipMemcpyHostToDevice, stream));
+    HIP_TRY(hipMemcpyAsync(h->d_tiles, h->tg.tiles.data(), h->tg.tiles.size() * sizeof(GramTile), hipMemcpyHostToDevice, stream));
+    HIP_TRY(hipMemcpyAsync(h->d_prior, prior.data(), prior.size() * sizeof(double), hipMemcpyHostToDevice, stream));
+    HIP_TRY(hipMemcpyAsync(h->d_count, g.count.data(), g.count.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream));
+    if (!g.K.empty())
+        HIP_TRY(hipMemcpyAsync(h->d_K, g.K.data(), g.K.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream));
+    if (!bucket.empty())
+        HIP_TRY(hipMemcpyAsync(h->d_bucket, bucket.data(), bucket.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream));
+
+    if (h->timing) {
+        for (auto &e : h->ev) HIP_TRY(hipEventCreate(&e));
+        HIP_TRY(hipEventRecord(h->ev[0], stream));
+    }
+    const ApertureDev apd = make_aperture_dev(optics);
+    const OpticsDev opd = make_optics_dev(optics);
+    HIP_TRY(launch_pixel_terms(h->d_pix, (int)h->act.pix.size(), apd, opd, nullptr, stream));
+    if (h->timing) HIP_TRY(hipEventRecord(h->ev[1], stream));
+
+    GramParams gp;
+    std::memset(&gp, 0, sizeof gp);
+    gp.G = (const float2 *)G_c64_dev;
+    gp.pix = h->d_pix;
+    gp.n_pix = (int)h->act.pix.size();
+    gp.N = g.N;
+    gp.nh = g.N / 2 + 1;
+    gp.dq = g.dq;
+    gp.ap = apd;
+    gp.op = opd;
+    gp.sys = h->d_sys;
+    gp.a_max = am;
+    gp.D = h->D;
+    // largest groups first
+    std::vector<int> order(h->tg.group_nj.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return h->tg.group_n[a] > h->tg.group_n[b]; });
+    for (int gi : order) {
+        gp.tiles = h->d_tiles + h->tg.group_off[gi];
+        HIP_TRY(launch_gram(gp, h->tg.group_nj[gi], h->method, h->tg.group_n[gi], stream));
+    }
+    if (h->timing) HIP_TRY(hipEventRecord(h->ev[2], stream));
+
+    if (h->method == DSP_PHASE) {
+        EigParams ep;
+        ep.sys = h->d_sys;
+        ep.D = h->D;
+        ep.a_max = am;
+        ep.prior = h->d_prior;
+        ep.lam = h->d_lam;
+        ep.U = h->d_U;
+        ep.c = h->d_c;
+        // frequencies without aliases keep zero eigen data
+        if (h->bucket_n[0] > 0) {
+            HIP_TRY(launch_fill_zero(h->d_lam, (size_t)g.n_q * am, stream));
+            HIP_TRY(launch_fill_zero((double *)h->d_U, (size_t)g.n_q * am * am * 2, stream));
+            HIP_TRY(launch_fill_zero((double *)h->d_c, (size_t)g.n_q * am * 2, stream));
+        }
+        for (int A = 1; A <= 9; ++A) {
+            if (h->bucket_n[A] == 0) continue;
+            ep.qlist = h->d_bucket + h->bucket_off[A];
+            ep.n = h->bucket_n[A];
+            HIP_TRY(launch_eig(ep, A, stream));
+        }
+    }
+    if (h->timing) HIP_TRY(hipEventRecord(h->ev[3], stream));
+    h->host_ms = now_ms() - t0;
+    *out = h.release();
+    return DSP_OK;
+}
+
+dsp_status dsp_solve(dsp_handle *h, const double *strengths_host, int S, void *x_out_c128_dev, double *resid_out_dev,
+                     void *hip_stream) {
+    if (!h) return fail(DSP_EINVAL, "handle is NULL");
+    if (S <= 0 || !strengths_host || !x_out_c128_dev) return fail(DSP_EINVAL, "need S > 0, strengths and x_out");
+    const int per = h->method == DSP_PHASE ? 1 : 2;
+    for (int i = 0; i < S * per; ++i)
+        if (!(strengths_host[i] >= 0.0) || !std::isfinite(strengths_host[i]))
+            return fail(DSP_EINVAL, "strength %d must be finite and >= 0", i);
+    HIP_TRY(hipSetDevice(h->device));
+    hipStream_t stream = (hipStream_t)hip_stream;
+    const Geometry &g = h->geo;
+    const int am = std::max(1, g.a_max);
+    const int chunk = h->method == DSP_PHASE ? 64 : 32;
+    double2 *x = (double2 *)x_out_c128_dev;
+    for (int s0 = 0; s0 < S; s0 += chunk) {
+        const int sn = std::min(chunk, S - s0);
+        SolveParams sp;
+        std::memset(&sp, 0, sizeof sp);
+        sp.sys = h->d_sys;
+        sp.D = h->D;
+        sp.a_max = am;
+        sp.n_q = g.n_q;
+        sp.prior = h->d_prior;
+        sp.lam = h->d_lam;
+        sp.U = h->d_U;
+        sp.c = h->d_c;
+        for (int i = 0; i < sn * per; ++i) sp.strengths[i] = strengths_host[s0 * per + i];
+        sp.S = sn;
+        sp.scale = h->scale;
+        sp.x = x + (size_t)s0 * h->n_comp * g.n_q * am;
+        sp.resid = resid_out_dev ? resid_out_dev + (size_t)s0 * g.n_q : nullptr;
+        for (int A = 0; A <= 9; ++A) {
+            if (h->bucket_n[A] == 0) continue;
+            sp.qlist = h->d_bucket + h->bucket_off[A];
+            sp.n = h->bucket_n[A];
+            HIP_TRY(launch_solve(sp, A, h->method, stream));
+        }
+    }
+    return DSP_OK;
+}
+
+dsp_status dsp_scatter(const dsp_handle *h, const void *x_packed_c128_dev, int S, void *spec_out_c128_dev,
+                       void *hip_stream) {
+    if (!h) return fail(DSP_EINVAL, "handle is NULL");
+    if (S <= 0 || !x_packed_c128_dev || !spec_out_c128_dev) return fail(DSP_EINVAL, "need S > 0, x and spec_out");
+    HIP_TRY(hipSetDevice(h->device));
+    hipStream_t stream = (hipStream_t)hip_stream;
+    const Geometry &g = h->geo;
+    const int nf = g.u * g.N;
+    const size_t plane = (size_t)nf * (nf / 2 + 1);
+    HIP_TRY(launch_fill_zero((double *)spec_out_c128_dev, (size_t)S * h->n_comp * plane * 2, stream));
+    ScatterParams p;
+    p.x = (const double2 *)x_packed_c128_dev;
+    p.SC = S * h->n_comp;
+    p.n_q = g.n_q;
+    p.a_max = std::max(1, g.a_max);
+    p.count = h->d_count;
+    p.K = h->d_K;
+    p.nf = nf;
+    p.spec = (double2 *)spec_out_c128_dev;
+    HIP_TRY(launch_scatter(p, stream));
+    return DSP_OK;
+}
+
+dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out) {
+    if (!h || !out) return fail(DSP_EINVAL, "NULL argument");
+    std::memset(out, 0, sizeof *out);
+    const Geometry &g = h->geo;
+    out->n_q = g.n_q;
+    out->a_max = g.a_max;
+    out->n_comp = h->n_comp;
+    out->dim = h->D;
+    out->n_bf = h->n_bf;
+    out->n_active_bf = (int)h->act.pix.size();
+    out->method = h->method;
+    out->upsampling = g.u;
+    out->n_scan = g.N;
+    out->n_tiles = (int)h->tg.tiles.size();
+    for (int i = 0; i < 10; ++i) out->alias_hist[i] = g.hist[i];
+    out->scale = h->scale;
+    out->g_bytes = (double)g.n_q * (double)h->act.pix.size() * 8.0;
+    out->host_ms = h->host_ms;
+    if (h->timing && h->ev[3]) {
+        HIP_TRY(hipSetDevice(h->device));
+        HIP_TRY(hipEventSynchronize(h->ev[3]));
+        float ms;
+        HIP_TRY(hipEventElapsedTime(&ms, h->ev[0], h->ev[1]));
+        out->stage_ms[0] = ms;
+        HIP_TRY(hipEventElapsedTime(&ms, h->ev[1], h->ev[2]));
+        out->stage_ms[1] = ms;
+        HIP_TRY(hipEventElapsedTime(&ms, h->ev[2], h->ev[3]));
+        out->stage_ms[2] = ms;
+        HIP_TRY(hipEventElapsedTime(&ms, h->ev[0], h->ev[3]));
+        out->stage_ms[3] = ms;
+    }
+    return DSP_OK;
+}
+
+dsp_status dsp_export_system(const dsp_handle *h, void *aug_out_c128_dev, double *eig_out_dev, void *hip_stream) {
+    if (!h) return fail(DSP_EINVAL, "handle is NULL");
+    HIP_TRY(hipSetDevice(h->device));
+    hipStream_t stream = (hipStream_t)hip_stream;
+    const Geometry &g = h->geo;
+    if (aug_out_c128_dev) HIP_TRY(launch_export(h->d_sys, g.n_q, h->D, (double2 *)aug_out_c128_dev, stream));
+    if (eig_out_dev) {
+        if (h->method != DSP_PHASE) return fail(DSP_EINVAL, "eigenvalues exist for the phase method only");
+        HIP_TRY(hipMemcpyAsync(eig_out_dev, h->d_lam, (size_t)g.n_q * std::max(1, g.a_max) * sizeof(double),
+                               hipMemcpyDeviceToDevice, stream));
+    }
+    return DSP_OK;
+}
+
+dsp_status dsp_alias_table(const dsp_handle *h, int32_t *q_host, int32_t *count_host, int32_t *K_host) {
+    if (!h) return fail(DSP_EINVAL, "handle is NULL");
+    const Geometry &g = h->geo;
+    if (q_host) std::memcpy(q_host, g.q.data(), g.q.size() * sizeof(int32_t));
+    if (count_host) std::memcpy(count_host, g.count.data(), g.count.size() * sizeof(int32_t));
+    if (K_host && g.a_max > 0) std::memcpy(K_host, g.K.data(), g.K.size() * sizeof(int32_t));
+    return DSP_OK;
+}
+
+dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
+                   const dsp_scan *scan, const dsp_optics *sets_host, int B, const double *band_invA,
+                   void *S_out_c128_dev, double *norm_out_dev, double *agreement_out_host, void *hip_stream) {
+    dsp_status st;
+    if ((st = check_scan(scan))) return st;
+    if (!sets_host || B < 1 || B > MAX_SETS) return fail(DSP_EINVAL, "need 1 <= B <= %d optics sets", MAX_SETS);
+    for (int b = 0; b < B; ++b)
+        if ((st = check_optics(sets_host + b))) return st;
+    for (int b = 1; b < B; ++b) {
+        const dsp_optics &a = sets_host[0], &c = sets_host[b];
+        if (a.wavelength_A != c.wavelength_A || a.semiangle_rad != c.semiangle_rad ||
+            a.det_step_invA != c.det_step_invA || a.soft_aperture != c.soft_aperture)
+            return fail(DSP_EINVAL, "set %d: aperture parameters differ from set 0", b);
+    }
+    if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
+    if (n_bf <= 0 || !bf_coords_host) return fail(DSP_EINVAL, "n_bf must be > 0 with bf_coords");
+    if (band_invA && !(band_invA[0] <= band_invA[1])) return fail(DSP_EINVAL, "band must satisfy lo <= hi");
+    hipStream_t stream = (hipStream_t)hip_stream;
+    const int N = scan->n_scan, nh = N / 2 + 1;
+    const double dq = 1.0 / (N * scan->step_A);
+
+    ActiveSet as;
+    if ((st = build_active(bf_coords_host, weights_host, n_bf, sets_host, N, as))) return st;
+    if (as.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
+    // tiles over every stored entry, lanes inside the band
+    std::vector<SsbTile> tiles;
+    for (int yh0 = -N / 2; yh0 <= N / 2 - 1; yh0 += TILE_Y) {
+        for (int ix0 = 0; ix0 <= N / 2; ix0 += TILE_X) {
+            SsbTile t;
+            std::memset(&t, 0, sizeof t);
+            t.yh0 = yh0;
+            t.ix0 = ix0;
+            for (int l = 0; l < 64; ++l) {
+                const int yh = yh0 + l / TILE_X, ix = ix0 + l % TILE_X;
+                if (yh > N / 2 - 1 || ix > N / 2) continue;
+                const double f = std::hypot((double)yh * dq, (double)ix * dq);
+                if (band_invA && !(f >= band_invA[0] && f <= band_invA[1])) continue;
+                t.valid |= 1ull << l;
+            }
+            if (t.valid) tiles.push_back(t);
+        }
+    }
+    const int n_tiles = (int)tiles.size();
+    const int n_pix = (int)as.pix.size();
+    const int stride = ssb_partial_stride(B);
+
+    PixelRec *d_pix = nullptr;
+    SsbTile *d_tiles = nullptr;
+    double *d_chi = nullptr, *d_part = nullptr, *d_E = nullptr;
+    HIP_TRY(hipMallocAsync((void **)&d_pix, sizeof(PixelRec) * n_pix, stream));
+    HIP_TRY(hipMallocAsync((void **)&d_tiles, sizeof(SsbTile) * std::max(1, n_tiles), stream));
+    HIP_TRY(hipMallocAsync((void **)&d_chi, sizeof(double) * (size_t)B * n_pix, stream));
+    HIP_TRY(hipMallocAsync((void **)&d_part, sizeof(double) * (size_t)std::max(1, n_tiles) * stride, stream));
+    HIP_TRY(hipMallocAsync((void **)&d_E, sizeof(double) * (B + 1), stream));
+    HIP_TRY(hipMemcpyAsync(d_pix, as.pix.data(), sizeof(PixelRec) * n_pix, hipMemcpyHostToDevice, stream));
+    if (n_tiles)
+        HIP_TRY(hipMemcpyAsync(d_tiles, tiles.data(), sizeof(SsbTile) * n_tiles, hipMemcpyHostToDevice, stream));
+
+    const ApertureDev apd = make_aperture_dev(sets_host);
+    SsbParams sp;
+    std::memset(&sp, 0, sizeof sp);
+    for (int b = 0; b < B; ++b) {
+        const OpticsDev od = make_optics_dev(sets_host + b);
+        // a(k) once (set 0 writes it), chi(k) per set
+        if (b == 0) HIP_TRY(launch_pixel_terms(d_pix, n_pix, apd, od, nullptr, stream));
+        HIP_TRY(launch_pixel_terms(d_pix, n_pix, apd, od, d_chi + (size_t)b * n_pix, stream));
+        sp.tau_y[b] = od.tau_y;
+        sp.tau_x[b] = od.tau_x;
+        std::memcpy(sp.chi_c[b], od.chi_c, sizeof od.chi_c);
+    }
+    const size_t plane = (size_t)N * nh;
+    if (S_out_c128_dev && band_invA) HIP_TRY(launch_fill_zero((double *)S_out_c128_dev, (size_t)B * plane * 2, stream));
+    if (norm_out_dev && band_invA) HIP_TRY(launch_fill_zero(norm_out_dev, (size_t)B * plane, stream));
+    sp.G = (const float2 *)G_c64_dev;
+    sp.pix = d_pix;
+    sp.chi_tab = d_chi;
+    sp.n_pix = n_pix;
+    sp.tiles = d_tiles;
+    sp.N = N;
+    sp.nh = nh;
+    sp.dq = dq;
+    sp.B = B;
+    sp.ap = apd;
+    sp.lam = sets_host[0].wavelength_A;
+    sp.S_out = (double2 *)S_out_c128_dev;
+    sp.N_out = norm_out_dev;
+    sp.partial = d_part;
+    HIP_TRY(launch_ssb(sp, n_tiles, stream));
+    std::vector<double> E(B + 1, 0.0);
+    if (agreement_out_host) {
+        if (n_tiles) {
+            HIP_TRY(launch_agreement(d_part, n_tiles, B, d_E, stream));
+            HIP_TRY(hipMemcpyAsync(E.data(), d_E, sizeof(double) * (B + 1), hipMemcpyDeviceToHost, stream));
+        }
+    }
+    HIP_TRY(hipFreeAsync(d_pix, stream));
+    HIP_TRY(hipFreeAsync(d_tiles, stream));
+    HIP_TRY(hipFreeAsync(d_chi, stream));
+    HIP_TRY(hipFreeAsync(d_part, stream));
+    HIP_TRY(hipFreeAsync(d_E, stream));
+    if (agreement_out_host) {
+        HIP_TRY(hipStreamSynchronize(stream));
+        for (int b = 0; b < B; ++b) agreement_out_host[b] = n_tiles ? E[b] : 0.0;
+    }
+    return DSP_OK;
+}
+
+}  // extern "C"

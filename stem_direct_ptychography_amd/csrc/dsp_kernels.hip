@@ -1,0 +1,971 @@
+// HIP kernels of libdsp for CDNA4 (gfx950, wave64).
+//
+// Regularized direct (single-side-band) ptychography, per scan frequency q:
+// transfer T(q, k, alias) evaluated in registers, weighted augmented Gram
+// [T g]^H W [T g] reduced over bright-field pixels in FP64, eigenbasis or
+// solve per q, and the SSB sum over pixels ("Where the 9 s of regularized
+// preparation goes", section "Code path"; "Preparation in one kernel per
+// alias count", section "What changed"; "Tilt-corrected SSB on CUDA",
+// section "Changes").
+//
+// Lane mapping of the streaming kernels: a wave owns a 4 x 16 tile of scan
+// frequencies (one per lane) and walks the bright-field pixels in lockstep.
+// Per-pixel data (k, weight, a(k), chi(k), plane offset) is wave-uniform and
+// comes through scalar loads; each lane reads its G(q, k) from a 128-byte
+// run of 16 consecutive stored columns; the lens-overlap zero-skip branches
+// almost never diverge because neighbouring frequencies see nearly the same
+// lens; each lane keeps its own frequency's sums, so there is no cross-lane
+// reduction.  A workgroup of P waves splits the pixels round-robin and adds
+// its waves' sums through LDS in a fixed order (deterministic).
+#include "dsp_internal.hpp"
+#include "dsp_kernels.hpp"
+
+namespace dsp {
+
+// ---------------------------------------------------------------------------
+// shared device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ bool inside_support(const ApertureDev &ap, double d2) {
+    return ap.soft ? (d2 < ap.rout2) : (d2 <= ap.rout2);
+}
+
+// a(k') for a point already known to be inside the support.
+__device__ __forceinline__ double lobe_aperture(const ApertureDev &ap, double d2) {
+    if (!ap.soft || d2 <= ap.rin2) return 1.0;
+    return fma(ap.kc - sqrt(d2), ap.inv_dk, 0.5);
+}
+
+__device__ __forceinline__ double aperture_at(const ApertureDev &ap, double d2) {
+    if (!inside_support(ap, d2)) return 0.0;
+    return lobe_aperture(ap, d2);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
+
+// ---------------------------------------------------------------------------
+// pixel terms: a(k) and chi(k) once per pixel and optics set
+// ---------------------------------------------------------------------------
+
+__global__ void pixel_terms_kernel(PixelRec *pix, int n_pix, ApertureDev ap, OpticsDev op, double *chi_tab) {
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n_pix) return;
+    const double ky = pix[p].ky, kx = pix[p].kx;
+    const double d2 = fma(ky, ky, kx * kx);
+    const double c = chi_poly(op.chi_c, fma(op.lam, kx, op.tau_x), fma(op.lam, ky, op.tau_y));
+    if (chi_tab) {
+        chi_tab[p] = c;
+    } else {
+        pix[p].a0 = aperture_at(ap, d2);
+        pix[p].chi0 = c;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// transfer + weighted augmented Gram
+// ---------------------------------------------------------------------------
+// METHOD 0 (phase): columns T_phi(slot 0..NJ-1), then g.
+// METHOD 1 (complex): columns L(slot 0..NJ-1), R(slot 0..NJ-1), then g; the
+// write-out turns them into [T_A, T_phi] (T_A = L + R, T_phi = i (L - R)),
+// which keeps the per-pixel update to the lobes actually present.
+template <int NJ, int METHOD>
+struct GramShape {
+    static constexpr int NC = METHOD == 0 ? NJ : 2 * NJ;
+    static constexpr int D = NC + 1;
+    static constexpr int NOFF = D * (D - 1) / 2;
+    static constexpr int NACC = D + 2 * NOFF;
+    // strict upper index of (c, d), c < d
+    static constexpr int off(int c, int d) { return c * (2 * D - c - 1) / 2 + (d - c - 1); }
+    static constexpr int re(int c, int d) { return D + 2 * off(c, d); }
+    static constexpr int im(int c, int d) { return D + 2 * off(c, d) + 1; }
+};
+
+template <int NJ, int METHOD>
+__device__ __forceinline__ void acc_get(const double *acc, int c, int d, double &xr, double &xi) {
+    using Sh = GramShape<NJ, METHOD>;
+    // <col c, col d> for any order (compile-time indices after unrolling)
+    if (c == d) {
+        xr = acc[c];
+        xi = 0.0;
+    } else if (c < d) {
+        xr = acc[Sh::re(c, d)];
+        xi = acc[Sh::im(c, d)];
+    } else {
+        xr = acc[Sh::re(d, c)];
+        xi = -acc[Sh::im(d, c)];
+    }
+}
+
+template <int NJ, int METHOD, int P>
+__global__ __launch_bounds__(64 * P) void gram_kernel(GramParams prm) {
+    using Sh = GramShape<NJ, METHOD>;
+    constexpr int NC = Sh::NC;
+    constexpr int D = Sh::D;
+    constexpr int NACC = Sh::NACC;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const GramTile *tile = prm.tiles + blockIdx.x;
+    const int yh = tile->yh0 + (lane >> 4);
+    const int ix = tile->ix0 + (lane & 15);
+    const int qi = tile->qidx[lane];
+    const bool valid = qi >= 0;
+    const unsigned mask = valid ? (unsigned)tile->mask[lane] : 0u;
+    const int iy = yh < 0 ? yh + prm.N : yh;
+    const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
+
+    double Qy[NJ], Qx[NJ];
+    bool act[NJ];
+#pragma unroll
+    for (int s = 0; s < NJ; ++s) {
+        Qy[s] = (double)(yh + (int)tile->jy[s] * prm.N) * prm.dq;
+        Qx[s] = (double)(ix + (int)tile->jx[s] * prm.N) * prm.dq;
+        act[s] = (mask >> s) & 1u;
+    }
+
+    double acc[NACC];
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
+
+    const ApertureDev ap = prm.ap;
+    const double lam = prm.op.lam, tau_y = prm.op.tau_y, tau_x = prm.op.tau_x;
+
+    for (int p = wave; p < prm.n_pix; p += P) {
+        const PixelRec *pr = prm.pix + p;
+        const double ky = pr->ky, kx = pr->kx, w = pr->w, a0 = pr->a0, chi0 = pr->chi0;
+        float2 gv = make_float2(0.f, 0.f);
+        if (valid) gv = prm.G[pr->goff + lane_off];
+        const double gr = (double)gv.x, gi = (double)gv.y;
+
+        double tr[NC], ti[NC];
+        bool nz[NC];
+#pragma unroll
+        for (int s = 0; s < NJ; ++s) {
+            const double dy = ky - Qy[s], dx = kx - Qx[s];
+            const double ey = ky + Qy[s], ex = kx + Qx[s];
+            const double dm2 = fma(dy, dy, dx * dx);
+            const double dp2 = fma(ey, ey, ex * ex);
+            const bool zl = act[s] && inside_support(ap, dm2);
+            const bool zr = act[s] && inside_support(ap, dp2);
+            double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
+            if (zl) {
+                const double amp = a0 * lobe_aperture(ap, dm2);
+                const double cm = chi_poly(prm.op.chi_c, fma(lam, dx, tau_x), fma(lam, dy, tau_y));
+                double sn, cs;
+                sincos(chi0 - cm, &sn, &cs);
+                Lr = amp * cs;
+                Li = amp * sn;
+            }
+            if (zr) {
+                const double amp = a0 * lobe_aperture(ap, dp2);
+                const double cp = chi_poly(prm.op.chi_c, fma(lam, ex, tau_x), fma(lam, ey, tau_y));
+                double sn, cs;
+                sincos(cp - chi0, &sn, &cs);
+                Rr = amp * cs;
+                Ri = amp * sn;
+            }
+            if (METHOD == 0) {
+                tr[s] = Ri - Li;   // T_phi = i (L - R)
+                ti[s] = Lr - Rr;
+                nz[s] = zl || zr;
+            } else {
+                tr[s] = Lr;
+                ti[s] = Li;
+                nz[s] = zl;
+                tr[NJ + s] = Rr;
+                ti[NJ + s] = Ri;
+                nz[NJ + s] = zr;
+            }
+        }
+
+        bool any[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) any[c] = wave_any(nz[c]);
+
+        const double gwr = w * gr, gwi = w * gi;
+        acc[NC] = fma(gr, gwr, fma(gi, gwi, acc[NC]));   // signal power
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (!any[c]) continue;
+            const double twr = w * tr[c], twi = w * ti[c];
+            acc[c] = fma(tr[c], twr, fma(ti[c], twi, acc[c]));
+            // right side <col c, g>
+            acc[Sh::re(c, NC)] = fma(tr[c], gwr, fma(ti[c], gwi, acc[Sh::re(c, NC)]));
+            acc[Sh::im(c, NC)] = fma(tr[c], gwi, fma(-ti[c], gwr, acc[Sh::im(c, NC)]));
+#pragma unroll
+            for (int d = c + 1; d < NC; ++d) {
+                if (!any[d]) continue;
+                const double uwr = w * tr[d], uwi = w * ti[d];
+                acc[Sh::re(c, d)] = fma(tr[c], uwr, fma(ti[c], uwi, acc[Sh::re(c, d)]));
+                acc[Sh::im(c, d)] = fma(tr[c], uwi, fma(-ti[c], uwr, acc[Sh::im(c, d)]));
+            }
+        }
+    }
+
+    // ---- add the P waves' sums in a fixed order through LDS ----
+    if (P > 1) {
+        extern __shared__ double lds[];
+        for (int wv = 1; wv < P; ++wv) {
+            if (wave == wv) {
+#pragma unroll
+                for (int i = 0; i < NACC; ++i) lds[i * 64 + lane] = acc[i];
+            }
+            __syncthreads();
+            if (wave == 0) {
+#pragma unroll
+                for (int i = 0; i < NACC; ++i) acc[i] += lds[i * 64 + lane];
+            }
+            __syncthreads();
+        }
+    }
+    if (wave != 0 || !valid) return;
+
+    // ---- write the frequency's system in slot coordinates ----
+    const int Dout = prm.D;
+    const int am = prm.a_max;
+    double2 *out = prm.sys + (size_t)qi * (size_t)tri_size(Dout);
+    for (int e = 0; e < tri_size(Dout); ++e) out[e] = make_double2(0.0, 0.0);
+    int rank[NJ];
+#pragma unroll
+    for (int s = 0; s < NJ; ++s) rank[s] = __popc(mask & ((1u << s) - 1u));
+    const int gcol = Dout - 1;
+    out[tri_idx(gcol, gcol, Dout)] = make_double2(acc[NC], 0.0);
+
+    if (METHOD == 0) {
+#pragma unroll
+        for (int s = 0; s < NJ; ++s) {
+            if (!act[s]) continue;
+            const int i = rank[s];
+            out[tri_idx(i, i, Dout)] = make_double2(acc[s], 0.0);
+            out[tri_idx(i, gcol, Dout)] = make_double2(acc[Sh::re(s, NC)], acc[Sh::im(s, NC)]);
+#pragma unroll
+            for (int t = s + 1; t < NJ; ++t) {
+                if (!act[t]) continue;
+                out[tri_idx(i, rank[t], Dout)] = make_double2(acc[Sh::re(s, t)], acc[Sh::im(s, t)]);
+            }
+        }
+    } else {
+        // <L_s|L_t>, <L_s|R_t>, <R_s|L_t>, <R_s|R_t> -> [T_A, T_phi] blocks
+#pragma unroll
+        for (int s = 0; s < NJ; ++s) {
+            if (!act[s]) continue;
+            const int i = rank[s];
+            double lgr, lgi, rgr, rgi;
+            acc_get<NJ, METHOD>(acc, s, NC, lgr, lgi);
+            acc_get<NJ, METHOD>(acc, NJ + s, NC, rgr, rgi);
+            // <T_A s, g> = Lg + Rg;  <T_phi s, g> = -i (Lg - Rg)
+            out[tri_idx(i, gcol, Dout)] = make_double2(lgr + rgr, lgi + rgi);
+            out[tri_idx(am + i, gcol, Dout)] = make_double2(lgi - rgi, -(lgr - rgr));
+#pragma unroll
+            for (int t = 0; t < NJ; ++t) {
+                if (!act[t]) continue;
+                const int j = rank[t];
+                double llr, lli, lrr, lri, rlr, rli, rrr, rri;
+                acc_get<NJ, METHOD>(acc, s, t, llr, lli);
+                acc_get<NJ, METHOD>(acc, s, NJ + t, lrr, lri);
+                acc_get<NJ, METHOD>(acc, NJ + s, t, rlr, rli);
+                acc_get<NJ, METHOD>(acc, NJ + s, NJ + t, rrr, rri);
+                // <T_A s, T_phi t> = i (LL - LR + RL - RR): all (s, t)
+                {
+                    const double zr = llr - lrr + rlr - rrr, zi = lli - lri + rli - rri;
+                    out[tri_idx(i, am + j, Dout)] = make_double2(-zi, zr);
+                }
+                if (t >= s) {
+                    // <T_A s, T_A t> = LL + LR + RL + RR
+                    const double ar = llr + lrr + rlr + rrr, ai = lli + lri + rli + rri;
+                    // <T_phi s, T_phi t> = LL - LR - RL + RR
+                    const double pr = llr - lrr - rlr + rrr, pi = lli - lri - rli + rri;
+                    out[tri_idx(i, j, Dout)] = make_double2(ar, t == s ? 0.0 : ai);
+                    out[tri_idx(am + i, am + j, Dout)] = make_double2(pr, t == s ? 0.0 : pi);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// phase eigenbasis: cyclic complex Jacobi, one lane per frequency
+// ---------------------------------------------------------------------------
+
+template <int A>
+__global__ __launch_bounds__(64) void eig_kernel(EigParams prm) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= prm.n) return;
+    const int q = prm.qlist[t];
+    const int D = prm.D;
+    const double2 *S = prm.sys + (size_t)q * (size_t)tri_size(D);
+    double sc[A];
+#pragma unroll
+    for (int i = 0; i < A; ++i) sc[i] = 1.0 / sqrt(prm.prior[(size_t)q * prm.a_max + i]);
+    // upper triangle of C = D^-1/2 M D^-1/2
+    double hr[A][A], hi[A][A], vr[A][A], vi[A][A];
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+#pragma unroll
+        for (int j = 0; j < A; ++j) {
+            vr[i][j] = (i == j) ? 1.0 : 0.0;
+            vi[i][j] = 0.0;
+            hr[i][j] = 0.0;
+            hi[i][j] = 0.0;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+#pragma unroll
+        for (int j = i; j < A; ++j) {
+            const double2 e = S[tri_idx(i, j, D)];
+            hr[i][j] = e.x * sc[i] * sc[j];
+            hi[i][j] = (i == j) ? 0.0 : e.y * sc[i] * sc[j];
+        }
+    }
+    for (int sweep = 0; sweep < 16; ++sweep) {
+        double off = 0.0, dia = 0.0;
+#pragma unroll
+        for (int i = 0; i < A; ++i) {
+            dia += hr[i][i] * hr[i][i];
+#pragma unroll
+            for (int j = i + 1; j < A; ++j) off += hr[i][j] * hr[i][j] + hi[i][j] * hi[i][j];
+        }
+        const bool done = off <= 1e-34 * dia;
+        if (__all(done)) break;
+#pragma unroll
+        for (int p = 0; p < A; ++p) {
+#pragma unroll
+            for (int qq = p + 1; qq < A; ++qq) {
+                const double br = hr[p][qq], bi = hi[p][qq];
+                const double bn = sqrt(br * br + bi * bi);
+                const bool rot = bn > 0.0;
+                const double er = rot ? br / bn : 1.0, ei = rot ? bi / bn : 0.0;   // e^{i phi}
+                const double a = hr[p][p], d = hr[qq][qq];
+                const double zeta = rot ? (d - a) / (2.0 * bn) : 0.0;
+                double tt = 1.0 / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+                tt = zeta < 0.0 ? -tt : tt;
+                tt = rot ? tt : 0.0;
+                const double c = 1.0 / sqrt(1.0 + tt * tt), s = tt * c;
+                // J = [[c, s], [-s e^{-i phi}, c e^{-i phi}]] on columns (p, qq)
+                hr[p][p] = a - tt * bn;
+                hr[qq][qq] = d + tt * bn;
+                hr[p][qq] = 0.0;
+                hi[p][qq] = 0.0;
+#pragma unroll
+                for (int r = 0; r < A; ++r) {
+                    if (r == p || r == qq) continue;
+                    // H[r][p], H[r][qq] from upper storage
+                    double xpr, xpi, xqr, xqi;
+                    if (r < p) { xpr = hr[r][p]; xpi = hi[r][p]; } else { xpr = hr[p][r]; xpi = -hi[p][r]; }
+                    if (r < qq) { xqr = hr[r][qq]; xqi = hi[r][qq]; } else { xqr = hr[qq][r]; xqi = -hi[qq][r]; }
+                    // e^{-i phi} H[r][qq]
+                    const double yr = er * xqr + ei * xqi, yi = er * xqi - ei * xqr;
+                    const double npr = c * xpr - s * yr, npi = c * xpi - s * yi;
+                    const double nqr = s * xpr + c * yr, nqi = s * xpi + c * yi;
+                    if (r < p) { hr[r][p] = npr; hi[r][p] = npi; } else { hr[p][r] = npr; hi[p][r] = -npi; }
+                    if (r < qq) { hr[r][qq] = nqr; hi[r][qq] = nqi; } else { hr[qq][r] = nqr; hi[qq][r] = -nqi; }
+                }
+#pragma unroll
+                for (int r = 0; r < A; ++r) {
+                    const double xpr = vr[r][p], xpi = vi[r][p], xqr = vr[r][qq], xqi = vi[r][qq];
+                    const double yr = er * xqr + ei * xqi, yi = er * xqi - ei * xqr;
+                    vr[r][p] = c * xpr - s * yr;
+                    vi[r][p] = c * xpi - s * yi;
+                    vr[r][qq] = s * xpr + c * yr;
+                    vi[r][qq] = s * xpi + c * yi;
+                }
+            }
+        }
+    }
+    // ascending order: odd-even transposition sort of (lambda, column)
+    double lam[A];
+#pragma unroll
+    for (int i = 0; i < A; ++i) lam[i] = hr[i][i];
+#pragma unroll
+    for (int pass = 0; pass < A; ++pass) {
+#pragma unroll
+        for (int i = pass & 1; i + 1 < A; i += 2) {
+            const bool sw = lam[i] > lam[i + 1];
+            const double l0 = lam[i], l1 = lam[i + 1];
+            lam[i] = sw ? l1 : l0;
+            lam[i + 1] = sw ? l0 : l1;
+#pragma unroll
+            for (int r = 0; r < A; ++r) {
+                const double a0 = vr[r][i], a1 = vr[r][i + 1], b0 = vi[r][i], b1 = vi[r][i + 1];
+                vr[r][i] = sw ? a1 : a0;
+                vr[r][i + 1] = sw ? a0 : a1;
+                vi[r][i] = sw ? b1 : b0;
+                vi[r][i + 1] = sw ? b0 : b1;
+            }
+        }
+    }
+    // U = D^-1/2 V, c = V^H D^-1/2 r
+    const int am = prm.a_max;
+    double rr[A], ri[A];
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+        const double2 e = S[tri_idx(i, D - 1, D)];
+        rr[i] = e.x * sc[i];
+        ri[i] = e.y * sc[i];
+    }
+    double *lo = prm.lam + (size_t)q * am;
+    double2 *Uo = prm.U + (size_t)q * am * am;
+    double2 *co = prm.c + (size_t)q * am;
+    for (int j = 0; j < am; ++j) {
+        lo[j] = 0.0;
+        co[j] = make_double2(0.0, 0.0);
+    }
+    for (int e = 0; e < am * am; ++e) Uo[e] = make_double2(0.0, 0.0);
+#pragma unroll
+    for (int j = 0; j < A; ++j) {
+        lo[j] = lam[j];
+        double cr = 0.0, ci = 0.0;
+#pragma unroll
+        for (int r = 0; r < A; ++r) {
+            // conj(V_rj) * (r_r / sqrt p_r)
+            cr = fma(vr[r][j], rr[r], fma(vi[r][j], ri[r], cr));
+            ci = fma(vr[r][j], ri[r], fma(-vi[r][j], rr[r], ci));
+            Uo[r * am + j] = make_double2(vr[r][j] * sc[r], vi[r][j] * sc[r]);
+        }
+        co[j] = make_double2(cr, ci);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// solves
+// ---------------------------------------------------------------------------
+
+template <int A>
+__global__ __launch_bounds__(64) void solve_phase_kernel(SolveParams prm) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= prm.n) return;
+    const int q = prm.qlist[t];
+    const int am = prm.a_max;
+    double lam[A], cr[A], ci[A], ur[A][A], ui[A][A];
+#pragma unroll
+    for (int j = 0; j < A; ++j) {
+        lam[j] = prm.lam[(size_t)q * am + j];
+        const double2 c = prm.c[(size_t)q * am + j];
+        cr[j] = c.x;
+        ci[j] = c.y;
+#pragma unroll
+        for (int r = 0; r < A; ++r) {
+            const double2 u = prm.U[((size_t)q * am + r) * am + j];
+            ur[r][j] = u.x;
+            ui[r][j] = u.y;
+        }
+    }
+    const double P = prm.sys[(size_t)q * tri_size(prm.D) + tri_idx(prm.D - 1, prm.D - 1, prm.D)].x;
+    for (int s = 0; s < prm.S; ++s) {
+        const double mu = prm.strengths[s] * prm.scale;
+        double yr[A], yi[A];
+        double xr_dot = 0.0, quad = 0.0;
+#pragma unroll
+        for (int j = 0; j < A; ++j) {
+            const double inv = 1.0 / (lam[j] + mu);
+            yr[j] = cr[j] * inv;
+            yi[j] = ci[j] * inv;
+            xr_dot += yr[j] * cr[j] + yi[j] * ci[j];
+            quad += lam[j] * (yr[j] * yr[j] + yi[j] * yi[j]);
+        }
+        double2 *xo = prm.x + ((size_t)s * prm.n_q + q) * am;
+#pragma unroll
+        for (int r = 0; r < A; ++r) {
+            double xr = 0.0, xi = 0.0;
+#pragma unroll
+            for (int j = 0; j < A; ++j) {
+                xr = fma(ur[r][j], yr[j], fma(-ui[r][j], yi[j], xr));
+                xi = fma(ur[r][j], yi[j], fma(ui[r][j], yr[j], xi));
+            }
+            xo[r] = make_double2(xr, xi);
+        }
+        for (int r = A; r < am; ++r) xo[r] = make_double2(0.0, 0.0);
+        if (prm.resid) prm.resid[(size_t)s * prm.n_q + q] = P - 2.0 * xr_dot + quad;
+    }
+}
+
+// frequencies without aliases: nothing to solve, x = 0, misfit = P
+__global__ __launch_bounds__(64) void solve_empty_kernel(SolveParams prm, int n_comp) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= prm.n) return;
+    const int q = prm.qlist[t];
+    const double P = prm.sys[(size_t)q * tri_size(prm.D) + tri_idx(prm.D - 1, prm.D - 1, prm.D)].x;
+    for (int s = 0; s < prm.S; ++s) {
+        for (int c = 0; c < n_comp; ++c) {
+            double2 *xo = prm.x + ((size_t)(s * n_comp + c) * prm.n_q + q) * prm.a_max;
+            for (int m = 0; m < prm.a_max; ++m) xo[m] = make_double2(0.0, 0.0);
+        }
+        if (prm.resid) prm.resid[(size_t)s * prm.n_q + q] = P;
+    }
+}
+
+// complex method: Cholesky of M + scale diag(lambda_A p, lambda_phi p), d = 2A
+template <int A>
+__global__ __launch_bounds__(64) void solve_complex_kernel(SolveParams prm) {
+    constexpr int d = 2 * A;
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= prm.n) return;
+    const int q = prm.qlist[t];
+    const int am = prm.a_max;
+    const int D = prm.D;
+    const double2 *S = prm.sys + (size_t)q * (size_t)tri_size(D);
+    int slot[d];
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+        slot[i] = i;
+        slot[A + i] = am + i;
+    }
+    double pr[d];
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+        pr[i] = prm.prior[(size_t)q * am + i];
+        pr[A + i] = pr[i];
+    }
+    double rr[d], ri[d];
+#pragma unroll
+    for (int i = 0; i < d; ++i) {
+        const double2 e = S[tri_idx(slot[i], D - 1, D)];
+        rr[i] = e.x;
+        ri[i] = e.y;
+    }
+    const double P = S[tri_idx(D - 1, D - 1, D)].x;
+    for (int s = 0; s < prm.S; ++s) {
+        const double la = prm.strengths[2 * s] * prm.scale, lp = prm.strengths[2 * s + 1] * prm.scale;
+        // lower triangle L (row i, col j <= i) of the Cholesky factor
+        double lr[d][d], li[d][d];
+#pragma unroll
+        for (int j = 0; j < d; ++j) {
+            // H_jj - sum_k |L_jk|^2
+            double hjj = S[tri_idx(slot[j], slot[j], D)].x + (j < A ? la : lp) * pr[j];
+#pragma unroll
+            for (int k = 0; k < j; ++k) hjj -= lr[j][k] * lr[j][k] + li[j][k] * li[j][k];
+            const double ljj = sqrt(hjj);
+            const double inv = 1.0 / ljj;
+            lr[j][j] = ljj;
+            li[j][j] = 0.0;
+#pragma unroll
+            for (int i = j + 1; i < d; ++i) {
+                // H_ij (i > j) = conj(M[slot j][slot i])
+                const double2 e = S[tri_idx(slot[j], slot[i], D)];
+                double zr = e.x, zi = -e.y;
+#pragma unroll
+                for (int k = 0; k < j; ++k) {
+                    // L_ik conj(L_jk)
+                    zr -= lr[i][k] * lr[j][k] + li[i][k] * li[j][k];
+                    zi -= li[i][k] * lr[j][k] - lr[i][k] * li[j][k];
+                }
+                lr[i][j] = zr * inv;
+                li[i][j] = zi * inv;
+            }
+        }
+        // forward L z = r, backward L^H x = z
+        double zr[d], zi[d];
+#pragma unroll
+        for (int i = 0; i < d; ++i) {
+            double ar = rr[i], ai = ri[i];
+#pragma unroll
+            for (int k = 0; k < i; ++k) {
+                ar -= lr[i][k] * zr[k] - li[i][k] * zi[k];
+                ai -= lr[i][k] * zi[k] + li[i][k] * zr[k];
+            }
+            zr[i] = ar / lr[i][i];
+            zi[i] = ai / lr[i][i];
+        }
+        double xr[d], xi[d];
+#pragma unroll
+        for (int i = d - 1; i >= 0; --i) {
+            double ar = zr[i], ai = zi[i];
+#pragma unroll
+            for (int k = i + 1; k < d; ++k) {
+                // conj(L_ki) x_k
+                ar -= lr[k][i] * xr[k] + li[k][i] * xi[k];
+                ai -= lr[k][i] * xi[k] - li[k][i] * xr[k];
+            }
+            xr[i] = ar / lr[i][i];
+            xi[i] = ai / lr[i][i];
+        }
+        double2 *xo = prm.x + ((size_t)(2 * s) * prm.n_q + q) * am;
+        double2 *xo2 = prm.x + ((size_t)(2 * s + 1) * prm.n_q + q) * am;
+#pragma unroll
+        for (int i = 0; i < A; ++i) {
+            xo[i] = make_double2(xr[i], xi[i]);
+            xo2[i] = make_double2(xr[A + i], xi[A + i]);
+        }
+        for (int i = A; i < am; ++i) {
+            xo[i] = make_double2(0.0, 0.0);
+            xo2[i] = make_double2(0.0, 0.0);
+        }
+        if (prm.resid) {
+            // P - 2 Re(x^H r) + x^H M x
+            double xr_dot = 0.0, quad = 0.0;
+#pragma unroll
+            for (int i = 0; i < d; ++i) {
+                xr_dot += xr[i] * rr[i] + xi[i] * ri[i];
+                double mr = 0.0, mi = 0.0;
+#pragma unroll
+                for (int j = 0; j < d; ++j) {
+                    double er, ei;
+                    if (i <= j) {
+                        const double2 e = S[tri_idx(slot[i], slot[j], D)];
+                        er = e.x;
+                        ei = i == j ? 0.0 : e.y;
+                    } else {
+                        const double2 e = S[tri_idx(slot[j], slot[i], D)];
+                        er = e.x;
+                        ei = -e.y;
+                    }
+                    mr += er * xr[j] - ei * xi[j];
+                    mi += er * xi[j] + ei * xr[j];
+                }
+                quad += xr[i] * mr + xi[i] * mi;
+            }
+            prm.resid[(size_t)s * prm.n_q + q] = P - 2.0 * xr_dot + quad;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fill, scatter, export
+// ---------------------------------------------------------------------------
+
+__global__ void fill_zero_kernel(double *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0.0;
+}
+
+__global__ void scatter_kernel(ScatterParams prm) {
+    // one thread per (strength x component, frequency)
+    const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)prm.SC * prm.n_q;
+    if (t >= total) return;
+    const int sc = (int)(t / prm.n_q);
+    const int q = (int)(t % prm.n_q);
+    const int A = prm.count[q];
+    const int nf = prm.nf, nfh = nf / 2 + 1;
+    for (int m = 0; m < A; ++m) {
+        const int ky = prm.K[((size_t)q * prm.a_max + m) * 2];
+        const int kx = prm.K[((size_t)q * prm.a_max + m) * 2 + 1];
+        const double2 v = prm.x[((size_t)sc * prm.n_q + q) * prm.a_max + m];
+        size_t o;
+        double2 val;
+        if (kx > 0 || (kx == 0 && ky >= 0)) {
+            o = (size_t)((ky % nf + nf) % nf) * nfh + kx;
+            val = v;
+        } else {
+            o = (size_t)(((-ky) % nf + nf) % nf) * nfh + (-kx);
+            val = make_double2(v.x, -v.y);
+        }
+        prm.spec[(size_t)sc * nf * nfh + o] = val;
+    }
+}
+
+__global__ void export_kernel(const double2 *sys, int n_q, int D, double2 *dense) {
+    const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t total = (size_t)n_q * D * D;
+    if (t >= total) return;
+    const int q = (int)(t / ((size_t)D * D));
+    const int ij = (int)(t % ((size_t)D * D));
+    const int i = ij / D, j = ij % D;
+    const double2 *S = sys + (size_t)q * tri_size(D);
+    double2 v;
+    if (i <= j) {
+        v = S[tri_idx(i, j, D)];
+    } else {
+        const double2 e = S[tri_idx(j, i, D)];
+        v = make_double2(e.x, -e.y);
+    }
+    dense[t] = v;
+}
+
+// ---------------------------------------------------------------------------
+// SSB / agreement pass
+// ---------------------------------------------------------------------------
+
+template <int MAXB, int P>
+__global__ __launch_bounds__(64 * P) void ssb_kernel(SsbParams prm) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const SsbTile *tile = prm.tiles + blockIdx.x;
+    const int yh = tile->yh0 + (lane >> 4);
+    const int ix = tile->ix0 + (lane & 15);
+    const bool valid = (tile->valid >> lane) & 1ull;
+    const int iy = yh < 0 ? yh + prm.N : yh;
+    const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
+    const double qy = (double)yh * prm.dq, qx = (double)ix * prm.dq;
+    const int B = prm.B;
+    const ApertureDev ap = prm.ap;
+    const double lam = prm.lam;
+
+    double sr[MAXB], si[MAXB], nn[MAXB];
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b) sr[b] = si[b] = nn[b] = 0.0;
+    double pw = 0.0;
+
+    for (int p = wave; p < prm.n_pix; p += P) {
+        const PixelRec *pr = prm.pix + p;
+        const double ky = pr->ky, kx = pr->kx, w = pr->w, a0 = pr->a0;
+        float2 gv = make_float2(0.f, 0.f);
+        if (valid) gv = prm.G[pr->goff + lane_off];
+        const double gr = (double)gv.x, gi = (double)gv.y;
+        const double gwr = w * gr, gwi = w * gi;
+        pw = fma(gr, gwr, fma(gi, gwi, pw));
+        const double dy = ky - qy, dx = kx - qx, ey = ky + qy, ex = kx + qx;
+        const double dm2 = fma(dy, dy, dx * dx), dp2 = fma(ey, ey, ex * ex);
+        const bool zl = valid && inside_support(ap, dm2);
+        const bool zr = valid && inside_support(ap, dp2);
+        const double aml = zl ? a0 * lobe_aperture(ap, dm2) : 0.0;
+        const double amr = zr ? a0 * lobe_aperture(ap, dp2) : 0.0;
+#pragma unroll
+        for (int b = 0; b < MAXB; ++b) {
+            if (b >= B) break;
+            const double chi0 = prm.chi_tab[(size_t)b * prm.n_pix + p];
+            double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
+            if (zl) {
+                const double cm = chi_poly(prm.chi_c[b], fma(lam, dx, prm.tau_x[b]), fma(lam, dy, prm.tau_y[b]));
+                double sn, cs;
+                sincos(chi0 - cm, &sn, &cs);
+                Lr = aml * cs;
+                Li = aml * sn;
+            }
+            if (zr) {
+                const double cp = chi_poly(prm.chi_c[b], fma(lam, ex, prm.tau_x[b]), fma(lam, ey, prm.tau_y[b]));
+                double sn, cs;
+                sincos(cp - chi0, &sn, &cs);
+                Rr = amr * cs;
+                Ri = amr * sn;
+            }
+            // Gamma = i (L - R); S += w conj(Gamma) g; N += w |Gamma|^2
+            const double gmr = Ri - Li, gmi = Lr - Rr;
+            sr[b] = fma(gmr, gwr, fma(gmi, gwi, sr[b]));
+            si[b] = fma(gmr, gwi, fma(-gmi, gwr, si[b]));
+            nn[b] = fma(w * gmr, gmr, fma(w * gmi, gmi, nn[b]));
+        }
+    }
+
+    constexpr int NACC = 3 * MAXB + 1;
+    __shared__ double lds[NACC * 64];
+    if (P > 1) {
+        for (int wv = 1; wv < P; ++wv) {
+            if (wave == wv) {
+#pragma unroll
+                for (int b = 0; b < MAXB; ++b) {
+                    lds[(3 * b) * 64 + lane] = sr[b];
+                    lds[(3 * b + 1) * 64 + lane] = si[b];
+                    lds[(3 * b + 2) * 64 + lane] = nn[b];
+                }
+                lds[(3 * MAXB) * 64 + lane] = pw;
+            }
+            __syncthreads();
+            if (wave == 0) {
+#pragma unroll
+                for (int b = 0; b < MAXB; ++b) {
+                    sr[b] += lds[(3 * b) * 64 + lane];
+                    si[b] += lds[(3 * b + 1) * 64 + lane];
+                    nn[b] += lds[(3 * b + 2) * 64 + lane];
+                }
+                pw += lds[(3 * MAXB) * 64 + lane];
+            }
+            __syncthreads();
+        }
+    }
+    if (wave != 0) return;
+
+    // outputs and per-tile agreement partials (fixed-order lane tree)
+    const size_t plane = (size_t)prm.N * prm.nh;
+    double part[MAXB + 1];
+#pragma unroll
+    for (int b = 0; b < MAXB; ++b) {
+        const bool ok = valid && b < B;
+        if (ok && prm.S_out) prm.S_out[(size_t)b * plane + lane_off] = make_double2(sr[b], si[b]);
+        if (ok && prm.N_out) prm.N_out[(size_t)b * plane + lane_off] = nn[b];
+        part[b] = (ok && nn[b] > 0.0) ? (sr[b] * sr[b] + si[b] * si[b]) / nn[b] : 0.0;
+    }
+    part[MAXB] = valid ? pw : 0.0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+#pragma unroll
+        for (int b = 0; b <= MAXB; ++b) part[b] += __shfl_xor(part[b], off);
+    }
+    if (lane == 0) {
+        double *po = prm.partial + (size_t)blockIdx.x * (MAXB + 1);
+#pragma unroll
+        for (int b = 0; b <= MAXB; ++b) po[b] = part[b];
+    }
+}
+
+__global__ void agreement_kernel(const double *partial, int n_tiles, int stride, int B, double *E) {
+    // one block of 64 threads; thread t sums tiles t, t+64, ... then a fixed tree
+    __shared__ double sh[64];
+    const int t = threadIdx.x;
+    for (int b = 0; b <= B; ++b) {
+        const int col = (b == B) ? stride - 1 : b;
+        double s = 0.0;
+        for (int i = t; i < n_tiles; i += 64) s += partial[(size_t)i * stride + col];
+        sh[t] = s;
+        __syncthreads();
+        for (int h = 32; h >= 1; h >>= 1) {
+            if (t < h) sh[t] += sh[t + h];
+            __syncthreads();
+        }
+        if (t == 0) E[b] = sh[0];
+        __syncthreads();
+    }
+    if (t == 0) {
+        const double den = E[B];
+        for (int b = 0; b < B; ++b) E[b] = E[b] / den;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+#define DSP_CHECK_LAUNCH() \
+    do { hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; } while (0)
+
+hipError_t launch_pixel_terms(PixelRec *pix, int n_pix, const ApertureDev &ap, const OpticsDev &op, double *chi_tab,
+                              hipStream_t st) {
+    if (n_pix <= 0) return hipSuccess;
+    pixel_terms_kernel<<<(n_pix + 255) / 256, 256, 0, st>>>(pix, n_pix, ap, op, chi_tab);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+template <int NJ, int METHOD, int P>
+static hipError_t launch_gram_t(const GramParams &prm, int n_tiles, hipStream_t st) {
+    constexpr size_t lds = P > 1 ? sizeof(double) * 64 * GramShape<NJ, METHOD>::NACC : 0;
+    gram_kernel<NJ, METHOD, P><<<n_tiles, 64 * P, lds, st>>>(prm);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+int gram_waves_per_tile(int nj, int method) {
+    if (method == 0) return nj <= 5 ? 4 : 2;
+    return nj <= 4 ? 2 : 1;
+}
+
+hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_tiles, hipStream_t st) {
+    if (n_tiles <= 0) return hipSuccess;
+    if (method == 0) {
+        switch (nj) {
+            case 1: return launch_gram_t<1, 0, 4>(prm, n_tiles, st);
+            case 2: return launch_gram_t<2, 0, 4>(prm, n_tiles, st);
+            case 3: return launch_gram_t<3, 0, 4>(prm, n_tiles, st);
+            case 4: return launch_gram_t<4, 0, 4>(prm, n_tiles, st);
+            case 5: return launch_gram_t<5, 0, 4>(prm, n_tiles, st);
+            case 6: return launch_gram_t<6, 0, 2>(prm, n_tiles, st);
+            case 7: return launch_gram_t<7, 0, 2>(prm, n_tiles, st);
+            case 8: return launch_gram_t<8, 0, 2>(prm, n_tiles, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (nj) {
+        case 1: return launch_gram_t<1, 1, 2>(prm, n_tiles, st);
+        case 2: return launch_gram_t<2, 1, 2>(prm, n_tiles, st);
+        case 3: return launch_gram_t<3, 1, 2>(prm, n_tiles, st);
+        case 4: return launch_gram_t<4, 1, 2>(prm, n_tiles, st);
+        case 5: return launch_gram_t<5, 1, 1>(prm, n_tiles, st);
+        case 6: return launch_gram_t<6, 1, 1>(prm, n_tiles, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_eig(const EigParams &prm, int A, hipStream_t st) {
+    if (prm.n <= 0) return hipSuccess;
+    const int blocks = (prm.n + 63) / 64;
+    switch (A) {
+        case 1: eig_kernel<1><<<blocks, 64, 0, st>>>(prm); break;
+        case 2: eig_kernel<2><<<blocks, 64, 0, st>>>(prm); break;
+        case 3: eig_kernel<3><<<blocks, 64, 0, st>>>(prm); break;
+        case 4: eig_kernel<4><<<blocks, 64, 0, st>>>(prm); break;
+        case 5: eig_kernel<5><<<blocks, 64, 0, st>>>(prm); break;
+        case 6: eig_kernel<6><<<blocks, 64, 0, st>>>(prm); break;
+        case 7: eig_kernel<7><<<blocks, 64, 0, st>>>(prm); break;
+        case 8: eig_kernel<8><<<blocks, 64, 0, st>>>(prm); break;
+        default: return hipErrorInvalidValue;
+    }
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_solve(const SolveParams &prm, int A, int method, hipStream_t st) {
+    if (prm.n <= 0) return hipSuccess;
+    const int blocks = (prm.n + 63) / 64;
+    if (A == 0) {
+        solve_empty_kernel<<<blocks, 64, 0, st>>>(prm, method == 0 ? 1 : 2);
+        DSP_CHECK_LAUNCH();
+        return hipSuccess;
+    }
+    if (method == 0) {
+        switch (A) {
+            case 1: solve_phase_kernel<1><<<blocks, 64, 0, st>>>(prm); break;
+            case 2: solve_phase_kernel<2><<<blocks, 64, 0, st>>>(prm); break;
+            case 3: solve_phase_kernel<3><<<blocks, 64, 0, st>>>(prm); break;
+            case 4: solve_phase_kernel<4><<<blocks, 64, 0, st>>>(prm); break;
+            case 5: solve_phase_kernel<5><<<blocks, 64, 0, st>>>(prm); break;
+            case 6: solve_phase_kernel<6><<<blocks, 64, 0, st>>>(prm); break;
+            case 7: solve_phase_kernel<7><<<blocks, 64, 0, st>>>(prm); break;
+            case 8: solve_phase_kernel<8><<<blocks, 64, 0, st>>>(prm); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (A) {
+            case 1: solve_complex_kernel<1><<<blocks, 64, 0, st>>>(prm); break;
+            case 2: solve_complex_kernel<2><<<blocks, 64, 0, st>>>(prm); break;
+            case 3: solve_complex_kernel<3><<<blocks, 64, 0, st>>>(prm); break;
+            case 4: solve_complex_kernel<4><<<blocks, 64, 0, st>>>(prm); break;
+            case 5: solve_complex_kernel<5><<<blocks, 64, 0, st>>>(prm); break;
+            case 6: solve_complex_kernel<6><<<blocks, 64, 0, st>>>(prm); break;
+            default: return hipErrorInvalidValue;
+        }
+    }
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_fill_zero(double *p, size_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    fill_zero_kernel<<<(unsigned)blocks, 256, 0, st>>>(p, n);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_scatter(const ScatterParams &prm, hipStream_t st) {
+    const size_t total = (size_t)prm.SC * prm.n_q;
+    if (total == 0) return hipSuccess;
+    scatter_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(prm);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_export(const double2 *sys, int n_q, int D, double2 *dense, hipStream_t st) {
+    const size_t total = (size_t)n_q * D * D;
+    if (total == 0) return hipSuccess;
+    export_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(sys, n_q, D, dense);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_ssb(const SsbParams &prm, int n_tiles, hipStream_t st) {
+    if (n_tiles <= 0) return hipSuccess;
+    constexpr int P = 4;
+    if (prm.B <= 1) ssb_kernel<1, P><<<n_tiles, 64 * P, 0, st>>>(prm);
+    else if (prm.B <= 2) ssb_kernel<2, P><<<n_tiles, 64 * P, 0, st>>>(prm);
+    else if (prm.B <= 4) ssb_kernel<4, P><<<n_tiles, 64 * P, 0, st>>>(prm);
+    else ssb_kernel<8, P><<<n_tiles, 64 * P, 0, st>>>(prm);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+int ssb_partial_stride(int B) {
+    if (B <= 1) return 2;
+    if (B <= 2) return 3;
+    if (B <= 4) return 5;
+    return 9;
+}
+
+hipError_t launch_agreement(const double *partial, int n_tiles, int B, double *E, hipStream_t st) {
+    agreement_kernel<<<1, 64, 0, st>>>(partial, n_tiles, ssb_partial_stride(B), B, E);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+}  // namespace dsp

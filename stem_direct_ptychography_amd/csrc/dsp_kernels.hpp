@@ -1,0 +1,63 @@
+// Kernel parameter blocks and launchers of libdsp (internal).
+#pragma once
+
+#include "dsp_internal.hpp"
+
+namespace dsp {
+
+struct EigParams {
+    const double2 *sys;   // packed systems [n_q][tri_size(D)]
+    int D, a_max;
+    const int32_t *qlist; // frequencies with this alias count
+    int n;
+    const double *prior;  // [n_q][a_max]
+    double *lam;          // [n_q][a_max]
+    double2 *U;           // [n_q][a_max][a_max]
+    double2 *c;           // [n_q][a_max]
+};
+
+struct SolveParams {
+    const double2 *sys;
+    int D, a_max, n_q;
+    const int32_t *qlist;
+    int n;
+    const double *prior;
+    const double *lam;
+    const double2 *U;
+    const double2 *c;
+    double strengths[64];     // by value: phase [S] (S <= 64), complex [S][2] (S <= 32)
+    int S;
+    double scale;
+    double2 *x;               // [S][n_comp][n_q][a_max]
+    double *resid;            // [S][n_q] or null
+};
+
+struct ScatterParams {
+    const double2 *x;         // [SC][n_q][a_max]
+    int SC, n_q, a_max;
+    const int32_t *count;     // [n_q]
+    const int32_t *K;         // [n_q][a_max][2]
+    int nf;                   // u N
+    double2 *spec;            // [SC][nf][nf/2+1]
+};
+
+hipError_t launch_pixel_terms(PixelRec *pix, int n_pix, const ApertureDev &ap, const OpticsDev &op, double *chi_tab,
+                              hipStream_t st);
+int gram_waves_per_tile(int nj, int method);
+hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_tiles, hipStream_t st);
+hipError_t launch_eig(const EigParams &prm, int A, hipStream_t st);
+hipError_t launch_solve(const SolveParams &prm, int A, int method, hipStream_t st);
+hipError_t launch_fill_zero(double *p, size_t n, hipStream_t st);
+hipError_t launch_scatter(const ScatterParams &prm, hipStream_t st);
+hipError_t launch_export(const double2 *sys, int n_q, int D, double2 *dense, hipStream_t st);
+hipError_t launch_ssb(const SsbParams &prm, int n_tiles, hipStream_t st);
+int ssb_partial_stride(int B);
+hipError_t launch_agreement(const double *partial, int n_tiles, int B, double *E, hipStream_t st);
+
+constexpr int MAX_NJ_PHASE = 8;
+constexpr int MAX_NJ_COMPLEX = 6;
+constexpr int MAX_A_SOLVE_COMPLEX = 6;
+constexpr int MAX_A_PHASE = 8;
+constexpr int MAX_SETS = 8;
+
+}  // namespace dsp

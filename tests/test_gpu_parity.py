@@ -1,0 +1,417 @@
+"""GPU parity: libdsp's HIP path against the CPU oracle, element by element.
+
+Tolerances (from the arithmetic: FP64 transfer and sums, complex64 G read
+exactly, summation order differs): augmented Gram / right side / power per
+frequency max|delta| / max|entry| <= 1e-9; eigenvalues <= 1e-9 of the largest;
+solutions and SSB sums <= 1e-5 globally (||delta|| / ||ref||) and per frequency
+(max|delta| / max(max|x_q|, 1e-3 global max)); agreement <= 1e-6 relative;
+index sets bit-exact; repeated runs bitwise equal.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import dsp_oracle as O
+from synthetic import (LAMBDA_300KV, Optics, bf_pixels, data_stack_numpy, data_stack_torch, random_weights,
+                       ssb_sets, workload)
+
+torch = pytest.importorskip("torch")
+dsp = pytest.importorskip("stem_direct_ptychography_amd")
+
+pytestmark = pytest.mark.gpu
+
+GRAM_TOL = 1e-9
+X_TOL = 1e-5
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+
+
+def slot_index(method, A, a_max):
+    """Compact unknown order of the oracle -> slot index of the export."""
+    if method == "phase":
+        return list(range(A))
+    return list(range(A)) + [a_max + m for m in range(A)]
+
+
+def oracle_aug(M, r, P):
+    d = M.shape[0]
+    out = np.zeros((d + 1, d + 1), dtype=np.complex128)
+    out[:d, :d] = M
+    out[:d, d] = r
+    out[d, :d] = np.conj(r)
+    out[d, d] = P
+    return out
+
+
+def compare_systems(aug_gpu, prep_o, sel, method, a_max):
+    """aug_gpu: (n_q, D, D) numpy; prep_o: oracle Prepared over frequencies sel."""
+    D = aug_gpu.shape[1]
+    worst = 0.0
+    for i, qi in enumerate(sel):
+        A = int(prep_o.A[i])
+        sl = slot_index(method, A, a_max) + [D - 1]
+        want = oracle_aug(prep_o.M[i], prep_o.r[i], prep_o.P[i])
+        got = aug_gpu[qi][np.ix_(sl, sl)]
+        scale = np.abs(want).max()
+        err = np.abs(got - want).max() / scale if scale > 0 else np.abs(got).max()
+        worst = max(worst, err)
+        # everything outside the frequency's slots is exactly zero
+        mask = np.ones((D, D), dtype=bool)
+        mask[np.ix_(sl, sl)] = False
+        assert not np.any(aug_gpu[qi][mask]), f"q {qi}: non-zero outside its slots"
+    assert worst <= GRAM_TOL, f"augmented system rel err {worst:.3e}"
+    return worst
+
+
+def compare_solutions(x_gpu, xs_o, prep_o, sel, method, a_max, comp):
+    """x_gpu: (n_comp, n_q, a_max) numpy for one strength; xs_o: oracle list."""
+    got_all, want_all = [], []
+    for i, qi in enumerate(sel):
+        A = int(prep_o.A[i])
+        if method == "phase":
+            got = x_gpu[0, qi, :A]
+        else:
+            got = np.concatenate([x_gpu[0, qi, :A], x_gpu[1, qi, :A]])
+        assert not np.any(x_gpu[:, qi, A:]), "padding slots must be zero"
+        got_all.append(got)
+        want_all.append(xs_o[i])
+    g = np.concatenate(got_all)
+    w = np.concatenate(want_all)
+    glob = np.linalg.norm(g - w) / np.linalg.norm(w)
+    assert glob <= X_TOL, f"global solution rel err {glob:.3e}"
+    gmax = np.abs(w).max()
+    worst = 0.0
+    for a, b in zip(got_all, want_all):
+        den = max(np.abs(b).max() if b.size else 0.0, 1e-3 * gmax)
+        worst = max(worst, np.abs(a - b).max() / den if b.size else 0.0)
+    assert worst <= X_TOL, f"per-frequency solution rel err {worst:.3e}"
+    return glob, worst
+
+
+def stratified(counts, per_count, rng, extra=()):
+    sel = []
+    for A in np.unique(counts):
+        idx = np.nonzero(counts == A)[0]
+        take = min(len(idx), per_count)
+        sel.extend(rng.choice(idx, size=take, replace=False).tolist())
+    sel.extend(extra)
+    return np.unique(np.asarray(sel, dtype=np.int64))
+
+
+def run_prepare_case(w, G_dev, k, wts, method, strengths, sel=None, per_count=None, seed=0):
+    """Prepare + export + solve on the GPU and check the frequencies ``sel``
+    (all when None) against the oracle."""
+    _say(f"prepare {w.name} method={method} N={w.n_scan} u={w.upsampling} n_bf={len(k)}")
+    prep = dsp.prepare(G_dev, k, w.optics, step=w.step, upsampling=w.upsampling, method=method, weights=wts,
+                       smoothness=w.smoothness)
+    inf = prep.info
+    a_max = inf["a_max"]
+    # alias table bit-exact
+    q_o, c_o, K_o = O.alias_table(w.n_scan, w.step, w.upsampling, w.optics)
+    q_g, c_g, K_g = prep.alias_table()
+    assert np.array_equal(q_g, q_o) and np.array_equal(c_g, c_o)
+    act = O.active_pixels(k, w.optics)
+    assert inf["n_active_bf"] == len(act)
+    aug, eig = prep.export_system()
+    S = len(strengths)
+    x, resid = prep.solve(strengths, residual=True)
+    torch.cuda.synchronize()
+    aug = aug.cpu().numpy()
+    eig = eig.cpu().numpy() if eig is not None else None
+    x = x.cpu().numpy()
+    resid = resid.cpu().numpy()
+    if sel is None:
+        sel = np.arange(len(q_o))
+    elif per_count is not None:
+        sel = stratified(c_o, per_count, np.random.default_rng(seed), extra=sel)
+    _say(f"oracle on {len(sel)} of {len(q_o)} frequencies")
+    wa = np.ones(len(act)) if wts is None else np.asarray(wts)[act]
+    G_sel = G_dev[:, torch.as_tensor(q_o[sel, 0], device=DEV), torch.as_tensor(q_o[sel, 1], device=DEV)]
+    G_sel = G_sel[torch.as_tensor(act, device=DEV)].cpu().numpy().astype(np.complex128)
+    cols = [G_sel[:, i] for i in range(len(sel))]
+    prep_o = O.prepare(q_o[sel], cols, k[act], wa, w.n_scan, w.step, w.upsampling, w.optics, method, w.smoothness)
+    assert inf["scale"] == pytest.approx(prep_o.scale, rel=1e-14)
+    for i, qi in enumerate(sel):
+        assert np.array_equal(K_g[qi, : c_o[qi]], K_o[qi])
+    compare_systems(aug, prep_o, sel, method, a_max)
+    if method == "phase":
+        worst = 0.0
+        for i, qi in enumerate(sel):
+            A = int(prep_o.A[i])
+            lo = prep_o.lam[i]
+            if A == 0:
+                continue
+            worst = max(worst, np.abs(eig[qi, :A] - lo).max() / max(np.abs(lo).max(), 1e-300))
+        assert worst <= GRAM_TOL, f"eigenvalue rel err {worst:.3e}"
+    for s in range(S):
+        st = strengths[s]
+        xs_o = O.solve(prep_o, st)
+        compare_solutions(x[s], xs_o, prep_o, sel, method, a_max, inf["n_comp"])
+        # residual identity against the oracle's definition
+        for i, qi in enumerate(sel[:50]):
+            rho = O.residual(prep_o.M[i], prep_o.r[i], prep_o.P[i], xs_o[i])
+            assert resid[s, qi] == pytest.approx(rho, rel=1e-6, abs=1e-9 * max(1.0, prep_o.P[i]))
+    return prep, x, sel, prep_o
+
+
+# ----------------------------------------------------------------------------
+# small workloads in full
+# ----------------------------------------------------------------------------
+
+
+def test_c1_phase_full_and_scatter():
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    G = data_stack_numpy(w, pix)
+    G_dev = torch.as_tensor(G, device=DEV)
+    prep, x, sel, prep_o = run_prepare_case(w, G_dev, k, None, "phase", list(w.strengths) + [0.1, 3.0])
+    # scatter against the oracle's
+    xt = torch.as_tensor(x, device=DEV)
+    spec = prep.scatter(xt).cpu().numpy()
+    for s, st in enumerate(list(w.strengths) + [0.1, 3.0]):
+        xs_o = O.solve(prep_o, st)
+        want = O.scatter(prep_o.q, prep_o.K, xs_o, w.n_scan, w.upsampling, 1)
+        err = np.linalg.norm(spec[s] - want) / np.linalg.norm(want)
+        assert err <= X_TOL
+        assert np.array_equal(spec[s] != 0, want != 0)
+
+
+def test_c2_complex_sampled():
+    w = workload("c2")
+    pix, k = bf_pixels(w)
+    G = data_stack_numpy(w, pix)
+    G_dev = torch.as_tensor(G, device=DEV)
+    wts = random_weights(len(k), 5)
+    prep, x, sel, prep_o = run_prepare_case(w, G_dev, k, wts, "complex", list(w.strengths),
+                                            sel=[0, 1, 2, 8063], per_count=400, seed=2)
+    spec = prep.scatter(torch.as_tensor(x, device=DEV)).cpu().numpy()
+    assert spec.shape == (8, 2, 256, 129)
+
+
+def test_c2_phase_sampled_weighted():
+    w = workload("c2")
+    pix, k = bf_pixels(w)
+    G = data_stack_numpy(w, pix)
+    G_dev = torch.as_tensor(G, device=DEV)
+    run_prepare_case(w, G_dev, k, random_weights(len(k), 9), "phase", [1e-3, 1e-1], sel=[5, 8000],
+                     per_count=300, seed=3)
+
+
+def _tiny(n=None, u=3, soft=True, step=None, method="phase"):
+    """Ragged tiles (N/2 < 16 stored columns, odd row count), several alias
+    counts (phase up to 7, complex up to 6), 14 aberration terms with tilt."""
+    if n is None:
+        n, step = (12, 0.45) if method == "phase" else (14, 0.4)
+    base = workload("c3")
+    opt = base.optics.replace(det_step=0.09, soft=soft)
+    from synthetic import Workload
+    return Workload("tiny", n, step, 40, opt, u, bf_radius_px=18.0, method=method, strengths=(1e-3, 0.05),
+                    dose=None, lattice_sites=0, smoothness=opt.semiangle / opt.wavelength, seed=77)
+
+
+@pytest.mark.parametrize("method", ["phase", "complex"])
+@pytest.mark.parametrize("soft", [True, False])
+def test_tiny_ragged_full(method, soft):
+    w = _tiny(soft=soft, method=method)
+    pix, k = bf_pixels(w)
+    G = data_stack_numpy(w, pix)
+    strengths = [1e-3, 0.05] if method == "phase" else [(1e-3, 2e-3), (0.05, 0.01)]
+    run_prepare_case(w, torch.as_tensor(G, device=DEV), k, random_weights(len(k), 1), method, strengths)
+
+
+def test_frequencies_without_aliases():
+    """A fine scan step leaves the outer frequencies with no overlapping
+    aperture (alias count 0): zero systems, zero solutions."""
+    from synthetic import Workload
+    opt = Optics(LAMBDA_300KV, 0.03, 0.25, soft=True, aberrations=[(1, 0, -80.0, 0.0)])
+    w = Workload("sparse", 16, 0.12, 24, opt, 1, bf_radius_px=7.0, smoothness=0.0, seed=5)
+    pix, k = bf_pixels(w)
+    q, counts, _ = O.alias_table(w.n_scan, w.step, 1, opt)
+    assert (counts == 0).any() and (counts == 1).any()
+    G = data_stack_numpy(w, pix)
+    prep, x, sel, prep_o = run_prepare_case(w, torch.as_tensor(G, device=DEV), k, None, "phase", [1e-2])
+    aug, eig = prep.export_system()
+    aug = aug.cpu().numpy()
+    for qi in np.nonzero(counts == 0)[0]:
+        assert not np.any(x[:, :, qi, :])
+        assert not np.any(aug[qi, :-1, :])
+
+
+def test_zero_data_and_zero_weights():
+    w = _tiny()
+    pix, k = bf_pixels(w)
+    G = torch.zeros((len(k), w.n_scan, w.n_half), dtype=torch.complex64, device=DEV)
+    wts = np.ones(len(k))
+    wts[::3] = 0.0
+    prep = dsp.prepare(G, k, w.optics, step=w.step, upsampling=w.upsampling, method="phase", weights=wts,
+                       smoothness=w.smoothness)
+    x = prep.solve([1e-2]).cpu().numpy()
+    assert not np.any(x)
+    aug, _ = prep.export_system()
+    aug = aug.cpu().numpy()
+    assert not np.any(aug[:, :, -1]) and not np.any(aug[:, -1, :])
+    assert prep.info["scale"] == pytest.approx(float(np.sum(wts[O.active_pixels(k, w.optics)])))
+
+
+def test_determinism_bitwise():
+    w = _tiny(method="complex")
+    pix, k = bf_pixels(w)
+    G = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    outs = []
+    for _ in range(2):
+        prep = dsp.prepare(G, k, w.optics, step=w.step, upsampling=w.upsampling, method="complex",
+                           smoothness=w.smoothness)
+        aug, _ = prep.export_system()
+        x = prep.solve([(1e-2, 1e-2)])
+        outs.append((aug.cpu().numpy(), x.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+# ----------------------------------------------------------------------------
+# SSB
+# ----------------------------------------------------------------------------
+
+
+def _ssb_case(w, G_dev, k, wts, sets, band, entries=None):
+    _say(f"ssb {w.name} B={len(sets)} band={band} n_bf={len(k)}")
+    S, Nn, E = dsp.ssb(G_dev, k, sets, step=w.step, band=band, weights=wts)
+    torch.cuda.synchronize()
+    S = S.cpu().numpy()
+    Nn = Nn.cpu().numpy()
+    act = O.active_pixels(k, sets[0])
+    wa = np.ones(len(act)) if wts is None else np.asarray(wts)[act]
+    mask = O.band_mask(w.n_scan, w.step, band)
+    all_entries = np.argwhere(mask)
+    if entries is None:
+        entries = all_entries
+    G_sel = G_dev[:, torch.as_tensor(entries[:, 0], device=DEV), torch.as_tensor(entries[:, 1], device=DEV)]
+    G_sel = G_sel[torch.as_tensor(act, device=DEV)].cpu().numpy().astype(np.complex128)
+    cols = [G_sel[:, i] for i in range(len(entries))]
+    S_o, N_o = O.ssb(entries, cols, k[act], wa, w.n_scan, w.step, sets)
+    for b in range(len(sets)):
+        got = S[b, entries[:, 0], entries[:, 1]]
+        glob = np.linalg.norm(got - S_o[b]) / np.linalg.norm(S_o[b])
+        assert glob <= X_TOL, f"set {b}: S rel err {glob:.3e}"
+        den = np.maximum(np.abs(S_o[b]), 1e-3 * np.abs(S_o[b]).max())
+        assert np.max(np.abs(got - S_o[b]) / den) <= X_TOL
+        gn = Nn[b, entries[:, 0], entries[:, 1]]
+        assert np.max(np.abs(gn - N_o[b]) / np.maximum(np.abs(N_o[b]), 1e-3 * N_o[b].max())) <= X_TOL
+    # outside the band: zero
+    assert not np.any(S[:, ~mask]) and not np.any(Nn[:, ~mask])
+    return S, Nn, E, S_o, N_o, cols, wa, entries
+
+
+def test_ssb_c1_full_agreement():
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    sets = [w.optics, w.optics.replace(aberrations=[(1, 0, -90.0, 0.0)]),
+            w.optics.replace(tilt=(1e-3, 2e-3))]
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G_dev, k, None, sets, None)
+    power = np.array([np.sum(wa * np.abs(c) ** 2) for c in cols])
+    E_o = O.agreement(S_o, N_o, power)
+    assert np.allclose(E, E_o, rtol=1e-6, atol=0)
+
+
+def test_ssb_tiny_band_weighted():
+    w = _tiny()
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    wts = random_weights(len(k), 4)
+    sets = [w.optics.replace(soft=True)] + [w.optics.replace(tilt=(0.0, 1e-3 * b)) for b in range(1, 5)]
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G_dev, k, wts, sets, (0.3, 1.5))
+    power = np.array([np.sum(wa * np.abs(c) ** 2) for c in cols])
+    assert np.allclose(E, O.agreement(S_o, N_o, power), rtol=1e-6, atol=0)
+
+
+def test_ssb_equals_prepare_at_u1():
+    """The two paths agree with each other at one alias per frequency,
+    zero strength and no prior: S/N = x."""
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    S, Nn, _ = dsp.ssb(G_dev, k, [w.optics], step=w.step, agreement=False)
+    prep = dsp.prepare(G_dev, k, w.optics, step=w.step, upsampling=1, method="phase", smoothness=0.0)
+    x = prep.solve([0.0]).cpu().numpy()[0, 0, :, 0]
+    q, _, _ = prep.alias_table()
+    s = S.cpu().numpy()[0, q[:, 0], q[:, 1]]
+    n = Nn.cpu().numpy()[0, q[:, 0], q[:, 1]]
+    ok = n > 1e-9 * n.max()
+    assert ok.sum() > 100
+    assert np.max(np.abs(s[ok] / n[ok] - x[ok]) / np.abs(x[ok]).max()) <= X_TOL
+
+
+# ----------------------------------------------------------------------------
+# full-frame workloads on sampled outputs, launch configuration of the bench
+# ----------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def c4_data():
+    w = workload("c4")
+    pix, k = bf_pixels(w)
+    _say("generating full-frame G (9298, 512, 257) on the GPU")
+    G = data_stack_torch(w, pix, DEV)
+    torch.cuda.synchronize()
+    yield w, k, G
+    del G
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("method", ["phase", "complex"])
+def test_c4_full_frame_sampled(c4_data, method):
+    w, k, G = c4_data
+    strengths = [1e-2] if method == "phase" else [(1e-2, 1e-2)]
+    prep, x, sel, prep_o = run_prepare_case(w, G, k, None, method, strengths, sel=[0, 130559], per_count=24,
+                                            seed=4)
+    inf = prep.info
+    assert inf["alias_hist"][3:7] == [3770, 106424, 19304, 1062]
+    assert inf["n_active_bf"] == 9298
+
+
+def test_c4_determinism(c4_data):
+    w, k, G = c4_data
+    a = []
+    for _ in range(2):
+        prep = dsp.prepare(G, k, w.optics, step=w.step, upsampling=3, method="phase", smoothness=w.smoothness)
+        aug, eig = prep.export_system()
+        a.append((aug.cpu().numpy(), eig.cpu().numpy()))
+        del prep
+    assert np.array_equal(a[0][0], a[1][0]) and np.array_equal(a[0][1], a[1][1])
+
+
+def test_c5_ssb_eight_sets_sampled():
+    w = workload("c5")
+    pix, k = bf_pixels(w)
+    _say("generating full-frame G (8807, 512, 257) on the GPU")
+    G = data_stack_torch(w, pix, DEV)
+    sets = ssb_sets(w, 8)
+    mask = O.band_mask(w.n_scan, w.step, w.band)
+    ent = np.argwhere(mask)
+    rng = np.random.default_rng(6)
+    pick = ent[np.sort(rng.choice(len(ent), size=96, replace=False))]
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G, k, None, sets, w.band, entries=pick)
+    # agreement from the kernel's own sums: property at full size
+    Sg, Ng, _ = dsp.ssb(G, k, sets, step=w.step, band=w.band, agreement=False)
+    act = torch.as_tensor(O.active_pixels(k, w.optics), device=DEV)
+    mt = torch.as_tensor(mask, device=DEV)
+    iy, ix = torch.nonzero(mt, as_tuple=True)
+    power = 0.0
+    for s0 in range(0, len(act), 512):
+        gc = G[act[s0:s0 + 512]][:, iy, ix].to(torch.complex128)
+        power += (gc.real ** 2 + gc.imag ** 2).sum().item()
+    num = torch.where(Ng > 0, Sg.abs() ** 2 / Ng.clamp_min(1e-300), torch.zeros_like(Ng))[:, mt].sum(dim=1)
+    E_prop = (num / power).cpu().numpy()
+    assert np.allclose(E, E_prop, rtol=1e-6, atol=0)
+    assert np.all(E > 0) and np.all(E <= 1.0)
+    del G, Sg, Ng
+    torch.cuda.empty_cache()

@@ -1,0 +1,147 @@
+"""Host logic of libdsp, checked on the CPU through its C ABI.
+
+No device calls: the library loads without a GPU, its host geometry is
+compared bit for bit with the oracle's independent implementation, and its
+argument validation returns the documented status codes.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import dsp_oracle as O
+from synthetic import LAMBDA_300KV, Optics, bf_pixels, random_weights, workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+dsp = pytest.importorskip("stem_direct_ptychography_amd")
+from stem_direct_ptychography_amd import _lib  # noqa: E402
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "dsp.h")).read()
+    declared = set(re.findall(r"\b(dsp_[a-z_]+)\s*\(", hdr))
+    assert declared, "no declarations parsed"
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert declared == set(_lib.EXPORTS)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_alias_geometry_bit_exact(name):
+    w = workload(name)
+    q, counts, Ks = O.alias_table(w.n_scan, w.step, w.upsampling, w.optics)
+    nq, am, hist = dsp.geometry_counts(w.n_scan, w.step, w.optics, w.upsampling)
+    assert nq == len(q)
+    assert am == counts.max()
+    want = np.bincount(counts, minlength=10)
+    assert np.array_equal(hist, want)
+    ql, cl, Kl = dsp.alias_geometry(w.n_scan, w.step, w.optics, w.upsampling)
+    assert np.array_equal(ql, q)
+    assert np.array_equal(cl, counts)
+    for i in range(0, len(q), max(1, len(q) // 5000)):
+        A = counts[i]
+        assert np.array_equal(Kl[i, :A], Ks[i])
+        assert not Kl[i, A:].any()
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_active_set_bit_exact(name):
+    w = workload(name)
+    _, k = bf_pixels(w)
+    assert np.array_equal(dsp.active_bf(k, w.optics), O.active_pixels(k, w.optics))
+    # a disk larger than the aperture: the edge pixels drop out identically
+    k2 = k * 1.3
+    assert np.array_equal(dsp.active_bf(k2, w.optics), O.active_pixels(k2, w.optics))
+
+
+def test_band_count_bit_exact():
+    w = workload("c5")
+    assert dsp.band_count(w.n_scan, w.step, w.band) == int(O.band_mask(w.n_scan, w.step, w.band).sum())
+    assert dsp.band_count(64, 0.5, None) == 64 * 33
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_chi_polynomial_matches_oracle(name):
+    w = workload(name)
+    rng = np.random.default_rng(0)
+    kc = w.optics.semiangle / w.optics.wavelength
+    k = rng.uniform(-2.2 * kc, 2.2 * kc, size=(2000, 2))
+    got = dsp.chi_host(w.optics, k)
+    want = O.chi(k[:, 0], k[:, 1], w.optics)
+    assert np.max(np.abs(got - want)) <= 1e-11 * max(1.0, np.max(np.abs(want)))
+
+
+def test_chi_polynomial_every_term():
+    rng = np.random.default_rng(1)
+    k = rng.uniform(-3.0, 3.0, size=(200, 2))
+    for n, m in [(1, 0), (1, 2), (2, 1), (2, 3), (3, 0), (3, 2), (3, 4), (4, 1), (4, 3), (4, 5),
+                 (5, 0), (5, 2), (5, 4), (5, 6)]:
+        o = Optics(LAMBDA_300KV, 0.03, 0.03, tilt=(1e-3, -2e-3), aberrations=[(n, m, 1.0e3 * n, 0.37 * m)])
+        got = dsp.chi_host(o, k)
+        want = O.chi(k[:, 0], k[:, 1], o)
+        assert np.max(np.abs(got - want)) <= 1e-11 * max(1.0, np.max(np.abs(want))), (n, m)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_validation_status_codes():
+    w = workload("c2")
+    good = _lib.ScanC(128, 0.4)
+    oc = dsp._optics(w.optics)
+    nq, am = ctypes.c_int(), ctypes.c_int()
+    L = dsp._L
+    assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(oc), 2, ctypes.byref(nq), ctypes.byref(am),
+                                 None) == _lib.DSP_OK
+    odd = _lib.ScanC(127, 0.4)
+    assert L.dsp_geometry_counts(ctypes.byref(odd), ctypes.byref(oc), 2, None, None, None) == _lib.DSP_EUNSUPPORTED
+    bad_step = _lib.ScanC(128, -1.0)
+    assert L.dsp_geometry_counts(ctypes.byref(bad_step), ctypes.byref(oc), 2, None, None, None) == _lib.DSP_EINVAL
+    assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(oc), 5, None, None, None) == _lib.DSP_EUNSUPPORTED
+    assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(oc), 0, None, None, None) == _lib.DSP_EINVAL
+    deep = dsp._optics(w.optics.replace(depth=124.0))
+    assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(deep), 2, None, None, None) == _lib.DSP_EUNSUPPORTED
+    bad_ab = dsp._optics(w.optics.replace(aberrations=[(1, 1, 10.0, 0.0)]))
+    assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(bad_ab), 2, None, None, None) == _lib.DSP_EINVAL
+    assert "Krivanek" in L.dsp_last_error().decode()
+    neg = dsp._optics(w.optics.replace(wavelength=0.0))
+    assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(neg), 2, None, None, None) == _lib.DSP_EINVAL
+    # prepare / ssb reject bad arguments before touching the device
+    _, k = bf_pixels(w)
+    k = np.ascontiguousarray(k)
+    kp = k.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    opts = _lib.PrepareOptsC(0, 2, 0.0, 0)
+    h = ctypes.c_void_p()
+    assert L.dsp_prepare(None, len(k), kp, None, ctypes.byref(good), ctypes.byref(oc), ctypes.byref(opts), None,
+                         ctypes.byref(h)) == _lib.DSP_EINVAL
+    fake = ctypes.c_void_p(0x1000)
+    bad_opts = _lib.PrepareOptsC(7, 2, 0.0, 0)
+    assert L.dsp_prepare(fake, len(k), kp, None, ctypes.byref(good), ctypes.byref(oc), ctypes.byref(bad_opts), None,
+                         ctypes.byref(h)) == _lib.DSP_EINVAL
+    assert L.dsp_prepare(fake, 0, kp, None, ctypes.byref(good), ctypes.byref(oc), ctypes.byref(opts), None,
+                         ctypes.byref(h)) == _lib.DSP_EINVAL
+    wneg = -np.ones(len(k))
+    assert L.dsp_prepare(fake, len(k), kp, wneg.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), ctypes.byref(good),
+                         ctypes.byref(oc), ctypes.byref(opts), None, ctypes.byref(h)) == _lib.DSP_EINVAL
+    arr = (_lib.OpticsC * 2)(oc, dsp._optics(w.optics.replace(semiangle=0.02)))
+    assert L.dsp_ssb(fake, len(k), kp, None, ctypes.byref(good), arr, 2, None, None, None, None,
+                     None) == _lib.DSP_EINVAL
+    assert L.dsp_ssb(fake, len(k), kp, None, ctypes.byref(good), arr, 9, None, None, None, None,
+                     None) == _lib.DSP_EINVAL
+    assert L.dsp_solve(None, None, 1, None, None, None) == _lib.DSP_EINVAL
+    assert L.dsp_info(None, None) == _lib.DSP_EINVAL
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    w = workload("c1")
+    _, k = bf_pixels(w)
+    G = torch.zeros((len(k), 32, 17), dtype=torch.complex64)
+    with pytest.raises(dsp.DspError):
+        dsp.prepare(G, k, w.optics, step=w.step, upsampling=1)
