@@ -1,0 +1,446 @@
+"""Throughput of the direct-ptychography hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ssb-sweep]
+
+Workload: the full-frame configuration (512 x 512 scan, 0.373 A step,
+192 x 192 detector, 300 kV, 30 mrad soft aperture, 9298 bright-field pixels,
+rotation 176.3 deg, 14 aberration terms, tilt (5.92, -0.07) mrad,
+upsampling 3, G = (9298, 512, 257) complex64 = 9.8 GB, Poisson noise),
+generated on the GPU with plain torch ops and resident in HBM before timing.
+
+One step is one pass of the whole path over that G:
+  phase prepare (pixel terms, transfer + Gram + right side, eigenbasis)
+  + solve at one strength + scatter to the fine half plane,
+  complex prepare (pixel terms, transfer + Gram + right side)
+  + solve at one strength pair + scatter,
+  SSB sum and agreement over the 0.2-0.9 1/A band for one optics set.
+
+value = solved scan frequencies per step / seconds per step.  The line also
+carries the phase prepare alone (the pages' headline stage), the G read
+rate, the roofline of the dominant kernel (HIP events on the stream the
+kernels run on), and the oracle's rate on a bounded sample of the same
+workload on the host cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "scan freqs/s for prepare (Gram+rhs+eigh) and G read GB/s, 512x512 scan"
+UNIT = "scan freqs/s"
+
+# MI355X published peaks
+HBM_PEAK_GBPS = 8000.0
+FP64_VECTOR_PEAK_TFLOPS = 78.6   # 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x 2.4 GHz
+
+# Algorithmic FP64 flops of the transfer + Gram kernel, per counted unit.
+#   support test (pixel, alias, lobe): k -/+ Q (2), squared length (3)      = 5
+#   non-zero lobe: theta = lambda k' + tau (2 FMA = 4), chi(theta) as a
+#     degree-6 bivariate polynomial of 28 coefficients by Horner (27 FMA = 54),
+#     phase difference (1), sincos counted as one Cody-Waite reduction and two
+#     minimax polynomials to double precision (18 FMA = 36), aperture product
+#     (1), amplitude times cos and sin (2)                                   = 98
+#   non-zero column per pixel: weight times column (2), diagonal |t|^2 w
+#     (2 FMA = 4), right side conj(t) w g (4 FMA = 8)                        = 14
+#   non-zero column pair c < d per pixel: conj(t_c) w t_d (4 FMA)           = 8
+#   (pixel, frequency) term: w g (2), power w |g|^2 (2 FMA = 4)              = 6
+FLOP_TEST, FLOP_LOBE, FLOP_COL, FLOP_PAIR, FLOP_TERM = 5.0, 98.0, 14.0, 8.0, 6.0
+
+KERNEL_SOURCES = ("stem_direct_ptychography_amd/csrc/dsp_kernels.hip",
+                  "stem_direct_ptychography_amd/csrc/dsp_internal.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gram_full_frame.txt")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def gram_flops(work: dict) -> float:
+    return (FLOP_TEST * work["tests"] + FLOP_LOBE * work["lobes"] + FLOP_COL * work["cols"]
+            + FLOP_PAIR * work["pairs"] + FLOP_TERM * work["terms"])
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary,
+    or None when there is none or the kernel sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                a, b = line.split("=", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash() or kv.get("kernel") != kernel:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------
+# workload
+# ----------------------------------------------------------------------------
+
+
+def build_inputs(dev):
+    from synthetic import bf_pixels, data_stack_torch, workload
+
+    w = workload("c4")
+    pix, k = bf_pixels(w)
+    log(f"generating G {(len(k), w.n_scan, w.n_half)} complex64 on {dev}")
+    t = time.perf_counter()
+    G = data_stack_torch(w, pix, dev)
+    import torch
+
+    torch.cuda.synchronize()
+    log(f"G ready in {time.perf_counter() - t:.1f} s ({G.numel() * 8 / 1e9:.2f} GB)")
+    return w, k, G
+
+
+class Step:
+    """One pass of the whole path; keeps the per-stage results of the last pass."""
+
+    def __init__(self, dsp, w, k, G, band):
+        self.dsp, self.w, self.k, self.G, self.band = dsp, w, k, G, band
+        self.strength = 1e-2
+        self.last = {}
+
+    def __call__(self, timing: bool):
+        dsp, w, k, G = self.dsp, self.w, self.k, self.G
+        pp = dsp.prepare(G, k, w.optics, step=w.step, upsampling=w.upsampling, method="phase",
+                         smoothness=w.smoothness, timing=timing)
+        xp = pp.solve([self.strength])
+        sp = pp.scatter(xp)
+        pc = dsp.prepare(G, k, w.optics, step=w.step, upsampling=w.upsampling, method="complex",
+                         smoothness=w.smoothness, timing=timing)
+        xc = pc.solve([(self.strength, self.strength)])
+        sc = pc.scatter(xc)
+        S, Nn, E = dsp.ssb(G, k, [w.optics], step=w.step, band=self.band)
+        self.last = {"phase": pp, "complex": pc, "outputs": (sp, sc, S, Nn), "E": E}
+        return self.last
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands on a bounded sample
+# ----------------------------------------------------------------------------
+
+
+def cpu_baseline(w, k, G, n_q: int, n_band: int, budget_s: float, strength: float):
+    import numpy as np
+    import torch
+
+    from oracle import dsp_oracle as O
+
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        act = O.active_pixels(k, w.optics)
+        ka = k[act]
+        wa = np.ones(len(act))
+        uq = O.unique_frequencies(w.n_scan)
+        bm = O.band_mask(w.n_scan, w.step, (0.2, 0.9))
+        ent = np.argwhere(bm)
+        rng = np.random.default_rng(12345)
+        qsel = uq[np.sort(rng.choice(len(uq), size=256, replace=False))]
+        esel = ent[np.sort(rng.choice(len(ent), size=256, replace=False))]
+        dev = G.device
+        act_t = torch.as_tensor(act, device=dev)
+
+        def cols(idx):
+            g = G[:, torch.as_tensor(idx[:, 0], device=dev), torch.as_tensor(idx[:, 1], device=dev)]
+            g = g[act_t].cpu().numpy().astype(np.complex128)
+            return [g[:, i] for i in range(len(idx))]
+
+        qcols, ecols = cols(qsel), cols(esel)
+        t_phase = t_cplx = t_ssb = 0.0
+        nq_done = ne_done = 0
+        t_all = time.perf_counter()
+        i = 0
+        while i < len(qsel) and time.perf_counter() - t_all < budget_s:
+            sl = slice(i, i + 8)
+            t0 = time.perf_counter()
+            pr = O.prepare(qsel[sl], qcols[sl], ka, wa, w.n_scan, w.step, w.upsampling, w.optics, "phase",
+                           w.smoothness)
+            O.solve(pr, strength)
+            t1 = time.perf_counter()
+            pr = O.prepare(qsel[sl], qcols[sl], ka, wa, w.n_scan, w.step, w.upsampling, w.optics, "complex",
+                           w.smoothness)
+            O.solve(pr, (strength, strength))
+            t2 = time.perf_counter()
+            O.ssb(esel[sl], ecols[sl], ka, wa, w.n_scan, w.step, [w.optics])
+            t3 = time.perf_counter()
+            t_phase += t1 - t0
+            t_cplx += t2 - t1
+            t_ssb += t3 - t2
+            nq_done += len(qsel[sl])
+            ne_done += len(esel[sl])
+            i += 8
+        per_q = (t_phase + t_cplx) / nq_done
+        per_e = t_ssb / ne_done
+        est_step = n_q * per_q + n_band * per_e
+        return {
+            "value": n_q / est_step,
+            "unit": UNIT,
+            "cores": 1,
+            "kind": "oracle",
+            "sample": (f"{nq_done} of {n_q} solved frequencies (seeded uniform) through phase prepare+solve and "
+                       f"complex prepare+solve, and {ne_done} of {n_band} band entries through the SSB sum, "
+                       f"{t_phase + t_cplx + t_ssb:.1f} s of CPU work on one thread; value = frequencies per "
+                       f"second of the whole step extrapolated from the per-item times"),
+            "phase_prepare_q_per_s": nq_done / t_phase,
+            "cpu_model": _cpu_model(),
+        }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ----------------------------------------------------------------------------
+# SSB sweep over optics sets (the agreement workload: 8807 pixels, band pass)
+# ----------------------------------------------------------------------------
+
+
+def ssb_sweep(dsp, dev, reps: int = 5):
+    import numpy as np
+    import torch
+
+    from synthetic import bf_pixels, data_stack_torch, ssb_sets, workload
+
+    w = workload("c5")
+    pix, k = bf_pixels(w)
+    log(f"generating agreement-pass G {(len(k), w.n_scan, w.n_half)} on {dev}")
+    G = data_stack_torch(w, pix, dev)
+    n_band = dsp.band_count(w.n_scan, w.step, w.band)
+    g_bytes = n_band * len(k) * 8.0
+    out = {"workload": f"512x512 scan, {len(k)} BF px, band {w.band[0]}-{w.band[1]} 1/A ({n_band} stored q)",
+           "g_bytes_per_pass": g_bytes, "passes": {}}
+    stream = torch.cuda.current_stream()
+    for B in (1, 2, 4, 8):
+        sets = ssb_sets(w, B)
+        dsp.ssb(G, k, sets, step=w.step, band=w.band, agreement=False)
+        ms = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dsp.ssb(G, k, sets, step=w.step, band=w.band, agreement=False)
+            e1.record(stream)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        m = float(np.median(ms))
+        out["passes"][str(B)] = {"ms": m, "q_sets_per_s": n_band * B / (m / 1e3),
+                                 "g_GBps": g_bytes / (m / 1e3) / 1e9}
+        log(f"ssb B={B}: {m:.3f} ms")
+    del G
+    torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# main
+# ----------------------------------------------------------------------------
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-ssb-sweep", action="store_true")
+    ap.add_argument("--copy-probe", type=float, default=0.0,
+                    help="only run a plain device copy of this many GiB (counter calibration) and exit")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the path shards by scan "
+              f"frequency with no exchange; this build runs and reports a single GPU)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+
+    if args.copy_probe > 0:
+        n = int(args.copy_probe * (1 << 30)) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}))
+        return 0
+
+    import stem_direct_ptychography_amd as dsp
+
+    log(f"library {dsp.LIB_PATH}")
+    w, k, G = build_inputs(dev)
+    band = (0.2, 0.9)
+    step = Step(dsp, w, k, G, band)
+
+    # work counts and flops per Gram launch (one instrumented prepare per method, untimed)
+    flops = {}
+    for method in ("phase", "complex"):
+        p = dsp.prepare(G, k, w.optics, step=w.step, upsampling=w.upsampling, method=method,
+                        smoothness=w.smoothness, count_work=True)
+        inf = p.timings()
+        for g in inf["gram"]:
+            flops[(method, g["nj"])] = (gram_flops(g["work"]), g["work"], g["tiles"])
+        flops[(method, "lobes")] = inf["lobes"]
+        del p
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        step(timing=True)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    stream = torch.cuda.current_stream()
+    per = {"phase": [], "complex": []}
+    gram_ms = {}
+    host_ms = {"phase": [], "complex": []}
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        r = step(timing=True)
+        for method in ("phase", "complex"):
+            inf = r[method].timings()   # synchronizes the prepare's events (already passed)
+            per[method].append(inf["stage_ms"])
+            host_ms[method].append(inf["host_ms"])
+            for g in inf["gram"]:
+                gram_ms.setdefault((method, g["nj"]), []).append(g["ms"])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    log(f"{args.steps} steps: wall {wall:.3f} s, stream {gpu_ms:.1f} ms")
+    ms_per_step = wall * 1e3 / args.steps
+
+    inf_p = step.last["phase"].info
+    n_q = inf_p["n_q"]
+    g_bytes = inf_p["g_bytes"]
+    n_band = dsp.band_count(w.n_scan, w.step, band)
+    ssb_bytes = n_band * inf_p["n_active_bf"] * 8.0
+    step_g_bytes = 2 * g_bytes + ssb_bytes
+
+    def med(v):
+        return float(np.median(v))
+
+    stages = {}
+    for method in ("phase", "complex"):
+        s = np.array(per[method])
+        stages[method] = {"pixel_terms_ms": med(s[:, 0]), "gram_ms": med(s[:, 1]), "eigenbasis_ms": med(s[:, 2]),
+                          "prepare_kernels_ms": med(s[:, 3]), "host_geometry_ms": med(host_ms[method]),
+                          "prepare_q_per_s": n_q / (med(s[:, 3]) / 1e3),
+                          "prepare_g_GBps": g_bytes / (med(s[:, 3]) / 1e3) / 1e9}
+
+    # dominant kernel: the Gram launch with the largest time per step
+    launches = []
+    for key, v in gram_ms.items():
+        f, work, tiles = flops[key]
+        m = float(np.mean(v))
+        launches.append({"method": key[0], "slots": key[1], "tiles": tiles, "avg_ms": m,
+                         "flops": f, "tflops": f / (m / 1e3) / 1e12, "lobes": work["lobes"]})
+    launches.sort(key=lambda d: -d["avg_ms"])
+    dom = launches[0]
+    kname = f"gram_kernel<{dom['slots']},{0 if dom['method'] == 'phase' else 1}>"
+    tr = measured_traffic(kname)
+    roofline = {"bound": "alu", "achieved": dom["tflops"], "peak": FP64_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": dom["tflops"] / FP64_VECTOR_PEAK_TFLOPS, "traffic": tr,
+                "kernel": f"{kname} ({dom['method']} Gram, tiles with {dom['slots']} alias slots, "
+                          f"{dom['tiles']} tiles, {dom['lobes']:.3e} non-zero lobes per launch)",
+                "avg_launch_ms": dom["avg_ms"], "flops_per_launch": dom["flops"]}
+    gram_stage = {}
+    for method in ("phase", "complex"):
+        ls = [d for d in launches if d["method"] == method]
+        tf = sum(d["flops"] for d in ls)
+        tm = sum(d["avg_ms"] for d in ls)
+        gram_stage[method] = {"ms": tm, "tflops": tf / (tm / 1e3) / 1e12,
+                              "frac_fp64_peak": tf / (tm / 1e3) / 1e12 / FP64_VECTOR_PEAK_TFLOPS,
+                              "g_GBps": g_bytes / (tm / 1e3) / 1e9,
+                              "frac_hbm_peak": g_bytes / (tm / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                              "lobes": flops[(method, "lobes")]}
+
+    result = {
+        "metric": METRIC,
+        "value": n_q / (ms_per_step / 1e3),
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "full frame: 512x512 scan, 0.373 A step, 192x192 detector, 300 kV, 30 mrad soft, "
+                               "9298 BF px, rot 176.3 deg, 14 aberrations, tilt (5.92,-0.07) mrad, upsampling 3, "
+                               "G (9298,512,257) complex64; step = phase prepare+solve+scatter, complex "
+                               "prepare+solve+scatter, SSB+agreement over the 0.2-0.9 1/A band",
+                   "n_q": n_q, "alias_hist": inf_p["alias_hist"][3:7], "n_active_bf": inf_p["n_active_bf"],
+                   "strength": step.strength},
+        "g_read_GBps": step_g_bytes / (ms_per_step / 1e3) / 1e9,
+        "g_bytes_per_step": step_g_bytes,
+        "phase_prepare_q_per_s": stages["phase"]["prepare_q_per_s"],
+        "phase_prepare_g_GBps": stages["phase"]["prepare_g_GBps"],
+        "stages": stages,
+        "gram_stage": gram_stage,
+        "gram_launches": launches,
+        "roofline": roofline,
+        "stream_ms_per_step": gpu_ms / args.steps,
+        "agreement": float(step.last["E"][0]),
+    }
+    del step.last
+    torch.cuda.synchronize()
+
+    if not args.no_cpu_baseline:
+        log(f"timing the oracle on a bounded sample ({args.cpu_budget:.0f} s budget)")
+        result["cpu_baseline"] = cpu_baseline(w, k, G, n_q, n_band, args.cpu_budget, step.strength)
+    else:
+        result["cpu_baseline"] = None
+    del G, step
+    torch.cuda.empty_cache()
+    if not args.no_ssb_sweep:
+        result["ssb_sweep"] = ssb_sweep(dsp, dev)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

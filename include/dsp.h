@@ -105,7 +105,9 @@ typedef struct {
     int flags;               /* DSP_FLAG_* */
 } dsp_prepare_opts;
 
-#define DSP_FLAG_TIMING 1    /* record per-stage HIP events (read by dsp_info) */
+#define DSP_FLAG_TIMING 1       /* record HIP events per stage and per Gram launch (read by dsp_info) */
+#define DSP_FLAG_COUNT_WORK 2   /* after the prepare's kernels, count the work of each Gram launch
+                                   (one extra kernel per launch; read by dsp_info) */
 
 typedef struct dsp_handle dsp_handle;
 
@@ -120,9 +122,22 @@ typedef struct {
     int alias_hist[10];      /* alias_hist[A] = frequencies with A aliases */
     double scale;            /* strength unit: sum of active weights */
     double g_bytes;          /* algorithmic G bytes a prepare reads: n_q * n_active * 8 */
-    double lobes;            /* nonzero weak-object lobes a prepare evaluates */
+    double lobes;            /* with DSP_FLAG_COUNT_WORK: non-zero weak-object lobes evaluated */
     double host_ms;          /* host geometry + upload enqueue of the last prepare */
     double stage_ms[4];      /* with DSP_FLAG_TIMING: pixel terms, Gram, eigenbasis, total */
+    /* one entry per Gram launch, in launch order (tiles grouped by alias slot
+     * count): slot count and tiles; with DSP_FLAG_TIMING the HIP-event
+     * duration on the caller's stream; with DSP_FLAG_COUNT_WORK the launch's
+     * work summed over its frequencies: [0] aperture-support tests (pixel,
+     * alias, lobe), [1] non-zero lobes, [2] non-zero Gram columns (pixel,
+     * column), [3] non-zero column pairs c < d, [4] (pixel, frequency) terms.
+     * A phase column is non-zero when either lobe is; complex columns are the
+     * two lobes. */
+    int n_gram_launches;
+    int gram_nj[16];
+    int gram_tiles[16];
+    double gram_ms[16];
+    double gram_work[16][5];
 } dsp_info_t;
 
 /*

@@ -137,7 +137,10 @@ class Prepared:
             "n_active_bf": inf.n_active_bf, "method": inf.method, "upsampling": inf.upsampling,
             "n_scan": inf.n_scan, "n_tiles": inf.n_tiles, "alias_hist": list(inf.alias_hist),
             "scale": inf.scale, "g_bytes": inf.g_bytes, "host_ms": inf.host_ms,
-            "stage_ms": list(inf.stage_ms),
+            "stage_ms": list(inf.stage_ms), "lobes": inf.lobes,
+            "gram": [{"nj": inf.gram_nj[i], "tiles": inf.gram_tiles[i], "ms": inf.gram_ms[i],
+                      "work": dict(zip(("tests", "lobes", "cols", "pairs", "terms"), list(inf.gram_work[i])))}
+                     for i in range(inf.n_gram_launches)],
         }
 
     def timings(self) -> dict:
@@ -201,7 +204,7 @@ class Prepared:
 
 
 def prepare(G, bf_coords, optics, step: float, upsampling: int, method: str = "phase", weights=None,
-            smoothness: float = 0.0, timing: bool = False, stream=None) -> Prepared:
+            smoothness: float = 0.0, timing: bool = False, count_work: bool = False, stream=None) -> Prepared:
     """Per-frequency normal equations (and, for "phase", the eigenbasis)."""
     n = _check_G(G)
     k = _coords(bf_coords)
@@ -211,8 +214,9 @@ def prepare(G, bf_coords, optics, step: float, upsampling: int, method: str = "p
     if method not in ("phase", "complex"):
         raise DspError(_lib.DSP_EINVAL, f"unknown method {method!r}")
     scan = _lib.ScanC(n, float(step))
+    flags = (_lib.DSP_FLAG_TIMING if timing else 0) | (_lib.DSP_FLAG_COUNT_WORK if count_work else 0)
     opts = _lib.PrepareOptsC(_lib.DSP_PHASE if method == "phase" else _lib.DSP_COMPLEX, int(upsampling),
-                             float(smoothness), _lib.DSP_FLAG_TIMING if timing else 0)
+                             float(smoothness), flags)
     oc = _optics(optics)
     h = ctypes.c_void_p()
     _check(_L.dsp_prepare(ctypes.c_void_p(G.data_ptr()), k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan),

@@ -13,6 +13,7 @@ STATUS_NAMES = {0: "DSP_OK", 1: "DSP_EINVAL", 2: "DSP_EUNSUPPORTED", 3: "DSP_EAL
                 5: "DSP_EDEVICE"}
 DSP_PHASE, DSP_COMPLEX = 0, 1
 DSP_FLAG_TIMING = 1
+DSP_FLAG_COUNT_WORK = 2
 MAX_ABERRATIONS = 16
 
 
@@ -49,6 +50,8 @@ class InfoC(ctypes.Structure):
         ("upsampling", ctypes.c_int), ("n_scan", ctypes.c_int), ("n_tiles", ctypes.c_int),
         ("alias_hist", ctypes.c_int * 10), ("scale", ctypes.c_double), ("g_bytes", ctypes.c_double),
         ("lobes", ctypes.c_double), ("host_ms", ctypes.c_double), ("stage_ms", ctypes.c_double * 4),
+        ("n_gram_launches", ctypes.c_int), ("gram_nj", ctypes.c_int * 16), ("gram_tiles", ctypes.c_int * 16),
+        ("gram_ms", ctypes.c_double * 16), ("gram_work", (ctypes.c_double * 5) * 16),
     ]
 
 

@@ -430,7 +430,11 @@ struct dsp_handle {
     double2 *d_U = nullptr;
     double2 *d_c = nullptr;
     bool timing = false;
+    bool count_work = false;
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    std::vector<int> gram_order;              // launch order of the tile groups
+    std::vector<hipEvent_t> gram_ev;          // two per launch (timing)
+    unsigned long long *d_work = nullptr;     // [tile][5] (DSP_FLAG_COUNT_WORK)
 
     ~dsp_handle() {
         hipSetDevice(device);
@@ -446,6 +450,9 @@ struct dsp_handle {
         hipFree(d_c);
         for (auto &e : ev)
             if (e) hipEventDestroy(e);
+        for (auto &e : gram_ev)
+            if (e) hipEventDestroy(e);
+        hipFree(d_work);
     }
 };
 
@@ -549,6 +556,7 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     h->method = opts->method;
     h->n_bf = n_bf;
     h->timing = (opts->flags & DSP_FLAG_TIMING) != 0;
+    h->count_work = (opts->flags & DSP_FLAG_COUNT_WORK) != 0;
     if ((st = build_geometry(scan, optics, opts->upsampling, h->geo))) return st;
     Geometry &g = h->geo;
     const int max_nj = h->method == DSP_PHASE ? MAX_NJ_PHASE : MAX_NJ_COMPLEX;
@@ -634,9 +642,17 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     std::vector<int> order(h->tg.group_nj.size());
     for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return h->tg.group_n[a] > h->tg.group_n[b]; });
-    for (int gi : order) {
+    h->gram_order = order;
+    if (h->timing) {
+        h->gram_ev.assign(2 * order.size(), nullptr);
+        for (auto &e : h->gram_ev) HIP_TRY(hipEventCreate(&e));
+    }
+    for (size_t oi = 0; oi < order.size(); ++oi) {
+        const int gi = order[oi];
         gp.tiles = h->d_tiles + h->tg.group_off[gi];
+        if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[2 * oi], stream));
         HIP_TRY(launch_gram(gp, h->tg.group_nj[gi], h->method, h->tg.group_n[gi], stream));
+        if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[2 * oi + 1], stream));
     }
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[2], stream));
 
@@ -663,6 +679,15 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
         }
     }
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[3], stream));
+    if (h->count_work) {
+        // instrumentation after the prepare's own kernels: work per tile
+        if ((st = dev_alloc(&h->d_work, h->tg.tiles.size() * 5))) return st;
+        for (size_t gi = 0; gi < h->tg.group_nj.size(); ++gi) {
+            gp.tiles = h->d_tiles + h->tg.group_off[gi];
+            HIP_TRY(launch_work_count(gp, h->method, h->tg.group_n[gi], h->d_work + (size_t)h->tg.group_off[gi] * 5,
+                                      stream));
+        }
+    }
     h->host_ms = now_ms() - t0;
     *out = h.release();
     return DSP_OK;
@@ -750,8 +775,14 @@ dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out) {
     out->scale = h->scale;
     out->g_bytes = (double)g.n_q * (double)h->act.pix.size() * 8.0;
     out->host_ms = h->host_ms;
+    out->n_gram_launches = (int)std::min<size_t>(16, h->gram_order.size());
+    for (int oi = 0; oi < out->n_gram_launches; ++oi) {
+        const int gi = h->gram_order[oi];
+        out->gram_nj[oi] = h->tg.group_nj[gi];
+        out->gram_tiles[oi] = h->tg.group_n[gi];
+    }
+    if ((h->timing && h->ev[3]) || (h->count_work && h->d_work)) HIP_TRY(hipSetDevice(h->device));
     if (h->timing && h->ev[3]) {
-        HIP_TRY(hipSetDevice(h->device));
         HIP_TRY(hipEventSynchronize(h->ev[3]));
         float ms;
         HIP_TRY(hipEventElapsedTime(&ms, h->ev[0], h->ev[1]));
@@ -762,6 +793,25 @@ dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out) {
         out->stage_ms[2] = ms;
         HIP_TRY(hipEventElapsedTime(&ms, h->ev[0], h->ev[3]));
         out->stage_ms[3] = ms;
+        for (int oi = 0; oi < out->n_gram_launches; ++oi) {
+            HIP_TRY(hipEventElapsedTime(&ms, h->gram_ev[2 * oi], h->gram_ev[2 * oi + 1]));
+            out->gram_ms[oi] = ms;
+        }
+    }
+    if (h->count_work && h->d_work) {
+        std::vector<unsigned long long> wk(h->tg.tiles.size() * 5, 0ull);
+        HIP_TRY(hipMemcpy(wk.data(), h->d_work, wk.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+        double total = 0.0;
+        for (size_t t = 0; t < h->tg.tiles.size(); ++t) total += (double)wk[t * 5 + 1];
+        for (int oi = 0; oi < out->n_gram_launches; ++oi) {
+            const int gi = h->gram_order[oi];
+            for (int c = 0; c < 5; ++c) {
+                double v = 0.0;
+                for (int t = 0; t < h->tg.group_n[gi]; ++t) v += (double)wk[(size_t)(h->tg.group_off[gi] + t) * 5 + c];
+                out->gram_work[oi][c] = v;
+            }
+        }
+        out->lobes = total;
     }
     return DSP_OK;
 }

@@ -283,6 +283,53 @@ __global__ __launch_bounds__(64 * P) void gram_kernel(GramParams prm) {
     }
 }
 
+// Work a Gram launch does per frequency, counted exactly per lane (not the
+// wave-wide union the Gram kernel evaluates): instrumentation, run after the
+// prepare's own kernels.  out[tile][0..4] = support tests (pixel, alias, lobe),
+// non-zero lobes, non-zero columns, non-zero column pairs c < d, and
+// (pixel, frequency) terms.  A phase column is non-zero when either lobe is;
+// complex columns are the L and R lobes themselves.
+template <int METHOD>
+__global__ __launch_bounds__(64) void work_count_kernel(GramParams prm, unsigned long long *out) {
+    const int lane = threadIdx.x & 63;
+    const GramTile *tile = prm.tiles + blockIdx.x;
+    const int yh = tile->yh0 + (lane >> 4);
+    const int ix = tile->ix0 + (lane & 15);
+    const bool valid = tile->qidx[lane] >= 0;
+    const unsigned mask = valid ? (unsigned)tile->mask[lane] : 0u;
+    const int nj = tile->nj;
+    unsigned long long tests = 0, lobes = 0, cols = 0, pairs = 0, terms = 0;
+    for (int p = 0; p < prm.n_pix; ++p) {
+        const double ky = prm.pix[p].ky, kx = prm.pix[p].kx;
+        unsigned long long nc = 0;
+        for (int s = 0; s < nj; ++s) {
+            if (!((mask >> s) & 1u)) continue;
+            const double Qy = (double)(yh + (int)tile->jy[s] * prm.N) * prm.dq;
+            const double Qx = (double)(ix + (int)tile->jx[s] * prm.N) * prm.dq;
+            const double dy = ky - Qy, dx = kx - Qx, ey = ky + Qy, ex = kx + Qx;
+            const bool zl = inside_support(prm.ap, fma(dy, dy, dx * dx));
+            const bool zr = inside_support(prm.ap, fma(ey, ey, ex * ex));
+            tests += 2;
+            lobes += (zl ? 1 : 0) + (zr ? 1 : 0);
+            if (METHOD == 0) nc += (zl || zr) ? 1 : 0;
+            else nc += (zl ? 1 : 0) + (zr ? 1 : 0);
+        }
+        cols += nc;
+        pairs += nc * (nc - 1) / 2;   // 0 when nc = 0 (unsigned wrap times 0)
+        terms += valid ? 1 : 0;
+    }
+    unsigned long long v[5] = {tests, lobes, cols, pairs, terms};
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v[i] += __shfl_xor(v[i], off);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < 5; ++i) out[(size_t)blockIdx.x * 5 + i] = v[i];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // phase eigenbasis: cyclic complex Jacobi, one lane per frequency
 // ---------------------------------------------------------------------------
@@ -864,6 +911,15 @@ hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_tiles, h
         case 6: return launch_gram_t<6, 1, 1>(prm, n_tiles, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_work_count(const GramParams &prm, int method, int n_tiles, unsigned long long *out,
+                             hipStream_t st) {
+    if (n_tiles <= 0) return hipSuccess;
+    if (method == 0) work_count_kernel<0><<<n_tiles, 64, 0, st>>>(prm, out);
+    else work_count_kernel<1><<<n_tiles, 64, 0, st>>>(prm, out);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
 }
 
 hipError_t launch_eig(const EigParams &prm, int A, hipStream_t st) {

@@ -45,6 +45,8 @@ hipError_t launch_pixel_terms(PixelRec *pix, int n_pix, const ApertureDev &ap, c
                               hipStream_t st);
 int gram_waves_per_tile(int nj, int method);
 hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_tiles, hipStream_t st);
+hipError_t launch_work_count(const GramParams &prm, int method, int n_tiles, unsigned long long *out,
+                             hipStream_t st);
 hipError_t launch_eig(const EigParams &prm, int A, hipStream_t st);
 hipError_t launch_solve(const SolveParams &prm, int A, int method, hipStream_t st);
 hipError_t launch_fill_zero(double *p, size_t n, hipStream_t st);
