@@ -330,6 +330,8 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
     per = {"phase": [], "complex": []}
     gram_ms = {}
+    fixup_ms = {}
+    waves = {}
     host_ms = {"phase": [], "complex": []}
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -344,6 +346,8 @@ def main(argv=None) -> int:
             host_ms[method].append(inf["host_ms"])
             for g in inf["gram"]:
                 gram_ms.setdefault((method, g["nj"]), []).append(g["ms"])
+                fixup_ms.setdefault((method, g["nj"]), []).append(g["fixup_ms"])
+                waves[(method, g["nj"])] = g["waves"]
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -374,7 +378,8 @@ def main(argv=None) -> int:
     for key, v in gram_ms.items():
         f, work, tiles = flops[key]
         m = float(np.mean(v))
-        launches.append({"method": key[0], "slots": key[1], "tiles": tiles, "avg_ms": m,
+        launches.append({"method": key[0], "slots": key[1], "tiles": tiles, "waves": waves[key], "avg_ms": m,
+                         "fixup_ms": float(np.mean(fixup_ms[key])),
                          "flops": f, "tflops": f / (m / 1e3) / 1e12, "lobes": work["lobes"]})
     launches.sort(key=lambda d: -d["avg_ms"])
     dom = launches[0]

@@ -125,8 +125,10 @@ typedef struct {
     double lobes;            /* with DSP_FLAG_COUNT_WORK: non-zero weak-object lobes evaluated */
     double host_ms;          /* host geometry + upload enqueue of the last prepare */
     double stage_ms[4];      /* with DSP_FLAG_TIMING: pixel terms, Gram, eigenbasis, total */
+    int timing_ready;        /* 1 when the timing fields are filled: dsp_info never waits; it
+                                fills them once the prepare's work has completed on its stream */
     /* one entry per Gram launch, in launch order (tiles grouped by alias slot
-     * count): slot count and tiles; with DSP_FLAG_TIMING the HIP-event
+     * count): slot count, tiles and waves; with DSP_FLAG_TIMING the HIP-event
      * duration on the caller's stream; with DSP_FLAG_COUNT_WORK the launch's
      * work summed over its frequencies: [0] aperture-support tests (pixel,
      * alias, lobe), [1] non-zero lobes, [2] non-zero Gram columns (pixel,
@@ -136,7 +138,9 @@ typedef struct {
     int n_gram_launches;
     int gram_nj[16];
     int gram_tiles[16];
+    int gram_waves[16];      /* waves (64-lane workgroups) of the launch */
     double gram_ms[16];
+    double gram_fixup_ms[16];/* with DSP_FLAG_TIMING: the launch's partial-sum fixup */
     double gram_work[16][5];
 } dsp_info_t;
 
@@ -200,8 +204,8 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
                    int B, const double *band_invA, void *S_out_c128_dev, double *norm_out_dev,
                    double *agreement_out_host, void *hip_stream);
 
-/* Sizes, histogram, timings of a prepared handle (synchronizes the timing
- * events when DSP_FLAG_TIMING was set). */
+/* Sizes, histogram, timings of a prepared handle.  Does not wait for the
+ * device, except to read DSP_FLAG_COUNT_WORK counts (a blocking copy). */
 dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out);
 
 /*
@@ -241,6 +245,11 @@ dsp_status dsp_band_count(const dsp_scan *scan, const double *band_invA, int *co
 /* The library's chi(k) (its polynomial expansion of the Krivanek terms)
  * evaluated on the host at n points k_host double[n][2]: chi_out double[n]. */
 dsp_status dsp_chi_host(const dsp_optics *optics, const double *k_host, int n, double *chi_out);
+
+/* The library's FP64 sine and cosine of the transfer's phase factors (the
+ * same source the kernels compile) evaluated on the host at n points:
+ * x_host double[n] -> sin_out, cos_out double[n]. */
+dsp_status dsp_sincos_host(const double *x_host, int n, double *sin_out, double *cos_out);
 
 #ifdef __cplusplus
 }

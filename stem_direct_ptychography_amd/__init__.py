@@ -26,7 +26,7 @@ from . import _lib
 _L = _lib.load()
 
 __all__ = ["DspError", "Prepared", "prepare", "ssb", "geometry_counts", "alias_geometry", "active_bf",
-           "band_count", "chi_host", "LIB_PATH"]
+           "band_count", "chi_host", "sincos_host", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
 
@@ -137,14 +137,18 @@ class Prepared:
             "n_active_bf": inf.n_active_bf, "method": inf.method, "upsampling": inf.upsampling,
             "n_scan": inf.n_scan, "n_tiles": inf.n_tiles, "alias_hist": list(inf.alias_hist),
             "scale": inf.scale, "g_bytes": inf.g_bytes, "host_ms": inf.host_ms,
-            "stage_ms": list(inf.stage_ms), "lobes": inf.lobes,
-            "gram": [{"nj": inf.gram_nj[i], "tiles": inf.gram_tiles[i], "ms": inf.gram_ms[i],
+            "stage_ms": list(inf.stage_ms), "timing_ready": bool(inf.timing_ready), "lobes": inf.lobes,
+            "gram": [{"nj": inf.gram_nj[i], "tiles": inf.gram_tiles[i], "waves": inf.gram_waves[i],
+                      "ms": inf.gram_ms[i], "fixup_ms": inf.gram_fixup_ms[i],
                       "work": dict(zip(("tests", "lobes", "cols", "pairs", "terms"), list(inf.gram_work[i])))}
                      for i in range(inf.n_gram_launches)],
         }
 
-    def timings(self) -> dict:
-        """Refresh and return info (synchronizes the timing events)."""
+    def timings(self, stream=None) -> dict:
+        """Wait for the prepare's stream, then refresh and return info."""
+        torch = _torch()
+        s = torch.cuda.current_stream() if stream is None else stream
+        s.synchronize()
         self.info = self._info()
         return self.info
 
@@ -298,6 +302,15 @@ def band_count(n_scan: int, step: float, band) -> int:
     n = ctypes.c_int()
     _check(_L.dsp_band_count(ctypes.byref(scan), _dptr(bd), ctypes.byref(n)))
     return n.value
+
+
+def sincos_host(x) -> Tuple[np.ndarray, np.ndarray]:
+    """The library's FP64 sine and cosine (the kernels' source) on the host."""
+    xx = np.ascontiguousarray(np.asarray(x, dtype=np.float64).reshape(-1))
+    s = np.zeros_like(xx)
+    c = np.zeros_like(xx)
+    _check(_L.dsp_sincos_host(_dptr(xx), xx.shape[0], _dptr(s), _dptr(c)))
+    return s, c
 
 
 def chi_host(optics, k) -> np.ndarray:

@@ -50,8 +50,9 @@ class InfoC(ctypes.Structure):
         ("upsampling", ctypes.c_int), ("n_scan", ctypes.c_int), ("n_tiles", ctypes.c_int),
         ("alias_hist", ctypes.c_int * 10), ("scale", ctypes.c_double), ("g_bytes", ctypes.c_double),
         ("lobes", ctypes.c_double), ("host_ms", ctypes.c_double), ("stage_ms", ctypes.c_double * 4),
+        ("timing_ready", ctypes.c_int),
         ("n_gram_launches", ctypes.c_int), ("gram_nj", ctypes.c_int * 16), ("gram_tiles", ctypes.c_int * 16),
-        ("gram_ms", ctypes.c_double * 16), ("gram_work", (ctypes.c_double * 5) * 16),
+        ("gram_waves", ctypes.c_int * 16), ("gram_ms", ctypes.c_double * 16), ("gram_fixup_ms", ctypes.c_double * 16), ("gram_work", (ctypes.c_double * 5) * 16),
     ]
 
 
@@ -59,7 +60,7 @@ class InfoC(ctypes.Structure):
 EXPORTS = (
     "dsp_prepare", "dsp_solve", "dsp_scatter", "dsp_ssb", "dsp_info", "dsp_export_system", "dsp_alias_table",
     "dsp_destroy", "dsp_last_error", "dsp_geometry_counts", "dsp_alias_geometry", "dsp_active_bf",
-    "dsp_band_count", "dsp_chi_host",
+    "dsp_band_count", "dsp_chi_host", "dsp_sincos_host",
 )
 
 _P = ctypes.c_void_p
@@ -108,4 +109,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsp_band_count.argtypes = [ctypes.POINTER(ScanC), _DP, ctypes.POINTER(_I)]
     lib.dsp_chi_host.restype = _I
     lib.dsp_chi_host.argtypes = [ctypes.POINTER(OpticsC), _DP, _I, _DP]
+    lib.dsp_sincos_host.restype = _I
+    lib.dsp_sincos_host.argtypes = [_DP, _I, _DP, _DP]
     return lib

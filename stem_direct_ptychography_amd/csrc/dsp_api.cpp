@@ -18,10 +18,14 @@
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
 using namespace dsp;
+
+// Gram launch size: resident waves (from the kernel's occupancy) times this.
+constexpr int GRAM_ROUNDS = 4;
 
 namespace {
 
@@ -138,9 +142,11 @@ ApertureDev make_aperture_dev(const dsp_optics *o) {
         const double rin = std::max(0.0, a.kc - h);
         a.rin2 = rin * rin;
         a.rout2 = (a.kc + h) * (a.kc + h);
+        a.rlim2 = a.rout2;
     } else {
         a.rin2 = a.kc * a.kc;
         a.rout2 = a.kc * a.kc;
+        a.rlim2 = std::nextafter(a.rout2, HUGE_VAL);   // d2 <= kc^2  <=>  d2 < next double
     }
     return a;
 }
@@ -380,11 +386,113 @@ dsp_status build_active(const double *k, const double *w, int n_bf, const dsp_op
         p.ky = ky;
         p.kx = kx;
         p.w = wi;
+        p.sw = std::sqrt(wi);
         p.goff = (long long)i * plane;
         as.idx.push_back(i);
         as.pix.push_back(p);
         as.scale += wi;
     }
+    return DSP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// stream-K plan of one Gram launch
+// ---------------------------------------------------------------------------
+// Estimated cost of a tile: per pixel a fixed part plus the support tests of
+// its slots, plus the lobes its wave evaluates.  A slot's lobes are non-zero
+// where the pixel disk overlaps the disk moved by -/+Q: two lenses of area
+// 2 R^2 acos(D / 2R) - (D / 2) sqrt(4 R^2 - D^2) at D = |Q| (tile centre).
+double tile_cost(const GramTile &t, const Geometry &g, double ra, int n_pix) {
+    constexpr double C_PIX = 30.0, C_SLOT = 10.0, C_LOBE = 80.0;
+    unsigned used = 0;
+    for (int l = 0; l < 64; ++l)
+        if (t.qidx[l] >= 0) used |= t.mask[l];
+    const double disk = M_PI * ra * ra;
+    double lobes = 0.0;
+    for (int s = 0; s < t.nj; ++s) {
+        if (!((used >> s) & 1u)) continue;
+        const double qy = (t.yh0 + 1.5 + (double)t.jy[s] * g.N) * g.dq;
+        const double qx = (t.ix0 + 7.5 + (double)t.jx[s] * g.N) * g.dq;
+        const double D = std::hypot(qy, qx);
+        if (D >= 2.0 * ra) continue;
+        const double lens = 2.0 * ra * ra * std::acos(D / (2.0 * ra)) - 0.5 * D * std::sqrt(4.0 * ra * ra - D * D);
+        lobes += 2.0 * lens / disk * n_pix;
+    }
+    return n_pix * (C_PIX + C_SLOT * t.nj) + C_LOBE * lobes;
+}
+
+struct StreamKPlan {
+    std::vector<long long> wbegin;   // [W + 1]
+    std::vector<int> seg_off;        // [W]
+    std::vector<int> seg_first;      // [T + 1]
+    int n_segs = 0;
+};
+
+// Split the tiles x pixels iteration space into n_waves contiguous ranges of
+// equal estimated cost (the cost of a tile spread evenly over its pixels),
+// then number each wave's tile segments.
+void plan_stream_k(const std::vector<double> &cost, int n_pix, int n_waves, StreamKPlan &pl) {
+    const int T = (int)cost.size();
+    std::vector<double> cum(T + 1, 0.0);
+    for (int t = 0; t < T; ++t) cum[t + 1] = cum[t] + std::max(cost[t], 1e-30);
+    const long long total_it = (long long)T * n_pix;
+    const int W = n_waves;
+    pl.wbegin.assign(W + 1, 0);
+    pl.wbegin[W] = total_it;
+    int t = 0;
+    for (int w = 1; w < W; ++w) {
+        const double target = cum[T] * ((double)w / W);
+        while (t < T - 1 && cum[t + 1] <= target) ++t;
+        double frac = (target - cum[t]) / (cum[t + 1] - cum[t]);
+        frac = std::min(1.0, std::max(0.0, frac));
+        long long b = (long long)t * n_pix + (long long)std::floor(frac * n_pix);
+        b = std::min(total_it, std::max(pl.wbegin[w - 1], b));
+        pl.wbegin[w] = b;
+    }
+    pl.seg_off.assign(W, 0);
+    pl.seg_first.assign(T + 1, -1);
+    int ns = 0;
+    for (int w = 0; w < W; ++w) {
+        pl.seg_off[w] = ns;
+        long long it = pl.wbegin[w];
+        const long long e = pl.wbegin[w + 1];
+        while (it < e) {
+            const int tt = (int)(it / n_pix);
+            if (pl.seg_first[tt] < 0) pl.seg_first[tt] = ns;
+            it = std::min(e, (long long)(tt + 1) * n_pix);
+            ++ns;
+        }
+    }
+    pl.seg_first[T] = ns;
+    pl.n_segs = ns;
+}
+
+// (cos, sin)(j pi / 32), j = 0..63, rounded from long double.
+void trig_table_host(double2 *T) {
+    const long double pi = 3.141592653589793238462643383279502884L;
+    for (int j = 0; j < TRIG_N; ++j) {
+        const long double a = pi * j / 32.0L;
+        T[j] = make_double2((double)std::cos(a), (double)std::sin(a));
+    }
+}
+
+// The table on a device: uploaded once per device, kept until the process ends.
+dsp_status trig_table_device(int device, const double2 **out) {
+    static std::mutex mu;
+    static std::map<int, double2 *> tables;
+    std::lock_guard<std::mutex> lock(mu);
+    auto f = tables.find(device);
+    if (f != tables.end()) {
+        *out = f->second;
+        return DSP_OK;
+    }
+    double2 host[TRIG_N];
+    trig_table_host(host);
+    double2 *d = nullptr;
+    HIP_TRY(hipMalloc((void **)&d, sizeof host));
+    HIP_TRY(hipMemcpy(d, host, sizeof host, hipMemcpyHostToDevice));
+    tables[device] = d;
+    *out = d;
     return DSP_OK;
 }
 
@@ -431,9 +539,15 @@ struct dsp_handle {
     double2 *d_c = nullptr;
     bool timing = false;
     bool count_work = false;
+    hipStream_t stream = nullptr;             // the prepare's stream
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     std::vector<int> gram_order;              // launch order of the tile groups
-    std::vector<hipEvent_t> gram_ev;          // two per launch (timing)
+    std::vector<hipEvent_t> gram_ev;          // three per launch: start, Gram done, fixup done (timing)
+    std::vector<int> sk_waves;                // waves of each group's Gram launch
+    std::vector<long long> sk_wbegin;         // stream-K tables (host copies kept for the async upload)
+    std::vector<int> sk_int;
+    long long *d_sk_wbegin = nullptr;
+    int *d_sk_int = nullptr;
     unsigned long long *d_work = nullptr;     // [tile][5] (DSP_FLAG_COUNT_WORK)
 
     ~dsp_handle() {
@@ -453,6 +567,8 @@ struct dsp_handle {
         for (auto &e : gram_ev)
             if (e) hipEventDestroy(e);
         hipFree(d_work);
+        hipFree(d_sk_wbegin);
+        hipFree(d_sk_int);
     }
 };
 
@@ -536,6 +652,14 @@ dsp_status dsp_chi_host(const dsp_optics *optics, const double *k_host, int n, d
     return DSP_OK;
 }
 
+dsp_status dsp_sincos_host(const double *x_host, int n, double *sin_out, double *cos_out) {
+    if (n < 0 || (n > 0 && (!x_host || !sin_out || !cos_out))) return fail(DSP_EINVAL, "bad arguments");
+    double2 T[TRIG_N];
+    trig_table_host(T);
+    for (int i = 0; i < n; ++i) sincos_tab(x_host[i], T, sin_out[i], cos_out[i]);
+    return DSP_OK;
+}
+
 dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
                        const dsp_scan *scan, const dsp_optics *optics, const dsp_prepare_opts *opts, void *hip_stream,
                        dsp_handle **out) {
@@ -557,6 +681,7 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     h->n_bf = n_bf;
     h->timing = (opts->flags & DSP_FLAG_TIMING) != 0;
     h->count_work = (opts->flags & DSP_FLAG_COUNT_WORK) != 0;
+    h->stream = stream;
     if ((st = build_geometry(scan, optics, opts->upsampling, h->geo))) return st;
     Geometry &g = h->geo;
     const int max_nj = h->method == DSP_PHASE ? MAX_NJ_PHASE : MAX_NJ_COMPLEX;
@@ -638,22 +763,77 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     gp.sys = h->d_sys;
     gp.a_max = am;
     gp.D = h->D;
+    if ((st = trig_table_device(h->device, &gp.trig))) return st;
+    // stream-K plan per tile group (one launch per alias-slot count)
+    const int n_groups = (int)h->tg.group_nj.size();
+    int n_cu = 0;
+    HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device));
+    const double ra = std::sqrt(apd.rlim2);
+    std::vector<StreamKPlan> plans(n_groups);
+    h->sk_waves.assign(n_groups, 0);
+    size_t max_partial = 0, n_wb = 0, n_int = 0;
+    for (int gi = 0; gi < n_groups; ++gi) {
+        const int nj = h->tg.group_nj[gi], nt = h->tg.group_n[gi];
+        int bpc = 0;
+        HIP_TRY(gram_occupancy(nj, h->method, &bpc));
+        bpc = std::max(1, bpc);
+        const long long total_it = (long long)nt * gp.n_pix;
+        const int W = (int)std::max(1LL, std::min((long long)bpc * n_cu * GRAM_ROUNDS, total_it / 64));
+        std::vector<double> cost(nt);
+        for (int t = 0; t < nt; ++t) cost[t] = tile_cost(h->tg.tiles[h->tg.group_off[gi] + t], g, ra, gp.n_pix);
+        plan_stream_k(cost, gp.n_pix, W, plans[gi]);
+        h->sk_waves[gi] = W;
+        max_partial = std::max(max_partial, (size_t)plans[gi].n_segs * gram_nacc(nj, h->method) * 64);
+        n_wb += W + 1;
+        n_int += W + nt + 1;
+    }
+    h->sk_wbegin.clear();
+    h->sk_int.clear();
+    h->sk_wbegin.reserve(n_wb);
+    h->sk_int.reserve(n_int);
+    std::vector<size_t> wb_off(n_groups), so_off(n_groups), sf_off(n_groups);
+    for (int gi = 0; gi < n_groups; ++gi) {
+        wb_off[gi] = h->sk_wbegin.size();
+        h->sk_wbegin.insert(h->sk_wbegin.end(), plans[gi].wbegin.begin(), plans[gi].wbegin.end());
+        so_off[gi] = h->sk_int.size();
+        h->sk_int.insert(h->sk_int.end(), plans[gi].seg_off.begin(), plans[gi].seg_off.end());
+        sf_off[gi] = h->sk_int.size();
+        h->sk_int.insert(h->sk_int.end(), plans[gi].seg_first.begin(), plans[gi].seg_first.end());
+    }
+    if ((st = dev_alloc(&h->d_sk_wbegin, h->sk_wbegin.size())) || (st = dev_alloc(&h->d_sk_int, h->sk_int.size())))
+        return st;
+    HIP_TRY(hipMemcpyAsync(h->d_sk_wbegin, h->sk_wbegin.data(), h->sk_wbegin.size() * sizeof(long long),
+                           hipMemcpyHostToDevice, stream));
+    HIP_TRY(hipMemcpyAsync(h->d_sk_int, h->sk_int.data(), h->sk_int.size() * sizeof(int), hipMemcpyHostToDevice,
+                           stream));
+    // partial sums live only for the Gram stage (stream-ordered)
+    double *d_partial = nullptr;
+    HIP_TRY(hipMallocAsync((void **)&d_partial, std::max<size_t>(1, max_partial) * sizeof(double), stream));
+
     // largest groups first
-    std::vector<int> order(h->tg.group_nj.size());
-    for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+    std::vector<int> order(n_groups);
+    for (int i = 0; i < n_groups; ++i) order[i] = i;
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return h->tg.group_n[a] > h->tg.group_n[b]; });
     h->gram_order = order;
     if (h->timing) {
-        h->gram_ev.assign(2 * order.size(), nullptr);
+        h->gram_ev.assign(3 * order.size(), nullptr);
         for (auto &e : h->gram_ev) HIP_TRY(hipEventCreate(&e));
     }
     for (size_t oi = 0; oi < order.size(); ++oi) {
         const int gi = order[oi];
         gp.tiles = h->d_tiles + h->tg.group_off[gi];
-        if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[2 * oi], stream));
-        HIP_TRY(launch_gram(gp, h->tg.group_nj[gi], h->method, h->tg.group_n[gi], stream));
-        if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[2 * oi + 1], stream));
+        gp.wbegin = h->d_sk_wbegin + wb_off[gi];
+        gp.seg_off = h->d_sk_int + so_off[gi];
+        gp.seg_first = h->d_sk_int + sf_off[gi];
+        gp.partial = d_partial;
+        gp.n_waves = h->sk_waves[gi];
+        if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[3 * oi], stream));
+        HIP_TRY(launch_gram(gp, h->tg.group_nj[gi], h->method, gp.n_waves, stream));
+        if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[3 * oi + 1], stream));
+        HIP_TRY(launch_gram_fixup(gp, h->tg.group_nj[gi], h->method, h->tg.group_n[gi], stream));
+        if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[3 * oi + 2], stream));
     }
+    HIP_TRY(hipFreeAsync(d_partial, stream));
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[2], stream));
 
     if (h->method == DSP_PHASE) {
@@ -780,10 +960,18 @@ dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out) {
         const int gi = h->gram_order[oi];
         out->gram_nj[oi] = h->tg.group_nj[gi];
         out->gram_tiles[oi] = h->tg.group_n[gi];
+        out->gram_waves[oi] = h->sk_waves[gi];
     }
     if ((h->timing && h->ev[3]) || (h->count_work && h->d_work)) HIP_TRY(hipSetDevice(h->device));
+    // timings are filled once the prepare's last event has completed (no wait)
+    bool timing_done = false;
     if (h->timing && h->ev[3]) {
-        HIP_TRY(hipEventSynchronize(h->ev[3]));
+        const hipError_t q = hipEventQuery(h->ev[3]);
+        if (q != hipSuccess && q != hipErrorNotReady) HIP_TRY(q);
+        timing_done = q == hipSuccess;
+    }
+    out->timing_ready = timing_done ? 1 : 0;
+    if (timing_done) {
         float ms;
         HIP_TRY(hipEventElapsedTime(&ms, h->ev[0], h->ev[1]));
         out->stage_ms[0] = ms;
@@ -794,11 +982,15 @@ dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out) {
         HIP_TRY(hipEventElapsedTime(&ms, h->ev[0], h->ev[3]));
         out->stage_ms[3] = ms;
         for (int oi = 0; oi < out->n_gram_launches; ++oi) {
-            HIP_TRY(hipEventElapsedTime(&ms, h->gram_ev[2 * oi], h->gram_ev[2 * oi + 1]));
+            HIP_TRY(hipEventElapsedTime(&ms, h->gram_ev[3 * oi], h->gram_ev[3 * oi + 1]));
             out->gram_ms[oi] = ms;
+            HIP_TRY(hipEventElapsedTime(&ms, h->gram_ev[3 * oi + 1], h->gram_ev[3 * oi + 2]));
+            out->gram_fixup_ms[oi] = ms;
         }
     }
     if (h->count_work && h->d_work) {
+        // the counts are read with a blocking copy (instrumentation only)
+        HIP_TRY(hipStreamSynchronize(h->stream));
         std::vector<unsigned long long> wk(h->tg.tiles.size() * 5, 0ull);
         HIP_TRY(hipMemcpy(wk.data(), h->d_work, wk.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
         double total = 0.0;
@@ -926,6 +1118,9 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
     sp.S_out = (double2 *)S_out_c128_dev;
     sp.N_out = norm_out_dev;
     sp.partial = d_part;
+    int device = 0;
+    HIP_TRY(hipGetDevice(&device));
+    if ((st = trig_table_device(device, &sp.trig))) return st;
     HIP_TRY(launch_ssb(sp, n_tiles, stream));
     std::vector<double> E(B + 1, 0.0);
     if (agreement_out_host) {

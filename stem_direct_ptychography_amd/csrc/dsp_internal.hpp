@@ -43,15 +43,51 @@ __host__ __device__ constexpr int tri_size(int n) { return n * (n + 1) / 2; }
 // device tables
 // ---------------------------------------------------------------------------
 // One active bright-field pixel; 64-byte records so a wave reads one with a
-// single scalar load.
+// single scalar load.  The weight enters the Gram through sqrt(w): with
+// u = sqrt(w) T and g' = sqrt(w) g, u^H u = T^H W T, u^H g' = T^H W g and
+// |g'|^2 = g^H W g, so the per-pixel update needs no weight products.
 struct alignas(64) PixelRec {
     double ky, kx;     // 1/A, scan frame
-    double w;          // weight
-    double a0;         // aperture a(k)            (pixel-terms kernel)
+    double amp0;       // sqrt(w) a(k)              (pixel-terms kernel)
+    double sw;         // sqrt(w)
     double chi0;       // chi(k) of the prepare's optics (pixel-terms kernel)
     long long goff;    // element offset of the pixel's plane in G
-    double pad[2];
+    double w;          // weight
+    double a0;         // aperture a(k)             (pixel-terms kernel)
 };
+
+// ---------------------------------------------------------------------------
+// FP64 sine and cosine for the transfer's phase factors
+// ---------------------------------------------------------------------------
+// Table-driven: x = n pi/32 + r with n = rint(32 x / pi) and |r| <= pi/64, by
+// a Cody-Waite reduction (W. J. Cody and W. Waite, "Software Manual for the
+// Elementary Functions", 1980) with a two-part constant P1 + P2 = pi/32
+// (P1 = double(pi)/32, P2 the rest to 1e-34).  The first step x - n P1 is
+// exact in one FMA for |x| < 2^30: both terms are multiples of 2^-57 (or x
+// is below 2^-4 and n is 0 or +-1) and the difference is below 2^-4.  Then the
+// Taylor series of sin r to r^7 and cos r to r^8 (truncation below 5e-18 at
+// |r| = pi/64) and the angle addition with T[n mod 64] = (cos, sin)(n pi/32).
+// Absolute error about 3e-16.  Branch-free; T is 64 double2 (1 KB).
+constexpr int TRIG_N = 64;
+
+__host__ __device__ inline void sincos_tab(double x, const double2 *__restrict__ T, double &s, double &c) {
+    const double n = rint(x * 10.185916357881302);             // 32 / pi
+    double r = fma(-n, 0.09817477042468103, x);                 // P1
+    r = fma(-n, 3.827021247335479e-18, r);                      // P2
+    const double z = r * r;
+    // sin r = r + r z (-1/3! + z (1/5! + z (-1/7!)))
+    double ps = fma(-1.9841269841269841270e-04, z, 8.3333333333333333333e-03);
+    ps = fma(ps, z, -1.6666666666666666667e-01);
+    const double sr = fma(r * z, ps, r);
+    // cos r = 1 + z (-1/2! + z (1/4! + z (-1/6! + z (1/8!))))
+    double pc = fma(2.4801587301587301587e-05, z, -1.3888888888888888889e-03);
+    pc = fma(pc, z, 4.1666666666666666667e-02);
+    pc = fma(pc, z, -0.5);
+    const double cr = fma(z, pc, 1.0);
+    const double2 t = T[((int)n) & (TRIG_N - 1)];
+    s = fma(t.y, cr, t.x * sr);
+    c = fma(t.x, cr, -(t.y * sr));
+}
 
 constexpr int TILE_Y = 4;
 constexpr int TILE_X = 16;
@@ -87,9 +123,17 @@ struct ApertureDev {
     double inv_dk;   // 1 / dk
     double rin2;     // (kc - dk/2)^2 : a == 1 inside (soft)
     double rout2;    // (kc + dk/2)^2 : a == 0 outside (soft); kc^2 (hard)
+    double rlim2;    // support is |k|^2 < rlim2: rout2 (soft, strict) or the
+                     // next double above kc^2 (hard, |k|^2 <= kc^2)
     int soft;
 };
 
+// Stream-K decomposition of one Gram launch: the launch's tiles x pixels form
+// one linear iteration space (tile-major); wave w takes the contiguous range
+// [wbegin[w], wbegin[w+1]) and writes one partial sum per tile segment it
+// touches, numbered from seg_off[w].  Tile t's segments are seg_first[t] ..
+// seg_first[t+1]-1 (consecutive, in iteration order); the fixup adds them in
+// that order, so the result does not depend on scheduling.
 struct GramParams {
     const float2 *G;
     const PixelRec *pix;
@@ -101,6 +145,12 @@ struct GramParams {
     OpticsDev op;
     double2 *sys;     // [n_q][tri_size(D)] packed augmented systems, slot coordinates
     int a_max, D;
+    const long long *wbegin;   // [n_waves + 1]
+    const int *seg_off;        // [n_waves]
+    const int *seg_first;      // [n_tiles + 1]
+    double *partial;           // [n_segments][NACC][64]
+    int n_waves;
+    const double2 *trig;       // [TRIG_N] (cos, sin)(j pi / 32)
 };
 
 struct SsbParams {
@@ -119,6 +169,7 @@ struct SsbParams {
     double2 *S_out;          // [B][N][nh] or null
     double *N_out;           // [B][N][nh] or null
     double *partial;         // [n_tiles][B + 1]
+    const double2 *trig;     // [TRIG_N] (cos, sin)(j pi / 32)
 };
 
 }  // namespace dsp

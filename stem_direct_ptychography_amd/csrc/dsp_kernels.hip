@@ -56,7 +56,9 @@ __global__ void pixel_terms_kernel(PixelRec *pix, int n_pix, ApertureDev ap, Opt
     if (chi_tab) {
         chi_tab[p] = c;
     } else {
-        pix[p].a0 = aperture_at(ap, d2);
+        const double a0 = aperture_at(ap, d2);
+        pix[p].a0 = a0;
+        pix[p].amp0 = pix[p].sw * a0;
         pix[p].chi0 = c;
     }
 }
@@ -96,138 +98,22 @@ __device__ __forceinline__ void acc_get(const double *acc, int c, int d, double 
     }
 }
 
-template <int NJ, int METHOD, int P>
-__global__ __launch_bounds__(64 * P) void gram_kernel(GramParams prm) {
+// Write one frequency's augmented system (lane = frequency) from its sums.
+template <int NJ, int METHOD>
+__device__ __forceinline__ void write_system(const double *acc, unsigned mask, int qi, const GramParams &prm) {
     using Sh = GramShape<NJ, METHOD>;
     constexpr int NC = Sh::NC;
-    constexpr int D = Sh::D;
-    constexpr int NACC = Sh::NACC;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const GramTile *tile = prm.tiles + blockIdx.x;
-    const int yh = tile->yh0 + (lane >> 4);
-    const int ix = tile->ix0 + (lane & 15);
-    const int qi = tile->qidx[lane];
-    const bool valid = qi >= 0;
-    const unsigned mask = valid ? (unsigned)tile->mask[lane] : 0u;
-    const int iy = yh < 0 ? yh + prm.N : yh;
-    const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
-
-    double Qy[NJ], Qx[NJ];
-    bool act[NJ];
-#pragma unroll
-    for (int s = 0; s < NJ; ++s) {
-        Qy[s] = (double)(yh + (int)tile->jy[s] * prm.N) * prm.dq;
-        Qx[s] = (double)(ix + (int)tile->jx[s] * prm.N) * prm.dq;
-        act[s] = (mask >> s) & 1u;
-    }
-
-    double acc[NACC];
-#pragma unroll
-    for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
-
-    const ApertureDev ap = prm.ap;
-    const double lam = prm.op.lam, tau_y = prm.op.tau_y, tau_x = prm.op.tau_x;
-
-    for (int p = wave; p < prm.n_pix; p += P) {
-        const PixelRec *pr = prm.pix + p;
-        const double ky = pr->ky, kx = pr->kx, w = pr->w, a0 = pr->a0, chi0 = pr->chi0;
-        float2 gv = make_float2(0.f, 0.f);
-        if (valid) gv = prm.G[pr->goff + lane_off];
-        const double gr = (double)gv.x, gi = (double)gv.y;
-
-        double tr[NC], ti[NC];
-        bool nz[NC];
-#pragma unroll
-        for (int s = 0; s < NJ; ++s) {
-            const double dy = ky - Qy[s], dx = kx - Qx[s];
-            const double ey = ky + Qy[s], ex = kx + Qx[s];
-            const double dm2 = fma(dy, dy, dx * dx);
-            const double dp2 = fma(ey, ey, ex * ex);
-            const bool zl = act[s] && inside_support(ap, dm2);
-            const bool zr = act[s] && inside_support(ap, dp2);
-            double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
-            if (zl) {
-                const double amp = a0 * lobe_aperture(ap, dm2);
-                const double cm = chi_poly(prm.op.chi_c, fma(lam, dx, tau_x), fma(lam, dy, tau_y));
-                double sn, cs;
-                sincos(chi0 - cm, &sn, &cs);
-                Lr = amp * cs;
-                Li = amp * sn;
-            }
-            if (zr) {
-                const double amp = a0 * lobe_aperture(ap, dp2);
-                const double cp = chi_poly(prm.op.chi_c, fma(lam, ex, tau_x), fma(lam, ey, tau_y));
-                double sn, cs;
-                sincos(cp - chi0, &sn, &cs);
-                Rr = amp * cs;
-                Ri = amp * sn;
-            }
-            if (METHOD == 0) {
-                tr[s] = Ri - Li;   // T_phi = i (L - R)
-                ti[s] = Lr - Rr;
-                nz[s] = zl || zr;
-            } else {
-                tr[s] = Lr;
-                ti[s] = Li;
-                nz[s] = zl;
-                tr[NJ + s] = Rr;
-                ti[NJ + s] = Ri;
-                nz[NJ + s] = zr;
-            }
-        }
-
-        bool any[NC];
-#pragma unroll
-        for (int c = 0; c < NC; ++c) any[c] = wave_any(nz[c]);
-
-        const double gwr = w * gr, gwi = w * gi;
-        acc[NC] = fma(gr, gwr, fma(gi, gwi, acc[NC]));   // signal power
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            if (!any[c]) continue;
-            const double twr = w * tr[c], twi = w * ti[c];
-            acc[c] = fma(tr[c], twr, fma(ti[c], twi, acc[c]));
-            // right side <col c, g>
-            acc[Sh::re(c, NC)] = fma(tr[c], gwr, fma(ti[c], gwi, acc[Sh::re(c, NC)]));
-            acc[Sh::im(c, NC)] = fma(tr[c], gwi, fma(-ti[c], gwr, acc[Sh::im(c, NC)]));
-#pragma unroll
-            for (int d = c + 1; d < NC; ++d) {
-                if (!any[d]) continue;
-                const double uwr = w * tr[d], uwi = w * ti[d];
-                acc[Sh::re(c, d)] = fma(tr[c], uwr, fma(ti[c], uwi, acc[Sh::re(c, d)]));
-                acc[Sh::im(c, d)] = fma(tr[c], uwi, fma(-ti[c], uwr, acc[Sh::im(c, d)]));
-            }
-        }
-    }
-
-    // ---- add the P waves' sums in a fixed order through LDS ----
-    if (P > 1) {
-        extern __shared__ double lds[];
-        for (int wv = 1; wv < P; ++wv) {
-            if (wave == wv) {
-#pragma unroll
-                for (int i = 0; i < NACC; ++i) lds[i * 64 + lane] = acc[i];
-            }
-            __syncthreads();
-            if (wave == 0) {
-#pragma unroll
-                for (int i = 0; i < NACC; ++i) acc[i] += lds[i * 64 + lane];
-            }
-            __syncthreads();
-        }
-    }
-    if (wave != 0 || !valid) return;
-
-    // ---- write the frequency's system in slot coordinates ----
     const int Dout = prm.D;
     const int am = prm.a_max;
     double2 *out = prm.sys + (size_t)qi * (size_t)tri_size(Dout);
     for (int e = 0; e < tri_size(Dout); ++e) out[e] = make_double2(0.0, 0.0);
+    bool act[NJ];
     int rank[NJ];
 #pragma unroll
-    for (int s = 0; s < NJ; ++s) rank[s] = __popc(mask & ((1u << s) - 1u));
+    for (int s = 0; s < NJ; ++s) {
+        act[s] = (mask >> s) & 1u;
+        rank[s] = __popc(mask & ((1u << s) - 1u));
+    }
     const int gcol = Dout - 1;
     out[tri_idx(gcol, gcol, Dout)] = make_double2(acc[NC], 0.0);
 
@@ -283,6 +169,194 @@ __global__ __launch_bounds__(64 * P) void gram_kernel(GramParams prm) {
     }
 }
 
+// Waves per SIMD the compiler must fit (caps the registers per lane).
+template <int NJ, int METHOD>
+struct GramWaves {
+    static constexpr int value = METHOD == 0 ? (NJ <= 2 ? 4 : (NJ <= 6 ? 2 : 1)) : (NJ <= 1 ? 4 : (NJ <= 3 ? 2 : 1));
+};
+
+// Pixel records are read through the constant address space so that the
+// wave-uniform fields land in scalar registers (one scalar load per field).
+typedef const __attribute__((address_space(4))) PixelRec ConstPixel;
+
+// One lobe of the transfer at the pixel (chi0 = chi(k), amp0 = sqrt(w) a(k))
+// and the displaced point k' = k -/+ Q given as e = k' (1/A, scan frame) with
+// |e|^2 = d2 inside the support:
+//   value = amp0 a(k') exp(i sgn (chi0 - chi(k'))), sgn = +1 (L), -1 (R).
+// a(k') = 1 except in the soft edge ring; the square root runs only when some
+// lane of the wave is in the ring.
+__device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, double ey, double ex, double d2,
+                                     double chi0, double amp0, double sgn, double &re, double &im) {
+    const double c1 = chi_poly(prm.op.chi_c, fma(prm.op.lam, ex, prm.op.tau_x), fma(prm.op.lam, ey, prm.op.tau_y));
+    double sn, cs;
+    sincos_tab(sgn * (chi0 - c1), T, sn, cs);
+    double amp = amp0;
+    const bool ring = d2 > prm.ap.rin2;
+    if (wave_any(ring)) {
+        if (ring) amp *= fma(prm.ap.kc - sqrt(d2), prm.ap.inv_dk, 0.5);
+    }
+    re = amp * cs;
+    im = amp * sn;
+}
+
+// Transfer + weighted augmented Gram over one wave's stream-K range.
+// METHOD 0 (phase): columns T_phi(slot 0..NJ-1), then g.
+// METHOD 1 (complex): columns L(slot 0..NJ-1), R(slot 0..NJ-1), then g; the
+// write-out turns them into [T_A, T_phi] (T_A = L + R, T_phi = i (L - R)),
+// which keeps the per-pixel update to the lobes actually present.
+// Lane = frequency of the tile; pixel records are wave-uniform scalar loads.
+// While pixel p is used, G for p + 1 is in flight (its plane offset was read
+// one pixel earlier) and the record of p + 1 and the offset of p + 2 load.
+template <int NJ, int METHOD>
+__global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kernel(GramParams prm) {
+    using Sh = GramShape<NJ, METHOD>;
+    constexpr int NC = Sh::NC;
+    constexpr int NACC = Sh::NACC;
+
+    __shared__ double2 T[TRIG_N];
+    const int lane = threadIdx.x;
+    T[lane] = prm.trig[lane];
+    __syncthreads();
+
+    const int wv = blockIdx.x;
+    const long long n_pix = prm.n_pix;
+    long long it = prm.wbegin[wv];
+    const long long end = prm.wbegin[wv + 1];
+    int seg = prm.seg_off[wv];
+    ConstPixel *pix = (ConstPixel *)prm.pix;
+    const float2 *__restrict__ G = prm.G;
+    const double rlim2 = prm.ap.rlim2;
+
+    while (it < end) {
+        const int t = (int)(it / n_pix);
+        const int p0 = (int)(it - (long long)t * n_pix);
+        const int p1 = (int)((end - it) < (n_pix - p0) ? p0 + (end - it) : n_pix);
+        const GramTile *tile = prm.tiles + t;
+        const int yh = tile->yh0 + (lane >> 4);
+        const int ix = tile->ix0 + (lane & 15);
+        const bool valid = tile->qidx[lane] >= 0;
+        const unsigned mask = valid ? (unsigned)tile->mask[lane] : 0u;
+        const int iy = yh < 0 ? yh + prm.N : yh;
+        const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
+
+        double Qy[NJ], Qx[NJ];
+        bool act[NJ];
+#pragma unroll
+        for (int s = 0; s < NJ; ++s) {
+            Qy[s] = (double)(yh + (int)tile->jy[s] * prm.N) * prm.dq;
+            Qx[s] = (double)(ix + (int)tile->jx[s] * prm.N) * prm.dq;
+            act[s] = (mask >> s) & 1u;
+        }
+
+        double acc[NACC];
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
+
+        double ky = pix[p0].ky, kx = pix[p0].kx, amp0 = pix[p0].amp0, sw = pix[p0].sw, chi0 = pix[p0].chi0;
+        float2 gv = G[pix[p0].goff + lane_off];
+        long long goff1 = pix[p0 + 1 < p1 ? p0 + 1 : p0].goff;
+        for (int p = p0; p < p1; ++p) {
+            const int pn = p + 1 < p1 ? p + 1 : p;
+            const int pnn = pn + 1 < p1 ? pn + 1 : pn;
+            const float2 ngv = G[goff1 + lane_off];
+            const long long goff2 = pix[pnn].goff;
+            const double nky = pix[pn].ky, nkx = pix[pn].kx, namp0 = pix[pn].amp0, nsw = pix[pn].sw,
+                         nchi0 = pix[pn].chi0;
+
+            const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
+            acc[NC] = fma(gr, gr, fma(gi, gi, acc[NC]));   // signal power w |g|^2
+
+            double tr[NC], ti[NC];
+            bool nz[NC];
+#pragma unroll
+            for (int s = 0; s < NJ; ++s) {
+                const double ey = ky - Qy[s], ex = kx - Qx[s];
+                const double fy = ky + Qy[s], fx = kx + Qx[s];
+                const double dm2 = fma(ey, ey, ex * ex);
+                const double dp2 = fma(fy, fy, fx * fx);
+                const bool zl = act[s] && dm2 < rlim2;
+                const bool zr = act[s] && dp2 < rlim2;
+                double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
+                if (zl) lobe(prm, T, ey, ex, dm2, chi0, amp0, 1.0, Lr, Li);
+                if (zr) lobe(prm, T, fy, fx, dp2, chi0, amp0, -1.0, Rr, Ri);
+                if (METHOD == 0) {
+                    tr[s] = Ri - Li;   // T_phi = i (L - R)
+                    ti[s] = Lr - Rr;
+                    nz[s] = zl || zr;
+                } else {
+                    tr[s] = Lr;
+                    ti[s] = Li;
+                    nz[s] = zl;
+                    tr[NJ + s] = Rr;
+                    ti[NJ + s] = Ri;
+                    nz[NJ + s] = zr;
+                }
+            }
+
+            bool any[NC];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) any[c] = wave_any(nz[c]);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if (!any[c]) continue;
+                acc[c] = fma(tr[c], tr[c], fma(ti[c], ti[c], acc[c]));
+                // right side <col c, g> = conj(t_c) g
+                acc[Sh::re(c, NC)] = fma(tr[c], gr, fma(ti[c], gi, acc[Sh::re(c, NC)]));
+                acc[Sh::im(c, NC)] = fma(tr[c], gi, fma(-ti[c], gr, acc[Sh::im(c, NC)]));
+#pragma unroll
+                for (int d = c + 1; d < NC; ++d) {
+                    if (!any[d]) continue;
+                    acc[Sh::re(c, d)] = fma(tr[c], tr[d], fma(ti[c], ti[d], acc[Sh::re(c, d)]));
+                    acc[Sh::im(c, d)] = fma(tr[c], ti[d], fma(-ti[c], tr[d], acc[Sh::im(c, d)]));
+                }
+            }
+            ky = nky;
+            kx = nkx;
+            amp0 = namp0;
+            sw = nsw;
+            chi0 = nchi0;
+            gv = ngv;
+            goff1 = goff2;
+        }
+
+        double *po = prm.partial + (size_t)seg * (NACC * 64);
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) po[i * 64 + lane] = acc[i];
+        ++seg;
+        it += p1 - p0;
+    }
+}
+
+// Fixup, step 1: thread (tile t, accumulator i, lane) adds tile t's segment
+// sums in iteration order and stores the total in the tile's first segment.
+// Grid (NACC, n_tiles) of 64-lane workgroups.
+__global__ __launch_bounds__(64) void gram_reduce_kernel(GramParams prm, int nacc) {
+    const int lane = threadIdx.x;
+    const int i = blockIdx.x;
+    const int t = blockIdx.y;
+    const int s0 = prm.seg_first[t], s1 = prm.seg_first[t + 1];
+    double acc = 0.0;
+    for (int sg = s0; sg < s1; ++sg) acc += prm.partial[((size_t)sg * nacc + i) * 64 + lane];
+    prm.partial[((size_t)s0 * nacc + i) * 64 + lane] = acc;
+}
+
+// Fixup, step 2: write each tile's systems from its reduced sums.
+template <int NJ, int METHOD>
+__global__ __launch_bounds__(64) void gram_write_kernel(GramParams prm) {
+    using Sh = GramShape<NJ, METHOD>;
+    constexpr int NACC = Sh::NACC;
+    const int lane = threadIdx.x;
+    const int t = blockIdx.x;
+    const GramTile *tile = prm.tiles + t;
+    const int qi = tile->qidx[lane];
+    if (qi < 0) return;
+    double acc[NACC];
+    const double *pi = prm.partial + (size_t)prm.seg_first[t] * (NACC * 64);
+#pragma unroll
+    for (int i = 0; i < NACC; ++i) acc[i] = pi[i * 64 + lane];
+    write_system<NJ, METHOD>(acc, (unsigned)tile->mask[lane], qi, prm);
+}
+
 // Work a Gram launch does per frequency, counted exactly per lane (not the
 // wave-wide union the Gram kernel evaluates): instrumentation, run after the
 // prepare's own kernels.  out[tile][0..4] = support tests (pixel, alias, lobe),
@@ -307,8 +381,8 @@ __global__ __launch_bounds__(64) void work_count_kernel(GramParams prm, unsigned
             const double Qy = (double)(yh + (int)tile->jy[s] * prm.N) * prm.dq;
             const double Qx = (double)(ix + (int)tile->jx[s] * prm.N) * prm.dq;
             const double dy = ky - Qy, dx = kx - Qx, ey = ky + Qy, ex = kx + Qx;
-            const bool zl = inside_support(prm.ap, fma(dy, dy, dx * dx));
-            const bool zr = inside_support(prm.ap, fma(ey, ey, ex * ex));
+            const bool zl = fma(dy, dy, dx * dx) < prm.ap.rlim2;
+            const bool zr = fma(ey, ey, ex * ex) < prm.ap.rlim2;
             tests += 2;
             lobes += (zl ? 1 : 0) + (zr ? 1 : 0);
             if (METHOD == 0) nc += (zl || zr) ? 1 : 0;
@@ -728,6 +802,9 @@ template <int MAXB, int P>
 __global__ __launch_bounds__(64 * P) void ssb_kernel(SsbParams prm) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ double2 T[TRIG_N];
+    if (threadIdx.x < TRIG_N) T[threadIdx.x] = prm.trig[threadIdx.x];
+    __syncthreads();
     const SsbTile *tile = prm.tiles + blockIdx.x;
     const int yh = tile->yh0 + (lane >> 4);
     const int ix = tile->ix0 + (lane & 15);
@@ -766,14 +843,14 @@ __global__ __launch_bounds__(64 * P) void ssb_kernel(SsbParams prm) {
             if (zl) {
                 const double cm = chi_poly(prm.chi_c[b], fma(lam, dx, prm.tau_x[b]), fma(lam, dy, prm.tau_y[b]));
                 double sn, cs;
-                sincos(chi0 - cm, &sn, &cs);
+                sincos_tab(chi0 - cm, T, sn, cs);
                 Lr = aml * cs;
                 Li = aml * sn;
             }
             if (zr) {
                 const double cp = chi_poly(prm.chi_c[b], fma(lam, ex, prm.tau_x[b]), fma(lam, ey, prm.tau_y[b]));
                 double sn, cs;
-                sincos(cp - chi0, &sn, &cs);
+                sincos_tab(cp - chi0, T, sn, cs);
                 Rr = amr * cs;
                 Ri = amr * sn;
             }
@@ -874,43 +951,79 @@ hipError_t launch_pixel_terms(PixelRec *pix, int n_pix, const ApertureDev &ap, c
     return hipSuccess;
 }
 
-template <int NJ, int METHOD, int P>
-static hipError_t launch_gram_t(const GramParams &prm, int n_tiles, hipStream_t st) {
-    constexpr size_t lds = P > 1 ? sizeof(double) * 64 * GramShape<NJ, METHOD>::NACC : 0;
-    gram_kernel<NJ, METHOD, P><<<n_tiles, 64 * P, lds, st>>>(prm);
-    DSP_CHECK_LAUNCH();
-    return hipSuccess;
-}
-
-int gram_waves_per_tile(int nj, int method) {
-    if (method == 0) return nj <= 5 ? 4 : 2;
-    return nj <= 4 ? 2 : 1;
-}
-
-hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_tiles, hipStream_t st) {
-    if (n_tiles <= 0) return hipSuccess;
+// Calls F<NJ, METHOD>::run(args...) for the compiled (slots, method) pairs.
+template <template <int, int> class F, class... Args>
+static hipError_t gram_dispatch(int nj, int method, Args &&...args) {
     if (method == 0) {
         switch (nj) {
-            case 1: return launch_gram_t<1, 0, 4>(prm, n_tiles, st);
-            case 2: return launch_gram_t<2, 0, 4>(prm, n_tiles, st);
-            case 3: return launch_gram_t<3, 0, 4>(prm, n_tiles, st);
-            case 4: return launch_gram_t<4, 0, 4>(prm, n_tiles, st);
-            case 5: return launch_gram_t<5, 0, 4>(prm, n_tiles, st);
-            case 6: return launch_gram_t<6, 0, 2>(prm, n_tiles, st);
-            case 7: return launch_gram_t<7, 0, 2>(prm, n_tiles, st);
-            case 8: return launch_gram_t<8, 0, 2>(prm, n_tiles, st);
+            case 1: return F<1, 0>::run(args...);
+            case 2: return F<2, 0>::run(args...);
+            case 3: return F<3, 0>::run(args...);
+            case 4: return F<4, 0>::run(args...);
+            case 5: return F<5, 0>::run(args...);
+            case 6: return F<6, 0>::run(args...);
+            case 7: return F<7, 0>::run(args...);
+            case 8: return F<8, 0>::run(args...);
             default: return hipErrorInvalidValue;
         }
     }
     switch (nj) {
-        case 1: return launch_gram_t<1, 1, 2>(prm, n_tiles, st);
-        case 2: return launch_gram_t<2, 1, 2>(prm, n_tiles, st);
-        case 3: return launch_gram_t<3, 1, 2>(prm, n_tiles, st);
-        case 4: return launch_gram_t<4, 1, 2>(prm, n_tiles, st);
-        case 5: return launch_gram_t<5, 1, 1>(prm, n_tiles, st);
-        case 6: return launch_gram_t<6, 1, 1>(prm, n_tiles, st);
+        case 1: return F<1, 1>::run(args...);
+        case 2: return F<2, 1>::run(args...);
+        case 3: return F<3, 1>::run(args...);
+        case 4: return F<4, 1>::run(args...);
+        case 5: return F<5, 1>::run(args...);
+        case 6: return F<6, 1>::run(args...);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int NJ, int METHOD>
+struct GramLaunch {
+    static hipError_t run(const GramParams &prm, int n_waves, hipStream_t st) {
+        gram_kernel<NJ, METHOD><<<n_waves, 64, 0, st>>>(prm);
+        DSP_CHECK_LAUNCH();
+        return hipSuccess;
+    }
+};
+
+template <int NJ, int METHOD>
+struct GramFixupLaunch {
+    static hipError_t run(const GramParams &prm, int n_tiles, hipStream_t st) {
+        const int nacc = GramShape<NJ, METHOD>::NACC;
+        gram_reduce_kernel<<<dim3(nacc, n_tiles), 64, 0, st>>>(prm, nacc);
+        DSP_CHECK_LAUNCH();
+        gram_write_kernel<NJ, METHOD><<<n_tiles, 64, 0, st>>>(prm);
+        DSP_CHECK_LAUNCH();
+        return hipSuccess;
+    }
+};
+
+template <int NJ, int METHOD>
+struct GramOccupancy {
+    static hipError_t run(int *blocks_per_cu) {
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, gram_kernel<NJ, METHOD>, 64, 0);
+    }
+};
+
+int gram_nacc(int nj, int method) {
+    const int nc = method == 0 ? nj : 2 * nj;
+    const int d = nc + 1;
+    return d + d * (d - 1);
+}
+
+hipError_t gram_occupancy(int nj, int method, int *blocks_per_cu) {
+    return gram_dispatch<GramOccupancy>(nj, method, blocks_per_cu);
+}
+
+hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_waves, hipStream_t st) {
+    if (n_waves <= 0) return hipSuccess;
+    return gram_dispatch<GramLaunch>(nj, method, prm, n_waves, st);
+}
+
+hipError_t launch_gram_fixup(const GramParams &prm, int nj, int method, int n_tiles, hipStream_t st) {
+    if (n_tiles <= 0) return hipSuccess;
+    return gram_dispatch<GramFixupLaunch>(nj, method, prm, n_tiles, st);
 }
 
 hipError_t launch_work_count(const GramParams &prm, int method, int n_tiles, unsigned long long *out,

@@ -43,8 +43,10 @@ struct ScatterParams {
 
 hipError_t launch_pixel_terms(PixelRec *pix, int n_pix, const ApertureDev &ap, const OpticsDev &op, double *chi_tab,
                               hipStream_t st);
-int gram_waves_per_tile(int nj, int method);
-hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_tiles, hipStream_t st);
+int gram_nacc(int nj, int method);   // doubles per lane of one partial sum
+hipError_t gram_occupancy(int nj, int method, int *blocks_per_cu);
+hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_waves, hipStream_t st);
+hipError_t launch_gram_fixup(const GramParams &prm, int nj, int method, int n_tiles, hipStream_t st);
 hipError_t launch_work_count(const GramParams &prm, int method, int n_tiles, unsigned long long *out,
                              hipStream_t st);
 hipError_t launch_eig(const EigParams &prm, int A, hipStream_t st);
