@@ -123,7 +123,9 @@ typedef struct {
     double scale;            /* strength unit: sum of active weights */
     double g_bytes;          /* algorithmic G bytes a prepare reads: n_q * n_active * 8 */
     double lobes;            /* with DSP_FLAG_COUNT_WORK: non-zero weak-object lobes evaluated */
-    double host_ms;          /* host geometry + upload enqueue of the last prepare */
+    double host_ms;          /* host time of the prepare call (validation, layout, enqueue) */
+    double layout_ms;        /* host time spent building the data-only layout (0 when reused) */
+    int layout_cached;       /* 1 when the prepare reused a cached data-only layout */
     double stage_ms[4];      /* with DSP_FLAG_TIMING: pixel terms, Gram, eigenbasis, total */
     int timing_ready;        /* 1 when the timing fields are filled: dsp_info never waits; it
                                 fills them once the prepare's work has completed on its stream */

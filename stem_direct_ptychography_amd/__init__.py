@@ -137,6 +137,7 @@ class Prepared:
             "n_active_bf": inf.n_active_bf, "method": inf.method, "upsampling": inf.upsampling,
             "n_scan": inf.n_scan, "n_tiles": inf.n_tiles, "alias_hist": list(inf.alias_hist),
             "scale": inf.scale, "g_bytes": inf.g_bytes, "host_ms": inf.host_ms,
+            "layout_ms": inf.layout_ms, "layout_cached": bool(inf.layout_cached),
             "stage_ms": list(inf.stage_ms), "timing_ready": bool(inf.timing_ready), "lobes": inf.lobes,
             "gram": [{"nj": inf.gram_nj[i], "tiles": inf.gram_tiles[i], "waves": inf.gram_waves[i],
                       "ms": inf.gram_ms[i], "fixup_ms": inf.gram_fixup_ms[i],

@@ -49,7 +49,8 @@ class InfoC(ctypes.Structure):
         ("n_bf", ctypes.c_int), ("n_active_bf", ctypes.c_int), ("method", ctypes.c_int),
         ("upsampling", ctypes.c_int), ("n_scan", ctypes.c_int), ("n_tiles", ctypes.c_int),
         ("alias_hist", ctypes.c_int * 10), ("scale", ctypes.c_double), ("g_bytes", ctypes.c_double),
-        ("lobes", ctypes.c_double), ("host_ms", ctypes.c_double), ("stage_ms", ctypes.c_double * 4),
+        ("lobes", ctypes.c_double), ("host_ms", ctypes.c_double), ("layout_ms", ctypes.c_double),
+        ("layout_cached", ctypes.c_int), ("stage_ms", ctypes.c_double * 4),
         ("timing_ready", ctypes.c_int),
         ("n_gram_launches", ctypes.c_int), ("gram_nj", ctypes.c_int * 16), ("gram_tiles", ctypes.c_int * 16),
         ("gram_waves", ctypes.c_int * 16), ("gram_ms", ctypes.c_double * 16), ("gram_fixup_ms", ctypes.c_double * 16), ("gram_work", (ctypes.c_double * 5) * 16),

@@ -509,6 +509,184 @@ dsp_status dev_alloc(T **p, size_t n) {
     return DSP_OK;
 }
 
+
+
+// ---------------------------------------------------------------------------
+// data-only layout, cached across prepares
+// ---------------------------------------------------------------------------
+// Everything a prepare needs that does not depend on the aberrations or the
+// data values: frequencies, aliases, tiles, priors, alias-count buckets,
+// active pixels and their weights, the stream-K plans, and device copies
+// ("Preparation in one kernel per alias count", What changed 4: a data-only
+// layout computed once per data, sampling and prior).  Keyed by device,
+// scan, aperture, upsampling, method, prior, and the exact bright-field
+// coordinates and weights.
+struct LayoutKey {
+    int device = 0, n_scan = 0, u = 0, method = 0, soft = 0, n_bf = 0;
+    double step = 0, lam = 0, alpha = 0, dk = 0, smooth = 0;
+    std::vector<double> coords, weights;   // weights empty when NULL
+    bool operator==(const LayoutKey &o) const {
+        return device == o.device && n_scan == o.n_scan && u == o.u && method == o.method && soft == o.soft &&
+               n_bf == o.n_bf && step == o.step && lam == o.lam && alpha == o.alpha && dk == o.dk &&
+               smooth == o.smooth && coords == o.coords && weights == o.weights;
+    }
+};
+
+struct Layout {
+    LayoutKey key;
+    Geometry geo;
+    TileGroups tg;
+    ActiveSet act;
+    std::vector<int> bucket_off, bucket_n;
+    std::vector<int32_t> bucket;
+    std::vector<double> prior;
+    std::vector<int> sk_waves;                // waves of each group's Gram launch
+    std::vector<size_t> wb_off, so_off, sf_off;
+    std::vector<long long> sk_wbegin;         // stream-K tables of all groups
+    std::vector<int> sk_int;
+    size_t max_partial = 0;                   // doubles of the largest group's partial sums
+    double host_ms = 0.0;                     // time to build
+    // device copies
+    PixelRec *d_pixbase = nullptr;            // k, weights, plane offsets (optics fields unset)
+    GramTile *d_tiles = nullptr;
+    double *d_prior = nullptr;                // [n_q][a_max]
+    int32_t *d_count = nullptr;               // [n_q]
+    int32_t *d_K = nullptr;                   // [n_q][a_max][2]
+    int32_t *d_bucket = nullptr;              // frequency lists by alias count
+    long long *d_sk_wbegin = nullptr;
+    int *d_sk_int = nullptr;
+
+    ~Layout() {
+        hipSetDevice(key.device);
+        hipFree(d_pixbase);
+        hipFree(d_tiles);
+        hipFree(d_prior);
+        hipFree(d_count);
+        hipFree(d_K);
+        hipFree(d_bucket);
+        hipFree(d_sk_wbegin);
+        hipFree(d_sk_int);
+    }
+};
+
+// Builds a layout (host work plus blocking uploads on the device current).
+dsp_status build_layout(const LayoutKey &key, const dsp_scan *scan, const dsp_optics *optics, const double *coords,
+                        const double *weights, std::shared_ptr<Layout> &out) {
+    const double t0 = now_ms();
+    dsp_status st;
+    auto L = std::make_shared<Layout>();
+    L->key = key;
+    if ((st = build_geometry(scan, optics, key.u, L->geo))) return st;
+    Geometry &g = L->geo;
+    const int max_nj = key.method == DSP_PHASE ? MAX_NJ_PHASE : MAX_NJ_COMPLEX;
+    const int max_a = key.method == DSP_PHASE ? MAX_A_PHASE : MAX_A_SOLVE_COMPLEX;
+    if (g.a_max > max_a) return fail(DSP_EALIAS, "alias count %d above the compiled maximum %d", g.a_max, max_a);
+    if ((st = build_gram_tiles(g, max_nj, L->tg))) return st;
+    if ((st = build_active(coords, weights, key.n_bf, optics, g.N, L->act))) return st;
+    if (L->act.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
+    const int am = std::max(1, g.a_max);
+
+    // prior per (frequency, alias)
+    L->prior.assign((size_t)g.n_q * am, 1.0);
+    const double sp = key.smooth;
+    if (sp > 0.0) {
+        for (int i = 0; i < g.n_q; ++i)
+            for (int m = 0; m < g.count[i]; ++m) {
+                const double qy = (double)g.K[((size_t)i * am + m) * 2] * g.dq;
+                const double qx = (double)g.K[((size_t)i * am + m) * 2 + 1] * g.dq;
+                const double b = 1.0 + (qy * qy + qx * qx) / (sp * sp);
+                L->prior[(size_t)i * am + m] = b * b;
+            }
+    }
+    // frequency lists by alias count
+    L->bucket_off.assign(10, 0);
+    L->bucket_n.assign(10, 0);
+    for (int i = 0; i < g.n_q; ++i) L->bucket_n[g.count[i]]++;
+    for (int A = 1; A <= 9; ++A) L->bucket_off[A] = L->bucket_off[A - 1] + L->bucket_n[A - 1];
+    L->bucket.assign(g.n_q, 0);
+    {
+        std::vector<int> fill(L->bucket_off);
+        for (int i = 0; i < g.n_q; ++i) L->bucket[fill[g.count[i]]++] = i;
+    }
+
+    // stream-K plan per tile group (one Gram launch per alias-slot count)
+    const int n_groups = (int)L->tg.group_nj.size();
+    const int n_pix = (int)L->act.pix.size();
+    int n_cu = 0;
+    HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, key.device));
+    const ApertureDev apd = make_aperture_dev(optics);
+    const double ra = std::sqrt(apd.rlim2);
+    L->sk_waves.assign(n_groups, 0);
+    L->wb_off.assign(n_groups, 0);
+    L->so_off.assign(n_groups, 0);
+    L->sf_off.assign(n_groups, 0);
+    for (int gi = 0; gi < n_groups; ++gi) {
+        const int nj = L->tg.group_nj[gi], nt = L->tg.group_n[gi];
+        int bpc = 0;
+        HIP_TRY(gram_occupancy(nj, key.method, &bpc));
+        bpc = std::max(1, bpc);
+        const long long total_it = (long long)nt * n_pix;
+        const int W = (int)std::max(1LL, std::min((long long)bpc * n_cu * GRAM_ROUNDS, total_it / 64));
+        std::vector<double> cost(nt);
+        for (int t = 0; t < nt; ++t) cost[t] = tile_cost(L->tg.tiles[L->tg.group_off[gi] + t], g, ra, n_pix);
+        StreamKPlan plan;
+        plan_stream_k(cost, n_pix, W, plan);
+        L->sk_waves[gi] = W;
+        L->max_partial = std::max(L->max_partial, (size_t)plan.n_segs * gram_nacc(nj, key.method) * 64);
+        L->wb_off[gi] = L->sk_wbegin.size();
+        L->sk_wbegin.insert(L->sk_wbegin.end(), plan.wbegin.begin(), plan.wbegin.end());
+        L->so_off[gi] = L->sk_int.size();
+        L->sk_int.insert(L->sk_int.end(), plan.seg_off.begin(), plan.seg_off.end());
+        L->sf_off[gi] = L->sk_int.size();
+        L->sk_int.insert(L->sk_int.end(), plan.seg_first.begin(), plan.seg_first.end());
+    }
+
+    // device copies (blocking: a layout is built once and reused)
+    if ((st = dev_alloc(&L->d_pixbase, L->act.pix.size())) || (st = dev_alloc(&L->d_tiles, L->tg.tiles.size())) ||
+        (st = dev_alloc(&L->d_prior, L->prior.size())) || (st = dev_alloc(&L->d_count, g.count.size())) ||
+        (st = dev_alloc(&L->d_K, g.K.size())) || (st = dev_alloc(&L->d_bucket, L->bucket.size())) ||
+        (st = dev_alloc(&L->d_sk_wbegin, L->sk_wbegin.size())) || (st = dev_alloc(&L->d_sk_int, L->sk_int.size())))
+        return st;
+    HIP_TRY(hipMemcpy(L->d_pixbase, L->act.pix.data(), L->act.pix.size() * sizeof(PixelRec), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(L->d_tiles, L->tg.tiles.data(), L->tg.tiles.size() * sizeof(GramTile), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(L->d_prior, L->prior.data(), L->prior.size() * sizeof(double), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(L->d_count, g.count.data(), g.count.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    if (!g.K.empty()) HIP_TRY(hipMemcpy(L->d_K, g.K.data(), g.K.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    if (!L->bucket.empty())
+        HIP_TRY(hipMemcpy(L->d_bucket, L->bucket.data(), L->bucket.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(L->d_sk_wbegin, L->sk_wbegin.data(), L->sk_wbegin.size() * sizeof(long long),
+                      hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(L->d_sk_int, L->sk_int.data(), L->sk_int.size() * sizeof(int), hipMemcpyHostToDevice));
+    L->host_ms = now_ms() - t0;
+    out = L;
+    return DSP_OK;
+}
+
+// Most recently used layouts (a handle keeps its own reference).
+constexpr size_t LAYOUT_CACHE_SIZE = 4;
+std::mutex g_layout_mu;
+std::vector<std::shared_ptr<Layout>> g_layouts;   // front = most recent
+
+dsp_status get_layout(const LayoutKey &key, const dsp_scan *scan, const dsp_optics *optics, const double *coords,
+                      const double *weights, std::shared_ptr<Layout> &out, bool &hit) {
+    std::lock_guard<std::mutex> lock(g_layout_mu);
+    for (size_t i = 0; i < g_layouts.size(); ++i) {
+        if (g_layouts[i]->key == key) {
+            out = g_layouts[i];
+            g_layouts.erase(g_layouts.begin() + i);
+            g_layouts.insert(g_layouts.begin(), out);
+            hit = true;
+            return DSP_OK;
+        }
+    }
+    hit = false;
+    dsp_status st = build_layout(key, scan, optics, coords, weights, out);
+    if (st) return st;
+    g_layouts.insert(g_layouts.begin(), out);
+    if (g_layouts.size() > LAYOUT_CACHE_SIZE) g_layouts.pop_back();
+    return DSP_OK;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -518,22 +696,14 @@ dsp_status dev_alloc(T **p, size_t n) {
 struct dsp_handle {
     int device = 0;
     int method = 0;
-    Geometry geo;
-    TileGroups tg;
-    ActiveSet act;
+    std::shared_ptr<const Layout> L;
     int n_bf = 0;
     int D = 0, n_comp = 1;
-    double scale = 0.0;
     double host_ms = 0.0;
-    // device
-    PixelRec *d_pix = nullptr;
-    GramTile *d_tiles = nullptr;
+    bool layout_hit = false;
+    // device, owned by the handle
+    PixelRec *d_pix = nullptr;      // records with this optics' chi(k) and a(k)
     double2 *d_sys = nullptr;       // [n_q][tri_size(D)]
-    double *d_prior = nullptr;      // [n_q][a_max]
-    int32_t *d_count = nullptr;     // [n_q]
-    int32_t *d_K = nullptr;         // [n_q][a_max][2]
-    int32_t *d_bucket = nullptr;    // frequency lists by alias count
-    std::vector<int> bucket_off, bucket_n;   // per alias count 0..9
     double *d_lam = nullptr;
     double2 *d_U = nullptr;
     double2 *d_c = nullptr;
@@ -543,22 +713,12 @@ struct dsp_handle {
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     std::vector<int> gram_order;              // launch order of the tile groups
     std::vector<hipEvent_t> gram_ev;          // three per launch: start, Gram done, fixup done (timing)
-    std::vector<int> sk_waves;                // waves of each group's Gram launch
-    std::vector<long long> sk_wbegin;         // stream-K tables (host copies kept for the async upload)
-    std::vector<int> sk_int;
-    long long *d_sk_wbegin = nullptr;
-    int *d_sk_int = nullptr;
     unsigned long long *d_work = nullptr;     // [tile][5] (DSP_FLAG_COUNT_WORK)
 
     ~dsp_handle() {
         hipSetDevice(device);
         hipFree(d_pix);
-        hipFree(d_tiles);
         hipFree(d_sys);
-        hipFree(d_prior);
-        hipFree(d_count);
-        hipFree(d_K);
-        hipFree(d_bucket);
         hipFree(d_lam);
         hipFree(d_U);
         hipFree(d_c);
@@ -567,8 +727,6 @@ struct dsp_handle {
         for (auto &e : gram_ev)
             if (e) hipEventDestroy(e);
         hipFree(d_work);
-        hipFree(d_sk_wbegin);
-        hipFree(d_sk_int);
     }
 };
 
@@ -674,6 +832,12 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
     if (n_bf <= 0 || !bf_coords_host) return fail(DSP_EINVAL, "n_bf must be > 0 with bf_coords");
     if (!std::isfinite(opts->smoothness_invA)) return fail(DSP_EINVAL, "smoothness not finite");
+    for (int i = 0; i < 2 * n_bf; ++i)
+        if (!std::isfinite(bf_coords_host[i])) return fail(DSP_EINVAL, "bf_coords[%d] not finite", i / 2);
+    if (weights_host)
+        for (int i = 0; i < n_bf; ++i)
+            if (!(weights_host[i] >= 0.0) || !std::isfinite(weights_host[i]))
+                return fail(DSP_EINVAL, "weights[%d] must be finite and >= 0", i);
     hipStream_t stream = (hipStream_t)hip_stream;
 
     std::unique_ptr<dsp_handle> h(new dsp_handle());
@@ -682,64 +846,40 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     h->timing = (opts->flags & DSP_FLAG_TIMING) != 0;
     h->count_work = (opts->flags & DSP_FLAG_COUNT_WORK) != 0;
     h->stream = stream;
-    if ((st = build_geometry(scan, optics, opts->upsampling, h->geo))) return st;
-    Geometry &g = h->geo;
-    const int max_nj = h->method == DSP_PHASE ? MAX_NJ_PHASE : MAX_NJ_COMPLEX;
-    const int max_a = h->method == DSP_PHASE ? MAX_A_PHASE : MAX_A_SOLVE_COMPLEX;
-    if (g.a_max > max_a) return fail(DSP_EALIAS, "alias count %d above the compiled maximum %d", g.a_max, max_a);
-    if ((st = build_gram_tiles(g, max_nj, h->tg))) return st;
-    if ((st = build_active(bf_coords_host, weights_host, n_bf, optics, g.N, h->act))) return st;
-    if (h->act.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
-    h->scale = h->act.scale;
     HIP_TRY(hipGetDevice(&h->device));
+
+    LayoutKey key;
+    key.device = h->device;
+    key.n_scan = scan->n_scan;
+    key.step = scan->step_A;
+    key.u = opts->upsampling;
+    key.method = opts->method;
+    key.soft = optics->soft_aperture;
+    key.lam = optics->wavelength_A;
+    key.alpha = optics->semiangle_rad;
+    key.dk = optics->det_step_invA;
+    key.smooth = opts->smoothness_invA > 0.0 ? opts->smoothness_invA : 0.0;
+    key.n_bf = n_bf;
+    key.coords.assign(bf_coords_host, bf_coords_host + 2 * (size_t)n_bf);
+    if (weights_host) key.weights.assign(weights_host, weights_host + n_bf);
+    std::shared_ptr<Layout> lay;
+    if ((st = get_layout(key, scan, optics, bf_coords_host, weights_host, lay, h->layout_hit))) return st;
+    h->L = lay;
+    const Layout &L = *lay;
+    const Geometry &g = L.geo;
     h->n_comp = h->method == DSP_PHASE ? 1 : 2;
     const int am = std::max(1, g.a_max);
     h->D = h->n_comp * am + 1;
+    const int n_pix = (int)L.act.pix.size();
 
-    // prior per (frequency, alias)
-    std::vector<double> prior((size_t)g.n_q * am, 1.0);
-    const double sp = opts->smoothness_invA;
-    for (int i = 0; i < g.n_q; ++i)
-        for (int m = 0; m < g.count[i]; ++m) {
-            if (sp > 0.0) {
-                const double qy = (double)g.K[((size_t)i * am + m) * 2] * g.dq;
-                const double qx = (double)g.K[((size_t)i * am + m) * 2 + 1] * g.dq;
-                const double q2 = qy * qy + qx * qx;
-                const double b = 1.0 + q2 / (sp * sp);
-                prior[(size_t)i * am + m] = b * b;
-            }
-        }
-    // frequency lists by alias count
-    std::vector<int32_t> bucket;
-    h->bucket_off.assign(10, 0);
-    h->bucket_n.assign(10, 0);
-    for (int A = 0; A <= 9; ++A) {
-        h->bucket_off[A] = (int)bucket.size();
-        for (int i = 0; i < g.n_q; ++i)
-            if (g.count[i] == A) bucket.push_back(i);
-        h->bucket_n[A] = (int)bucket.size() - h->bucket_off[A];
-    }
-
-    // device buffers
+    // per-handle buffers
     const size_t n_sys = (size_t)g.n_q * tri_size(h->D);
-    if ((st = dev_alloc(&h->d_pix, h->act.pix.size())) || (st = dev_alloc(&h->d_tiles, h->tg.tiles.size())) ||
-        (st = dev_alloc(&h->d_sys, n_sys)) || (st = dev_alloc(&h->d_prior, prior.size())) ||
-        (st = dev_alloc(&h->d_count, g.count.size())) || (st = dev_alloc(&h->d_K, g.K.size())) ||
-        (st = dev_alloc(&h->d_bucket, bucket.size())))
-        return st;
+    if ((st = dev_alloc(&h->d_pix, (size_t)n_pix)) || (st = dev_alloc(&h->d_sys, n_sys))) return st;
     if (h->method == DSP_PHASE) {
         if ((st = dev_alloc(&h->d_lam, (size_t)g.n_q * am)) || (st = dev_alloc(&h->d_U, (size_t)g.n_q * am * am)) ||
             (st = dev_alloc(&h->d_c, (size_t)g.n_q * am)))
             return st;
     }
-    HIP_TRY(hipMemcpyAsync(h->d_pix, h->act.pix.data(), h->act.pix.size() * sizeof(PixelRec), hipMemcpyHostToDevice, stream));
-    HIP_TRY(hipMemcpyAsync(h->d_tiles, h->tg.tiles.data(), h->tg.tiles.size() * sizeof(GramTile), hipMemcpyHostToDevice, stream));
-    HIP_TRY(hipMemcpyAsync(h->d_prior, prior.data(), prior.size() * sizeof(double), hipMemcpyHostToDevice, stream));
-    HIP_TRY(hipMemcpyAsync(h->d_count, g.count.data(), g.count.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream));
-    if (!g.K.empty())
-        HIP_TRY(hipMemcpyAsync(h->d_K, g.K.data(), g.K.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream));
-    if (!bucket.empty())
-        HIP_TRY(hipMemcpyAsync(h->d_bucket, bucket.data(), bucket.size() * sizeof(int32_t), hipMemcpyHostToDevice, stream));
 
     if (h->timing) {
         for (auto &e : h->ev) HIP_TRY(hipEventCreate(&e));
@@ -747,14 +887,14 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     }
     const ApertureDev apd = make_aperture_dev(optics);
     const OpticsDev opd = make_optics_dev(optics);
-    HIP_TRY(launch_pixel_terms(h->d_pix, (int)h->act.pix.size(), apd, opd, nullptr, stream));
+    HIP_TRY(launch_pixel_terms(L.d_pixbase, h->d_pix, n_pix, apd, opd, nullptr, stream));
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[1], stream));
 
     GramParams gp;
     std::memset(&gp, 0, sizeof gp);
     gp.G = (const float2 *)G_c64_dev;
     gp.pix = h->d_pix;
-    gp.n_pix = (int)h->act.pix.size();
+    gp.n_pix = n_pix;
     gp.N = g.N;
     gp.nh = g.N / 2 + 1;
     gp.dq = g.dq;
@@ -764,56 +904,15 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     gp.a_max = am;
     gp.D = h->D;
     if ((st = trig_table_device(h->device, &gp.trig))) return st;
-    // stream-K plan per tile group (one launch per alias-slot count)
-    const int n_groups = (int)h->tg.group_nj.size();
-    int n_cu = 0;
-    HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, h->device));
-    const double ra = std::sqrt(apd.rlim2);
-    std::vector<StreamKPlan> plans(n_groups);
-    h->sk_waves.assign(n_groups, 0);
-    size_t max_partial = 0, n_wb = 0, n_int = 0;
-    for (int gi = 0; gi < n_groups; ++gi) {
-        const int nj = h->tg.group_nj[gi], nt = h->tg.group_n[gi];
-        int bpc = 0;
-        HIP_TRY(gram_occupancy(nj, h->method, &bpc));
-        bpc = std::max(1, bpc);
-        const long long total_it = (long long)nt * gp.n_pix;
-        const int W = (int)std::max(1LL, std::min((long long)bpc * n_cu * GRAM_ROUNDS, total_it / 64));
-        std::vector<double> cost(nt);
-        for (int t = 0; t < nt; ++t) cost[t] = tile_cost(h->tg.tiles[h->tg.group_off[gi] + t], g, ra, gp.n_pix);
-        plan_stream_k(cost, gp.n_pix, W, plans[gi]);
-        h->sk_waves[gi] = W;
-        max_partial = std::max(max_partial, (size_t)plans[gi].n_segs * gram_nacc(nj, h->method) * 64);
-        n_wb += W + 1;
-        n_int += W + nt + 1;
-    }
-    h->sk_wbegin.clear();
-    h->sk_int.clear();
-    h->sk_wbegin.reserve(n_wb);
-    h->sk_int.reserve(n_int);
-    std::vector<size_t> wb_off(n_groups), so_off(n_groups), sf_off(n_groups);
-    for (int gi = 0; gi < n_groups; ++gi) {
-        wb_off[gi] = h->sk_wbegin.size();
-        h->sk_wbegin.insert(h->sk_wbegin.end(), plans[gi].wbegin.begin(), plans[gi].wbegin.end());
-        so_off[gi] = h->sk_int.size();
-        h->sk_int.insert(h->sk_int.end(), plans[gi].seg_off.begin(), plans[gi].seg_off.end());
-        sf_off[gi] = h->sk_int.size();
-        h->sk_int.insert(h->sk_int.end(), plans[gi].seg_first.begin(), plans[gi].seg_first.end());
-    }
-    if ((st = dev_alloc(&h->d_sk_wbegin, h->sk_wbegin.size())) || (st = dev_alloc(&h->d_sk_int, h->sk_int.size())))
-        return st;
-    HIP_TRY(hipMemcpyAsync(h->d_sk_wbegin, h->sk_wbegin.data(), h->sk_wbegin.size() * sizeof(long long),
-                           hipMemcpyHostToDevice, stream));
-    HIP_TRY(hipMemcpyAsync(h->d_sk_int, h->sk_int.data(), h->sk_int.size() * sizeof(int), hipMemcpyHostToDevice,
-                           stream));
     // partial sums live only for the Gram stage (stream-ordered)
     double *d_partial = nullptr;
-    HIP_TRY(hipMallocAsync((void **)&d_partial, std::max<size_t>(1, max_partial) * sizeof(double), stream));
+    HIP_TRY(hipMallocAsync((void **)&d_partial, std::max<size_t>(1, L.max_partial) * sizeof(double), stream));
 
     // largest groups first
+    const int n_groups = (int)L.tg.group_nj.size();
     std::vector<int> order(n_groups);
     for (int i = 0; i < n_groups; ++i) order[i] = i;
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return h->tg.group_n[a] > h->tg.group_n[b]; });
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return L.tg.group_n[a] > L.tg.group_n[b]; });
     h->gram_order = order;
     if (h->timing) {
         h->gram_ev.assign(3 * order.size(), nullptr);
@@ -821,16 +920,16 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     }
     for (size_t oi = 0; oi < order.size(); ++oi) {
         const int gi = order[oi];
-        gp.tiles = h->d_tiles + h->tg.group_off[gi];
-        gp.wbegin = h->d_sk_wbegin + wb_off[gi];
-        gp.seg_off = h->d_sk_int + so_off[gi];
-        gp.seg_first = h->d_sk_int + sf_off[gi];
+        gp.tiles = L.d_tiles + L.tg.group_off[gi];
+        gp.wbegin = L.d_sk_wbegin + L.wb_off[gi];
+        gp.seg_off = L.d_sk_int + L.so_off[gi];
+        gp.seg_first = L.d_sk_int + L.sf_off[gi];
         gp.partial = d_partial;
-        gp.n_waves = h->sk_waves[gi];
+        gp.n_waves = L.sk_waves[gi];
         if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[3 * oi], stream));
-        HIP_TRY(launch_gram(gp, h->tg.group_nj[gi], h->method, gp.n_waves, stream));
+        HIP_TRY(launch_gram(gp, L.tg.group_nj[gi], h->method, gp.n_waves, stream));
         if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[3 * oi + 1], stream));
-        HIP_TRY(launch_gram_fixup(gp, h->tg.group_nj[gi], h->method, h->tg.group_n[gi], stream));
+        HIP_TRY(launch_gram_fixup(gp, L.tg.group_nj[gi], h->method, L.tg.group_n[gi], stream));
         if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[3 * oi + 2], stream));
     }
     HIP_TRY(hipFreeAsync(d_partial, stream));
@@ -841,30 +940,30 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
         ep.sys = h->d_sys;
         ep.D = h->D;
         ep.a_max = am;
-        ep.prior = h->d_prior;
+        ep.prior = L.d_prior;
         ep.lam = h->d_lam;
         ep.U = h->d_U;
         ep.c = h->d_c;
         // frequencies without aliases keep zero eigen data
-        if (h->bucket_n[0] > 0) {
+        if (L.bucket_n[0] > 0) {
             HIP_TRY(launch_fill_zero(h->d_lam, (size_t)g.n_q * am, stream));
             HIP_TRY(launch_fill_zero((double *)h->d_U, (size_t)g.n_q * am * am * 2, stream));
             HIP_TRY(launch_fill_zero((double *)h->d_c, (size_t)g.n_q * am * 2, stream));
         }
         for (int A = 1; A <= 9; ++A) {
-            if (h->bucket_n[A] == 0) continue;
-            ep.qlist = h->d_bucket + h->bucket_off[A];
-            ep.n = h->bucket_n[A];
+            if (L.bucket_n[A] == 0) continue;
+            ep.qlist = L.d_bucket + L.bucket_off[A];
+            ep.n = L.bucket_n[A];
             HIP_TRY(launch_eig(ep, A, stream));
         }
     }
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[3], stream));
     if (h->count_work) {
         // instrumentation after the prepare's own kernels: work per tile
-        if ((st = dev_alloc(&h->d_work, h->tg.tiles.size() * 5))) return st;
-        for (size_t gi = 0; gi < h->tg.group_nj.size(); ++gi) {
-            gp.tiles = h->d_tiles + h->tg.group_off[gi];
-            HIP_TRY(launch_work_count(gp, h->method, h->tg.group_n[gi], h->d_work + (size_t)h->tg.group_off[gi] * 5,
+        if ((st = dev_alloc(&h->d_work, L.tg.tiles.size() * 5))) return st;
+        for (int gi = 0; gi < n_groups; ++gi) {
+            gp.tiles = L.d_tiles + L.tg.group_off[gi];
+            HIP_TRY(launch_work_count(gp, h->method, L.tg.group_n[gi], h->d_work + (size_t)L.tg.group_off[gi] * 5,
                                       stream));
         }
     }
@@ -883,7 +982,7 @@ dsp_status dsp_solve(dsp_handle *h, const double *strengths_host, int S, void *x
             return fail(DSP_EINVAL, "strength %d must be finite and >= 0", i);
     HIP_TRY(hipSetDevice(h->device));
     hipStream_t stream = (hipStream_t)hip_stream;
-    const Geometry &g = h->geo;
+    const Geometry &g = h->L->geo;
     const int am = std::max(1, g.a_max);
     const int chunk = h->method == DSP_PHASE ? 64 : 32;
     double2 *x = (double2 *)x_out_c128_dev;
@@ -895,19 +994,19 @@ dsp_status dsp_solve(dsp_handle *h, const double *strengths_host, int S, void *x
         sp.D = h->D;
         sp.a_max = am;
         sp.n_q = g.n_q;
-        sp.prior = h->d_prior;
+        sp.prior = h->L->d_prior;
         sp.lam = h->d_lam;
         sp.U = h->d_U;
         sp.c = h->d_c;
         for (int i = 0; i < sn * per; ++i) sp.strengths[i] = strengths_host[s0 * per + i];
         sp.S = sn;
-        sp.scale = h->scale;
+        sp.scale = h->L->act.scale;
         sp.x = x + (size_t)s0 * h->n_comp * g.n_q * am;
         sp.resid = resid_out_dev ? resid_out_dev + (size_t)s0 * g.n_q : nullptr;
         for (int A = 0; A <= 9; ++A) {
-            if (h->bucket_n[A] == 0) continue;
-            sp.qlist = h->d_bucket + h->bucket_off[A];
-            sp.n = h->bucket_n[A];
+            if (h->L->bucket_n[A] == 0) continue;
+            sp.qlist = h->L->d_bucket + h->L->bucket_off[A];
+            sp.n = h->L->bucket_n[A];
             HIP_TRY(launch_solve(sp, A, h->method, stream));
         }
     }
@@ -920,7 +1019,7 @@ dsp_status dsp_scatter(const dsp_handle *h, const void *x_packed_c128_dev, int S
     if (S <= 0 || !x_packed_c128_dev || !spec_out_c128_dev) return fail(DSP_EINVAL, "need S > 0, x and spec_out");
     HIP_TRY(hipSetDevice(h->device));
     hipStream_t stream = (hipStream_t)hip_stream;
-    const Geometry &g = h->geo;
+    const Geometry &g = h->L->geo;
     const int nf = g.u * g.N;
     const size_t plane = (size_t)nf * (nf / 2 + 1);
     HIP_TRY(launch_fill_zero((double *)spec_out_c128_dev, (size_t)S * h->n_comp * plane * 2, stream));
@@ -929,8 +1028,8 @@ dsp_status dsp_scatter(const dsp_handle *h, const void *x_packed_c128_dev, int S
     p.SC = S * h->n_comp;
     p.n_q = g.n_q;
     p.a_max = std::max(1, g.a_max);
-    p.count = h->d_count;
-    p.K = h->d_K;
+    p.count = h->L->d_count;
+    p.K = h->L->d_K;
     p.nf = nf;
     p.spec = (double2 *)spec_out_c128_dev;
     HIP_TRY(launch_scatter(p, stream));
@@ -940,27 +1039,29 @@ dsp_status dsp_scatter(const dsp_handle *h, const void *x_packed_c128_dev, int S
 dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out) {
     if (!h || !out) return fail(DSP_EINVAL, "NULL argument");
     std::memset(out, 0, sizeof *out);
-    const Geometry &g = h->geo;
+    const Geometry &g = h->L->geo;
     out->n_q = g.n_q;
     out->a_max = g.a_max;
     out->n_comp = h->n_comp;
     out->dim = h->D;
     out->n_bf = h->n_bf;
-    out->n_active_bf = (int)h->act.pix.size();
+    out->n_active_bf = (int)h->L->act.pix.size();
     out->method = h->method;
     out->upsampling = g.u;
     out->n_scan = g.N;
-    out->n_tiles = (int)h->tg.tiles.size();
+    out->n_tiles = (int)h->L->tg.tiles.size();
     for (int i = 0; i < 10; ++i) out->alias_hist[i] = g.hist[i];
-    out->scale = h->scale;
-    out->g_bytes = (double)g.n_q * (double)h->act.pix.size() * 8.0;
+    out->scale = h->L->act.scale;
+    out->g_bytes = (double)g.n_q * (double)h->L->act.pix.size() * 8.0;
     out->host_ms = h->host_ms;
+    out->layout_ms = h->layout_hit ? 0.0 : h->L->host_ms;
+    out->layout_cached = h->layout_hit ? 1 : 0;
     out->n_gram_launches = (int)std::min<size_t>(16, h->gram_order.size());
     for (int oi = 0; oi < out->n_gram_launches; ++oi) {
         const int gi = h->gram_order[oi];
-        out->gram_nj[oi] = h->tg.group_nj[gi];
-        out->gram_tiles[oi] = h->tg.group_n[gi];
-        out->gram_waves[oi] = h->sk_waves[gi];
+        out->gram_nj[oi] = h->L->tg.group_nj[gi];
+        out->gram_tiles[oi] = h->L->tg.group_n[gi];
+        out->gram_waves[oi] = h->L->sk_waves[gi];
     }
     if ((h->timing && h->ev[3]) || (h->count_work && h->d_work)) HIP_TRY(hipSetDevice(h->device));
     // timings are filled once the prepare's last event has completed (no wait)
@@ -991,15 +1092,15 @@ dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out) {
     if (h->count_work && h->d_work) {
         // the counts are read with a blocking copy (instrumentation only)
         HIP_TRY(hipStreamSynchronize(h->stream));
-        std::vector<unsigned long long> wk(h->tg.tiles.size() * 5, 0ull);
+        std::vector<unsigned long long> wk(h->L->tg.tiles.size() * 5, 0ull);
         HIP_TRY(hipMemcpy(wk.data(), h->d_work, wk.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
         double total = 0.0;
-        for (size_t t = 0; t < h->tg.tiles.size(); ++t) total += (double)wk[t * 5 + 1];
+        for (size_t t = 0; t < h->L->tg.tiles.size(); ++t) total += (double)wk[t * 5 + 1];
         for (int oi = 0; oi < out->n_gram_launches; ++oi) {
             const int gi = h->gram_order[oi];
             for (int c = 0; c < 5; ++c) {
                 double v = 0.0;
-                for (int t = 0; t < h->tg.group_n[gi]; ++t) v += (double)wk[(size_t)(h->tg.group_off[gi] + t) * 5 + c];
+                for (int t = 0; t < h->L->tg.group_n[gi]; ++t) v += (double)wk[(size_t)(h->L->tg.group_off[gi] + t) * 5 + c];
                 out->gram_work[oi][c] = v;
             }
         }
@@ -1012,7 +1113,7 @@ dsp_status dsp_export_system(const dsp_handle *h, void *aug_out_c128_dev, double
     if (!h) return fail(DSP_EINVAL, "handle is NULL");
     HIP_TRY(hipSetDevice(h->device));
     hipStream_t stream = (hipStream_t)hip_stream;
-    const Geometry &g = h->geo;
+    const Geometry &g = h->L->geo;
     if (aug_out_c128_dev) HIP_TRY(launch_export(h->d_sys, g.n_q, h->D, (double2 *)aug_out_c128_dev, stream));
     if (eig_out_dev) {
         if (h->method != DSP_PHASE) return fail(DSP_EINVAL, "eigenvalues exist for the phase method only");
@@ -1024,7 +1125,7 @@ dsp_status dsp_export_system(const dsp_handle *h, void *aug_out_c128_dev, double
 
 dsp_status dsp_alias_table(const dsp_handle *h, int32_t *q_host, int32_t *count_host, int32_t *K_host) {
     if (!h) return fail(DSP_EINVAL, "handle is NULL");
-    const Geometry &g = h->geo;
+    const Geometry &g = h->L->geo;
     if (q_host) std::memcpy(q_host, g.q.data(), g.q.size() * sizeof(int32_t));
     if (count_host) std::memcpy(count_host, g.count.data(), g.count.size() * sizeof(int32_t));
     if (K_host && g.a_max > 0) std::memcpy(K_host, g.K.data(), g.K.size() * sizeof(int32_t));
@@ -1095,8 +1196,8 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
     for (int b = 0; b < B; ++b) {
         const OpticsDev od = make_optics_dev(sets_host + b);
         // a(k) once (set 0 writes it), chi(k) per set
-        if (b == 0) HIP_TRY(launch_pixel_terms(d_pix, n_pix, apd, od, nullptr, stream));
-        HIP_TRY(launch_pixel_terms(d_pix, n_pix, apd, od, d_chi + (size_t)b * n_pix, stream));
+        if (b == 0) HIP_TRY(launch_pixel_terms(d_pix, d_pix, n_pix, apd, od, nullptr, stream));
+        HIP_TRY(launch_pixel_terms(d_pix, d_pix, n_pix, apd, od, d_chi + (size_t)b * n_pix, stream));
         sp.tau_y[b] = od.tau_y;
         sp.tau_x[b] = od.tau_x;
         std::memcpy(sp.chi_c[b], od.chi_c, sizeof od.chi_c);

@@ -47,19 +47,24 @@ __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 // pixel terms: a(k) and chi(k) once per pixel and optics set
 // ---------------------------------------------------------------------------
 
-__global__ void pixel_terms_kernel(PixelRec *pix, int n_pix, ApertureDev ap, OpticsDev op, double *chi_tab) {
+// in[p] -> out[p] with a(k), sqrt(w) a(k) and chi(k) filled in, or (chi_tab
+// non-null) chi(k) alone into chi_tab[p].  in and out may be the same array.
+__global__ void pixel_terms_kernel(const PixelRec *in, PixelRec *out, int n_pix, ApertureDev ap, OpticsDev op,
+                                   double *chi_tab) {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= n_pix) return;
-    const double ky = pix[p].ky, kx = pix[p].kx;
+    const double ky = in[p].ky, kx = in[p].kx;
     const double d2 = fma(ky, ky, kx * kx);
     const double c = chi_poly(op.chi_c, fma(op.lam, kx, op.tau_x), fma(op.lam, ky, op.tau_y));
     if (chi_tab) {
         chi_tab[p] = c;
     } else {
+        PixelRec r = in[p];
         const double a0 = aperture_at(ap, d2);
-        pix[p].a0 = a0;
-        pix[p].amp0 = pix[p].sw * a0;
-        pix[p].chi0 = c;
+        r.a0 = a0;
+        r.amp0 = r.sw * a0;
+        r.chi0 = c;
+        out[p] = r;
     }
 }
 
@@ -943,10 +948,10 @@ __global__ void agreement_kernel(const double *partial, int n_tiles, int stride,
 #define DSP_CHECK_LAUNCH() \
     do { hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; } while (0)
 
-hipError_t launch_pixel_terms(PixelRec *pix, int n_pix, const ApertureDev &ap, const OpticsDev &op, double *chi_tab,
-                              hipStream_t st) {
+hipError_t launch_pixel_terms(const PixelRec *in, PixelRec *out, int n_pix, const ApertureDev &ap, const OpticsDev &op,
+                              double *chi_tab, hipStream_t st) {
     if (n_pix <= 0) return hipSuccess;
-    pixel_terms_kernel<<<(n_pix + 255) / 256, 256, 0, st>>>(pix, n_pix, ap, op, chi_tab);
+    pixel_terms_kernel<<<(n_pix + 255) / 256, 256, 0, st>>>(in, out, n_pix, ap, op, chi_tab);
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }

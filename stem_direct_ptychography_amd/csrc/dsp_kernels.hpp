@@ -41,8 +41,8 @@ struct ScatterParams {
     double2 *spec;            // [SC][nf][nf/2+1]
 };
 
-hipError_t launch_pixel_terms(PixelRec *pix, int n_pix, const ApertureDev &ap, const OpticsDev &op, double *chi_tab,
-                              hipStream_t st);
+hipError_t launch_pixel_terms(const PixelRec *in, PixelRec *out, int n_pix, const ApertureDev &ap, const OpticsDev &op,
+                              double *chi_tab, hipStream_t st);
 int gram_nacc(int nj, int method);   // doubles per lane of one partial sum
 hipError_t gram_occupancy(int nj, int method, int *blocks_per_cu);
 hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_waves, hipStream_t st);
