@@ -148,6 +148,11 @@ ApertureDev make_aperture_dev(const dsp_optics *o) {
         a.rout2 = a.kc * a.kc;
         a.rlim2 = std::nextafter(a.rout2, HUGE_VAL);   // d2 <= kc^2  <=>  d2 < next double
     }
+    const double lam = o->wavelength_A;
+    a.lrlim2 = lam * lam * a.rlim2;
+    a.lrin2 = lam * lam * a.rin2;
+    a.lkc = o->semiangle_rad;                      // lambda (alpha / lambda)
+    a.inv_ldk = 1.0 / (lam * o->det_step_invA);
     return a;
 }
 
@@ -366,13 +371,15 @@ dsp_status build_gram_tiles(const Geometry &g, int max_nj, TileGroups &tg) {
 
 struct ActiveSet {
     std::vector<int32_t> idx;
-    std::vector<PixelRec> pix;
+    std::vector<PixelBase> pix;
+    std::vector<long long> goff;   // element offset of each active pixel's plane in G
     double scale = 0.0;
 };
 
 dsp_status build_active(const double *k, const double *w, int n_bf, const dsp_optics *o, int N, ActiveSet &as) {
     as.idx.clear();
     as.pix.clear();
+    as.goff.clear();
     as.scale = 0.0;
     const long long plane = (long long)N * (N / 2 + 1);
     for (int i = 0; i < n_bf; ++i) {
@@ -381,15 +388,14 @@ dsp_status build_active(const double *k, const double *w, int n_bf, const dsp_op
         const double wi = w ? w[i] : 1.0;
         if (!(wi >= 0.0) || !std::isfinite(wi)) return fail(DSP_EINVAL, "weights[%d] must be finite and >= 0", i);
         if (!pixel_active(o, ky, kx)) continue;
-        PixelRec p;
-        std::memset(&p, 0, sizeof p);
+        PixelBase p;
         p.ky = ky;
         p.kx = kx;
         p.w = wi;
         p.sw = std::sqrt(wi);
-        p.goff = (long long)i * plane;
         as.idx.push_back(i);
         as.pix.push_back(p);
+        as.goff.push_back((long long)i * plane);
         as.scale += wi;
     }
     return DSP_OK;
@@ -496,6 +502,56 @@ dsp_status trig_table_device(int device, const double2 **out) {
     return DSP_OK;
 }
 
+// Scratch memory per (device, stream) for temporaries that live within one
+// call (Gram partial sums, SSB per-call tables).  Work on one stream runs in
+// order, so consecutive calls can reuse the same bytes; the arena only grows
+// (hipFree of the old block waits for the device first).  Kept until the
+// process ends.
+struct Arena {
+    int device;
+    hipStream_t stream;
+    char *ptr;
+    size_t size;
+};
+
+dsp_status arena_get(int device, hipStream_t stream, size_t bytes, char **out) {
+    static std::mutex mu;
+    static std::vector<Arena> arenas;
+    std::lock_guard<std::mutex> lock(mu);
+    bytes = std::max<size_t>(bytes, 256);
+    for (auto &a : arenas) {
+        if (a.device != device || a.stream != stream) continue;
+        if (a.size < bytes) {
+            const size_t grow = std::max(bytes, a.size + a.size / 2);
+            HIP_TRY(hipFree(a.ptr));   // waits for the device before freeing
+            a.ptr = nullptr;
+            a.size = 0;
+            HIP_TRY(hipMalloc((void **)&a.ptr, grow));
+            a.size = grow;
+        }
+        *out = a.ptr;
+        return DSP_OK;
+    }
+    Arena a{device, stream, nullptr, bytes};
+    HIP_TRY(hipMalloc((void **)&a.ptr, bytes));
+    arenas.push_back(a);
+    *out = a.ptr;
+    return DSP_OK;
+}
+
+// Carves aligned pieces out of one arena block.
+struct Carve {
+    char *base;
+    size_t off = 0;
+    template <class T>
+    T *take(size_t n) {
+        T *p = (T *)(base + off);
+        off += (n * sizeof(T) + 255) / 256 * 256;
+        return p;
+    }
+};
+inline size_t carve_size(size_t n, size_t elem) { return (n * elem + 255) / 256 * 256; }
+
 double now_ms() {
     using namespace std::chrono;
     return duration<double, std::milli>(steady_clock::now().time_since_epoch()).count();
@@ -547,7 +603,8 @@ struct Layout {
     size_t max_partial = 0;                   // doubles of the largest group's partial sums
     double host_ms = 0.0;                     // time to build
     // device copies
-    PixelRec *d_pixbase = nullptr;            // k, weights, plane offsets (optics fields unset)
+    PixelBase *d_pixbase = nullptr;           // active pixels: k and weights
+    long long *d_goff = nullptr;              // their plane offsets in G
     GramTile *d_tiles = nullptr;
     double *d_prior = nullptr;                // [n_q][a_max]
     int32_t *d_count = nullptr;               // [n_q]
@@ -559,6 +616,7 @@ struct Layout {
     ~Layout() {
         hipSetDevice(key.device);
         hipFree(d_pixbase);
+        hipFree(d_goff);
         hipFree(d_tiles);
         hipFree(d_prior);
         hipFree(d_count);
@@ -642,12 +700,14 @@ dsp_status build_layout(const LayoutKey &key, const dsp_scan *scan, const dsp_op
     }
 
     // device copies (blocking: a layout is built once and reused)
-    if ((st = dev_alloc(&L->d_pixbase, L->act.pix.size())) || (st = dev_alloc(&L->d_tiles, L->tg.tiles.size())) ||
+    if ((st = dev_alloc(&L->d_pixbase, L->act.pix.size())) || (st = dev_alloc(&L->d_goff, L->act.goff.size())) ||
+        (st = dev_alloc(&L->d_tiles, L->tg.tiles.size())) ||
         (st = dev_alloc(&L->d_prior, L->prior.size())) || (st = dev_alloc(&L->d_count, g.count.size())) ||
         (st = dev_alloc(&L->d_K, g.K.size())) || (st = dev_alloc(&L->d_bucket, L->bucket.size())) ||
         (st = dev_alloc(&L->d_sk_wbegin, L->sk_wbegin.size())) || (st = dev_alloc(&L->d_sk_int, L->sk_int.size())))
         return st;
-    HIP_TRY(hipMemcpy(L->d_pixbase, L->act.pix.data(), L->act.pix.size() * sizeof(PixelRec), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(L->d_pixbase, L->act.pix.data(), L->act.pix.size() * sizeof(PixelBase), hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(L->d_goff, L->act.goff.data(), L->act.goff.size() * sizeof(long long), hipMemcpyHostToDevice));
     HIP_TRY(hipMemcpy(L->d_tiles, L->tg.tiles.data(), L->tg.tiles.size() * sizeof(GramTile), hipMemcpyHostToDevice));
     HIP_TRY(hipMemcpy(L->d_prior, L->prior.data(), L->prior.size() * sizeof(double), hipMemcpyHostToDevice));
     HIP_TRY(hipMemcpy(L->d_count, g.count.data(), g.count.size() * sizeof(int32_t), hipMemcpyHostToDevice));
@@ -684,6 +744,153 @@ dsp_status get_layout(const LayoutKey &key, const dsp_scan *scan, const dsp_opti
     if (st) return st;
     g_layouts.insert(g_layouts.begin(), out);
     if (g_layouts.size() > LAYOUT_CACHE_SIZE) g_layouts.pop_back();
+    return DSP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// SSB layout, cached: active pixels, band tiles, stream-K plans per set count
+// ---------------------------------------------------------------------------
+struct SsbKey {
+    int device = 0, n_scan = 0, soft = 0, n_bf = 0, has_band = 0;
+    double step = 0, lam = 0, alpha = 0, dk = 0, lo = 0, hi = 0;
+    std::vector<double> coords, weights;
+    bool operator==(const SsbKey &o) const {
+        return device == o.device && n_scan == o.n_scan && soft == o.soft && n_bf == o.n_bf && has_band == o.has_band &&
+               step == o.step && lam == o.lam && alpha == o.alpha && dk == o.dk && lo == o.lo && hi == o.hi &&
+               coords == o.coords && weights == o.weights;
+    }
+};
+
+struct SsbLayout {
+    SsbKey key;
+    ActiveSet act;
+    std::vector<SsbTile> tiles;
+    // per compiled set count (1, 2, 4, 8): waves, segments, stream-K tables
+    int waves[4] = {0, 0, 0, 0};
+    int n_segs[4] = {0, 0, 0, 0};
+    std::vector<long long> wbegin[4];
+    std::vector<int> seg_off[4], seg_first[4];
+    PixelBase *d_pixbase = nullptr;
+    long long *d_goff = nullptr;
+    SsbTile *d_tiles = nullptr;
+    long long *d_wbegin[4] = {nullptr, nullptr, nullptr, nullptr};
+    int *d_seg_off[4] = {nullptr, nullptr, nullptr, nullptr};
+    int *d_seg_first[4] = {nullptr, nullptr, nullptr, nullptr};
+    double host_ms = 0.0;
+    ~SsbLayout() {
+        hipSetDevice(key.device);
+        hipFree(d_pixbase);
+        hipFree(d_goff);
+        hipFree(d_tiles);
+        for (int i = 0; i < 4; ++i) {
+            hipFree(d_wbegin[i]);
+            hipFree(d_seg_off[i]);
+            hipFree(d_seg_first[i]);
+        }
+    }
+};
+
+int maxb_index(int maxb) { return maxb == 1 ? 0 : (maxb == 2 ? 1 : (maxb == 4 ? 2 : 3)); }
+
+dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const double *coords,
+                            const double *weights, std::shared_ptr<SsbLayout> &out) {
+    const double t0 = now_ms();
+    dsp_status st;
+    auto L = std::make_shared<SsbLayout>();
+    L->key = key;
+    const int N = key.n_scan;
+    const double dq = 1.0 / (N * key.step);
+    if ((st = build_active(coords, weights, key.n_bf, optics, N, L->act))) return st;
+    if (L->act.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
+    // tiles over every stored entry, lanes inside the band
+    for (int yh0 = -N / 2; yh0 <= N / 2 - 1; yh0 += TILE_Y) {
+        for (int ix0 = 0; ix0 <= N / 2; ix0 += TILE_X) {
+            SsbTile t;
+            std::memset(&t, 0, sizeof t);
+            t.yh0 = yh0;
+            t.ix0 = ix0;
+            for (int l = 0; l < 64; ++l) {
+                const int yh = yh0 + l / TILE_X, ix = ix0 + l % TILE_X;
+                if (yh > N / 2 - 1 || ix > N / 2) continue;
+                const double f = std::hypot((double)yh * dq, (double)ix * dq);
+                if (key.has_band && !(f >= key.lo && f <= key.hi)) continue;
+                t.valid |= 1ull << l;
+            }
+            if (t.valid) L->tiles.push_back(t);
+        }
+    }
+    const int n_tiles = (int)L->tiles.size();
+    const int n_pix = (int)L->act.pix.size();
+    if ((st = dev_alloc(&L->d_pixbase, (size_t)n_pix)) || (st = dev_alloc(&L->d_goff, (size_t)n_pix)) ||
+        (st = dev_alloc(&L->d_tiles, (size_t)std::max(1, n_tiles))))
+        return st;
+    HIP_TRY(hipMemcpy(L->d_pixbase, L->act.pix.data(), sizeof(PixelBase) * n_pix, hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(L->d_goff, L->act.goff.data(), sizeof(long long) * n_pix, hipMemcpyHostToDevice));
+    if (n_tiles) HIP_TRY(hipMemcpy(L->d_tiles, L->tiles.data(), sizeof(SsbTile) * n_tiles, hipMemcpyHostToDevice));
+    if (n_tiles) {
+        int n_cu = 0;
+        HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, key.device));
+        const double ra = std::sqrt(make_aperture_dev(optics).rlim2);
+        const double disk = M_PI * ra * ra;
+        static const int maxbs[4] = {1, 2, 4, 8};
+        for (int mi = 0; mi < 4; ++mi) {
+            const int maxb = maxbs[mi];
+            // per tile: fixed per-pixel work plus the sets' lobes (two lenses at the tile centre)
+            std::vector<double> cost(n_tiles);
+            for (int t = 0; t < n_tiles; ++t) {
+                const SsbTile &tt = L->tiles[t];
+                const double D = std::hypot((tt.yh0 + 1.5) * dq, (tt.ix0 + 7.5) * dq);
+                double lens = 0.0;
+                if (D < 2.0 * ra)
+                    lens = 2.0 * ra * ra * std::acos(D / (2.0 * ra)) - 0.5 * D * std::sqrt(4.0 * ra * ra - D * D);
+                cost[t] = n_pix * 40.0 + 80.0 * maxb * 2.0 * lens / disk * n_pix;
+            }
+            int bpc = 0;
+            HIP_TRY(ssb_occupancy(maxb, &bpc));
+            bpc = std::max(1, bpc);
+            const long long total_it = (long long)n_tiles * n_pix;
+            const int W = (int)std::max(1LL, std::min((long long)bpc * n_cu * GRAM_ROUNDS, total_it / 64));
+            StreamKPlan plan;
+            plan_stream_k(cost, n_pix, W, plan);
+            L->waves[mi] = W;
+            L->n_segs[mi] = plan.n_segs;
+            L->wbegin[mi] = plan.wbegin;
+            L->seg_off[mi] = plan.seg_off;
+            L->seg_first[mi] = plan.seg_first;
+            if ((st = dev_alloc(&L->d_wbegin[mi], plan.wbegin.size())) ||
+                (st = dev_alloc(&L->d_seg_off[mi], plan.seg_off.size())) ||
+                (st = dev_alloc(&L->d_seg_first[mi], plan.seg_first.size())))
+                return st;
+            HIP_TRY(hipMemcpy(L->d_wbegin[mi], plan.wbegin.data(), plan.wbegin.size() * sizeof(long long),
+                              hipMemcpyHostToDevice));
+            HIP_TRY(hipMemcpy(L->d_seg_off[mi], plan.seg_off.data(), plan.seg_off.size() * sizeof(int),
+                              hipMemcpyHostToDevice));
+            HIP_TRY(hipMemcpy(L->d_seg_first[mi], plan.seg_first.data(), plan.seg_first.size() * sizeof(int),
+                              hipMemcpyHostToDevice));
+        }
+    }
+    L->host_ms = now_ms() - t0;
+    out = L;
+    return DSP_OK;
+}
+
+std::vector<std::shared_ptr<SsbLayout>> g_ssb_layouts;   // front = most recent (under g_layout_mu)
+
+dsp_status get_ssb_layout(const SsbKey &key, const dsp_optics *optics, const double *coords, const double *weights,
+                          std::shared_ptr<SsbLayout> &out) {
+    std::lock_guard<std::mutex> lock(g_layout_mu);
+    for (size_t i = 0; i < g_ssb_layouts.size(); ++i) {
+        if (g_ssb_layouts[i]->key == key) {
+            out = g_ssb_layouts[i];
+            g_ssb_layouts.erase(g_ssb_layouts.begin() + i);
+            g_ssb_layouts.insert(g_ssb_layouts.begin(), out);
+            return DSP_OK;
+        }
+    }
+    dsp_status st = build_ssb_layout(key, optics, coords, weights, out);
+    if (st) return st;
+    g_ssb_layouts.insert(g_ssb_layouts.begin(), out);
+    if (g_ssb_layouts.size() > LAYOUT_CACHE_SIZE) g_ssb_layouts.pop_back();
     return DSP_OK;
 }
 
@@ -887,26 +1094,32 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     }
     const ApertureDev apd = make_aperture_dev(optics);
     const OpticsDev opd = make_optics_dev(optics);
-    HIP_TRY(launch_pixel_terms(L.d_pixbase, h->d_pix, n_pix, apd, opd, nullptr, stream));
+    HIP_TRY(launch_pixel_terms(L.d_pixbase, h->d_pix, n_pix, apd, opd, nullptr, 0, stream));
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[1], stream));
 
     GramParams gp;
     std::memset(&gp, 0, sizeof gp);
     gp.G = (const float2 *)G_c64_dev;
     gp.pix = h->d_pix;
+    gp.goff = L.d_goff;
     gp.n_pix = n_pix;
     gp.N = g.N;
     gp.nh = g.N / 2 + 1;
     gp.dq = g.dq;
+    gp.ldq = optics->wavelength_A * g.dq;
     gp.ap = apd;
     gp.op = opd;
     gp.sys = h->d_sys;
     gp.a_max = am;
     gp.D = h->D;
     if ((st = trig_table_device(h->device, &gp.trig))) return st;
-    // partial sums live only for the Gram stage (stream-ordered)
+    // partial sums live only for the Gram stage (the stream's scratch arena)
     double *d_partial = nullptr;
-    HIP_TRY(hipMallocAsync((void **)&d_partial, std::max<size_t>(1, L.max_partial) * sizeof(double), stream));
+    {
+        char *scr = nullptr;
+        if ((st = arena_get(h->device, stream, std::max<size_t>(1, L.max_partial) * sizeof(double), &scr))) return st;
+        d_partial = (double *)scr;
+    }
 
     // largest groups first
     const int n_groups = (int)L.tg.group_nj.size();
@@ -932,7 +1145,6 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
         HIP_TRY(launch_gram_fixup(gp, L.tg.group_nj[gi], h->method, L.tg.group_n[gi], stream));
         if (h->timing) HIP_TRY(hipEventRecord(h->gram_ev[3 * oi + 2], stream));
     }
-    HIP_TRY(hipFreeAsync(d_partial, stream));
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[2], stream));
 
     if (h->method == DSP_PHASE) {
@@ -1149,46 +1361,64 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
     if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
     if (n_bf <= 0 || !bf_coords_host) return fail(DSP_EINVAL, "n_bf must be > 0 with bf_coords");
     if (band_invA && !(band_invA[0] <= band_invA[1])) return fail(DSP_EINVAL, "band must satisfy lo <= hi");
+    for (int i = 0; i < 2 * n_bf; ++i)
+        if (!std::isfinite(bf_coords_host[i])) return fail(DSP_EINVAL, "bf_coords[%d] not finite", i / 2);
+    if (weights_host)
+        for (int i = 0; i < n_bf; ++i)
+            if (!(weights_host[i] >= 0.0) || !std::isfinite(weights_host[i]))
+                return fail(DSP_EINVAL, "weights[%d] must be finite and >= 0", i);
     hipStream_t stream = (hipStream_t)hip_stream;
     const int N = scan->n_scan, nh = N / 2 + 1;
     const double dq = 1.0 / (N * scan->step_A);
+    int device = 0;
+    HIP_TRY(hipGetDevice(&device));
 
-    ActiveSet as;
-    if ((st = build_active(bf_coords_host, weights_host, n_bf, sets_host, N, as))) return st;
-    if (as.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
-    // tiles over every stored entry, lanes inside the band
-    std::vector<SsbTile> tiles;
-    for (int yh0 = -N / 2; yh0 <= N / 2 - 1; yh0 += TILE_Y) {
-        for (int ix0 = 0; ix0 <= N / 2; ix0 += TILE_X) {
-            SsbTile t;
-            std::memset(&t, 0, sizeof t);
-            t.yh0 = yh0;
-            t.ix0 = ix0;
-            for (int l = 0; l < 64; ++l) {
-                const int yh = yh0 + l / TILE_X, ix = ix0 + l % TILE_X;
-                if (yh > N / 2 - 1 || ix > N / 2) continue;
-                const double f = std::hypot((double)yh * dq, (double)ix * dq);
-                if (band_invA && !(f >= band_invA[0] && f <= band_invA[1])) continue;
-                t.valid |= 1ull << l;
-            }
-            if (t.valid) tiles.push_back(t);
-        }
-    }
-    const int n_tiles = (int)tiles.size();
-    const int n_pix = (int)as.pix.size();
+    SsbKey key;
+    key.device = device;
+    key.n_scan = N;
+    key.step = scan->step_A;
+    key.soft = sets_host[0].soft_aperture;
+    key.lam = sets_host[0].wavelength_A;
+    key.alpha = sets_host[0].semiangle_rad;
+    key.dk = sets_host[0].det_step_invA;
+    key.has_band = band_invA ? 1 : 0;
+    key.lo = band_invA ? band_invA[0] : 0.0;
+    key.hi = band_invA ? band_invA[1] : 0.0;
+    key.n_bf = n_bf;
+    key.coords.assign(bf_coords_host, bf_coords_host + 2 * (size_t)n_bf);
+    if (weights_host) key.weights.assign(weights_host, weights_host + n_bf);
+    std::shared_ptr<SsbLayout> lay;
+    if ((st = get_ssb_layout(key, sets_host, bf_coords_host, weights_host, lay))) return st;
+    const SsbLayout &L = *lay;
+    const int n_tiles = (int)L.tiles.size();
+    const int n_pix = (int)L.act.pix.size();
+    const int maxb = ssb_maxb(B);
+    const int mi = maxb_index(maxb);
     const int stride = ssb_partial_stride(B);
+    const size_t plane = (size_t)N * nh;
+    if (S_out_c128_dev && band_invA) HIP_TRY(launch_fill_zero((double *)S_out_c128_dev, (size_t)B * plane * 2, stream));
+    if (norm_out_dev && band_invA) HIP_TRY(launch_fill_zero(norm_out_dev, (size_t)B * plane, stream));
+    if (n_tiles == 0) {
+        if (agreement_out_host) {
+            HIP_TRY(hipStreamSynchronize(stream));
+            for (int b = 0; b < B; ++b) agreement_out_host[b] = 0.0;
+        }
+        return DSP_OK;
+    }
 
-    PixelRec *d_pix = nullptr;
-    SsbTile *d_tiles = nullptr;
-    double *d_chi = nullptr, *d_part = nullptr, *d_E = nullptr;
-    HIP_TRY(hipMallocAsync((void **)&d_pix, sizeof(PixelRec) * n_pix, stream));
-    HIP_TRY(hipMallocAsync((void **)&d_tiles, sizeof(SsbTile) * std::max(1, n_tiles), stream));
-    HIP_TRY(hipMallocAsync((void **)&d_chi, sizeof(double) * (size_t)B * n_pix, stream));
-    HIP_TRY(hipMallocAsync((void **)&d_part, sizeof(double) * (size_t)std::max(1, n_tiles) * stride, stream));
-    HIP_TRY(hipMallocAsync((void **)&d_E, sizeof(double) * (B + 1), stream));
-    HIP_TRY(hipMemcpyAsync(d_pix, as.pix.data(), sizeof(PixelRec) * n_pix, hipMemcpyHostToDevice, stream));
-    if (n_tiles)
-        HIP_TRY(hipMemcpyAsync(d_tiles, tiles.data(), sizeof(SsbTile) * n_tiles, hipMemcpyHostToDevice, stream));
+    // per-call tables in the stream's scratch arena
+    const size_t n_part = (size_t)L.n_segs[mi] * ssb_nacc(maxb) * 64;
+    const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) +
+                        carve_size(n_part, sizeof(double)) + carve_size((size_t)n_tiles * stride, sizeof(double)) +
+                        carve_size(B + 1, sizeof(double));
+    char *scr = nullptr;
+    if ((st = arena_get(device, stream, need, &scr))) return st;
+    Carve cv{scr};
+    PixelRec *d_pix = cv.take<PixelRec>(n_pix);
+    double *d_chi = cv.take<double>((size_t)MAX_SETS_DEV * n_pix);
+    double *d_part = cv.take<double>(n_part);
+    double *d_tile_part = cv.take<double>((size_t)n_tiles * stride);
+    double *d_E = cv.take<double>(B + 1);
 
     const ApertureDev apd = make_aperture_dev(sets_host);
     SsbParams sp;
@@ -1196,48 +1426,41 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
     for (int b = 0; b < B; ++b) {
         const OpticsDev od = make_optics_dev(sets_host + b);
         // a(k) once (set 0 writes it), chi(k) per set
-        if (b == 0) HIP_TRY(launch_pixel_terms(d_pix, d_pix, n_pix, apd, od, nullptr, stream));
-        HIP_TRY(launch_pixel_terms(d_pix, d_pix, n_pix, apd, od, d_chi + (size_t)b * n_pix, stream));
+        if (b == 0) HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, od, nullptr, 0, stream));
+        HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, od, d_chi + b, MAX_SETS_DEV, stream));
         sp.tau_y[b] = od.tau_y;
         sp.tau_x[b] = od.tau_x;
         std::memcpy(sp.chi_c[b], od.chi_c, sizeof od.chi_c);
     }
-    const size_t plane = (size_t)N * nh;
-    if (S_out_c128_dev && band_invA) HIP_TRY(launch_fill_zero((double *)S_out_c128_dev, (size_t)B * plane * 2, stream));
-    if (norm_out_dev && band_invA) HIP_TRY(launch_fill_zero(norm_out_dev, (size_t)B * plane, stream));
     sp.G = (const float2 *)G_c64_dev;
     sp.pix = d_pix;
+    sp.goff = L.d_goff;
     sp.chi_tab = d_chi;
     sp.n_pix = n_pix;
-    sp.tiles = d_tiles;
+    sp.tiles = L.d_tiles;
     sp.N = N;
     sp.nh = nh;
     sp.dq = dq;
+    sp.ldq = sets_host[0].wavelength_A * dq;
     sp.B = B;
     sp.ap = apd;
     sp.lam = sets_host[0].wavelength_A;
     sp.S_out = (double2 *)S_out_c128_dev;
     sp.N_out = norm_out_dev;
+    sp.wbegin = L.d_wbegin[mi];
+    sp.seg_off = L.d_seg_off[mi];
+    sp.seg_first = L.d_seg_first[mi];
     sp.partial = d_part;
-    int device = 0;
-    HIP_TRY(hipGetDevice(&device));
     if ((st = trig_table_device(device, &sp.trig))) return st;
-    HIP_TRY(launch_ssb(sp, n_tiles, stream));
+    HIP_TRY(launch_ssb(sp, L.waves[mi], n_tiles, d_tile_part, stream));
     std::vector<double> E(B + 1, 0.0);
     if (agreement_out_host) {
-        if (n_tiles) {
-            HIP_TRY(launch_agreement(d_part, n_tiles, B, d_E, stream));
-            HIP_TRY(hipMemcpyAsync(E.data(), d_E, sizeof(double) * (B + 1), hipMemcpyDeviceToHost, stream));
-        }
+        HIP_TRY(launch_agreement(d_tile_part, n_tiles, B, d_E, stream));
+        HIP_TRY(hipMemcpyAsync(E.data(), d_E, sizeof(double) * (B + 1), hipMemcpyDeviceToHost, stream));
     }
-    HIP_TRY(hipFreeAsync(d_pix, stream));
-    HIP_TRY(hipFreeAsync(d_tiles, stream));
-    HIP_TRY(hipFreeAsync(d_chi, stream));
-    HIP_TRY(hipFreeAsync(d_part, stream));
-    HIP_TRY(hipFreeAsync(d_E, stream));
     if (agreement_out_host) {
         HIP_TRY(hipStreamSynchronize(stream));
-        for (int b = 0; b < B; ++b) agreement_out_host[b] = n_tiles ? E[b] : 0.0;
+        for (int b = 0; b < B; ++b) agreement_out_host[b] = E[b];
     }
     return DSP_OK;
 }

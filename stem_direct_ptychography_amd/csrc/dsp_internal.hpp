@@ -42,18 +42,27 @@ __host__ __device__ constexpr int tri_size(int n) { return n * (n + 1) / 2; }
 // ---------------------------------------------------------------------------
 // device tables
 // ---------------------------------------------------------------------------
-// One active bright-field pixel; 64-byte records so a wave reads one with a
-// single scalar load.  The weight enters the Gram through sqrt(w): with
-// u = sqrt(w) T and g' = sqrt(w) g, u^H u = T^H W T, u^H g' = T^H W g and
-// |g'|^2 = g^H W g, so the per-pixel update needs no weight products.
-struct alignas(64) PixelRec {
+// One active bright-field pixel as given: k (1/A, scan frame) and its weight.
+struct PixelBase {
     double ky, kx;     // 1/A, scan frame
-    double amp0;       // sqrt(w) a(k)              (pixel-terms kernel)
+    double w, sw;      // weight and sqrt(w)
+};
+
+// Per-prepare pixel record.  Lengths are scaled by lambda, so theta =
+// lambda (k -/+ Q) + tau is the pixel's theta(k) = lambda k + tau minus or
+// plus lambda Q, and the support test of k' = k -/+ Q is |lambda k|^2 +
+// |lambda Q|^2 -/+ 2 (lambda k).(lambda Q) against (lambda r)^2.  The kernels
+// form theta(k) = lky + tau_y (a separately rounded add, as chi0 was built),
+// so at Q = 0 the two phases agree exactly.  The weight enters the Gram
+// through sqrt(w): with u = sqrt(w) T and g' = sqrt(w) g, u^H u = T^H W T,
+// u^H g' = T^H W g and |g'|^2 = g^H W g, so the update needs no weight
+// products.
+struct alignas(16) PixelRec {
+    double lky, lkx;   // lambda k (rounded products)
+    double amp0;       // sqrt(w) a(k)
     double sw;         // sqrt(w)
-    double chi0;       // chi(k) of the prepare's optics (pixel-terms kernel)
-    long long goff;    // element offset of the pixel's plane in G
-    double w;          // weight
-    double a0;         // aperture a(k)             (pixel-terms kernel)
+    double chi0;       // chi(theta(k)), theta(k) = (lky + tau_y, lkx + tau_x)
+    double pad;
 };
 
 // ---------------------------------------------------------------------------
@@ -125,6 +134,11 @@ struct ApertureDev {
     double rout2;    // (kc + dk/2)^2 : a == 0 outside (soft); kc^2 (hard)
     double rlim2;    // support is |k|^2 < rlim2: rout2 (soft, strict) or the
                      // next double above kc^2 (hard, |k|^2 <= kc^2)
+    // the same in lambda-scaled lengths (|lambda k'|^2 against these)
+    double lrlim2;   // lambda^2 rlim2
+    double lrin2;    // lambda^2 rin2
+    double lkc;      // lambda kc
+    double inv_ldk;  // 1 / (lambda dk)
     int soft;
 };
 
@@ -137,10 +151,12 @@ struct ApertureDev {
 struct GramParams {
     const float2 *G;
     const PixelRec *pix;
+    const long long *goff;     // [n_pix] element offset of each pixel's plane in G
     int n_pix;
     const GramTile *tiles;
     int N, nh;
     double dq;
+    double ldq;                // lambda dq
     ApertureDev ap;
     OpticsDev op;
     double2 *sys;     // [n_q][tri_size(D)] packed augmented systems, slot coordinates
@@ -153,14 +169,20 @@ struct GramParams {
     const double2 *trig;       // [TRIG_N] (cos, sin)(j pi / 32)
 };
 
+constexpr int MAX_SETS_DEV = 8;   // optics sets of one SSB pass
+
+// SSB pass: stream-K over (band tile, pixel) like the Gram launches, with
+// partial sums [n_segments][3 MAXB + 1][64].
 struct SsbParams {
     const float2 *G;
     const PixelRec *pix;
-    const double *chi_tab;   // [B][n_pix]
+    const long long *goff;   // [n_pix]
+    const double *chi_tab;   // [n_pix][MAX_SETS_DEV] chi(k) per set
     int n_pix;
     const SsbTile *tiles;
     int N, nh;
     double dq;
+    double ldq;              // lambda dq
     int B;
     ApertureDev ap;
     double lam;
@@ -168,7 +190,10 @@ struct SsbParams {
     double chi_c[8][CHI_NCOEF];
     double2 *S_out;          // [B][N][nh] or null
     double *N_out;           // [B][N][nh] or null
-    double *partial;         // [n_tiles][B + 1]
+    const long long *wbegin; // [n_waves + 1]
+    const int *seg_off;      // [n_waves]
+    const int *seg_first;    // [n_tiles + 1]
+    double *partial;         // [n_segments][3 MAXB + 1][64]
     const double2 *trig;     // [TRIG_N] (cos, sin)(j pi / 32)
 };
 

@@ -20,6 +20,8 @@
 #include "dsp_internal.hpp"
 #include "dsp_kernels.hpp"
 
+#include <cstring>
+
 namespace dsp {
 
 // ---------------------------------------------------------------------------
@@ -47,25 +49,30 @@ __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 // pixel terms: a(k) and chi(k) once per pixel and optics set
 // ---------------------------------------------------------------------------
 
-// in[p] -> out[p] with a(k), sqrt(w) a(k) and chi(k) filled in, or (chi_tab
-// non-null) chi(k) alone into chi_tab[p].  in and out may be the same array.
-__global__ void pixel_terms_kernel(const PixelRec *in, PixelRec *out, int n_pix, ApertureDev ap, OpticsDev op,
-                                   double *chi_tab) {
+// in[p] -> out[p]: lambda k, sqrt(w) a(k) and chi(theta(k)), theta(k) =
+// lambda k + tau formed as a rounded product then a rounded add (never
+// fused), exactly as the Gram and SSB kernels form it; with chi_tab
+// non-null, chi alone into chi_tab[p * chi_stride] (an SSB pass's sets).
+__global__ void pixel_terms_kernel(const PixelBase *in, PixelRec *out, int n_pix, ApertureDev ap, OpticsDev op,
+                                   double *chi_tab, int chi_stride) {
+#pragma clang fp contract(off)
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= n_pix) return;
     const double ky = in[p].ky, kx = in[p].kx;
-    const double d2 = fma(ky, ky, kx * kx);
-    const double c = chi_poly(op.chi_c, fma(op.lam, kx, op.tau_x), fma(op.lam, ky, op.tau_y));
+    const double lky = op.lam * ky, lkx = op.lam * kx;
+    const double c = chi_poly(op.chi_c, lkx + op.tau_x, lky + op.tau_y);
     if (chi_tab) {
-        chi_tab[p] = c;
-    } else {
-        PixelRec r = in[p];
-        const double a0 = aperture_at(ap, d2);
-        r.a0 = a0;
-        r.amp0 = r.sw * a0;
-        r.chi0 = c;
-        out[p] = r;
+        chi_tab[(size_t)p * chi_stride] = c;
+        return;
     }
+    PixelRec r;
+    r.lky = lky;
+    r.lkx = lkx;
+    r.amp0 = in[p].sw * aperture_at(ap, fma(ky, ky, kx * kx));
+    r.sw = in[p].sw;
+    r.chi0 = c;
+    r.pad = 0.0;
+    out[p] = r;
 }
 
 // ---------------------------------------------------------------------------
@@ -180,25 +187,31 @@ struct GramWaves {
     static constexpr int value = METHOD == 0 ? (NJ <= 2 ? 4 : (NJ <= 6 ? 2 : 1)) : (NJ <= 1 ? 4 : (NJ <= 3 ? 2 : 1));
 };
 
-// Pixel records are read through the constant address space so that the
-// wave-uniform fields land in scalar registers (one scalar load per field).
-typedef const __attribute__((address_space(4))) PixelRec ConstPixel;
+// Pixel records and plane offsets are written by earlier kernels or copies,
+// so they are read with ordinary (vector) loads: reading them through the
+// constant address space (scalar loads) returned stale values when a freed
+// buffer's address was reused by the next prepare.  Only the kernel
+// arguments, which the host writes for each launch, go through scalar loads.
+typedef const PixelRec ConstPixel;
+typedef const long long ConstLong;
 
 // One lobe of the transfer at the pixel (chi0 = chi(k), amp0 = sqrt(w) a(k))
-// and the displaced point k' = k -/+ Q given as e = k' (1/A, scan frame) with
-// |e|^2 = d2 inside the support:
-//   value = amp0 a(k') exp(i sgn (chi0 - chi(k'))), sgn = +1 (L), -1 (R).
+// and the displaced point k' = k -/+ Q, given by theta' = lambda k' + tau and
+// d2 = |lambda k'|^2 (inside the support):
+//   value = amp0 a(k') exp(i sgn (chi0 - chi(theta'))), sgn = +1 (L), -1 (R).
 // a(k') = 1 except in the soft edge ring; the square root runs only when some
-// lane of the wave is in the ring.
-__device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, double ey, double ex, double d2,
+// lane of the wave is in the ring (the empty asm keeps the compiler from
+// computing it unconditionally).
+__device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, double ty, double tx, double d2,
                                      double chi0, double amp0, double sgn, double &re, double &im) {
-    const double c1 = chi_poly(prm.op.chi_c, fma(prm.op.lam, ex, prm.op.tau_x), fma(prm.op.lam, ey, prm.op.tau_y));
+    const double c1 = chi_poly(prm.op.chi_c, tx, ty);
     double sn, cs;
     sincos_tab(sgn * (chi0 - c1), T, sn, cs);
     double amp = amp0;
-    const bool ring = d2 > prm.ap.rin2;
+    const bool ring = d2 > prm.ap.lrin2;
     if (wave_any(ring)) {
-        if (ring) amp *= fma(prm.ap.kc - sqrt(d2), prm.ap.inv_dk, 0.5);
+        asm volatile("");
+        if (ring) amp *= fma(prm.ap.lkc - sqrt(d2), prm.ap.inv_ldk, 0.5);
     }
     re = amp * cs;
     im = amp * sn;
@@ -209,7 +222,7 @@ __device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, do
 // METHOD 1 (complex): columns L(slot 0..NJ-1), R(slot 0..NJ-1), then g; the
 // write-out turns them into [T_A, T_phi] (T_A = L + R, T_phi = i (L - R)),
 // which keeps the per-pixel update to the lobes actually present.
-// Lane = frequency of the tile; pixel records are wave-uniform scalar loads.
+// Lane = frequency of the tile; pixel records are wave-uniform.
 // While pixel p is used, G for p + 1 is in flight (its plane offset was read
 // one pixel earlier) and the record of p + 1 and the offset of p + 2 load.
 template <int NJ, int METHOD>
@@ -229,8 +242,10 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
     const long long end = prm.wbegin[wv + 1];
     int seg = prm.seg_off[wv];
     ConstPixel *pix = (ConstPixel *)prm.pix;
+    ConstLong *goffs = (ConstLong *)prm.goff;
     const float2 *__restrict__ G = prm.G;
-    const double rlim2 = prm.ap.rlim2;
+    const double lrlim2 = prm.ap.lrlim2;
+    const double tau_y = prm.op.tau_y, tau_x = prm.op.tau_x;
 
     while (it < end) {
         const int t = (int)(it / n_pix);
@@ -244,12 +259,14 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
         const int iy = yh < 0 ? yh + prm.N : yh;
         const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
 
-        double Qy[NJ], Qx[NJ];
+        // lambda Q per slot and |lambda Q|^2
+        double Qy[NJ], Qx[NJ], Q2[NJ];
         bool act[NJ];
 #pragma unroll
         for (int s = 0; s < NJ; ++s) {
-            Qy[s] = (double)(yh + (int)tile->jy[s] * prm.N) * prm.dq;
-            Qx[s] = (double)(ix + (int)tile->jx[s] * prm.N) * prm.dq;
+            Qy[s] = (double)(yh + (int)tile->jy[s] * prm.N) * prm.ldq;
+            Qx[s] = (double)(ix + (int)tile->jx[s] * prm.N) * prm.ldq;
+            Q2[s] = fma(Qy[s], Qy[s], Qx[s] * Qx[s]);
             act[s] = (mask >> s) & 1u;
         }
 
@@ -257,16 +274,18 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
 #pragma unroll
         for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
 
-        double ky = pix[p0].ky, kx = pix[p0].kx, amp0 = pix[p0].amp0, sw = pix[p0].sw, chi0 = pix[p0].chi0;
-        float2 gv = G[pix[p0].goff + lane_off];
-        long long goff1 = pix[p0 + 1 < p1 ? p0 + 1 : p0].goff;
+        double lky = pix[p0].lky, lkx = pix[p0].lkx, amp0 = pix[p0].amp0, sw = pix[p0].sw, chi0 = pix[p0].chi0;
+        float2 gv = G[goffs[p0] + lane_off];
+        long long goff1 = goffs[p0 + 1 < p1 ? p0 + 1 : p0];
         for (int p = p0; p < p1; ++p) {
             const int pn = p + 1 < p1 ? p + 1 : p;
             const int pnn = pn + 1 < p1 ? pn + 1 : pn;
             const float2 ngv = G[goff1 + lane_off];
-            const long long goff2 = pix[pnn].goff;
-            const double nky = pix[pn].ky, nkx = pix[pn].kx, namp0 = pix[pn].amp0, nsw = pix[pn].sw,
+            const long long goff2 = goffs[pnn];
+            const double nlky = pix[pn].lky, nlkx = pix[pn].lkx, namp0 = pix[pn].amp0, nsw = pix[pn].sw,
                          nchi0 = pix[pn].chi0;
+            const double lk2 = fma(lky, lky, lkx * lkx);
+            const double py = lky + tau_y, px = lkx + tau_x;
 
             const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
             acc[NC] = fma(gr, gr, fma(gi, gi, acc[NC]));   // signal power w |g|^2
@@ -275,15 +294,16 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
             bool nz[NC];
 #pragma unroll
             for (int s = 0; s < NJ; ++s) {
-                const double ey = ky - Qy[s], ex = kx - Qx[s];
-                const double fy = ky + Qy[s], fx = kx + Qx[s];
-                const double dm2 = fma(ey, ey, ex * ex);
-                const double dp2 = fma(fy, fy, fx * fx);
-                const bool zl = act[s] && dm2 < rlim2;
-                const bool zr = act[s] && dp2 < rlim2;
+                // |lambda (k -/+ Q)|^2 = |lambda k|^2 + |lambda Q|^2 -/+ 2 (lambda k).(lambda Q)
+                const double kq = fma(lky, Qy[s], lkx * Qx[s]);
+                const double base = lk2 + Q2[s];
+                const double dm2 = fma(-2.0, kq, base);
+                const double dp2 = fma(2.0, kq, base);
+                const bool zl = act[s] && dm2 < lrlim2;
+                const bool zr = act[s] && dp2 < lrlim2;
                 double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
-                if (zl) lobe(prm, T, ey, ex, dm2, chi0, amp0, 1.0, Lr, Li);
-                if (zr) lobe(prm, T, fy, fx, dp2, chi0, amp0, -1.0, Rr, Ri);
+                if (zl) lobe(prm, T, py - Qy[s], px - Qx[s], dm2, chi0, amp0, 1.0, Lr, Li);
+                if (zr) lobe(prm, T, py + Qy[s], px + Qx[s], dp2, chi0, amp0, -1.0, Rr, Ri);
                 if (METHOD == 0) {
                     tr[s] = Ri - Li;   // T_phi = i (L - R)
                     ti[s] = Lr - Rr;
@@ -315,8 +335,8 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
                     acc[Sh::im(c, d)] = fma(tr[c], ti[d], fma(-ti[c], tr[d], acc[Sh::im(c, d)]));
                 }
             }
-            ky = nky;
-            kx = nkx;
+            lky = nlky;
+            lkx = nlkx;
             amp0 = namp0;
             sw = nsw;
             chi0 = nchi0;
@@ -379,15 +399,16 @@ __global__ __launch_bounds__(64) void work_count_kernel(GramParams prm, unsigned
     const int nj = tile->nj;
     unsigned long long tests = 0, lobes = 0, cols = 0, pairs = 0, terms = 0;
     for (int p = 0; p < prm.n_pix; ++p) {
-        const double ky = prm.pix[p].ky, kx = prm.pix[p].kx;
+        const double lky = prm.pix[p].lky, lkx = prm.pix[p].lkx, lk2 = fma(lky, lky, lkx * lkx);
         unsigned long long nc = 0;
         for (int s = 0; s < nj; ++s) {
             if (!((mask >> s) & 1u)) continue;
-            const double Qy = (double)(yh + (int)tile->jy[s] * prm.N) * prm.dq;
-            const double Qx = (double)(ix + (int)tile->jx[s] * prm.N) * prm.dq;
-            const double dy = ky - Qy, dx = kx - Qx, ey = ky + Qy, ex = kx + Qx;
-            const bool zl = fma(dy, dy, dx * dx) < prm.ap.rlim2;
-            const bool zr = fma(ey, ey, ex * ex) < prm.ap.rlim2;
+            const double Qy = (double)(yh + (int)tile->jy[s] * prm.N) * prm.ldq;
+            const double Qx = (double)(ix + (int)tile->jx[s] * prm.N) * prm.ldq;
+            const double kq = fma(lky, Qy, lkx * Qx);
+            const double base = lk2 + fma(Qy, Qy, Qx * Qx);
+            const bool zl = fma(-2.0, kq, base) < prm.ap.lrlim2;
+            const bool zr = fma(2.0, kq, base) < prm.ap.lrlim2;
             tests += 2;
             lobes += (zl ? 1 : 0) + (zr ? 1 : 0);
             if (METHOD == 0) nc += (zl || zr) ? 1 : 0;
@@ -803,118 +824,163 @@ __global__ void export_kernel(const double2 *sys, int n_q, int D, double2 *dense
 // SSB / agreement pass
 // ---------------------------------------------------------------------------
 
-template <int MAXB, int P>
-__global__ __launch_bounds__(64 * P) void ssb_kernel(SsbParams prm) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// Waves per SIMD the SSB kernel must fit.
+template <int MAXB>
+struct SsbWaves {
+    static constexpr int value = MAXB <= 2 ? 4 : 2;
+};
+
+// SSB sums over one wave's stream-K range of (band tile, pixel) iterations;
+// lane = stored frequency q (one alias, Q = q).  Per set b:
+//   Gamma_b = T_phi(q, k; b) = i (L_b - R_b),
+//   S_b += w conj(Gamma_b) g,  N_b += w |Gamma_b|^2,  and P += w |g|^2.
+// The support, a(k -/+ q), G and the weight are shared by the sets; chi and
+// its phase factor are per set.  Partial layout: [3b] Re S_b, [3b+1] Im S_b,
+// [3b+2] N_b, [3 MAXB] P.
+template <int MAXB>
+__global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbParams prm) {
+    constexpr int NACC = 3 * MAXB + 1;
     __shared__ double2 T[TRIG_N];
-    if (threadIdx.x < TRIG_N) T[threadIdx.x] = prm.trig[threadIdx.x];
+    const int lane = threadIdx.x;
+    T[lane] = prm.trig[lane];
     __syncthreads();
-    const SsbTile *tile = prm.tiles + blockIdx.x;
+
+    const int wv = blockIdx.x;
+    const long long n_pix = prm.n_pix;
+    long long it = prm.wbegin[wv];
+    const long long end = prm.wbegin[wv + 1];
+    int seg = prm.seg_off[wv];
+    ConstPixel *pix = (ConstPixel *)prm.pix;
+    ConstLong *goffs = (ConstLong *)prm.goff;
+    const double *__restrict__ chi_tab = prm.chi_tab;
+    const float2 *__restrict__ G = prm.G;
+    const double lrlim2 = prm.ap.lrlim2, lrin2 = prm.ap.lrin2, lkc = prm.ap.lkc, inv_ldk = prm.ap.inv_ldk;
+    const int B = prm.B;
+
+    while (it < end) {
+        const int t = (int)(it / n_pix);
+        const int p0 = (int)(it - (long long)t * n_pix);
+        const int p1 = (int)((end - it) < (n_pix - p0) ? p0 + (end - it) : n_pix);
+        const SsbTile *tile = prm.tiles + t;
+        const int yh = tile->yh0 + (lane >> 4);
+        const int ix = tile->ix0 + (lane & 15);
+        const bool valid = (tile->valid >> lane) & 1ull;
+        const int iy = yh < 0 ? yh + prm.N : yh;
+        const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
+        const double qy = (double)yh * prm.ldq, qx = (double)ix * prm.ldq;   // lambda q
+        const double q2 = fma(qy, qy, qx * qx);
+
+        double acc[NACC];
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
+
+        double lky = pix[p0].lky, lkx = pix[p0].lkx, amp0 = pix[p0].amp0, sw = pix[p0].sw;
+        float2 gv = G[goffs[p0] + lane_off];
+        long long goff1 = goffs[p0 + 1 < p1 ? p0 + 1 : p0];
+        for (int p = p0; p < p1; ++p) {
+            const int pn = p + 1 < p1 ? p + 1 : p;
+            const int pnn = pn + 1 < p1 ? pn + 1 : pn;
+            const float2 ngv = G[goff1 + lane_off];
+            const long long goff2 = goffs[pnn];
+            const double nlky = pix[pn].lky, nlkx = pix[pn].lkx, namp0 = pix[pn].amp0, nsw = pix[pn].sw;
+            const double lk2 = fma(lky, lky, lkx * lkx);
+
+            const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
+            acc[NACC - 1] = fma(gr, gr, fma(gi, gi, acc[NACC - 1]));
+            const double kq = fma(lky, qy, lkx * qx);
+            const double base = lk2 + q2;
+            const double dm2 = fma(-2.0, kq, base), dp2 = fma(2.0, kq, base);
+            const bool zl = valid && dm2 < lrlim2;
+            const bool zr = valid && dp2 < lrlim2;
+            double aml = amp0, amr = amp0;
+            const bool rl = zl && dm2 > lrin2, rr = zr && dp2 > lrin2;
+            if (wave_any(rl || rr)) {
+                asm volatile("");
+                if (rl) aml *= fma(lkc - sqrt(dm2), inv_ldk, 0.5);
+                if (rr) amr *= fma(lkc - sqrt(dp2), inv_ldk, 0.5);
+            }
+#pragma unroll
+            for (int b = 0; b < MAXB; ++b) {
+                if (b >= B) break;
+                const double chi0 = chi_tab[(size_t)p * MAX_SETS_DEV + b];
+                // The set's coefficients are read from the kernel arguments
+                // per use (scalar loads, constant cache): an opaque zero
+                // offset keeps the compiler from hoisting all sets' values
+                // into scalar registers, which would spill.
+                int zb = 0;
+                if (MAXB > 1) asm volatile("" : "+s"(zb));
+                const double *cb = &prm.chi_c[b][zb];
+                // theta(k) = lambda k + tau_b exactly as chi0 was formed, then -/+ lambda q
+                const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
+                double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
+                if (zl) {
+                    const double c1 = chi_poly(cb, px - qx, py - qy);
+                    double sn, cs;
+                    sincos_tab(chi0 - c1, T, sn, cs);
+                    Lr = aml * cs;
+                    Li = aml * sn;
+                }
+                if (zr) {
+                    const double c1 = chi_poly(cb, px + qx, py + qy);
+                    double sn, cs;
+                    sincos_tab(c1 - chi0, T, sn, cs);
+                    Rr = amr * cs;
+                    Ri = amr * sn;
+                }
+                // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
+                const double gmr = Ri - Li, gmi = Lr - Rr;
+                acc[3 * b] = fma(gmr, gr, fma(gmi, gi, acc[3 * b]));
+                acc[3 * b + 1] = fma(gmr, gi, fma(-gmi, gr, acc[3 * b + 1]));
+                acc[3 * b + 2] = fma(gmr, gmr, fma(gmi, gmi, acc[3 * b + 2]));
+            }
+            lky = nlky;
+            lkx = nlkx;
+            amp0 = namp0;
+            sw = nsw;
+            gv = ngv;
+            goff1 = goff2;
+        }
+        double *po = prm.partial + (size_t)seg * (NACC * 64);
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) po[i * 64 + lane] = acc[i];
+        ++seg;
+        it += p1 - p0;
+    }
+}
+
+// Per band tile: the reduced sums -> S, N outputs and the tile's agreement
+// partials (|S_b|^2 / N_b and P summed over the lanes by a fixed tree).
+template <int MAXB>
+__global__ __launch_bounds__(64) void ssb_write_kernel(SsbParams prm, double *tile_part) {
+    constexpr int NACC = 3 * MAXB + 1;
+    const int lane = threadIdx.x;
+    const int t = blockIdx.x;
+    const SsbTile *tile = prm.tiles + t;
     const int yh = tile->yh0 + (lane >> 4);
     const int ix = tile->ix0 + (lane & 15);
     const bool valid = (tile->valid >> lane) & 1ull;
     const int iy = yh < 0 ? yh + prm.N : yh;
     const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
-    const double qy = (double)yh * prm.dq, qx = (double)ix * prm.dq;
-    const int B = prm.B;
-    const ApertureDev ap = prm.ap;
-    const double lam = prm.lam;
-
-    double sr[MAXB], si[MAXB], nn[MAXB];
-#pragma unroll
-    for (int b = 0; b < MAXB; ++b) sr[b] = si[b] = nn[b] = 0.0;
-    double pw = 0.0;
-
-    for (int p = wave; p < prm.n_pix; p += P) {
-        const PixelRec *pr = prm.pix + p;
-        const double ky = pr->ky, kx = pr->kx, w = pr->w, a0 = pr->a0;
-        float2 gv = make_float2(0.f, 0.f);
-        if (valid) gv = prm.G[pr->goff + lane_off];
-        const double gr = (double)gv.x, gi = (double)gv.y;
-        const double gwr = w * gr, gwi = w * gi;
-        pw = fma(gr, gwr, fma(gi, gwi, pw));
-        const double dy = ky - qy, dx = kx - qx, ey = ky + qy, ex = kx + qx;
-        const double dm2 = fma(dy, dy, dx * dx), dp2 = fma(ey, ey, ex * ex);
-        const bool zl = valid && inside_support(ap, dm2);
-        const bool zr = valid && inside_support(ap, dp2);
-        const double aml = zl ? a0 * lobe_aperture(ap, dm2) : 0.0;
-        const double amr = zr ? a0 * lobe_aperture(ap, dp2) : 0.0;
-#pragma unroll
-        for (int b = 0; b < MAXB; ++b) {
-            if (b >= B) break;
-            const double chi0 = prm.chi_tab[(size_t)b * prm.n_pix + p];
-            double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
-            if (zl) {
-                const double cm = chi_poly(prm.chi_c[b], fma(lam, dx, prm.tau_x[b]), fma(lam, dy, prm.tau_y[b]));
-                double sn, cs;
-                sincos_tab(chi0 - cm, T, sn, cs);
-                Lr = aml * cs;
-                Li = aml * sn;
-            }
-            if (zr) {
-                const double cp = chi_poly(prm.chi_c[b], fma(lam, ex, prm.tau_x[b]), fma(lam, ey, prm.tau_y[b]));
-                double sn, cs;
-                sincos_tab(cp - chi0, T, sn, cs);
-                Rr = amr * cs;
-                Ri = amr * sn;
-            }
-            // Gamma = i (L - R); S += w conj(Gamma) g; N += w |Gamma|^2
-            const double gmr = Ri - Li, gmi = Lr - Rr;
-            sr[b] = fma(gmr, gwr, fma(gmi, gwi, sr[b]));
-            si[b] = fma(gmr, gwi, fma(-gmi, gwr, si[b]));
-            nn[b] = fma(w * gmr, gmr, fma(w * gmi, gmi, nn[b]));
-        }
-    }
-
-    constexpr int NACC = 3 * MAXB + 1;
-    __shared__ double lds[NACC * 64];
-    if (P > 1) {
-        for (int wv = 1; wv < P; ++wv) {
-            if (wave == wv) {
-#pragma unroll
-                for (int b = 0; b < MAXB; ++b) {
-                    lds[(3 * b) * 64 + lane] = sr[b];
-                    lds[(3 * b + 1) * 64 + lane] = si[b];
-                    lds[(3 * b + 2) * 64 + lane] = nn[b];
-                }
-                lds[(3 * MAXB) * 64 + lane] = pw;
-            }
-            __syncthreads();
-            if (wave == 0) {
-#pragma unroll
-                for (int b = 0; b < MAXB; ++b) {
-                    sr[b] += lds[(3 * b) * 64 + lane];
-                    si[b] += lds[(3 * b + 1) * 64 + lane];
-                    nn[b] += lds[(3 * b + 2) * 64 + lane];
-                }
-                pw += lds[(3 * MAXB) * 64 + lane];
-            }
-            __syncthreads();
-        }
-    }
-    if (wave != 0) return;
-
-    // outputs and per-tile agreement partials (fixed-order lane tree)
+    const double *pi = prm.partial + (size_t)prm.seg_first[t] * (NACC * 64);
     const size_t plane = (size_t)prm.N * prm.nh;
     double part[MAXB + 1];
 #pragma unroll
     for (int b = 0; b < MAXB; ++b) {
-        const bool ok = valid && b < B;
-        if (ok && prm.S_out) prm.S_out[(size_t)b * plane + lane_off] = make_double2(sr[b], si[b]);
-        if (ok && prm.N_out) prm.N_out[(size_t)b * plane + lane_off] = nn[b];
-        part[b] = (ok && nn[b] > 0.0) ? (sr[b] * sr[b] + si[b] * si[b]) / nn[b] : 0.0;
+        const double sr = pi[(3 * b) * 64 + lane], si = pi[(3 * b + 1) * 64 + lane], nn = pi[(3 * b + 2) * 64 + lane];
+        const bool ok = valid && b < prm.B;
+        if (ok && prm.S_out) prm.S_out[(size_t)b * plane + lane_off] = make_double2(sr, si);
+        if (ok && prm.N_out) prm.N_out[(size_t)b * plane + lane_off] = nn;
+        part[b] = (ok && nn > 0.0) ? (sr * sr + si * si) / nn : 0.0;
     }
-    part[MAXB] = valid ? pw : 0.0;
+    part[MAXB] = valid ? pi[(NACC - 1) * 64 + lane] : 0.0;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
 #pragma unroll
         for (int b = 0; b <= MAXB; ++b) part[b] += __shfl_xor(part[b], off);
     }
     if (lane == 0) {
-        double *po = prm.partial + (size_t)blockIdx.x * (MAXB + 1);
 #pragma unroll
-        for (int b = 0; b <= MAXB; ++b) po[b] = part[b];
+        for (int b = 0; b <= MAXB; ++b) tile_part[(size_t)t * (MAXB + 1) + b] = part[b];
     }
 }
 
@@ -948,10 +1014,10 @@ __global__ void agreement_kernel(const double *partial, int n_tiles, int stride,
 #define DSP_CHECK_LAUNCH() \
     do { hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; } while (0)
 
-hipError_t launch_pixel_terms(const PixelRec *in, PixelRec *out, int n_pix, const ApertureDev &ap, const OpticsDev &op,
-                              double *chi_tab, hipStream_t st) {
+hipError_t launch_pixel_terms(const PixelBase *in, PixelRec *out, int n_pix, const ApertureDev &ap, const OpticsDev &op,
+                              double *chi_tab, int chi_stride, hipStream_t st) {
     if (n_pix <= 0) return hipSuccess;
-    pixel_terms_kernel<<<(n_pix + 255) / 256, 256, 0, st>>>(in, out, n_pix, ap, op, chi_tab);
+    pixel_terms_kernel<<<(n_pix + 255) / 256, 256, 0, st>>>(in, out, n_pix, ap, op, chi_tab, chi_stride);
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }
@@ -1118,23 +1184,49 @@ hipError_t launch_export(const double2 *sys, int n_q, int D, double2 *dense, hip
     return hipSuccess;
 }
 
-hipError_t launch_ssb(const SsbParams &prm, int n_tiles, hipStream_t st) {
-    if (n_tiles <= 0) return hipSuccess;
-    constexpr int P = 4;
-    if (prm.B <= 1) ssb_kernel<1, P><<<n_tiles, 64 * P, 0, st>>>(prm);
-    else if (prm.B <= 2) ssb_kernel<2, P><<<n_tiles, 64 * P, 0, st>>>(prm);
-    else if (prm.B <= 4) ssb_kernel<4, P><<<n_tiles, 64 * P, 0, st>>>(prm);
-    else ssb_kernel<8, P><<<n_tiles, 64 * P, 0, st>>>(prm);
+int ssb_maxb(int B) { return B <= 1 ? 1 : (B <= 2 ? 2 : (B <= 4 ? 4 : 8)); }
+
+int ssb_nacc(int maxb) { return 3 * maxb + 1; }
+
+hipError_t ssb_occupancy(int maxb, int *blocks_per_cu) {
+    switch (maxb) {
+        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1>, 64, 0);
+        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2>, 64, 0);
+        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4>, 64, 0);
+        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8>, 64, 0);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *tile_part, hipStream_t st) {
+    if (n_waves <= 0 || n_tiles <= 0) return hipSuccess;
+    const int maxb = ssb_maxb(prm.B);
+    const int nacc = ssb_nacc(maxb);
+    switch (maxb) {
+        case 1: ssb_kernel<1><<<n_waves, 64, 0, st>>>(prm); break;
+        case 2: ssb_kernel<2><<<n_waves, 64, 0, st>>>(prm); break;
+        case 4: ssb_kernel<4><<<n_waves, 64, 0, st>>>(prm); break;
+        default: ssb_kernel<8><<<n_waves, 64, 0, st>>>(prm); break;
+    }
+    DSP_CHECK_LAUNCH();
+    // reduce each tile's segments (same reduction as the Gram fixup)
+    GramParams gp;
+    memset(&gp, 0, sizeof gp);
+    gp.seg_first = prm.seg_first;
+    gp.partial = prm.partial;
+    gram_reduce_kernel<<<dim3(nacc, n_tiles), 64, 0, st>>>(gp, nacc);
+    DSP_CHECK_LAUNCH();
+    switch (maxb) {
+        case 1: ssb_write_kernel<1><<<n_tiles, 64, 0, st>>>(prm, tile_part); break;
+        case 2: ssb_write_kernel<2><<<n_tiles, 64, 0, st>>>(prm, tile_part); break;
+        case 4: ssb_write_kernel<4><<<n_tiles, 64, 0, st>>>(prm, tile_part); break;
+        default: ssb_write_kernel<8><<<n_tiles, 64, 0, st>>>(prm, tile_part); break;
+    }
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }
 
-int ssb_partial_stride(int B) {
-    if (B <= 1) return 2;
-    if (B <= 2) return 3;
-    if (B <= 4) return 5;
-    return 9;
-}
+int ssb_partial_stride(int B) { return ssb_maxb(B) + 1; }
 
 hipError_t launch_agreement(const double *partial, int n_tiles, int B, double *E, hipStream_t st) {
     agreement_kernel<<<1, 64, 0, st>>>(partial, n_tiles, ssb_partial_stride(B), B, E);

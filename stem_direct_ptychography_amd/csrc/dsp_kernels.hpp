@@ -41,8 +41,8 @@ struct ScatterParams {
     double2 *spec;            // [SC][nf][nf/2+1]
 };
 
-hipError_t launch_pixel_terms(const PixelRec *in, PixelRec *out, int n_pix, const ApertureDev &ap, const OpticsDev &op,
-                              double *chi_tab, hipStream_t st);
+hipError_t launch_pixel_terms(const PixelBase *in, PixelRec *out, int n_pix, const ApertureDev &ap, const OpticsDev &op,
+                              double *chi_tab, int chi_stride, hipStream_t st);
 int gram_nacc(int nj, int method);   // doubles per lane of one partial sum
 hipError_t gram_occupancy(int nj, int method, int *blocks_per_cu);
 hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_waves, hipStream_t st);
@@ -54,7 +54,12 @@ hipError_t launch_solve(const SolveParams &prm, int A, int method, hipStream_t s
 hipError_t launch_fill_zero(double *p, size_t n, hipStream_t st);
 hipError_t launch_scatter(const ScatterParams &prm, hipStream_t st);
 hipError_t launch_export(const double2 *sys, int n_q, int D, double2 *dense, hipStream_t st);
-hipError_t launch_ssb(const SsbParams &prm, int n_tiles, hipStream_t st);
+int ssb_maxb(int B);                 // compiled set count used for B sets
+int ssb_nacc(int maxb);              // doubles per lane of one SSB partial sum
+hipError_t ssb_occupancy(int maxb, int *blocks_per_cu);
+// SSB kernel over n_waves stream-K ranges, then per-tile reduction and
+// write-out; tile_part receives [n_tiles][MAXB + 1] agreement partials.
+hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *tile_part, hipStream_t st);
 int ssb_partial_stride(int B);
 hipError_t launch_agreement(const double *partial, int n_tiles, int B, double *E, hipStream_t st);
 
