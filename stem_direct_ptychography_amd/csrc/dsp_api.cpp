@@ -251,10 +251,51 @@ dsp_status build_geometry(const dsp_scan *scan, const dsp_optics *o, int u, Geom
     return DSP_OK;
 }
 
-// Group the solved frequencies into 4 x 16 tiles (rows = signed row, cols =
-// ix) and collect each tile's sorted union of alias offsets.  A tile whose
-// union exceeds the kernels' slot maximum is split into sub-tiles with the
-// same origin and disjoint lane subsets (greedy over the lanes' alias sets).
+// Lane groups of at most 64 scan frequencies, cut along G's 128-byte lines.
+// Row yh (stored row iy = yh mod N) starts at element iy nh of a plane, so its
+// first line boundary lies at column h = (-iy nh) mod 16.  Its columns
+// [0, ncol) split into runs that each fill part of one line: the head [0, h)
+// is block 0 and the run starting at column h + 16 (b - 1) is block b.  Within
+// a block the runs of consecutive rows, cut down to the columns `keep`
+// accepts, are packed in row order into groups of at most 64 lanes, spanning
+// at most `max_rows` rows; a run is never split, so each line feeds one group.
+typedef std::vector<std::pair<int16_t, int16_t>> Lanes;   // (yh, ix) per lane
+
+template <class Keep>
+std::vector<Lanes> pack_line_runs(int N, int nh, int yh_lo, int yh_hi, int ncol, int max_rows, Keep keep) {
+    std::vector<Lanes> out;
+    const int n_blk = 2 + (ncol - 1) / TILE_X;
+    Lanes cur, run;
+    int cur_row0 = 0;
+    for (int b = 0; b < n_blk; ++b) {
+        for (int yh = yh_lo; yh <= yh_hi; ++yh) {
+            const long long iy = yh < 0 ? yh + N : yh;
+            const int h = (int)((TILE_X - (iy * nh) % TILE_X) % TILE_X);
+            const int c0 = b == 0 ? 0 : h + TILE_X * (b - 1);
+            const int c1 = std::min(ncol, b == 0 ? h : c0 + TILE_X);
+            run.clear();
+            for (int ix = c0; ix < c1; ++ix)
+                if (keep(yh, ix)) run.emplace_back((int16_t)yh, (int16_t)ix);
+            if (run.empty()) continue;
+            if (!cur.empty() && (cur.size() + run.size() > 64 || yh - cur_row0 >= max_rows)) {
+                out.push_back(cur);
+                cur.clear();
+            }
+            if (cur.empty()) cur_row0 = yh;
+            cur.insert(cur.end(), run.begin(), run.end());
+        }
+        if (!cur.empty()) {
+            out.push_back(cur);
+            cur.clear();
+        }
+    }
+    return out;
+}
+
+// Group the solved frequencies into lane groups (pack_line_runs) and collect
+// each tile's sorted union of alias offsets.  A tile whose union exceeds the
+// kernels' slot maximum is split into sub-tiles with disjoint lane subsets
+// (greedy over the lanes' alias sets).
 struct TileGroups {
     std::vector<GramTile> tiles;      // grouped by nj, groups in ascending nj
     std::vector<int> group_nj, group_off, group_n;
@@ -273,10 +314,15 @@ void finish_tile(GramTile &t, const JSet &js_in, const Geometry &g,
         t.jy[s] = (int8_t)js[s].first;
         t.jx[s] = (int8_t)js[s].second;
     }
+    double sy = 0.0, sx = 0.0;
+    int nv = 0;
     for (int l = 0; l < 64; ++l) {
         const int qi = t.qidx[l];
         t.mask[l] = 0;
         if (qi < 0) continue;
+        sy += t.lyh[l];
+        sx += t.lix[l];
+        ++nv;
         cost += g.count[qi];
         unsigned msk = 0;
         for (int m = 0; m < g.count[qi]; ++m) {
@@ -286,6 +332,8 @@ void finish_tile(GramTile &t, const JSet &js_in, const Geometry &g,
         }
         t.mask[l] = (uint16_t)msk;
     }
+    t.cy = (float)(nv ? sy / nv : 0.0);
+    t.cx = (float)(nv ? sx / nv : 0.0);
     by_nj[t.nj].emplace_back(-cost, t);
 }
 
@@ -295,62 +343,63 @@ dsp_status build_gram_tiles(const Geometry &g, int max_nj, TileGroups &tg) {
     std::vector<int32_t> qidx((size_t)N * (N / 2), -1);
     for (int i = 0; i < g.n_q; ++i) qidx[(size_t)g.q[2 * i] * (N / 2) + g.q[2 * i + 1]] = i;
     std::map<int, std::vector<std::pair<long long, GramTile>>> by_nj;
-    for (int yh0 = -N / 2 + 1; yh0 <= N / 2 - 1; yh0 += TILE_Y) {
-        for (int ix0 = 0; ix0 < N / 2; ix0 += TILE_X) {
-            int lane_q[64];
-            JSet lane_js[64];
-            JSet uni;
-            int nvalid = 0;
+    const int nh = N / 2 + 1;
+    // rows -N/2+1 .. N/2-1 and columns 0 .. N/2-1: the solved half-plane
+    // leaves out the Nyquist row and column
+    auto solved = [&](int yh, int ix) { return qidx[(size_t)(yh < 0 ? yh + N : yh) * (N / 2) + ix] >= 0; };
+    const std::vector<Lanes> groups = pack_line_runs(N, nh, -N / 2 + 1, N / 2 - 1, N / 2, 8, solved);
+    for (const Lanes &grp : groups) {
+        int lane_q[64];
+        JSet lane_js[64];
+        JSet uni;
+        int nvalid = 0;
+        GramTile base;
+        std::memset(&base, 0, sizeof base);
+        for (int l = 0; l < 64; ++l) {
+            lane_q[l] = -1;
+            if (l >= (int)grp.size()) continue;
+            const int yh = grp[l].first, ix = grp[l].second;
+            base.lyh[l] = (int16_t)yh;
+            base.lix[l] = (int16_t)ix;
+            const int qi = qidx[(size_t)(yh < 0 ? yh + N : yh) * (N / 2) + ix];
+            lane_q[l] = qi;
+            ++nvalid;
+            for (int m = 0; m < g.count[qi]; ++m)
+                lane_js[l].emplace_back(g.jy[(size_t)qi * am + m], g.jx[(size_t)qi * am + m]);
+            uni.insert(uni.end(), lane_js[l].begin(), lane_js[l].end());
+        }
+        if (nvalid == 0) continue;
+        std::sort(uni.begin(), uni.end());
+        uni.erase(std::unique(uni.begin(), uni.end()), uni.end());
+        if ((int)uni.size() <= max_nj) {
+            for (int l = 0; l < 64; ++l) base.qidx[l] = lane_q[l];
+            finish_tile(base, uni, g, by_nj);
+            continue;
+        }
+        // split: each sub-tile takes lanes while its union stays within max_nj
+        bool taken[64] = {false};
+        int left = nvalid;
+        while (left > 0) {
+            GramTile t = base;
+            JSet js;
+            for (int l = 0; l < 64; ++l) t.qidx[l] = -1;
             for (int l = 0; l < 64; ++l) {
-                const int yh = yh0 + l / TILE_X, ix = ix0 + l % TILE_X;
-                lane_q[l] = -1;
-                if (yh > N / 2 - 1 || ix >= N / 2) continue;
-                const int iy = yh < 0 ? yh + N : yh;
-                const int qi = qidx[(size_t)iy * (N / 2) + ix];
-                if (qi < 0) continue;
-                lane_q[l] = qi;
-                ++nvalid;
-                for (int m = 0; m < g.count[qi]; ++m)
-                    lane_js[l].emplace_back(g.jy[(size_t)qi * am + m], g.jx[(size_t)qi * am + m]);
-                uni.insert(uni.end(), lane_js[l].begin(), lane_js[l].end());
+                if (lane_q[l] < 0 || taken[l]) continue;
+                JSet tryu = js;
+                tryu.insert(tryu.end(), lane_js[l].begin(), lane_js[l].end());
+                std::sort(tryu.begin(), tryu.end());
+                tryu.erase(std::unique(tryu.begin(), tryu.end()), tryu.end());
+                if ((int)tryu.size() > max_nj) continue;
+                js.swap(tryu);
+                t.qidx[l] = lane_q[l];
+                taken[l] = true;
+                --left;
             }
-            if (nvalid == 0) continue;
-            std::sort(uni.begin(), uni.end());
-            uni.erase(std::unique(uni.begin(), uni.end()), uni.end());
-            GramTile base;
-            std::memset(&base, 0, sizeof base);
-            base.yh0 = yh0;
-            base.ix0 = ix0;
-            if ((int)uni.size() <= max_nj) {
-                for (int l = 0; l < 64; ++l) base.qidx[l] = lane_q[l];
-                finish_tile(base, uni, g, by_nj);
-                continue;
+            if (js.empty() && left > 0) {
+                // a single frequency above the maximum (checked by the caller)
+                return fail(DSP_EALIAS, "a frequency needs more than %d alias slots", max_nj);
             }
-            // split: each sub-tile takes lanes while its union stays within max_nj
-            bool taken[64] = {false};
-            int left = nvalid;
-            while (left > 0) {
-                GramTile t = base;
-                JSet js;
-                for (int l = 0; l < 64; ++l) t.qidx[l] = -1;
-                for (int l = 0; l < 64; ++l) {
-                    if (lane_q[l] < 0 || taken[l]) continue;
-                    JSet tryu = js;
-                    tryu.insert(tryu.end(), lane_js[l].begin(), lane_js[l].end());
-                    std::sort(tryu.begin(), tryu.end());
-                    tryu.erase(std::unique(tryu.begin(), tryu.end()), tryu.end());
-                    if ((int)tryu.size() > max_nj) continue;
-                    js.swap(tryu);
-                    t.qidx[l] = lane_q[l];
-                    taken[l] = true;
-                    --left;
-                }
-                if (js.empty() && left > 0) {
-                    // a single frequency above the maximum (checked by the caller)
-                    return fail(DSP_EALIAS, "a frequency needs more than %d alias slots", max_nj);
-                }
-                finish_tile(t, js, g, by_nj);
-            }
+            finish_tile(t, js, g, by_nj);
         }
     }
     tg.tiles.clear();
@@ -417,8 +466,8 @@ double tile_cost(const GramTile &t, const Geometry &g, double ra, int n_pix) {
     double lobes = 0.0;
     for (int s = 0; s < t.nj; ++s) {
         if (!((used >> s) & 1u)) continue;
-        const double qy = (t.yh0 + 1.5 + (double)t.jy[s] * g.N) * g.dq;
-        const double qx = (t.ix0 + 7.5 + (double)t.jx[s] * g.N) * g.dq;
+        const double qy = (t.cy + (double)t.jy[s] * g.N) * g.dq;
+        const double qx = (t.cx + (double)t.jx[s] * g.N) * g.dq;
         const double D = std::hypot(qy, qx);
         if (D >= 2.0 * ra) continue;
         const double lens = 2.0 * ra * ra * std::acos(D / (2.0 * ra)) - 0.5 * D * std::sqrt(4.0 * ra * ra - D * D);
@@ -802,22 +851,26 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
     const double dq = 1.0 / (N * key.step);
     if ((st = build_active(coords, weights, key.n_bf, optics, N, L->act))) return st;
     if (L->act.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
-    // tiles over every stored entry, lanes inside the band
-    for (int yh0 = -N / 2; yh0 <= N / 2 - 1; yh0 += TILE_Y) {
-        for (int ix0 = 0; ix0 <= N / 2; ix0 += TILE_X) {
-            SsbTile t;
-            std::memset(&t, 0, sizeof t);
-            t.yh0 = yh0;
-            t.ix0 = ix0;
-            for (int l = 0; l < 64; ++l) {
-                const int yh = yh0 + l / TILE_X, ix = ix0 + l % TILE_X;
-                if (yh > N / 2 - 1 || ix > N / 2) continue;
-                const double f = std::hypot((double)yh * dq, (double)ix * dq);
-                if (key.has_band && !(f >= key.lo && f <= key.hi)) continue;
-                t.valid |= 1ull << l;
-            }
-            if (t.valid) L->tiles.push_back(t);
+    // lane groups over every stored entry inside the band
+    const int nh = N / 2 + 1;
+    auto in_band = [&](int yh, int ix) {
+        const double f = std::hypot((double)yh * dq, (double)ix * dq);
+        return !key.has_band || (f >= key.lo && f <= key.hi);
+    };
+    for (const Lanes &grp : pack_line_runs(N, nh, -N / 2, N / 2 - 1, nh, 16, in_band)) {
+        SsbTile t;
+        std::memset(&t, 0, sizeof t);
+        double sy = 0.0, sx = 0.0;
+        for (size_t l = 0; l < grp.size(); ++l) {
+            t.lyh[l] = grp[l].first;
+            t.lix[l] = grp[l].second;
+            t.valid |= 1ull << l;
+            sy += grp[l].first;
+            sx += grp[l].second;
         }
+        t.cy = (float)(sy / grp.size());
+        t.cx = (float)(sx / grp.size());
+        L->tiles.push_back(t);
     }
     const int n_tiles = (int)L->tiles.size();
     const int n_pix = (int)L->act.pix.size();
@@ -839,7 +892,7 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
             std::vector<double> cost(n_tiles);
             for (int t = 0; t < n_tiles; ++t) {
                 const SsbTile &tt = L->tiles[t];
-                const double D = std::hypot((tt.yh0 + 1.5) * dq, (tt.ix0 + 7.5) * dq);
+                const double D = std::hypot(tt.cy * dq, tt.cx * dq);
                 double lens = 0.0;
                 if (D < 2.0 * ra)
                     lens = 2.0 * ra * ra * std::acos(D / (2.0 * ra)) - 0.5 * D * std::sqrt(4.0 * ra * ra - D * D);

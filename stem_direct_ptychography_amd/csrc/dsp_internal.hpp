@@ -98,28 +98,34 @@ __host__ __device__ inline void sincos_tab(double x, const double2 *__restrict__
     c = fma(t.x, cr, -(t.y * sr));
 }
 
+// A tile is a group of up to 64 scan frequencies, one per lane, with
+// explicit coordinates (signed row yh, column ix).  The host cuts every
+// stored row of G into the runs that fill one 128-byte line (16 complex64;
+// a row is N/2 + 1 entries long, so line boundaries move from row to row)
+// and packs them: full runs of four consecutive rows form one tile, and the
+// short runs at the row ends are packed with those of neighbouring rows.
+// Each lane's G value then comes from a line no other tile reads, and
+// neighbouring lanes see nearly the same lens overlap.
 constexpr int TILE_Y = 4;
 constexpr int TILE_X = 16;
 constexpr int MAX_SLOTS = 9;   // fine aliases of one coarse frequency for u <= 3 per axis pair
 
-// 4 x 16 block of scan frequencies (rows = signed row index, cols = ix); lane
-// l holds (yh0 + l / 16, ix0 + l % 16).  The union of the lanes' alias
-// offsets (j_y, j_x), sorted, forms the tile's alias slots.
 struct alignas(64) GramTile {
-    int yh0, ix0;
-    int nj;
+    int nj;              // alias slots: the sorted union of the lanes' offsets (j_y, j_x)
     int pad0;
+    float cy, cx;        // mean (yh, ix) of the valid lanes (cost estimate)
     int8_t jy[12], jx[12];
     uint16_t mask[64];   // per lane: bit s set when slot s is an alias of the lane's frequency
     int32_t qidx[64];    // per lane: index of the frequency in the solved list, -1 if none
-    int32_t pad1[8];
+    int16_t lyh[64];     // per lane: signed row
+    int16_t lix[64];     // per lane: column
 };
 
 struct alignas(64) SsbTile {
-    int yh0, ix0;
-    int pad0[2];
     uint64_t valid;      // lanes inside the band (and inside the stored plane)
-    int32_t pad1[12];
+    float cy, cx;        // mean (yh, ix) of the valid lanes (cost estimate)
+    int16_t lyh[64];
+    int16_t lix[64];
 };
 
 struct OpticsDev {

@@ -184,7 +184,8 @@ __device__ __forceinline__ void write_system(const double *acc, unsigned mask, i
 // Waves per SIMD the compiler must fit (caps the registers per lane).
 template <int NJ, int METHOD>
 struct GramWaves {
-    static constexpr int value = METHOD == 0 ? (NJ <= 2 ? 4 : (NJ <= 6 ? 2 : 1)) : (NJ <= 1 ? 4 : (NJ <= 3 ? 2 : 1));
+    static constexpr int value = METHOD == 0 ? (NJ <= 2 ? 4 : (NJ <= 4 ? 3 : (NJ <= 6 ? 2 : 1)))
+                                             : (NJ <= 1 ? 4 : (NJ <= 2 ? 3 : (NJ <= 3 ? 2 : 1)));
 };
 
 // Pixel records and plane offsets are written by earlier kernels or copies,
@@ -252,21 +253,20 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
         const int p0 = (int)(it - (long long)t * n_pix);
         const int p1 = (int)((end - it) < (n_pix - p0) ? p0 + (end - it) : n_pix);
         const GramTile *tile = prm.tiles + t;
-        const int yh = tile->yh0 + (lane >> 4);
-        const int ix = tile->ix0 + (lane & 15);
+        const int yh = tile->lyh[lane];
+        const int ix = tile->lix[lane];
         const bool valid = tile->qidx[lane] >= 0;
         const unsigned mask = valid ? (unsigned)tile->mask[lane] : 0u;
         const int iy = yh < 0 ? yh + prm.N : yh;
         const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
 
-        // lambda Q per slot and |lambda Q|^2
-        double Qy[NJ], Qx[NJ], Q2[NJ];
+        // lambda Q per slot
+        double Qy[NJ], Qx[NJ];
         bool act[NJ];
 #pragma unroll
         for (int s = 0; s < NJ; ++s) {
             Qy[s] = (double)(yh + (int)tile->jy[s] * prm.N) * prm.ldq;
             Qx[s] = (double)(ix + (int)tile->jx[s] * prm.N) * prm.ldq;
-            Q2[s] = fma(Qy[s], Qy[s], Qx[s] * Qx[s]);
             act[s] = (mask >> s) & 1u;
         }
 
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
             for (int s = 0; s < NJ; ++s) {
                 // |lambda (k -/+ Q)|^2 = |lambda k|^2 + |lambda Q|^2 -/+ 2 (lambda k).(lambda Q)
                 const double kq = fma(lky, Qy[s], lkx * Qx[s]);
-                const double base = lk2 + Q2[s];
+                const double base = lk2 + fma(Qy[s], Qy[s], Qx[s] * Qx[s]);
                 const double dm2 = fma(-2.0, kq, base);
                 const double dp2 = fma(2.0, kq, base);
                 const bool zl = act[s] && dm2 < lrlim2;
@@ -392,8 +392,8 @@ template <int METHOD>
 __global__ __launch_bounds__(64) void work_count_kernel(GramParams prm, unsigned long long *out) {
     const int lane = threadIdx.x & 63;
     const GramTile *tile = prm.tiles + blockIdx.x;
-    const int yh = tile->yh0 + (lane >> 4);
-    const int ix = tile->ix0 + (lane & 15);
+    const int yh = tile->lyh[lane];
+    const int ix = tile->lix[lane];
     const bool valid = tile->qidx[lane] >= 0;
     const unsigned mask = valid ? (unsigned)tile->mask[lane] : 0u;
     const int nj = tile->nj;
@@ -862,8 +862,8 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
         const int p0 = (int)(it - (long long)t * n_pix);
         const int p1 = (int)((end - it) < (n_pix - p0) ? p0 + (end - it) : n_pix);
         const SsbTile *tile = prm.tiles + t;
-        const int yh = tile->yh0 + (lane >> 4);
-        const int ix = tile->ix0 + (lane & 15);
+        const int yh = tile->lyh[lane];
+        const int ix = tile->lix[lane];
         const bool valid = (tile->valid >> lane) & 1ull;
         const int iy = yh < 0 ? yh + prm.N : yh;
         const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
@@ -956,8 +956,8 @@ __global__ __launch_bounds__(64) void ssb_write_kernel(SsbParams prm, double *ti
     const int lane = threadIdx.x;
     const int t = blockIdx.x;
     const SsbTile *tile = prm.tiles + t;
-    const int yh = tile->yh0 + (lane >> 4);
-    const int ix = tile->ix0 + (lane & 15);
+    const int yh = tile->lyh[lane];
+    const int ix = tile->lix[lane];
     const bool valid = (tile->valid >> lane) & 1ull;
     const int iy = yh < 0 ? yh + prm.N : yh;
     const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
