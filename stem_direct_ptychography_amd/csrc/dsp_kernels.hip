@@ -181,6 +181,15 @@ __device__ __forceinline__ void write_system(const double *acc, unsigned mask, i
     }
 }
 
+// Pixels whose records are staged in LDS at a time (one per lane).
+constexpr int GRAM_CHUNK = 64;
+
+// G values fetched ahead per lane: one group of PF pixels (divides GRAM_CHUNK).
+template <int NJ, int METHOD>
+struct GramPrefetch {
+    static constexpr int value = 4;
+};
+
 // Waves per SIMD the compiler must fit (caps the registers per lane).
 template <int NJ, int METHOD>
 struct GramWaves {
@@ -218,6 +227,72 @@ __device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, do
     im = amp * sn;
 }
 
+// One pixel's update of a lane's sums: the lobes of every slot, then the
+// rank-one update of the augmented Gram restricted to the columns some lane
+// of the wave has (the rest of the wave adds exact zeros there).
+template <int NJ, int METHOD>
+__device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 *T,
+                                           double (&acc)[GramShape<NJ, METHOD>::NACC], int yh, int ix,
+                                           const int (&jyN)[NJ], const int (&jxN)[NJ], const bool (&act)[NJ],
+                                           double lky, double lkx, double amp0, double sw, double chi0, float2 gv) {
+    using Sh = GramShape<NJ, METHOD>;
+    constexpr int NC = Sh::NC;
+    const double ldq = prm.ldq, lrlim2 = prm.ap.lrlim2;
+    const double tau_y = prm.op.tau_y, tau_x = prm.op.tau_x;
+    const double lk2 = fma(lky, lky, lkx * lkx);
+    const double py = lky + tau_y, px = lkx + tau_x;
+
+    const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
+    acc[NC] = fma(gr, gr, fma(gi, gi, acc[NC]));   // signal power w |g|^2
+
+    double tr[NC], ti[NC];
+    bool nz[NC];
+#pragma unroll
+    for (int s = 0; s < NJ; ++s) {
+        const double Qy_s = (double)(yh + jyN[s]) * ldq, Qx_s = (double)(ix + jxN[s]) * ldq;
+        // |lambda (k -/+ Q)|^2 = |lambda k|^2 + |lambda Q|^2 -/+ 2 (lambda k).(lambda Q)
+        const double kq = fma(lky, Qy_s, lkx * Qx_s);
+        const double base = lk2 + fma(Qy_s, Qy_s, Qx_s * Qx_s);
+        const double dm2 = fma(-2.0, kq, base);
+        const double dp2 = fma(2.0, kq, base);
+        const bool zl = act[s] && dm2 < lrlim2;
+        const bool zr = act[s] && dp2 < lrlim2;
+        double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
+        if (zl) lobe(prm, T, py - Qy_s, px - Qx_s, dm2, chi0, amp0, 1.0, Lr, Li);
+        if (zr) lobe(prm, T, py + Qy_s, px + Qx_s, dp2, chi0, amp0, -1.0, Rr, Ri);
+        if (METHOD == 0) {
+            tr[s] = Ri - Li;   // T_phi = i (L - R)
+            ti[s] = Lr - Rr;
+            nz[s] = zl || zr;
+        } else {
+            tr[s] = Lr;
+            ti[s] = Li;
+            nz[s] = zl;
+            tr[NJ + s] = Rr;
+            ti[NJ + s] = Ri;
+            nz[NJ + s] = zr;
+        }
+    }
+
+    bool any[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) any[c] = wave_any(nz[c]);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (!any[c]) continue;
+        acc[c] = fma(tr[c], tr[c], fma(ti[c], ti[c], acc[c]));
+        // right side <col c, g> = conj(t_c) g
+        acc[Sh::re(c, NC)] = fma(tr[c], gr, fma(ti[c], gi, acc[Sh::re(c, NC)]));
+        acc[Sh::im(c, NC)] = fma(tr[c], gi, fma(-ti[c], gr, acc[Sh::im(c, NC)]));
+#pragma unroll
+        for (int d = c + 1; d < NC; ++d) {
+            if (!any[d]) continue;
+            acc[Sh::re(c, d)] = fma(tr[c], tr[d], fma(ti[c], ti[d], acc[Sh::re(c, d)]));
+            acc[Sh::im(c, d)] = fma(tr[c], ti[d], fma(-ti[c], tr[d], acc[Sh::im(c, d)]));
+        }
+    }
+}
+
 // Transfer + weighted augmented Gram over one wave's stream-K range.
 // METHOD 0 (phase): columns T_phi(slot 0..NJ-1), then g.
 // METHOD 1 (complex): columns L(slot 0..NJ-1), R(slot 0..NJ-1), then g; the
@@ -232,10 +307,12 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
     constexpr int NC = Sh::NC;
     constexpr int NACC = Sh::NACC;
 
+    constexpr int PF = GramPrefetch<NJ, METHOD>::value;
     __shared__ double2 T[TRIG_N];
+    __shared__ PixelRec srec[GRAM_CHUNK];
+    __shared__ long long sgoff[GRAM_CHUNK + PF];
     const int lane = threadIdx.x;
     T[lane] = prm.trig[lane];
-    __syncthreads();
 
     const int wv = blockIdx.x;
     const long long n_pix = prm.n_pix;
@@ -245,9 +322,6 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
     ConstPixel *pix = (ConstPixel *)prm.pix;
     ConstLong *goffs = (ConstLong *)prm.goff;
     const float2 *__restrict__ G = prm.G;
-    const double lrlim2 = prm.ap.lrlim2;
-    const double tau_y = prm.op.tau_y, tau_x = prm.op.tau_x;
-
     while (it < end) {
         const int t = (int)(it / n_pix);
         const int p0 = (int)(it - (long long)t * n_pix);
@@ -260,88 +334,59 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
         const int iy = yh < 0 ? yh + prm.N : yh;
         const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
 
-        // lambda Q per slot
-        double Qy[NJ], Qx[NJ];
+        // slot offsets (j_y N, j_x N); lambda Q is rebuilt from them per
+        // pixel, which keeps eight doubles per slot out of the registers
+        int jyN[NJ], jxN[NJ];
         bool act[NJ];
 #pragma unroll
         for (int s = 0; s < NJ; ++s) {
-            Qy[s] = (double)(yh + (int)tile->jy[s] * prm.N) * prm.ldq;
-            Qx[s] = (double)(ix + (int)tile->jx[s] * prm.N) * prm.ldq;
+            jyN[s] = (int)tile->jy[s] * prm.N;
+            jxN[s] = (int)tile->jx[s] * prm.N;
             act[s] = (mask >> s) & 1u;
         }
-
         double acc[NACC];
 #pragma unroll
         for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
 
-        double lky = pix[p0].lky, lkx = pix[p0].lkx, amp0 = pix[p0].amp0, sw = pix[p0].sw, chi0 = pix[p0].chi0;
-        float2 gv = G[goffs[p0] + lane_off];
-        long long goff1 = goffs[p0 + 1 < p1 ? p0 + 1 : p0];
-        for (int p = p0; p < p1; ++p) {
-            const int pn = p + 1 < p1 ? p + 1 : p;
-            const int pnn = pn + 1 < p1 ? pn + 1 : pn;
-            const float2 ngv = G[goff1 + lane_off];
-            const long long goff2 = goffs[pnn];
-            const double nlky = pix[pn].lky, nlkx = pix[pn].lkx, namp0 = pix[pn].amp0, nsw = pix[pn].sw,
-                         nchi0 = pix[pn].chi0;
-            const double lk2 = fma(lky, lky, lkx * lkx);
-            const double py = lky + tau_y, px = lkx + tau_x;
-
-            const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
-            acc[NC] = fma(gr, gr, fma(gi, gi, acc[NC]));   // signal power w |g|^2
-
-            double tr[NC], ti[NC];
-            bool nz[NC];
+        // Pixel records and plane offsets go through LDS a chunk of GRAM_CHUNK
+        // pixels at a time, so the only global loads in the pixel loop are
+        // the G values (vector loads complete in issue order: a record load
+        // in the loop would wait for every older G load).  G is fetched a
+        // group of PF pixels ahead: while group r0 is used from ga, the loads
+        // of group r0 + PF go out into gb, and gb moves to ga at the group's
+        // end, one group's work after issue.  A chunk's tail up to a multiple
+        // of PF runs on zero records (amplitude, sqrt(w) and g all zero:
+        // nothing is added); plane offsets past the segment are clamped to
+        // its last pixel.
+        float2 ga[PF];
 #pragma unroll
-            for (int s = 0; s < NJ; ++s) {
-                // |lambda (k -/+ Q)|^2 = |lambda k|^2 + |lambda Q|^2 -/+ 2 (lambda k).(lambda Q)
-                const double kq = fma(lky, Qy[s], lkx * Qx[s]);
-                const double base = lk2 + fma(Qy[s], Qy[s], Qx[s] * Qx[s]);
-                const double dm2 = fma(-2.0, kq, base);
-                const double dp2 = fma(2.0, kq, base);
-                const bool zl = act[s] && dm2 < lrlim2;
-                const bool zr = act[s] && dp2 < lrlim2;
-                double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
-                if (zl) lobe(prm, T, py - Qy[s], px - Qx[s], dm2, chi0, amp0, 1.0, Lr, Li);
-                if (zr) lobe(prm, T, py + Qy[s], px + Qx[s], dp2, chi0, amp0, -1.0, Rr, Ri);
-                if (METHOD == 0) {
-                    tr[s] = Ri - Li;   // T_phi = i (L - R)
-                    ti[s] = Lr - Rr;
-                    nz[s] = zl || zr;
-                } else {
-                    tr[s] = Lr;
-                    ti[s] = Li;
-                    nz[s] = zl;
-                    tr[NJ + s] = Rr;
-                    ti[NJ + s] = Ri;
-                    nz[NJ + s] = zr;
-                }
+        for (int i = 0; i < PF; ++i) ga[i] = G[goffs[p0 + i < p1 ? p0 + i : p1 - 1] + lane_off];
+        for (int c0 = p0; c0 < p1; c0 += GRAM_CHUNK) {
+            const int cn = (p1 - c0) < GRAM_CHUNK ? (p1 - c0) : GRAM_CHUNK;
+            __syncthreads();   // the previous chunk's records are no longer read
+            if (lane < cn) {
+                srec[lane] = pix[c0 + lane];
+            } else {
+                PixelRec z;
+                z.lky = z.lkx = z.amp0 = z.sw = z.chi0 = z.pad = 0.0;
+                srec[lane] = z;
             }
-
-            bool any[NC];
+            for (int i = lane; i < GRAM_CHUNK + PF; i += 64) sgoff[i] = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
+            __syncthreads();
+            for (int r0 = 0; r0 < cn; r0 += PF) {
+                float2 gb[PF];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) any[c] = wave_any(nz[c]);
+                for (int k = 0; k < PF; ++k) gb[k] = G[sgoff[r0 + PF + k] + lane_off];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                if (!any[c]) continue;
-                acc[c] = fma(tr[c], tr[c], fma(ti[c], ti[c], acc[c]));
-                // right side <col c, g> = conj(t_c) g
-                acc[Sh::re(c, NC)] = fma(tr[c], gr, fma(ti[c], gi, acc[Sh::re(c, NC)]));
-                acc[Sh::im(c, NC)] = fma(tr[c], gi, fma(-ti[c], gr, acc[Sh::im(c, NC)]));
-#pragma unroll
-                for (int d = c + 1; d < NC; ++d) {
-                    if (!any[d]) continue;
-                    acc[Sh::re(c, d)] = fma(tr[c], tr[d], fma(ti[c], ti[d], acc[Sh::re(c, d)]));
-                    acc[Sh::im(c, d)] = fma(tr[c], ti[d], fma(-ti[c], tr[d], acc[Sh::im(c, d)]));
+                for (int k = 0; k < PF; ++k) {
+                    const int r = r0 + k;
+                    const float2 gv = r < cn ? ga[k] : make_float2(0.0f, 0.0f);
+                    gram_pixel<NJ, METHOD>(prm, T, acc, yh, ix, jyN, jxN, act, srec[r].lky, srec[r].lkx,
+                                           srec[r].amp0, srec[r].sw, srec[r].chi0, gv);
                 }
+#pragma unroll
+                for (int k = 0; k < PF; ++k) ga[k] = gb[k];
             }
-            lky = nlky;
-            lkx = nlkx;
-            amp0 = namp0;
-            sw = nsw;
-            chi0 = nchi0;
-            gv = ngv;
-            goff1 = goff2;
         }
 
         double *po = prm.partial + (size_t)seg * (NACC * 64);
