@@ -94,6 +94,21 @@ struct GramShape {
     static constexpr int im(int c, int d) { return D + 2 * off(c, d) + 1; }
 };
 
+// Complex method: the sums of column pairs within one side (L x L and R x R,
+// both columns below NJ or both in NJ .. 2 NJ - 1) live in LDS, one double2
+// per pair and lane; they are updated least often, and keeping them out of
+// the registers lets two waves share a SIMD.
+template <int NJ, int METHOD>
+struct GramLds {
+    static constexpr int NH = NJ * (NJ - 1) / 2;              // pairs per side
+    static constexpr int NP = METHOD == 1 ? 2 * NH : 0;
+    static constexpr bool in_lds(int c, int d) {
+        return METHOD == 1 && c < d && d < 2 * NJ && ((d < NJ) || (c >= NJ));
+    }
+    static constexpr int tri(int c, int d) { return c * (2 * NJ - c - 1) / 2 + (d - c - 1); }   // c < d < NJ
+    static constexpr int idx(int c, int d) { return c < NJ ? tri(c, d) : NH + tri(c - NJ, d - NJ); }
+};
+
 template <int NJ, int METHOD>
 __device__ __forceinline__ void acc_get(const double *acc, int c, int d, double &xr, double &xi) {
     using Sh = GramShape<NJ, METHOD>;
@@ -194,7 +209,7 @@ struct GramPrefetch {
 template <int NJ, int METHOD>
 struct GramWaves {
     static constexpr int value = METHOD == 0 ? (NJ <= 2 ? 4 : (NJ <= 4 ? 3 : (NJ <= 6 ? 2 : 1)))
-                                             : (NJ <= 1 ? 4 : (NJ <= 2 ? 3 : (NJ <= 3 ? 2 : 1)));
+                                             : (NJ <= 1 ? 4 : (NJ <= 2 ? 3 : (NJ <= 4 ? 2 : 1)));
 };
 
 // Pixel records and plane offsets are written by earlier kernels or copies,
@@ -228,11 +243,12 @@ __device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, do
 }
 
 // One pixel's update of a lane's sums: the lobes of every slot, then the
-// rank-one update of the augmented Gram restricted to the columns some lane
-// of the wave has (the rest of the wave adds exact zeros there).
+// rank-one update of the augmented Gram.  A column's terms run when some
+// lane of the wave has it, a pair's when some lane has both (the other lanes
+// add exact zeros).
 template <int NJ, int METHOD>
 __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 *T,
-                                           double (&acc)[GramShape<NJ, METHOD>::NACC], int yh, int ix,
+                                           double (&acc)[GramShape<NJ, METHOD>::NACC], double2 *lpair, int yh, int ix,
                                            const int (&jyN)[NJ], const int (&jxN)[NJ], const bool (&act)[NJ],
                                            double lky, double lkx, double amp0, double sw, double chi0, float2 gv) {
     using Sh = GramShape<NJ, METHOD>;
@@ -246,7 +262,7 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
     acc[NC] = fma(gr, gr, fma(gi, gi, acc[NC]));   // signal power w |g|^2
 
     double tr[NC], ti[NC];
-    bool nz[NC];
+    unsigned long long bal[NC];   // lanes whose column is non-zero
 #pragma unroll
     for (int s = 0; s < NJ; ++s) {
         const double Qy_s = (double)(yh + jyN[s]) * ldq, Qx_s = (double)(ix + jxN[s]) * ldq;
@@ -263,32 +279,36 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
         if (METHOD == 0) {
             tr[s] = Ri - Li;   // T_phi = i (L - R)
             ti[s] = Lr - Rr;
-            nz[s] = zl || zr;
+            bal[s] = __ballot(zl || zr);
         } else {
             tr[s] = Lr;
             ti[s] = Li;
-            nz[s] = zl;
+            bal[s] = __ballot(zl);
             tr[NJ + s] = Rr;
             ti[NJ + s] = Ri;
-            nz[NJ + s] = zr;
+            bal[NJ + s] = __ballot(zr);
         }
     }
 
-    bool any[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) any[c] = wave_any(nz[c]);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        if (!any[c]) continue;
+        if (!bal[c]) continue;
         acc[c] = fma(tr[c], tr[c], fma(ti[c], ti[c], acc[c]));
         // right side <col c, g> = conj(t_c) g
         acc[Sh::re(c, NC)] = fma(tr[c], gr, fma(ti[c], gi, acc[Sh::re(c, NC)]));
         acc[Sh::im(c, NC)] = fma(tr[c], gi, fma(-ti[c], gr, acc[Sh::im(c, NC)]));
 #pragma unroll
         for (int d = c + 1; d < NC; ++d) {
-            if (!any[d]) continue;
-            acc[Sh::re(c, d)] = fma(tr[c], tr[d], fma(ti[c], ti[d], acc[Sh::re(c, d)]));
-            acc[Sh::im(c, d)] = fma(tr[c], ti[d], fma(-ti[c], tr[d], acc[Sh::im(c, d)]));
+            if (!(bal[c] & bal[d])) continue;
+            if (GramLds<NJ, METHOD>::in_lds(c, d)) {
+                double2 v = lpair[GramLds<NJ, METHOD>::idx(c, d) * 64];
+                v.x = fma(tr[c], tr[d], fma(ti[c], ti[d], v.x));
+                v.y = fma(tr[c], ti[d], fma(-ti[c], tr[d], v.y));
+                lpair[GramLds<NJ, METHOD>::idx(c, d) * 64] = v;
+            } else {
+                acc[Sh::re(c, d)] = fma(tr[c], tr[d], fma(ti[c], ti[d], acc[Sh::re(c, d)]));
+                acc[Sh::im(c, d)] = fma(tr[c], ti[d], fma(-ti[c], tr[d], acc[Sh::im(c, d)]));
+            }
         }
     }
 }
@@ -311,6 +331,8 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
     __shared__ double2 T[TRIG_N];
     __shared__ PixelRec srec[GRAM_CHUNK];
     __shared__ long long sgoff[GRAM_CHUNK + PF];
+    constexpr int NP = GramLds<NJ, METHOD>::NP;
+    __shared__ double2 lpair_all[(NP > 0 ? NP : 1) * 64];
     const int lane = threadIdx.x;
     T[lane] = prm.trig[lane];
 
@@ -347,6 +369,9 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
         double acc[NACC];
 #pragma unroll
         for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
+        double2 *lpair = lpair_all + lane;   // this lane's LDS sums, stride 64
+#pragma unroll
+        for (int i = 0; i < NP; ++i) lpair[i * 64] = make_double2(0.0, 0.0);
 
         // Pixel records and plane offsets go through LDS a chunk of GRAM_CHUNK
         // pixels at a time, so the only global loads in the pixel loop are
@@ -381,7 +406,7 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
                 for (int k = 0; k < PF; ++k) {
                     const int r = r0 + k;
                     const float2 gv = r < cn ? ga[k] : make_float2(0.0f, 0.0f);
-                    gram_pixel<NJ, METHOD>(prm, T, acc, yh, ix, jyN, jxN, act, srec[r].lky, srec[r].lkx,
+                    gram_pixel<NJ, METHOD>(prm, T, acc, lpair, yh, ix, jyN, jxN, act, srec[r].lky, srec[r].lkx,
                                            srec[r].amp0, srec[r].sw, srec[r].chi0, gv);
                 }
 #pragma unroll
@@ -392,6 +417,16 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
         double *po = prm.partial + (size_t)seg * (NACC * 64);
 #pragma unroll
         for (int i = 0; i < NACC; ++i) po[i * 64 + lane] = acc[i];
+#pragma unroll
+        for (int c = 0; c < GramShape<NJ, METHOD>::NC; ++c) {
+#pragma unroll
+            for (int d = c + 1; d < GramShape<NJ, METHOD>::NC; ++d) {
+                if (!GramLds<NJ, METHOD>::in_lds(c, d)) continue;
+                const double2 v = lpair[GramLds<NJ, METHOD>::idx(c, d) * 64];
+                po[GramShape<NJ, METHOD>::re(c, d) * 64 + lane] = v.x;
+                po[GramShape<NJ, METHOD>::im(c, d) * 64 + lane] = v.y;
+            }
+        }
         ++seg;
         it += p1 - p0;
     }
