@@ -388,8 +388,11 @@ def main(argv=None) -> int:
     dom = launches[0]
     kname = f"gram_kernel<{dom['slots']},{0 if dom['method'] == 'phase' else 1}>"
     tr = measured_traffic(kname)
+    # algorithmic HBM bytes of the launch: one complex64 G value per (pixel, frequency) term
+    alg_bytes = 8.0 * flops[(dom["method"], dom["slots"])][1]["terms"]
     roofline = {"bound": "alu", "achieved": dom["tflops"], "peak": FP64_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": dom["tflops"] / FP64_VECTOR_PEAK_TFLOPS, "traffic": tr,
+                "alg_bytes": alg_bytes, "traffic_over_alg": (tr / alg_bytes) if tr else None,
                 "kernel": f"{kname} ({dom['method']} Gram, tiles with {dom['slots']} alias slots, "
                           f"{dom['tiles']} tiles, {dom['lobes']:.3e} non-zero lobes per launch)",
                 "avg_launch_ms": dom["avg_ms"], "flops_per_launch": dom["flops"]}

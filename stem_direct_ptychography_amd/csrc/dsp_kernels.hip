@@ -8,15 +8,16 @@
 // alias count", section "What changed"; "Tilt-corrected SSB on CUDA",
 // section "Changes").
 //
-// Lane mapping of the streaming kernels: a wave owns a 4 x 16 tile of scan
-// frequencies (one per lane) and walks the bright-field pixels in lockstep.
-// Per-pixel data (k, weight, a(k), chi(k), plane offset) is wave-uniform and
-// comes through scalar loads; each lane reads its G(q, k) from a 128-byte
-// run of 16 consecutive stored columns; the lens-overlap zero-skip branches
+// Lane mapping of the streaming kernels: a wave owns a tile of up to 64 scan
+// frequencies (one per lane, cut along G's 128-byte lines by the host) and
+// walks the bright-field pixels in lockstep.  Per-pixel data (lambda k,
+// sqrt(w) a(k), chi(k), plane offset) is wave-uniform and staged in LDS;
+// each lane reads its own G(q, k); the lens-overlap zero-skip branches
 // almost never diverge because neighbouring frequencies see nearly the same
 // lens; each lane keeps its own frequency's sums, so there is no cross-lane
-// reduction.  A workgroup of P waves splits the pixels round-robin and adds
-// its waves' sums through LDS in a fixed order (deterministic).
+// reduction.  The tiles x pixels of a launch are split into equal-cost
+// contiguous ranges (stream-K), one per wave; partial sums are added per
+// tile in a fixed order afterwards (deterministic).
 #include "dsp_internal.hpp"
 #include "dsp_kernels.hpp"
 
