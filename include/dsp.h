@@ -206,6 +206,23 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
                    int B, const double *band_invA, void *S_out_c128_dev, double *norm_out_dev,
                    double *agreement_out_host, void *hip_stream);
 
+/*
+ * Phase model derived from a prepared complex model, without a pass over G
+ * ("Where the 9 s of regularized preparation goes", section "Code path":
+ * the complex system contains the phase one).  For every frequency the phase
+ * system is the T_phi block of the complex system ([T_A, T_phi] order), the
+ * T_phi part of its right side and the same signal power; the phase
+ * eigenbasis is then computed as in dsp_prepare.
+ *   complex_h: a handle from dsp_prepare with method DSP_COMPLEX (not
+ *              modified; it may be destroyed before or after the new handle).
+ *   out: a new DSP_PHASE handle, owned by the caller (dsp_destroy), usable with
+ *        dsp_solve, dsp_scatter, dsp_info, dsp_export_system, dsp_alias_table.
+ * Kernels run on hip_stream; complex_h's prepare must be ordered before them
+ * (same stream, or synchronized).  DSP_EINVAL for a NULL argument or a phase
+ * source handle; on error *out is NULL.
+ */
+dsp_status dsp_derive_phase(const dsp_handle *complex_h, void *hip_stream, dsp_handle **out);
+
 /* Sizes, histogram, timings of a prepared handle.  Does not wait for the
  * device, except to read DSP_FLAG_COUNT_WORK counts (a blocking copy). */
 dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out);

@@ -125,7 +125,7 @@ class Prepared:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        if h and _L is not None:   # _L is None during interpreter teardown
             _L.dsp_destroy(h)
             self._h = None
 
@@ -152,6 +152,15 @@ class Prepared:
         s.synchronize()
         self.info = self._info()
         return self.info
+
+    def derive_phase(self, stream=None) -> "Prepared":
+        """Phase model from this complex model's systems, with no pass over G
+        (dsp_derive_phase)."""
+        if self.method != "complex":
+            raise ValueError("derive_phase needs a complex-method prepare")
+        h = ctypes.c_void_p()
+        _check(_L.dsp_derive_phase(self._h, ctypes.c_void_p(_stream(stream)), ctypes.byref(h)))
+        return Prepared(h, self.device, "phase")
 
     def solve(self, strengths, residual: bool = False, stream=None):
         torch = _torch()

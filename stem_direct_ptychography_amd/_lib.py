@@ -61,7 +61,7 @@ class InfoC(ctypes.Structure):
 EXPORTS = (
     "dsp_prepare", "dsp_solve", "dsp_scatter", "dsp_ssb", "dsp_info", "dsp_export_system", "dsp_alias_table",
     "dsp_destroy", "dsp_last_error", "dsp_geometry_counts", "dsp_alias_geometry", "dsp_active_bf",
-    "dsp_band_count", "dsp_chi_host", "dsp_sincos_host",
+    "dsp_band_count", "dsp_chi_host", "dsp_sincos_host", "dsp_derive_phase",
 )
 
 _P = ctypes.c_void_p
@@ -86,6 +86,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsp_prepare.restype = _I
     lib.dsp_prepare.argtypes = [_P, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC),
                                 ctypes.POINTER(PrepareOptsC), _P, ctypes.POINTER(_P)]
+    lib.dsp_derive_phase.restype = _I
+    lib.dsp_derive_phase.argtypes = [_P, _P, ctypes.POINTER(_P)]
     lib.dsp_solve.restype = _I
     lib.dsp_solve.argtypes = [_P, _DP, _I, _P, _P, _P]
     lib.dsp_scatter.restype = _I

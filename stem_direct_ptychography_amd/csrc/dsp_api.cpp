@@ -990,6 +990,35 @@ struct dsp_handle {
     }
 };
 
+// Phase eigenbasis of every frequency from the handle's systems, one Jacobi
+// launch per alias count.
+static dsp_status phase_eigen(dsp_handle *h, hipStream_t stream) {
+    const Layout &L = *h->L;
+    const Geometry &g = L.geo;
+    const int am = std::max(1, g.a_max);
+    EigParams ep;
+    ep.sys = h->d_sys;
+    ep.D = h->D;
+    ep.a_max = am;
+    ep.prior = L.d_prior;
+    ep.lam = h->d_lam;
+    ep.U = h->d_U;
+    ep.c = h->d_c;
+    // frequencies without aliases keep zero eigen data
+    if (L.bucket_n[0] > 0) {
+        HIP_TRY(launch_fill_zero(h->d_lam, (size_t)g.n_q * am, stream));
+        HIP_TRY(launch_fill_zero((double *)h->d_U, (size_t)g.n_q * am * am * 2, stream));
+        HIP_TRY(launch_fill_zero((double *)h->d_c, (size_t)g.n_q * am * 2, stream));
+    }
+    for (int A = 1; A <= 9; ++A) {
+        if (L.bucket_n[A] == 0) continue;
+        ep.qlist = L.d_bucket + L.bucket_off[A];
+        ep.n = L.bucket_n[A];
+        HIP_TRY(launch_eig(ep, A, stream));
+    }
+    return DSP_OK;
+}
+
 extern "C" {
 
 const char *dsp_last_error(void) { return g_err.c_str(); }
@@ -1200,28 +1229,7 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     }
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[2], stream));
 
-    if (h->method == DSP_PHASE) {
-        EigParams ep;
-        ep.sys = h->d_sys;
-        ep.D = h->D;
-        ep.a_max = am;
-        ep.prior = L.d_prior;
-        ep.lam = h->d_lam;
-        ep.U = h->d_U;
-        ep.c = h->d_c;
-        // frequencies without aliases keep zero eigen data
-        if (L.bucket_n[0] > 0) {
-            HIP_TRY(launch_fill_zero(h->d_lam, (size_t)g.n_q * am, stream));
-            HIP_TRY(launch_fill_zero((double *)h->d_U, (size_t)g.n_q * am * am * 2, stream));
-            HIP_TRY(launch_fill_zero((double *)h->d_c, (size_t)g.n_q * am * 2, stream));
-        }
-        for (int A = 1; A <= 9; ++A) {
-            if (L.bucket_n[A] == 0) continue;
-            ep.qlist = L.d_bucket + L.bucket_off[A];
-            ep.n = L.bucket_n[A];
-            HIP_TRY(launch_eig(ep, A, stream));
-        }
-    }
+    if (h->method == DSP_PHASE && (st = phase_eigen(h.get(), stream))) return st;
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[3], stream));
     if (h->count_work) {
         // instrumentation after the prepare's own kernels: work per tile
@@ -1232,6 +1240,37 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
                                       stream));
         }
     }
+    h->host_ms = now_ms() - t0;
+    *out = h.release();
+    return DSP_OK;
+}
+
+dsp_status dsp_derive_phase(const dsp_handle *src, void *hip_stream, dsp_handle **out) {
+    if (!out) return fail(DSP_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (!src) return fail(DSP_EINVAL, "handle is NULL");
+    if (src->method != DSP_COMPLEX) return fail(DSP_EINVAL, "the source handle must come from a complex prepare");
+    const double t0 = now_ms();
+    HIP_TRY(hipSetDevice(src->device));
+    hipStream_t stream = (hipStream_t)hip_stream;
+    dsp_status st;
+    std::unique_ptr<dsp_handle> h(new dsp_handle());
+    h->device = src->device;
+    h->method = DSP_PHASE;
+    h->L = src->L;
+    h->n_bf = src->n_bf;
+    h->n_comp = 1;
+    h->layout_hit = true;
+    h->stream = stream;
+    const Geometry &g = h->L->geo;
+    const int am = std::max(1, g.a_max);
+    h->D = am + 1;
+    if ((st = dev_alloc(&h->d_sys, (size_t)g.n_q * tri_size(h->D))) ||
+        (st = dev_alloc(&h->d_lam, (size_t)g.n_q * am)) || (st = dev_alloc(&h->d_U, (size_t)g.n_q * am * am)) ||
+        (st = dev_alloc(&h->d_c, (size_t)g.n_q * am)))
+        return st;
+    HIP_TRY(launch_phase_from_complex(src->d_sys, h->d_sys, am, g.n_q, stream));
+    if ((st = phase_eigen(h.get(), stream))) return st;
     h->host_ms = now_ms() - t0;
     *out = h.release();
     return DSP_OK;

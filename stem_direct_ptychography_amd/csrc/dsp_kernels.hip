@@ -201,9 +201,11 @@ __device__ __forceinline__ void write_system(const double *acc, unsigned mask, i
 constexpr int GRAM_CHUNK = 64;
 
 // G values fetched ahead per lane: one group of PF pixels (divides GRAM_CHUNK).
+// Two for the phase kernels (no measurable loss, and it keeps the 4-slot
+// kernel within three waves per SIMD without spills), four for complex.
 template <int NJ, int METHOD>
 struct GramPrefetch {
-    static constexpr int value = 4;
+    static constexpr int value = METHOD == 0 ? 2 : 4;
 };
 
 // Waves per SIMD the compiler must fit (caps the registers per lane).
@@ -512,6 +514,29 @@ __global__ __launch_bounds__(64) void work_count_kernel(GramParams prm, unsigned
 }
 
 // ---------------------------------------------------------------------------
+// phase system from a complex one
+// ---------------------------------------------------------------------------
+// Thread = (frequency, packed entry of the phase triangle).  Slot m of the
+// phase system is the complex system's T_phi slot a_max + m; g is slot a_max
+// in the phase system and 2 a_max in the complex one.
+__global__ void phase_from_complex_kernel(const double2 *csys, double2 *psys, int am, int n_q) {
+    const int Dp = am + 1, Dc = 2 * am + 1;
+    const int T = tri_size(Dp);
+    const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long long)n_q * T) return;
+    const int q = (int)(idx / T);
+    int rem = (int)(idx - (long long)q * T);
+    int i = 0;
+    while (rem >= Dp - i) {
+        rem -= Dp - i;
+        ++i;
+    }
+    const int j = i + rem;
+    const int ci = i < am ? am + i : 2 * am, cj = j < am ? am + j : 2 * am;
+    psys[idx] = csys[(size_t)q * tri_size(Dc) + tri_idx(ci, cj, Dc)];
+}
+
+// ---------------------------------------------------------------------------
 // phase eigenbasis: cyclic complex Jacobi, one lane per frequency
 // ---------------------------------------------------------------------------
 
@@ -561,16 +586,26 @@ __global__ __launch_bounds__(64) void eig_kernel(EigParams prm) {
 #pragma unroll
             for (int qq = p + 1; qq < A; ++qq) {
                 const double br = hr[p][qq], bi = hi[p][qq];
-                const double bn = sqrt(br * br + bi * bi);
-                const bool rot = bn > 0.0;
-                const double er = rot ? br / bn : 1.0, ei = rot ? bi / bn : 0.0;   // e^{i phi}
                 const double a = hr[p][p], d = hr[qq][qq];
+                // |b| and e^{i phi} = b / |b| from components scaled to
+                // order one, so |e| = 1 to rounding even where b * b would
+                // underflow.  A rotation is applied only where |b| is above
+                // 2^-60 (|a| + |d|): below that it changes the eigenvalues by
+                // less than the rounding of the convergence test, and a phase
+                // factor taken from a tiny |b| would only add error to V.
+                const double bm = fmax(fabs(br), fabs(bi));
+                const double sbr = bm > 0.0 ? br / bm : 0.0, sbi = bm > 0.0 ? bi / bm : 0.0;
+                const double sn = sqrt(sbr * sbr + sbi * sbi);
+                const double bn = bm * sn;
+                const bool rot = bn > 0x1p-60 * (fabs(a) + fabs(d)) && bn > 0.0;
+                const double er = rot ? sbr / sn : 1.0, ei = rot ? sbi / sn : 0.0;   // e^{i phi}
                 const double zeta = rot ? (d - a) / (2.0 * bn) : 0.0;
                 double tt = 1.0 / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
                 tt = zeta < 0.0 ? -tt : tt;
                 tt = rot ? tt : 0.0;
                 const double c = 1.0 / sqrt(1.0 + tt * tt), s = tt * c;
                 // J = [[c, s], [-s e^{-i phi}, c e^{-i phi}]] on columns (p, qq)
+                if (!rot) continue;   // negligible: left in place (below the convergence test)
                 hr[p][p] = a - tt * bn;
                 hr[qq][qq] = d + tt * bn;
                 hr[p][qq] = 0.0;
@@ -1183,6 +1218,14 @@ hipError_t launch_work_count(const GramParams &prm, int method, int n_tiles, uns
     if (n_tiles <= 0) return hipSuccess;
     if (method == 0) work_count_kernel<0><<<n_tiles, 64, 0, st>>>(prm, out);
     else work_count_kernel<1><<<n_tiles, 64, 0, st>>>(prm, out);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_phase_from_complex(const double2 *csys, double2 *psys, int a_max, int n_q, hipStream_t st) {
+    const long long n = (long long)n_q * tri_size(a_max + 1);
+    if (n <= 0) return hipSuccess;
+    phase_from_complex_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(csys, psys, a_max, n_q);
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }
