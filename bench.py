@@ -441,6 +441,16 @@ def main(argv=None) -> int:
         "stream_ms_per_step": gpu_ms / args.steps,
         "agreement": float(step.last["E"][0]),
     }
+    # phase model derived from the last complex model (no pass over G), outside the step
+    d_ms = []
+    for _ in range(3):
+        e0.record(stream)
+        pd = step.last["complex"].derive_phase()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        d_ms.append(e0.elapsed_time(e1))
+        del pd
+    result["phase_derived_from_complex_ms"] = float(np.median(d_ms))
     del step.last
     torch.cuda.synchronize()
 
