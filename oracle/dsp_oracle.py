@@ -169,13 +169,36 @@ def chi(ky, kx, optics):
     return (2.0 * math.pi / lam) * acc
 
 
+def depth_factor(delta, optics):
+    """Depth term of one lobe for a weak object spread evenly through the
+    thickness t = optics.depth (A) downstream of the plane chi refers to.
+
+    A slice at depth z sees the probe propagated by z, A(k) exp(-i pi z
+    |theta_k|^2 / lambda) (paraxial, theta_k = lambda k + tau the beam
+    direction, so a tilted beam also walks sideways with depth).  The lobe
+    built from the probe at k and at k' then carries exp(i pi z delta /
+    lambda) with delta = |theta_k|^2 - |theta_k'|^2 (L) or |theta_k'|^2 -
+    |theta_k|^2 (R); its mean over z in [0, t] is
+        exp(i phi / 2) sinc(phi / 2),   phi = pi t delta / lambda,
+    the "sinc and phase factor" of [P1] What changed 2 and of the thick-sample
+    fits of [P3] Where the time went.  Exactly 1 at t = 0.
+    """
+    t = float(getattr(optics, "depth", 0.0))
+    delta = np.asarray(delta, dtype=np.float64)
+    if t == 0.0:
+        return np.ones(delta.shape, dtype=np.complex128)
+    h = 0.5 * math.pi * t * delta / optics.wavelength
+    return np.exp(1j * h) * np.sinc(h / math.pi)          # np.sinc(x) = sin(pi x) / (pi x)
+
+
 def lobes(ky, kx, Qy: float, Qx: float, optics):
     """The two weak-object lobes at scattering vector k for object frequency Q.
 
     L = a(k) a(k - Q) exp(+i [chi(k) - chi(k - Q)])      (= conj A(k) A(k - Q))
     R = a(k) a(k + Q) exp(-i [chi(k) - chi(k + Q)])      (= A(k) conj A(k + Q))
     Each is exactly zero where its two apertures do not overlap ([P1] What
-    changed 2: exact zeros skipped).  Depth terms are 1 (depth 0).
+    changed 2: exact zeros skipped).  With a depth, each lobe is multiplied by
+    its depth_factor (1 at depth 0).
     """
     ky = np.asarray(ky, dtype=np.float64)
     kx = np.asarray(kx, dtype=np.float64)
@@ -187,6 +210,16 @@ def lobes(ky, kx, Qy: float, Qx: float, optics):
     cp = chi(ky + Qy, kx + Qx, optics)
     L = a0 * am * np.exp(1j * (c0 - cm))
     R = a0 * ap * np.exp(-1j * (c0 - cp))
+    if float(getattr(optics, "depth", 0.0)) != 0.0:
+        lam = optics.wavelength
+        ty, tx = optics.tilt
+
+        def th2(y, x):
+            return (lam * y + ty) ** 2 + (lam * x + tx) ** 2
+
+        t0 = th2(ky, kx)
+        L = L * depth_factor(t0 - th2(ky - Qy, kx - Qx), optics)
+        R = R * depth_factor(th2(ky + Qy, kx + Qx) - t0, optics)
     return L, R
 
 

@@ -22,6 +22,8 @@ With c sampled on the u N fine grid, N^2 c^(K) = fft2(c)[K] / u^2.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from .dsp_oracle import aperture, chi, scan_frequency_step, signed_index
@@ -89,7 +91,8 @@ def band_limited_field(nf: int, rng: np.random.Generator, std: float = 1.0, cuto
     return f * (std / f.std())
 
 
-def wave_optics_G(n_scan: int, step: float, m_sim: int, optics, c_fine: np.ndarray, upsampling: int):
+def wave_optics_G(n_scan: int, step: float, m_sim: int, optics, c_fine: np.ndarray, upsampling: int,
+                  n_slices: int = 1):
     """Brute-force data for object transmission exp(c), c = A_l + i phi.
 
     The simulation grid spans the scan's field of view L = N s with m_sim
@@ -99,6 +102,13 @@ def wave_optics_G(n_scan: int, step: float, m_sim: int, optics, c_fine: np.ndarr
     the N x N scan positions; the object is the fine-grid field Fourier
     interpolated onto the simulation grid.  Returns (k (m^2, 2) detector
     vectors (1/A), G (m^2, N, N/2+1) complex128).
+
+    With optics.depth = t > 0 the object is a multislice stack: n_slices
+    slices of transmission exp(c / n_slices) at depths (j + 1/2) t /
+    n_slices below the plane chi refers to, the wave propagated between them
+    by the paraxial Fresnel factor exp(-i pi dz |lambda k + tau|^2 / lambda)
+    (beam direction theta = lambda k + tau, numpy's exp(+2 pi i k.r) inverse
+    transform).  The far-field intensity after the last slice is the data.
     """
     n = n_scan
     m = m_sim
@@ -114,12 +124,33 @@ def wave_optics_G(n_scan: int, step: float, m_sim: int, optics, c_fine: np.ndarr
     idx = signed_index(np.arange(nf), nf)
     Fs[np.ix_(idx % m, idx % m)] = F
     c_sim = np.fft.ifft2(Fs) * (m / nf) ** 2
-    obj = np.exp(c_sim)
+    t = float(getattr(optics, "depth", 0.0))
     I = np.empty((n, n, m, m))
-    for py in range(n):
-        for px in range(n):
-            ps = np.roll(psi, (py * shift, px * shift), axis=(0, 1))
-            I[py, px] = np.abs(np.fft.fft2(ps * obj)) ** 2
+    if t == 0.0:
+        obj = np.exp(c_sim)
+        for py in range(n):
+            for px in range(n):
+                ps = np.roll(psi, (py * shift, px * shift), axis=(0, 1))
+                I[py, px] = np.abs(np.fft.fft2(ps * obj)) ** 2
+    else:
+        lam = optics.wavelength
+        th2 = (lam * KY + optics.tilt[0]) ** 2 + (lam * KX + optics.tilt[1]) ** 2
+        dz = t / n_slices
+
+        def prop(z):
+            return np.exp(-1j * math.pi * z * th2 / lam)
+
+        first, between = prop(0.5 * dz), prop(dz)
+        sl = np.exp(c_sim / n_slices)
+        for py in range(n):
+            for px in range(n):
+                ps = np.roll(psi, (py * shift, px * shift), axis=(0, 1))
+                W = np.fft.fft2(ps) * first
+                for j in range(n_slices):
+                    if j:
+                        W = W * between
+                    W = np.fft.fft2(np.fft.ifft2(W) * sl)
+                I[py, px] = np.abs(W) ** 2
     G = np.fft.rfft2(I, axes=(0, 1))                    # (n, n/2+1, m, m)
     G = np.transpose(G, (2, 3, 0, 1)).reshape(m * m, n, n // 2 + 1)
     k = np.stack([KY.ravel(), KX.ravel()], axis=1)

@@ -262,6 +262,82 @@ def test_wave_optics_pin_catches_planted_mistakes(monkeypatch):
     assert r_bad > 0.05
 
 
+# ----------------------------------------------------------------------------
+# depth (thick sample): the lobe's sinc and phase factor
+# ----------------------------------------------------------------------------
+
+
+def test_depth_factor_is_the_mean_over_the_slab():
+    """depth_factor against brute-force quadrature of exp(i pi z delta / lambda)
+    over z in [0, t]; exactly 1 at depth 0."""
+    opt = tiny_optics(0.1).replace(depth=80.0)
+    delta = np.array([-3e-3, -1e-4, 0.0, 2e-5, 7e-4, 2.5e-3])
+    z = (np.arange(20000) + 0.5) / 20000 * opt.depth
+    brute = np.exp(1j * math.pi * z[None, :] * delta[:, None] / opt.wavelength).mean(axis=1)
+    assert np.allclose(O.depth_factor(delta, opt), brute, rtol=0, atol=1e-8)
+    assert np.all(O.depth_factor(delta, opt.replace(depth=0.0)) == 1.0)
+    ky, kx = np.array([0.3, -0.5]), np.array([0.1, 0.7])
+    L0, R0 = O.lobes(ky, kx, 0.4, -0.2, opt.replace(depth=0.0))
+    L1, R1 = O.lobes(ky, kx, 0.4, -0.2, opt.replace(depth=1e-12))
+    assert np.allclose(L0, L1, rtol=1e-12, atol=0) and np.allclose(R0, R1, rtol=1e-12, atol=0)
+
+
+def _depth_residual(sigma, opt, n=16, step=0.5, u=2, m=64, seed=5, n_slices=64):
+    rng = np.random.default_rng(seed)
+    nf = u * n
+    c = sigma * (S.band_limited_field(nf, rng) + 1j * S.band_limited_field(nf, rng))
+    k, G = S.wave_optics_G(n, step, m, opt, c, u, n_slices=n_slices)
+    act = O.active_pixels(k, opt)
+    dq = O.scan_frequency_step(n, step)
+    q, _, Ks = O.alias_table(n, step, u, opt)
+    FA, FP = S.fine_spectrum(c.real, u), S.fine_spectrum(c.imag, u)
+    num = den = 0.0
+    for (iy, ix), K in zip(q, Ks):
+        T = O.transfer(k[act], K * dq, opt, "complex")
+        x = np.concatenate([FA[K[:, 0] % nf, K[:, 1] % nf], FP[K[:, 0] % nf, K[:, 1] % nf]])
+        model = T @ x
+        num += np.sum(np.abs(G[act, iy, ix] - model) ** 2)
+        den += np.sum(np.abs(model) ** 2)
+    return math.sqrt(num / den)
+
+
+def test_depth_transfer_matches_multislice(monkeypatch):
+    """The depth terms (sinc and phase factor per lobe, tilt included) against
+    a 64-slice multislice simulation of a 60 A weak object; planted mistakes
+    (no depth term, conjugated phase factor, sinc without its phase, the
+    tilt left out of the depth term) fail by O(1)."""
+    n, step = 16, 0.5
+    opt = tiny_optics(O.scan_frequency_step(n, step)).replace(depth=60.0)
+    r1 = _depth_residual(1e-3, opt)
+    r2 = _depth_residual(5e-4, opt)
+    assert r1 < 1e-2
+    assert 0.4 < r2 / r1 < 0.6
+    true_factor = O.depth_factor
+    true_lobes = O.lobes
+    for name, bad in [
+        ("no depth", lambda d, o: np.ones(np.shape(d), dtype=np.complex128)),
+        ("conjugate phase", lambda d, o: np.conj(true_factor(d, o))),
+        ("sinc only", lambda d, o: np.sinc(0.5 * o.depth * np.asarray(d) / o.wavelength) + 0j),
+    ]:
+        monkeypatch.setattr(O, "depth_factor", bad)
+        r_bad = _depth_residual(1e-3, opt)
+        monkeypatch.setattr(O, "depth_factor", true_factor)
+        assert r_bad > 0.3, name
+
+    def untilted(ky, kx, Qy, Qx, o):
+        L, R = true_lobes(ky, kx, Qy, Qx, o.replace(depth=0.0))
+        lam = o.wavelength
+        t0 = (lam * ky) ** 2 + (lam * kx) ** 2
+        dl = t0 - ((lam * (ky - Qy)) ** 2 + (lam * (kx - Qx)) ** 2)
+        dr = (lam * (ky + Qy)) ** 2 + (lam * (kx + Qx)) ** 2 - t0
+        return L * true_factor(dl, o), R * true_factor(dr, o)
+
+    monkeypatch.setattr(O, "lobes", untilted)
+    r_bad = _depth_residual(1e-3, opt)
+    monkeypatch.setattr(O, "lobes", true_lobes)
+    assert r_bad > 0.1
+
+
 def test_first_order_model_equals_transfer_sum():
     """The physics-form first-order data (written from A(k)) equals
     sum_Q T x over the oracle's aliases."""
