@@ -242,8 +242,10 @@ def ssb_sweep(dsp, dev, reps: int = 5):
     out = {"workload": f"512x512 scan, {len(k)} BF px, band {w.band[0]}-{w.band[1]} 1/A ({n_band} stored q)",
            "g_bytes_per_pass": g_bytes, "passes": {}}
     stream = torch.cuda.current_stream()
-    for B in (1, 2, 4, 8):
-        sets = ssb_sets(w, B)
+    # the pages' thick-sample fit batch: the same sets at depth 136 A
+    runs = [(B, 0.0) for B in (1, 2, 4, 8)] + [(1, 136.0), (8, 136.0)]
+    for B, depth in runs:
+        sets = [o.replace(depth=depth) for o in ssb_sets(w, B)]
         dsp.ssb(G, k, sets, step=w.step, band=w.band, agreement=False)
         ms = []
         for _ in range(reps):
@@ -255,9 +257,10 @@ def ssb_sweep(dsp, dev, reps: int = 5):
             e1.synchronize()
             ms.append(e0.elapsed_time(e1))
         m = float(np.median(ms))
-        out["passes"][str(B)] = {"ms": m, "q_sets_per_s": n_band * B / (m / 1e3),
-                                 "g_GBps": g_bytes / (m / 1e3) / 1e9}
-        log(f"ssb B={B}: {m:.3f} ms")
+        name = str(B) if depth == 0.0 else f"{B} depth {depth:g} A"
+        out["passes"][name] = {"ms": m, "q_sets_per_s": n_band * B / (m / 1e3),
+                               "g_GBps": g_bytes / (m / 1e3) / 1e9}
+        log(f"ssb B={B} depth {depth:g} A: {m:.3f} ms")
     del G
     torch.cuda.empty_cache()
     return out
@@ -451,6 +454,19 @@ def main(argv=None) -> int:
         d_ms.append(e0.elapsed_time(e1))
         del pd
     result["phase_derived_from_complex_ms"] = float(np.median(d_ms))
+    # the same prepares with the depth of the pages' saved fit (12.4 nm), outside the step
+    deep = w.optics.replace(depth=124.0)
+    depth_ms = {}
+    for method in ("phase", "complex"):
+        ts = []
+        for _ in range(3):
+            p = dsp.prepare(G, k, deep, step=w.step, upsampling=w.upsampling, method=method,
+                            smoothness=w.smoothness, timing=True)
+            ts.append(p.timings()["stage_ms"][3])
+            del p
+        depth_ms[method + "_prepare_ms"] = float(np.median(ts))
+    result["depth_124A"] = depth_ms
+    log(f"depth 124 A prepares: {depth_ms}")
     del step.last
     torch.cuda.synchronize()
 

@@ -64,7 +64,7 @@ extern "C" {
 typedef enum {
     DSP_OK = 0,
     DSP_EINVAL = 1,        /* bad argument: NULL, size, range, layout */
-    DSP_EUNSUPPORTED = 2,  /* valid but not built: depth != 0, odd N, u > 4 */
+    DSP_EUNSUPPORTED = 2,  /* valid but not built: odd N, u > 4 */
     DSP_EALIAS = 3,        /* an alias count above the compiled maximum */
     DSP_ENOMEM = 4,        /* device or host allocation failed */
     DSP_EDEVICE = 5        /* HIP runtime / launch failure */
@@ -88,7 +88,11 @@ typedef struct {
     double det_step_invA;    /* dk: detector pixel pitch in the scan frame */
     int soft_aperture;       /* 1: soft edge one pixel wide, 0: hard */
     double tilt_rad[2];      /* (tau_y, tau_x) */
-    double depth_A;          /* must be 0 */
+    double depth_A;          /* t >= 0: weak object spread evenly through depth t below the
+                                plane chi refers to; each lobe gains exp(i h) sinc(h),
+                                h = pi t (|theta_k|^2 - |theta_k'|^2) / (2 lambda)
+                                ("Where the 9 s of regularized preparation goes", What
+                                changed 2); 0: thin object */
     int n_aber;              /* <= DSP_MAX_ABERRATIONS */
     dsp_aberration aber[DSP_MAX_ABERRATIONS];
 } dsp_optics;

@@ -68,7 +68,7 @@ dsp_status check_optics(const dsp_optics *o) {
     if (!(o->semiangle_rad > 0.0) || !std::isfinite(o->semiangle_rad)) return fail(DSP_EINVAL, "semiangle must be > 0");
     if (!(o->det_step_invA > 0.0) || !std::isfinite(o->det_step_invA)) return fail(DSP_EINVAL, "det_step must be > 0");
     if (o->soft_aperture != 0 && o->soft_aperture != 1) return fail(DSP_EINVAL, "soft_aperture must be 0 or 1");
-    if (o->depth_A != 0.0) return fail(DSP_EUNSUPPORTED, "depth terms are not built (depth_A must be 0)");
+    if (!(o->depth_A >= 0.0) || !std::isfinite(o->depth_A)) return fail(DSP_EINVAL, "depth_A must be finite and >= 0");
     if (!std::isfinite(o->tilt_rad[0]) || !std::isfinite(o->tilt_rad[1])) return fail(DSP_EINVAL, "tilt not finite");
     if (o->n_aber < 0 || o->n_aber > DSP_MAX_ABERRATIONS)
         return fail(DSP_EINVAL, "n_aber %d outside [0, %d]", o->n_aber, DSP_MAX_ABERRATIONS);
@@ -128,6 +128,7 @@ OpticsDev make_optics_dev(const dsp_optics *o) {
     d.lam = o->wavelength_A;
     d.tau_y = o->tilt_rad[0];
     d.tau_x = o->tilt_rad[1];
+    d.pt2 = M_PI * o->depth_A / (2.0 * o->wavelength_A);
     chi_coefficients(o, d.chi_c);
     return d;
 }
@@ -1522,6 +1523,7 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
         HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, od, d_chi + b, MAX_SETS_DEV, stream));
         sp.tau_y[b] = od.tau_y;
         sp.tau_x[b] = od.tau_x;
+        sp.pt2[b] = od.pt2;
         std::memcpy(sp.chi_c[b], od.chi_c, sizeof od.chi_c);
     }
     sp.G = (const float2 *)G_c64_dev;

@@ -130,6 +130,7 @@ struct alignas(64) SsbTile {
 
 struct OpticsDev {
     double lam, tau_y, tau_x;
+    double pt2;      // pi t / (2 lambda), t the depth (0: no depth terms)
     double chi_c[CHI_NCOEF];
 };
 
@@ -193,6 +194,7 @@ struct SsbParams {
     ApertureDev ap;
     double lam;
     double tau_y[8], tau_x[8];
+    double pt2[8];           // pi t_b / (2 lambda) per set
     double chi_c[8][CHI_NCOEF];
     double2 *S_out;          // [B][N][nh] or null
     double *N_out;           // [B][N][nh] or null

@@ -223,6 +223,20 @@ struct GramWaves {
 typedef const PixelRec ConstPixel;
 typedef const long long ConstLong;
 
+// Depth term of a lobe (the weak object spread evenly through the depth t
+// below the plane chi refers to; "Where the 9 s of regularized preparation
+// goes", What changed 2: "chi, sinc and phase factor"): with
+// h = pi t (|theta_k|^2 - |theta'|^2) / (2 lambda) the lobe's phase argument
+// chi(k) - chi(k') gains h and its amplitude is multiplied by sinc(h).
+// sinc(h) = sin(h) / h, from its series below |h| = 1e-4 (error < 1e-28).
+__device__ __forceinline__ double sinc_tab(double h, const double2 *T) {
+    double sn, cs;
+    sincos_tab(h, T, sn, cs);
+    const double h2 = h * h;
+    const double series = fma(h2, fma(h2, 1.0 / 120.0, -1.0 / 6.0), 1.0);
+    return fabs(h) < 1e-4 ? series : sn / h;
+}
+
 // One lobe of the transfer at the pixel (chi0 = chi(k), amp0 = sqrt(w) a(k))
 // and the displaced point k' = k -/+ Q, given by theta' = lambda k' + tau and
 // d2 = |lambda k'|^2 (inside the support):
@@ -230,12 +244,20 @@ typedef const long long ConstLong;
 // a(k') = 1 except in the soft edge ring; the square root runs only when some
 // lane of the wave is in the ring (the empty asm keeps the compiler from
 // computing it unconditionally).
+// With DEPTH, th0 = |theta_k|^2 and the depth term (sinc_tab) is applied.
+template <bool DEPTH>
 __device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, double ty, double tx, double d2,
-                                     double chi0, double amp0, double sgn, double &re, double &im) {
+                                     double chi0, double amp0, double sgn, double th0, double &re, double &im) {
     const double c1 = chi_poly(prm.op.chi_c, tx, ty);
-    double sn, cs;
-    sincos_tab(sgn * (chi0 - c1), T, sn, cs);
+    double arg = chi0 - c1;
     double amp = amp0;
+    if (DEPTH) {
+        const double h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
+        arg += h;
+        amp *= sinc_tab(h, T);
+    }
+    double sn, cs;
+    sincos_tab(sgn * arg, T, sn, cs);
     const bool ring = d2 > prm.ap.lrin2;
     if (wave_any(ring)) {
         asm volatile("");
@@ -249,7 +271,7 @@ __device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, do
 // rank-one update of the augmented Gram.  A column's terms run when some
 // lane of the wave has it, a pair's when some lane has both (the other lanes
 // add exact zeros).
-template <int NJ, int METHOD>
+template <int NJ, int METHOD, bool DEPTH>
 __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 *T,
                                            double (&acc)[GramShape<NJ, METHOD>::NACC], double2 *lpair, int yh, int ix,
                                            const int (&jyN)[NJ], const int (&jxN)[NJ], const bool (&act)[NJ],
@@ -260,6 +282,7 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
     const double tau_y = prm.op.tau_y, tau_x = prm.op.tau_x;
     const double lk2 = fma(lky, lky, lkx * lkx);
     const double py = lky + tau_y, px = lkx + tau_x;
+    const double th0 = DEPTH ? fma(px, px, py * py) : 0.0;   // |theta_k|^2 for the depth term
 
     const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
     acc[NC] = fma(gr, gr, fma(gi, gi, acc[NC]));   // signal power w |g|^2
@@ -277,8 +300,8 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
         const bool zl = act[s] && dm2 < lrlim2;
         const bool zr = act[s] && dp2 < lrlim2;
         double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
-        if (zl) lobe(prm, T, py - Qy_s, px - Qx_s, dm2, chi0, amp0, 1.0, Lr, Li);
-        if (zr) lobe(prm, T, py + Qy_s, px + Qx_s, dp2, chi0, amp0, -1.0, Rr, Ri);
+        if (zl) lobe<DEPTH>(prm, T, py - Qy_s, px - Qx_s, dm2, chi0, amp0, 1.0, th0, Lr, Li);
+        if (zr) lobe<DEPTH>(prm, T, py + Qy_s, px + Qx_s, dp2, chi0, amp0, -1.0, th0, Rr, Ri);
         if (METHOD == 0) {
             tr[s] = Ri - Li;   // T_phi = i (L - R)
             ti[s] = Lr - Rr;
@@ -324,7 +347,7 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
 // Lane = frequency of the tile; pixel records are wave-uniform.
 // While pixel p is used, G for p + 1 is in flight (its plane offset was read
 // one pixel earlier) and the record of p + 1 and the offset of p + 2 load.
-template <int NJ, int METHOD>
+template <int NJ, int METHOD, bool DEPTH>
 __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kernel(GramParams prm) {
     using Sh = GramShape<NJ, METHOD>;
     constexpr int NC = Sh::NC;
@@ -409,7 +432,7 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
                 for (int k = 0; k < PF; ++k) {
                     const int r = r0 + k;
                     const float2 gv = r < cn ? ga[k] : make_float2(0.0f, 0.0f);
-                    gram_pixel<NJ, METHOD>(prm, T, acc, lpair, yh, ix, jyN, jxN, act, srec[r].lky, srec[r].lkx,
+                    gram_pixel<NJ, METHOD, DEPTH>(prm, T, acc, lpair, yh, ix, jyN, jxN, act, srec[r].lky, srec[r].lkx,
                                            srec[r].amp0, srec[r].sw, srec[r].chi0, gv);
                 }
 #pragma unroll
@@ -953,7 +976,7 @@ struct SsbWaves {
 // The support, a(k -/+ q), G and the weight are shared by the sets; chi and
 // its phase factor are per set.  Partial layout: [3b] Re S_b, [3b+1] Im S_b,
 // [3b+2] N_b, [3 MAXB] P.
-template <int MAXB>
+template <int MAXB, bool DEPTH>
 __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbParams prm) {
     constexpr int NACC = 3 * MAXB + 1;
     __shared__ double2 T[TRIG_N];
@@ -1028,20 +1051,35 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                 const double *cb = &prm.chi_c[b][zb];
                 // theta(k) = lambda k + tau_b exactly as chi0 was formed, then -/+ lambda q
                 const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
+                const double th0 = DEPTH ? fma(px, px, py * py) : 0.0;
                 double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
                 if (zl) {
-                    const double c1 = chi_poly(cb, px - qx, py - qy);
+                    const double ty = py - qy, tx = px - qx;
+                    const double c1 = chi_poly(cb, tx, ty);
+                    double arg = chi0 - c1, a = aml;
+                    if (DEPTH) {   // depth term: phase + h, amplitude sinc(h)
+                        const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
+                        arg += h;
+                        a *= sinc_tab(h, T);
+                    }
                     double sn, cs;
-                    sincos_tab(chi0 - c1, T, sn, cs);
-                    Lr = aml * cs;
-                    Li = aml * sn;
+                    sincos_tab(arg, T, sn, cs);
+                    Lr = a * cs;
+                    Li = a * sn;
                 }
                 if (zr) {
-                    const double c1 = chi_poly(cb, px + qx, py + qy);
+                    const double ty = py + qy, tx = px + qx;
+                    const double c1 = chi_poly(cb, tx, ty);
+                    double arg = chi0 - c1, a = amr;
+                    if (DEPTH) {
+                        const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
+                        arg += h;
+                        a *= sinc_tab(h, T);
+                    }
                     double sn, cs;
-                    sincos_tab(c1 - chi0, T, sn, cs);
-                    Rr = amr * cs;
-                    Ri = amr * sn;
+                    sincos_tab(-arg, T, sn, cs);
+                    Rr = a * cs;
+                    Ri = a * sn;
                 }
                 // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
                 const double gmr = Ri - Li, gmi = Lr - Rr;
@@ -1168,7 +1206,8 @@ static hipError_t gram_dispatch(int nj, int method, Args &&...args) {
 template <int NJ, int METHOD>
 struct GramLaunch {
     static hipError_t run(const GramParams &prm, int n_waves, hipStream_t st) {
-        gram_kernel<NJ, METHOD><<<n_waves, 64, 0, st>>>(prm);
+        if (prm.op.pt2 != 0.0) gram_kernel<NJ, METHOD, true><<<n_waves, 64, 0, st>>>(prm);
+        else gram_kernel<NJ, METHOD, false><<<n_waves, 64, 0, st>>>(prm);
         DSP_CHECK_LAUNCH();
         return hipSuccess;
     }
@@ -1189,7 +1228,7 @@ struct GramFixupLaunch {
 template <int NJ, int METHOD>
 struct GramOccupancy {
     static hipError_t run(int *blocks_per_cu) {
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, gram_kernel<NJ, METHOD>, 64, 0);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, gram_kernel<NJ, METHOD, false>, 64, 0);
     }
 };
 
@@ -1314,10 +1353,10 @@ int ssb_nacc(int maxb) { return 3 * maxb + 1; }
 
 hipError_t ssb_occupancy(int maxb, int *blocks_per_cu) {
     switch (maxb) {
-        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1>, 64, 0);
-        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2>, 64, 0);
-        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4>, 64, 0);
-        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8>, 64, 0);
+        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1, false>, 64, 0);
+        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2, false>, 64, 0);
+        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4, false>, 64, 0);
+        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8, false>, 64, 0);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1326,11 +1365,13 @@ hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *ti
     if (n_waves <= 0 || n_tiles <= 0) return hipSuccess;
     const int maxb = ssb_maxb(prm.B);
     const int nacc = ssb_nacc(maxb);
+    bool depth = false;   // depth terms when any set has a depth
+    for (int b = 0; b < prm.B; ++b) depth = depth || prm.pt2[b] != 0.0;
     switch (maxb) {
-        case 1: ssb_kernel<1><<<n_waves, 64, 0, st>>>(prm); break;
-        case 2: ssb_kernel<2><<<n_waves, 64, 0, st>>>(prm); break;
-        case 4: ssb_kernel<4><<<n_waves, 64, 0, st>>>(prm); break;
-        default: ssb_kernel<8><<<n_waves, 64, 0, st>>>(prm); break;
+        case 1: if (depth) ssb_kernel<1, true><<<n_waves, 64, 0, st>>>(prm); else ssb_kernel<1, false><<<n_waves, 64, 0, st>>>(prm); break;
+        case 2: if (depth) ssb_kernel<2, true><<<n_waves, 64, 0, st>>>(prm); else ssb_kernel<2, false><<<n_waves, 64, 0, st>>>(prm); break;
+        case 4: if (depth) ssb_kernel<4, true><<<n_waves, 64, 0, st>>>(prm); else ssb_kernel<4, false><<<n_waves, 64, 0, st>>>(prm); break;
+        default: if (depth) ssb_kernel<8, true><<<n_waves, 64, 0, st>>>(prm); else ssb_kernel<8, false><<<n_waves, 64, 0, st>>>(prm); break;
     }
     DSP_CHECK_LAUNCH();
     // reduce each tile's segments (same reduction as the Gram fixup)

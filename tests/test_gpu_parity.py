@@ -7,6 +7,7 @@ solutions and SSB sums <= 1e-5 globally (||delta|| / ||ref||) and per frequency
 (max|delta| / max(max|x_q|, 1e-3 global max)); agreement <= 1e-6 relative;
 index sets bit-exact; repeated runs bitwise equal.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -331,6 +332,43 @@ def test_phase_derived_c2_sampled():
                      smoothness=w.smoothness)
     pd = pc.derive_phase()
     check_prepared(pd, w, G_dev, k, None, "phase", [1e-3, 1e-1], sel=[7, 8063], per_count=300, seed=11)
+
+
+# ----------------------------------------------------------------------------
+# depth terms (thick sample)
+# ----------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("method", ["phase", "complex"])
+@pytest.mark.parametrize("soft", [True, False])
+def test_tiny_depth_full(method, soft):
+    """Depth 80 A with tilt on the ragged tiny scan, every frequency."""
+    w = _tiny(soft=soft, method=method)
+    w = dataclasses.replace(w, optics=w.optics.replace(depth=80.0))
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    strengths = [1e-3, 0.05] if method == "phase" else [(1e-3, 2e-3), (0.05, 0.01)]
+    run_prepare_case(w, G_dev, k, random_weights(len(k), 2), method, strengths)
+
+
+def test_c2_depth_complex_sampled():
+    w = workload("c2")
+    w = dataclasses.replace(w, optics=w.optics.replace(depth=124.0, tilt=(1e-3, -2e-3)))
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    run_prepare_case(w, G_dev, k, None, "complex", [(1e-3, 1e-3), (0.1, 0.02)], sel=[1, 8000], per_count=200,
+                     seed=21)
+
+
+def test_ssb_depth_per_set():
+    """Sets with different depths (and one without) in one pass."""
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    sets = [w.optics.replace(depth=136.0), w.optics, w.optics.replace(depth=40.0, tilt=(1e-3, 2e-3))]
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G_dev, k, None, sets, None)
+    power = np.array([np.sum(wa * np.abs(c) ** 2) for c in cols])
+    assert np.allclose(E, O.agreement(S_o, N_o, power), rtol=1e-6, atol=0)
 
 
 def test_frequencies_without_aliases():

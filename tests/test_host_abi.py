@@ -120,7 +120,10 @@ def test_validation_status_codes():
     assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(oc), 5, None, None, None) == _lib.DSP_EUNSUPPORTED
     assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(oc), 0, None, None, None) == _lib.DSP_EINVAL
     deep = dsp._optics(w.optics.replace(depth=124.0))
-    assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(deep), 2, None, None, None) == _lib.DSP_EUNSUPPORTED
+    assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(deep), 2, None, None, None) == _lib.DSP_OK
+    for bad_depth in (-1.0, float("nan"), float("inf")):
+        o = dsp._optics(w.optics.replace(depth=bad_depth))
+        assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(o), 2, None, None, None) == _lib.DSP_EINVAL
     bad_ab = dsp._optics(w.optics.replace(aberrations=[(1, 1, 10.0, 0.0)]))
     assert L.dsp_geometry_counts(ctypes.byref(good), ctypes.byref(bad_ab), 2, None, None, None) == _lib.DSP_EINVAL
     assert "Krivanek" in L.dsp_last_error().decode()
