@@ -979,10 +979,13 @@ struct SsbWaves {
 template <int MAXB, bool DEPTH>
 __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbParams prm) {
     constexpr int NACC = 3 * MAXB + 1;
+    constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
     __shared__ double2 T[TRIG_N];
+    __shared__ PixelRec srec[GRAM_CHUNK];
+    __shared__ long long sgoff[GRAM_CHUNK + PF];
+    __shared__ double schi[MAXB * GRAM_CHUNK];   // [set][pixel of the chunk] chi(k)
     const int lane = threadIdx.x;
     T[lane] = prm.trig[lane];
-    __syncthreads();
 
     const int wv = blockIdx.x;
     const long long n_pix = prm.n_pix;
@@ -993,8 +996,6 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
     ConstLong *goffs = (ConstLong *)prm.goff;
     const double *__restrict__ chi_tab = prm.chi_tab;
     const float2 *__restrict__ G = prm.G;
-    const double lrlim2 = prm.ap.lrlim2, lrin2 = prm.ap.lrin2, lkc = prm.ap.lkc, inv_ldk = prm.ap.inv_ldk;
-    const int B = prm.B;
 
     while (it < end) {
         const int t = (int)(it / n_pix);
@@ -1013,86 +1014,108 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
 #pragma unroll
         for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
 
-        double lky = pix[p0].lky, lkx = pix[p0].lkx, amp0 = pix[p0].amp0, sw = pix[p0].sw;
-        float2 gv = G[goffs[p0] + lane_off];
-        long long goff1 = goffs[p0 + 1 < p1 ? p0 + 1 : p0];
-        for (int p = p0; p < p1; ++p) {
-            const int pn = p + 1 < p1 ? p + 1 : p;
-            const int pnn = pn + 1 < p1 ? pn + 1 : pn;
-            const float2 ngv = G[goff1 + lane_off];
-            const long long goff2 = goffs[pnn];
-            const double nlky = pix[pn].lky, nlkx = pix[pn].lkx, namp0 = pix[pn].amp0, nsw = pix[pn].sw;
-            const double lk2 = fma(lky, lky, lkx * lkx);
-
-            const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
-            acc[NACC - 1] = fma(gr, gr, fma(gi, gi, acc[NACC - 1]));
-            const double kq = fma(lky, qy, lkx * qx);
-            const double base = lk2 + q2;
-            const double dm2 = fma(-2.0, kq, base), dp2 = fma(2.0, kq, base);
-            const bool zl = valid && dm2 < lrlim2;
-            const bool zr = valid && dp2 < lrlim2;
-            double aml = amp0, amr = amp0;
-            const bool rl = zl && dm2 > lrin2, rr = zr && dp2 > lrin2;
-            if (wave_any(rl || rr)) {
-                asm volatile("");
-                if (rl) aml *= fma(lkc - sqrt(dm2), inv_ldk, 0.5);
-                if (rr) amr *= fma(lkc - sqrt(dp2), inv_ldk, 0.5);
+        // records, plane offsets and the sets' chi(k) staged in LDS per chunk;
+        // G a group of PF pixels ahead; the chunk's tail runs on zero records
+        float2 ga[PF];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) ga[i] = G[goffs[p0 + i < p1 ? p0 + i : p1 - 1] + lane_off];
+        for (int c0 = p0; c0 < p1; c0 += GRAM_CHUNK) {
+            const int cn = (p1 - c0) < GRAM_CHUNK ? (p1 - c0) : GRAM_CHUNK;
+            __syncthreads();
+            if (lane < cn) {
+                srec[lane] = pix[c0 + lane];
+            } else {
+                PixelRec z;
+                z.lky = z.lkx = z.amp0 = z.sw = z.chi0 = z.pad = 0.0;
+                srec[lane] = z;
             }
 #pragma unroll
-            for (int b = 0; b < MAXB; ++b) {
-                if (b >= B) break;
-                const double chi0 = chi_tab[(size_t)p * MAX_SETS_DEV + b];
-                // The set's coefficients are read from the kernel arguments
-                // per use (scalar loads, constant cache): an opaque zero
-                // offset keeps the compiler from hoisting all sets' values
-                // into scalar registers, which would spill.
-                int zb = 0;
-                if (MAXB > 1) asm volatile("" : "+s"(zb));
-                const double *cb = &prm.chi_c[b][zb];
-                // theta(k) = lambda k + tau_b exactly as chi0 was formed, then -/+ lambda q
-                const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
-                const double th0 = DEPTH ? fma(px, px, py * py) : 0.0;
-                double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
-                if (zl) {
-                    const double ty = py - qy, tx = px - qx;
-                    const double c1 = chi_poly(cb, tx, ty);
-                    double arg = chi0 - c1, a = aml;
-                    if (DEPTH) {   // depth term: phase + h, amplitude sinc(h)
-                        const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
-                        arg += h;
-                        a *= sinc_tab(h, T);
+            for (int b = 0; b < MAXB; ++b)
+                schi[b * GRAM_CHUNK + lane] = (lane < cn && b < prm.B) ? chi_tab[(size_t)(c0 + lane) * MAX_SETS_DEV + b] : 0.0;
+            for (int i = lane; i < GRAM_CHUNK + PF; i += 64) sgoff[i] = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
+            __syncthreads();
+            for (int r0 = 0; r0 < cn; r0 += PF) {
+                float2 gb[PF];
+#pragma unroll
+                for (int k = 0; k < PF; ++k) gb[k] = G[sgoff[r0 + PF + k] + lane_off];
+#pragma unroll
+                for (int k = 0; k < PF; ++k) {
+                    const int r = r0 + k;
+                    const float2 gv = r < cn ? ga[k] : make_float2(0.0f, 0.0f);
+                    const double lky = srec[r].lky, lkx = srec[r].lkx, amp0 = srec[r].amp0, sw = srec[r].sw;
+                    const double *chi0s = schi + r;
+                    // one pixel's update (kept in the kernel body: the sets' chi
+                    // coefficients are read straight from the kernel arguments)
+                    const double lrlim2 = prm.ap.lrlim2, lrin2 = prm.ap.lrin2, lkc = prm.ap.lkc, inv_ldk = prm.ap.inv_ldk;
+                    const int B = prm.B;
+                    const double lk2 = fma(lky, lky, lkx * lkx);
+                    const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
+                    acc[NACC - 1] = fma(gr, gr, fma(gi, gi, acc[NACC - 1]));
+                    const double kq = fma(lky, qy, lkx * qx);
+                    const double base = lk2 + q2;
+                    const double dm2 = fma(-2.0, kq, base), dp2 = fma(2.0, kq, base);
+                    const bool zl = valid && dm2 < lrlim2;
+                    const bool zr = valid && dp2 < lrlim2;
+                    double aml = amp0, amr = amp0;
+                    const bool rl = zl && dm2 > lrin2, rr = zr && dp2 > lrin2;
+                    if (wave_any(rl || rr)) {
+                        asm volatile("");
+                        if (rl) aml *= fma(lkc - sqrt(dm2), inv_ldk, 0.5);
+                        if (rr) amr *= fma(lkc - sqrt(dp2), inv_ldk, 0.5);
                     }
-                    double sn, cs;
-                    sincos_tab(arg, T, sn, cs);
-                    Lr = a * cs;
-                    Li = a * sn;
-                }
-                if (zr) {
-                    const double ty = py + qy, tx = px + qx;
-                    const double c1 = chi_poly(cb, tx, ty);
-                    double arg = chi0 - c1, a = amr;
-                    if (DEPTH) {
-                        const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
-                        arg += h;
-                        a *= sinc_tab(h, T);
+                #pragma unroll
+                    for (int b = 0; b < MAXB; ++b) {
+                        if (b >= B) continue;   // uniform; keeps the loop fully unrolled
+                        const double chi0 = chi0s[b * GRAM_CHUNK];   // this pixel's chi(k) of set b (LDS)
+                        // The set's coefficients are read from the kernel arguments
+                        // per use (scalar loads, constant cache): an opaque zero
+                        // offset keeps the compiler from hoisting all sets' values
+                        // into scalar registers, which would spill.
+                        int zb = 0;
+                        if (MAXB > 1) asm volatile("" : "+s"(zb));
+                        const double *cb = &prm.chi_c[b][zb];
+                        // theta(k) = lambda k + tau_b exactly as chi0 was formed, then -/+ lambda q
+                        const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
+                        const double th0 = DEPTH ? fma(px, px, py * py) : 0.0;
+                        double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
+                        if (zl) {
+                            const double ty = py - qy, tx = px - qx;
+                            const double c1 = chi_poly(cb, tx, ty);
+                            double arg = chi0 - c1, a = aml;
+                            if (DEPTH) {   // depth term: phase + h, amplitude sinc(h)
+                                const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
+                                arg += h;
+                                a *= sinc_tab(h, T);
+                            }
+                            double sn, cs;
+                            sincos_tab(arg, T, sn, cs);
+                            Lr = a * cs;
+                            Li = a * sn;
+                        }
+                        if (zr) {
+                            const double ty = py + qy, tx = px + qx;
+                            const double c1 = chi_poly(cb, tx, ty);
+                            double arg = chi0 - c1, a = amr;
+                            if (DEPTH) {
+                                const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
+                                arg += h;
+                                a *= sinc_tab(h, T);
+                            }
+                            double sn, cs;
+                            sincos_tab(-arg, T, sn, cs);
+                            Rr = a * cs;
+                            Ri = a * sn;
+                        }
+                        // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
+                        const double gmr = Ri - Li, gmi = Lr - Rr;
+                        acc[3 * b] = fma(gmr, gr, fma(gmi, gi, acc[3 * b]));
+                        acc[3 * b + 1] = fma(gmr, gi, fma(-gmi, gr, acc[3 * b + 1]));
+                        acc[3 * b + 2] = fma(gmr, gmr, fma(gmi, gmi, acc[3 * b + 2]));
                     }
-                    double sn, cs;
-                    sincos_tab(-arg, T, sn, cs);
-                    Rr = a * cs;
-                    Ri = a * sn;
                 }
-                // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
-                const double gmr = Ri - Li, gmi = Lr - Rr;
-                acc[3 * b] = fma(gmr, gr, fma(gmi, gi, acc[3 * b]));
-                acc[3 * b + 1] = fma(gmr, gi, fma(-gmi, gr, acc[3 * b + 1]));
-                acc[3 * b + 2] = fma(gmr, gmr, fma(gmi, gmi, acc[3 * b + 2]));
+#pragma unroll
+                for (int k = 0; k < PF; ++k) ga[k] = gb[k];
             }
-            lky = nlky;
-            lkx = nlkx;
-            amp0 = namp0;
-            sw = nsw;
-            gv = ngv;
-            goff1 = goff2;
         }
         double *po = prm.partial + (size_t)seg * (NACC * 64);
 #pragma unroll
