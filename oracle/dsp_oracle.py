@@ -483,6 +483,56 @@ def agreement(S: np.ndarray, Nn: np.ndarray, power: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# compact G: Hermitian half plane as snorm16 pairs with one scale per pixel
+# ----------------------------------------------------------------------------
+
+HERM16_ONE = 32767
+
+
+def herm16_scale(G: np.ndarray) -> np.ndarray:
+    """One float32 scale per bright-field pixel: the largest |G(q, k)| over
+    its stored half plane ([P4] compact preview: "per-BF-pixel max |G| over
+    the half-plane").  |G|^2 = re^2 + im^2 is formed in float64 from the
+    complex64 components (exact squares, one rounding for the sum), the root
+    in float64 and the result rounded to float32."""
+    G = np.asarray(G)
+    re = G.real.astype(np.float64)
+    im = G.imag.astype(np.float64)
+    m = (re * re + im * im).reshape(G.shape[0], -1).max(axis=1)
+    return np.sqrt(m).astype(np.float32)
+
+
+def herm16_quantize(G: np.ndarray):
+    """([P4] compact preview: pack2x16snorm(clamp(v / scale))) Each component
+    v of G(q, k) becomes the int16 floor(0.5 + 32767 clamp(v / s_k, -1, 1)),
+    the division and the product in float64, each rounded once; all zero
+    where s_k = 0.  Returns (Q int16 (n_bf, N, N/2+1, 2), scale float32 (n_bf,))."""
+    G = np.asarray(G)
+    s = herm16_scale(G)
+    sd = s.astype(np.float64).reshape((-1,) + (1,) * (G.ndim - 1))
+    Q = np.zeros(G.shape + (2,), dtype=np.int16)
+    nz = s > 0
+    for c, part in enumerate((G.real, G.imag)):
+        v = part.astype(np.float64)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            x = np.clip(v / sd, -1.0, 1.0)
+        q = np.floor(0.5 + HERM16_ONE * x)
+        q[~nz] = 0.0
+        Q[..., c] = q.astype(np.int16)
+    return Q, s
+
+
+def herm16_dequantize(Q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """G ~ max(q * (1/32767), -1) * s_k per component, in float64 ([P4]
+    compact preview: unpack2x16snorm(word) * scale); returns complex128."""
+    r = 1.0 / HERM16_ONE
+    sd = np.asarray(scale, dtype=np.float32).astype(np.float64).reshape((-1,) + (1,) * (Q.ndim - 2))
+    re = np.maximum(Q[..., 0].astype(np.float64) * r, -1.0) * sd
+    im = np.maximum(Q[..., 1].astype(np.float64) * r, -1.0) * sd
+    return re + 1j * im
+
+
+# ----------------------------------------------------------------------------
 # convenience: whole small problems
 # ----------------------------------------------------------------------------
 

@@ -338,6 +338,39 @@ def test_depth_transfer_matches_multislice(monkeypatch):
     assert r_bad > 0.1
 
 
+# ----------------------------------------------------------------------------
+# compact G (herm16)
+# ----------------------------------------------------------------------------
+
+
+def test_herm16_error_bound_and_exact_values():
+    """Each dequantized component is within half a quantization step of the
+    original (round to nearest; truncation would reach a full step), values
+    on the grid round-trip exactly, the scale is the plane's largest |G|, and
+    an all-zero plane stays zero."""
+    rng = np.random.default_rng(3)
+    G = (rng.standard_normal((5, 8, 5)) + 1j * rng.standard_normal((5, 8, 5))).astype(np.complex64)
+    G[1] *= 1e-6                       # pixels of very different magnitude
+    G[3] = 0
+    Q, s = O.herm16_quantize(G)
+    assert Q.dtype == np.int16 and s.dtype == np.float32
+    mag = np.abs(G.astype(np.complex128)).reshape(5, -1).max(axis=1)
+    assert np.allclose(s, mag, rtol=1e-7, atol=0)
+    assert not np.any(Q[3]) and s[3] == 0
+    D = O.herm16_dequantize(Q, s)
+    step = s.astype(np.float64)[:, None, None] / 32767.0
+    assert np.all(np.abs(D.real - G.real) <= 0.5 * step * (1 + 1e-9) + 1e-300)
+    assert np.all(np.abs(D.imag - G.imag) <= 0.5 * step * (1 + 1e-9) + 1e-300)
+    # the largest component of each pixel maps to +-32767 (the scale is |G|,
+    # so only a purely real or imaginary maximum reaches the end points)
+    assert np.abs(Q).max() <= 32767
+    grid = np.zeros((1, 2, 2), dtype=np.complex64)
+    grid[0, 0, 0] = 1.0
+    grid[0, 1, 1] = -0.5 + 0.25j
+    Qg, sg = O.herm16_quantize(grid)
+    assert sg[0] == 1.0 and Qg[0, 0, 0, 0] == 32767 and Qg[0, 1, 1, 0] == -16383 and Qg[0, 1, 1, 1] == 8192
+
+
 def test_first_order_model_equals_transfer_sum():
     """The physics-form first-order data (written from A(k)) equals
     sum_Q T x over the oracle's aliases."""
