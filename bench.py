@@ -242,26 +242,39 @@ def ssb_sweep(dsp, dev, reps: int = 5):
     out = {"workload": f"512x512 scan, {len(k)} BF px, band {w.band[0]}-{w.band[1]} 1/A ({n_band} stored q)",
            "g_bytes_per_pass": g_bytes, "passes": {}}
     stream = torch.cuda.current_stream()
-    # the pages' thick-sample fit batch: the same sets at depth 136 A
-    runs = [(B, 0.0) for B in (1, 2, 4, 8)] + [(1, 136.0), (8, 136.0)]
-    for B, depth in runs:
-        sets = [o.replace(depth=depth) for o in ssb_sets(w, B)]
-        dsp.ssb(G, k, sets, step=w.step, band=w.band, agreement=False)
+    def timed(fn):
+        fn()
         ms = []
         for _ in range(reps):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            dsp.ssb(G, k, sets, step=w.step, band=w.band, agreement=False)
+            fn()
             e1.record(stream)
             e1.synchronize()
             ms.append(e0.elapsed_time(e1))
-        m = float(np.median(ms))
-        name = str(B) if depth == 0.0 else f"{B} depth {depth:g} A"
-        out["passes"][name] = {"ms": m, "q_sets_per_s": n_band * B / (m / 1e3),
-                               "g_GBps": g_bytes / (m / 1e3) / 1e9}
-        log(f"ssb B={B} depth {depth:g} A: {m:.3f} ms")
-    del G
+        return float(np.median(ms))
+
+    # herm16 compact copy of the same stack (half the bytes per entry)
+    h16 = dsp.quantize_herm16(G)
+    out["herm16_quantize_ms"] = timed(lambda: dsp.quantize_herm16(G))
+    out["herm16_bytes"] = int(h16[0].numel() * 2 + h16[1].numel() * 4)
+    out["complex64_bytes"] = int(G.numel() * 8)
+    log(f"herm16 quantize: {out['herm16_quantize_ms']:.3f} ms")
+    # the pages' thick-sample fit batch: the same sets at depth 136 A
+    runs = [(B, 0.0, False) for B in (1, 2, 4, 8)] + [(1, 136.0, False), (8, 136.0, False), (1, 0.0, True),
+                                                       (8, 0.0, True)]
+    for B, depth, packed in runs:
+        sets = [o.replace(depth=depth) for o in ssb_sets(w, B)]
+        if packed:
+            m = timed(lambda: dsp.ssb(None, k, sets, step=w.step, band=w.band, agreement=False, herm16=h16))
+        else:
+            m = timed(lambda: dsp.ssb(G, k, sets, step=w.step, band=w.band, agreement=False))
+        name = str(B) + ("" if depth == 0.0 else f" depth {depth:g} A") + (" herm16" if packed else "")
+        gb = g_bytes / 2 if packed else g_bytes
+        out["passes"][name] = {"ms": m, "q_sets_per_s": n_band * B / (m / 1e3), "g_GBps": gb / (m / 1e3) / 1e9}
+        log(f"ssb B={name}: {m:.3f} ms")
+    del G, h16
     torch.cuda.empty_cache()
     return out
 

@@ -25,7 +25,7 @@ from . import _lib
 
 _L = _lib.load()
 
-__all__ = ["DspError", "Prepared", "prepare", "ssb", "geometry_counts", "alias_geometry", "active_bf",
+__all__ = ["DspError", "Prepared", "prepare", "ssb", "quantize_herm16", "geometry_counts", "alias_geometry", "active_bf",
            "band_count", "chi_host", "sincos_host", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -238,16 +238,50 @@ def prepare(G, bf_coords, optics, step: float, upsampling: int, method: str = "p
     return Prepared(h, G.device, method)
 
 
-def ssb(G, bf_coords, optics_sets: Sequence, step: float, band: Optional[Tuple[float, float]] = None,
-        weights=None, want_S: bool = True, want_N: bool = True, agreement: bool = True, stream=None):
-    """SSB sums for up to 8 optics sets in one pass over G.
-
-    Returns (S (B, N, N/2+1) complex128 or None, N (B, N, N/2+1) float64 or
-    None, E (B,) numpy float64 or None)."""
+def quantize_herm16(G, stream=None):
+    """Compact herm16 copy of G (dsp_quantize_herm16): returns (Q int16
+    (n_bf, N, N/2+1, 2), scale float32 (n_bf,)), both on G's device."""
     torch = _torch()
     n = _check_G(G)
+    Q = torch.empty(tuple(G.shape) + (2,), dtype=torch.int16, device=G.device)
+    sc = torch.empty((G.shape[0],), dtype=torch.float32, device=G.device)
+    _check(_L.dsp_quantize_herm16(ctypes.c_void_p(G.data_ptr()), G.shape[0], n, ctypes.c_void_p(Q.data_ptr()),
+                                  ctypes.c_void_p(sc.data_ptr()), ctypes.c_void_p(_stream(stream))))
+    return Q, sc
+
+
+def _check_Q(Q, scale):
+    torch = _torch()
+    if not isinstance(Q, torch.Tensor) or not Q.is_cuda or Q.dtype != torch.int16 or Q.dim() != 4 \
+            or Q.shape[3] != 2 or not Q.is_contiguous():
+        raise DspError(_lib.DSP_EINVAL, "Q must be contiguous int16 (n_bf, N, N/2+1, 2) on the GPU")
+    n = Q.shape[1]
+    if Q.shape[2] != n // 2 + 1:
+        raise DspError(_lib.DSP_EINVAL, f"Q's third axis must be N/2+1 = {n // 2 + 1}")
+    if not isinstance(scale, torch.Tensor) or scale.dtype != torch.float32 or scale.device != Q.device \
+            or scale.shape != (Q.shape[0],) or not scale.is_contiguous():
+        raise DspError(_lib.DSP_EINVAL, "scale must be contiguous float32 (n_bf,) on Q's device")
+    return n
+
+
+def ssb(G, bf_coords, optics_sets: Sequence, step: float, band: Optional[Tuple[float, float]] = None,
+        weights=None, want_S: bool = True, want_N: bool = True, agreement: bool = True, stream=None,
+        herm16=None):
+    """SSB sums for up to 8 optics sets in one pass over G.
+
+    ``herm16=(Q, scale)`` from quantize_herm16 runs the pass over the compact
+    copy instead (G may then be None).  Returns (S (B, N, N/2+1) complex128
+    or None, N (B, N, N/2+1) float64 or None, E (B,) numpy float64 or None)."""
+    torch = _torch()
+    if herm16 is not None:
+        Q, sc = herm16
+        n = _check_Q(Q, sc)
+        n_rows, device = Q.shape[0], Q.device
+    else:
+        n = _check_G(G)
+        n_rows, device = G.shape[0], G.device
     k = _coords(bf_coords)
-    if k.shape[0] != G.shape[0]:
+    if k.shape[0] != n_rows:
         raise DspError(_lib.DSP_EINVAL, "bf_coords rows must match G's first axis")
     w = _weights(weights, k.shape[0])
     B = len(optics_sets)
@@ -256,14 +290,19 @@ def ssb(G, bf_coords, optics_sets: Sequence, step: float, band: Optional[Tuple[f
         arr[i] = _optics(o)
     scan = _lib.ScanC(n, float(step))
     nh = n // 2 + 1
-    S = torch.empty((B, n, nh), dtype=torch.complex128, device=G.device) if want_S else None
-    Nn = torch.empty((B, n, nh), dtype=torch.float64, device=G.device) if want_N else None
+    S = torch.empty((B, n, nh), dtype=torch.complex128, device=device) if want_S else None
+    Nn = torch.empty((B, n, nh), dtype=torch.float64, device=device) if want_N else None
     E = np.zeros(max(1, B), dtype=np.float64) if agreement else None
     bd = np.asarray(band, dtype=np.float64) if band is not None else None
-    _check(_L.dsp_ssb(ctypes.c_void_p(G.data_ptr()), k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan), arr, B,
-                      _dptr(bd), ctypes.c_void_p(S.data_ptr()) if S is not None else None,
-                      ctypes.c_void_p(Nn.data_ptr()) if Nn is not None else None,
-                      _dptr(E) if E is not None else None, ctypes.c_void_p(_stream(stream))))
+    outs = (_dptr(bd), ctypes.c_void_p(S.data_ptr()) if S is not None else None,
+            ctypes.c_void_p(Nn.data_ptr()) if Nn is not None else None, _dptr(E) if E is not None else None,
+            ctypes.c_void_p(_stream(stream)))
+    if herm16 is not None:
+        _check(_L.dsp_ssb_herm16(ctypes.c_void_p(Q.data_ptr()), ctypes.c_void_p(sc.data_ptr()), k.shape[0], _dptr(k),
+                                 _dptr(w), ctypes.byref(scan), arr, B, *outs))
+    else:
+        _check(_L.dsp_ssb(ctypes.c_void_p(G.data_ptr()), k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan), arr, B,
+                          *outs))
     return S, Nn, (E[:B] if E is not None else None)
 
 

@@ -1437,9 +1437,13 @@ dsp_status dsp_alias_table(const dsp_handle *h, int32_t *q_host, int32_t *count_
     return DSP_OK;
 }
 
-dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
-                   const dsp_scan *scan, const dsp_optics *sets_host, int B, const double *band_invA,
-                   void *S_out_c128_dev, double *norm_out_dev, double *agreement_out_host, void *hip_stream) {
+}  // extern "C"
+
+// The SSB pass over complex64 G (GQ null) or herm16 G (GQ, gscale).
+static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const float *gscale_dev, int n_bf,
+                           const double *bf_coords_host, const double *weights_host, const dsp_scan *scan,
+                           const dsp_optics *sets_host, int B, const double *band_invA, void *S_out_c128_dev,
+                           double *norm_out_dev, double *agreement_out_host, void *hip_stream) {
     dsp_status st;
     if ((st = check_scan(scan))) return st;
     if (!sets_host || B < 1 || B > MAX_SETS) return fail(DSP_EINVAL, "need 1 <= B <= %d optics sets", MAX_SETS);
@@ -1451,7 +1455,7 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
             a.det_step_invA != c.det_step_invA || a.soft_aperture != c.soft_aperture)
             return fail(DSP_EINVAL, "set %d: aperture parameters differ from set 0", b);
     }
-    if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
+    if (!G_c64_dev && !(GQ_dev && gscale_dev)) return fail(DSP_EINVAL, "G is NULL");
     if (n_bf <= 0 || !bf_coords_host) return fail(DSP_EINVAL, "n_bf must be > 0 with bf_coords");
     if (band_invA && !(band_invA[0] <= band_invA[1])) return fail(DSP_EINVAL, "band must satisfy lo <= hi");
     for (int i = 0; i < 2 * n_bf; ++i)
@@ -1527,6 +1531,9 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
         std::memcpy(sp.chi_c[b], od.chi_c, sizeof od.chi_c);
     }
     sp.G = (const float2 *)G_c64_dev;
+    sp.GQ = (const short2 *)GQ_dev;
+    sp.gscale = gscale_dev;
+    sp.plane = (long long)plane;
     sp.pix = d_pix;
     sp.goff = L.d_goff;
     sp.chi_tab = d_chi;
@@ -1556,6 +1563,36 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
         HIP_TRY(hipStreamSynchronize(stream));
         for (int b = 0; b < B; ++b) agreement_out_host[b] = E[b];
     }
+    return DSP_OK;
+}
+
+extern "C" {
+
+dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
+                   const dsp_scan *scan, const dsp_optics *sets_host, int B, const double *band_invA,
+                   void *S_out_c128_dev, double *norm_out_dev, double *agreement_out_host, void *hip_stream) {
+    if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
+    return ssb_impl(G_c64_dev, nullptr, nullptr, n_bf, bf_coords_host, weights_host, scan, sets_host, B, band_invA,
+                    S_out_c128_dev, norm_out_dev, agreement_out_host, hip_stream);
+}
+
+dsp_status dsp_ssb_herm16(const void *Q_i16_dev, const float *scale_dev, int n_bf, const double *bf_coords_host,
+                          const double *weights_host, const dsp_scan *scan, const dsp_optics *sets_host, int B,
+                          const double *band_invA, void *S_out_c128_dev, double *norm_out_dev,
+                          double *agreement_out_host, void *hip_stream) {
+    if (!Q_i16_dev || !scale_dev) return fail(DSP_EINVAL, "Q and scale must be non-NULL");
+    return ssb_impl(nullptr, Q_i16_dev, scale_dev, n_bf, bf_coords_host, weights_host, scan, sets_host, B, band_invA,
+                    S_out_c128_dev, norm_out_dev, agreement_out_host, hip_stream);
+}
+
+dsp_status dsp_quantize_herm16(const void *G_c64_dev, int n_bf, int n_scan, void *Q_i16_dev, float *scale_dev,
+                               void *hip_stream) {
+    if (!G_c64_dev || !Q_i16_dev || !scale_dev) return fail(DSP_EINVAL, "G, Q and scale must be non-NULL");
+    if (n_bf <= 0) return fail(DSP_EINVAL, "n_bf must be > 0");
+    if (n_scan < 4 || (n_scan & 1)) return fail(DSP_EINVAL, "n_scan must be even and >= 4");
+    const long long plane = (long long)n_scan * (n_scan / 2 + 1);
+    HIP_TRY(launch_herm16((const float2 *)G_c64_dev, n_bf, plane, (short2 *)Q_i16_dev, scale_dev,
+                          (hipStream_t)hip_stream));
     return DSP_OK;
 }
 

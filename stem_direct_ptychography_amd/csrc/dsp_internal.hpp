@@ -181,7 +181,10 @@ constexpr int MAX_SETS_DEV = 8;   // optics sets of one SSB pass
 // SSB pass: stream-K over (band tile, pixel) like the Gram launches, with
 // partial sums [n_segments][3 MAXB + 1][64].
 struct SsbParams {
-    const float2 *G;
+    const float2 *G;         // complex64 G, or null with GQ
+    const short2 *GQ;        // herm16 G: snorm16 pairs, one scale per pixel
+    const float *gscale;     // [n_bf] herm16 scales, indexed by the pixel's plane
+    long long plane;         // N (N/2 + 1): plane offset -> pixel index
     const PixelRec *pix;
     const long long *goff;   // [n_pix]
     const double *chi_tab;   // [n_pix][MAX_SETS_DEV] chi(k) per set

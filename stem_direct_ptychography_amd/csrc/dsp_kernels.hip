@@ -22,6 +22,7 @@
 #include "dsp_kernels.hpp"
 
 #include <cstring>
+#include <type_traits>
 
 namespace dsp {
 
@@ -976,10 +977,13 @@ struct SsbWaves {
 // The support, a(k -/+ q), G and the weight are shared by the sets; chi and
 // its phase factor are per set.  Partial layout: [3b] Re S_b, [3b+1] Im S_b,
 // [3b+2] N_b, [3 MAXB] P.
-template <int MAXB, bool DEPTH>
+// H16: G comes as herm16 snorm16 pairs with one scale per pixel (staged with
+// the pixel record), unpacked as max(q / 32767, -1) s in FP64 at use.
+template <int MAXB, bool DEPTH, bool H16>
 __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbParams prm) {
     constexpr int NACC = 3 * MAXB + 1;
     constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
+    using GT = typename std::conditional<H16, short2, float2>::type;
     __shared__ double2 T[TRIG_N];
     __shared__ PixelRec srec[GRAM_CHUNK];
     __shared__ long long sgoff[GRAM_CHUNK + PF];
@@ -995,7 +999,7 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
     ConstPixel *pix = (ConstPixel *)prm.pix;
     ConstLong *goffs = (ConstLong *)prm.goff;
     const double *__restrict__ chi_tab = prm.chi_tab;
-    const float2 *__restrict__ G = prm.G;
+    const GT *__restrict__ G = H16 ? (const GT *)prm.GQ : (const GT *)prm.G;
 
     while (it < end) {
         const int t = (int)(it / n_pix);
@@ -1016,14 +1020,17 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
 
         // records, plane offsets and the sets' chi(k) staged in LDS per chunk;
         // G a group of PF pixels ahead; the chunk's tail runs on zero records
-        float2 ga[PF];
+        GT ga[PF];
 #pragma unroll
         for (int i = 0; i < PF; ++i) ga[i] = G[goffs[p0 + i < p1 ? p0 + i : p1 - 1] + lane_off];
         for (int c0 = p0; c0 < p1; c0 += GRAM_CHUNK) {
             const int cn = (p1 - c0) < GRAM_CHUNK ? (p1 - c0) : GRAM_CHUNK;
             __syncthreads();
             if (lane < cn) {
-                srec[lane] = pix[c0 + lane];
+                PixelRec rec = pix[c0 + lane];
+                // herm16: the pixel's scale rides in the record's spare field
+                if (H16) rec.pad = (double)prm.gscale[goffs[c0 + lane] / prm.plane];
+                srec[lane] = rec;
             } else {
                 PixelRec z;
                 z.lky = z.lkx = z.amp0 = z.sw = z.chi0 = z.pad = 0.0;
@@ -1035,21 +1042,30 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
             for (int i = lane; i < GRAM_CHUNK + PF; i += 64) sgoff[i] = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
             __syncthreads();
             for (int r0 = 0; r0 < cn; r0 += PF) {
-                float2 gb[PF];
+                GT gb[PF];
 #pragma unroll
                 for (int k = 0; k < PF; ++k) gb[k] = G[sgoff[r0 + PF + k] + lane_off];
 #pragma unroll
                 for (int k = 0; k < PF; ++k) {
                     const int r = r0 + k;
-                    const float2 gv = r < cn ? ga[k] : make_float2(0.0f, 0.0f);
                     const double lky = srec[r].lky, lkx = srec[r].lkx, amp0 = srec[r].amp0, sw = srec[r].sw;
+                    double gre, gim;   // G(q, k) in FP64
+                    if (H16) {
+                        const double sc = srec[r].pad;
+                        gre = fmax((double)ga[k].x * (1.0 / 32767.0), -1.0) * sc;
+                        gim = fmax((double)ga[k].y * (1.0 / 32767.0), -1.0) * sc;
+                    } else {
+                        gre = (double)ga[k].x;
+                        gim = (double)ga[k].y;
+                    }
+                    if (r >= cn) gre = gim = 0.0;
                     const double *chi0s = schi + r;
                     // one pixel's update (kept in the kernel body: the sets' chi
                     // coefficients are read straight from the kernel arguments)
                     const double lrlim2 = prm.ap.lrlim2, lrin2 = prm.ap.lrin2, lkc = prm.ap.lkc, inv_ldk = prm.ap.inv_ldk;
                     const int B = prm.B;
                     const double lk2 = fma(lky, lky, lkx * lkx);
-                    const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
+                    const double gr = gre * sw, gi = gim * sw;
                     acc[NACC - 1] = fma(gr, gr, fma(gi, gi, acc[NACC - 1]));
                     const double kq = fma(lky, qy, lkx * qx);
                     const double base = lk2 + q2;
@@ -1122,6 +1138,49 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
         for (int i = 0; i < NACC; ++i) po[i * 64 + lane] = acc[i];
         ++seg;
         it += p1 - p0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// herm16 compact G ("Historical WebGPU G(q,k) memory experiment", compact
+// preview): one scale per pixel, the largest |G| over its half plane, and
+// each component packed as floor(0.5 + 32767 clamp(v / s, -1, 1)).
+// ---------------------------------------------------------------------------
+
+// Block = one pixel's plane: |G|^2 as a rounded sum of rounded squares in
+// FP64, an exact max tree, the root rounded to float.
+__global__ __launch_bounds__(256) void herm16_scale_kernel(const float2 *G, long long plane, float *scale) {
+    __shared__ double red[256];
+    const float2 *Gp = G + (size_t)blockIdx.x * plane;
+    double m = 0.0;
+    for (long long e = threadIdx.x; e < plane; e += 256) {
+        const double re = Gp[e].x, im = Gp[e].y;
+        m = fmax(m, __dadd_rn(__dmul_rn(re, re), __dmul_rn(im, im)));
+    }
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) scale[blockIdx.x] = (float)sqrt(red[0]);
+}
+
+// grid-stride over the n_bf planes' entries
+__global__ __launch_bounds__(256) void herm16_pack_kernel(const float2 *G, long long plane, long long n,
+                                                          const float *scale, short2 *Q) {
+#pragma clang fp contract(off)
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const double s = scale[i / plane];
+        const float2 v = G[i];
+        short2 q = make_short2(0, 0);
+        if (s > 0.0) {
+            const double x = fmin(fmax((double)v.x / s, -1.0), 1.0), y = fmin(fmax((double)v.y / s, -1.0), 1.0);
+            q.x = (short)floor(0.5 + 32767.0 * x);
+            q.y = (short)floor(0.5 + 32767.0 * y);
+        }
+        Q[i] = q;
     }
 }
 
@@ -1376,12 +1435,34 @@ int ssb_nacc(int maxb) { return 3 * maxb + 1; }
 
 hipError_t ssb_occupancy(int maxb, int *blocks_per_cu) {
     switch (maxb) {
-        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1, false>, 64, 0);
-        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2, false>, 64, 0);
-        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4, false>, 64, 0);
-        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8, false>, 64, 0);
+        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1, false, false>, 64, 0);
+        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2, false, false>, 64, 0);
+        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4, false, false>, 64, 0);
+        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8, false, false>, 64, 0);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <int MAXB>
+static void ssb_dispatch(const SsbParams &prm, bool depth, bool h16, int n_waves, hipStream_t st) {
+    if (depth) {
+        if (h16) ssb_kernel<MAXB, true, true><<<n_waves, 64, 0, st>>>(prm);
+        else ssb_kernel<MAXB, true, false><<<n_waves, 64, 0, st>>>(prm);
+    } else {
+        if (h16) ssb_kernel<MAXB, false, true><<<n_waves, 64, 0, st>>>(prm);
+        else ssb_kernel<MAXB, false, false><<<n_waves, 64, 0, st>>>(prm);
+    }
+}
+
+hipError_t launch_herm16(const float2 *G, int n_bf, long long plane, short2 *Q, float *scale, hipStream_t st) {
+    if (n_bf <= 0 || plane <= 0) return hipSuccess;
+    herm16_scale_kernel<<<n_bf, 256, 0, st>>>(G, plane, scale);
+    DSP_CHECK_LAUNCH();
+    const long long n = (long long)n_bf * plane;
+    const long long blocks = (n + 255) / 256;
+    herm16_pack_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, st>>>(G, plane, n, scale, Q);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
 }
 
 hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *tile_part, hipStream_t st) {
@@ -1390,11 +1471,12 @@ hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *ti
     const int nacc = ssb_nacc(maxb);
     bool depth = false;   // depth terms when any set has a depth
     for (int b = 0; b < prm.B; ++b) depth = depth || prm.pt2[b] != 0.0;
+    const bool h16 = prm.GQ != nullptr;
     switch (maxb) {
-        case 1: if (depth) ssb_kernel<1, true><<<n_waves, 64, 0, st>>>(prm); else ssb_kernel<1, false><<<n_waves, 64, 0, st>>>(prm); break;
-        case 2: if (depth) ssb_kernel<2, true><<<n_waves, 64, 0, st>>>(prm); else ssb_kernel<2, false><<<n_waves, 64, 0, st>>>(prm); break;
-        case 4: if (depth) ssb_kernel<4, true><<<n_waves, 64, 0, st>>>(prm); else ssb_kernel<4, false><<<n_waves, 64, 0, st>>>(prm); break;
-        default: if (depth) ssb_kernel<8, true><<<n_waves, 64, 0, st>>>(prm); else ssb_kernel<8, false><<<n_waves, 64, 0, st>>>(prm); break;
+        case 1: ssb_dispatch<1>(prm, depth, h16, n_waves, st); break;
+        case 2: ssb_dispatch<2>(prm, depth, h16, n_waves, st); break;
+        case 4: ssb_dispatch<4>(prm, depth, h16, n_waves, st); break;
+        default: ssb_dispatch<8>(prm, depth, h16, n_waves, st); break;
     }
     DSP_CHECK_LAUNCH();
     // reduce each tile's segments (same reduction as the Gram fixup)

@@ -424,9 +424,12 @@ def test_determinism_bitwise():
 # ----------------------------------------------------------------------------
 
 
-def _ssb_case(w, G_dev, k, wts, sets, band, entries=None):
-    _say(f"ssb {w.name} B={len(sets)} band={band} n_bf={len(k)}")
-    S, Nn, E = dsp.ssb(G_dev, k, sets, step=w.step, band=band, weights=wts)
+def _ssb_case(w, G_dev, k, wts, sets, band, entries=None, h16=None):
+    """SSB through the library against the oracle on the same entries.  With
+    h16 = (Q, scale) the pass runs over the herm16 copy and the oracle sees
+    that copy's dequantized values."""
+    _say(f"ssb {w.name} B={len(sets)} band={band} n_bf={len(k)} herm16={h16 is not None}")
+    S, Nn, E = dsp.ssb(None if h16 is not None else G_dev, k, sets, step=w.step, band=band, weights=wts, herm16=h16)
     torch.cuda.synchronize()
     S = S.cpu().numpy()
     Nn = Nn.cpu().numpy()
@@ -436,8 +439,13 @@ def _ssb_case(w, G_dev, k, wts, sets, band, entries=None):
     all_entries = np.argwhere(mask)
     if entries is None:
         entries = all_entries
-    G_sel = G_dev[:, torch.as_tensor(entries[:, 0], device=DEV), torch.as_tensor(entries[:, 1], device=DEV)]
-    G_sel = G_sel[torch.as_tensor(act, device=DEV)].cpu().numpy().astype(np.complex128)
+    ey, ex = torch.as_tensor(entries[:, 0], device=DEV), torch.as_tensor(entries[:, 1], device=DEV)
+    if h16 is not None:
+        Q, sc = h16
+        Q_sel = Q[:, ey, ex][torch.as_tensor(act, device=DEV)].cpu().numpy()
+        G_sel = O.herm16_dequantize(Q_sel, sc.cpu().numpy()[act])
+    else:
+        G_sel = G_dev[:, ey, ex][torch.as_tensor(act, device=DEV)].cpu().numpy().astype(np.complex128)
     cols = [G_sel[:, i] for i in range(len(entries))]
     S_o, N_o = O.ssb(entries, cols, k[act], wa, w.n_scan, w.step, sets)
     for b in range(len(sets)):
@@ -472,6 +480,60 @@ def test_ssb_tiny_band_weighted():
     wts = random_weights(len(k), 4)
     sets = [w.optics.replace(soft=True)] + [w.optics.replace(tilt=(0.0, 1e-3 * b)) for b in range(1, 5)]
     S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G_dev, k, wts, sets, (0.3, 1.5))
+    power = np.array([np.sum(wa * np.abs(c) ** 2) for c in cols])
+    assert np.allclose(E, O.agreement(S_o, N_o, power), rtol=1e-6, atol=0)
+
+
+def test_herm16_quantize_bit_exact():
+    """The compact copy matches the oracle's to the bit: scales and codes,
+    with a zero plane (scale 0, codes 0) and a plane whose largest entry is
+    a negative real (code -32767)."""
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    G = data_stack_numpy(w, pix)
+    G[3] = 0.0
+    G[5, 7, 9] = -4.0 * np.abs(G[5]).max()
+    Q, sc = dsp.quantize_herm16(torch.as_tensor(G, device=DEV))
+    torch.cuda.synchronize()
+    Q_o, s_o = O.herm16_quantize(G)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+    assert np.array_equal(Q.cpu().numpy(), Q_o)
+    assert Q_o[5, 7, 9, 0] == -32767 and not np.any(Q_o[3])
+
+
+@pytest.mark.parametrize("depth", [0.0, 136.0])
+def test_ssb_herm16_c1_full(depth):
+    """SSB over the herm16 copy against the oracle on its dequantized values,
+    every band entry, with the agreement; and within the quantisation's reach
+    of the pass over complex64 G."""
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    h16 = dsp.quantize_herm16(G_dev)
+    sets = [w.optics.replace(depth=depth), w.optics.replace(aberrations=[(1, 0, -90.0, 0.0)]),
+            w.optics.replace(tilt=(1e-3, 2e-3))]
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G_dev, k, None, sets, None, h16=h16)
+    power = np.array([np.sum(wa * np.abs(c) ** 2) for c in cols])
+    assert np.allclose(E, O.agreement(S_o, N_o, power), rtol=1e-6, atol=0)
+    # N does not see G: the complex64 pass's.  S moves by at most the codes'
+    # rounding: each component of G is off by <= s_k / (2 * 32767), so
+    # |dS(q)| <= sum_k w_k |Gamma| |dG| <= sqrt(2) sum_k s_k / 32767 (|Gamma| <= 2)
+    S32, N32, _ = dsp.ssb(G_dev, k, sets, step=w.step)
+    assert np.allclose(N32.cpu().numpy(), Nn, rtol=1e-12, atol=0)
+    act = O.active_pixels(k, w.optics)
+    bound = math.sqrt(2.0) * float(np.sum(h16[1].cpu().numpy()[act].astype(np.float64))) / 32767.0 * 1.001
+    dS = np.abs(S - S32.cpu().numpy())
+    assert dS.max() <= bound, f"herm16 vs complex64 |dS| {dS.max():.3e} > bound {bound:.3e}"
+
+
+def test_ssb_herm16_tiny_band_weighted():
+    w = _tiny()
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    wts = random_weights(len(k), 4)
+    sets = [w.optics.replace(soft=True)] + [w.optics.replace(tilt=(0.0, 1e-3 * b)) for b in range(1, 5)]
+    h16 = dsp.quantize_herm16(G_dev)
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G_dev, k, wts, sets, (0.3, 1.5), h16=h16)
     power = np.array([np.sum(wa * np.abs(c) ** 2) for c in cols])
     assert np.allclose(E, O.agreement(S_o, N_o, power), rtol=1e-6, atol=0)
 
@@ -559,4 +621,30 @@ def test_c5_ssb_eight_sets_sampled():
     assert np.allclose(E, E_prop, rtol=1e-6, atol=0)
     assert np.all(E > 0) and np.all(E <= 1.0)
     del G, Sg, Ng
+    torch.cuda.empty_cache()
+
+
+def test_c5_herm16_eight_sets_sampled():
+    """Full-frame herm16: codes and scales bit-exact on sampled pixel planes,
+    SSB over the compact copy against the oracle on sampled band entries."""
+    w = workload("c5")
+    pix, k = bf_pixels(w)
+    _say("generating full-frame G (8807, 512, 257) on the GPU")
+    G = data_stack_torch(w, pix, DEV)
+    Q, sc = dsp.quantize_herm16(G)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = np.sort(rng.choice(G.shape[0], size=12, replace=False))
+    for r in rows:
+        Q_o, s_o = O.herm16_quantize(G[int(r):int(r) + 1].cpu().numpy())
+        assert np.array_equal(sc[int(r):int(r) + 1].cpu().numpy().view(np.uint32), s_o.view(np.uint32)), r
+        assert np.array_equal(Q[int(r):int(r) + 1].cpu().numpy(), Q_o), r
+    del G
+    torch.cuda.empty_cache()
+    sets = ssb_sets(w, 8)
+    ent = np.argwhere(O.band_mask(w.n_scan, w.step, w.band))
+    pick = ent[np.sort(rng.choice(len(ent), size=64, replace=False))]
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, None, k, None, sets, w.band, entries=pick, h16=(Q, sc))
+    assert np.all(E > 0) and np.all(E <= 1.0)
+    del Q, sc
     torch.cuda.empty_cache()

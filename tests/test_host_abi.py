@@ -23,7 +23,7 @@ from stem_direct_ptychography_amd import _lib  # noqa: E402
 
 def test_library_exports_every_declared_symbol():
     hdr = open(os.path.join(ROOT, "include", "dsp.h")).read()
-    declared = set(re.findall(r"\b(dsp_[a-z_]+)\s*\(", hdr))
+    declared = set(re.findall(r"\b(dsp_[a-z0-9_]+)\s*\(", hdr))
     assert declared, "no declarations parsed"
     lib = ctypes.CDLL(_lib.LIB_PATH)
     for name in sorted(declared):
@@ -152,6 +152,14 @@ def test_validation_status_codes():
     assert L.dsp_ssb(fake, len(k), kp, None, ctypes.byref(good), arr, 9, None, None, None, None,
                      None) == _lib.DSP_EINVAL
     assert L.dsp_solve(None, None, 1, None, None, None) == _lib.DSP_EINVAL
+    # herm16: null buffers, bad sizes (caught before any device call)
+    assert L.dsp_quantize_herm16(None, 4, 16, None, None, None) == _lib.DSP_EINVAL
+    assert L.dsp_quantize_herm16(ctypes.c_void_p(16), 0, 16, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                 None) == _lib.DSP_EINVAL
+    assert L.dsp_quantize_herm16(ctypes.c_void_p(16), 4, 15, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                 None) == _lib.DSP_EINVAL
+    assert L.dsp_ssb_herm16(None, None, 1, None, None, ctypes.byref(good), ctypes.byref(oc), 1, None, None, None,
+                            None, None) == _lib.DSP_EINVAL
     assert L.dsp_info(None, None) == _lib.DSP_EINVAL
 
 
