@@ -293,6 +293,17 @@ dsp_status dsp_band_count(const dsp_scan *scan, const double *band_invA, int *co
  * evaluated on the host at n points k_host double[n][2]: chi_out double[n]. */
 dsp_status dsp_chi_host(const dsp_optics *optics, const double *k_host, int n, double *chi_out);
 
+/* The phase differences of the transfer's two lobes as the Gram kernels form
+ * them (the same source: chi expanded about theta(k) = lambda k + tau, one
+ * evaluation of its even and odd parts in d = lambda Q for both lobes),
+ * evaluated on the host.  k_host and q_host double[2 n] (ky, kx) and
+ * (Qy, Qx) in 1/A, scan frame; out double[2 n]: (chi(k - Q) - chi(k),
+ * chi(k + Q) - chi(k)): the phases of the lobes L and R of the weak-object
+ * transfer above ("Where the 9 s of regularized preparation goes", section
+ * "Code path").  EINVAL on bad optics or NULL buffers. */
+dsp_status dsp_chi_shift_host(const dsp_optics *optics, const double *k_host, const double *q_host, int n,
+                              double *out);
+
 /* The library's FP64 sine and cosine of the transfer's phase factors (the
  * same source the kernels compile) evaluated on the host at n points:
  * x_host double[n] -> sin_out, cos_out double[n]. */

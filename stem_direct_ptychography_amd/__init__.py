@@ -26,7 +26,7 @@ from . import _lib
 _L = _lib.load()
 
 __all__ = ["DspError", "Prepared", "prepare", "ssb", "quantize_herm16", "geometry_counts", "alias_geometry", "active_bf",
-           "band_count", "chi_host", "sincos_host", "LIB_PATH"]
+           "band_count", "chi_host", "chi_shift_host", "sincos_host", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
 
@@ -367,4 +367,16 @@ def chi_host(optics, k) -> np.ndarray:
     kk = _coords(k)
     out = np.zeros(kk.shape[0], dtype=np.float64)
     _check(_L.dsp_chi_host(ctypes.byref(_optics(optics)), _dptr(kk), kk.shape[0], _dptr(out)))
+    return out
+
+
+def chi_shift_host(optics, k, Q) -> np.ndarray:
+    """The lobes' phase differences as the Gram kernels form them, on the
+    host: (n, 2) of (chi(k - Q) - chi(k), chi(k + Q) - chi(k))."""
+    kk = _coords(k)
+    qq = _coords(Q)
+    if qq.shape != kk.shape:
+        raise DspError(_lib.DSP_EINVAL, "k and Q must have the same shape")
+    out = np.zeros((kk.shape[0], 2), dtype=np.float64)
+    _check(_L.dsp_chi_shift_host(ctypes.byref(_optics(optics)), _dptr(kk), _dptr(qq), kk.shape[0], _dptr(out)))
     return out

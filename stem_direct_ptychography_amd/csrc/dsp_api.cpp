@@ -964,6 +964,7 @@ struct dsp_handle {
     bool layout_hit = false;
     // device, owned by the handle
     PixelRec *d_pix = nullptr;      // records with this optics' chi(k) and a(k)
+    double *d_tay = nullptr;        // [n_pix][TAY_N] chi's Taylor coefficients about theta(k)
     double2 *d_sys = nullptr;       // [n_q][tri_size(D)]
     double *d_lam = nullptr;
     double2 *d_U = nullptr;
@@ -979,6 +980,7 @@ struct dsp_handle {
     ~dsp_handle() {
         hipSetDevice(device);
         hipFree(d_pix);
+        hipFree(d_tay);
         hipFree(d_sys);
         hipFree(d_lam);
         hipFree(d_U);
@@ -1100,6 +1102,26 @@ dsp_status dsp_chi_host(const dsp_optics *optics, const double *k_host, int n, d
     return DSP_OK;
 }
 
+dsp_status dsp_chi_shift_host(const dsp_optics *optics, const double *k_host, const double *q_host, int n,
+                              double *out) {
+    dsp_status st;
+    if ((st = check_optics(optics))) return st;
+    if (n < 0 || (n > 0 && (!k_host || !q_host || !out))) return fail(DSP_EINVAL, "bad arguments");
+    double c[CHI_NCOEF];
+    chi_coefficients(optics, c);
+    const double lam = optics->wavelength_A;
+    for (int i = 0; i < n; ++i) {
+        const double ty = lam * k_host[2 * i] + optics->tilt_rad[0];
+        const double tx = lam * k_host[2 * i + 1] + optics->tilt_rad[1];
+        double t[TAY_N], E, O;
+        chi_taylor(c, tx, ty, t);
+        chi_even_odd(t, c, lam * q_host[2 * i + 1], lam * q_host[2 * i], E, O);
+        out[2 * i] = E - O;       // chi(k - Q) - chi(k)
+        out[2 * i + 1] = E + O;   // chi(k + Q) - chi(k)
+    }
+    return DSP_OK;
+}
+
 dsp_status dsp_sincos_host(const double *x_host, int n, double *sin_out, double *cos_out) {
     if (n < 0 || (n > 0 && (!x_host || !sin_out || !cos_out))) return fail(DSP_EINVAL, "bad arguments");
     double2 T[TRIG_N];
@@ -1164,7 +1186,9 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
 
     // per-handle buffers
     const size_t n_sys = (size_t)g.n_q * tri_size(h->D);
-    if ((st = dev_alloc(&h->d_pix, (size_t)n_pix)) || (st = dev_alloc(&h->d_sys, n_sys))) return st;
+    if ((st = dev_alloc(&h->d_pix, (size_t)n_pix)) || (st = dev_alloc(&h->d_tay, (size_t)n_pix * TAY_N)) ||
+        (st = dev_alloc(&h->d_sys, n_sys)))
+        return st;
     if (h->method == DSP_PHASE) {
         if ((st = dev_alloc(&h->d_lam, (size_t)g.n_q * am)) || (st = dev_alloc(&h->d_U, (size_t)g.n_q * am * am)) ||
             (st = dev_alloc(&h->d_c, (size_t)g.n_q * am)))
@@ -1177,13 +1201,14 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     }
     const ApertureDev apd = make_aperture_dev(optics);
     const OpticsDev opd = make_optics_dev(optics);
-    HIP_TRY(launch_pixel_terms(L.d_pixbase, h->d_pix, n_pix, apd, opd, nullptr, 0, stream));
+    HIP_TRY(launch_pixel_terms(L.d_pixbase, h->d_pix, n_pix, apd, opd, nullptr, 0, h->d_tay, stream));
     if (h->timing) HIP_TRY(hipEventRecord(h->ev[1], stream));
 
     GramParams gp;
     std::memset(&gp, 0, sizeof gp);
     gp.G = (const float2 *)G_c64_dev;
     gp.pix = h->d_pix;
+    gp.tay = h->d_tay;
     gp.goff = L.d_goff;
     gp.n_pix = n_pix;
     gp.N = g.N;
@@ -1523,8 +1548,8 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
     for (int b = 0; b < B; ++b) {
         const OpticsDev od = make_optics_dev(sets_host + b);
         // a(k) once (set 0 writes it), chi(k) per set
-        if (b == 0) HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, od, nullptr, 0, stream));
-        HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, od, d_chi + b, MAX_SETS_DEV, stream));
+        if (b == 0) HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, od, nullptr, 0, nullptr, stream));
+        HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, od, d_chi + b, MAX_SETS_DEV, nullptr, stream));
         sp.tau_y[b] = od.tau_y;
         sp.tau_x[b] = od.tau_x;
         sp.pt2[b] = od.pt2;

@@ -34,6 +34,89 @@ __host__ __device__ inline double chi_poly(const double *__restrict__ c, double 
 }
 
 // ---------------------------------------------------------------------------
+// chi about a pixel's theta: both lobes' phases from one evaluation
+// ---------------------------------------------------------------------------
+// The transfer's two lobes at scan frequency Q need chi at theta -/+ d with
+// d = lambda Q.  Expanded about theta, chi(theta + d) - chi(theta) =
+// E(d) + O(d) with E the terms of even and O those of odd total degree in
+// d, so chi(theta - d) - chi(theta) = E - O: one evaluation of E and O
+// serves both lobes.  The coefficients t_ab of d_x^a d_y^b come from chi's
+// own by a Taylor shift (repeated synthetic division, the Ruffini-Horner
+// scheme) in x, then in y: 112 FMAs per theta.  Degree 6 is shift-invariant
+// (chi's own coefficients); degrees 1..5 (20 values) depend on theta.
+// Per-theta layout (groups as the evaluation reads them):
+//   A: t20 t02 t40 t22 t04 | B: t11 t31 t13 |
+//   C: t10 t30 t12 t50 t32 t14 | D: t01 t21 t03 t41 t23 t05
+constexpr int TAY_N = 20;
+
+__host__ __device__ inline void chi_taylor(const double *__restrict__ c, double tx, double ty,
+                                           double *__restrict__ t) {
+    double a[CHI_NCOEF];
+#pragma unroll
+    for (int i = 0; i < CHI_NCOEF; ++i) a[i] = c[i];
+    // shift in x: row j is a polynomial of degree 6 - j in theta_x
+#pragma unroll
+    for (int j = 0; j < CHI_DEG; ++j) {
+        const int n = CHI_DEG - j, o = chi_off(j);
+#pragma unroll
+        for (int k = 0; k < n; ++k)
+#pragma unroll
+            for (int i = n - 1; i >= k; --i) a[o + i] = fma(tx, a[o + i + 1], a[o + i]);
+    }
+    // shift in y: column i is a polynomial of degree 6 - i in theta_y
+#pragma unroll
+    for (int i = 0; i < CHI_DEG; ++i) {
+        const int n = CHI_DEG - i;
+#pragma unroll
+        for (int k = 0; k < n; ++k)
+#pragma unroll
+            for (int j = n - 1; j >= k; --j) a[chi_off(j) + i] = fma(ty, a[chi_off(j + 1) + i], a[chi_off(j) + i]);
+    }
+#define DSP_T(x, y) a[chi_off(y) + (x)]
+    t[0] = DSP_T(2, 0);  t[1] = DSP_T(0, 2);  t[2] = DSP_T(4, 0);  t[3] = DSP_T(2, 2);  t[4] = DSP_T(0, 4);
+    t[5] = DSP_T(1, 1);  t[6] = DSP_T(3, 1);  t[7] = DSP_T(1, 3);
+    t[8] = DSP_T(1, 0);  t[9] = DSP_T(3, 0);  t[10] = DSP_T(1, 2); t[11] = DSP_T(5, 0); t[12] = DSP_T(3, 2);
+    t[13] = DSP_T(1, 4);
+    t[14] = DSP_T(0, 1); t[15] = DSP_T(2, 1); t[16] = DSP_T(0, 3); t[17] = DSP_T(4, 1); t[18] = DSP_T(2, 3);
+    t[19] = DSP_T(0, 5);
+#undef DSP_T
+}
+
+// E(d) and O(d) from the per-theta coefficients t and chi's degree-6 ones
+// (c), with X = d_x^2, Y = d_y^2, Z = d_x d_y:
+//   E = X (t20 + X (t40 + X c60 + Y c42) + Y (t22 + Y c24)) + Y (t02 + Y (t04 + Y c06))
+//     + Z (t11 + X (t31 + X c51 + Y c33) + Y (t13 + Y c15))
+//   O = d_x (t10 + X (t30 + X t50 + Y t32) + Y (t12 + Y t14))
+//     + d_y (t01 + X (t21 + X t41 + Y t23) + Y (t03 + Y t05))
+// 30 FP64 operations.
+// The even part reads t[0..7], the odd part t[8..19] (to = t + 8).
+__host__ __device__ inline double chi_even(const double *__restrict__ t, const double *__restrict__ c, double X,
+                                           double Y, double Z) {
+    const double c60 = c[chi_off(0) + 6], c42 = c[chi_off(2) + 4], c24 = c[chi_off(4) + 2], c06 = c[chi_off(6)];
+    const double c51 = c[chi_off(1) + 5], c33 = c[chi_off(3) + 3], c15 = c[chi_off(5) + 1];
+    const double u = fma(Y, c42, fma(X, c60, t[2]));
+    const double v = fma(Y, c24, t[3]);
+    const double P = fma(Y, v, fma(X, u, t[0]));
+    const double R = fma(Y, fma(Y, c06, t[4]), t[1]);
+    const double A = fma(X, P, Y * R);
+    const double B = fma(Y, fma(Y, c15, t[7]), fma(X, fma(Y, c33, fma(X, c51, t[6])), t[5]));
+    return fma(Z, B, A);
+}
+
+__host__ __device__ inline double chi_odd(const double *__restrict__ to, double dx, double dy, double X, double Y) {
+    const double C = fma(Y, fma(Y, to[5], to[2]), fma(X, fma(Y, to[4], fma(X, to[3], to[1])), to[0]));
+    const double D = fma(Y, fma(Y, to[11], to[8]), fma(X, fma(Y, to[10], fma(X, to[9], to[7])), to[6]));
+    return fma(dx, C, dy * D);
+}
+
+__host__ __device__ inline void chi_even_odd(const double *__restrict__ t, const double *__restrict__ c, double dx,
+                                             double dy, double &E, double &O) {
+    const double X = dx * dx, Y = dy * dy, Z = dx * dy;
+    E = chi_even(t, c, X, Y, Z);
+    O = chi_odd(t + 8, dx, dy, X, Y);
+}
+
+// ---------------------------------------------------------------------------
 // packed upper-triangle index of an n x n matrix, i <= j
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int tri_idx(int i, int j, int n) { return i * (2 * n - i + 1) / 2 + (j - i); }
@@ -158,6 +241,7 @@ struct ApertureDev {
 struct GramParams {
     const float2 *G;
     const PixelRec *pix;
+    const double *tay;         // [n_pix][TAY_N] chi's Taylor coefficients about theta(k)
     const long long *goff;     // [n_pix] element offset of each pixel's plane in G
     int n_pix;
     const GramTile *tiles;

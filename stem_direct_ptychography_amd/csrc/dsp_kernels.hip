@@ -54,9 +54,11 @@ __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 // in[p] -> out[p]: lambda k, sqrt(w) a(k) and chi(theta(k)), theta(k) =
 // lambda k + tau formed as a rounded product then a rounded add (never
 // fused), exactly as the Gram and SSB kernels form it; with chi_tab
-// non-null, chi alone into chi_tab[p * chi_stride] (an SSB pass's sets).
+// non-null, chi alone into chi_tab[p * chi_stride] (an SSB pass's sets);
+// with tay non-null also chi's Taylor coefficients about theta(k) into
+// tay[p * TAY_N] (the Gram kernels' lobe phases).
 __global__ void pixel_terms_kernel(const PixelBase *in, PixelRec *out, int n_pix, ApertureDev ap, OpticsDev op,
-                                   double *chi_tab, int chi_stride) {
+                                   double *chi_tab, int chi_stride, double *tay) {
 #pragma clang fp contract(off)
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= n_pix) return;
@@ -66,6 +68,12 @@ __global__ void pixel_terms_kernel(const PixelBase *in, PixelRec *out, int n_pix
     if (chi_tab) {
         chi_tab[(size_t)p * chi_stride] = c;
         return;
+    }
+    if (tay) {
+        double t[TAY_N];
+        chi_taylor(op.chi_c, lkx + op.tau_x, lky + op.tau_y, t);
+#pragma unroll
+        for (int m = 0; m < TAY_N; ++m) tay[(size_t)p * TAY_N + m] = t[m];
     }
     PixelRec r;
     r.lky = lky;
@@ -198,10 +206,26 @@ __device__ __forceinline__ void write_system(const double *acc, unsigned mask, i
     }
 }
 
-// Pixels whose records are staged in LDS at a time (one per lane).
-constexpr int GRAM_CHUNK = 64;
+// Lobe-phase scheme of a Gram kernel (see gram_pixel).  The Taylor scheme
+// saves about a third of a slot's lobe arithmetic but holds twenty more
+// doubles per lane; it pays only where that costs no wave per SIMD (measured
+// on the 512 x 512 full-frame prepare: 5-slot phase 2.73 -> 2.52 ms, 5-slot
+// complex 5.16 -> 5.08 ms; the 4-slot phase kernel, pushed from three waves
+// to two, went 8.43 -> 9.23 ms).
+template <int NJ, int METHOD>
+struct GramTaylor {
+    static constexpr bool value = (METHOD == 0 && NJ == 5) || (METHOD == 1 && NJ >= 5);
+};
 
-// G values fetched ahead per lane: one group of PF pixels (divides GRAM_CHUNK).
+// Pixels whose records (and, with the Taylor scheme, chi's coefficients
+// about theta(k): 160 bytes each) are staged in LDS at a time.
+template <int NJ, int METHOD>
+struct GramChunk {
+    static constexpr int value = GramTaylor<NJ, METHOD>::value ? 32 : 64;
+};
+constexpr int SSB_CHUNK = 64;
+
+// G values fetched ahead per lane: one group of PF pixels (divides the chunk).
 // Two for the phase kernels (no measurable loss, and it keeps the 4-slot
 // kernel within three waves per SIMD without spills), four for complex.
 template <int NJ, int METHOD>
@@ -238,27 +262,21 @@ __device__ __forceinline__ double sinc_tab(double h, const double2 *T) {
     return fabs(h) < 1e-4 ? series : sn / h;
 }
 
-// One lobe of the transfer at the pixel (chi0 = chi(k), amp0 = sqrt(w) a(k))
-// and the displaced point k' = k -/+ Q, given by theta' = lambda k' + tau and
-// d2 = |lambda k'|^2 (inside the support):
-//   value = amp0 a(k') exp(i sgn (chi0 - chi(theta'))), sgn = +1 (L), -1 (R).
+// One lobe of the transfer at the pixel (amp0 = sqrt(w) a(k)) and the
+// displaced point k' = k -/+ Q with d2 = |lambda k'|^2 (inside the support):
+//   value = amp0 a(k') exp(i arg),
+// arg = chi(k) - chi(k - Q) (L) or chi(k + Q) - chi(k) (R), plus the depth
+// term h with DEPTH (the amplitude then gains sinc(h)).
 // a(k') = 1 except in the soft edge ring; the square root runs only when some
 // lane of the wave is in the ring (the empty asm keeps the compiler from
 // computing it unconditionally).
-// With DEPTH, th0 = |theta_k|^2 and the depth term (sinc_tab) is applied.
 template <bool DEPTH>
-__device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, double ty, double tx, double d2,
-                                     double chi0, double amp0, double sgn, double th0, double &re, double &im) {
-    const double c1 = chi_poly(prm.op.chi_c, tx, ty);
-    double arg = chi0 - c1;
+__device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, double arg, double h, double d2,
+                                     double amp0, double &re, double &im) {
     double amp = amp0;
-    if (DEPTH) {
-        const double h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
-        arg += h;
-        amp *= sinc_tab(h, T);
-    }
+    if (DEPTH) amp *= sinc_tab(h, T);
     double sn, cs;
-    sincos_tab(sgn * arg, T, sn, cs);
+    sincos_tab(arg, T, sn, cs);
     const bool ring = d2 > prm.ap.lrin2;
     if (wave_any(ring)) {
         asm volatile("");
@@ -272,18 +290,29 @@ __device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, do
 // rank-one update of the augmented Gram.  A column's terms run when some
 // lane of the wave has it, a pair's when some lane has both (the other lanes
 // add exact zeros).
-template <int NJ, int METHOD, bool DEPTH>
+// Lobe phases, two schemes (GramTaylor picks one per kernel):
+//  TAY: chi expanded about theta(k) (the pixel's Taylor coefficients, read
+//       from LDS into registers once per pixel); one evaluation of the even
+//       and odd parts in d = lambda Q serves both lobes of a slot;
+//  else: the aberration polynomial at both displaced points, minus chi(k).
+template <int NJ, int METHOD, bool DEPTH, bool TAY>
 __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 *T,
                                            double (&acc)[GramShape<NJ, METHOD>::NACC], double2 *lpair, int yh, int ix,
                                            const int (&jyN)[NJ], const int (&jxN)[NJ], const bool (&act)[NJ],
-                                           double lky, double lkx, double amp0, double sw, double chi0, float2 gv) {
+                                           double lky, double lkx, double amp0, double sw, double chi0,
+                                           const double *tay, float2 gv) {
     using Sh = GramShape<NJ, METHOD>;
     constexpr int NC = Sh::NC;
     const double ldq = prm.ldq, lrlim2 = prm.ap.lrlim2;
     const double tau_y = prm.op.tau_y, tau_x = prm.op.tau_x;
     const double lk2 = fma(lky, lky, lkx * lkx);
-    const double py = lky + tau_y, px = lkx + tau_x;
-    const double th0 = DEPTH ? fma(px, px, py * py) : 0.0;   // |theta_k|^2 for the depth term
+    const double py = lky + tau_y, px = lkx + tau_x;   // theta(k)
+    const double th0 = (DEPTH && !TAY) ? fma(px, px, py * py) : 0.0;
+    double tc[TAY ? TAY_N : 1];
+    if (TAY) {
+#pragma unroll
+        for (int m = 0; m < TAY_N; ++m) tc[m] = tay[m];
+    }
 
     const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
     acc[NC] = fma(gr, gr, fma(gi, gi, acc[NC]));   // signal power w |g|^2
@@ -295,14 +324,52 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
         const double Qy_s = (double)(yh + jyN[s]) * ldq, Qx_s = (double)(ix + jxN[s]) * ldq;
         // |lambda (k -/+ Q)|^2 = |lambda k|^2 + |lambda Q|^2 -/+ 2 (lambda k).(lambda Q)
         const double kq = fma(lky, Qy_s, lkx * Qx_s);
-        const double base = lk2 + fma(Qy_s, Qy_s, Qx_s * Qx_s);
+        const double q2 = fma(Qy_s, Qy_s, Qx_s * Qx_s);
+        const double base = lk2 + q2;
         const double dm2 = fma(-2.0, kq, base);
         const double dp2 = fma(2.0, kq, base);
         const bool zl = act[s] && dm2 < lrlim2;
         const bool zr = act[s] && dp2 < lrlim2;
         double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
-        if (zl) lobe<DEPTH>(prm, T, py - Qy_s, px - Qx_s, dm2, chi0, amp0, 1.0, th0, Lr, Li);
-        if (zr) lobe<DEPTH>(prm, T, py + Qy_s, px + Qx_s, dp2, chi0, amp0, -1.0, th0, Rr, Ri);
+        if (TAY) {
+            if (zl || zr) {
+                // chi(theta -/+ d) - chi(theta) = E -/+ O with d = lambda Q
+                const double X = Qx_s * Qx_s, Y = Qy_s * Qy_s;
+                const double E = chi_even(tc, prm.op.chi_c, X, Y, Qx_s * Qy_s);
+                const double O = chi_odd(tc + 8, Qx_s, Qy_s, X, Y);
+                if (DEPTH) {
+                    // |theta|^2 - |theta - d|^2 = 2 theta.d - |d|^2 (L),
+                    // |theta + d|^2 - |theta|^2 = 2 theta.d + |d|^2 (R)
+                    const double td2 = 2.0 * fma(py, Qy_s, px * Qx_s);
+                    const double hl = prm.op.pt2 * (td2 - q2), hr = prm.op.pt2 * (td2 + q2);
+                    if (zl) lobe<DEPTH>(prm, T, (O - E) + hl, hl, dm2, amp0, Lr, Li);
+                    if (zr) lobe<DEPTH>(prm, T, (O + E) + hr, hr, dp2, amp0, Rr, Ri);
+                } else {
+                    if (zl) lobe<DEPTH>(prm, T, O - E, 0.0, dm2, amp0, Lr, Li);
+                    if (zr) lobe<DEPTH>(prm, T, O + E, 0.0, dp2, amp0, Rr, Ri);
+                }
+            }
+        } else {
+            // L: chi(k) - chi(k - Q) (+ h); R: the negation of chi(k) - chi(k + Q) (+ h)
+            if (zl) {
+                const double ty = py - Qy_s, tx = px - Qx_s;
+                double arg = chi0 - chi_poly(prm.op.chi_c, tx, ty), h = 0.0;
+                if (DEPTH) {
+                    h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
+                    arg += h;
+                }
+                lobe<DEPTH>(prm, T, arg, h, dm2, amp0, Lr, Li);
+            }
+            if (zr) {
+                const double ty = py + Qy_s, tx = px + Qx_s;
+                double arg = chi0 - chi_poly(prm.op.chi_c, tx, ty), h = 0.0;
+                if (DEPTH) {
+                    h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
+                    arg += h;
+                }
+                lobe<DEPTH>(prm, T, -arg, h, dp2, amp0, Rr, Ri);
+            }
+        }
         if (METHOD == 0) {
             tr[s] = Ri - Li;   // T_phi = i (L - R)
             ti[s] = Lr - Rr;
@@ -355,9 +422,12 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
     constexpr int NACC = Sh::NACC;
 
     constexpr int PF = GramPrefetch<NJ, METHOD>::value;
+    constexpr bool TAY = GramTaylor<NJ, METHOD>::value;
+    constexpr int GRAM_CHUNK = GramChunk<NJ, METHOD>::value;
     __shared__ double2 T[TRIG_N];
     __shared__ PixelRec srec[GRAM_CHUNK];
     __shared__ long long sgoff[GRAM_CHUNK + PF];
+    __shared__ double stay[TAY ? GRAM_CHUNK * TAY_N : 1];   // [pixel][TAY_N] chi about theta(k)
     constexpr int NP = GramLds<NJ, METHOD>::NP;
     __shared__ double2 lpair_all[(NP > 0 ? NP : 1) * 64];
     const int lane = threadIdx.x;
@@ -416,12 +486,20 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
         for (int c0 = p0; c0 < p1; c0 += GRAM_CHUNK) {
             const int cn = (p1 - c0) < GRAM_CHUNK ? (p1 - c0) : GRAM_CHUNK;
             __syncthreads();   // the previous chunk's records are no longer read
-            if (lane < cn) {
-                srec[lane] = pix[c0 + lane];
-            } else {
-                PixelRec z;
-                z.lky = z.lkx = z.amp0 = z.sw = z.chi0 = z.pad = 0.0;
-                srec[lane] = z;
+            if (lane < GRAM_CHUNK) {
+                // lane = pixel of the chunk (zero records past the end); then
+                // the chunk's Taylor coefficients, coalesced
+                PixelRec rec;
+                if (lane < cn) {
+                    rec = pix[c0 + lane];
+                } else {
+                    rec.lky = rec.lkx = rec.amp0 = rec.sw = rec.chi0 = rec.pad = 0.0;
+                }
+                srec[lane] = rec;
+            }
+            if (TAY) {
+                for (int i = lane; i < GRAM_CHUNK * TAY_N; i += 64)
+                    stay[i] = i < cn * TAY_N ? prm.tay[(size_t)c0 * TAY_N + i] : 0.0;
             }
             for (int i = lane; i < GRAM_CHUNK + PF; i += 64) sgoff[i] = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
             __syncthreads();
@@ -433,8 +511,9 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
                 for (int k = 0; k < PF; ++k) {
                     const int r = r0 + k;
                     const float2 gv = r < cn ? ga[k] : make_float2(0.0f, 0.0f);
-                    gram_pixel<NJ, METHOD, DEPTH>(prm, T, acc, lpair, yh, ix, jyN, jxN, act, srec[r].lky, srec[r].lkx,
-                                           srec[r].amp0, srec[r].sw, srec[r].chi0, gv);
+                    gram_pixel<NJ, METHOD, DEPTH, TAY>(prm, T, acc, lpair, yh, ix, jyN, jxN, act, srec[r].lky,
+                                                       srec[r].lkx, srec[r].amp0, srec[r].sw, srec[r].chi0,
+                                                       stay + (TAY ? r * TAY_N : 0), gv);
                 }
 #pragma unroll
                 for (int k = 0; k < PF; ++k) ga[k] = gb[k];
@@ -985,9 +1064,9 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
     constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
     using GT = typename std::conditional<H16, short2, float2>::type;
     __shared__ double2 T[TRIG_N];
-    __shared__ PixelRec srec[GRAM_CHUNK];
-    __shared__ long long sgoff[GRAM_CHUNK + PF];
-    __shared__ double schi[MAXB * GRAM_CHUNK];   // [set][pixel of the chunk] chi(k)
+    __shared__ PixelRec srec[SSB_CHUNK];
+    __shared__ long long sgoff[SSB_CHUNK + PF];
+    __shared__ double schi[MAXB * SSB_CHUNK];   // [set][pixel of the chunk] chi(k)
     const int lane = threadIdx.x;
     T[lane] = prm.trig[lane];
 
@@ -1023,8 +1102,8 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
         GT ga[PF];
 #pragma unroll
         for (int i = 0; i < PF; ++i) ga[i] = G[goffs[p0 + i < p1 ? p0 + i : p1 - 1] + lane_off];
-        for (int c0 = p0; c0 < p1; c0 += GRAM_CHUNK) {
-            const int cn = (p1 - c0) < GRAM_CHUNK ? (p1 - c0) : GRAM_CHUNK;
+        for (int c0 = p0; c0 < p1; c0 += SSB_CHUNK) {
+            const int cn = (p1 - c0) < SSB_CHUNK ? (p1 - c0) : SSB_CHUNK;
             __syncthreads();
             if (lane < cn) {
                 PixelRec rec = pix[c0 + lane];
@@ -1038,8 +1117,8 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
             }
 #pragma unroll
             for (int b = 0; b < MAXB; ++b)
-                schi[b * GRAM_CHUNK + lane] = (lane < cn && b < prm.B) ? chi_tab[(size_t)(c0 + lane) * MAX_SETS_DEV + b] : 0.0;
-            for (int i = lane; i < GRAM_CHUNK + PF; i += 64) sgoff[i] = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
+                schi[b * SSB_CHUNK + lane] = (lane < cn && b < prm.B) ? chi_tab[(size_t)(c0 + lane) * MAX_SETS_DEV + b] : 0.0;
+            for (int i = lane; i < SSB_CHUNK + PF; i += 64) sgoff[i] = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
             __syncthreads();
             for (int r0 = 0; r0 < cn; r0 += PF) {
                 GT gb[PF];
@@ -1082,7 +1161,7 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                 #pragma unroll
                     for (int b = 0; b < MAXB; ++b) {
                         if (b >= B) continue;   // uniform; keeps the loop fully unrolled
-                        const double chi0 = chi0s[b * GRAM_CHUNK];   // this pixel's chi(k) of set b (LDS)
+                        const double chi0 = chi0s[b * SSB_CHUNK];   // this pixel's chi(k) of set b (LDS)
                         // The set's coefficients are read from the kernel arguments
                         // per use (scalar loads, constant cache): an opaque zero
                         // offset keeps the compiler from hoisting all sets' values
@@ -1251,9 +1330,9 @@ __global__ void agreement_kernel(const double *partial, int n_tiles, int stride,
     do { hipError_t e_ = hipGetLastError(); if (e_ != hipSuccess) return e_; } while (0)
 
 hipError_t launch_pixel_terms(const PixelBase *in, PixelRec *out, int n_pix, const ApertureDev &ap, const OpticsDev &op,
-                              double *chi_tab, int chi_stride, hipStream_t st) {
+                              double *chi_tab, int chi_stride, double *tay, hipStream_t st) {
     if (n_pix <= 0) return hipSuccess;
-    pixel_terms_kernel<<<(n_pix + 255) / 256, 256, 0, st>>>(in, out, n_pix, ap, op, chi_tab, chi_stride);
+    pixel_terms_kernel<<<(n_pix + 255) / 256, 256, 0, st>>>(in, out, n_pix, ap, op, chi_tab, chi_stride, tay);
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }

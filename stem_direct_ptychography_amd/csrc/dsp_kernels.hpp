@@ -42,7 +42,7 @@ struct ScatterParams {
 };
 
 hipError_t launch_pixel_terms(const PixelBase *in, PixelRec *out, int n_pix, const ApertureDev &ap, const OpticsDev &op,
-                              double *chi_tab, int chi_stride, hipStream_t st);
+                              double *chi_tab, int chi_stride, double *tay, hipStream_t st);
 int gram_nacc(int nj, int method);   // doubles per lane of one partial sum
 hipError_t gram_occupancy(int nj, int method, int *blocks_per_cu);
 hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_waves, hipStream_t st);

@@ -76,6 +76,27 @@ def test_chi_polynomial_matches_oracle(name):
     assert np.max(np.abs(got - want)) <= 1e-11 * max(1.0, np.max(np.abs(want)))
 
 
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_chi_shift_matches_oracle(name):
+    """The Gram kernels' lobe phases (chi expanded about theta(k), even and
+    odd parts in lambda Q) against the oracle's chi differences, pixels in
+    the aperture and frequencies out to the alias radius."""
+    w = workload(name)
+    rng = np.random.default_rng(2)
+    kc = w.optics.semiangle / w.optics.wavelength
+    k = rng.uniform(-1.05 * kc, 1.05 * kc, size=(3000, 2))
+    Q = rng.uniform(-2.1 * kc, 2.1 * kc, size=(3000, 2))
+    Q[:5] = 0.0
+    got = dsp.chi_shift_host(w.optics, k, Q)
+    c0 = O.chi(k[:, 0], k[:, 1], w.optics)
+    want_l = O.chi(k[:, 0] - Q[:, 0], k[:, 1] - Q[:, 1], w.optics) - c0
+    want_r = O.chi(k[:, 0] + Q[:, 0], k[:, 1] + Q[:, 1], w.optics) - c0
+    scale = max(1.0, np.max(np.abs(c0)), np.max(np.abs(want_l)), np.max(np.abs(want_r)))
+    assert np.max(np.abs(got[:, 0] - want_l)) <= 1e-11 * scale
+    assert np.max(np.abs(got[:, 1] - want_r)) <= 1e-11 * scale
+    assert not np.any(got[:5])   # Q = 0: no phase difference, exactly
+
+
 def test_chi_polynomial_every_term():
     rng = np.random.default_rng(1)
     k = rng.uniform(-3.0, 3.0, size=(200, 2))
