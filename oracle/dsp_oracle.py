@@ -11,7 +11,7 @@ Pages:
         count: 9.1 s to 35 ms" (What changed).
   [P3]  "Tilt-corrected SSB on CUDA: fit and preview speed" (Setup; Changes).
   [P4]  "Historical WebGPU G(q,k) memory experiment" (Why herm is exactly
-        lossless; Object-redraw fast path).
+        lossless; Implementation; Object-redraw fast path).
 
 Readings where the pages are silent are the ones listed in the design notes
 (frequency set, alias rule, aperture edge, aberration convention, tilt,
@@ -19,7 +19,9 @@ weights, scale, prior, agreement); each function states the one it uses.
 
 Parity unpinned (values fixed by these readings, not by the pages): the
 strength scale (sum of weights), the prior's constant s_p, the weights, the
-agreement's normalisation, the rotation sign.
+agreement's normalisation, the rotation sign, the previews' correction (the
+SSB sum's matched filter conj(Gamma)) and the loss (the weighted mean
+variance of the pixels' phases).
 """
 from __future__ import annotations
 
@@ -480,6 +482,126 @@ def agreement(S: np.ndarray, Nn: np.ndarray, power: np.ndarray) -> np.ndarray:
         m = Nn[b] > 0
         num[b] = np.sum((S[b, m].real ** 2 + S[b, m].imag ** 2) / Nn[b, m])
     return num / float(np.sum(power))
+
+
+# ----------------------------------------------------------------------------
+# previews and the loss path
+# ----------------------------------------------------------------------------
+
+
+def g_full(G_act: np.ndarray, iy: int, ix: int, n_scan: int) -> np.ndarray:
+    """G(q, k) over the given pixels at any full-plane index (iy, ix) from the
+    stored half plane: G(-q, k) = conj G(q, k) ([P4] Why herm is exactly
+    lossless)."""
+    iy %= n_scan
+    ix %= n_scan
+    if ix <= n_scan // 2:
+        return np.asarray(G_act[:, iy, ix], dtype=np.complex128)
+    return np.conj(np.asarray(G_act[:, (-iy) % n_scan, n_scan - ix], dtype=np.complex128))
+
+
+def corrected_term(ka: np.ndarray, wa: np.ndarray, G_act: np.ndarray, Ky: int, Kx: int, n_scan: int,
+                   step: float, optics) -> np.ndarray:
+    """Per-pixel corrected G at fine frequency K (signed indices), K != 0:
+    C_k(K) = i w_k conj(Gamma(K, k)) G(K mod N, k) with Gamma = T_phi = i (L - R)
+    at Q = K dq.  ([P4] Object-redraw fast path: the gamma-corrected G(q, k);
+    [P3] Open: the corrected spectrum of a real image is anti-Hermitian except
+    at DC, which the factor i gives.)  Reading, parity unpinned as a
+    definition: the correction is the SSB sum's matched filter conj(Gamma)."""
+    dq = scan_frequency_step(n_scan, step)
+    L, R = lobes(ka[:, 0], ka[:, 1], Ky * dq, Kx * dq, optics)
+    gam = 1j * (L - R)
+    return 1j * wa * np.conj(gam) * g_full(G_act, Ky, Kx, n_scan)
+
+
+def preview_spectrum(G: np.ndarray, k: np.ndarray, w: Optional[np.ndarray], n_scan: int, step: float,
+                     upsampling: int, optics) -> np.ndarray:
+    """Fine half plane P (uN, uN/2 + 1) of the object fast path: the corrected
+    G summed over the active pixels at every fine frequency K (signed row,
+    column 0..uN/2), P(K) = sum_k C_k(K); at K = 0 the uncorrected
+    P(0) = sum_k w_k G(0, k).  ([P4] Object-redraw fast path: sum over BF
+    pixels in Fourier space, then one inverse FFT; [P3] Changes: the 1x and
+    3x drag previews.)"""
+    act = active_pixels(k, optics)
+    ka = k[act]
+    wa = np.ones(len(act)) if w is None else np.asarray(w, dtype=np.float64)[act]
+    Ga = G[act]
+    m = upsampling * n_scan
+    P = np.zeros((m, m // 2 + 1), dtype=np.complex128)
+    for iy in range(m):
+        Ky = int(signed_index(iy, m))
+        for Kx in range(m // 2 + 1):
+            if Ky == 0 and Kx == 0:
+                P[0, 0] = np.sum(wa * np.asarray(Ga[:, 0, 0], dtype=np.complex128))
+            else:
+                P[iy, Kx] = np.sum(corrected_term(ka, wa, Ga, Ky, Kx, n_scan, step, optics))
+    return P
+
+
+def full_plane(P: np.ndarray) -> np.ndarray:
+    """The (M, M) plane from its half (M, M/2 + 1) by P(-K) = -conj P(K) for
+    K != 0 ([P3] Open: anti-Hermitian except at DC)."""
+    m = P.shape[0]
+    F = np.zeros((m, m), dtype=np.complex128)
+    F[:, : m // 2 + 1] = P
+    for iy in range(m):
+        for ix in range(m // 2 + 1, m):
+            F[iy, ix] = -np.conj(P[(-iy) % m, m - ix])
+    return F
+
+
+def preview_phase(P: np.ndarray) -> np.ndarray:
+    """Object phase of the fast path, angle(ifft2(full plane)) on the (M, M)
+    grid ([P4] Object-redraw fast path: ONE 2D inverse FFT and one atan2;
+    the estimator angle(mean(object)))."""
+    return np.angle(np.fft.ifft2(full_plane(P)))
+
+
+def pixel_planes(G: np.ndarray, k: np.ndarray, w: Optional[np.ndarray], n_scan: int, step: float, optics):
+    """Yields (w_k, C_k) for every active pixel: its corrected full (N, N)
+    plane, the corrected terms at every q != 0 and w_k G(0, k) at DC ([P3]
+    Changes, loss path: the corrected full plane straight from the stored
+    half plane)."""
+    act = active_pixels(k, optics)
+    ka = k[act]
+    wa = np.ones(len(act)) if w is None else np.asarray(w, dtype=np.float64)[act]
+    Ga = G[act]
+    n = n_scan
+    dq = scan_frequency_step(n, step)
+    yy = signed_index(np.arange(n), n).astype(np.float64)
+    QY, QX = np.meshgrid(yy * dq, yy * dq, indexing="ij")     # full-plane signed frequencies
+    for j in range(len(act)):
+        gfull = np.zeros((n, n), dtype=np.complex128)
+        for iy in range(n):
+            for ix in range(n):
+                gfull[iy, ix] = g_full(Ga[j:j + 1], iy, ix, n)[0]
+        L, R = lobes(np.full(QY.shape, ka[j, 0]), np.full(QY.shape, ka[j, 1]), QY, QX, optics)
+        C = 1j * wa[j] * np.conj(1j * (L - R)) * gfull
+        C[0, 0] = wa[j] * gfull[0, 0]
+        yield float(wa[j]), C
+
+
+def loss_path(G: np.ndarray, k: np.ndarray, w: Optional[np.ndarray], n_scan: int, step: float, optics):
+    """Mean phase and loss over the pixels' objects ([P3] Changes, loss path:
+    inverse FFT of each pixel's corrected plane and phase moments; [P4]:
+    mean(angle(object)) needs the per-pixel phases).  Pixel k's object is
+    o_k = ifft2(C_k), theta_k = angle(o_k).  Returns (mean phase
+    sum_k w_k theta_k / sum_k w_k (N, N), loss = mean over r of
+    sum_k w_k (theta_k - mean)^2 / sum_k w_k).  Reading, parity unpinned as a
+    definition: weighted moments, the loss as the mean variance of the
+    pixels' phases."""
+    n = n_scan
+    s0 = 0.0
+    s1 = np.zeros((n, n))
+    s2 = np.zeros((n, n))
+    for wk, C in pixel_planes(G, k, w, n_scan, step, optics):
+        th = np.angle(np.fft.ifft2(C))
+        s0 += wk
+        s1 += wk * th
+        s2 += wk * th * th
+    mean = s1 / s0
+    var = s2 / s0 - mean * mean
+    return mean, float(np.mean(var))
 
 
 # ----------------------------------------------------------------------------

@@ -339,6 +339,183 @@ def test_depth_transfer_matches_multislice(monkeypatch):
 
 
 # ----------------------------------------------------------------------------
+# previews and the loss path
+# ----------------------------------------------------------------------------
+
+
+def _phase_object_data(n=8, step=0.5, sigma=0.05, seed=11, depth=0.0):
+    """First-order data of a pure phase object at u = 1 from the simulator's
+    probe-amplitude formula (independent of the oracle's lobes)."""
+    opt = tiny_optics(O.scan_frequency_step(n, step)).replace(depth=depth)
+    rng = np.random.default_rng(seed)
+    phi = sigma * S.band_limited_field(n, rng)
+    kc = opt.semiangle / opt.wavelength
+    k = rng.uniform(-1.1 * kc, 1.1 * kc, size=(40, 2))
+    G = S.first_order_G(k, 1j * phi, n, step, 1, opt)
+    return opt, phi, k, G
+
+
+def test_preview_phase_closed_form_for_a_phase_object():
+    """Noise-free first-order data of a phase object phi: the corrected sum is
+    P(q) = i N(q) Phi(q) with N = sum_k w |Gamma|^2, so the fast path's phase
+    is atan2(ifft2(N Phi), D / N^2), D = sum_k w G(0, k).  A conjugation or a
+    dropped factor i in the correction fails it."""
+    n, step = 8, 0.5
+    opt, phi, k, G = _phase_object_data(n, step)
+    w = np.linspace(0.5, 1.5, len(k))
+    P = O.preview_spectrum(G, k, w, n, step, 1, opt)
+    act = O.active_pixels(k, opt)
+    ent = np.argwhere(np.ones((n, n // 2 + 1), dtype=bool))
+    cols = [np.zeros(len(act), dtype=np.complex128)] * len(ent)
+    _, Nh = O.ssb(ent, cols, k[act], w[act], n, step, [opt])
+    Nf = np.zeros((n, n))
+    Nf[ent[:, 0], ent[:, 1]] = Nh[0]
+    for iy in range(n):
+        for ix in range(n // 2 + 1, n):
+            Nf[iy, ix] = Nf[(-iy) % n, n - ix]      # N(-q) = N(q)
+    D = float(np.sum(w[act] * G[act, 0, 0].real))
+    want = np.arctan2(np.real(np.fft.ifft2(Nf * np.fft.fft2(phi))), D / (n * n))
+    got = O.preview_phase(P)
+    assert np.max(np.abs(got - want)) <= 1e-12
+    assert np.std(want) > 1e-3                          # a non-trivial image
+    true_corrected = O.corrected_term
+    for bad in ("conj", "no_i"):
+        def planted(ka, wa, Ga, Ky, Kx, n_scan, stp, optics, bad=bad):
+            c = true_corrected(ka, wa, Ga, Ky, Kx, n_scan, stp, optics)
+            if bad == "conj":   # Gamma instead of conj(Gamma)
+                dq = O.scan_frequency_step(n_scan, stp)
+                L, R = O.lobes(ka[:, 0], ka[:, 1], Ky * dq, Kx * dq, optics)
+                return 1j * wa * (1j * (L - R)) * O.g_full(Ga, Ky, Kx, n_scan)
+            return c / 1j
+        O.corrected_term = planted
+        try:
+            bad_phase = O.preview_phase(O.preview_spectrum(G, k, w, n, step, 1, opt))
+        finally:
+            O.corrected_term = true_corrected
+        assert np.max(np.abs(bad_phase - want)) > 0.1 * np.std(want)
+
+
+def test_preview_at_u1_is_the_ssb_sum():
+    """At u = 1 the fast path's spectrum is i S(q) with S the SSB sum at every
+    stored q != 0, and sum_k w G(0, k) at DC."""
+    w_ = workload("c1")
+    n, step = w_.n_scan, w_.step
+    opt, _, k, G = _phase_object_data(n=n, step=step, seed=3)
+    rng = np.random.default_rng(4)
+    G = G + 0.1 * np.fft.rfft2(rng.standard_normal((G.shape[0], n, n)))
+    w = rng.uniform(0.5, 1.5, len(k))
+    P = O.preview_spectrum(G, k, w, n, step, 1, opt)
+    act = O.active_pixels(k, opt)
+    ent = np.argwhere(np.ones((n, n // 2 + 1), dtype=bool))
+    Sv, _ = O.ssb(ent, [G[act, iy, ix] for iy, ix in ent], k[act], w[act], n, step, [opt])
+    Sp = np.zeros((n, n // 2 + 1), dtype=np.complex128)
+    Sp[ent[:, 0], ent[:, 1]] = Sv[0]
+    Sp[0, 0] = 0.0
+    assert np.allclose(P[1:], 1j * Sp[1:], rtol=1e-12, atol=1e-12 * np.abs(Sp).max())
+    assert np.allclose(P[0, 1:], 1j * Sp[0, 1:], rtol=1e-12, atol=1e-12 * np.abs(Sp).max())
+    assert P[0, 0] == pytest.approx(np.sum(w[act] * G[act, 0, 0]), rel=1e-14)
+
+
+def test_preview_fine_grid_is_the_prepare_rhs():
+    """On the u-times finer grid, the corrected sum at an alias K of q equals
+    i r_K with r = T_phi^H W g the phase prepare's right side: the fine
+    frequency, the G index K mod N and the mirror agree with the alias
+    table."""
+    n, step, u = 8, 0.5, 3
+    opt = tiny_optics(O.scan_frequency_step(n, step))
+    rng = np.random.default_rng(6)
+    kc = opt.semiangle / opt.wavelength
+    k = rng.uniform(-1.1 * kc, 1.1 * kc, size=(30, 2))
+    G = np.fft.rfft2(rng.standard_normal((30, n, n)))      # real traces: Hermitian-consistent
+    w = rng.uniform(0.5, 1.5, 30)
+    P = O.preview_spectrum(G, k, w, n, step, u, opt)
+    Fp = O.full_plane(P)
+    act = O.active_pixels(k, opt)
+    dq = O.scan_frequency_step(n, step)
+    q, counts, Ks = O.alias_table(n, step, u, opt)
+    m = u * n
+    checked = 0
+    for (iy, ix), K in zip(q, Ks):
+        if len(K) == 0:
+            continue
+        T = O.transfer(k[act], K * dq, opt, "phase")
+        _, r, _ = O.normal_equations(T, G[act, iy, ix], w[act])
+        for j, (Ky, Kx) in enumerate(K):
+            got = Fp[Ky % m, Kx % m]
+            assert abs(got - 1j * r[j]) <= 1e-11 * max(1.0, abs(r[j])), (iy, ix, Ky, Kx)
+            checked += 1
+    assert checked > 100
+
+
+def test_preview_is_antihermitian_off_dc():
+    """Direct evaluation at K and -K: P(-K) = -conj P(K) for K != 0 ([P3] Open:
+    the corrected spectrum of a real image)."""
+    n, step, u = 8, 0.5, 2
+    opt = tiny_optics(O.scan_frequency_step(n, step)).replace(depth=60.0)
+    rng = np.random.default_rng(7)
+    kc = opt.semiangle / opt.wavelength
+    k = rng.uniform(-1.1 * kc, 1.1 * kc, size=(25, 2))
+    G = np.fft.rfft2(rng.standard_normal((25, n, n)))
+    w = rng.uniform(0.5, 1.5, 25)
+    act = O.active_pixels(k, opt)
+    for Ky, Kx in [(1, 2), (-3, 5), (7, -6), (0, 3), (-8, 1), (5, 8)]:
+        a = np.sum(O.corrected_term(k[act], w[act], G[act], Ky, Kx, n, step, opt))
+        b = np.sum(O.corrected_term(k[act], w[act], G[act], -Ky, -Kx, n, step, opt))
+        assert abs(b + np.conj(a)) <= 1e-12 * max(1.0, abs(a))
+
+
+def test_fast_path_identity_and_single_pixel_loss():
+    """[P4]'s identity: the mean of the pixels' objects is the inverse FFT of
+    the summed corrected planes, so angle(sum_k o_k) is the fast path's
+    phase; with one pixel, mean(angle) = angle(mean) and the loss is 0.  A
+    pixel's object by explicit DFT double sums (e^{+2 pi i q.r} / N^2) equals
+    the inverse FFT."""
+    n, step = 8, 0.5
+    opt, _, k, G = _phase_object_data(n, step, seed=12)
+    w = np.linspace(0.7, 1.3, len(k))
+    objs = [np.fft.ifft2(C) for _, C in O.pixel_planes(G, k, w, n, step, opt)]
+    fast = O.preview_phase(O.preview_spectrum(G, k, w, n, step, 1, opt))
+    assert np.max(np.abs(np.angle(np.sum(objs, axis=0)) - fast)) <= 1e-12
+    # explicit DFT of one pixel's plane
+    _, C0 = next(iter(O.pixel_planes(G, k, w, n, step, opt)))
+    r = np.arange(n)
+    E = np.exp(2j * math.pi * np.outer(r, r) / n)
+    brute = (E @ C0 @ E.T) / (n * n)
+    assert np.allclose(brute, objs[0], rtol=0, atol=1e-12 * np.abs(objs[0]).max())
+    # one pixel
+    act = O.active_pixels(k, opt)
+    k1 = k[act[:1]]
+    G1 = G[act[:1]]
+    mean, loss = O.loss_path(G1, k1, None, n, step, opt)
+    assert loss == pytest.approx(0.0, abs=1e-15)
+    assert np.max(np.abs(mean - O.preview_phase(O.preview_spectrum(G1, k1, None, n, step, 1, opt)))) <= 1e-12
+
+
+def test_loss_is_a_weighted_variance():
+    """The loss against explicit per-pixel phases: the weighted variance about
+    the weighted mean, averaged over the scan; zero-weight pixels drop out."""
+    n, step = 8, 0.5
+    opt, _, k, G = _phase_object_data(n, step, seed=13)
+    rng = np.random.default_rng(14)
+    G = G + 0.5 * np.fft.rfft2(rng.standard_normal((G.shape[0], n, n)))
+    w = rng.uniform(0.5, 1.5, len(k))
+    w[::4] = 0.0
+    th, ws = [], []
+    for wk, C in O.pixel_planes(G, k, w, n, step, opt):
+        th.append(np.angle(np.fft.ifft2(C)))
+        ws.append(wk)
+    th = np.array(th)
+    ws = np.array(ws)
+    keep = ws > 0
+    mean_b = np.average(th[keep], axis=0, weights=ws[keep])
+    var_b = np.average((th[keep] - mean_b) ** 2, axis=0, weights=ws[keep])
+    mean, loss = O.loss_path(G, k, w, n, step, opt)
+    assert np.allclose(mean, mean_b, rtol=0, atol=1e-13)
+    assert loss == pytest.approx(float(var_b.mean()), rel=1e-9)
+    assert loss > 1e-4
+
+
+# ----------------------------------------------------------------------------
 # compact G (herm16)
 # ----------------------------------------------------------------------------
 
