@@ -521,7 +521,10 @@ def preview_spectrum(G: np.ndarray, k: np.ndarray, w: Optional[np.ndarray], n_sc
     column 0..uN/2), P(K) = sum_k C_k(K); at K = 0 the uncorrected
     P(0) = sum_k w_k G(0, k).  ([P4] Object-redraw fast path: sum over BF
     pixels in Fourier space, then one inverse FFT; [P3] Changes: the 1x and
-    3x drag previews.)"""
+    3x drag previews.)  The fine grid's Nyquist row and column stay 0: index
+    uN/2 stands for two frequencies, +-uN/2 dq, whose corrections differ, so
+    no anti-Hermitian value exists there (the reading the prepare takes for
+    the Nyquist lines' aliases)."""
     act = active_pixels(k, optics)
     ka = k[act]
     wa = np.ones(len(act)) if w is None else np.asarray(w, dtype=np.float64)[act]
@@ -531,6 +534,8 @@ def preview_spectrum(G: np.ndarray, k: np.ndarray, w: Optional[np.ndarray], n_sc
     for iy in range(m):
         Ky = int(signed_index(iy, m))
         for Kx in range(m // 2 + 1):
+            if Ky == -(m // 2) or Kx == m // 2:
+                continue
             if Ky == 0 and Kx == 0:
                 P[0, 0] = np.sum(wa * np.asarray(Ga[:, 0, 0], dtype=np.complex128))
             else:
