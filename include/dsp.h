@@ -293,6 +293,32 @@ dsp_status dsp_band_count(const dsp_scan *scan, const double *band_invA, int *co
  * evaluated on the host at n points k_host double[n][2]: chi_out double[n]. */
 dsp_status dsp_chi_host(const dsp_optics *optics, const double *k_host, int n, double *chi_out);
 
+/* Upsampled SSB preview: the object fast path ("Historical WebGPU G(q,k)
+ * memory experiment", section "Object-redraw fast path": the corrected G
+ * summed over the bright-field pixels in Fourier space, then one inverse FFT
+ * and one angle; "Tilt-corrected SSB on CUDA: fit and preview speed",
+ * section "Changes": the 1x and 3x drag previews).  On the fine grid
+ * M = u N, for every K != 0 of its half plane (signed row, column 0..M/2):
+ *   P(K) = i sum_k w_k conj(Gamma(K, k)) G(K mod N, k),  Gamma = T_phi at Q = K dq,
+ * over the active pixels (G(-q) = conj G(q) supplies q beyond column N/2),
+ * and P(0) = sum_k w_k G(0, k); P = 0 on the fine Nyquist row and column
+ * (index M/2 stands for +-M/2 dq, whose corrections differ).  The corrected spectrum of a real image is
+ * anti-Hermitian off DC (same page, section "Open"): the full plane has
+ * P(-K) = -conj P(K), the object is o = ifft2(full plane), the phase angle(o).
+ *   G_c64_dev, n_bf, bf_coords_host, weights_host, scan, optics: as dsp_ssb
+ *       with one optics set (depth terms included).
+ *   upsampling: u in 1..4.
+ *   spec_out_c128_dev: [M][M/2+1] complex128 P, or NULL.
+ *   phase_out_dev: [M][M] float64 phase (rad, in [-pi, pi]), or NULL; at
+ *       least one output.
+ * Asynchronous on hip_stream; scratch from the stream's arena.  The inverse
+ * FFT is hipFFT's Z2D; its plan per (device, M) is kept until the process
+ * ends.  DSP_EUNSUPPORTED for u outside 1..4, DSP_EINVAL for bad arguments,
+ * DSP_EDEVICE for a hipFFT failure. */
+dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
+                       const dsp_scan *scan, const dsp_optics *optics, int upsampling, void *spec_out_c128_dev,
+                       double *phase_out_dev, void *hip_stream);
+
 /* The phase differences of the transfer's two lobes as the Gram kernels form
  * them (the same source: chi expanded about theta(k) = lambda k + tau, one
  * evaluation of its even and odd parts in d = lambda Q for both lobes),

@@ -25,7 +25,7 @@ from . import _lib
 
 _L = _lib.load()
 
-__all__ = ["DspError", "Prepared", "prepare", "ssb", "quantize_herm16", "geometry_counts", "alias_geometry", "active_bf",
+__all__ = ["DspError", "Prepared", "prepare", "ssb", "preview", "quantize_herm16", "geometry_counts", "alias_geometry", "active_bf",
            "band_count", "chi_host", "chi_shift_host", "sincos_host", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -248,6 +248,28 @@ def quantize_herm16(G, stream=None):
     _check(_L.dsp_quantize_herm16(ctypes.c_void_p(G.data_ptr()), G.shape[0], n, ctypes.c_void_p(Q.data_ptr()),
                                   ctypes.c_void_p(sc.data_ptr()), ctypes.c_void_p(_stream(stream))))
     return Q, sc
+
+
+def preview(G, bf_coords, optics, step: float, upsampling: int = 1, weights=None, spectrum: bool = True,
+            phase: bool = True, stream=None):
+    """Upsampled SSB preview (dsp_preview): returns (P (uN, uN/2+1)
+    complex128 or None, phase (uN, uN) float64 or None) on G's device."""
+    torch = _torch()
+    n = _check_G(G)
+    k = _coords(bf_coords)
+    if k.shape[0] != G.shape[0]:
+        raise DspError(_lib.DSP_EINVAL, "bf_coords rows must match G's first axis")
+    w = _weights(weights, k.shape[0])
+    m = int(upsampling) * n
+    P = torch.empty((m, m // 2 + 1), dtype=torch.complex128, device=G.device) if spectrum else None
+    ph = torch.empty((m, m), dtype=torch.float64, device=G.device) if phase else None
+    scan = _lib.ScanC(n, float(step))
+    _check(_L.dsp_preview(ctypes.c_void_p(G.data_ptr()), k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan),
+                          ctypes.byref(_optics(optics)), int(upsampling),
+                          ctypes.c_void_p(P.data_ptr()) if P is not None else None,
+                          ctypes.c_void_p(ph.data_ptr()) if ph is not None else None,
+                          ctypes.c_void_p(_stream(stream))))
+    return P, ph
 
 
 def _check_Q(Q, scale):

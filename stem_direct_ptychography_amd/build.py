@@ -20,6 +20,9 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# the previews' and loss path's inverse real FFTs
+LIBS = ["-lhipfft"]
+
 
 def hipcc_path() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -31,7 +34,7 @@ def hipcc_path() -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source into libdsp.so next to this file; returns its path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc_path()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    cmd = [hipcc_path()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + LIBS + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -10,6 +10,8 @@
 #include "dsp_internal.hpp"
 #include "dsp_kernels.hpp"
 
+#include <hipfft/hipfft.h>
+
 #include <algorithm>
 #include <chrono>
 #include <cmath>
@@ -20,6 +22,7 @@
 #include <memory>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <vector>
 
 using namespace dsp;
@@ -802,12 +805,14 @@ dsp_status get_layout(const LayoutKey &key, const dsp_scan *scan, const dsp_opti
 // ---------------------------------------------------------------------------
 struct SsbKey {
     int device = 0, n_scan = 0, soft = 0, n_bf = 0, has_band = 0;
+    int up = 1;         // lanes on the u-times finer grid (previews)
+    int preview = 0;    // lanes: every fine K != 0 that some lobe can reach (else the stored band)
     double step = 0, lam = 0, alpha = 0, dk = 0, lo = 0, hi = 0;
     std::vector<double> coords, weights;
     bool operator==(const SsbKey &o) const {
         return device == o.device && n_scan == o.n_scan && soft == o.soft && n_bf == o.n_bf && has_band == o.has_band &&
-               step == o.step && lam == o.lam && alpha == o.alpha && dk == o.dk && lo == o.lo && hi == o.hi &&
-               coords == o.coords && weights == o.weights;
+               up == o.up && preview == o.preview && step == o.step && lam == o.lam && alpha == o.alpha &&
+               dk == o.dk && lo == o.lo && hi == o.hi && coords == o.coords && weights == o.weights;
     }
 };
 
@@ -852,13 +857,19 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
     const double dq = 1.0 / (N * key.step);
     if ((st = build_active(coords, weights, key.n_bf, optics, N, L->act))) return st;
     if (L->act.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
-    // lane groups over every stored entry inside the band
-    const int nh = N / 2 + 1;
-    auto in_band = [&](int yh, int ix) {
+    // lane groups over every stored entry inside the band; for a preview,
+    // over the fine half plane's K != 0 within reach of two overlapping
+    // apertures (|K| < 2 r_lim) and off the fine Nyquist row and column
+    // (index M/2 stands for +-M/2 dq, whose corrections differ); the rest of
+    // the plane is zero
+    const int M = key.up * N, mh = M / 2 + 1;
+    const double reach = 2.0 * std::sqrt(make_aperture_dev(optics).rlim2) * (1.0 + 1e-9);
+    auto keep = [&](int yh, int ix) {
         const double f = std::hypot((double)yh * dq, (double)ix * dq);
+        if (key.preview) return !(yh == 0 && ix == 0) && yh != -M / 2 && ix != M / 2 && f < reach;
         return !key.has_band || (f >= key.lo && f <= key.hi);
     };
-    for (const Lanes &grp : pack_line_runs(N, nh, -N / 2, N / 2 - 1, nh, 16, in_band)) {
+    for (const Lanes &grp : pack_line_runs(M, mh, -M / 2, M / 2 - 1, mh, 16, keep)) {
         SsbTile t;
         std::memset(&t, 0, sizeof t);
         double sy = 0.0, sx = 0.0;
@@ -1465,6 +1476,129 @@ dsp_status dsp_alias_table(const dsp_handle *h, int32_t *q_host, int32_t *count_
 }  // extern "C"
 
 // The SSB pass over complex64 G (GQ null) or herm16 G (GQ, gscale).
+// Scratch of one SSB pass (the stream's arena).
+struct SsbPassBufs {
+    PixelRec *pix;
+    double *chi;        // [n_pix][MAX_SETS_DEV]
+    double *part;       // stream-K partial sums
+    double *tile_part;  // [n_tiles][partial stride]
+};
+
+// One pass over G for B sets on layout L: pixel terms, then the SSB kernel
+// with lanes on the (M, M/2 + 1) grid writing S and N there.
+static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int B, const void *G_c64_dev,
+                           const void *GQ_dev, const float *gscale_dev, int N, int M, double2 *S_out, double *N_out,
+                           const SsbPassBufs &bufs, int device, hipStream_t stream) {
+    dsp_status st;
+    const int n_tiles = (int)L.tiles.size();
+    const int n_pix = (int)L.act.pix.size();
+    const int mi = maxb_index(ssb_maxb(B));
+    const double dq = 1.0 / (N * L.key.step);
+    const ApertureDev apd = make_aperture_dev(sets_host);
+    SsbParams sp;
+    std::memset(&sp, 0, sizeof sp);
+    for (int b = 0; b < B; ++b) {
+        const OpticsDev od = make_optics_dev(sets_host + b);
+        // a(k) once (set 0 writes it), chi(k) per set
+        if (b == 0) HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, nullptr, 0, nullptr, stream));
+        HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, bufs.chi + b, MAX_SETS_DEV, nullptr, stream));
+        sp.tau_y[b] = od.tau_y;
+        sp.tau_x[b] = od.tau_x;
+        sp.pt2[b] = od.pt2;
+        std::memcpy(sp.chi_c[b], od.chi_c, sizeof od.chi_c);
+    }
+    sp.G = (const float2 *)G_c64_dev;
+    sp.GQ = (const short2 *)GQ_dev;
+    sp.gscale = gscale_dev;
+    sp.plane = (long long)N * (N / 2 + 1);
+    sp.pix = bufs.pix;
+    sp.goff = L.d_goff;
+    sp.chi_tab = bufs.chi;
+    sp.n_pix = n_pix;
+    sp.tiles = L.d_tiles;
+    sp.N = N;
+    sp.nh = N / 2 + 1;
+    sp.M = M;
+    sp.mh = M / 2 + 1;
+    sp.dq = dq;
+    sp.ldq = sets_host[0].wavelength_A * dq;
+    sp.B = B;
+    sp.ap = apd;
+    sp.lam = sets_host[0].wavelength_A;
+    sp.S_out = S_out;
+    sp.N_out = N_out;
+    sp.wbegin = L.d_wbegin[mi];
+    sp.seg_off = L.d_seg_off[mi];
+    sp.seg_first = L.d_seg_first[mi];
+    sp.partial = bufs.part;
+    if ((st = trig_table_device(device, &sp.trig))) return st;
+    HIP_TRY(launch_ssb(sp, L.waves[mi], n_tiles, bufs.tile_part, stream));
+    return DSP_OK;
+}
+
+// Inverse real FFTs (hipFFT Z2D, unnormalized): batch planes of (m, m/2 + 1)
+// complex -> (m, m) real.  Plans are made once per (device, m, batch) and
+// kept for the process (their work areas with them); a plan is bound to the
+// caller's stream for each execution under the lock.  hipFFT may overwrite
+// the input.
+static std::mutex g_fft_mu;
+static std::map<std::tuple<int, int, int>, hipfftHandle> g_fft_plans;
+
+static dsp_status fft_z2d(int device, int m, int batch, double2 *in, double *out, hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(g_fft_mu);
+    const auto key = std::make_tuple(device, m, batch);
+    hipfftHandle plan;
+    auto it = g_fft_plans.find(key);
+    if (it == g_fft_plans.end()) {
+        hipfftResult r;
+        if (batch == 1) {
+            r = hipfftPlan2d(&plan, m, m, HIPFFT_Z2D);
+        } else {
+            int n[2] = {m, m};
+            r = hipfftPlanMany(&plan, 2, n, nullptr, 1, m * (m / 2 + 1), nullptr, 1, m * m, HIPFFT_Z2D, batch);
+        }
+        if (r != HIPFFT_SUCCESS) return fail(DSP_EDEVICE, "hipfft plan %d x %d (batch %d): error %d", m, m, batch, (int)r);
+        g_fft_plans[key] = plan;
+    } else {
+        plan = it->second;
+    }
+    hipfftResult r = hipfftSetStream(plan, stream);
+    if (r == HIPFFT_SUCCESS) r = hipfftExecZ2D(plan, (hipfftDoubleComplex *)in, (hipfftDoubleReal *)out);
+    if (r != HIPFFT_SUCCESS) return fail(DSP_EDEVICE, "hipfft Z2D %d x %d (batch %d): error %d", m, m, batch, (int)r);
+    return DSP_OK;
+}
+
+// Validation shared by the passes over G.
+static dsp_status check_pass_args(const dsp_scan *scan, const dsp_optics *optics, int n_bf, const double *coords,
+                                  const double *weights) {
+    dsp_status st;
+    if ((st = check_scan(scan)) || (st = check_optics(optics))) return st;
+    if (n_bf <= 0 || !coords) return fail(DSP_EINVAL, "n_bf must be > 0 with bf_coords");
+    for (int i = 0; i < 2 * n_bf; ++i)
+        if (!std::isfinite(coords[i])) return fail(DSP_EINVAL, "bf_coords[%d] not finite", i / 2);
+    if (weights)
+        for (int i = 0; i < n_bf; ++i)
+            if (!(weights[i] >= 0.0) || !std::isfinite(weights[i]))
+                return fail(DSP_EINVAL, "weights[%d] must be finite and >= 0", i);
+    return DSP_OK;
+}
+
+static SsbKey pass_key(int device, const dsp_scan *scan, const dsp_optics *o, int n_bf, const double *coords,
+                       const double *weights) {
+    SsbKey key;
+    key.device = device;
+    key.n_scan = scan->n_scan;
+    key.step = scan->step_A;
+    key.soft = o->soft_aperture;
+    key.lam = o->wavelength_A;
+    key.alpha = o->semiangle_rad;
+    key.dk = o->det_step_invA;
+    key.n_bf = n_bf;
+    key.coords.assign(coords, coords + 2 * (size_t)n_bf);
+    if (weights) key.weights.assign(weights, weights + n_bf);
+    return key;
+}
+
 static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const float *gscale_dev, int n_bf,
                            const double *bf_coords_host, const double *weights_host, const dsp_scan *scan,
                            const dsp_optics *sets_host, int B, const double *band_invA, void *S_out_c128_dev,
@@ -1542,43 +1676,10 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
     double *d_tile_part = cv.take<double>((size_t)n_tiles * stride);
     double *d_E = cv.take<double>(B + 1);
 
-    const ApertureDev apd = make_aperture_dev(sets_host);
-    SsbParams sp;
-    std::memset(&sp, 0, sizeof sp);
-    for (int b = 0; b < B; ++b) {
-        const OpticsDev od = make_optics_dev(sets_host + b);
-        // a(k) once (set 0 writes it), chi(k) per set
-        if (b == 0) HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, od, nullptr, 0, nullptr, stream));
-        HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, od, d_chi + b, MAX_SETS_DEV, nullptr, stream));
-        sp.tau_y[b] = od.tau_y;
-        sp.tau_x[b] = od.tau_x;
-        sp.pt2[b] = od.pt2;
-        std::memcpy(sp.chi_c[b], od.chi_c, sizeof od.chi_c);
-    }
-    sp.G = (const float2 *)G_c64_dev;
-    sp.GQ = (const short2 *)GQ_dev;
-    sp.gscale = gscale_dev;
-    sp.plane = (long long)plane;
-    sp.pix = d_pix;
-    sp.goff = L.d_goff;
-    sp.chi_tab = d_chi;
-    sp.n_pix = n_pix;
-    sp.tiles = L.d_tiles;
-    sp.N = N;
-    sp.nh = nh;
-    sp.dq = dq;
-    sp.ldq = sets_host[0].wavelength_A * dq;
-    sp.B = B;
-    sp.ap = apd;
-    sp.lam = sets_host[0].wavelength_A;
-    sp.S_out = (double2 *)S_out_c128_dev;
-    sp.N_out = norm_out_dev;
-    sp.wbegin = L.d_wbegin[mi];
-    sp.seg_off = L.d_seg_off[mi];
-    sp.seg_first = L.d_seg_first[mi];
-    sp.partial = d_part;
-    if ((st = trig_table_device(device, &sp.trig))) return st;
-    HIP_TRY(launch_ssb(sp, L.waves[mi], n_tiles, d_tile_part, stream));
+    SsbPassBufs bufs{d_pix, d_chi, d_part, d_tile_part};
+    if ((st = ssb_pass(L, sets_host, B, G_c64_dev, GQ_dev, gscale_dev, N, N, (double2 *)S_out_c128_dev, norm_out_dev,
+                       bufs, device, stream)))
+        return st;
     std::vector<double> E(B + 1, 0.0);
     if (agreement_out_host) {
         HIP_TRY(launch_agreement(d_tile_part, n_tiles, B, d_E, stream));
@@ -1608,6 +1709,57 @@ dsp_status dsp_ssb_herm16(const void *Q_i16_dev, const float *scale_dev, int n_b
     if (!Q_i16_dev || !scale_dev) return fail(DSP_EINVAL, "Q and scale must be non-NULL");
     return ssb_impl(nullptr, Q_i16_dev, scale_dev, n_bf, bf_coords_host, weights_host, scan, sets_host, B, band_invA,
                     S_out_c128_dev, norm_out_dev, agreement_out_host, hip_stream);
+}
+
+dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
+                       const dsp_scan *scan, const dsp_optics *optics, int upsampling, void *spec_out_c128_dev,
+                       double *phase_out_dev, void *hip_stream) {
+    dsp_status st;
+    if ((st = check_pass_args(scan, optics, n_bf, bf_coords_host, weights_host))) return st;
+    if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
+    if (upsampling < 1 || upsampling > 4) return fail(DSP_EUNSUPPORTED, "upsampling %d not in 1..4", upsampling);
+    if (!spec_out_c128_dev && !phase_out_dev) return fail(DSP_EINVAL, "no output requested");
+    hipStream_t stream = (hipStream_t)hip_stream;
+    const int N = scan->n_scan, M = upsampling * N, mh = M / 2 + 1;
+    const long long n_half = (long long)M * mh;
+    int device = 0;
+    HIP_TRY(hipGetDevice(&device));
+    SsbKey key = pass_key(device, scan, optics, n_bf, bf_coords_host, weights_host);
+    key.up = upsampling;
+    key.preview = 1;
+    std::shared_ptr<SsbLayout> lay;
+    if ((st = get_ssb_layout(key, optics, bf_coords_host, weights_host, lay))) return st;
+    const SsbLayout &L = *lay;
+    const int n_tiles = (int)L.tiles.size();
+    const int n_pix = (int)L.act.pix.size();
+    const int mi = maxb_index(ssb_maxb(1));
+    const size_t n_part = (size_t)L.n_segs[mi] * ssb_nacc(1) * 64;
+    const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) +
+                        carve_size(n_part, sizeof(double)) +
+                        carve_size((size_t)std::max(1, n_tiles) * ssb_partial_stride(1), sizeof(double)) +
+                        carve_size((size_t)n_half, sizeof(double2)) + carve_size(1, sizeof(double2));
+    char *scr = nullptr;
+    if ((st = arena_get(device, stream, need, &scr))) return st;
+    Carve cv{scr};
+    SsbPassBufs bufs;
+    bufs.pix = cv.take<PixelRec>(n_pix);
+    bufs.chi = cv.take<double>((size_t)MAX_SETS_DEV * n_pix);
+    bufs.part = cv.take<double>(n_part);
+    bufs.tile_part = cv.take<double>((size_t)std::max(1, n_tiles) * ssb_partial_stride(1));
+    double2 *d_S = cv.take<double2>((size_t)n_half);
+    double2 *d_dc = cv.take<double2>(1);
+    // S on the fine half plane (zero where no lane runs: K = 0 and beyond reach)
+    HIP_TRY(launch_fill_zero((double *)d_S, (size_t)n_half * 2, stream));
+    if (n_tiles > 0 &&
+        (st = ssb_pass(L, optics, 1, G_c64_dev, nullptr, nullptr, N, M, d_S, nullptr, bufs, device, stream)))
+        return st;
+    HIP_TRY(launch_preview_dc(L.d_pixbase, L.d_goff, n_pix, (const float2 *)G_c64_dev, d_dc, stream));
+    if (spec_out_c128_dev) HIP_TRY(launch_preview_spectrum(d_S, d_dc, n_half, (double2 *)spec_out_c128_dev, stream));
+    if (phase_out_dev) {
+        if ((st = fft_z2d(device, M, 1, d_S, phase_out_dev, stream))) return st;
+        HIP_TRY(launch_preview_phase(phase_out_dev, (long long)M * M, d_dc, stream));
+    }
+    return DSP_OK;
 }
 
 dsp_status dsp_quantize_herm16(const void *G_c64_dev, int n_bf, int n_scan, void *Q_i16_dev, float *scale_dev,

@@ -275,6 +275,7 @@ struct SsbParams {
     int n_pix;
     const SsbTile *tiles;
     int N, nh;
+    int M, mh;               // output grid: lanes hold fine frequencies K of the (M, mh) half plane, M = u N
     double dq;
     double ldq;              // lambda dq
     int B;

@@ -1085,12 +1085,21 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
         const int p0 = (int)(it - (long long)t * n_pix);
         const int p1 = (int)((end - it) < (n_pix - p0) ? p0 + (end - it) : n_pix);
         const SsbTile *tile = prm.tiles + t;
-        const int yh = tile->lyh[lane];
+        const int yh = tile->lyh[lane];   // the lane's frequency K (fine grid; the stored q when M = N)
         const int ix = tile->lix[lane];
         const bool valid = (tile->valid >> lane) & 1ull;
-        const int iy = yh < 0 ? yh + prm.N : yh;
-        const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
-        const double qy = (double)yh * prm.ldq, qx = (double)ix * prm.ldq;   // lambda q
+        // G at q = K mod N from the stored half plane: G(-q) = conj G(q) where
+        // q's column exceeds N/2 (never when M = N)
+        int iyq = yh % prm.N;
+        if (iyq < 0) iyq += prm.N;
+        int ixq = ix % prm.N;
+        const bool cj = ixq > prm.N / 2;
+        if (cj) {
+            iyq = iyq == 0 ? 0 : prm.N - iyq;
+            ixq = prm.N - ixq;
+        }
+        const long long lane_off = valid ? (long long)iyq * prm.nh + ixq : 0;
+        const double qy = (double)yh * prm.ldq, qx = (double)ix * prm.ldq;   // lambda K
         const double q2 = fma(qy, qy, qx * qx);
 
         double acc[NACC];
@@ -1137,6 +1146,7 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                         gre = (double)ga[k].x;
                         gim = (double)ga[k].y;
                     }
+                    if (cj) gim = -gim;
                     if (r >= cn) gre = gim = 0.0;
                     const double *chi0s = schi + r;
                     // one pixel's update (kept in the kernel body: the sets' chi
@@ -1263,6 +1273,53 @@ __global__ __launch_bounds__(256) void herm16_pack_kernel(const float2 *G, long 
     }
 }
 
+// ---------------------------------------------------------------------------
+// preview: DC term, spectrum and phase image
+// ---------------------------------------------------------------------------
+// dc = sum_k w_k G(0, k) over the active pixels: thread t adds pixels t,
+// t + 256, ... in order, then a fixed tree (one block; deterministic).
+__global__ __launch_bounds__(256) void preview_dc_kernel(const PixelBase *pix, const long long *goff, int n_pix,
+                                                          const float2 *G, double2 *dc) {
+    __shared__ double sr[256], si[256];
+    double ar = 0.0, ai = 0.0;
+    for (int p = threadIdx.x; p < n_pix; p += 256) {
+        const float2 g = G[goff[p]];
+        ar = fma(pix[p].w, (double)g.x, ar);
+        ai = fma(pix[p].w, (double)g.y, ai);
+    }
+    sr[threadIdx.x] = ar;
+    si[threadIdx.x] = ai;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) {
+            sr[threadIdx.x] += sr[threadIdx.x + h];
+            si[threadIdx.x] += si[threadIdx.x + h];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) dc[0] = make_double2(sr[0], si[0]);
+}
+
+// P(K) = i S(K) for K != 0, P(0) = dc (grid-stride over the half plane).
+__global__ __launch_bounds__(256) void preview_spectrum_kernel(const double2 *S, const double2 *dc, long long n,
+                                                                double2 *P) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+        const double2 v = S[e];
+        P[e] = e == 0 ? dc[0] : make_double2(-v.y, v.x);
+    }
+}
+
+// img[r] holds sum_{K != 0} S(K) e^{2 pi i K.r / M} (the unnormalized
+// inverse real transform); the object is M^2 o(r) = dc + i img[r], so its
+// phase is atan2(img[r] + Im dc, Re dc).
+__global__ __launch_bounds__(256) void preview_phase_kernel(double *img, long long n, const double2 *dc) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    const double2 d = dc[0];
+    for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride)
+        img[e] = atan2(img[e] + d.y, d.x);
+}
+
 // Per band tile: the reduced sums -> S, N outputs and the tile's agreement
 // partials (|S_b|^2 / N_b and P summed over the lanes by a fixed tree).
 template <int MAXB>
@@ -1274,10 +1331,10 @@ __global__ __launch_bounds__(64) void ssb_write_kernel(SsbParams prm, double *ti
     const int yh = tile->lyh[lane];
     const int ix = tile->lix[lane];
     const bool valid = (tile->valid >> lane) & 1ull;
-    const int iy = yh < 0 ? yh + prm.N : yh;
-    const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
+    const int iy = yh < 0 ? yh + prm.M : yh;
+    const long long lane_off = valid ? (long long)iy * prm.mh + ix : 0;
     const double *pi = prm.partial + (size_t)prm.seg_first[t] * (NACC * 64);
-    const size_t plane = (size_t)prm.N * prm.nh;
+    const size_t plane = (size_t)prm.M * prm.mh;
     double part[MAXB + 1];
 #pragma unroll
     for (int b = 0; b < MAXB; ++b) {
@@ -1540,6 +1597,30 @@ hipError_t launch_herm16(const float2 *G, int n_bf, long long plane, short2 *Q, 
     const long long n = (long long)n_bf * plane;
     const long long blocks = (n + 255) / 256;
     herm16_pack_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, st>>>(G, plane, n, scale, Q);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+static unsigned grid_blocks(long long n) {
+    const long long b = (n + 255) / 256;
+    return (unsigned)(b < 65536 ? (b > 0 ? b : 1) : 65536);
+}
+
+hipError_t launch_preview_dc(const PixelBase *pix, const long long *goff, int n_pix, const float2 *G, double2 *dc,
+                             hipStream_t st) {
+    preview_dc_kernel<<<1, 256, 0, st>>>(pix, goff, n_pix, G, dc);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_preview_spectrum(const double2 *S, const double2 *dc, long long n, double2 *P, hipStream_t st) {
+    preview_spectrum_kernel<<<grid_blocks(n), 256, 0, st>>>(S, dc, n, P);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_preview_phase(double *img, long long n, const double2 *dc, hipStream_t st) {
+    preview_phase_kernel<<<grid_blocks(n), 256, 0, st>>>(img, n, dc);
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }

@@ -61,6 +61,10 @@ int ssb_nacc(int maxb);              // doubles per lane of one SSB partial sum
 hipError_t ssb_occupancy(int maxb, int *blocks_per_cu);
 // SSB kernel over n_waves stream-K ranges, then per-tile reduction and
 // write-out; tile_part receives [n_tiles][MAXB + 1] agreement partials.
+hipError_t launch_preview_dc(const PixelBase *pix, const long long *goff, int n_pix, const float2 *G, double2 *dc,
+                             hipStream_t st);
+hipError_t launch_preview_spectrum(const double2 *S, const double2 *dc, long long n, double2 *P, hipStream_t st);
+hipError_t launch_preview_phase(double *img, long long n, const double2 *dc, hipStream_t st);
 hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *tile_part, hipStream_t st);
 int ssb_partial_stride(int B);
 hipError_t launch_agreement(const double *partial, int n_tiles, int B, double *E, hipStream_t st);

@@ -538,6 +538,95 @@ def test_ssb_herm16_tiny_band_weighted():
     assert np.allclose(E, O.agreement(S_o, N_o, power), rtol=1e-6, atol=0)
 
 
+# ----------------------------------------------------------------------------
+# previews
+# ----------------------------------------------------------------------------
+
+
+def _preview_case(w, G_np, k, wts, optics, u, check_phase=True):
+    _say(f"preview {w.name} N={w.n_scan} u={u} n_bf={len(k)} depth={optics.depth}")
+    G_dev = torch.as_tensor(G_np, device=DEV)
+    P, ph = dsp.preview(G_dev, k, optics, step=w.step, upsampling=u, weights=wts)
+    torch.cuda.synchronize()
+    P = P.cpu().numpy()
+    ph = ph.cpu().numpy()
+    P_o = O.preview_spectrum(G_np.astype(np.complex128), k, wts, w.n_scan, w.step, u, optics)
+    scale = np.abs(P_o[1:]).max() if P_o.shape[0] > 1 else 1.0
+    glob = np.linalg.norm(P[1:] - P_o[1:]) / np.linalg.norm(P_o[1:])
+    assert glob <= X_TOL, f"spectrum rel err {glob:.3e}"
+    assert np.max(np.abs(P - P_o)[1:] / np.maximum(np.abs(P_o[1:]), 1e-3 * scale)) <= X_TOL
+    assert abs(P[0, 0] - P_o[0, 0]) <= 1e-12 * abs(P_o[0, 0])
+    if check_phase:
+        ph_o = O.preview_phase(P_o)
+        assert np.max(np.abs(ph - ph_o)) <= 1e-6
+        assert np.std(ph_o) > 1e-4
+    return P, ph, P_o
+
+
+@pytest.mark.parametrize("u", [1, 2, 3])
+def test_preview_tiny_full(u):
+    """Every entry of the fine half plane and the phase image, ragged sizes
+    (N = 12: N/2 + 1 = 7 stored columns), tilt and 14 aberration terms,
+    weights, depth on the 3x grid."""
+    w = _tiny()
+    pix, k = bf_pixels(w)
+    G = data_stack_numpy(w, pix)
+    opt = w.optics.replace(depth=90.0) if u == 3 else w.optics
+    _preview_case(w, G, k, random_weights(len(k), 5 + u), opt, u)
+
+
+def test_preview_c1_and_c2():
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    _preview_case(w, data_stack_numpy(w, pix), k, None, w.optics, 1)
+    w = workload("c2")
+    pix, k = bf_pixels(w)
+    _preview_case(w, data_stack_numpy(w, pix), k, random_weights(len(k), 8), w.optics, 2)
+
+
+def test_preview_c4_sampled_3x():
+    """Full frame on the 3x grid (1536 x 769): sampled fine entries against the
+    oracle's corrected sums, the DC term, and the phase image against the
+    oracle's inverse transform of the library's own spectrum."""
+    w = workload("c4")
+    pix, k = bf_pixels(w)
+    _say("generating full-frame G (9298, 512, 257) on the GPU")
+    G = data_stack_torch(w, pix, DEV)
+    u, n = 3, w.n_scan
+    m = u * n
+    P, ph = dsp.preview(G, k, w.optics, step=w.step, upsampling=u)
+    torch.cuda.synchronize()
+    P = P.cpu().numpy()
+    ph = ph.cpu().numpy()
+    act = O.active_pixels(k, w.optics)
+    rng = np.random.default_rng(9)
+    dq = O.scan_frequency_step(n, w.step)
+    R = O.alias_radius(w.optics)
+    picks = []
+    while len(picks) < 40:
+        iy, ix = int(rng.integers(0, m)), int(rng.integers(0, m // 2 + 1))
+        Ky = int(O.signed_index(iy, m))
+        if (Ky, ix) != (0, 0) and math.hypot(Ky * dq, ix * dq) < R:
+            picks.append((iy, Ky, ix))
+    for iy, Ky, ix in picks:
+        q = ((Ky % n), (ix % n))
+        qm = ((-q[0]) % n, (-q[1]) % n)
+        need = sorted({q[0], qm[0]})
+        G_rows = G[:, torch.as_tensor(need, device=DEV)][torch.as_tensor(act, device=DEV)].cpu().numpy()
+        G_loc = np.zeros((len(act), n, n // 2 + 1), dtype=np.complex128)
+        for j, r in enumerate(need):
+            G_loc[:, r] = G_rows[:, j]
+        want = np.sum(O.corrected_term(k[act], np.ones(len(act)), G_loc, Ky, ix, n, w.step, w.optics))
+        assert abs(P[iy, ix] - want) <= X_TOL * max(abs(want), 1e-3 * np.abs(P).max()), (Ky, ix)
+    dc = np.sum(G[torch.as_tensor(act, device=DEV), 0, 0].cpu().numpy().astype(np.complex128))
+    assert abs(P[0, 0] - dc) <= 1e-12 * abs(dc)
+    assert not np.any(P[np.hypot(O.signed_index(np.arange(m), m)[:, None] * dq,
+                                 np.arange(m // 2 + 1)[None, :] * dq) >= R * 1.001])
+    assert np.max(np.abs(ph - O.preview_phase(P))) <= 1e-9
+    del G
+    torch.cuda.empty_cache()
+
+
 def test_ssb_equals_prepare_at_u1():
     """The two paths agree with each other at one alias per frequency,
     zero strength and no prior: S/N = x."""
