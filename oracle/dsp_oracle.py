@@ -566,7 +566,8 @@ def pixel_planes(G: np.ndarray, k: np.ndarray, w: Optional[np.ndarray], n_scan: 
     """Yields (w_k, C_k) for every active pixel: its corrected full (N, N)
     plane, the corrected terms at every q != 0 and w_k G(0, k) at DC ([P3]
     Changes, loss path: the corrected full plane straight from the stored
-    half plane)."""
+    half plane).  The Nyquist row and column are 0, as in the preview
+    (index N/2 stands for +-N/2 dq)."""
     act = active_pixels(k, optics)
     ka = k[act]
     wa = np.ones(len(act)) if w is None else np.asarray(w, dtype=np.float64)[act]
@@ -583,6 +584,8 @@ def pixel_planes(G: np.ndarray, k: np.ndarray, w: Optional[np.ndarray], n_scan: 
         L, R = lobes(np.full(QY.shape, ka[j, 0]), np.full(QY.shape, ka[j, 1]), QY, QX, optics)
         C = 1j * wa[j] * np.conj(1j * (L - R)) * gfull
         C[0, 0] = wa[j] * gfull[0, 0]
+        C[n // 2, :] = 0.0
+        C[:, n // 2] = 0.0
         yield float(wa[j]), C
 
 

@@ -481,8 +481,13 @@ def test_fast_path_identity_and_single_pixel_loss():
     objs = [np.fft.ifft2(C) for _, C in O.pixel_planes(G, k, w, n, step, opt)]
     fast = O.preview_phase(O.preview_spectrum(G, k, w, n, step, 1, opt))
     assert np.max(np.abs(np.angle(np.sum(objs, axis=0)) - fast)) <= 1e-12
-    # explicit DFT of one pixel's plane
+    # explicit DFT of one pixel's plane; the plane is anti-Hermitian off DC,
+    # so its object is C(0) / N^2 + i (a real image)
     _, C0 = next(iter(O.pixel_planes(G, k, w, n, step, opt)))
+    mirror = -np.conj(C0[(-np.arange(n)) % n][:, (-np.arange(n)) % n])
+    mirror[0, 0] = C0[0, 0]
+    assert np.allclose(C0, mirror, rtol=0, atol=1e-12 * np.abs(C0).max())
+    assert np.allclose(objs[0].real, C0[0, 0].real / n ** 2, rtol=0, atol=1e-12 * np.abs(objs[0]).max())
     r = np.arange(n)
     E = np.exp(2j * math.pi * np.outer(r, r) / n)
     brute = (E @ C0 @ E.T) / (n * n)
