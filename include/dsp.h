@@ -319,6 +319,29 @@ dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_
                        const dsp_scan *scan, const dsp_optics *optics, int upsampling, void *spec_out_c128_dev,
                        double *phase_out_dev, void *hip_stream);
 
+/* Loss path: every active pixel's own object and their phase moments
+ * ("Tilt-corrected SSB on CUDA: fit and preview speed", section "Changes",
+ * loss path: each pixel's corrected full plane straight from its stored half
+ * plane, an unscaled inverse FFT, and phase moments reduced as the angles are
+ * read; "Historical WebGPU G(q,k) memory experiment", section "Object-redraw
+ * fast path": mean(angle(object)) needs the per-pixel phases).  Pixel k's
+ * corrected plane is C_k(q) = i w_k conj(Gamma(q, k)) G(q, k) for q != 0
+ * (zero on the Nyquist row and column) and w_k G(0, k) at DC; its object
+ * o_k = ifft2(C_k) and theta_k = angle(o_k).  Outputs:
+ *   mean_phase_out_dev: [N][N] float64 sum_k w_k theta_k / sum_k w_k, or NULL;
+ *   loss_out_host: the mean over the scan of sum_k w_k (theta_k - mean)^2 /
+ *       sum_k w_k, or NULL (non-NULL synchronizes the stream).
+ * Arguments as dsp_preview (u = 1).  G's self-conjugate column (ix = 0)
+ * should hold conjugate pairs G(-q) = conj G(q), as a real transform gives;
+ * where rounding breaks them, the inverse real FFT uses their Hermitian
+ * part.  The inverse FFTs are hipFFT's batched
+ * Z2D over chunks of pixels (about 1 GB of planes per batch, from the
+ * stream's arena; plans kept until the process ends).  DSP_EINVAL for bad
+ * arguments or weights summing to zero, DSP_EDEVICE for a hipFFT failure. */
+dsp_status dsp_loss(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
+                    const dsp_scan *scan, const dsp_optics *optics, double *mean_phase_out_dev, double *loss_out_host,
+                    void *hip_stream);
+
 /* The phase differences of the transfer's two lobes as the Gram kernels form
  * them (the same source: chi expanded about theta(k) = lambda k + tau, one
  * evaluation of its even and odd parts in d = lambda Q for both lobes),

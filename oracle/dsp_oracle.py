@@ -576,11 +576,14 @@ def pixel_planes(G: np.ndarray, k: np.ndarray, w: Optional[np.ndarray], n_scan: 
     dq = scan_frequency_step(n, step)
     yy = signed_index(np.arange(n), n).astype(np.float64)
     QY, QX = np.meshgrid(yy * dq, yy * dq, indexing="ij")     # full-plane signed frequencies
+    iy = np.arange(n)[:, None]
+    ix = np.arange(n)[None, :]
+    direct = np.broadcast_to(ix <= n // 2, (n, n))
+    src_y = np.where(direct, iy, (-iy) % n)       # G(-q) = conj G(q) beyond column N/2
+    src_x = np.where(direct, ix, n - ix)
     for j in range(len(act)):
-        gfull = np.zeros((n, n), dtype=np.complex128)
-        for iy in range(n):
-            for ix in range(n):
-                gfull[iy, ix] = g_full(Ga[j:j + 1], iy, ix, n)[0]
+        gfull = np.asarray(Ga[j], dtype=np.complex128)[src_y, src_x]
+        gfull = np.where(direct, gfull, np.conj(gfull))
         L, R = lobes(np.full(QY.shape, ka[j, 0]), np.full(QY.shape, ka[j, 1]), QY, QX, optics)
         C = 1j * wa[j] * np.conj(1j * (L - R)) * gfull
         C[0, 0] = wa[j] * gfull[0, 0]

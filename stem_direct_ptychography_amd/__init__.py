@@ -25,7 +25,7 @@ from . import _lib
 
 _L = _lib.load()
 
-__all__ = ["DspError", "Prepared", "prepare", "ssb", "preview", "quantize_herm16", "geometry_counts", "alias_geometry", "active_bf",
+__all__ = ["DspError", "Prepared", "prepare", "ssb", "preview", "loss", "quantize_herm16", "geometry_counts", "alias_geometry", "active_bf",
            "band_count", "chi_host", "chi_shift_host", "sincos_host", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -270,6 +270,24 @@ def preview(G, bf_coords, optics, step: float, upsampling: int = 1, weights=None
                           ctypes.c_void_p(ph.data_ptr()) if ph is not None else None,
                           ctypes.c_void_p(_stream(stream))))
     return P, ph
+
+
+def loss(G, bf_coords, optics, step: float, weights=None, mean_phase: bool = True, stream=None):
+    """Loss path (dsp_loss): returns (mean phase (N, N) float64 on G's device
+    or None, loss float)."""
+    torch = _torch()
+    n = _check_G(G)
+    k = _coords(bf_coords)
+    if k.shape[0] != G.shape[0]:
+        raise DspError(_lib.DSP_EINVAL, "bf_coords rows must match G's first axis")
+    w = _weights(weights, k.shape[0])
+    mp = torch.empty((n, n), dtype=torch.float64, device=G.device) if mean_phase else None
+    out = np.zeros(1, dtype=np.float64)
+    scan = _lib.ScanC(n, float(step))
+    _check(_L.dsp_loss(ctypes.c_void_p(G.data_ptr()), k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan),
+                       ctypes.byref(_optics(optics)), ctypes.c_void_p(mp.data_ptr()) if mp is not None else None,
+                       _dptr(out), ctypes.c_void_p(_stream(stream))))
+    return mp, float(out[0])
 
 
 def _check_Q(Q, scale):

@@ -1762,6 +1762,79 @@ dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_
     return DSP_OK;
 }
 
+dsp_status dsp_loss(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
+                    const dsp_scan *scan, const dsp_optics *optics, double *mean_phase_out_dev, double *loss_out_host,
+                    void *hip_stream) {
+    dsp_status st;
+    if ((st = check_pass_args(scan, optics, n_bf, bf_coords_host, weights_host))) return st;
+    if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
+    if (!mean_phase_out_dev && !loss_out_host) return fail(DSP_EINVAL, "no output requested");
+    hipStream_t stream = (hipStream_t)hip_stream;
+    const int N = scan->n_scan, nh = N / 2 + 1;
+    const long long plane = (long long)N * nh, nn = (long long)N * N;
+    int device = 0;
+    HIP_TRY(hipGetDevice(&device));
+    std::shared_ptr<SsbLayout> lay;
+    if ((st = get_ssb_layout(pass_key(device, scan, optics, n_bf, bf_coords_host, weights_host), optics,
+                             bf_coords_host, weights_host, lay)))
+        return st;
+    const SsbLayout &L = *lay;
+    const int n_pix = (int)L.act.pix.size();
+    double W = 0.0;
+    for (const PixelBase &p : L.act.pix) W += p.w;
+    if (!(W > 0.0)) return fail(DSP_EINVAL, "the active pixels' weights sum to zero");
+    // chunk of pixels per inverse-FFT batch: about 1 GB of planes
+    const size_t per_pix = (size_t)plane * sizeof(double2) + (size_t)nn * sizeof(double);
+    const int CH = (int)std::max<size_t>(1, std::min<size_t>(256, ((size_t)1 << 30) / per_pix));
+    const int nb = loss_blocks(nn);
+    const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)CH * plane, sizeof(double2)) +
+                        carve_size((size_t)CH * nn, sizeof(double)) + carve_size(CH, sizeof(double2)) +
+                        2 * carve_size((size_t)nn, sizeof(double)) + carve_size(nb, sizeof(double)) +
+                        carve_size(1, sizeof(double));
+    char *scr = nullptr;
+    if ((st = arena_get(device, stream, need, &scr))) return st;
+    Carve cv{scr};
+    PixelRec *d_pix = cv.take<PixelRec>(n_pix);
+    double2 *d_H = cv.take<double2>((size_t)CH * plane);
+    double *d_img = cv.take<double>((size_t)CH * nn);
+    double2 *d_D = cv.take<double2>(CH);
+    double *d_s1 = cv.take<double>((size_t)nn);
+    double *d_s2 = cv.take<double>((size_t)nn);
+    double *d_part = cv.take<double>(nb);
+    double *d_loss = cv.take<double>(1);
+    const ApertureDev apd = make_aperture_dev(optics);
+    const OpticsDev opd = make_optics_dev(optics);
+    HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, opd, nullptr, 0, nullptr, stream));
+    HIP_TRY(launch_fill_zero(d_s1, (size_t)nn, stream));
+    HIP_TRY(launch_fill_zero(d_s2, (size_t)nn, stream));
+    CorrParams cp;
+    std::memset(&cp, 0, sizeof cp);
+    cp.G = (const float2 *)G_c64_dev;
+    cp.N = N;
+    cp.nh = nh;
+    cp.ldq = optics->wavelength_A / (N * scan->step_A);
+    cp.ap = apd;
+    cp.op = opd;
+    cp.H = d_H;
+    cp.D = d_D;
+    if ((st = trig_table_device(device, &cp.trig))) return st;
+    for (int c0 = 0; c0 < n_pix; c0 += CH) {
+        const int cn = std::min(CH, n_pix - c0);
+        cp.pix = d_pix + c0;
+        cp.goff = L.d_goff + c0;
+        cp.n_valid = cn;
+        HIP_TRY(launch_corrected_half(cp, CH, stream));
+        if ((st = fft_z2d(device, N, CH, d_H, d_img, stream))) return st;
+        HIP_TRY(launch_phase_moments(d_img, d_D, L.d_pixbase + c0, cn, nn, d_s1, d_s2, stream));
+    }
+    HIP_TRY(launch_loss(d_s1, d_s2, nn, W, mean_phase_out_dev, d_part, d_loss, stream));
+    if (loss_out_host) {
+        HIP_TRY(hipMemcpyAsync(loss_out_host, d_loss, sizeof(double), hipMemcpyDeviceToHost, stream));
+        HIP_TRY(hipStreamSynchronize(stream));
+    }
+    return DSP_OK;
+}
+
 dsp_status dsp_quantize_herm16(const void *G_c64_dev, int n_bf, int n_scan, void *Q_i16_dev, float *scale_dev,
                                void *hip_stream) {
     if (!G_c64_dev || !Q_i16_dev || !scale_dev) return fail(DSP_EINVAL, "G, Q and scale must be non-NULL");

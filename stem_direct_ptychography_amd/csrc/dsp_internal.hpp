@@ -293,4 +293,19 @@ struct SsbParams {
     const double2 *trig;     // [TRIG_N] (cos, sin)(j pi / 32)
 };
 
+// Loss path: corrected half planes of a chunk of pixels.
+struct CorrParams {
+    const float2 *G;
+    const PixelRec *pix;       // the chunk's records
+    const long long *goff;     // the chunk's plane offsets
+    int n_valid;               // pixels in the chunk (planes beyond are zero)
+    int N, nh;
+    double ldq;                // lambda dq
+    ApertureDev ap;
+    OpticsDev op;
+    const double2 *trig;
+    double2 *H;                // [chunk][N][nh] conj(Gamma') G, Gamma' = sqrt(w) Gamma
+    double2 *D;                // [chunk] sqrt(w) G(0, k)
+};
+
 }  // namespace dsp

@@ -22,6 +22,7 @@
 #include "dsp_kernels.hpp"
 
 #include <cstring>
+#include <algorithm>
 #include <type_traits>
 
 namespace dsp {
@@ -1320,6 +1321,135 @@ __global__ __launch_bounds__(256) void preview_phase_kernel(double *img, long lo
         img[e] = atan2(img[e] + d.y, d.x);
 }
 
+// ---------------------------------------------------------------------------
+// loss path: per-pixel corrected planes, phase moments
+// ---------------------------------------------------------------------------
+// Block (x, j): 256 stored frequencies q of chunk pixel j.  Pixel k's object
+// is C_k(0) + i (inverse real transform of H_k) up to the positive factor
+// sqrt(w_k), which the phase does not see: H_k(q) = conj(Gamma'(q, k)) G(q, k)
+// with Gamma' = sqrt(w) Gamma = i (L - R) built on amp0 = sqrt(w) a(k), and
+// D_k = sqrt(w) G(0, k).  H is 0 at DC and on the Nyquist row and column.
+__global__ __launch_bounds__(256) void corrected_half_kernel(CorrParams prm) {
+    __shared__ double2 T[TRIG_N];
+    if (threadIdx.x < TRIG_N) T[threadIdx.x] = prm.trig[threadIdx.x];
+    __syncthreads();
+    const int j = blockIdx.y;
+    const int N = prm.N, nh = prm.nh;
+    const long long plane = (long long)N * nh;
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= plane) return;
+    double2 *Hj = prm.H + (size_t)j * plane;
+    if (j >= prm.n_valid) {
+        Hj[e] = make_double2(0.0, 0.0);
+        if (e == 0) prm.D[j] = make_double2(0.0, 0.0);
+        return;
+    }
+    const PixelRec rec = prm.pix[j];
+    const float2 gv = prm.G[prm.goff[j] + e];
+    const int iy = (int)(e / nh), ix = (int)(e - (long long)iy * nh);
+    if (e == 0) prm.D[j] = make_double2(rec.sw * (double)gv.x, rec.sw * (double)gv.y);
+    if (e == 0 || iy == N / 2 || ix == N / 2) {
+        Hj[e] = make_double2(0.0, 0.0);
+        return;
+    }
+    const int yh = iy < N / 2 ? iy : iy - N;
+    const double qy = (double)yh * prm.ldq, qx = (double)ix * prm.ldq;   // lambda q
+    const double lky = rec.lky, lkx = rec.lkx;
+    const double lk2 = fma(lky, lky, lkx * lkx);
+    const double q2 = fma(qy, qy, qx * qx);
+    const double kq = fma(lky, qy, lkx * qx);
+    const double base = lk2 + q2;
+    const double dm2 = fma(-2.0, kq, base), dp2 = fma(2.0, kq, base);
+    const bool zl = dm2 < prm.ap.lrlim2, zr = dp2 < prm.ap.lrlim2;
+    const double py = lky + prm.op.tau_y, px = lkx + prm.op.tau_x;   // theta(k), as chi0 was formed
+    const bool depth = prm.op.pt2 != 0.0;
+    const double th0 = fma(px, px, py * py);
+    double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
+    if (zl) {
+        double a = rec.amp0;
+        if (dm2 > prm.ap.lrin2) a *= fma(prm.ap.lkc - sqrt(dm2), prm.ap.inv_ldk, 0.5);
+        const double ty = py - qy, tx = px - qx;
+        double arg = rec.chi0 - chi_poly(prm.op.chi_c, tx, ty);
+        if (depth) {
+            const double h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
+            arg += h;
+            a *= sinc_tab(h, T);
+        }
+        double sn, cs;
+        sincos_tab(arg, T, sn, cs);
+        Lr = a * cs;
+        Li = a * sn;
+    }
+    if (zr) {
+        double a = rec.amp0;
+        if (dp2 > prm.ap.lrin2) a *= fma(prm.ap.lkc - sqrt(dp2), prm.ap.inv_ldk, 0.5);
+        const double ty = py + qy, tx = px + qx;
+        double arg = rec.chi0 - chi_poly(prm.op.chi_c, tx, ty);
+        if (depth) {
+            const double h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
+            arg += h;
+            a *= sinc_tab(h, T);
+        }
+        double sn, cs;
+        sincos_tab(-arg, T, sn, cs);
+        Rr = a * cs;
+        Ri = a * sn;
+    }
+    const double gmr = Ri - Li, gmi = Lr - Rr;   // Gamma' = i (L - R)
+    const double gr = gv.x, gi = gv.y;
+    Hj[e] = make_double2(fma(gmr, gr, gmi * gi), fma(gmr, gi, -(gmi * gr)));
+}
+
+// r over the N^2 scan positions: theta_j = atan2(img_j[r] + Im D_j, Re D_j)
+// (img_j the unnormalized inverse real transform of H_j); s1 += w_j theta_j,
+// s2 += w_j theta_j^2 over the chunk's pixels in order.
+__global__ __launch_bounds__(256) void phase_moments_kernel(const double *img, const double2 *D, const PixelBase *pb,
+                                                            int cn, long long nn, double *s1, double *s2) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x; r < nn; r += stride) {
+        double a1 = s1[r], a2 = s2[r];
+        for (int j = 0; j < cn; ++j) {
+            const double2 d = D[j];
+            const double w = pb[j].w;
+            const double th = atan2(img[(size_t)j * nn + r] + d.y, d.x);
+            a1 = fma(w, th, a1);
+            a2 = fma(w * th, th, a2);
+        }
+        s1[r] = a1;
+        s2[r] = a2;
+    }
+}
+
+// mean = s1 / W, var = s2 / W - mean^2; block b writes the sum of var over
+// its positions (b, b + nblk, ... in 256-wide steps, fixed tree).
+__global__ __launch_bounds__(256) void loss_partial_kernel(const double *s1, const double *s2, long long nn, double W,
+                                                           double *mean_out, double *part) {
+    __shared__ double sh[256];
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    double acc = 0.0;
+    for (long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x; r < nn; r += stride) {
+        const double m = s1[r] / W;
+        if (mean_out) mean_out[r] = m;
+        acc += s2[r] / W - m * m;
+    }
+    sh[threadIdx.x] = acc;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) sh[threadIdx.x] += sh[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[blockIdx.x] = sh[0];
+}
+
+// loss = (sum of the blocks' sums, in block order) / nn
+__global__ void loss_final_kernel(const double *part, int nblk, long long nn, double *loss) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        double s = 0.0;
+        for (int b = 0; b < nblk; ++b) s += part[b];
+        loss[0] = s / (double)nn;
+    }
+}
+
 // Per band tile: the reduced sums -> S, N outputs and the tile's agreement
 // partials (|S_b|^2 / N_b and P summed over the lanes by a fixed tree).
 template <int MAXB>
@@ -1621,6 +1751,32 @@ hipError_t launch_preview_spectrum(const double2 *S, const double2 *dc, long lon
 
 hipError_t launch_preview_phase(double *img, long long n, const double2 *dc, hipStream_t st) {
     preview_phase_kernel<<<grid_blocks(n), 256, 0, st>>>(img, n, dc);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_corrected_half(const CorrParams &prm, int n_planes, hipStream_t st) {
+    const long long plane = (long long)prm.N * prm.nh;
+    corrected_half_kernel<<<dim3((unsigned)((plane + 255) / 256), (unsigned)n_planes), 256, 0, st>>>(prm);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+hipError_t launch_phase_moments(const double *img, const double2 *D, const PixelBase *pb, int cn, long long nn,
+                                double *s1, double *s2, hipStream_t st) {
+    phase_moments_kernel<<<grid_blocks(nn), 256, 0, st>>>(img, D, pb, cn, nn, s1, s2);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+int loss_blocks(long long nn) { return (int)std::min<long long>(1024, std::max<long long>(1, (nn + 255) / 256)); }
+
+hipError_t launch_loss(const double *s1, const double *s2, long long nn, double W, double *mean_out, double *part,
+                       double *loss, hipStream_t st) {
+    const int nb = loss_blocks(nn);
+    loss_partial_kernel<<<nb, 256, 0, st>>>(s1, s2, nn, W, mean_out, part);
+    DSP_CHECK_LAUNCH();
+    loss_final_kernel<<<1, 64, 0, st>>>(part, nb, nn, loss);
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }

@@ -65,6 +65,12 @@ hipError_t launch_preview_dc(const PixelBase *pix, const long long *goff, int n_
                              hipStream_t st);
 hipError_t launch_preview_spectrum(const double2 *S, const double2 *dc, long long n, double2 *P, hipStream_t st);
 hipError_t launch_preview_phase(double *img, long long n, const double2 *dc, hipStream_t st);
+hipError_t launch_corrected_half(const CorrParams &prm, int n_planes, hipStream_t st);
+hipError_t launch_phase_moments(const double *img, const double2 *D, const PixelBase *pb, int cn, long long nn,
+                                double *s1, double *s2, hipStream_t st);
+int loss_blocks(long long nn);
+hipError_t launch_loss(const double *s1, const double *s2, long long nn, double W, double *mean_out, double *part,
+                       double *loss, hipStream_t st);
 hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *tile_part, hipStream_t st);
 int ssb_partial_stride(int B);
 hipError_t launch_agreement(const double *partial, int n_tiles, int B, double *E, hipStream_t st);

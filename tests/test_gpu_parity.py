@@ -627,6 +627,87 @@ def test_preview_c4_sampled_3x():
     torch.cuda.empty_cache()
 
 
+# ----------------------------------------------------------------------------
+# loss path
+# ----------------------------------------------------------------------------
+
+
+def _loss_case(w, G_np, k, wts, optics):
+    _say(f"loss {w.name} N={w.n_scan} n_bf={len(k)} depth={optics.depth}")
+    mp, loss = dsp.loss(torch.as_tensor(G_np, device=DEV), k, optics, step=w.step, weights=wts)
+    torch.cuda.synchronize()
+    mp = mp.cpu().numpy()
+    mp_o, loss_o = O.loss_path(G_np.astype(np.complex128), k, wts, w.n_scan, w.step, optics)
+    assert np.max(np.abs(mp - mp_o)) <= 1e-9
+    assert loss == pytest.approx(loss_o, rel=1e-9, abs=1e-15)
+    return mp, loss
+
+
+def test_loss_tiny_and_c1():
+    """Ragged N = 12 with zero weights and depth, and c1 (hard aperture)."""
+    w = _tiny()
+    pix, k = bf_pixels(w)
+    G = data_stack_numpy(w, pix)
+    wts = random_weights(len(k), 21)
+    wts[::5] = 0.0
+    _, l1 = _loss_case(w, G, k, wts, w.optics)
+    _, l2 = _loss_case(w, G, k, None, w.optics.replace(depth=70.0))
+    assert l1 > 0 and l2 > 0
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    _loss_case(w, data_stack_numpy(w, pix), k, None, w.optics)
+
+
+def test_loss_c2():
+    """1005 pixels (several chunks' worth of planes per batch at 128 x 128)."""
+    w = workload("c2")
+    pix, k = bf_pixels(w)
+    _loss_case(w, data_stack_numpy(w, pix), k, random_weights(len(k), 22), w.optics)
+
+
+def test_loss_full_frame():
+    """512 x 512: 16 pixels of the full frame against the oracle; all 9298
+    pixels (37 batches of inverse FFTs) against two disjoint halves, whose
+    weighted moments combine exactly: mean = (W_a m_a + W_b m_b) / W and
+    loss = (W_a l_a + W_b l_b) / W + mean_r[(W_a m_a^2 + W_b m_b^2) / W - mean^2]."""
+    w = workload("c4")
+    pix, k = bf_pixels(w)
+    _say("generating full-frame G (9298, 512, 257) on the GPU")
+    G = data_stack_torch(w, pix, DEV)
+    act = O.active_pixels(k, w.optics)
+    rng = np.random.default_rng(31)
+    sub = np.sort(rng.choice(act, size=16, replace=False))
+    Gs = G[torch.as_tensor(sub, device=DEV)].contiguous()
+    # A real transform's column 0 holds conjugate pairs; the float32 transform
+    # that made this G misses them by rounding, and an inverse real FFT uses
+    # their Hermitian part where the oracle's complex one uses both values.
+    iy = torch.arange(1, w.n_scan // 2, device=DEV)
+    Gs[:, w.n_scan - iy, 0] = Gs[:, iy, 0].conj()
+    mp, loss = dsp.loss(Gs, k[sub], w.optics, step=w.step)
+    mp_o, loss_o = O.loss_path(Gs.cpu().numpy().astype(np.complex128), k[sub], None, w.n_scan, w.step, w.optics)
+    assert np.max(np.abs(mp.cpu().numpy() - mp_o)) <= 1e-9
+    assert loss == pytest.approx(loss_o, rel=1e-9)
+    wts = random_weights(len(k), 32)
+    m_all, l_all = dsp.loss(G, k, w.optics, step=w.step, weights=wts)
+    half = np.zeros(len(k), dtype=bool)
+    half[rng.choice(len(k), size=len(k) // 2, replace=False)] = True
+    parts = []
+    for sel in (half, ~half):
+        idx = torch.as_tensor(np.nonzero(sel)[0], device=DEV)
+        m, l = dsp.loss(G[idx].contiguous(), k[sel], w.optics, step=w.step, weights=wts[sel])
+        parts.append((float(np.sum(wts[sel & np.isin(np.arange(len(k)), act)])), m.cpu().numpy(), l))
+    (Wa, ma, la), (Wb, mb, lb) = parts
+    W = Wa + Wb
+    m_want = (Wa * ma + Wb * mb) / W
+    m_all = m_all.cpu().numpy()
+    assert np.max(np.abs(m_all - m_want)) <= 1e-9
+    l_want = (Wa * la + Wb * lb) / W + float(np.mean((Wa * ma ** 2 + Wb * mb ** 2) / W - m_want ** 2))
+    assert l_all == pytest.approx(l_want, rel=1e-9)
+    assert np.all(np.abs(m_all) <= math.pi) and l_all > 0
+    del G, Gs
+    torch.cuda.empty_cache()
+
+
 def test_ssb_equals_prepare_at_u1():
     """The two paths agree with each other at one alias per frequency,
     zero strength and no prior: S/N = x."""
