@@ -480,6 +480,30 @@ def main(argv=None) -> int:
         depth_ms[method + "_prepare_ms"] = float(np.median(ts))
     result["depth_124A"] = depth_ms
     log(f"depth 124 A prepares: {depth_ms}")
+    # previews (spectrum + phase image) at 1x and 3x and the loss path, outside the step
+    pv = {}
+    for u in (1, 3):
+        ts = []
+        for _ in range(4):
+            e0.record(stream)
+            P, ph = dsp.preview(G, k, w.optics, step=w.step, upsampling=u)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+            del P, ph
+        pv[f"preview_{u}x_ms"] = float(np.median(ts[1:]))
+    ts = []
+    for _ in range(3):
+        e0.record(stream)
+        mp, lv = dsp.loss(G, k, w.optics, step=w.step)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+        del mp
+    pv["loss_path_ms"] = float(np.median(ts[1:]))
+    pv["loss"] = lv
+    result["preview"] = pv
+    log(f"previews and loss path: {pv}")
     del step.last
     torch.cuda.synchronize()
 
