@@ -396,10 +396,15 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
         for (int d = c + 1; d < NC; ++d) {
             if (!(bal[c] & bal[d])) continue;
             if (GramLds<NJ, METHOD>::in_lds(c, d)) {
-                double2 v = lpair[GramLds<NJ, METHOD>::idx(c, d) * 64];
-                v.x = fma(tr[c], tr[d], fma(ti[c], ti[d], v.x));
-                v.y = fma(tr[c], ti[d], fma(-ti[c], tr[d], v.y));
-                lpair[GramLds<NJ, METHOD>::idx(c, d) * 64] = v;
+                // LDS FP64 atomic adds without return: the wave does not wait
+                // for a read of the running sum.  Each lane owns its address
+                // and a wave's LDS operations run in issue order, so the sums
+                // are deterministic.
+                double *lp = (double *)(lpair + GramLds<NJ, METHOD>::idx(c, d) * 64);
+                const double pr = fma(tr[c], tr[d], ti[c] * ti[d]);
+                const double pim = fma(tr[c], ti[d], -(ti[c] * tr[d]));
+                __hip_atomic_fetch_add(lp, pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                __hip_atomic_fetch_add(lp + 1, pim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             } else {
                 acc[Sh::re(c, d)] = fma(tr[c], tr[d], fma(ti[c], ti[d], acc[Sh::re(c, d)]));
                 acc[Sh::im(c, d)] = fma(tr[c], ti[d], fma(-ti[c], tr[d], acc[Sh::im(c, d)]));
