@@ -526,11 +526,11 @@ void plan_stream_k(const std::vector<double> &cost, int n_pix, int n_waves, Stre
     pl.n_segs = ns;
 }
 
-// (cos, sin)(j pi / 32), j = 0..63, rounded from long double.
+// (cos, sin)(j pi / 128), j = 0..255, rounded from long double.
 void trig_table_host(double2 *T) {
     const long double pi = 3.141592653589793238462643383279502884L;
     for (int j = 0; j < TRIG_N; ++j) {
-        const long double a = pi * j / 32.0L;
+        const long double a = pi * j / 128.0L;
         T[j] = make_double2((double)std::cos(a), (double)std::sin(a));
     }
 }

@@ -151,29 +151,28 @@ struct alignas(16) PixelRec {
 // ---------------------------------------------------------------------------
 // FP64 sine and cosine for the transfer's phase factors
 // ---------------------------------------------------------------------------
-// Table-driven: x = n pi/32 + r with n = rint(32 x / pi) and |r| <= pi/64, by
-// a Cody-Waite reduction (W. J. Cody and W. Waite, "Software Manual for the
-// Elementary Functions", 1980) with a two-part constant P1 + P2 = pi/32
-// (P1 = double(pi)/32, P2 the rest to 1e-34).  The first step x - n P1 is
-// exact in one FMA for |x| < 2^30: both terms are multiples of 2^-57 (or x
-// is below 2^-4 and n is 0 or +-1) and the difference is below 2^-4.  Then the
-// Taylor series of sin r to r^7 and cos r to r^8 (truncation below 5e-18 at
-// |r| = pi/64) and the angle addition with T[n mod 64] = (cos, sin)(n pi/32).
-// Absolute error about 3e-16.  Branch-free; T is 64 double2 (1 KB).
-constexpr int TRIG_N = 64;
+// Table-driven: x = n pi/128 + r with n = rint(128 x / pi) and |r| <= pi/256,
+// by a Cody-Waite reduction (W. J. Cody and W. Waite, "Software Manual for
+// the Elementary Functions", 1980) with a two-part constant P1 + P2 = pi/128
+// (P1 = double(pi)/128, P2 the rest to 1e-34).  The first step x - n P1 is
+// exact in one FMA for |x| < 2^30: both terms are multiples of 2^-58 (or x
+// is below 2^-6 and n is 0 or +-1, with x a multiple of 2^-59) and the
+// difference is below 2^-6.  Then the Taylor series of sin r to r^5 and
+// cos r to r^6 (truncation below 1e-17 at |r| = pi/256) and the angle
+// addition with T[n mod 256] = (cos, sin)(n pi/128).  Absolute error about
+// 3e-16.  Branch-free; T is 256 double2 (4 KB).
+constexpr int TRIG_N = 256;
 
 __host__ __device__ inline void sincos_tab(double x, const double2 *__restrict__ T, double &s, double &c) {
-    const double n = rint(x * 10.185916357881302);             // 32 / pi
-    double r = fma(-n, 0.09817477042468103, x);                 // P1
-    r = fma(-n, 3.827021247335479e-18, r);                      // P2
+    const double n = rint(x * 40.74366543152521);              // 128 / pi
+    double r = fma(-n, 0.02454369260617026, x);                // P1
+    r = fma(-n, 9.567553118338697e-19, r);                     // P2
     const double z = r * r;
-    // sin r = r + r z (-1/3! + z (1/5! + z (-1/7!)))
-    double ps = fma(-1.9841269841269841270e-04, z, 8.3333333333333333333e-03);
-    ps = fma(ps, z, -1.6666666666666666667e-01);
+    // sin r = r + r z (-1/3! + z (1/5!))
+    const double ps = fma(8.3333333333333333333e-03, z, -1.6666666666666666667e-01);
     const double sr = fma(r * z, ps, r);
-    // cos r = 1 + z (-1/2! + z (1/4! + z (-1/6! + z (1/8!))))
-    double pc = fma(2.4801587301587301587e-05, z, -1.3888888888888888889e-03);
-    pc = fma(pc, z, 4.1666666666666666667e-02);
+    // cos r = 1 + z (-1/2! + z (1/4! + z (-1/6!)))
+    double pc = fma(-1.3888888888888888889e-03, z, 4.1666666666666666667e-02);
     pc = fma(pc, z, -0.5);
     const double cr = fma(z, pc, 1.0);
     const double2 t = T[((int)n) & (TRIG_N - 1)];
@@ -257,7 +256,7 @@ struct GramParams {
     const int *seg_first;      // [n_tiles + 1]
     double *partial;           // [n_segments][NACC][64]
     int n_waves;
-    const double2 *trig;       // [TRIG_N] (cos, sin)(j pi / 32)
+    const double2 *trig;       // [TRIG_N] (cos, sin)(j pi / 128)
 };
 
 constexpr int MAX_SETS_DEV = 8;   // optics sets of one SSB pass
@@ -290,7 +289,7 @@ struct SsbParams {
     const int *seg_off;      // [n_waves]
     const int *seg_first;    // [n_tiles + 1]
     double *partial;         // [n_segments][3 MAXB + 1][64]
-    const double2 *trig;     // [TRIG_N] (cos, sin)(j pi / 32)
+    const double2 *trig;     // [TRIG_N] (cos, sin)(j pi / 128)
 };
 
 // Loss path: corrected half planes of a chunk of pixels.

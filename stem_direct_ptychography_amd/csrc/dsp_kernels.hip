@@ -219,10 +219,12 @@ struct GramTaylor {
 };
 
 // Pixels whose records (and, with the Taylor scheme, chi's coefficients
-// about theta(k): 160 bytes each) are staged in LDS at a time.
+// about theta(k): 160 bytes each) are staged in LDS at a time.  16 for the
+// 6-slot complex kernel keeps four of its blocks (30 KB of pair sums each)
+// within a CU's 160 KB.
 template <int NJ, int METHOD>
 struct GramChunk {
-    static constexpr int value = GramTaylor<NJ, METHOD>::value ? 32 : 64;
+    static constexpr int value = GramTaylor<NJ, METHOD>::value ? ((METHOD == 1 && NJ >= 6) ? 16 : 32) : 64;
 };
 constexpr int SSB_CHUNK = 64;
 
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
     constexpr int NP = GramLds<NJ, METHOD>::NP;
     __shared__ double2 lpair_all[(NP > 0 ? NP : 1) * 64];
     const int lane = threadIdx.x;
-    T[lane] = prm.trig[lane];
+    for (int i = lane; i < TRIG_N; i += 64) T[i] = prm.trig[i];
 
     const int wv = blockIdx.x;
     const long long n_pix = prm.n_pix;
@@ -1074,7 +1076,7 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
     __shared__ long long sgoff[SSB_CHUNK + PF];
     __shared__ double schi[MAXB * SSB_CHUNK];   // [set][pixel of the chunk] chi(k)
     const int lane = threadIdx.x;
-    T[lane] = prm.trig[lane];
+    for (int i = lane; i < TRIG_N; i += 64) T[i] = prm.trig[i];
 
     const int wv = blockIdx.x;
     const long long n_pix = prm.n_pix;
