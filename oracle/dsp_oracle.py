@@ -622,29 +622,40 @@ def loss_path(G: np.ndarray, k: np.ndarray, w: Optional[np.ndarray], n_scan: int
 HERM16_ONE = 32767
 
 
-def herm16_scale(G: np.ndarray) -> np.ndarray:
-    """One float32 scale per bright-field pixel: the largest |G(q, k)| over
-    its stored half plane ([P4] compact preview: "per-BF-pixel max |G| over
-    the half-plane").  |G|^2 = re^2 + im^2 is formed in float64 from the
-    complex64 components (exact squares, one rounding for the sum), the root
-    in float64 and the result rounded to float32."""
+def herm16_scale(G: np.ndarray, rows: bool = False) -> np.ndarray:
+    """float32 scales: the largest |G(q, k)| over each bright-field pixel's
+    stored half plane ([P4] compact preview: "per-BF-pixel max |G| over the
+    half-plane"), shape (n_bf,); with rows, over each stored row instead
+    ([P4] Conclusions: per-q-row block scales, n per pixel), shape (n_bf, N).
+    |G|^2 = re^2 + im^2 is formed in float64 from the complex64 components
+    (exact squares, one rounding for the sum), the root in float64 and the
+    result rounded to float32."""
     G = np.asarray(G)
     re = G.real.astype(np.float64)
     im = G.imag.astype(np.float64)
-    m = (re * re + im * im).reshape(G.shape[0], -1).max(axis=1)
+    m2 = re * re + im * im
+    m = m2.max(axis=2) if rows else m2.reshape(G.shape[0], -1).max(axis=1)
     return np.sqrt(m).astype(np.float32)
 
 
-def herm16_quantize(G: np.ndarray):
+def _scale_grid(scale: np.ndarray, ndim: int) -> np.ndarray:
+    """Scales broadcast against (n_bf, N, N/2+1): per pixel or per row."""
+    sd = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    return sd.reshape(sd.shape + (1,) * (ndim - sd.ndim))
+
+
+def herm16_quantize(G: np.ndarray, rows: bool = False):
     """([P4] compact preview: pack2x16snorm(clamp(v / scale))) Each component
-    v of G(q, k) becomes the int16 floor(0.5 + 32767 clamp(v / s_k, -1, 1)),
-    the division and the product in float64, each rounded once; all zero
-    where s_k = 0.  Returns (Q int16 (n_bf, N, N/2+1, 2), scale float32 (n_bf,))."""
+    v of G(q, k) becomes the int16 floor(0.5 + 32767 clamp(v / s, -1, 1)),
+    the division and the product in float64, each rounded once, s the
+    pixel's (or, with rows, the row's) scale; all zero where s = 0.
+    Returns (Q int16 (n_bf, N, N/2+1, 2), scale float32 (n_bf,) or
+    (n_bf, N))."""
     G = np.asarray(G)
-    s = herm16_scale(G)
-    sd = s.astype(np.float64).reshape((-1,) + (1,) * (G.ndim - 1))
+    s = herm16_scale(G, rows)
+    sd = _scale_grid(s, G.ndim)
     Q = np.zeros(G.shape + (2,), dtype=np.int16)
-    nz = s > 0
+    nz = np.broadcast_to(sd > 0, G.shape)
     for c, part in enumerate((G.real, G.imag)):
         v = part.astype(np.float64)
         with np.errstate(invalid="ignore", divide="ignore"):
@@ -656,10 +667,11 @@ def herm16_quantize(G: np.ndarray):
 
 
 def herm16_dequantize(Q: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    """G ~ max(q * (1/32767), -1) * s_k per component, in float64 ([P4]
-    compact preview: unpack2x16snorm(word) * scale); returns complex128."""
+    """G ~ max(q * (1/32767), -1) * s per component, in float64 ([P4]
+    compact preview: unpack2x16snorm(word) * scale), s per pixel or per row;
+    returns complex128."""
     r = 1.0 / HERM16_ONE
-    sd = np.asarray(scale, dtype=np.float32).astype(np.float64).reshape((-1,) + (1,) * (Q.ndim - 2))
+    sd = _scale_grid(scale, Q.ndim - 1)
     re = np.maximum(Q[..., 0].astype(np.float64) * r, -1.0) * sd
     im = np.maximum(Q[..., 1].astype(np.float64) * r, -1.0) * sd
     return re + 1j * im

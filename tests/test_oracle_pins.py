@@ -558,6 +558,37 @@ def test_herm16_error_bound_and_exact_values():
     assert sg[0] == 1.0 and Qg[0, 0, 0, 0] == 32767 and Qg[0, 1, 1, 0] == -16383 and Qg[0, 1, 1, 1] == 8192
 
 
+def test_herm16_row_scales():
+    """Per-row scales: each is its row's largest |G|, the error stays within
+    half a step of that row's scale (never more than the per-pixel bound),
+    an all-zero row packs to zeros, and a row of one known value round-trips
+    at its codes."""
+    rng = np.random.default_rng(4)
+    n = 8
+    G = np.fft.rfft2(rng.standard_normal((3, n, n))).astype(np.complex64)
+    G[:, :, 0] *= 50.0                     # a strong column, as DC-dominated planes have
+    G[2, 5] = 0
+    Q, s = O.herm16_quantize(G, rows=True)
+    assert s.shape == (3, n) and s.dtype == np.float32
+    mag = np.abs(G.astype(np.complex128)).max(axis=2)
+    assert np.allclose(s, mag, rtol=1e-7, atol=0)
+    assert s[2, 5] == 0 and not np.any(Q[2, 5])
+    D = O.herm16_dequantize(Q, s)
+    step = s.astype(np.float64)[:, :, None] / 32767.0
+    assert np.all(np.abs(D.real - G.real) <= 0.5 * step * (1 + 1e-9) + 1e-300)
+    assert np.all(np.abs(D.imag - G.imag) <= 0.5 * step * (1 + 1e-9) + 1e-300)
+    _, s_pix = O.herm16_quantize(G)
+    assert np.all(s <= s_pix[:, None])
+    err_rows = np.abs(D - G).max()
+    err_pix = np.abs(O.herm16_dequantize(*O.herm16_quantize(G)) - G).max()
+    assert err_rows < err_pix
+    one = np.zeros((1, 2, 2), dtype=np.complex64)
+    one[0, 1, :] = [0.5 - 0.25j, -1.0 + 0.0j]
+    Qo, so = O.herm16_quantize(one, rows=True)
+    assert so[0, 1] == 1.0 and so[0, 0] == 0.0
+    assert list(Qo[0, 1, 0]) == [16384, -8192] and list(Qo[0, 1, 1]) == [-32767, 0]
+
+
 def test_first_order_model_equals_transfer_sum():
     """The physics-form first-order data (written from A(k)) equals
     sum_Q T x over the oracle's aliases."""
