@@ -255,22 +255,34 @@ def ssb_sweep(dsp, dev, reps: int = 5):
             ms.append(e0.elapsed_time(e1))
         return float(np.median(ms))
 
-    # herm16 compact copy of the same stack (half the bytes per entry)
-    h16 = dsp.quantize_herm16(G)
+    # herm16 compact copies of the same stack (half the bytes per entry), one
+    # scale per pixel or per stored row
+    h16 = {"herm16": dsp.quantize_herm16(G), "herm16 rows": dsp.quantize_herm16(G, rows=True)}
     out["herm16_quantize_ms"] = timed(lambda: dsp.quantize_herm16(G))
-    out["herm16_bytes"] = int(h16[0].numel() * 2 + h16[1].numel() * 4)
+    out["herm16_rows_quantize_ms"] = timed(lambda: dsp.quantize_herm16(G, rows=True))
+    out["herm16_bytes"] = int(h16["herm16"][0].numel() * 2 + h16["herm16"][1].numel() * 4)
+    out["herm16_rows_bytes"] = int(h16["herm16 rows"][0].numel() * 2 + h16["herm16 rows"][1].numel() * 4)
     out["complex64_bytes"] = int(G.numel() * 8)
-    log(f"herm16 quantize: {out['herm16_quantize_ms']:.3f} ms")
+    log(f"herm16 quantize: {out['herm16_quantize_ms']:.3f} ms, rows {out['herm16_rows_quantize_ms']:.3f} ms")
+    # how far each compact copy moves the one-set SSB sums from complex64's
+    S32, _, _ = dsp.ssb(G, k, ssb_sets(w, 1), step=w.step, band=w.band, agreement=False, want_N=False)
+    for name, hq in h16.items():
+        Sh, _, _ = dsp.ssb(None, k, ssb_sets(w, 1), step=w.step, band=w.band, agreement=False, want_N=False,
+                           herm16=hq)
+        out[name.replace(" ", "_") + "_rel_S_diff"] = float(torch.linalg.norm(Sh - S32) / torch.linalg.norm(S32))
+        del Sh
+    del S32
     # the pages' thick-sample fit batch: the same sets at depth 136 A
-    runs = [(B, 0.0, False) for B in (1, 2, 4, 8)] + [(1, 136.0, False), (8, 136.0, False), (1, 0.0, True),
-                                                       (8, 0.0, True)]
+    runs = [(B, 0.0, None) for B in (1, 2, 4, 8)] + [(1, 136.0, None), (8, 136.0, None), (1, 0.0, "herm16"),
+                                                      (8, 0.0, "herm16"), (1, 0.0, "herm16 rows"),
+                                                      (8, 0.0, "herm16 rows")]
     for B, depth, packed in runs:
         sets = [o.replace(depth=depth) for o in ssb_sets(w, B)]
         if packed:
-            m = timed(lambda: dsp.ssb(None, k, sets, step=w.step, band=w.band, agreement=False, herm16=h16))
+            m = timed(lambda: dsp.ssb(None, k, sets, step=w.step, band=w.band, agreement=False, herm16=h16[packed]))
         else:
             m = timed(lambda: dsp.ssb(G, k, sets, step=w.step, band=w.band, agreement=False))
-        name = str(B) + ("" if depth == 0.0 else f" depth {depth:g} A") + (" herm16" if packed else "")
+        name = str(B) + ("" if depth == 0.0 else f" depth {depth:g} A") + (" " + packed if packed else "")
         gb = g_bytes / 2 if packed else g_bytes
         out["passes"][name] = {"ms": m, "q_sets_per_s": n_band * B / (m / 1e3), "g_GBps": gb / (m / 1e3) / 1e9}
         log(f"ssb B={name}: {m:.3f} ms")

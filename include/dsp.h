@@ -230,26 +230,30 @@ dsp_status dsp_derive_phase(const dsp_handle *complex_h, void *hip_stream, dsp_h
 /*
  * Compact G ("Historical WebGPU G(q,k) memory experiment", compact preview /
  * herm16): the stored half plane of each pixel as pairs of signed
- * normalized 16-bit integers and one float scale per pixel.
- *   scale[k] = max over the pixel's plane of |G| (|G|^2 = re^2 + im^2 in
- *              FP64, the root rounded to float);
- *   Q[k][iy][ix][c] = floor(0.5 + 32767 clamp(v / scale[k], -1, 1)) for the
- *              components v = Re G, Im G (FP64; 0 where scale[k] = 0);
- *   G is read back as max(Q / 32767, -1) * scale[k].
+ * normalized 16-bit integers and one float scale per pixel, or with
+ * row_scales one per stored row (same page, "Conclusions": per-q-row block
+ * scales, n per pixel, resolve the weak high-q tail).  With s the pixel's
+ * (or the row's) scale:
+ *   s = max over the pixel's plane (row) of |G| (|G|^2 = re^2 + im^2 in
+ *       FP64, the root rounded to float);
+ *   Q[k][iy][ix][c] = floor(0.5 + 32767 clamp(v / s, -1, 1)) for the
+ *       components v = Re G, Im G (FP64; 0 where s = 0);
+ *   G is read back as max(Q / 32767, -1) * s.
  * G_c64_dev: complex64 [n_bf][n_scan][n_scan/2+1]; Q_i16_dev: int16
- * [n_bf][n_scan][n_scan/2+1][2]; scale_dev: float [n_bf]; all device,
- * caller-owned.  Runs on hip_stream.  DSP_EINVAL for NULL pointers,
- * n_bf <= 0, odd or too small n_scan.
+ * [n_bf][n_scan][n_scan/2+1][2]; scale_dev: float [n_bf], or [n_bf][n_scan]
+ * with row_scales; all device, caller-owned.  Runs on hip_stream.
+ * DSP_EINVAL for NULL pointers, n_bf <= 0, odd or too small n_scan.
  */
-dsp_status dsp_quantize_herm16(const void *G_c64_dev, int n_bf, int n_scan, void *Q_i16_dev, float *scale_dev,
-                               void *hip_stream);
+dsp_status dsp_quantize_herm16(const void *G_c64_dev, int n_bf, int n_scan, int row_scales, void *Q_i16_dev,
+                               float *scale_dev, void *hip_stream);
 
 /* dsp_ssb over herm16 G (Q and scale from dsp_quantize_herm16, half the
- * bytes of complex64 G): same arguments, outputs and errors as dsp_ssb. */
-dsp_status dsp_ssb_herm16(const void *Q_i16_dev, const float *scale_dev, int n_bf, const double *bf_coords_host,
-                          const double *weights_host, const dsp_scan *scan, const dsp_optics *sets_host, int B,
-                          const double *band_invA, void *S_out_c128_dev, double *norm_out_dev,
-                          double *agreement_out_host, void *hip_stream);
+ * bytes of complex64 G; row_scales as given to it): same arguments, outputs
+ * and errors as dsp_ssb. */
+dsp_status dsp_ssb_herm16(const void *Q_i16_dev, const float *scale_dev, int row_scales, int n_bf,
+                          const double *bf_coords_host, const double *weights_host, const dsp_scan *scan,
+                          const dsp_optics *sets_host, int B, const double *band_invA, void *S_out_c128_dev,
+                          double *norm_out_dev, double *agreement_out_host, void *hip_stream);
 
 /* Sizes, histogram, timings of a prepared handle.  Does not wait for the
  * device, except to read DSP_FLAG_COUNT_WORK counts (a blocking copy). */

@@ -238,15 +238,17 @@ def prepare(G, bf_coords, optics, step: float, upsampling: int, method: str = "p
     return Prepared(h, G.device, method)
 
 
-def quantize_herm16(G, stream=None):
+def quantize_herm16(G, rows: bool = False, stream=None):
     """Compact herm16 copy of G (dsp_quantize_herm16): returns (Q int16
-    (n_bf, N, N/2+1, 2), scale float32 (n_bf,)), both on G's device."""
+    (n_bf, N, N/2+1, 2), scale float32 (n_bf,), or (n_bf, N) with one scale
+    per stored row), both on G's device."""
     torch = _torch()
     n = _check_G(G)
     Q = torch.empty(tuple(G.shape) + (2,), dtype=torch.int16, device=G.device)
-    sc = torch.empty((G.shape[0],), dtype=torch.float32, device=G.device)
-    _check(_L.dsp_quantize_herm16(ctypes.c_void_p(G.data_ptr()), G.shape[0], n, ctypes.c_void_p(Q.data_ptr()),
-                                  ctypes.c_void_p(sc.data_ptr()), ctypes.c_void_p(_stream(stream))))
+    sc = torch.empty((G.shape[0], n) if rows else (G.shape[0],), dtype=torch.float32, device=G.device)
+    _check(_L.dsp_quantize_herm16(ctypes.c_void_p(G.data_ptr()), G.shape[0], n, 1 if rows else 0,
+                                  ctypes.c_void_p(Q.data_ptr()), ctypes.c_void_p(sc.data_ptr()),
+                                  ctypes.c_void_p(_stream(stream))))
     return Q, sc
 
 
@@ -299,8 +301,8 @@ def _check_Q(Q, scale):
     if Q.shape[2] != n // 2 + 1:
         raise DspError(_lib.DSP_EINVAL, f"Q's third axis must be N/2+1 = {n // 2 + 1}")
     if not isinstance(scale, torch.Tensor) or scale.dtype != torch.float32 or scale.device != Q.device \
-            or scale.shape != (Q.shape[0],) or not scale.is_contiguous():
-        raise DspError(_lib.DSP_EINVAL, "scale must be contiguous float32 (n_bf,) on Q's device")
+            or tuple(scale.shape) not in ((Q.shape[0],), (Q.shape[0], n)) or not scale.is_contiguous():
+        raise DspError(_lib.DSP_EINVAL, "scale must be contiguous float32 (n_bf,) or (n_bf, N) on Q's device")
     return n
 
 
@@ -338,8 +340,9 @@ def ssb(G, bf_coords, optics_sets: Sequence, step: float, band: Optional[Tuple[f
             ctypes.c_void_p(Nn.data_ptr()) if Nn is not None else None, _dptr(E) if E is not None else None,
             ctypes.c_void_p(_stream(stream)))
     if herm16 is not None:
-        _check(_L.dsp_ssb_herm16(ctypes.c_void_p(Q.data_ptr()), ctypes.c_void_p(sc.data_ptr()), k.shape[0], _dptr(k),
-                                 _dptr(w), ctypes.byref(scan), arr, B, *outs))
+        _check(_L.dsp_ssb_herm16(ctypes.c_void_p(Q.data_ptr()), ctypes.c_void_p(sc.data_ptr()),
+                                 1 if sc.dim() == 2 else 0, k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan), arr,
+                                 B, *outs))
     else:
         _check(_L.dsp_ssb(ctypes.c_void_p(G.data_ptr()), k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan), arr, B,
                           *outs))

@@ -97,14 +97,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsp_ssb.argtypes = [_P, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _I, _DP, _P, _P,
                             _DP, _P]
     lib.dsp_ssb_herm16.restype = _I
-    lib.dsp_ssb_herm16.argtypes = [_P, _P, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _I, _DP,
-                                   _P, _P, _DP, _P]
+    lib.dsp_ssb_herm16.argtypes = [_P, _P, _I, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _I,
+                                   _DP, _P, _P, _DP, _P]
     lib.dsp_preview.restype = _I
     lib.dsp_preview.argtypes = [_P, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _I, _P, _P, _P]
     lib.dsp_loss.restype = _I
     lib.dsp_loss.argtypes = [_P, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _P, _DP, _P]
     lib.dsp_quantize_herm16.restype = _I
-    lib.dsp_quantize_herm16.argtypes = [_P, _I, _I, _P, _P, _P]
+    lib.dsp_quantize_herm16.argtypes = [_P, _I, _I, _I, _P, _P, _P]
     lib.dsp_info.restype = _I
     lib.dsp_info.argtypes = [_P, ctypes.POINTER(InfoC)]
     lib.dsp_export_system.restype = _I

@@ -1487,8 +1487,8 @@ struct SsbPassBufs {
 // One pass over G for B sets on layout L: pixel terms, then the SSB kernel
 // with lanes on the (M, M/2 + 1) grid writing S and N there.
 static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int B, const void *G_c64_dev,
-                           const void *GQ_dev, const float *gscale_dev, int N, int M, double2 *S_out, double *N_out,
-                           const SsbPassBufs &bufs, int device, hipStream_t stream) {
+                           const void *GQ_dev, const float *gscale_dev, int h16_rows, int N, int M, double2 *S_out,
+                           double *N_out, const SsbPassBufs &bufs, int device, hipStream_t stream) {
     dsp_status st;
     const int n_tiles = (int)L.tiles.size();
     const int n_pix = (int)L.act.pix.size();
@@ -1510,6 +1510,7 @@ static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int 
     sp.G = (const float2 *)G_c64_dev;
     sp.GQ = (const short2 *)GQ_dev;
     sp.gscale = gscale_dev;
+    sp.h16_rows = h16_rows;
     sp.plane = (long long)N * (N / 2 + 1);
     sp.pix = bufs.pix;
     sp.goff = L.d_goff;
@@ -1599,7 +1600,7 @@ static SsbKey pass_key(int device, const dsp_scan *scan, const dsp_optics *o, in
     return key;
 }
 
-static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const float *gscale_dev, int n_bf,
+static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const float *gscale_dev, int h16_rows, int n_bf,
                            const double *bf_coords_host, const double *weights_host, const dsp_scan *scan,
                            const dsp_optics *sets_host, int B, const double *band_invA, void *S_out_c128_dev,
                            double *norm_out_dev, double *agreement_out_host, void *hip_stream) {
@@ -1677,8 +1678,8 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
     double *d_E = cv.take<double>(B + 1);
 
     SsbPassBufs bufs{d_pix, d_chi, d_part, d_tile_part};
-    if ((st = ssb_pass(L, sets_host, B, G_c64_dev, GQ_dev, gscale_dev, N, N, (double2 *)S_out_c128_dev, norm_out_dev,
-                       bufs, device, stream)))
+    if ((st = ssb_pass(L, sets_host, B, G_c64_dev, GQ_dev, gscale_dev, h16_rows, N, N, (double2 *)S_out_c128_dev,
+                       norm_out_dev, bufs, device, stream)))
         return st;
     std::vector<double> E(B + 1, 0.0);
     if (agreement_out_host) {
@@ -1698,17 +1699,17 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
                    const dsp_scan *scan, const dsp_optics *sets_host, int B, const double *band_invA,
                    void *S_out_c128_dev, double *norm_out_dev, double *agreement_out_host, void *hip_stream) {
     if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
-    return ssb_impl(G_c64_dev, nullptr, nullptr, n_bf, bf_coords_host, weights_host, scan, sets_host, B, band_invA,
+    return ssb_impl(G_c64_dev, nullptr, nullptr, 0, n_bf, bf_coords_host, weights_host, scan, sets_host, B, band_invA,
                     S_out_c128_dev, norm_out_dev, agreement_out_host, hip_stream);
 }
 
-dsp_status dsp_ssb_herm16(const void *Q_i16_dev, const float *scale_dev, int n_bf, const double *bf_coords_host,
-                          const double *weights_host, const dsp_scan *scan, const dsp_optics *sets_host, int B,
-                          const double *band_invA, void *S_out_c128_dev, double *norm_out_dev,
-                          double *agreement_out_host, void *hip_stream) {
+dsp_status dsp_ssb_herm16(const void *Q_i16_dev, const float *scale_dev, int row_scales, int n_bf,
+                          const double *bf_coords_host, const double *weights_host, const dsp_scan *scan,
+                          const dsp_optics *sets_host, int B, const double *band_invA, void *S_out_c128_dev,
+                          double *norm_out_dev, double *agreement_out_host, void *hip_stream) {
     if (!Q_i16_dev || !scale_dev) return fail(DSP_EINVAL, "Q and scale must be non-NULL");
-    return ssb_impl(nullptr, Q_i16_dev, scale_dev, n_bf, bf_coords_host, weights_host, scan, sets_host, B, band_invA,
-                    S_out_c128_dev, norm_out_dev, agreement_out_host, hip_stream);
+    return ssb_impl(nullptr, Q_i16_dev, scale_dev, row_scales ? 1 : 0, n_bf, bf_coords_host, weights_host, scan,
+                    sets_host, B, band_invA, S_out_c128_dev, norm_out_dev, agreement_out_host, hip_stream);
 }
 
 dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
@@ -1751,7 +1752,7 @@ dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_
     // S on the fine half plane (zero where no lane runs: K = 0 and beyond reach)
     HIP_TRY(launch_fill_zero((double *)d_S, (size_t)n_half * 2, stream));
     if (n_tiles > 0 &&
-        (st = ssb_pass(L, optics, 1, G_c64_dev, nullptr, nullptr, N, M, d_S, nullptr, bufs, device, stream)))
+        (st = ssb_pass(L, optics, 1, G_c64_dev, nullptr, nullptr, 0, N, M, d_S, nullptr, bufs, device, stream)))
         return st;
     HIP_TRY(launch_preview_dc(L.d_pixbase, L.d_goff, n_pix, (const float2 *)G_c64_dev, d_dc, stream));
     if (spec_out_c128_dev) HIP_TRY(launch_preview_spectrum(d_S, d_dc, n_half, (double2 *)spec_out_c128_dev, stream));
@@ -1835,14 +1836,13 @@ dsp_status dsp_loss(const void *G_c64_dev, int n_bf, const double *bf_coords_hos
     return DSP_OK;
 }
 
-dsp_status dsp_quantize_herm16(const void *G_c64_dev, int n_bf, int n_scan, void *Q_i16_dev, float *scale_dev,
-                               void *hip_stream) {
+dsp_status dsp_quantize_herm16(const void *G_c64_dev, int n_bf, int n_scan, int row_scales, void *Q_i16_dev,
+                               float *scale_dev, void *hip_stream) {
     if (!G_c64_dev || !Q_i16_dev || !scale_dev) return fail(DSP_EINVAL, "G, Q and scale must be non-NULL");
     if (n_bf <= 0) return fail(DSP_EINVAL, "n_bf must be > 0");
     if (n_scan < 4 || (n_scan & 1)) return fail(DSP_EINVAL, "n_scan must be even and >= 4");
-    const long long plane = (long long)n_scan * (n_scan / 2 + 1);
-    HIP_TRY(launch_herm16((const float2 *)G_c64_dev, n_bf, plane, (short2 *)Q_i16_dev, scale_dev,
-                          (hipStream_t)hip_stream));
+    HIP_TRY(launch_herm16((const float2 *)G_c64_dev, n_bf, n_scan, n_scan / 2 + 1, row_scales != 0,
+                          (short2 *)Q_i16_dev, scale_dev, (hipStream_t)hip_stream));
     return DSP_OK;
 }
 

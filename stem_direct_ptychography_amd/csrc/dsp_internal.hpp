@@ -266,7 +266,8 @@ constexpr int MAX_SETS_DEV = 8;   // optics sets of one SSB pass
 struct SsbParams {
     const float2 *G;         // complex64 G, or null with GQ
     const short2 *GQ;        // herm16 G: snorm16 pairs, one scale per pixel
-    const float *gscale;     // [n_bf] herm16 scales, indexed by the pixel's plane
+    const float *gscale;     // herm16 scales: [n_bf] by the pixel's plane, or [n_bf][N] by its stored row
+    int h16_rows;            // scales per row
     long long plane;         // N (N/2 + 1): plane offset -> pixel index
     const PixelRec *pix;
     const long long *goff;   // [n_pix]

@@ -1064,16 +1064,18 @@ struct SsbWaves {
 // The support, a(k -/+ q), G and the weight are shared by the sets; chi and
 // its phase factor are per set.  Partial layout: [3b] Re S_b, [3b+1] Im S_b,
 // [3b+2] N_b, [3 MAXB] P.
-// H16: G comes as herm16 snorm16 pairs with one scale per pixel (staged with
-// the pixel record), unpacked as max(q / 32767, -1) s in FP64 at use.
-template <int MAXB, bool DEPTH, bool H16>
+// H16: G comes as herm16 snorm16 pairs, unpacked as max(q / 32767, -1) s in
+// FP64 at use; H16 = 1: one scale per pixel (staged with the pixel record);
+// H16 = 2: one scale per stored row, fetched with G for the lane's row.
+template <int MAXB, bool DEPTH, int H16>
 __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbParams prm) {
     constexpr int NACC = 3 * MAXB + 1;
     constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
-    using GT = typename std::conditional<H16, short2, float2>::type;
+    using GT = typename std::conditional<H16 != 0, short2, float2>::type;
     __shared__ double2 T[TRIG_N];
     __shared__ PixelRec srec[SSB_CHUNK];
     __shared__ long long sgoff[SSB_CHUNK + PF];
+    __shared__ long long sgrow[H16 == 2 ? SSB_CHUNK + PF : 1];   // pixel index x N (row scales)
     __shared__ double schi[MAXB * SSB_CHUNK];   // [set][pixel of the chunk] chi(k)
     const int lane = threadIdx.x;
     for (int i = lane; i < TRIG_N; i += 64) T[i] = prm.trig[i];
@@ -1087,6 +1089,7 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
     ConstLong *goffs = (ConstLong *)prm.goff;
     const double *__restrict__ chi_tab = prm.chi_tab;
     const GT *__restrict__ G = H16 ? (const GT *)prm.GQ : (const GT *)prm.G;
+    const float *__restrict__ gsc = prm.gscale;
 
     while (it < end) {
         const int t = (int)(it / n_pix);
@@ -1117,15 +1120,20 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
         // records, plane offsets and the sets' chi(k) staged in LDS per chunk;
         // G a group of PF pixels ahead; the chunk's tail runs on zero records
         GT ga[PF];
+        float sa[PF];   // row scales of the group (H16 == 2)
 #pragma unroll
-        for (int i = 0; i < PF; ++i) ga[i] = G[goffs[p0 + i < p1 ? p0 + i : p1 - 1] + lane_off];
+        for (int i = 0; i < PF; ++i) {
+            const long long go = goffs[p0 + i < p1 ? p0 + i : p1 - 1];
+            ga[i] = G[go + lane_off];
+            if (H16 == 2) sa[i] = gsc[(go / prm.plane) * prm.N + iyq];
+        }
         for (int c0 = p0; c0 < p1; c0 += SSB_CHUNK) {
             const int cn = (p1 - c0) < SSB_CHUNK ? (p1 - c0) : SSB_CHUNK;
             __syncthreads();
             if (lane < cn) {
                 PixelRec rec = pix[c0 + lane];
                 // herm16: the pixel's scale rides in the record's spare field
-                if (H16) rec.pad = (double)prm.gscale[goffs[c0 + lane] / prm.plane];
+                if (H16 == 1) rec.pad = (double)gsc[goffs[c0 + lane] / prm.plane];
                 srec[lane] = rec;
             } else {
                 PixelRec z;
@@ -1135,19 +1143,27 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
 #pragma unroll
             for (int b = 0; b < MAXB; ++b)
                 schi[b * SSB_CHUNK + lane] = (lane < cn && b < prm.B) ? chi_tab[(size_t)(c0 + lane) * MAX_SETS_DEV + b] : 0.0;
-            for (int i = lane; i < SSB_CHUNK + PF; i += 64) sgoff[i] = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
+            for (int i = lane; i < SSB_CHUNK + PF; i += 64) {
+                const long long go = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
+                sgoff[i] = go;
+                if (H16 == 2) sgrow[i] = (go / prm.plane) * prm.N;
+            }
             __syncthreads();
             for (int r0 = 0; r0 < cn; r0 += PF) {
                 GT gb[PF];
+                float sb[PF];
 #pragma unroll
-                for (int k = 0; k < PF; ++k) gb[k] = G[sgoff[r0 + PF + k] + lane_off];
+                for (int k = 0; k < PF; ++k) {
+                    gb[k] = G[sgoff[r0 + PF + k] + lane_off];
+                    if (H16 == 2) sb[k] = gsc[sgrow[r0 + PF + k] + iyq];
+                }
 #pragma unroll
                 for (int k = 0; k < PF; ++k) {
                     const int r = r0 + k;
                     const double lky = srec[r].lky, lkx = srec[r].lkx, amp0 = srec[r].amp0, sw = srec[r].sw;
                     double gre, gim;   // G(q, k) in FP64
                     if (H16) {
-                        const double sc = srec[r].pad;
+                        const double sc = H16 == 1 ? srec[r].pad : (double)sa[k];
                         gre = fmax((double)ga[k].x * (1.0 / 32767.0), -1.0) * sc;
                         gim = fmax((double)ga[k].y * (1.0 / 32767.0), -1.0) * sc;
                     } else {
@@ -1227,7 +1243,10 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                     }
                 }
 #pragma unroll
-                for (int k = 0; k < PF; ++k) ga[k] = gb[k];
+                for (int k = 0; k < PF; ++k) {
+                    ga[k] = gb[k];
+                    if (H16 == 2) sa[k] = sb[k];
+                }
             }
         }
         double *po = prm.partial + (size_t)seg * (NACC * 64);
@@ -1263,13 +1282,32 @@ __global__ __launch_bounds__(256) void herm16_scale_kernel(const float2 *G, long
     if (threadIdx.x == 0) scale[blockIdx.x] = (float)sqrt(red[0]);
 }
 
-// grid-stride over the n_bf planes' entries
-__global__ __launch_bounds__(256) void herm16_pack_kernel(const float2 *G, long long plane, long long n,
+// One scale per stored row: wave w of the block takes row 4 b + w and its
+// lanes the row's entries; the maximum is order-independent.
+__global__ __launch_bounds__(256) void herm16_row_scale_kernel(const float2 *G, long long n_rows, int nh,
+                                                                float *scale) {
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= n_rows) return;
+    const float2 *Gr = G + (size_t)row * nh;
+    double m = 0.0;
+    for (int e = lane; e < nh; e += 64) {
+        const double re = Gr[e].x, im = Gr[e].y;
+        m = fmax(m, __dadd_rn(__dmul_rn(re, re), __dmul_rn(im, im)));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    if (lane == 0) scale[row] = (float)sqrt(m);
+}
+
+// grid-stride over the n_bf planes' entries; entry i uses scale[i / per]
+// (per = the plane, or the row for row scales)
+__global__ __launch_bounds__(256) void herm16_pack_kernel(const float2 *G, long long per, long long n,
                                                           const float *scale, short2 *Q) {
 #pragma clang fp contract(off)
     const long long stride = (long long)gridDim.x * blockDim.x;
     for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const double s = scale[i / plane];
+        const double s = scale[i / per];
         const float2 v = G[i];
         short2 q = make_short2(0, 0);
         if (s > 0.0) {
@@ -1708,32 +1746,42 @@ int ssb_nacc(int maxb) { return 3 * maxb + 1; }
 
 hipError_t ssb_occupancy(int maxb, int *blocks_per_cu) {
     switch (maxb) {
-        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1, false, false>, 64, 0);
-        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2, false, false>, 64, 0);
-        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4, false, false>, 64, 0);
-        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8, false, false>, 64, 0);
+        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1, false, 0>, 64, 0);
+        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2, false, 0>, 64, 0);
+        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4, false, 0>, 64, 0);
+        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8, false, 0>, 64, 0);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int MAXB>
-static void ssb_dispatch(const SsbParams &prm, bool depth, bool h16, int n_waves, hipStream_t st) {
-    if (depth) {
-        if (h16) ssb_kernel<MAXB, true, true><<<n_waves, 64, 0, st>>>(prm);
-        else ssb_kernel<MAXB, true, false><<<n_waves, 64, 0, st>>>(prm);
-    } else {
-        if (h16) ssb_kernel<MAXB, false, true><<<n_waves, 64, 0, st>>>(prm);
-        else ssb_kernel<MAXB, false, false><<<n_waves, 64, 0, st>>>(prm);
-    }
+template <int MAXB, bool DEPTH>
+static void ssb_dispatch_h(const SsbParams &prm, int h16, int n_waves, hipStream_t st) {
+    if (h16 == 2) ssb_kernel<MAXB, DEPTH, 2><<<n_waves, 64, 0, st>>>(prm);
+    else if (h16 == 1) ssb_kernel<MAXB, DEPTH, 1><<<n_waves, 64, 0, st>>>(prm);
+    else ssb_kernel<MAXB, DEPTH, 0><<<n_waves, 64, 0, st>>>(prm);
 }
 
-hipError_t launch_herm16(const float2 *G, int n_bf, long long plane, short2 *Q, float *scale, hipStream_t st) {
+template <int MAXB>
+static void ssb_dispatch(const SsbParams &prm, bool depth, int h16, int n_waves, hipStream_t st) {
+    if (depth) ssb_dispatch_h<MAXB, true>(prm, h16, n_waves, st);
+    else ssb_dispatch_h<MAXB, false>(prm, h16, n_waves, st);
+}
+
+hipError_t launch_herm16(const float2 *G, int n_bf, int N, int nh, bool rows, short2 *Q, float *scale,
+                         hipStream_t st) {
+    const long long plane = (long long)N * nh;
     if (n_bf <= 0 || plane <= 0) return hipSuccess;
-    herm16_scale_kernel<<<n_bf, 256, 0, st>>>(G, plane, scale);
+    if (rows) {
+        const long long n_rows = (long long)n_bf * N;
+        herm16_row_scale_kernel<<<(unsigned)((n_rows + 3) / 4), 256, 0, st>>>(G, n_rows, nh, scale);
+    } else {
+        herm16_scale_kernel<<<n_bf, 256, 0, st>>>(G, plane, scale);
+    }
     DSP_CHECK_LAUNCH();
     const long long n = (long long)n_bf * plane;
     const long long blocks = (n + 255) / 256;
-    herm16_pack_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, st>>>(G, plane, n, scale, Q);
+    herm16_pack_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, st>>>(G, rows ? nh : plane, n, scale,
+                                                                                     Q);
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }
@@ -1794,7 +1842,7 @@ hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *ti
     const int nacc = ssb_nacc(maxb);
     bool depth = false;   // depth terms when any set has a depth
     for (int b = 0; b < prm.B; ++b) depth = depth || prm.pt2[b] != 0.0;
-    const bool h16 = prm.GQ != nullptr;
+    const int h16 = prm.GQ == nullptr ? 0 : (prm.h16_rows ? 2 : 1);
     switch (maxb) {
         case 1: ssb_dispatch<1>(prm, depth, h16, n_waves, st); break;
         case 2: ssb_dispatch<2>(prm, depth, h16, n_waves, st); break;

@@ -49,7 +49,8 @@ hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_waves, h
 hipError_t launch_gram_fixup(const GramParams &prm, int nj, int method, int n_tiles, hipStream_t st);
 hipError_t launch_work_count(const GramParams &prm, int method, int n_tiles, unsigned long long *out,
                              hipStream_t st);
-hipError_t launch_herm16(const float2 *G, int n_bf, long long plane, short2 *Q, float *scale, hipStream_t st);
+hipError_t launch_herm16(const float2 *G, int n_bf, int N, int nh, bool rows, short2 *Q, float *scale,
+                         hipStream_t st);
 hipError_t launch_phase_from_complex(const double2 *csys, double2 *psys, int a_max, int n_q, hipStream_t st);
 hipError_t launch_eig(const EigParams &prm, int A, hipStream_t st);
 hipError_t launch_solve(const SolveParams &prm, int A, int method, hipStream_t st);

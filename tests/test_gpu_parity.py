@@ -443,7 +443,10 @@ def _ssb_case(w, G_dev, k, wts, sets, band, entries=None, h16=None):
     if h16 is not None:
         Q, sc = h16
         Q_sel = Q[:, ey, ex][torch.as_tensor(act, device=DEV)].cpu().numpy()
-        G_sel = O.herm16_dequantize(Q_sel, sc.cpu().numpy()[act])
+        sc_act = sc.cpu().numpy()[act]
+        if sc_act.ndim == 2:
+            sc_act = sc_act[:, entries[:, 0]]          # the entries' row scales
+        G_sel = O.herm16_dequantize(Q_sel, sc_act)
     else:
         G_sel = G_dev[:, ey, ex][torch.as_tensor(act, device=DEV)].cpu().numpy().astype(np.complex128)
     cols = [G_sel[:, i] for i in range(len(entries))]
@@ -493,23 +496,25 @@ def test_herm16_quantize_bit_exact():
     G = data_stack_numpy(w, pix)
     G[3] = 0.0
     G[5, 7, 9] = -4.0 * np.abs(G[5]).max()
-    Q, sc = dsp.quantize_herm16(torch.as_tensor(G, device=DEV))
-    torch.cuda.synchronize()
-    Q_o, s_o = O.herm16_quantize(G)
-    assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
-    assert np.array_equal(Q.cpu().numpy(), Q_o)
-    assert Q_o[5, 7, 9, 0] == -32767 and not np.any(Q_o[3])
+    for rows in (False, True):
+        Q, sc = dsp.quantize_herm16(torch.as_tensor(G, device=DEV), rows=rows)
+        torch.cuda.synchronize()
+        Q_o, s_o = O.herm16_quantize(G, rows=rows)
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_o.view(np.uint32)), rows
+        assert np.array_equal(Q.cpu().numpy(), Q_o), rows
+        assert Q_o[5, 7, 9, 0] == -32767 and not np.any(Q_o[3])
 
 
+@pytest.mark.parametrize("rows", [False, True])
 @pytest.mark.parametrize("depth", [0.0, 136.0])
-def test_ssb_herm16_c1_full(depth):
+def test_ssb_herm16_c1_full(depth, rows):
     """SSB over the herm16 copy against the oracle on its dequantized values,
     every band entry, with the agreement; and within the quantisation's reach
     of the pass over complex64 G."""
     w = workload("c1")
     pix, k = bf_pixels(w)
     G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
-    h16 = dsp.quantize_herm16(G_dev)
+    h16 = dsp.quantize_herm16(G_dev, rows=rows)
     sets = [w.optics.replace(depth=depth), w.optics.replace(aberrations=[(1, 0, -90.0, 0.0)]),
             w.optics.replace(tilt=(1e-3, 2e-3))]
     S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G_dev, k, None, sets, None, h16=h16)
@@ -521,9 +526,13 @@ def test_ssb_herm16_c1_full(depth):
     S32, N32, _ = dsp.ssb(G_dev, k, sets, step=w.step)
     assert np.allclose(N32.cpu().numpy(), Nn, rtol=1e-12, atol=0)
     act = O.active_pixels(k, w.optics)
-    bound = math.sqrt(2.0) * float(np.sum(h16[1].cpu().numpy()[act].astype(np.float64))) / 32767.0 * 1.001
+    sc = h16[1].cpu().numpy()[act].astype(np.float64)
+    if rows:   # per stored row iy: sqrt(2) sum_k s_k(iy) / 32767
+        bound = (math.sqrt(2.0) * sc.sum(axis=0) / 32767.0 * 1.001)[:, None]
+    else:
+        bound = math.sqrt(2.0) * float(sc.sum()) / 32767.0 * 1.001
     dS = np.abs(S - S32.cpu().numpy())
-    assert dS.max() <= bound, f"herm16 vs complex64 |dS| {dS.max():.3e} > bound {bound:.3e}"
+    assert np.all(dS <= bound), f"herm16 vs complex64 |dS| {dS.max():.3e} beyond the codes' bound"
 
 
 def test_ssb_herm16_tiny_band_weighted():
@@ -794,19 +803,20 @@ def test_c5_ssb_eight_sets_sampled():
     torch.cuda.empty_cache()
 
 
-def test_c5_herm16_eight_sets_sampled():
+@pytest.mark.parametrize("row_scales", [False, True])
+def test_c5_herm16_eight_sets_sampled(row_scales):
     """Full-frame herm16: codes and scales bit-exact on sampled pixel planes,
     SSB over the compact copy against the oracle on sampled band entries."""
     w = workload("c5")
     pix, k = bf_pixels(w)
-    _say("generating full-frame G (8807, 512, 257) on the GPU")
+    _say(f"generating full-frame G (8807, 512, 257) on the GPU (row scales {row_scales})")
     G = data_stack_torch(w, pix, DEV)
-    Q, sc = dsp.quantize_herm16(G)
+    Q, sc = dsp.quantize_herm16(G, rows=row_scales)
     torch.cuda.synchronize()
     rng = np.random.default_rng(8)
     rows = np.sort(rng.choice(G.shape[0], size=12, replace=False))
     for r in rows:
-        Q_o, s_o = O.herm16_quantize(G[int(r):int(r) + 1].cpu().numpy())
+        Q_o, s_o = O.herm16_quantize(G[int(r):int(r) + 1].cpu().numpy(), rows=row_scales)
         assert np.array_equal(sc[int(r):int(r) + 1].cpu().numpy().view(np.uint32), s_o.view(np.uint32)), r
         assert np.array_equal(Q[int(r):int(r) + 1].cpu().numpy(), Q_o), r
     del G

@@ -174,12 +174,12 @@ def test_validation_status_codes():
                      None) == _lib.DSP_EINVAL
     assert L.dsp_solve(None, None, 1, None, None, None) == _lib.DSP_EINVAL
     # herm16: null buffers, bad sizes (caught before any device call)
-    assert L.dsp_quantize_herm16(None, 4, 16, None, None, None) == _lib.DSP_EINVAL
-    assert L.dsp_quantize_herm16(ctypes.c_void_p(16), 0, 16, ctypes.c_void_p(16), ctypes.c_void_p(16),
+    assert L.dsp_quantize_herm16(None, 4, 16, 0, None, None, None) == _lib.DSP_EINVAL
+    assert L.dsp_quantize_herm16(ctypes.c_void_p(16), 0, 16, 1, ctypes.c_void_p(16), ctypes.c_void_p(16),
                                  None) == _lib.DSP_EINVAL
-    assert L.dsp_quantize_herm16(ctypes.c_void_p(16), 4, 15, ctypes.c_void_p(16), ctypes.c_void_p(16),
+    assert L.dsp_quantize_herm16(ctypes.c_void_p(16), 4, 15, 0, ctypes.c_void_p(16), ctypes.c_void_p(16),
                                  None) == _lib.DSP_EINVAL
-    assert L.dsp_ssb_herm16(None, None, 1, None, None, ctypes.byref(good), ctypes.byref(oc), 1, None, None, None,
+    assert L.dsp_ssb_herm16(None, None, 0, 1, None, None, ctypes.byref(good), ctypes.byref(oc), 1, None, None, None,
                             None, None) == _lib.DSP_EINVAL
     assert L.dsp_info(None, None) == _lib.DSP_EINVAL
 
