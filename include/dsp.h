@@ -228,6 +228,33 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
 dsp_status dsp_derive_phase(const dsp_handle *complex_h, void *hip_stream, dsp_handle **out);
 
 /*
+ * Two-slot prepared-model cache: one slot per method under the same data and
+ * optics key, so phase -> complex -> phase prepares each model once ("Where
+ * the 9 s of regularized preparation goes", conclusion 3: a one-slot cache
+ * keyed with the method prepares three times; two slots fix it).
+ * dsp_cache_get returns the slot's model when its key matches (G's address,
+ * g_version, the pixels and weights, scan, optics, upsampling, smoothness
+ * and flags, all compared bit for bit), else prepares it (dsp_prepare), or,
+ * for DSP_PHASE with derive != 0 while the complex slot holds the same key,
+ * derives it from the complex model (dsp_derive_phase), and replaces the
+ * slot.
+ *   g_version: the caller's generation number of G's contents; change it
+ *              when G is rewritten in place.
+ *   out: the model, owned by the cache: valid until a later dsp_cache_get
+ *        replaces its slot or dsp_cache_destroy; never dsp_destroy it.
+ *   how (may be NULL): 1 slot hit, 0 prepared, 2 derived.
+ * Calls on one cache are serialized by a lock.  On error the slot keeps its
+ * model and *out is NULL; errors as dsp_prepare and dsp_derive_phase.
+ */
+typedef struct dsp_cache dsp_cache;
+dsp_status dsp_cache_create(dsp_cache **out);
+void dsp_cache_destroy(dsp_cache *c);
+dsp_status dsp_cache_get(dsp_cache *c, const void *G_c64_dev, unsigned long long g_version, int n_bf,
+                         const double *bf_coords_host, const double *weights_host, const dsp_scan *scan,
+                         const dsp_optics *optics, const dsp_prepare_opts *opts, int derive, void *hip_stream,
+                         dsp_handle **out, int *how);
+
+/*
  * Compact G ("Historical WebGPU G(q,k) memory experiment", compact preview /
  * herm16): the stored half plane of each pixel as pairs of signed
  * normalized 16-bit integers and one float scale per pixel, or with

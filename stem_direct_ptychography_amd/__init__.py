@@ -25,7 +25,7 @@ from . import _lib
 
 _L = _lib.load()
 
-__all__ = ["DspError", "Prepared", "prepare", "ssb", "preview", "loss", "quantize_herm16", "geometry_counts", "alias_geometry", "active_bf",
+__all__ = ["DspError", "Prepared", "PreparedCache", "prepare", "ssb", "preview", "loss", "quantize_herm16", "geometry_counts", "alias_geometry", "active_bf",
            "band_count", "chi_host", "chi_shift_host", "sincos_host", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -117,15 +117,16 @@ def _stream(stream=None) -> int:
 class Prepared:
     """Prepared per-frequency systems (a handle of libdsp)."""
 
-    def __init__(self, handle: ctypes.c_void_p, device, method: str):
+    def __init__(self, handle: ctypes.c_void_p, device, method: str, owner=None):
         self._h = handle
+        self._owner = owner          # a PreparedCache holding the model, or None (we own it)
         self.device = device
         self.method = method
         self.info = self._info()
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h and _L is not None:   # _L is None during interpreter teardown
+        if h and getattr(self, "_owner", None) is None and _L is not None:   # _L is None at teardown
             _L.dsp_destroy(h)
             self._h = None
 
@@ -236,6 +237,45 @@ def prepare(G, bf_coords, optics, step: float, upsampling: int, method: str = "p
     _check(_L.dsp_prepare(ctypes.c_void_p(G.data_ptr()), k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan),
                           ctypes.byref(oc), ctypes.byref(opts), ctypes.c_void_p(_stream(stream)), ctypes.byref(h)))
     return Prepared(h, G.device, method)
+
+
+class PreparedCache:
+    """Two-slot prepared-model cache (dsp_cache_get): one slot per method
+    under the same data and optics key.  Models it returns stay owned by the
+    cache and are valid until the slot is replaced."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(_L.dsp_cache_create(ctypes.byref(h)))
+        self._c = h
+
+    def __del__(self):
+        c = getattr(self, "_c", None)
+        if c and _L is not None:
+            _L.dsp_cache_destroy(c)
+            self._c = None
+
+    def get(self, G, bf_coords, optics, step: float, upsampling: int, method: str = "phase", weights=None,
+            smoothness: float = 0.0, g_version: int = 0, derive: bool = False, stream=None):
+        """Returns (Prepared, how) with how "hit", "prepared" or "derived"."""
+        n = _check_G(G)
+        k = _coords(bf_coords)
+        if k.shape[0] != G.shape[0]:
+            raise DspError(_lib.DSP_EINVAL, "bf_coords rows must match G's first axis")
+        w = _weights(weights, k.shape[0])
+        if method not in ("phase", "complex"):
+            raise DspError(_lib.DSP_EINVAL, f"unknown method {method!r}")
+        scan = _lib.ScanC(n, float(step))
+        opts = _lib.PrepareOptsC(_lib.DSP_PHASE if method == "phase" else _lib.DSP_COMPLEX, int(upsampling),
+                                 float(smoothness), 0)
+        oc = _optics(optics)
+        h = ctypes.c_void_p()
+        how = ctypes.c_int(-1)
+        _check(_L.dsp_cache_get(self._c, ctypes.c_void_p(G.data_ptr()), int(g_version), k.shape[0], _dptr(k),
+                                _dptr(w), ctypes.byref(scan), ctypes.byref(oc), ctypes.byref(opts),
+                                1 if derive else 0, ctypes.c_void_p(_stream(stream)), ctypes.byref(h),
+                                ctypes.byref(how)))
+        return Prepared(h, G.device, method, owner=self), {0: "prepared", 1: "hit", 2: "derived"}[how.value]
 
 
 def quantize_herm16(G, rows: bool = False, stream=None):

@@ -62,7 +62,7 @@ EXPORTS = (
     "dsp_prepare", "dsp_solve", "dsp_scatter", "dsp_ssb", "dsp_info", "dsp_export_system", "dsp_alias_table",
     "dsp_destroy", "dsp_last_error", "dsp_geometry_counts", "dsp_alias_geometry", "dsp_active_bf",
     "dsp_band_count", "dsp_chi_host", "dsp_chi_shift_host", "dsp_sincos_host", "dsp_derive_phase", "dsp_quantize_herm16",
-    "dsp_ssb_herm16", "dsp_preview", "dsp_loss",
+    "dsp_ssb_herm16", "dsp_preview", "dsp_loss", "dsp_cache_create", "dsp_cache_destroy", "dsp_cache_get",
 )
 
 _P = ctypes.c_void_p
@@ -101,6 +101,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                    _DP, _P, _P, _DP, _P]
     lib.dsp_preview.restype = _I
     lib.dsp_preview.argtypes = [_P, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _I, _P, _P, _P]
+    lib.dsp_cache_create.restype = _I
+    lib.dsp_cache_create.argtypes = [ctypes.POINTER(_P)]
+    lib.dsp_cache_destroy.restype = None
+    lib.dsp_cache_destroy.argtypes = [_P]
+    lib.dsp_cache_get.restype = _I
+    lib.dsp_cache_get.argtypes = [_P, _P, ctypes.c_ulonglong, _I, _DP, _DP, ctypes.POINTER(ScanC),
+                                  ctypes.POINTER(OpticsC), ctypes.POINTER(PrepareOptsC), _I, _P, ctypes.POINTER(_P),
+                                  ctypes.POINTER(_I)]
     lib.dsp_loss.restype = _I
     lib.dsp_loss.argtypes = [_P, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _P, _DP, _P]
     lib.dsp_quantize_herm16.restype = _I

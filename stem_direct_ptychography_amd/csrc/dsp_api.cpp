@@ -1313,6 +1313,107 @@ dsp_status dsp_derive_phase(const dsp_handle *src, void *hip_stream, dsp_handle 
     return DSP_OK;
 }
 
+// ---------------------------------------------------------------------------
+// two-slot prepared-model cache
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+// Everything a prepared model depends on except its method, as doubles
+// compared bit for bit (G by address and the caller's generation number).
+static std::vector<double> cache_key(const void *G, unsigned long long g_version, int n_bf, const double *coords,
+                                     const double *weights, const dsp_scan *scan, const dsp_optics *o,
+                                     const dsp_prepare_opts *opts) {
+    std::vector<double> k;
+    auto put_u64 = [&](unsigned long long v) {
+        double d;
+        std::memcpy(&d, &v, sizeof d);
+        k.push_back(d);
+    };
+    put_u64((unsigned long long)(uintptr_t)G);
+    put_u64(g_version);
+    k.push_back(n_bf);
+    k.insert(k.end(), coords, coords + 2 * (size_t)n_bf);
+    k.push_back(weights ? 1.0 : 0.0);
+    if (weights) k.insert(k.end(), weights, weights + n_bf);
+    k.push_back(scan->n_scan);
+    k.push_back(scan->step_A);
+    k.push_back(o->wavelength_A);
+    k.push_back(o->semiangle_rad);
+    k.push_back(o->det_step_invA);
+    k.push_back(o->soft_aperture);
+    k.push_back(o->tilt_rad[0]);
+    k.push_back(o->tilt_rad[1]);
+    k.push_back(o->depth_A);
+    k.push_back(o->n_aber);
+    for (int a = 0; a < o->n_aber && a < DSP_MAX_ABERRATIONS; ++a) {
+        k.push_back(o->aber[a].n);
+        k.push_back(o->aber[a].m);
+        k.push_back(o->aber[a].c_A);
+        k.push_back(o->aber[a].phi_rad);
+    }
+    k.push_back(opts->upsampling);
+    k.push_back(opts->smoothness_invA);
+    k.push_back(opts->flags);
+    return k;
+}
+
+static bool same_key(const std::vector<double> &a, const std::vector<double> &b) {
+    return a.size() == b.size() && (a.empty() || std::memcmp(a.data(), b.data(), a.size() * sizeof(double)) == 0);
+}
+
+struct dsp_cache {
+    std::mutex mu;
+    std::vector<double> key[2];   // per method
+    dsp_handle *h[2] = {nullptr, nullptr};
+    ~dsp_cache() {
+        for (auto &x : h) dsp_destroy(x);
+    }
+};
+
+extern "C" {
+
+dsp_status dsp_cache_create(dsp_cache **out) {
+    if (!out) return fail(DSP_EINVAL, "out is NULL");
+    *out = new dsp_cache;
+    return DSP_OK;
+}
+
+void dsp_cache_destroy(dsp_cache *c) { delete c; }
+
+dsp_status dsp_cache_get(dsp_cache *c, const void *G_c64_dev, unsigned long long g_version, int n_bf,
+                         const double *bf_coords_host, const double *weights_host, const dsp_scan *scan,
+                         const dsp_optics *optics, const dsp_prepare_opts *opts, int derive, void *hip_stream,
+                         dsp_handle **out, int *how) {
+    if (!c || !out || !scan || !optics || !opts || !bf_coords_host || n_bf <= 0)
+        return fail(DSP_EINVAL, "cache, out, scan, optics, opts and bf_coords must be given");
+    if (opts->method != DSP_PHASE && opts->method != DSP_COMPLEX) return fail(DSP_EINVAL, "unknown method");
+    *out = nullptr;
+    const int m = opts->method == DSP_COMPLEX ? 1 : 0;
+    std::vector<double> k = cache_key(G_c64_dev, g_version, n_bf, bf_coords_host, weights_host, scan, optics, opts);
+    std::lock_guard<std::mutex> lock(c->mu);
+    if (c->h[m] && same_key(c->key[m], k)) {
+        *out = c->h[m];
+        if (how) *how = 1;
+        return DSP_OK;
+    }
+    dsp_handle *nh = nullptr;
+    dsp_status st;
+    int got = 0;
+    if (m == 0 && derive && c->h[1] && same_key(c->key[1], k)) {
+        st = dsp_derive_phase(c->h[1], hip_stream, &nh);
+        got = 2;
+    } else {
+        st = dsp_prepare(G_c64_dev, n_bf, bf_coords_host, weights_host, scan, optics, opts, hip_stream, &nh);
+    }
+    if (st) return st;   // the slot keeps its model
+    dsp_destroy(c->h[m]);
+    c->h[m] = nh;
+    c->key[m] = std::move(k);
+    *out = nh;
+    if (how) *how = got;
+    return DSP_OK;
+}
+
 dsp_status dsp_solve(dsp_handle *h, const double *strengths_host, int S, void *x_out_c128_dev, double *resid_out_dev,
                      void *hip_stream) {
     if (!h) return fail(DSP_EINVAL, "handle is NULL");

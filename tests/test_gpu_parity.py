@@ -389,6 +389,49 @@ def test_frequencies_without_aliases():
         assert not np.any(aug[qi, :-1, :])
 
 
+def test_prepared_cache_two_slots():
+    """phase -> complex -> phase prepares each model once; the hit is the same
+    model, bit for bit what a fresh prepare gives; with derive the phase
+    model comes from the complex slot, equal to derive_phase's; a new G
+    generation or new optics prepares again in that slot only."""
+    w = workload("c2")
+    pix, k = bf_pixels(w)
+    G = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    kw = dict(step=w.step, upsampling=w.upsampling, smoothness=w.smoothness)
+    cache = dsp.PreparedCache()
+    p1, how1 = cache.get(G, k, w.optics, method="phase", **kw)
+    x1 = p1.solve([1e-2])
+    p2, how2 = cache.get(G, k, w.optics, method="complex", **kw)
+    p3, how3 = cache.get(G, k, w.optics, method="phase", **kw)
+    assert (how1, how2, how3) == ("prepared", "prepared", "hit")
+    assert p3._h.value == p1._h.value
+    assert torch.equal(p3.solve([1e-2]), x1)
+    fresh = dsp.prepare(G, k, w.optics, method="phase", **kw)
+    for a, b in zip(p3.export_system(), fresh.export_system()):
+        assert torch.equal(a, b)
+    c_aug = p2.export_system()
+    _, how4 = cache.get(G, k, w.optics, method="complex", **kw)
+    assert how4 == "hit"
+    # a new generation of G: prepared again (phase slot), the complex slot keeps its key
+    p5, how5 = cache.get(G, k, w.optics, method="phase", g_version=1, **kw)
+    assert how5 == "prepared"
+    _, how6 = cache.get(G, k, w.optics, method="complex", **kw)
+    assert how6 == "hit"
+    # derived from the complex slot
+    cache2 = dsp.PreparedCache()
+    pc, _ = cache2.get(G, k, w.optics, method="complex", **kw)
+    pd, how7 = cache2.get(G, k, w.optics, method="phase", derive=True, **kw)
+    assert how7 == "derived"
+    ref = pc.derive_phase()
+    for a, b in zip(pd.export_system(), ref.export_system()):
+        assert torch.equal(a, b)
+    # other optics miss
+    _, how8 = cache2.get(G, k, w.optics.replace(aberrations=[(1, 0, -80.0, 0.0)]), method="phase", derive=True, **kw)
+    assert how8 == "prepared"
+    del p1, p2, p3, p5, pc, pd, fresh, ref, cache, cache2, c_aug
+    torch.cuda.synchronize()
+
+
 def test_zero_data_and_zero_weights():
     w = _tiny()
     pix, k = bf_pixels(w)

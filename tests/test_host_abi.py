@@ -173,6 +173,16 @@ def test_validation_status_codes():
     assert L.dsp_ssb(fake, len(k), kp, None, ctypes.byref(good), arr, 9, None, None, None, None,
                      None) == _lib.DSP_EINVAL
     assert L.dsp_solve(None, None, 1, None, None, None) == _lib.DSP_EINVAL
+    # prepared-model cache: argument checks need no device
+    cache = ctypes.c_void_p()
+    assert L.dsp_cache_create(None) == _lib.DSP_EINVAL
+    assert L.dsp_cache_create(ctypes.byref(cache)) == _lib.DSP_OK and cache.value
+    hh = ctypes.c_void_p()
+    assert L.dsp_cache_get(None, fake, 0, len(k), kp, None, ctypes.byref(good), ctypes.byref(oc), ctypes.byref(opts),
+                           0, None, ctypes.byref(hh), None) == _lib.DSP_EINVAL
+    assert L.dsp_cache_get(cache, fake, 0, len(k), kp, None, ctypes.byref(good), ctypes.byref(oc),
+                           ctypes.byref(bad_opts), 0, None, ctypes.byref(hh), None) == _lib.DSP_EINVAL
+    L.dsp_cache_destroy(cache)
     # herm16: null buffers, bad sizes (caught before any device call)
     assert L.dsp_quantize_herm16(None, 4, 16, 0, None, None, None) == _lib.DSP_EINVAL
     assert L.dsp_quantize_herm16(ctypes.c_void_p(16), 0, 16, 1, ctypes.c_void_p(16), ctypes.c_void_p(16),
