@@ -1453,6 +1453,7 @@ __global__ __launch_bounds__(256) void phase_moments_kernel(const double *img, c
     const long long stride = (long long)gridDim.x * blockDim.x;
     for (long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x; r < nn; r += stride) {
         double a1 = s1[r], a2 = s2[r];
+#pragma unroll 4
         for (int j = 0; j < cn; ++j) {
             const double2 d = D[j];
             const double w = pb[j].w;
