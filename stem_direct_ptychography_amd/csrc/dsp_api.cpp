@@ -338,6 +338,14 @@ void finish_tile(GramTile &t, const JSet &js_in, const Geometry &g,
     }
     t.cy = (float)(nv ? sy / nv : 0.0);
     t.cx = (float)(nv ? sx / nv : 0.0);
+    // radius of the valid lanes about the stored centre, for the kernels'
+    // per-pixel slot test (a bound: rounded up and widened by a part in 1e6)
+    double rad = 0.0;
+    for (int l = 0; l < 64; ++l) {
+        if (t.qidx[l] < 0) continue;
+        rad = std::max(rad, std::hypot((double)t.lyh[l] - (double)t.cy, (double)t.lix[l] - (double)t.cx));
+    }
+    t.rad = std::nextafter((float)(rad * (1.0 + 1e-6)), INFINITY);
     by_nj[t.nj].emplace_back(-cost, t);
 }
 

@@ -194,8 +194,8 @@ constexpr int MAX_SLOTS = 9;   // fine aliases of one coarse frequency for u <= 
 
 struct alignas(64) GramTile {
     int nj;              // alias slots: the sorted union of the lanes' offsets (j_y, j_x)
-    int pad0;
-    float cy, cx;        // mean (yh, ix) of the valid lanes (cost estimate)
+    float rad;           // largest distance of a valid lane's (yh, ix) from (cy, cx), rounded up
+    float cy, cx;        // mean (yh, ix) of the valid lanes (cost estimate, centre of the slot test)
     int8_t jy[12], jx[12];
     uint16_t mask[64];   // per lane: bit s set when slot s is an alias of the lane's frequency
     int32_t qidx[64];    // per lane: index of the frequency in the solved list, -1 if none

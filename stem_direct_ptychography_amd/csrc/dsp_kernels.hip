@@ -290,7 +290,9 @@ __device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, do
 }
 
 // One pixel's update of a lane's sums: the lobes of every slot, then the
-// rank-one update of the augmented Gram.  A column's terms run when some
+// rank-one update of the augmented Gram.  pm (wave-uniform) holds two bits
+// per slot, L and R, clear when no lane of the tile can have that lobe in
+// support at this pixel; a slot with both clear is skipped whole.  A column's terms run when some
 // lane of the wave has it, a pair's when some lane has both (the other lanes
 // add exact zeros).
 // Lobe phases, two schemes (GramTaylor picks one per kernel):
@@ -302,8 +304,8 @@ template <int NJ, int METHOD, bool DEPTH, bool TAY>
 __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 *T,
                                            double (&acc)[GramShape<NJ, METHOD>::NACC], double2 *lpair, int yh, int ix,
                                            const int (&jyN)[NJ], const int (&jxN)[NJ], const bool (&act)[NJ],
-                                           double lky, double lkx, double amp0, double sw, double chi0,
-                                           const double *tay, float2 gv) {
+                                           unsigned pm, double lky, double lkx, double amp0, double sw,
+                                           double chi0, const double *tay, float2 gv) {
     using Sh = GramShape<NJ, METHOD>;
     constexpr int NC = Sh::NC;
     const double ldq = prm.ldq, lrlim2 = prm.ap.lrlim2;
@@ -324,6 +326,13 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
     unsigned long long bal[NC];   // lanes whose column is non-zero
 #pragma unroll
     for (int s = 0; s < NJ; ++s) {
+        if (!((pm >> (2 * s)) & 3u)) {
+            // no lane of the tile has either lobe of this slot in support:
+            // the column stays out of the update (its values are never read)
+            bal[s] = 0ull;
+            if (METHOD == 1) bal[NJ + s] = 0ull;
+            continue;
+        }
         const double Qy_s = (double)(yh + jyN[s]) * ldq, Qx_s = (double)(ix + jxN[s]) * ldq;
         // |lambda (k -/+ Q)|^2 = |lambda k|^2 + |lambda Q|^2 -/+ 2 (lambda k).(lambda Q)
         const double kq = fma(lky, Qy_s, lkx * Qx_s);
@@ -435,6 +444,9 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
     __shared__ double2 T[TRIG_N];
     __shared__ PixelRec srec[GRAM_CHUNK];
     __shared__ long long sgoff[GRAM_CHUNK + PF];
+    __shared__ unsigned smask[GRAM_CHUNK];   // per pixel of the chunk: the slot test's L/R bits
+    __shared__ double2 scent[NJ];             // lambda (c + j_s N dq) per slot, c the tile centre
+    __shared__ double sthr;                   // the slot test's squared bound
     __shared__ double stay[TAY ? GRAM_CHUNK * TAY_N : 1];   // [pixel][TAY_N] chi about theta(k)
     constexpr int NP = GramLds<NJ, METHOD>::NP;
     __shared__ double2 lpair_all[(NP > 0 ? NP : 1) * 64];
@@ -471,6 +483,24 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
             jxN[s] = (int)tile->jx[s] * prm.N;
             act[s] = (mask >> s) & 1u;
         }
+        unsigned live = 0;   // slots some lane of the tile has
+#pragma unroll
+        for (int s = 0; s < NJ; ++s)
+            if (__ballot(act[s])) live |= 1u << s;
+        // Slot test: lane frequencies lie within rad of the tile centre c,
+        // so a lobe of slot s can be in support at pixel k only if
+        // |lambda k -/+ lambda (c + j_s N dq)| < lambda r + rad lambda dq;
+        // sthr is that bound squared, widened by a part in 1e9 against
+        // rounding.  The values go through LDS so that the chunk loop reads
+        // them afresh instead of holding them in registers.
+        if (lane < NJ) {
+            scent[lane] = make_double2(((double)tile->cy + (double)((int)tile->jy[lane] * prm.N)) * prm.ldq,
+                                       ((double)tile->cx + (double)((int)tile->jx[lane] * prm.N)) * prm.ldq);
+        }
+        if (lane == 0) {
+            const double rr = sqrt(prm.ap.lrlim2) + (double)tile->rad * prm.ldq;
+            sthr = rr * rr * (1.0 + 1e-9);
+        }
         double acc[NACC];
 #pragma unroll
         for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
@@ -504,6 +534,18 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
                     rec.lky = rec.lkx = rec.amp0 = rec.sw = rec.chi0 = rec.pad = 0.0;
                 }
                 srec[lane] = rec;
+                const double thr = sthr;
+                unsigned m = 0;
+#pragma unroll
+                for (int s = 0; s < NJ; ++s) {
+                    if (!((live >> s) & 1u)) continue;
+                    const double2 c = scent[s];
+                    const double ly = rec.lky - c.x, lx = rec.lkx - c.y;
+                    const double ry = rec.lky + c.x, rx = rec.lkx + c.y;
+                    if (fma(ly, ly, lx * lx) < thr) m |= 1u << (2 * s);
+                    if (fma(ry, ry, rx * rx) < thr) m |= 2u << (2 * s);
+                }
+                smask[lane] = m;
             }
             if (TAY) {
                 for (int i = lane; i < GRAM_CHUNK * TAY_N; i += 64)
@@ -519,7 +561,8 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
                 for (int k = 0; k < PF; ++k) {
                     const int r = r0 + k;
                     const float2 gv = r < cn ? ga[k] : make_float2(0.0f, 0.0f);
-                    gram_pixel<NJ, METHOD, DEPTH, TAY>(prm, T, acc, lpair, yh, ix, jyN, jxN, act, srec[r].lky,
+                    const unsigned pm = __builtin_amdgcn_readfirstlane(smask[r]);
+                    gram_pixel<NJ, METHOD, DEPTH, TAY>(prm, T, acc, lpair, yh, ix, jyN, jxN, act, pm, srec[r].lky,
                                                        srec[r].lkx, srec[r].amp0, srec[r].sw, srec[r].chi0,
                                                        stay + (TAY ? r * TAY_N : 0), gv);
                 }
