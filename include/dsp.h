@@ -112,6 +112,10 @@ typedef struct {
 #define DSP_FLAG_TIMING 1       /* record HIP events per stage and per Gram launch (read by dsp_info) */
 #define DSP_FLAG_COUNT_WORK 2   /* after the prepare's kernels, count the work of each Gram launch
                                    (one extra kernel per launch; read by dsp_info) */
+#define DSP_FLAG_NO_SLOT_TEST 4 /* evaluate every alias slot at every pixel: the Gram kernels' per-pixel
+                                   slot test (a conservative bound that skips slots out of reach) off.
+                                   The systems are bitwise those with the test on; the flag exists to
+                                   check that. */
 
 typedef struct dsp_handle dsp_handle;
 

@@ -219,8 +219,12 @@ class Prepared:
 
 
 def prepare(G, bf_coords, optics, step: float, upsampling: int, method: str = "phase", weights=None,
-            smoothness: float = 0.0, timing: bool = False, count_work: bool = False, stream=None) -> Prepared:
-    """Per-frequency normal equations (and, for "phase", the eigenbasis)."""
+            smoothness: float = 0.0, timing: bool = False, count_work: bool = False, slot_test: bool = True,
+            stream=None) -> Prepared:
+    """Per-frequency normal equations (and, for "phase", the eigenbasis).
+
+    slot_test=False turns off the Gram kernels' per-pixel slot test (every
+    alias slot is evaluated at every pixel); the systems do not change."""
     n = _check_G(G)
     k = _coords(bf_coords)
     if k.shape[0] != G.shape[0]:
@@ -229,7 +233,8 @@ def prepare(G, bf_coords, optics, step: float, upsampling: int, method: str = "p
     if method not in ("phase", "complex"):
         raise DspError(_lib.DSP_EINVAL, f"unknown method {method!r}")
     scan = _lib.ScanC(n, float(step))
-    flags = (_lib.DSP_FLAG_TIMING if timing else 0) | (_lib.DSP_FLAG_COUNT_WORK if count_work else 0)
+    flags = ((_lib.DSP_FLAG_TIMING if timing else 0) | (_lib.DSP_FLAG_COUNT_WORK if count_work else 0)
+             | (0 if slot_test else _lib.DSP_FLAG_NO_SLOT_TEST))
     opts = _lib.PrepareOptsC(_lib.DSP_PHASE if method == "phase" else _lib.DSP_COMPLEX, int(upsampling),
                              float(smoothness), flags)
     oc = _optics(optics)

@@ -14,6 +14,7 @@ STATUS_NAMES = {0: "DSP_OK", 1: "DSP_EINVAL", 2: "DSP_EUNSUPPORTED", 3: "DSP_EAL
 DSP_PHASE, DSP_COMPLEX = 0, 1
 DSP_FLAG_TIMING = 1
 DSP_FLAG_COUNT_WORK = 2
+DSP_FLAG_NO_SLOT_TEST = 4
 MAX_ABERRATIONS = 16
 
 

@@ -990,6 +990,7 @@ struct dsp_handle {
     double2 *d_c = nullptr;
     bool timing = false;
     bool count_work = false;
+    bool slot_test = true;                    // DSP_FLAG_NO_SLOT_TEST clears it
     hipStream_t stream = nullptr;             // the prepare's stream
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     std::vector<int> gram_order;              // launch order of the tile groups
@@ -1169,6 +1170,8 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
         for (int i = 0; i < n_bf; ++i)
             if (!(weights_host[i] >= 0.0) || !std::isfinite(weights_host[i]))
                 return fail(DSP_EINVAL, "weights[%d] must be finite and >= 0", i);
+    if (opts->flags & ~(DSP_FLAG_TIMING | DSP_FLAG_COUNT_WORK | DSP_FLAG_NO_SLOT_TEST))
+        return fail(DSP_EINVAL, "unknown flags 0x%x", (unsigned)opts->flags);
     hipStream_t stream = (hipStream_t)hip_stream;
 
     std::unique_ptr<dsp_handle> h(new dsp_handle());
@@ -1176,6 +1179,7 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     h->n_bf = n_bf;
     h->timing = (opts->flags & DSP_FLAG_TIMING) != 0;
     h->count_work = (opts->flags & DSP_FLAG_COUNT_WORK) != 0;
+    h->slot_test = (opts->flags & DSP_FLAG_NO_SLOT_TEST) == 0;
     h->stream = stream;
     HIP_TRY(hipGetDevice(&h->device));
 
@@ -1239,6 +1243,7 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     gp.sys = h->d_sys;
     gp.a_max = am;
     gp.D = h->D;
+    gp.slot_test = h->slot_test ? 1 : 0;
     if ((st = trig_table_device(h->device, &gp.trig))) return st;
     // partial sums live only for the Gram stage (the stream's scratch arena)
     double *d_partial = nullptr;

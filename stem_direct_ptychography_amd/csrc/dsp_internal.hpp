@@ -257,6 +257,7 @@ struct GramParams {
     double *partial;           // [n_segments][NACC][64]
     int n_waves;
     const double2 *trig;       // [TRIG_N] (cos, sin)(j pi / 128)
+    int slot_test;             // 1: skip slots the per-pixel bound puts out of reach; 0: run all
 };
 
 constexpr int MAX_SETS_DEV = 8;   // optics sets of one SSB pass

@@ -561,7 +561,7 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
                 for (int k = 0; k < PF; ++k) {
                     const int r = r0 + k;
                     const float2 gv = r < cn ? ga[k] : make_float2(0.0f, 0.0f);
-                    const unsigned pm = __builtin_amdgcn_readfirstlane(smask[r]);
+                    const unsigned pm = prm.slot_test ? __builtin_amdgcn_readfirstlane(smask[r]) : ~0u;
                     gram_pixel<NJ, METHOD, DEPTH, TAY>(prm, T, acc, lpair, yh, ix, jyN, jxN, act, pm, srec[r].lky,
                                                        srec[r].lkx, srec[r].amp0, srec[r].sw, srec[r].chi0,
                                                        stay + (TAY ? r * TAY_N : 0), gv);

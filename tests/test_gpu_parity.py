@@ -341,6 +341,26 @@ def test_phase_derived_c2_sampled():
 
 @pytest.mark.parametrize("method", ["phase", "complex"])
 @pytest.mark.parametrize("soft", [True, False])
+def test_tiny_slot_test_bitwise(method, soft):
+    """Ragged tiny scans at every slot count, hard and soft apertures, with and
+    without depth: the per-pixel slot test leaves the systems bitwise
+    unchanged."""
+    w = _tiny(soft=soft, method=method)
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    wts = random_weights(len(k), 3)
+    for depth in (0.0, 80.0):
+        opt = w.optics.replace(depth=depth)
+        a = dsp.prepare(G_dev, k, opt, step=w.step, upsampling=w.upsampling, method=method, weights=wts,
+                        smoothness=w.smoothness)
+        b = dsp.prepare(G_dev, k, opt, step=w.step, upsampling=w.upsampling, method=method, weights=wts,
+                        smoothness=w.smoothness, slot_test=False)
+        for x, y in zip(a.export_system(), b.export_system()):
+            assert (x is None and y is None) or torch.equal(x, y), (method, soft, depth)
+
+
+@pytest.mark.parametrize("method", ["phase", "complex"])
+@pytest.mark.parametrize("soft", [True, False])
 def test_tiny_depth_full(method, soft):
     """Depth 80 A with tilt on the ragged tiny scan, every frequency."""
     w = _tiny(soft=soft, method=method)
@@ -816,6 +836,23 @@ def test_c4_determinism(c4_data):
         a.append((aug.cpu().numpy(), eig.cpu().numpy()))
         del prep
     assert np.array_equal(a[0][0], a[1][0]) and np.array_equal(a[0][1], a[1][1])
+
+
+@pytest.mark.parametrize("method", ["phase", "complex"])
+def test_c4_slot_test_bitwise(c4_data, method):
+    """The Gram kernels' per-pixel slot test only skips slots with no lobe in
+    support: the full-frame systems (depth 0 and 124 A) are bitwise those of
+    a prepare that evaluates every slot at every pixel."""
+    w, k, G = c4_data
+    for depth in (0.0, 124.0):
+        opt = w.optics.replace(depth=depth)
+        a = dsp.prepare(G, k, opt, step=w.step, upsampling=3, method=method, smoothness=w.smoothness)
+        b = dsp.prepare(G, k, opt, step=w.step, upsampling=3, method=method, smoothness=w.smoothness,
+                        slot_test=False)
+        for x, y in zip(a.export_system(), b.export_system()):
+            assert (x is None and y is None) or torch.equal(x, y), (method, depth)
+        del a, b
+    _say(f"c4 {method}: systems with and without the slot test bitwise equal")
 
 
 def test_c5_ssb_eight_sets_sampled():

@@ -164,6 +164,10 @@ def test_validation_status_codes():
                          ctypes.byref(h)) == _lib.DSP_EINVAL
     assert L.dsp_prepare(fake, 0, kp, None, ctypes.byref(good), ctypes.byref(oc), ctypes.byref(opts), None,
                          ctypes.byref(h)) == _lib.DSP_EINVAL
+    bad_flags = _lib.PrepareOptsC(0, 2, 0.0, 8)
+    assert L.dsp_prepare(fake, len(k), kp, None, ctypes.byref(good), ctypes.byref(oc), ctypes.byref(bad_flags), None,
+                         ctypes.byref(h)) == _lib.DSP_EINVAL
+    assert "flags" in L.dsp_last_error().decode()
     wneg = -np.ones(len(k))
     assert L.dsp_prepare(fake, len(k), kp, wneg.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), ctypes.byref(good),
                          ctypes.byref(oc), ctypes.byref(opts), None, ctypes.byref(h)) == _lib.DSP_EINVAL
