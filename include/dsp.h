@@ -303,6 +303,13 @@ dsp_status dsp_export_system(const dsp_handle *h, void *aug_out_c128_dev, double
  * count_host int32[n_q], K_host int32[n_q][a_max][2] (0 past A(q)). */
 dsp_status dsp_alias_table(const dsp_handle *h, int32_t *q_host, int32_t *count_host, int32_t *K_host);
 
+/* Releases a handle (NULL is ignored).  Its device buffers (one block per
+ * handle) go back to the library's per-device cache behind events recorded
+ * after the last work queued with them on each stream the handle was used
+ * on; the call does not wait for the device, and a later prepare reuses the
+ * block after making its own stream wait on those events.  The cache keeps
+ * at most 4 GiB per device (older blocks are then freed) and gives its blocks
+ * back when an allocation would otherwise fail. */
 void dsp_destroy(dsp_handle *h);
 const char *dsp_last_error(void);
 

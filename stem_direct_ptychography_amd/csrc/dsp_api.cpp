@@ -613,6 +613,135 @@ struct Carve {
 };
 inline size_t carve_size(size_t n, size_t elem) { return (n * elem + 255) / 256 * 256; }
 
+// Per-device cache of handle buffers.  A destroyed handle's buffers are
+// kept, each with the events of the last work queued with them on every
+// stream the handle ran on; a later request that fits a kept block takes it
+// after making its own stream wait on those events.  Neither the release
+// nor the reuse waits on the host, and repeated prepares of one workload
+// allocate nothing.  Sizes are rounded up to 2 MiB; a request takes the
+// smallest kept block of at least its size and at most twice it.  Above
+// 4 GiB kept per device the oldest blocks are freed (after their events).
+// Events that a reuse has waited on are destroyed once they have completed.
+struct PoolBlock {
+    void *ptr;
+    size_t bytes;
+    std::vector<hipEvent_t> ev;
+};
+struct DevicePool {
+    int device;
+    std::vector<PoolBlock> kept;      // oldest first
+    std::vector<hipEvent_t> retired;  // waited on; destroyed once complete
+    size_t bytes = 0;
+};
+constexpr size_t kPoolCap = size_t(4) << 30;
+constexpr size_t kPoolGrain = size_t(2) << 20;
+std::mutex g_pool_mu;
+std::vector<DevicePool> g_pools;
+
+DevicePool &pool_of(int device) {
+    for (auto &p : g_pools)
+        if (p.device == device) return p;
+    g_pools.push_back(DevicePool{device, {}, {}, 0});
+    return g_pools.back();
+}
+
+void pool_sweep(DevicePool &P) {
+    size_t j = 0;
+    for (size_t i = 0; i < P.retired.size(); ++i) {
+        if (hipEventQuery(P.retired[i]) == hipSuccess)
+            hipEventDestroy(P.retired[i]);
+        else
+            P.retired[j++] = P.retired[i];
+    }
+    P.retired.resize(j);
+}
+
+// Frees every kept block of the device (after its events); the caller holds
+// the lock and has made the device current.
+void pool_drain(DevicePool &P) {
+    for (auto &b : P.kept) {
+        for (auto e : b.ev) {
+            hipEventSynchronize(e);
+            hipEventDestroy(e);
+        }
+        hipFree(b.ptr);
+    }
+    P.kept.clear();
+    P.bytes = 0;
+}
+
+// The device must be current.
+dsp_status pool_alloc(int device, hipStream_t stream, size_t bytes, void **out) {
+    *out = nullptr;
+    bytes = (std::max<size_t>(bytes, 1) + kPoolGrain - 1) / kPoolGrain * kPoolGrain;
+    PoolBlock blk{nullptr, 0, {}};
+    {
+        std::lock_guard<std::mutex> lock(g_pool_mu);
+        DevicePool &P = pool_of(device);
+        pool_sweep(P);
+        int best = -1;
+        for (int i = 0; i < (int)P.kept.size(); ++i) {
+            const size_t b = P.kept[i].bytes;
+            if (b >= bytes && b <= 2 * bytes && (best < 0 || b < P.kept[best].bytes)) best = i;
+        }
+        if (best >= 0) {
+            blk = P.kept[best];
+            P.kept.erase(P.kept.begin() + best);
+            P.bytes -= blk.bytes;
+            for (auto e : blk.ev) {
+                const hipError_t err = hipStreamWaitEvent(stream, e, 0);
+                P.retired.push_back(e);
+                if (err != hipSuccess) {
+                    hipFree(blk.ptr);
+                    return fail(DSP_EDEVICE, "hipStreamWaitEvent: %s", hipGetErrorString(err));
+                }
+            }
+            *out = blk.ptr;
+            return DSP_OK;
+        }
+    }
+    hipError_t err = hipMalloc(out, bytes);
+    if (err == hipErrorOutOfMemory) {
+        // give the kept blocks back and try once more
+        (void)hipGetLastError();
+        {
+            std::lock_guard<std::mutex> lock(g_pool_mu);
+            pool_drain(pool_of(device));
+        }
+        err = hipMalloc(out, bytes);
+    }
+    if (err != hipSuccess) {
+        *out = nullptr;
+        return fail(err == hipErrorOutOfMemory ? DSP_ENOMEM : DSP_EDEVICE, "hipMalloc(%zu): %s", bytes,
+                    hipGetErrorString(err));
+    }
+    return DSP_OK;
+}
+
+// Keeps a block for reuse once the events (moved in) have completed.  The
+// device must be current.
+void pool_release(int device, void *ptr, size_t bytes, std::vector<hipEvent_t> ev) {
+    if (!ptr) {
+        for (auto e : ev) hipEventDestroy(e);
+        return;
+    }
+    bytes = (std::max<size_t>(bytes, 1) + kPoolGrain - 1) / kPoolGrain * kPoolGrain;
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    DevicePool &P = pool_of(device);
+    P.kept.push_back(PoolBlock{ptr, bytes, std::move(ev)});
+    P.bytes += bytes;
+    while (P.bytes > kPoolCap && !P.kept.empty()) {
+        PoolBlock b = P.kept.front();
+        P.kept.erase(P.kept.begin());
+        P.bytes -= b.bytes;
+        for (auto e : b.ev) {
+            hipEventSynchronize(e);
+            hipEventDestroy(e);
+        }
+        hipFree(b.ptr);
+    }
+}
+
 double now_ms() {
     using namespace std::chrono;
     return duration<double, std::milli>(steady_clock::now().time_since_epoch()).count();
@@ -981,7 +1110,13 @@ struct dsp_handle {
     int D = 0, n_comp = 1;
     double host_ms = 0.0;
     bool layout_hit = false;
-    // device, owned by the handle
+    // device, owned by the handle: pieces of one block from the device's
+    // buffer cache (block, block_bytes)
+    void *block = nullptr;
+    size_t block_bytes = 0;
+    // per stream the handle's buffers were used on, an event after the last
+    // such work: the block goes back to the cache behind these events
+    mutable std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
     PixelRec *d_pix = nullptr;      // records with this optics' chi(k) and a(k)
     double *d_tay = nullptr;        // [n_pix][TAY_N] chi's Taylor coefficients about theta(k)
     double2 *d_sys = nullptr;       // [n_q][tri_size(D)]
@@ -997,19 +1132,62 @@ struct dsp_handle {
     std::vector<hipEvent_t> gram_ev;          // three per launch: start, Gram done, fixup done (timing)
     unsigned long long *d_work = nullptr;     // [tile][5] (DSP_FLAG_COUNT_WORK)
 
+    // Records that work using the buffers has been queued on s.
+    void mark(hipStream_t s) const {
+        for (auto &u : uses) {
+            if (u.first == s) {
+                hipEventRecord(u.second, s);
+                return;
+            }
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+            // no event: wait here instead, so the block is free to reuse
+            hipStreamSynchronize(s);
+            return;
+        }
+        hipEventRecord(e, s);
+        uses.emplace_back(s, e);
+    }
+
+    // One block for the buffers: sizes in elements of PixelRec, double
+    // (Taylor), double2 (systems), double (eigenvalues), double2 (U, c).
+    dsp_status alloc(hipStream_t s, size_t n_pix, size_t n_tay, size_t n_sys, size_t n_lam, size_t n_U, size_t n_c) {
+        const size_t total = carve_size(n_pix, sizeof(PixelRec)) + carve_size(n_tay, sizeof(double)) +
+                             carve_size(n_sys, sizeof(double2)) + carve_size(n_lam, sizeof(double)) +
+                             carve_size(n_U, sizeof(double2)) + carve_size(n_c, sizeof(double2));
+        dsp_status st = pool_alloc(device, s, total, &block);
+        if (st) return st;
+        block_bytes = total;
+        Carve cv{(char *)block};
+        d_pix = n_pix ? cv.take<PixelRec>(n_pix) : nullptr;
+        d_tay = n_tay ? cv.take<double>(n_tay) : nullptr;
+        d_sys = n_sys ? cv.take<double2>(n_sys) : nullptr;
+        d_lam = n_lam ? cv.take<double>(n_lam) : nullptr;
+        d_U = n_U ? cv.take<double2>(n_U) : nullptr;
+        d_c = n_c ? cv.take<double2>(n_c) : nullptr;
+        return DSP_OK;
+    }
+
     ~dsp_handle() {
         hipSetDevice(device);
-        hipFree(d_pix);
-        hipFree(d_tay);
-        hipFree(d_sys);
-        hipFree(d_lam);
-        hipFree(d_U);
-        hipFree(d_c);
+        std::vector<hipEvent_t> evs;
+        for (auto &u : uses) evs.push_back(u.second);
+        pool_release(device, block, block_bytes, std::move(evs));
         for (auto &e : ev)
             if (e) hipEventDestroy(e);
         for (auto &e : gram_ev)
             if (e) hipEventDestroy(e);
         hipFree(d_work);
+    }
+};
+
+// Marks a handle's use on a stream when the scope ends (success or failure).
+struct MarkOnExit {
+    const dsp_handle *h;
+    hipStream_t s;
+    ~MarkOnExit() {
+        if (h) h->mark(s);
     }
 };
 
@@ -1207,16 +1385,15 @@ dsp_status dsp_prepare(const void *G_c64_dev, int n_bf, const double *bf_coords_
     h->D = h->n_comp * am + 1;
     const int n_pix = (int)L.act.pix.size();
 
-    // per-handle buffers
+    // per-handle buffers: one block from the device's buffer cache; on every
+    // way out of this call (the guard runs before h is freed on failure) an
+    // event on the stream marks the last queued work with them
     const size_t n_sys = (size_t)g.n_q * tri_size(h->D);
-    if ((st = dev_alloc(&h->d_pix, (size_t)n_pix)) || (st = dev_alloc(&h->d_tay, (size_t)n_pix * TAY_N)) ||
-        (st = dev_alloc(&h->d_sys, n_sys)))
+    const bool ph = h->method == DSP_PHASE;
+    if ((st = h->alloc(stream, (size_t)n_pix, (size_t)n_pix * TAY_N, n_sys, ph ? (size_t)g.n_q * am : 0,
+                       ph ? (size_t)g.n_q * am * am : 0, ph ? (size_t)g.n_q * am : 0)))
         return st;
-    if (h->method == DSP_PHASE) {
-        if ((st = dev_alloc(&h->d_lam, (size_t)g.n_q * am)) || (st = dev_alloc(&h->d_U, (size_t)g.n_q * am * am)) ||
-            (st = dev_alloc(&h->d_c, (size_t)g.n_q * am)))
-            return st;
-    }
+    MarkOnExit mark_guard{h.get(), stream};
 
     if (h->timing) {
         for (auto &e : h->ev) HIP_TRY(hipEventCreate(&e));
@@ -1315,10 +1492,11 @@ dsp_status dsp_derive_phase(const dsp_handle *src, void *hip_stream, dsp_handle 
     const Geometry &g = h->L->geo;
     const int am = std::max(1, g.a_max);
     h->D = am + 1;
-    if ((st = dev_alloc(&h->d_sys, (size_t)g.n_q * tri_size(h->D))) ||
-        (st = dev_alloc(&h->d_lam, (size_t)g.n_q * am)) || (st = dev_alloc(&h->d_U, (size_t)g.n_q * am * am)) ||
-        (st = dev_alloc(&h->d_c, (size_t)g.n_q * am)))
+    if ((st = h->alloc(stream, 0, 0, (size_t)g.n_q * tri_size(h->D), (size_t)g.n_q * am, (size_t)g.n_q * am * am,
+                       (size_t)g.n_q * am)))
         return st;
+    MarkOnExit mark_guard{h.get(), stream};
+    MarkOnExit mark_src{src, stream};   // the source's systems are read on this stream
     HIP_TRY(launch_phase_from_complex(src->d_sys, h->d_sys, am, g.n_q, stream));
     if ((st = phase_eigen(h.get(), stream))) return st;
     h->host_ms = now_ms() - t0;
@@ -1437,6 +1615,7 @@ dsp_status dsp_solve(dsp_handle *h, const double *strengths_host, int S, void *x
             return fail(DSP_EINVAL, "strength %d must be finite and >= 0", i);
     HIP_TRY(hipSetDevice(h->device));
     hipStream_t stream = (hipStream_t)hip_stream;
+    MarkOnExit mark_guard{h, stream};
     const Geometry &g = h->L->geo;
     const int am = std::max(1, g.a_max);
     const int chunk = h->method == DSP_PHASE ? 64 : 32;
@@ -1568,6 +1747,7 @@ dsp_status dsp_export_system(const dsp_handle *h, void *aug_out_c128_dev, double
     if (!h) return fail(DSP_EINVAL, "handle is NULL");
     HIP_TRY(hipSetDevice(h->device));
     hipStream_t stream = (hipStream_t)hip_stream;
+    MarkOnExit mark_guard{h, stream};
     const Geometry &g = h->L->geo;
     if (aug_out_c128_dev) HIP_TRY(launch_export(h->d_sys, g.n_q, h->D, (double2 *)aug_out_c128_dev, stream));
     if (eig_out_dev) {
