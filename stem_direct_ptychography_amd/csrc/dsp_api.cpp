@@ -1019,6 +1019,12 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
         }
         t.cy = (float)(sy / grp.size());
         t.cx = (float)(sx / grp.size());
+        // radius of the lanes about the stored centre, for the kernel's
+        // per-pixel test (a bound: rounded up and widened by a part in 1e6)
+        double rad = 0.0;
+        for (size_t l = 0; l < grp.size(); ++l)
+            rad = std::max(rad, std::hypot((double)t.lyh[l] - (double)t.cy, (double)t.lix[l] - (double)t.cx));
+        t.rad = std::nextafter((float)(rad * (1.0 + 1e-6)), INFINITY);
         L->tiles.push_back(t);
     }
     const int n_tiles = (int)L->tiles.size();

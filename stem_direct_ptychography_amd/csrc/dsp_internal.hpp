@@ -205,7 +205,9 @@ struct alignas(64) GramTile {
 
 struct alignas(64) SsbTile {
     uint64_t valid;      // lanes inside the band (and inside the stored plane)
-    float cy, cx;        // mean (yh, ix) of the valid lanes (cost estimate)
+    float cy, cx;        // mean (yh, ix) of the valid lanes (cost estimate, centre of the pixel test)
+    float rad;           // largest distance of a valid lane's (yh, ix) from (cy, cx), rounded up
+    int pad;
     int16_t lyh[64];
     int16_t lix[64];
 };

@@ -1120,6 +1120,9 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
     __shared__ long long sgoff[SSB_CHUNK + PF];
     __shared__ long long sgrow[H16 == 2 ? SSB_CHUNK + PF : 1];   // pixel index x N (row scales)
     __shared__ double schi[MAXB * SSB_CHUNK];   // [set][pixel of the chunk] chi(k)
+    __shared__ unsigned smask[SSB_CHUNK];        // per pixel of the chunk: the reach test's L/R bits
+    __shared__ double2 scent;                    // lambda c, c the tile centre
+    __shared__ double sthr;                      // the reach test's squared bound
     const int lane = threadIdx.x;
     for (int i = lane; i < TRIG_N; i += 64) T[i] = prm.trig[i];
 
@@ -1159,6 +1162,16 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
         double acc[NACC];
 #pragma unroll
         for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
+        // Reach test: the lanes' frequencies lie within rad of the tile
+        // centre c, so a lobe can be in support at pixel k only if
+        // |lambda k -/+ lambda c| < lambda r + rad lambda dq; sthr is that
+        // bound squared, widened by a part in 1e9 against rounding.  Pixels
+        // failing both tests add only their signal power.
+        if (lane == 0) {
+            scent = make_double2((double)tile->cy * prm.ldq, (double)tile->cx * prm.ldq);
+            const double rr = sqrt(prm.ap.lrlim2) + (double)tile->rad * prm.ldq;
+            sthr = rr * rr * (1.0 + 1e-9);
+        }
 
         // records, plane offsets and the sets' chi(k) staged in LDS per chunk;
         // G a group of PF pixels ahead; the chunk's tail runs on zero records
@@ -1178,10 +1191,16 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                 // herm16: the pixel's scale rides in the record's spare field
                 if (H16 == 1) rec.pad = (double)gsc[goffs[c0 + lane] / prm.plane];
                 srec[lane] = rec;
+                const double2 c = scent;
+                const double thr = sthr;
+                const double ly = rec.lky - c.x, lx = rec.lkx - c.y;
+                const double ry = rec.lky + c.x, rx = rec.lkx + c.y;
+                smask[lane] = (fma(ly, ly, lx * lx) < thr ? 1u : 0u) | (fma(ry, ry, rx * rx) < thr ? 2u : 0u);
             } else {
                 PixelRec z;
                 z.lky = z.lkx = z.amp0 = z.sw = z.chi0 = z.pad = 0.0;
                 srec[lane] = z;
+                smask[lane] = 0u;
             }
 #pragma unroll
             for (int b = 0; b < MAXB; ++b)
@@ -1216,6 +1235,14 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                     if (cj) gim = -gim;
                     if (r >= cn) gre = gim = 0.0;
                     const double *chi0s = schi + r;
+                    // (one set only: with more, the branch costs registers, spills or
+                    // a wave per SIMD)
+                    if (MAXB == 1 && __builtin_amdgcn_readfirstlane(smask[r]) == 0u) {
+                        // no lane can have a lobe in support: signal power only
+                        const double gr = gre * sw, gi = gim * sw;
+                        acc[NACC - 1] = fma(gr, gr, fma(gi, gi, acc[NACC - 1]));
+                        continue;
+                    }
                     // one pixel's update (kept in the kernel body: the sets' chi
                     // coefficients are read straight from the kernel arguments)
                     const double lrlim2 = prm.ap.lrlim2, lrin2 = prm.ap.lrin2, lkc = prm.ap.lkc, inv_ldk = prm.ap.inv_ldk;
