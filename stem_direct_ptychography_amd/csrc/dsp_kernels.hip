@@ -292,9 +292,8 @@ __device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, do
 // One pixel's update of a lane's sums: the lobes of every slot, then the
 // rank-one update of the augmented Gram.  pm (wave-uniform) holds two bits
 // per slot, L and R, clear when no lane of the tile can have that lobe in
-// support at this pixel; a slot with both clear is skipped whole.  A column's terms run when some
-// lane of the wave has it, a pair's when some lane has both (the other lanes
-// add exact zeros).
+// support at this pixel; a slot with both clear is skipped whole (its
+// columns are zero).
 // Lobe phases, two schemes (GramTaylor picks one per kernel):
 //  TAY: chi expanded about theta(k) (the pixel's Taylor coefficients, read
 //       from LDS into registers once per pixel); one evaluation of the even
@@ -327,10 +326,13 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
 #pragma unroll
     for (int s = 0; s < NJ; ++s) {
         if (!((pm >> (2 * s)) & 3u)) {
-            // no lane of the tile has either lobe of this slot in support:
-            // the column stays out of the update (its values are never read)
+            // no lane of the tile has either lobe of this slot in support
             bal[s] = 0ull;
-            if (METHOD == 1) bal[NJ + s] = 0ull;
+            tr[s] = ti[s] = 0.0;
+            if (METHOD == 1) {
+                bal[NJ + s] = 0ull;
+                tr[NJ + s] = ti[NJ + s] = 0.0;
+            }
             continue;
         }
         const double Qy_s = (double)(yh + jyN[s]) * ldq, Qx_s = (double)(ix + jxN[s]) * ldq;
@@ -396,17 +398,24 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
         }
     }
 
+    // Column c is updated when the slot test admits its lobe (phase: either
+    // lobe) at this pixel: the bits are known at the pixel's start, so the
+    // branch does not wait for the lobes, and columns that no lane has add
+    // exact zeros.  Pairs held in registers then run without a test (a
+    // branch costs more than their FMAs); pairs held in LDS, whose atomics
+    // are dearer, run when some lane has both columns.
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        if (!bal[c]) continue;
+        const unsigned bits = METHOD == 0 ? (pm >> (2 * c)) & 3u : (pm >> (c < NJ ? 2 * c : 2 * (c - NJ) + 1)) & 1u;
+        if (!bits) continue;
         acc[c] = fma(tr[c], tr[c], fma(ti[c], ti[c], acc[c]));
         // right side <col c, g> = conj(t_c) g
         acc[Sh::re(c, NC)] = fma(tr[c], gr, fma(ti[c], gi, acc[Sh::re(c, NC)]));
         acc[Sh::im(c, NC)] = fma(tr[c], gi, fma(-ti[c], gr, acc[Sh::im(c, NC)]));
 #pragma unroll
         for (int d = c + 1; d < NC; ++d) {
-            if (!(bal[c] & bal[d])) continue;
             if (GramLds<NJ, METHOD>::in_lds(c, d)) {
+                if (!(bal[c] & bal[d])) continue;
                 // LDS FP64 atomic adds without return: the wave does not wait
                 // for a read of the running sum.  Each lane owns its address
                 // and a wave's LDS operations run in issue order, so the sums
