@@ -22,13 +22,18 @@
 #include <memory>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <tuple>
 #include <vector>
 
 using namespace dsp;
 
 // Gram launch size: resident waves (from the kernel's occupancy) times this.
-constexpr int GRAM_ROUNDS = 4;
+// Stream-K waves per resident wave slot.  More, shorter waves let the
+// hardware's dispatch even out SIMDs that run at different speeds; past
+// eight the partial-sum fixup costs more than the launches gain (whole
+// full-frame step: 27.6 ms at 4, 27.2 at 8, 27.3 at 12 and at 16).
+constexpr int GRAM_ROUNDS = 8;
 
 namespace {
 
@@ -465,29 +470,6 @@ dsp_status build_active(const double *k, const double *w, int n_bf, const dsp_op
 // ---------------------------------------------------------------------------
 // stream-K plan of one Gram launch
 // ---------------------------------------------------------------------------
-// Estimated cost of a tile: per pixel a fixed part plus the support tests of
-// its slots, plus the lobes its wave evaluates.  A slot's lobes are non-zero
-// where the pixel disk overlaps the disk moved by -/+Q: two lenses of area
-// 2 R^2 acos(D / 2R) - (D / 2) sqrt(4 R^2 - D^2) at D = |Q| (tile centre).
-double tile_cost(const GramTile &t, const Geometry &g, double ra, int n_pix) {
-    constexpr double C_PIX = 30.0, C_SLOT = 10.0, C_LOBE = 80.0;
-    unsigned used = 0;
-    for (int l = 0; l < 64; ++l)
-        if (t.qidx[l] >= 0) used |= t.mask[l];
-    const double disk = M_PI * ra * ra;
-    double lobes = 0.0;
-    for (int s = 0; s < t.nj; ++s) {
-        if (!((used >> s) & 1u)) continue;
-        const double qy = (t.cy + (double)t.jy[s] * g.N) * g.dq;
-        const double qx = (t.cx + (double)t.jx[s] * g.N) * g.dq;
-        const double D = std::hypot(qy, qx);
-        if (D >= 2.0 * ra) continue;
-        const double lens = 2.0 * ra * ra * std::acos(D / (2.0 * ra)) - 0.5 * D * std::sqrt(4.0 * ra * ra - D * D);
-        lobes += 2.0 * lens / disk * n_pix;
-    }
-    return n_pix * (C_PIX + C_SLOT * t.nj) + C_LOBE * lobes;
-}
-
 struct StreamKPlan {
     std::vector<long long> wbegin;   // [W + 1]
     std::vector<int> seg_off;        // [W]
@@ -523,6 +505,85 @@ void plan_stream_k(const std::vector<double> &cost, int n_pix, int n_waves, Stre
         pl.seg_off[w] = ns;
         long long it = pl.wbegin[w];
         const long long e = pl.wbegin[w + 1];
+        while (it < e) {
+            const int tt = (int)(it / n_pix);
+            if (pl.seg_first[tt] < 0) pl.seg_first[tt] = ns;
+            it = std::min(e, (long long)(tt + 1) * n_pix);
+            ++ns;
+        }
+    }
+    pl.seg_first[T] = ns;
+    pl.n_segs = ns;
+}
+
+// Estimated cost of every (tile, pixel) iteration of one Gram launch, in
+// units of about four instructions: a fixed part per pixel, and per slot
+// the kernels' own reach test (tile centre and radius): a slot that may
+// have a lobe in support costs its support tests, each admitted lobe an
+// evaluation.  Tile-major, n_pix per tile; threads split the tiles.
+void gram_iteration_costs(const GramTile *tiles, int nt, const std::vector<PixelBase> &pix, const Geometry &g,
+                          double ra, std::vector<uint16_t> &cost) {
+    constexpr int C_PIX = 8, C_SLOT = 3, C_LOBE = 20;
+    const int n_pix = (int)pix.size();
+    cost.assign((size_t)nt * n_pix, 0);
+    auto work = [&](int t0, int t1) {
+        for (int t = t0; t < t1; ++t) {
+            const GramTile &tl = tiles[t];
+            unsigned used = 0;
+            for (int l = 0; l < 64; ++l)
+                if (tl.qidx[l] >= 0) used |= tl.mask[l];
+            double cy[MAX_SLOTS], cx[MAX_SLOTS];
+            for (int s = 0; s < tl.nj; ++s) {
+                cy[s] = ((double)tl.cy + (double)tl.jy[s] * g.N) * g.dq;
+                cx[s] = ((double)tl.cx + (double)tl.jx[s] * g.N) * g.dq;
+            }
+            const double rr = ra + (double)tl.rad * g.dq;
+            const double thr = rr * rr;
+            uint16_t *c = cost.data() + (size_t)t * n_pix;
+            for (int p = 0; p < n_pix; ++p) {
+                const double ky = pix[p].ky, kx = pix[p].kx;
+                int v = C_PIX;
+                for (int s = 0; s < tl.nj; ++s) {
+                    if (!((used >> s) & 1u)) continue;
+                    const double ly = ky - cy[s], lx = kx - cx[s], ry = ky + cy[s], rx = kx + cx[s];
+                    const int nl = (ly * ly + lx * lx < thr) + (ry * ry + rx * rx < thr);
+                    if (nl) v += C_SLOT + C_LOBE * nl;
+                }
+                c[p] = (uint16_t)v;
+            }
+        }
+    };
+    const int nth = std::max(1, std::min<int>({16, (int)std::thread::hardware_concurrency(), nt / 16 + 1}));
+    std::vector<std::thread> th;
+    for (int i = 1; i < nth; ++i) th.emplace_back(work, (int)((long long)nt * i / nth), (int)((long long)nt * (i + 1) / nth));
+    work(0, (int)((long long)nt / nth));
+    for (auto &x : th) x.join();
+}
+
+// Split the tiles x pixels iteration space into n_waves contiguous ranges of
+// equal estimated cost (per-iteration costs, tile-major), then number each
+// wave's tile segments.
+void plan_stream_k_iter(const std::vector<uint16_t> &cost, int T, int n_pix, int n_waves, StreamKPlan &pl) {
+    const long long total_it = (long long)T * n_pix;
+    unsigned long long total = 0;
+    for (uint16_t v : cost) total += v;
+    const int W = n_waves;
+    pl.wbegin.assign(W + 1, total_it);
+    pl.wbegin[0] = 0;
+    unsigned long long acc = 0;
+    int w = 1;
+    for (long long i = 0; i < total_it && w < W; ++i) {
+        acc += cost[i];
+        // boundary w after the iteration where the running cost reaches w / W
+        while (w < W && acc * (unsigned long long)W >= total * (unsigned long long)w) pl.wbegin[w++] = i + 1;
+    }
+    pl.seg_off.assign(W, 0);
+    pl.seg_first.assign(T + 1, -1);
+    int ns = 0;
+    for (int ww = 0; ww < W; ++ww) {
+        pl.seg_off[ww] = ns;
+        long long it = pl.wbegin[ww];
+        const long long e = pl.wbegin[ww + 1];
         while (it < e) {
             const int tt = (int)(it / n_pix);
             if (pl.seg_first[tt] < 0) pl.seg_first[tt] = ns;
@@ -875,10 +936,10 @@ dsp_status build_layout(const LayoutKey &key, const dsp_scan *scan, const dsp_op
         bpc = std::max(1, bpc);
         const long long total_it = (long long)nt * n_pix;
         const int W = (int)std::max(1LL, std::min((long long)bpc * n_cu * GRAM_ROUNDS, total_it / 64));
-        std::vector<double> cost(nt);
-        for (int t = 0; t < nt; ++t) cost[t] = tile_cost(L->tg.tiles[L->tg.group_off[gi] + t], g, ra, n_pix);
+        std::vector<uint16_t> cost;
+        gram_iteration_costs(L->tg.tiles.data() + L->tg.group_off[gi], nt, L->act.pix, g, ra, cost);
         StreamKPlan plan;
-        plan_stream_k(cost, n_pix, W, plan);
+        plan_stream_k_iter(cost, nt, n_pix, W, plan);
         L->sk_waves[gi] = W;
         L->max_partial = std::max(L->max_partial, (size_t)plan.n_segs * gram_nacc(nj, key.method) * 64);
         L->wb_off[gi] = L->sk_wbegin.size();

@@ -600,14 +600,28 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
 
 // Fixup, step 1: thread (tile t, accumulator i, lane) adds tile t's segment
 // sums in iteration order and stores the total in the tile's first segment.
-// Grid (NACC, n_tiles) of 64-lane workgroups.
-__global__ __launch_bounds__(64) void gram_reduce_kernel(GramParams prm, int nacc) {
-    const int lane = threadIdx.x;
-    const int i = blockIdx.x;
+// Grid (ceil(NACC / 4), n_tiles) of 256-thread workgroups, four accumulators
+// per workgroup; the loads of four segments go out together, the adds stay
+// in segment order.
+__global__ __launch_bounds__(256) void gram_reduce_kernel(GramParams prm, int nacc) {
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int t = blockIdx.y;
+    if (i >= nacc) return;
     const int s0 = prm.seg_first[t], s1 = prm.seg_first[t + 1];
+    const double *P = prm.partial + (size_t)i * 64 + lane;
+    const size_t stride = (size_t)nacc * 64;
     double acc = 0.0;
-    for (int sg = s0; sg < s1; ++sg) acc += prm.partial[((size_t)sg * nacc + i) * 64 + lane];
+    int sg = s0;
+    for (; sg + 4 <= s1; sg += 4) {
+        const double a0 = P[(size_t)sg * stride], a1 = P[(size_t)(sg + 1) * stride];
+        const double a2 = P[(size_t)(sg + 2) * stride], a3 = P[(size_t)(sg + 3) * stride];
+        acc += a0;
+        acc += a1;
+        acc += a2;
+        acc += a3;
+    }
+    for (; sg < s1; ++sg) acc += P[(size_t)sg * stride];
     prm.partial[((size_t)s0 * nacc + i) * 64 + lane] = acc;
 }
 
@@ -1690,7 +1704,7 @@ template <int NJ, int METHOD>
 struct GramFixupLaunch {
     static hipError_t run(const GramParams &prm, int n_tiles, hipStream_t st) {
         const int nacc = GramShape<NJ, METHOD>::NACC;
-        gram_reduce_kernel<<<dim3(nacc, n_tiles), 64, 0, st>>>(prm, nacc);
+        gram_reduce_kernel<<<dim3((nacc + 3) / 4, n_tiles), 256, 0, st>>>(prm, nacc);
         DSP_CHECK_LAUNCH();
         gram_write_kernel<NJ, METHOD><<<n_tiles, 64, 0, st>>>(prm);
         DSP_CHECK_LAUNCH();
@@ -1935,7 +1949,7 @@ hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *ti
     memset(&gp, 0, sizeof gp);
     gp.seg_first = prm.seg_first;
     gp.partial = prm.partial;
-    gram_reduce_kernel<<<dim3(nacc, n_tiles), 64, 0, st>>>(gp, nacc);
+    gram_reduce_kernel<<<dim3((nacc + 3) / 4, n_tiles), 256, 0, st>>>(gp, nacc);
     DSP_CHECK_LAUNCH();
     switch (maxb) {
         case 1: ssb_write_kernel<1><<<n_tiles, 64, 0, st>>>(prm, tile_part); break;
