@@ -477,45 +477,6 @@ struct StreamKPlan {
     int n_segs = 0;
 };
 
-// Split the tiles x pixels iteration space into n_waves contiguous ranges of
-// equal estimated cost (the cost of a tile spread evenly over its pixels),
-// then number each wave's tile segments.
-void plan_stream_k(const std::vector<double> &cost, int n_pix, int n_waves, StreamKPlan &pl) {
-    const int T = (int)cost.size();
-    std::vector<double> cum(T + 1, 0.0);
-    for (int t = 0; t < T; ++t) cum[t + 1] = cum[t] + std::max(cost[t], 1e-30);
-    const long long total_it = (long long)T * n_pix;
-    const int W = n_waves;
-    pl.wbegin.assign(W + 1, 0);
-    pl.wbegin[W] = total_it;
-    int t = 0;
-    for (int w = 1; w < W; ++w) {
-        const double target = cum[T] * ((double)w / W);
-        while (t < T - 1 && cum[t + 1] <= target) ++t;
-        double frac = (target - cum[t]) / (cum[t + 1] - cum[t]);
-        frac = std::min(1.0, std::max(0.0, frac));
-        long long b = (long long)t * n_pix + (long long)std::floor(frac * n_pix);
-        b = std::min(total_it, std::max(pl.wbegin[w - 1], b));
-        pl.wbegin[w] = b;
-    }
-    pl.seg_off.assign(W, 0);
-    pl.seg_first.assign(T + 1, -1);
-    int ns = 0;
-    for (int w = 0; w < W; ++w) {
-        pl.seg_off[w] = ns;
-        long long it = pl.wbegin[w];
-        const long long e = pl.wbegin[w + 1];
-        while (it < e) {
-            const int tt = (int)(it / n_pix);
-            if (pl.seg_first[tt] < 0) pl.seg_first[tt] = ns;
-            it = std::min(e, (long long)(tt + 1) * n_pix);
-            ++ns;
-        }
-    }
-    pl.seg_first[T] = ns;
-    pl.n_segs = ns;
-}
-
 // Estimated cost of every (tile, pixel) iteration of one Gram launch, in
 // units of about four instructions: a fixed part per pixel, and per slot
 // the kernels' own reach test (tile centre and radius): a slot that may
@@ -523,7 +484,9 @@ void plan_stream_k(const std::vector<double> &cost, int n_pix, int n_waves, Stre
 // evaluation.  Tile-major, n_pix per tile; threads split the tiles.
 void gram_iteration_costs(const GramTile *tiles, int nt, const std::vector<PixelBase> &pix, const Geometry &g,
                           double ra, std::vector<uint16_t> &cost) {
-    constexpr int C_PIX = 8, C_SLOT = 3, C_LOBE = 20;
+    // C_PIX covers the pixel's G load and power term as well as its
+    // instructions (measured: 8 and 32 bracket the best plans)
+    constexpr int C_PIX = 16, C_SLOT = 3, C_LOBE = 20;
     const int n_pix = (int)pix.size();
     cost.assign((size_t)nt * n_pix, 0);
     auto work = [&](int t0, int t1) {
@@ -563,10 +526,11 @@ void gram_iteration_costs(const GramTile *tiles, int nt, const std::vector<Pixel
 // Split the tiles x pixels iteration space into n_waves contiguous ranges of
 // equal estimated cost (per-iteration costs, tile-major), then number each
 // wave's tile segments.
-void plan_stream_k_iter(const std::vector<uint16_t> &cost, int T, int n_pix, int n_waves, StreamKPlan &pl) {
+template <class Cost>
+void plan_stream_k_iter(const Cost &cost, int T, int n_pix, int n_waves, StreamKPlan &pl) {
     const long long total_it = (long long)T * n_pix;
     unsigned long long total = 0;
-    for (uint16_t v : cost) total += v;
+    for (long long i = 0; i < total_it; ++i) total += cost[i];
     const int W = n_waves;
     pl.wbegin.assign(W + 1, total_it);
     pl.wbegin[0] = 0;
@@ -593,6 +557,33 @@ void plan_stream_k_iter(const std::vector<uint16_t> &cost, int T, int n_pix, int
     }
     pl.seg_first[T] = ns;
     pl.n_segs = ns;
+}
+
+// Reach bits of every (SSB tile, pixel) iteration, as the one-set SSB kernel
+// tests them (tile centre and radius): bit 0 when the L lobe may be in
+// support for some lane, bit 1 the R lobe.  Tile-major; threads split the
+// tiles.
+void ssb_reach_bits(const std::vector<SsbTile> &tiles, const std::vector<PixelBase> &pix, double dq, double ra,
+                    std::vector<uint8_t> &bits) {
+    const int nt = (int)tiles.size(), n_pix = (int)pix.size();
+    bits.assign((size_t)nt * n_pix, 0);
+    auto work = [&](int t0, int t1) {
+        for (int t = t0; t < t1; ++t) {
+            const SsbTile &tl = tiles[t];
+            const double cy = (double)tl.cy * dq, cx = (double)tl.cx * dq;
+            const double rr = ra + (double)tl.rad * dq, thr = rr * rr;
+            uint8_t *b = bits.data() + (size_t)t * n_pix;
+            for (int p = 0; p < n_pix; ++p) {
+                const double ly = pix[p].ky - cy, lx = pix[p].kx - cx, ry = pix[p].ky + cy, rx = pix[p].kx + cx;
+                b[p] = (uint8_t)((ly * ly + lx * lx < thr ? 1 : 0) | (ry * ry + rx * rx < thr ? 2 : 0));
+            }
+        }
+    };
+    const int nth = std::max(1, std::min<int>({16, (int)std::thread::hardware_concurrency(), nt / 16 + 1}));
+    std::vector<std::thread> th;
+    for (int i = 1; i < nth; ++i) th.emplace_back(work, (int)((long long)nt * i / nth), (int)((long long)nt * (i + 1) / nth));
+    work(0, (int)((long long)nt / nth));
+    for (auto &x : th) x.join();
 }
 
 // (cos, sin)(j pi / 128), j = 0..255, rounded from long double.
@@ -1100,27 +1091,32 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
         int n_cu = 0;
         HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, key.device));
         const double ra = std::sqrt(make_aperture_dev(optics).rlim2);
-        const double disk = M_PI * ra * ra;
+        // per (tile, pixel): the lobes the kernels' reach test admits; the
+        // cost, in units of about four instructions, is a fixed part per
+        // pixel (all the one-set kernel pays when no lobe is admitted), the
+        // sets' sums, and per admitted lobe and set an evaluation
+        std::vector<uint8_t> reach;
+        ssb_reach_bits(L->tiles, L->act.pix, dq, ra, reach);
         static const int maxbs[4] = {1, 2, 4, 8};
         for (int mi = 0; mi < 4; ++mi) {
             const int maxb = maxbs[mi];
-            // per tile: fixed per-pixel work plus the sets' lobes (two lenses at the tile centre)
-            std::vector<double> cost(n_tiles);
-            for (int t = 0; t < n_tiles; ++t) {
-                const SsbTile &tt = L->tiles[t];
-                const double D = std::hypot(tt.cy * dq, tt.cx * dq);
-                double lens = 0.0;
-                if (D < 2.0 * ra)
-                    lens = 2.0 * ra * ra * std::acos(D / (2.0 * ra)) - 0.5 * D * std::sqrt(4.0 * ra * ra - D * D);
-                cost[t] = n_pix * 40.0 + 80.0 * maxb * 2.0 * lens / disk * n_pix;
-            }
+            struct Cost {
+                const std::vector<uint8_t> *bits;
+                int maxb;
+                unsigned operator[](long long i) const {
+                    const unsigned b = (*bits)[(size_t)i], nl = (b & 1u) + (b >> 1);
+                    constexpr unsigned C_PIX = 14;   // G load and power; measured 6..14
+                    if (maxb == 1 && nl == 0) return C_PIX;
+                    return C_PIX + 2u * maxb + 20u * maxb * nl;
+                }
+            } cost{&reach, maxb};
             int bpc = 0;
             HIP_TRY(ssb_occupancy(maxb, &bpc));
             bpc = std::max(1, bpc);
             const long long total_it = (long long)n_tiles * n_pix;
             const int W = (int)std::max(1LL, std::min((long long)bpc * n_cu * GRAM_ROUNDS, total_it / 64));
             StreamKPlan plan;
-            plan_stream_k(cost, n_pix, W, plan);
+            plan_stream_k_iter(cost, n_tiles, n_pix, W, plan);
             L->waves[mi] = W;
             L->n_segs[mi] = plan.n_segs;
             L->wbegin[mi] = plan.wbegin;
