@@ -477,6 +477,24 @@ struct StreamKPlan {
     int n_segs = 0;
 };
 
+// Runs work(t0, t1) over [0, nt) split among up to 16 threads; a range whose
+// thread cannot be started runs on the calling thread.
+template <class F>
+void parallel_tiles(int nt, const F &work) {
+    const int nth = std::max(1, std::min<int>({16, (int)std::thread::hardware_concurrency(), nt / 16 + 1}));
+    std::vector<std::thread> th;
+    for (int i = 1; i < nth; ++i) {
+        const int t0 = (int)((long long)nt * i / nth), t1 = (int)((long long)nt * (i + 1) / nth);
+        try {
+            th.emplace_back(work, t0, t1);
+        } catch (...) {
+            work(t0, t1);
+        }
+    }
+    work(0, (int)((long long)nt / nth));
+    for (auto &x : th) x.join();
+}
+
 // Estimated cost of every (tile, pixel) iteration of one Gram launch, in
 // units of about four instructions: a fixed part per pixel, and per slot
 // the kernels' own reach test (tile centre and radius): a slot that may
@@ -516,11 +534,7 @@ void gram_iteration_costs(const GramTile *tiles, int nt, const std::vector<Pixel
             }
         }
     };
-    const int nth = std::max(1, std::min<int>({16, (int)std::thread::hardware_concurrency(), nt / 16 + 1}));
-    std::vector<std::thread> th;
-    for (int i = 1; i < nth; ++i) th.emplace_back(work, (int)((long long)nt * i / nth), (int)((long long)nt * (i + 1) / nth));
-    work(0, (int)((long long)nt / nth));
-    for (auto &x : th) x.join();
+    parallel_tiles(nt, work);
 }
 
 // Split the tiles x pixels iteration space into n_waves contiguous ranges of
@@ -579,11 +593,7 @@ void ssb_reach_bits(const std::vector<SsbTile> &tiles, const std::vector<PixelBa
             }
         }
     };
-    const int nth = std::max(1, std::min<int>({16, (int)std::thread::hardware_concurrency(), nt / 16 + 1}));
-    std::vector<std::thread> th;
-    for (int i = 1; i < nth; ++i) th.emplace_back(work, (int)((long long)nt * i / nth), (int)((long long)nt * (i + 1) / nth));
-    work(0, (int)((long long)nt / nth));
-    for (auto &x : th) x.join();
+    parallel_tiles(nt, work);
 }
 
 // (cos, sin)(j pi / 128), j = 0..255, rounded from long double.
