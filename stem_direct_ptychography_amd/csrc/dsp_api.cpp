@@ -1849,10 +1849,14 @@ struct SsbPassBufs {
     double *chi;        // [n_pix][MAX_SETS_DEV]
     double *part;       // stream-K partial sums
     double *tile_part;  // [n_tiles][partial stride]
+    double *tay;        // [n_pix][TAY_N] for a Taylor pass, else null
 };
 
 // One pass over G for B sets on layout L: pixel terms, then the SSB kernel
-// with lanes on the (M, M/2 + 1) grid writing S and N there.
+// with lanes on the (M, M/2 + 1) grid writing S and N there.  With one set
+// and bufs.tay, the kernel takes both lobes' phases from chi's Taylor
+// coefficients about theta(k) (one evaluation of the even and odd parts in
+// lambda q per pixel instead of the polynomial at both displaced points).
 static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int B, const void *G_c64_dev,
                            const void *GQ_dev, const float *gscale_dev, int h16_rows, int N, int M, double2 *S_out,
                            double *N_out, const SsbPassBufs &bufs, int device, hipStream_t stream) {
@@ -1867,7 +1871,9 @@ static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int 
     for (int b = 0; b < B; ++b) {
         const OpticsDev od = make_optics_dev(sets_host + b);
         // a(k) once (set 0 writes it), chi(k) per set
-        if (b == 0) HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, nullptr, 0, nullptr, stream));
+        if (b == 0)
+            HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, nullptr, 0, B == 1 ? bufs.tay : nullptr,
+                                       stream));
         HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, bufs.chi + b, MAX_SETS_DEV, nullptr, stream));
         sp.tau_y[b] = od.tau_y;
         sp.tau_x[b] = od.tau_x;
@@ -1882,6 +1888,7 @@ static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int 
     sp.pix = bufs.pix;
     sp.goff = L.d_goff;
     sp.chi_tab = bufs.chi;
+    sp.tay = B == 1 ? bufs.tay : nullptr;
     sp.n_pix = n_pix;
     sp.tiles = L.d_tiles;
     sp.N = N;
@@ -2032,9 +2039,10 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
 
     // per-call tables in the stream's scratch arena
     const size_t n_part = (size_t)L.n_segs[mi] * ssb_nacc(maxb) * 64;
+    const size_t n_tay = B == 1 ? (size_t)n_pix * TAY_N : 0;
     const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) +
                         carve_size(n_part, sizeof(double)) + carve_size((size_t)n_tiles * stride, sizeof(double)) +
-                        carve_size(B + 1, sizeof(double));
+                        carve_size(B + 1, sizeof(double)) + carve_size(std::max<size_t>(1, n_tay), sizeof(double));
     char *scr = nullptr;
     if ((st = arena_get(device, stream, need, &scr))) return st;
     Carve cv{scr};
@@ -2043,8 +2051,9 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
     double *d_part = cv.take<double>(n_part);
     double *d_tile_part = cv.take<double>((size_t)n_tiles * stride);
     double *d_E = cv.take<double>(B + 1);
+    double *d_tay = cv.take<double>(std::max<size_t>(1, n_tay));
 
-    SsbPassBufs bufs{d_pix, d_chi, d_part, d_tile_part};
+    SsbPassBufs bufs{d_pix, d_chi, d_part, d_tile_part, B == 1 ? d_tay : nullptr};
     if ((st = ssb_pass(L, sets_host, B, G_c64_dev, GQ_dev, gscale_dev, h16_rows, N, N, (double2 *)S_out_c128_dev,
                        norm_out_dev, bufs, device, stream)))
         return st;
@@ -2110,6 +2119,7 @@ dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_
     if ((st = arena_get(device, stream, need, &scr))) return st;
     Carve cv{scr};
     SsbPassBufs bufs;
+    bufs.tay = nullptr;   // previews keep the direct polynomial (mostly one lobe per pixel)
     bufs.pix = cv.take<PixelRec>(n_pix);
     bufs.chi = cv.take<double>((size_t)MAX_SETS_DEV * n_pix);
     bufs.part = cv.take<double>(n_part);

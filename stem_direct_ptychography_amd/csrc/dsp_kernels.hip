@@ -1133,17 +1133,22 @@ struct SsbWaves {
 // H16: G comes as herm16 snorm16 pairs, unpacked as max(q / 32767, -1) s in
 // FP64 at use; H16 = 1: one scale per pixel (staged with the pixel record);
 // H16 = 2: one scale per stored row, fetched with G for the lane's row.
-template <int MAXB, bool DEPTH, int H16>
+template <int MAXB, bool DEPTH, int H16, bool TAYS>
 __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbParams prm) {
     constexpr int NACC = 3 * MAXB + 1;
     constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
     using GT = typename std::conditional<H16 != 0, short2, float2>::type;
     __shared__ double2 T[TRIG_N];
-    __shared__ PixelRec srec[SSB_CHUNK];
-    __shared__ long long sgoff[SSB_CHUNK + PF];
-    __shared__ long long sgrow[H16 == 2 ? SSB_CHUNK + PF : 1];   // pixel index x N (row scales)
-    __shared__ double schi[MAXB * SSB_CHUNK];   // [set][pixel of the chunk] chi(k)
-    __shared__ unsigned smask[SSB_CHUNK];        // per pixel of the chunk: the reach test's L/R bits
+    // TAYS (one set): both lobes' phases from chi's Taylor coefficients about
+    // theta(k), staged per chunk (16 pixels keep four waves per SIMD)
+    constexpr int CHK = TAYS ? 16 : SSB_CHUNK;
+    static_assert(!TAYS || MAXB == 1, "the Taylor pass has one set");
+    __shared__ PixelRec srec[CHK];
+    __shared__ long long sgoff[CHK + PF];
+    __shared__ long long sgrow[H16 == 2 ? CHK + PF : 1];   // pixel index x N (row scales)
+    __shared__ double schi[MAXB * CHK];   // [set][pixel of the chunk] chi(k)
+    __shared__ unsigned smask[CHK];        // per pixel of the chunk: the reach test's L/R bits
+    __shared__ double stay[TAYS ? CHK * TAY_N : 1];   // [pixel][TAY_N]
     __shared__ double2 scent;                    // lambda c, c the tile centre
     __shared__ double sthr;                      // the reach test's squared bound
     const int lane = threadIdx.x;
@@ -1181,6 +1186,7 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
         const long long lane_off = valid ? (long long)iyq * prm.nh + ixq : 0;
         const double qy = (double)yh * prm.ldq, qx = (double)ix * prm.ldq;   // lambda K
         const double q2 = fma(qy, qy, qx * qx);
+        const double qX = qx * qx, qY = qy * qy, qZ = qx * qy;   // Taylor pass: powers of d = lambda q
 
         double acc[NACC];
 #pragma unroll
@@ -1206,10 +1212,12 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
             ga[i] = G[go + lane_off];
             if (H16 == 2) sa[i] = gsc[(go / prm.plane) * prm.N + iyq];
         }
-        for (int c0 = p0; c0 < p1; c0 += SSB_CHUNK) {
-            const int cn = (p1 - c0) < SSB_CHUNK ? (p1 - c0) : SSB_CHUNK;
+        for (int c0 = p0; c0 < p1; c0 += CHK) {
+            const int cn = (p1 - c0) < CHK ? (p1 - c0) : CHK;
             __syncthreads();
-            if (lane < cn) {
+            if (lane >= CHK) {
+                // lanes past the chunk stage nothing
+            } else if (lane < cn) {
                 PixelRec rec = pix[c0 + lane];
                 // herm16: the pixel's scale rides in the record's spare field
                 if (H16 == 1) rec.pad = (double)gsc[goffs[c0 + lane] / prm.plane];
@@ -1225,10 +1233,17 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                 srec[lane] = z;
                 smask[lane] = 0u;
             }
+            if (lane < CHK) {
 #pragma unroll
-            for (int b = 0; b < MAXB; ++b)
-                schi[b * SSB_CHUNK + lane] = (lane < cn && b < prm.B) ? chi_tab[(size_t)(c0 + lane) * MAX_SETS_DEV + b] : 0.0;
-            for (int i = lane; i < SSB_CHUNK + PF; i += 64) {
+                for (int b = 0; b < MAXB; ++b)
+                    schi[b * CHK + lane] =
+                        (lane < cn && b < prm.B) ? chi_tab[(size_t)(c0 + lane) * MAX_SETS_DEV + b] : 0.0;
+            }
+            if (TAYS) {
+                for (int i = lane; i < CHK * TAY_N; i += 64)
+                    stay[i] = i < cn * TAY_N ? prm.tay[(size_t)c0 * TAY_N + i] : 0.0;
+            }
+            for (int i = lane; i < CHK + PF; i += 64) {
                 const long long go = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
                 sgoff[i] = go;
                 if (H16 == 2) sgrow[i] = (go / prm.plane) * prm.N;
@@ -1288,7 +1303,7 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                 #pragma unroll
                     for (int b = 0; b < MAXB; ++b) {
                         if (b >= B) continue;   // uniform; keeps the loop fully unrolled
-                        const double chi0 = chi0s[b * SSB_CHUNK];   // this pixel's chi(k) of set b (LDS)
+                        const double chi0 = chi0s[b * CHK];   // this pixel's chi(k) of set b (LDS)
                         // The set's coefficients are read from the kernel arguments
                         // per use (scalar loads, constant cache): an opaque zero
                         // offset keeps the compiler from hoisting all sets' values
@@ -1300,6 +1315,39 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                         const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
                         const double th0 = DEPTH ? fma(px, px, py * py) : 0.0;
                         double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
+                        if (TAYS) {
+                            if (zl || zr) {
+                                // chi(theta -/+ d) - chi(theta) = E -/+ O with d = lambda q:
+                                // L = O - E (+ hl), R = O + E (+ hr); X, Y, Z are the lane's
+                                double tc[TAY_N];
+#pragma unroll
+                                for (int m = 0; m < TAY_N; ++m) tc[m] = stay[r * TAY_N + m];
+                                const double E = chi_even(tc, cb, qX, qY, qZ);
+                                const double O = chi_odd(tc + 8, qx, qy, qX, qY);
+                                double hl = 0.0, hr = 0.0;
+                                if (DEPTH) {
+                                    const double td2 = 2.0 * fma(py, qy, px * qx);
+                                    hl = prm.pt2[b] * (td2 - q2);
+                                    hr = prm.pt2[b] * (td2 + q2);
+                                }
+                                if (zl) {
+                                    double a = aml;
+                                    if (DEPTH) a *= sinc_tab(hl, T);
+                                    double sn, cs;
+                                    sincos_tab((O - E) + hl, T, sn, cs);
+                                    Lr = a * cs;
+                                    Li = a * sn;
+                                }
+                                if (zr) {
+                                    double a = amr;
+                                    if (DEPTH) a *= sinc_tab(hr, T);
+                                    double sn, cs;
+                                    sincos_tab((O + E) + hr, T, sn, cs);
+                                    Rr = a * cs;
+                                    Ri = a * sn;
+                                }
+                            }
+                        } else {
                         if (zl) {
                             const double ty = py - qy, tx = px - qx;
                             const double c1 = chi_poly(cb, tx, ty);
@@ -1327,6 +1375,7 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                             sincos_tab(-arg, T, sn, cs);
                             Rr = a * cs;
                             Ri = a * sn;
+                        }
                         }
                         // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
                         const double gmr = Ri - Li, gmi = Lr - Rr;
@@ -1840,19 +1889,27 @@ int ssb_nacc(int maxb) { return 3 * maxb + 1; }
 
 hipError_t ssb_occupancy(int maxb, int *blocks_per_cu) {
     switch (maxb) {
-        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1, false, 0>, 64, 0);
-        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2, false, 0>, 64, 0);
-        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4, false, 0>, 64, 0);
-        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8, false, 0>, 64, 0);
+        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1, false, 0, false>, 64, 0);
+        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2, false, 0, false>, 64, 0);
+        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4, false, 0, false>, 64, 0);
+        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8, false, 0, false>, 64, 0);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int MAXB, bool DEPTH>
 static void ssb_dispatch_h(const SsbParams &prm, int h16, int n_waves, hipStream_t st) {
-    if (h16 == 2) ssb_kernel<MAXB, DEPTH, 2><<<n_waves, 64, 0, st>>>(prm);
-    else if (h16 == 1) ssb_kernel<MAXB, DEPTH, 1><<<n_waves, 64, 0, st>>>(prm);
-    else ssb_kernel<MAXB, DEPTH, 0><<<n_waves, 64, 0, st>>>(prm);
+    if constexpr (MAXB == 1) {
+        if (prm.tay) {
+            if (h16 == 2) ssb_kernel<1, DEPTH, 2, true><<<n_waves, 64, 0, st>>>(prm);
+            else if (h16 == 1) ssb_kernel<1, DEPTH, 1, true><<<n_waves, 64, 0, st>>>(prm);
+            else ssb_kernel<1, DEPTH, 0, true><<<n_waves, 64, 0, st>>>(prm);
+            return;
+        }
+    }
+    if (h16 == 2) ssb_kernel<MAXB, DEPTH, 2, false><<<n_waves, 64, 0, st>>>(prm);
+    else if (h16 == 1) ssb_kernel<MAXB, DEPTH, 1, false><<<n_waves, 64, 0, st>>>(prm);
+    else ssb_kernel<MAXB, DEPTH, 0, false><<<n_waves, 64, 0, st>>>(prm);
 }
 
 template <int MAXB>
