@@ -1853,10 +1853,11 @@ struct SsbPassBufs {
 };
 
 // One pass over G for B sets on layout L: pixel terms, then the SSB kernel
-// with lanes on the (M, M/2 + 1) grid writing S and N there.  With one set
-// and bufs.tay, the kernel takes both lobes' phases from chi's Taylor
-// coefficients about theta(k) (one evaluation of the even and odd parts in
-// lambda q per pixel instead of the polynomial at both displaced points).
+// with lanes on the (M, M/2 + 1) grid writing S and N there.  With bufs.tay
+// (B tables of [n_pix][TAY_N]), the kernel takes both lobes' phases from each
+// set's chi Taylor coefficients about theta(k) (one evaluation of the even and
+// odd parts in lambda q per pixel and set instead of the polynomial at both
+// displaced points).
 static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int B, const void *G_c64_dev,
                            const void *GQ_dev, const float *gscale_dev, int h16_rows, int N, int M, double2 *S_out,
                            double *N_out, const SsbPassBufs &bufs, int device, hipStream_t stream) {
@@ -1871,9 +1872,9 @@ static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int 
     for (int b = 0; b < B; ++b) {
         const OpticsDev od = make_optics_dev(sets_host + b);
         // a(k) once (set 0 writes it), chi(k) per set
-        if (b == 0)
-            HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, nullptr, 0, B == 1 ? bufs.tay : nullptr,
-                                       stream));
+        double *tb = bufs.tay ? bufs.tay + (size_t)b * n_pix * TAY_N : nullptr;   // set b's Taylor table
+        if (b == 0) HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, nullptr, 0, tb, stream));
+        else if (tb) HIP_TRY(launch_pixel_terms(L.d_pixbase, nullptr, n_pix, apd, od, nullptr, 0, tb, stream));
         HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, bufs.chi + b, MAX_SETS_DEV, nullptr, stream));
         sp.tau_y[b] = od.tau_y;
         sp.tau_x[b] = od.tau_x;
@@ -1888,7 +1889,7 @@ static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int 
     sp.pix = bufs.pix;
     sp.goff = L.d_goff;
     sp.chi_tab = bufs.chi;
-    sp.tay = B == 1 ? bufs.tay : nullptr;
+    sp.tay = bufs.tay;
     sp.n_pix = n_pix;
     sp.tiles = L.d_tiles;
     sp.N = N;
@@ -2039,7 +2040,7 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
 
     // per-call tables in the stream's scratch arena
     const size_t n_part = (size_t)L.n_segs[mi] * ssb_nacc(maxb) * 64;
-    const size_t n_tay = B == 1 ? (size_t)n_pix * TAY_N : 0;
+    const size_t n_tay = (size_t)B * n_pix * TAY_N;
     const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) +
                         carve_size(n_part, sizeof(double)) + carve_size((size_t)n_tiles * stride, sizeof(double)) +
                         carve_size(B + 1, sizeof(double)) + carve_size(std::max<size_t>(1, n_tay), sizeof(double));
@@ -2053,7 +2054,7 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
     double *d_E = cv.take<double>(B + 1);
     double *d_tay = cv.take<double>(std::max<size_t>(1, n_tay));
 
-    SsbPassBufs bufs{d_pix, d_chi, d_part, d_tile_part, B == 1 ? d_tay : nullptr};
+    SsbPassBufs bufs{d_pix, d_chi, d_part, d_tile_part, d_tay};
     if ((st = ssb_pass(L, sets_host, B, G_c64_dev, GQ_dev, gscale_dev, h16_rows, N, N, (double2 *)S_out_c128_dev,
                        norm_out_dev, bufs, device, stream)))
         return st;

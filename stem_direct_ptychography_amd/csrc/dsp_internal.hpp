@@ -275,7 +275,7 @@ struct SsbParams {
     const PixelRec *pix;
     const long long *goff;   // [n_pix]
     const double *chi_tab;   // [n_pix][MAX_SETS_DEV] chi(k) per set
-    const double *tay;       // one-set band pass: [n_pix][TAY_N] chi's Taylor coefficients about theta(k), else null
+    const double *tay;       // band pass: B tables [n_pix][TAY_N] of chi Taylor coefficients about theta(k), else null
     int n_pix;
     const SsbTile *tiles;
     int N, nh;

@@ -15,9 +15,13 @@
 // each lane reads its own G(q, k); the lens-overlap zero-skip branches
 // almost never diverge because neighbouring frequencies see nearly the same
 // lens; each lane keeps its own frequency's sums, so there is no cross-lane
-// reduction.  The tiles x pixels of a launch are split into equal-cost
-// contiguous ranges (stream-K), one per wave; partial sums are added per
-// tile in a fixed order afterwards (deterministic).
+// reduction.  While a chunk of pixels is staged, a wave-uniform test against
+// the tile's centre and radius marks the alias slots (and, in the one-set SSB
+// kernel, the pixels) that no lane can have in support; they are skipped
+// with scalar branches.  The tiles x pixels of a launch are split into
+// equal-cost contiguous ranges (stream-K, costed per iteration by the same
+// test on the host), eight per resident wave slot; partial sums are added
+// per tile in a fixed order afterwards (deterministic).
 #include "dsp_internal.hpp"
 #include "dsp_kernels.hpp"
 
@@ -76,6 +80,7 @@ __global__ void pixel_terms_kernel(const PixelBase *in, PixelRec *out, int n_pix
 #pragma unroll
         for (int m = 0; m < TAY_N; ++m) tay[(size_t)p * TAY_N + m] = t[m];
     }
+    if (!out) return;   // Taylor coefficients only
     PixelRec r;
     r.lky = lky;
     r.lkx = lkx;
@@ -1139,16 +1144,16 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
     constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
     using GT = typename std::conditional<H16 != 0, short2, float2>::type;
     __shared__ double2 T[TRIG_N];
-    // TAYS (one set): both lobes' phases from chi's Taylor coefficients about
-    // theta(k), staged per chunk (16 pixels keep four waves per SIMD)
-    constexpr int CHK = TAYS ? 16 : SSB_CHUNK;
-    static_assert(!TAYS || MAXB == 1, "the Taylor pass has one set");
+    // TAYS: both lobes' phases from each set's chi Taylor coefficients about
+    // theta(k), staged per chunk (chunks of 16 or 8 pixels keep the LDS within
+    // the kernel's waves per SIMD)
+    constexpr int CHK = TAYS ? (MAXB <= 2 ? 16 : 8) : SSB_CHUNK;
     __shared__ PixelRec srec[CHK];
     __shared__ long long sgoff[CHK + PF];
     __shared__ long long sgrow[H16 == 2 ? CHK + PF : 1];   // pixel index x N (row scales)
     __shared__ double schi[MAXB * CHK];   // [set][pixel of the chunk] chi(k)
     __shared__ unsigned smask[CHK];        // per pixel of the chunk: the reach test's L/R bits
-    __shared__ double stay[TAYS ? CHK * TAY_N : 1];   // [pixel][TAY_N]
+    __shared__ double stay[TAYS ? MAXB * CHK * TAY_N : 1];   // [set][pixel][TAY_N]
     __shared__ double2 scent;                    // lambda c, c the tile centre
     __shared__ double sthr;                      // the reach test's squared bound
     const int lane = threadIdx.x;
@@ -1240,8 +1245,13 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                         (lane < cn && b < prm.B) ? chi_tab[(size_t)(c0 + lane) * MAX_SETS_DEV + b] : 0.0;
             }
             if (TAYS) {
-                for (int i = lane; i < CHK * TAY_N; i += 64)
-                    stay[i] = i < cn * TAY_N ? prm.tay[(size_t)c0 * TAY_N + i] : 0.0;
+                // set b's table starts at b n_pix TAY_N
+#pragma unroll
+                for (int b = 0; b < MAXB; ++b) {
+                    if (b >= prm.B) continue;
+                    const double *tb = prm.tay + ((size_t)b * prm.n_pix + c0) * TAY_N;
+                    for (int i = lane; i < CHK * TAY_N; i += 64) stay[b * CHK * TAY_N + i] = i < cn * TAY_N ? tb[i] : 0.0;
+                }
             }
             for (int i = lane; i < CHK + PF; i += 64) {
                 const long long go = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
@@ -1321,7 +1331,7 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbPar
                                 // L = O - E (+ hl), R = O + E (+ hr); X, Y, Z are the lane's
                                 double tc[TAY_N];
 #pragma unroll
-                                for (int m = 0; m < TAY_N; ++m) tc[m] = stay[r * TAY_N + m];
+                                for (int m = 0; m < TAY_N; ++m) tc[m] = stay[(b * CHK + r) * TAY_N + m];
                                 const double E = chi_even(tc, cb, qX, qY, qZ);
                                 const double O = chi_odd(tc + 8, qx, qy, qX, qY);
                                 double hl = 0.0, hr = 0.0;
@@ -1899,13 +1909,11 @@ hipError_t ssb_occupancy(int maxb, int *blocks_per_cu) {
 
 template <int MAXB, bool DEPTH>
 static void ssb_dispatch_h(const SsbParams &prm, int h16, int n_waves, hipStream_t st) {
-    if constexpr (MAXB == 1) {
-        if (prm.tay) {
-            if (h16 == 2) ssb_kernel<1, DEPTH, 2, true><<<n_waves, 64, 0, st>>>(prm);
-            else if (h16 == 1) ssb_kernel<1, DEPTH, 1, true><<<n_waves, 64, 0, st>>>(prm);
-            else ssb_kernel<1, DEPTH, 0, true><<<n_waves, 64, 0, st>>>(prm);
-            return;
-        }
+    if (prm.tay) {
+        if (h16 == 2) ssb_kernel<MAXB, DEPTH, 2, true><<<n_waves, 64, 0, st>>>(prm);
+        else if (h16 == 1) ssb_kernel<MAXB, DEPTH, 1, true><<<n_waves, 64, 0, st>>>(prm);
+        else ssb_kernel<MAXB, DEPTH, 0, true><<<n_waves, 64, 0, st>>>(prm);
+        return;
     }
     if (h16 == 2) ssb_kernel<MAXB, DEPTH, 2, false><<<n_waves, 64, 0, st>>>(prm);
     else if (h16 == 1) ssb_kernel<MAXB, DEPTH, 1, false><<<n_waves, 64, 0, st>>>(prm);
