@@ -1138,8 +1138,10 @@ struct SsbWaves {
 // H16: G comes as herm16 snorm16 pairs, unpacked as max(q / 32767, -1) s in
 // FP64 at use; H16 = 1: one scale per pixel (staged with the pixel record);
 // H16 = 2: one scale per stored row, fetched with G for the lane's row.
+// The eight-set Taylor pass is held to three waves per SIMD: a few spilled
+// registers cost less than the third wave gains (13.9 -> 13.2 ms).
 template <int MAXB, bool DEPTH, int H16, bool TAYS>
-__global__ __launch_bounds__(64, (SsbWaves<MAXB>::value)) void ssb_kernel(SsbParams prm) {
+__global__ __launch_bounds__(64, ((TAYS && MAXB == 8) ? 3 : SsbWaves<MAXB>::value)) void ssb_kernel(SsbParams prm) {
     constexpr int NACC = 3 * MAXB + 1;
     constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
     using GT = typename std::conditional<H16 != 0, short2, float2>::type;
