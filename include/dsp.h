@@ -37,10 +37,16 @@
  *   T_phi = i (L - R) (phase), T_A = L + R (log-amplitude).
  *
  * Solved frequencies: stored (iy, ix) with ix < N/2, iy != N/2, excluding
- * ix = 0 with signed row <= 0; row-major order; n_q = N (N - 2) / 2.  Aliases
- * of q on the u-times finer grid: K = (iy_signed + j_y N, ix + j_x N) inside
- * [-uN/2, uN/2)^2 with |K|^2 dq^2 < R^2, R = 2 alpha/lambda (+ dk when soft);
- * order (j_y, j_x) ascending; A(q) = number of aliases (1..9).
+ * ix = 0 with signed row <= 0; row-major order; n_q = N (N - 2) / 2 (the
+ * 130560 frequencies of a 512 x 512 scan, "Where the 9 s of regularized
+ * preparation goes", section "Code path").  Aliases of q on the u-times
+ * finer grid (same page, "Code path": the prepare loops over alias counts):
+ * K = (iy_signed + j_y N, ix + j_x N) inside [-uN/2, uN/2)^2 with
+ * |K|^2 dq^2 < R^2, R = 2 alpha/lambda (+ dk when soft), i.e. the two
+ * aperture discs of the transfer's lobes overlap; order (j_y, j_x)
+ * ascending; A(q) = number of aliases (1..9).  At the page's 512 x 512,
+ * 0.373 A, 30 mrad, upsampling-3 setup this rule gives its alias-count
+ * histogram (same page, "Raw numbers": 3770 / 106424 / 19304 / 1062).
  *
  * Asynchrony: validation and host geometry run synchronously in the call;
  * kernels are enqueued on the caller's HIP stream (hipStream_t passed as
@@ -126,7 +132,8 @@ typedef struct {
     int dim;                 /* slot dimension D = n_comp * a_max + 1 */
     int n_bf, n_active_bf;
     int method, upsampling, n_scan;
-    int n_tiles;             /* 4 x 16 frequency tiles of the Gram kernels */
+    int n_tiles;             /* frequency tiles of the Gram kernels: up to 64 frequencies each, cut
+                                along G's 128-byte lines (one per lane of a wave) */
     int alias_hist[10];      /* alias_hist[A] = frequencies with A aliases */
     double scale;            /* strength unit: sum of active weights */
     double g_bytes;          /* algorithmic G bytes a prepare reads: n_q * n_active * 8 */
@@ -188,7 +195,15 @@ dsp_status dsp_solve(dsp_handle *h, const double *strengths_host, int S, void *x
  * Scatter packed solutions to the fine half plane: spec_out_c128_dev
  * complex128 [S][n_comp][uN][uN/2+1]; alias K lands at (K_y mod uN, K_x)
  * when K_x > 0 or (K_x = 0 and K_y >= 0), otherwise its conjugate lands at
- * -K.  Entries no alias reaches are 0.
+ * -K: the spectrum of a real field at -K is the conjugate of the one at K
+ * ("Historical WebGPU G(q,k) memory experiment", section "Why herm is
+ * exactly lossless"), and the solved aliases are the object's spectrum on
+ * the upsampled grid ("Where the 9 s of regularized preparation goes",
+ * sections "Question" and "Code path": upsampling_factor, the per-alias
+ * unknowns).  Entries no alias reaches are 0.
+ * x_packed_c128_dev: device [S][n_comp][n_q][a_max] from dsp_solve (borrowed).
+ * spec_out_c128_dev: device, caller-owned, fully written (zeros included).
+ * DSP_EINVAL for a NULL handle or buffer or S <= 0.  Runs on hip_stream.
  */
 dsp_status dsp_scatter(const dsp_handle *h, const void *x_packed_c128_dev, int S,
                        void *spec_out_c128_dev, void *hip_stream);
@@ -244,9 +259,14 @@ dsp_status dsp_derive_phase(const dsp_handle *complex_h, void *hip_stream, dsp_h
  * slot.
  *   g_version: the caller's generation number of G's contents; change it
  *              when G is rewritten in place.
- *   out: the model, owned by the cache: valid until a later dsp_cache_get
- *        replaces its slot or dsp_cache_destroy; never dsp_destroy it.
+ *   out: a new reference to the slot's model, owned by the caller: release
+ *        it with dsp_destroy.  The model lives until the cache and every
+ *        reference handed out have released it, so a reference stays valid
+ *        after a later dsp_cache_get replaces its slot or the cache is
+ *        destroyed.
  *   how (may be NULL): 1 slot hit, 0 prepared, 2 derived.
+ * G is identified by its address and g_version only: a caller that frees G
+ * and allocates new data at the same address must pass a new g_version.
  * Calls on one cache are serialized by a lock.  On error the slot keeps its
  * model and *out is NULL; errors as dsp_prepare and dsp_derive_phase.
  */
@@ -299,17 +319,23 @@ dsp_status dsp_info(const dsp_handle *h, dsp_info_t *out);
 dsp_status dsp_export_system(const dsp_handle *h, void *aug_out_c128_dev, double *eig_out_dev,
                              void *hip_stream);
 
-/* Host copies of the handle's alias table: q_host int32[n_q][2] (iy, ix),
- * count_host int32[n_q], K_host int32[n_q][a_max][2] (0 past A(q)). */
+/* Host copies of the handle's alias table (the frequencies and their
+ * aliases defined above: "Where the 9 s of regularized preparation goes",
+ * sections "Code path" and "Raw numbers"): q_host int32[n_q][2] (iy, ix),
+ * count_host int32[n_q], K_host int32[n_q][a_max][2] (0 past A(q)).  Any
+ * pointer may be NULL (not written); all are caller-owned host memory.  No
+ * device call.  DSP_EINVAL for a NULL handle. */
 dsp_status dsp_alias_table(const dsp_handle *h, int32_t *q_host, int32_t *count_host, int32_t *K_host);
 
-/* Releases a handle (NULL is ignored).  Its device buffers (one block per
- * handle) go back to the library's per-device cache behind events recorded
- * after the last work queued with them on each stream the handle was used
- * on; the call does not wait for the device, and a later prepare reuses the
- * block after making its own stream wait on those events.  The cache keeps
- * at most 4 GiB per device (older blocks are then freed) and gives its blocks
- * back when an allocation would otherwise fail. */
+/* Releases a reference to a handle (NULL is ignored); the handle is freed
+ * with its last reference (dsp_prepare and dsp_derive_phase create one, and
+ * a cache holds one per slot and hands out one per dsp_cache_get).  Its
+ * device buffers (one block per handle) go back to the library's per-device
+ * cache behind events recorded after the last work queued with them on each
+ * stream the handle was used on; the call does not wait for the device, and
+ * a later prepare reuses the block after making its own stream wait on those
+ * events.  The cache keeps at most 4 GiB per device (older blocks are then
+ * freed) and gives its blocks back when an allocation would otherwise fail. */
 void dsp_destroy(dsp_handle *h);
 const char *dsp_last_error(void);
 
@@ -319,12 +345,19 @@ const char *dsp_last_error(void);
 dsp_status dsp_geometry_counts(const dsp_scan *scan, const dsp_optics *optics, int upsampling,
                                int *n_q, int *a_max, int32_t *hist_out);
 
-/* Solved frequencies and their aliases, same layout as dsp_alias_table
- * (K_host sized n_q * a_max * 2 with a_max from dsp_geometry_counts). */
+/* Solved frequencies and their aliases (the rule above; "Where the 9 s of
+ * regularized preparation goes", sections "Code path" and "Raw numbers"),
+ * same layout as dsp_alias_table (K_host sized n_q * a_max * 2 with a_max
+ * from dsp_geometry_counts).  Host only; errors as dsp_geometry_counts. */
 dsp_status dsp_alias_geometry(const dsp_scan *scan, const dsp_optics *optics, int upsampling,
                               int32_t *q_host, int32_t *count_host, int32_t *K_host);
 
-/* Active bright-field pixels (a(k) > 0), input order: idx_out int32[n_bf]. */
+/* Active bright-field pixels: those with non-zero aperture weight a(k) > 0
+ * ("Historical WebGPU G(q,k) memory experiment", section "Gotchas recorded": the
+ * active set, not the labelled set, carries signal), in input order.
+ * bf_coords_host double[n_bf][2]; idx_out int32[n_bf] (caller-owned; may be
+ * NULL to count only); *n_active receives the count.  Host only.
+ * DSP_EINVAL for bad optics, n_bf < 0, NULL coordinates or NULL n_active. */
 dsp_status dsp_active_bf(const double *bf_coords_host, int n_bf, const dsp_optics *optics,
                          int32_t *idx_out, int *n_active);
 

@@ -115,18 +115,18 @@ def _stream(stream=None) -> int:
 
 
 class Prepared:
-    """Prepared per-frequency systems (a handle of libdsp)."""
+    """Prepared per-frequency systems: one reference to a libdsp handle,
+    released when the wrapper dies."""
 
-    def __init__(self, handle: ctypes.c_void_p, device, method: str, owner=None):
+    def __init__(self, handle: ctypes.c_void_p, device, method: str):
         self._h = handle
-        self._owner = owner          # a PreparedCache holding the model, or None (we own it)
         self.device = device
         self.method = method
         self.info = self._info()
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h and getattr(self, "_owner", None) is None and _L is not None:   # _L is None at teardown
+        if h and _L is not None:   # _L is None at teardown
             _L.dsp_destroy(h)
             self._h = None
 
@@ -246,13 +246,32 @@ def prepare(G, bf_coords, optics, step: float, upsampling: int, method: str = "p
 
 class PreparedCache:
     """Two-slot prepared-model cache (dsp_cache_get): one slot per method
-    under the same data and optics key.  Models it returns stay owned by the
-    cache and are valid until the slot is replaced."""
+    under the same data and optics key.  Each model it returns holds its own
+    reference, so it stays valid after its slot is replaced.
+
+    G is keyed by the tensor itself: the cache keeps a reference to the last
+    G it saw and counts a new generation whenever G is a different tensor or
+    storage, or its in-place version counter moved, so a new tensor at a
+    reused address, or G rewritten in place, is a miss.  The library sees
+    that generation times 2^32 plus the caller's own g_version (0 <= g_version
+    < 2^32) as its generation number."""
 
     def __init__(self):
         h = ctypes.c_void_p()
         _check(_L.dsp_cache_create(ctypes.byref(h)))
         self._c = h
+        self._G = None          # the last G seen (kept alive so its address is not reused)
+        self._G_key = None      # (data_ptr, storage ptr, shape, _version)
+        self._gen = 0
+
+    def _generation(self, G, g_version: int) -> int:
+        if not 0 <= int(g_version) < (1 << 32):
+            raise DspError(_lib.DSP_EINVAL, "g_version must be in [0, 2^32)")
+        key = (G.data_ptr(), G.untyped_storage().data_ptr(), tuple(G.shape), G._version)
+        if self._G is not G or self._G_key != key:
+            self._gen += 1
+            self._G, self._G_key = G, key
+        return (self._gen << 32) | int(g_version)
 
     def __del__(self):
         c = getattr(self, "_c", None)
@@ -276,11 +295,12 @@ class PreparedCache:
         oc = _optics(optics)
         h = ctypes.c_void_p()
         how = ctypes.c_int(-1)
-        _check(_L.dsp_cache_get(self._c, ctypes.c_void_p(G.data_ptr()), int(g_version), k.shape[0], _dptr(k),
+        gen = self._generation(G, g_version)
+        _check(_L.dsp_cache_get(self._c, ctypes.c_void_p(G.data_ptr()), gen, k.shape[0], _dptr(k),
                                 _dptr(w), ctypes.byref(scan), ctypes.byref(oc), ctypes.byref(opts),
                                 1 if derive else 0, ctypes.c_void_p(_stream(stream)), ctypes.byref(h),
                                 ctypes.byref(how)))
-        return Prepared(h, G.device, method, owner=self), {0: "prepared", 1: "hit", 2: "derived"}[how.value]
+        return Prepared(h, G.device, method), {0: "prepared", 1: "hit", 2: "derived"}[how.value]
 
 
 def quantize_herm16(G, rows: bool = False, stream=None):

@@ -13,6 +13,7 @@
 #include <hipfft/hipfft.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
@@ -273,15 +274,15 @@ typedef std::vector<std::pair<int16_t, int16_t>> Lanes;   // (yh, ix) per lane
 template <class Keep>
 std::vector<Lanes> pack_line_runs(int N, int nh, int yh_lo, int yh_hi, int ncol, int max_rows, Keep keep) {
     std::vector<Lanes> out;
-    const int n_blk = 2 + (ncol - 1) / TILE_X;
+    const int n_blk = 2 + (ncol - 1) / LINE_X;
     Lanes cur, run;
     int cur_row0 = 0;
     for (int b = 0; b < n_blk; ++b) {
         for (int yh = yh_lo; yh <= yh_hi; ++yh) {
             const long long iy = yh < 0 ? yh + N : yh;
-            const int h = (int)((TILE_X - (iy * nh) % TILE_X) % TILE_X);
-            const int c0 = b == 0 ? 0 : h + TILE_X * (b - 1);
-            const int c1 = std::min(ncol, b == 0 ? h : c0 + TILE_X);
+            const int h = (int)((LINE_X - (iy * nh) % LINE_X) % LINE_X);
+            const int c0 = b == 0 ? 0 : h + LINE_X * (b - 1);
+            const int c1 = std::min(ncol, b == 0 ? h : c0 + LINE_X);
             run.clear();
             for (int ix = c0; ix < c1; ++ix)
                 if (keep(yh, ix)) run.emplace_back((int16_t)yh, (int16_t)ix);
@@ -974,10 +975,13 @@ dsp_status build_layout(const LayoutKey &key, const dsp_scan *scan, const dsp_op
     return DSP_OK;
 }
 
-// Most recently used layouts (a handle keeps its own reference).
+// Most recently used layouts (a handle keeps its own reference).  The
+// caches are heap objects that are never destroyed: a layout's destructor
+// frees device memory, and static destruction at process exit may run after
+// the HIP runtime has shut down, so no HIP call may be left for it.
 constexpr size_t LAYOUT_CACHE_SIZE = 4;
 std::mutex g_layout_mu;
-std::vector<std::shared_ptr<Layout>> g_layouts;   // front = most recent
+std::vector<std::shared_ptr<Layout>> &g_layouts = *new std::vector<std::shared_ptr<Layout>>();   // front = most recent
 
 dsp_status get_layout(const LayoutKey &key, const dsp_scan *scan, const dsp_optics *optics, const double *coords,
                       const double *weights, std::shared_ptr<Layout> &out, bool &hit) {
@@ -1149,7 +1153,8 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
     return DSP_OK;
 }
 
-std::vector<std::shared_ptr<SsbLayout>> g_ssb_layouts;   // front = most recent (under g_layout_mu)
+// front = most recent (under g_layout_mu); never destroyed, like g_layouts
+std::vector<std::shared_ptr<SsbLayout>> &g_ssb_layouts = *new std::vector<std::shared_ptr<SsbLayout>>();
 
 dsp_status get_ssb_layout(const SsbKey &key, const dsp_optics *optics, const double *coords, const double *weights,
                           std::shared_ptr<SsbLayout> &out) {
@@ -1176,6 +1181,9 @@ dsp_status get_ssb_layout(const SsbKey &key, const dsp_optics *optics, const dou
 // ---------------------------------------------------------------------------
 
 struct dsp_handle {
+    // references: the creator's, plus one per cache slot and per reference a
+    // cache hands out; dsp_destroy drops one and frees at zero
+    std::atomic<int> refs{1};
     int device = 0;
     int method = 0;
     std::shared_ptr<const Layout> L;
@@ -1297,7 +1305,9 @@ extern "C" {
 
 const char *dsp_last_error(void) { return g_err.c_str(); }
 
-void dsp_destroy(dsp_handle *h) { delete h; }
+void dsp_destroy(dsp_handle *h) {
+    if (h && h->refs.fetch_sub(1, std::memory_order_acq_rel) == 1) delete h;
+}
 
 dsp_status dsp_geometry_counts(const dsp_scan *scan, const dsp_optics *optics, int upsampling, int *n_q, int *a_max,
                                int32_t *hist_out) {
@@ -1656,6 +1666,7 @@ dsp_status dsp_cache_get(dsp_cache *c, const void *G_c64_dev, unsigned long long
     std::vector<double> k = cache_key(G_c64_dev, g_version, n_bf, bf_coords_host, weights_host, scan, optics, opts);
     std::lock_guard<std::mutex> lock(c->mu);
     if (c->h[m] && same_key(c->key[m], k)) {
+        c->h[m]->refs.fetch_add(1, std::memory_order_relaxed);   // the caller's reference
         *out = c->h[m];
         if (how) *how = 1;
         return DSP_OK;
@@ -1670,9 +1681,12 @@ dsp_status dsp_cache_get(dsp_cache *c, const void *G_c64_dev, unsigned long long
         st = dsp_prepare(G_c64_dev, n_bf, bf_coords_host, weights_host, scan, optics, opts, hip_stream, &nh);
     }
     if (st) return st;   // the slot keeps its model
+    // the slot drops its reference to the old model; references handed out
+    // earlier keep it alive until their holders release them
     dsp_destroy(c->h[m]);
     c->h[m] = nh;
     c->key[m] = std::move(k);
+    nh->refs.fetch_add(1, std::memory_order_relaxed);   // the caller's reference
     *out = nh;
     if (how) *how = got;
     return DSP_OK;

@@ -182,14 +182,15 @@ __host__ __device__ inline void sincos_tab(double x, const double2 *__restrict__
 
 // A tile is a group of up to 64 scan frequencies, one per lane, with
 // explicit coordinates (signed row yh, column ix).  The host cuts every
-// stored row of G into the runs that fill one 128-byte line (16 complex64;
-// a row is N/2 + 1 entries long, so line boundaries move from row to row)
-// and packs them: full runs of four consecutive rows form one tile, and the
-// short runs at the row ends are packed with those of neighbouring rows.
+// stored row of G into the runs that fill one 128-byte line (LINE_X = 16
+// complex64; a row is N/2 + 1 entries long, so line boundaries move from row
+// to row): the head run up to the row's first line boundary, then full
+// 16-entry runs, then the tail.  Runs of the same block (head, first full,
+// second full, ...) of consecutive rows are packed whole, in row order, into
+// tiles of at most 64 lanes spanning at most 8 rows (16 for the SSB pass).
 // Each lane's G value then comes from a line no other tile reads, and
 // neighbouring lanes see nearly the same lens overlap.
-constexpr int TILE_Y = 4;
-constexpr int TILE_X = 16;
+constexpr int LINE_X = 16;
 constexpr int MAX_SLOTS = 9;   // fine aliases of one coarse frequency for u <= 3 per axis pair
 
 struct alignas(64) GramTile {

@@ -149,6 +149,43 @@ def stratified(counts, per_count, rng, extra=()):
     return np.unique(np.asarray(sel, dtype=np.int64))
 
 
+def check_scatter(prep, x, spec, prep_o=None, sel=None, strengths=()):
+    """Scatter of the library's own packed solutions x (S, n_comp, n_q, a_max)
+    against the oracle's placement of the same values: bit-exact over the
+    whole fine half plane (it only moves and conjugates values).  With
+    prep_o / sel, also the oracle's solutions at the sampled frequencies,
+    placed by the oracle, against the library's spectrum at those entries
+    (1e-5).  Returns the number of conjugate-mirrored aliases checked."""
+    inf = prep.info
+    n, u, nc = inf["n_scan"], inf["upsampling"], inf["n_comp"]
+    q, c, K = prep.alias_table()
+    Ks = [K[i, :c[i]].astype(np.int64) for i in range(len(q))]
+    mirrored = sum(int(np.sum((k_[:, 1] < 0) | ((k_[:, 1] == 0) & (k_[:, 0] < 0)))) for k_ in Ks)
+    for s_ in range(x.shape[0]):
+        xs = [np.concatenate([x[s_, comp, i, :c[i]] for comp in range(nc)]) for i in range(len(q))]
+        want = O.scatter(q, Ks, xs, n, u, nc)
+        assert np.array_equal(spec[s_], want), f"strength {s_}: scatter differs from the oracle's placement"
+    if prep_o is not None:
+        nf = u * n
+        for s_, st in enumerate(strengths):
+            xs_o = O.solve(prep_o, st)
+            want = O.scatter(prep_o.q, prep_o.K, xs_o, n, u, nc)
+            pos = []
+            for Kq in prep_o.K:
+                for ky, kx in Kq:
+                    if kx > 0 or (kx == 0 and ky >= 0):
+                        pos.append((ky % nf, kx))
+                    else:
+                        pos.append(((-ky) % nf, -kx))
+            pos = np.asarray(pos, dtype=np.int64).reshape(-1, 2)
+            got = spec[s_][:, pos[:, 0], pos[:, 1]]
+            ref = want[:, pos[:, 0], pos[:, 1]]
+            glob = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+            den = np.maximum(np.abs(ref), 1e-3 * np.abs(ref).max())
+            assert glob <= X_TOL and np.max(np.abs(got - ref) / den) <= X_TOL, f"strength {st}: {glob:.3e}"
+    return mirrored
+
+
 def run_prepare_case(w, G_dev, k, wts, method, strengths, sel=None, per_count=None, seed=0):
     """Prepare + export + solve on the GPU and check the frequencies ``sel``
     (all when None) against the oracle."""
@@ -231,6 +268,7 @@ def test_c1_phase_full_and_scatter():
         err = np.linalg.norm(spec[s] - want) / np.linalg.norm(want)
         assert err <= X_TOL
         assert np.array_equal(spec[s] != 0, want != 0)
+    check_scatter(prep, x, spec, prep_o, np.arange(len(prep_o.q)), list(w.strengths) + [0.1, 3.0])
 
 
 def test_c2_complex_sampled():
@@ -243,6 +281,9 @@ def test_c2_complex_sampled():
                                             sel=[0, 1, 2, 8063], per_count=400, seed=2)
     spec = prep.scatter(torch.as_tensor(x, device=DEV)).cpu().numpy()
     assert spec.shape == (8, 2, 256, 129)
+    mirrored = check_scatter(prep, x, spec, prep_o, sel, list(w.strengths))
+    assert mirrored > 10000, mirrored   # about half of c2's 31,370 aliases take the conjugate branch
+    _say(f"c2 complex scatter: 8 pairs, {mirrored} mirrored aliases, bit-exact placement")
 
 
 def test_c2_phase_sampled_weighted():
@@ -273,7 +314,12 @@ def test_tiny_ragged_full(method, soft):
     pix, k = bf_pixels(w)
     G = data_stack_numpy(w, pix)
     strengths = [1e-3, 0.05] if method == "phase" else [(1e-3, 2e-3), (0.05, 0.01)]
-    run_prepare_case(w, torch.as_tensor(G, device=DEV), k, random_weights(len(k), 1), method, strengths)
+    prep, x, sel, prep_o = run_prepare_case(w, torch.as_tensor(G, device=DEV), k, random_weights(len(k), 1),
+                                            method, strengths)
+    spec = prep.scatter(torch.as_tensor(x, device=DEV)).cpu().numpy()
+    assert w.upsampling == 3
+    mirrored = check_scatter(prep, x, spec, prep_o, sel, strengths)
+    assert mirrored > 0
 
 
 def test_phase_derived_from_complex():
@@ -452,6 +498,52 @@ def test_prepared_cache_two_slots():
     torch.cuda.synchronize()
 
 
+def test_prepared_cache_new_tensor_same_address():
+    """A model handed out by the cache stays valid after its slot is
+    replaced and after the cache is gone; a new G at a reused address, and
+    G rewritten in place, are misses whose models match a fresh prepare."""
+    w = _tiny()
+    pix, k = bf_pixels(w)
+    G_np = data_stack_numpy(w, pix)
+    kw = dict(step=w.step, upsampling=w.upsampling, smoothness=w.smoothness)
+    cache = dsp.PreparedCache()
+    G1 = torch.as_tensor(G_np, device=DEV)
+    p1, how1 = cache.get(G1, k, w.optics, method="phase", **kw)
+    x1 = p1.solve([1e-2])
+    torch.cuda.synchronize()
+    addr = G1.data_ptr()
+    # another tensor takes the cache's attention; G1 is then freed
+    other = torch.as_tensor(G_np * 0.5, device=DEV)
+    _, how2 = cache.get(other, k, w.optics, method="complex", **kw)
+    del G1
+    G3 = torch.empty((len(k), w.n_scan, w.n_half), dtype=torch.complex64, device=DEV)
+    G3.copy_(torch.as_tensor(G_np * 3.0, device=DEV))
+    p3, how3 = cache.get(G3, k, w.optics, method="phase", **kw)
+    assert (how1, how2, how3) == ("prepared", "prepared", "prepared")
+    _say(f"cache: reused address {G3.data_ptr() == addr}")
+    fresh = dsp.prepare(G3, k, w.optics, method="phase", **kw)
+    for a, b in zip(p3.export_system(), fresh.export_system()):
+        assert torch.equal(a, b)
+    # p1's slot was replaced: its model is still the first one, bit for bit
+    assert torch.equal(p1.solve([1e-2]), x1)
+    # in-place rewrite: the version counter moved, so the slot misses
+    G3.mul_(2.0)
+    p4, how4 = cache.get(G3, k, w.optics, method="phase", **kw)
+    assert how4 == "prepared"
+    fresh2 = dsp.prepare(G3, k, w.optics, method="phase", **kw)
+    for a, b in zip(p4.export_system(), fresh2.export_system()):
+        assert torch.equal(a, b)
+    p5, how5 = cache.get(G3, k, w.optics, method="phase", **kw)
+    assert how5 == "hit" and p5._h.value == p4._h.value
+    # the cache goes away first; its models live on in their wrappers
+    del cache
+    assert torch.equal(p1.solve([1e-2]), x1)
+    for a, b in zip(p4.export_system(), fresh2.export_system()):
+        assert torch.equal(a, b)
+    del p1, p3, p4, p5, fresh, fresh2
+    torch.cuda.synchronize()
+
+
 def test_zero_data_and_zero_weights():
     w = _tiny()
     pix, k = bf_pixels(w)
@@ -537,6 +629,17 @@ def test_ssb_c1_full_agreement():
     power = np.array([np.sum(wa * np.abs(c) ** 2) for c in cols])
     E_o = O.agreement(S_o, N_o, power)
     assert np.allclose(E, E_o, rtol=1e-6, atol=0)
+
+
+def test_ssb_c1_two_sets_full():
+    """The two-set pass (its own compiled set count) on every stored entry."""
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    G_dev = torch.as_tensor(data_stack_numpy(w, pix), device=DEV)
+    sets = [w.optics, w.optics.replace(aberrations=[(1, 0, -115.0, 0.0)], tilt=(0.5e-3, -1e-3))]
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G_dev, k, random_weights(len(k), 12), sets, None)
+    power = np.array([np.sum(wa * np.abs(c) ** 2) for c in cols])
+    assert np.allclose(E, O.agreement(S_o, N_o, power), rtol=1e-6, atol=0)
 
 
 def test_ssb_tiny_band_weighted():
@@ -798,6 +901,119 @@ def test_ssb_equals_prepare_at_u1():
 
 
 # ----------------------------------------------------------------------------
+# a known weak-phase object recovered through the library
+# ----------------------------------------------------------------------------
+
+
+def _recovery_case(w, k, c_fine, method, tol):
+    """Noise-free first-order data of the fine-grid object c = A_l + i phi
+    (the oracle's forward model, rounded to complex64) through the library's
+    prepare and solve at a vanishing strength: every frequency whose system is
+    well conditioned returns the object's spectrum at its aliases,
+    fft2(c) / u^2, and the scatter places it on the fine grid."""
+    from oracle import simulate as SIM
+
+    n, u = w.n_scan, w.upsampling
+    act = O.active_pixels(k, w.optics)
+    G = np.zeros((len(k), n, n // 2 + 1), dtype=np.complex128)
+    G[act] = SIM.first_order_G(k[act], c_fine, n, w.step, u, w.optics)
+    G_dev = torch.as_tensor(G.astype(np.complex64), device=DEV)
+    _say(f"recovery {w.name} method={method} N={n} u={u} n_active={len(act)}")
+    prep = dsp.prepare(G_dev, k, w.optics, step=w.step, upsampling=u, method=method, smoothness=w.smoothness)
+    st = 1e-12 if method == "phase" else (1e-12, 1e-12)
+    x = prep.solve([st])
+    spec = prep.scatter(x)
+    aug, _ = prep.export_system()
+    torch.cuda.synchronize()
+    x, spec, aug = x.cpu().numpy()[0], spec.cpu().numpy()[0], aug.cpu().numpy()
+    q, cnt, K = prep.alias_table()
+    am = prep.info["a_max"]
+    nf = u * n
+    FA = SIM.fine_spectrum(c_fine.real, u)
+    FP = SIM.fine_spectrum(c_fine.imag, u)
+    checked = 0
+    for i in range(len(q)):
+        A = int(cnt[i])
+        if A == 0:
+            continue
+        Ki = K[i, :A]
+        xt = FP[Ki[:, 0] % nf, Ki[:, 1] % nf]
+        got = x[0, i, :A]
+        sl = slot_index(method, A, am)
+        if method == "complex":
+            xt = np.concatenate([FA[Ki[:, 0] % nf, Ki[:, 1] % nf], xt])
+            got = np.concatenate([x[0, i, :A], x[1, i, :A]])
+        M = aug[i][np.ix_(sl, sl)]
+        ev = np.linalg.eigvalsh(M)
+        if ev[0] > 1e-6 * ev[-1] and np.linalg.norm(xt) > 0:
+            assert np.linalg.norm(got - xt) <= tol * np.linalg.norm(xt), (i, q[i])
+            checked += 1
+            for m in range(A):
+                ky, kx = int(Ki[m, 0]), int(Ki[m, 1])
+                if kx > 0 or (kx == 0 and ky >= 0):
+                    assert abs(spec[-1, ky % nf, kx] - FP[ky % nf, kx]) <= tol * np.linalg.norm(xt) * 2
+    assert checked > 0.5 * len(q), (checked, len(q))
+    return checked
+
+
+def test_recover_weak_phase_object_c1():
+    """The tiny SSB configuration's object (seeded, Gaussian-filtered, 0.05 rad
+    phase) from its closed-form noise-free weak-phase data."""
+    from synthetic import object_map
+
+    w = workload("c1")
+    pix, k = bf_pixels(w)
+    phi = object_map(w.n_scan, w.step, w.lattice_sites, w.seed)
+    n = _recovery_case(w, k, 1j * phi, "phase", 1e-5)
+    _say(f"c1: {n} of 480 frequencies recovered to 1e-5")
+
+
+@pytest.mark.parametrize("method", ["phase", "complex"])
+def test_recover_object_tiny_aliased(method):
+    """Three aliases per axis on a ragged tiny scan: the library separates the
+    aliases of a band-limited object (phase, or log-amplitude and phase)."""
+    from oracle import simulate as SIM
+
+    w = _tiny(method=method)
+    pix, k = bf_pixels(w)
+    rng = np.random.default_rng(41)
+    nf = w.upsampling * w.n_scan
+    phi = SIM.band_limited_field(nf, rng, std=0.05)
+    amp = SIM.band_limited_field(nf, rng, std=0.02) if method == "complex" else np.zeros_like(phi)
+    _recovery_case(w, k, amp + 1j * phi, method, 1e-4)
+
+
+# ----------------------------------------------------------------------------
+# the 256 x 256 phase workload: prepare, then a 32-strength sweep
+# ----------------------------------------------------------------------------
+
+
+def test_c3_phase_sweep():
+    """256 x 256 scan, 4093 pixels, 14 aberrations with tilt, upsampling 3:
+    stratified frequencies against the oracle (systems, eigenvalues and
+    three of the strengths), every frequency at all 32 strengths against a
+    LAPACK solve of the exported systems, and the scatter bit-exact."""
+    w = workload("c3")
+    pix, k = bf_pixels(w)
+    _say("generating the 256 x 256 G (4093, 256, 129) on the GPU")
+    G = data_stack_torch(w, pix, DEV)
+    torch.cuda.synchronize()
+    strengths = list(w.strengths)
+    few = [strengths[0], strengths[16], strengths[31]]
+    prep, x, sel, prep_o = run_prepare_case(w, G, k, None, "phase", few, sel=[0, 32511], per_count=40, seed=13)
+    inf = prep.info
+    assert inf["n_q"] == 32512 and inf["alias_hist"][3:7] == [626, 25940, 5586, 360]
+    assert inf["n_active_bf"] == 4093
+    worst = check_all_solutions(prep, w, strengths)
+    _say(f"c3: all 32512 frequencies at 32 strengths within {worst:.2e} of LAPACK on the exported systems")
+    spec = prep.scatter(torch.as_tensor(x, device=DEV)).cpu().numpy()
+    mirrored = check_scatter(prep, x, spec, prep_o, sel, few)
+    assert mirrored > 0
+    del G
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
 # full-frame workloads on sampled outputs, launch configuration of the bench
 # ----------------------------------------------------------------------------
 
@@ -825,6 +1041,10 @@ def test_c4_full_frame_sampled(c4_data, method):
     assert inf["n_active_bf"] == 9298
     worst = check_all_solutions(prep, w, strengths)
     _say(f"c4 {method}: all 130560 solutions within {worst:.2e} of LAPACK on the exported systems")
+    spec = prep.scatter(torch.as_tensor(x, device=DEV)).cpu().numpy()
+    mirrored = check_scatter(prep, x, spec, prep_o, sel, strengths)
+    assert mirrored > 100000
+    _say(f"c4 {method}: scatter bit-exact over the (1536, 769) plane, {mirrored} mirrored aliases")
 
 
 def test_c4_determinism(c4_data):
@@ -855,16 +1075,29 @@ def test_c4_slot_test_bitwise(c4_data, method):
     _say(f"c4 {method}: systems with and without the slot test bitwise equal")
 
 
-def test_c5_ssb_eight_sets_sampled():
+@pytest.fixture(scope="module")
+def c5_data():
     w = workload("c5")
     pix, k = bf_pixels(w)
-    _say("generating full-frame G (8807, 512, 257) on the GPU")
+    _say("generating the agreement-pass G (8807, 512, 257) on the GPU")
     G = data_stack_torch(w, pix, DEV)
+    torch.cuda.synchronize()
+    yield w, k, G
+    del G
+    torch.cuda.empty_cache()
+
+
+def _band_entries(w, n, seed):
+    ent = np.argwhere(O.band_mask(w.n_scan, w.step, w.band))
+    rng = np.random.default_rng(seed)
+    return ent[np.sort(rng.choice(len(ent), size=n, replace=False))]
+
+
+def test_c5_ssb_eight_sets_sampled(c5_data):
+    w, k, G = c5_data
     sets = ssb_sets(w, 8)
     mask = O.band_mask(w.n_scan, w.step, w.band)
-    ent = np.argwhere(mask)
-    rng = np.random.default_rng(6)
-    pick = ent[np.sort(rng.choice(len(ent), size=96, replace=False))]
+    pick = _band_entries(w, 96, 6)
     S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G, k, None, sets, w.band, entries=pick)
     # agreement from the kernel's own sums: property at full size
     Sg, Ng, _ = dsp.ssb(G, k, sets, step=w.step, band=w.band, agreement=False)
@@ -879,18 +1112,56 @@ def test_c5_ssb_eight_sets_sampled():
     E_prop = (num / power).cpu().numpy()
     assert np.allclose(E, E_prop, rtol=1e-6, atol=0)
     assert np.all(E > 0) and np.all(E <= 1.0)
-    del G, Sg, Ng
+    del Sg, Ng
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_c5_band_pass_sampled(c5_data, B):
+    """The one- and two-set band passes at full-frame size (the bench's timed
+    SSB pass is the one-set one) on sampled band entries, and each set's sums
+    equal to the same set's in the eight-set pass (nested sets)."""
+    w, k, G = c5_data
+    sets = ssb_sets(w, B)
+    pick = _band_entries(w, 256 if B == 1 else 128, 10 + B)
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G, k, None, sets, w.band, entries=pick)
+    assert np.all(E > 0) and np.all(E <= 1.0)
+    S8, N8, _ = dsp.ssb(G, k, ssb_sets(w, 8), step=w.step, band=w.band, agreement=False)
+    for b in range(B):
+        got = S8[b, entries[:, 0], entries[:, 1]].cpu().numpy()
+        assert np.linalg.norm(got - S[b, entries[:, 0], entries[:, 1]]) <= X_TOL * np.linalg.norm(got)
+    del S8, N8
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_c5_depth_136_sampled(c5_data, B):
+    """The thick-sample agreement pass at the pages' fitted depth, 136 A."""
+    w, k, G = c5_data
+    sets = [o.replace(depth=136.0) for o in ssb_sets(w, B)]
+    pick = _band_entries(w, 128 if B == 1 else 64, 20 + B)
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, G, k, None, sets, w.band, entries=pick)
+    assert np.all(E > 0) and np.all(E <= 1.0)
+
+
+@pytest.mark.parametrize("row_scales", [False, True])
+def test_c5_herm16_one_set_sampled(c5_data, row_scales):
+    """The one-set pass over the full-frame herm16 copy (one scale per pixel
+    or per stored row) against the oracle on the dequantized values."""
+    w, k, G = c5_data
+    Q, sc = dsp.quantize_herm16(G, rows=row_scales)
+    pick = _band_entries(w, 128, 30 + int(row_scales))
+    S, Nn, E, S_o, N_o, cols, wa, entries = _ssb_case(w, None, k, None, ssb_sets(w, 1), w.band, entries=pick,
+                                                      h16=(Q, sc))
+    assert 0 < E[0] <= 1.0
+    del Q, sc
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("row_scales", [False, True])
-def test_c5_herm16_eight_sets_sampled(row_scales):
+def test_c5_herm16_eight_sets_sampled(c5_data, row_scales):
     """Full-frame herm16: codes and scales bit-exact on sampled pixel planes,
     SSB over the compact copy against the oracle on sampled band entries."""
-    w = workload("c5")
-    pix, k = bf_pixels(w)
-    _say(f"generating full-frame G (8807, 512, 257) on the GPU (row scales {row_scales})")
-    G = data_stack_torch(w, pix, DEV)
+    w, k, G = c5_data
+    _say(f"full-frame herm16 (row scales {row_scales})")
     Q, sc = dsp.quantize_herm16(G, rows=row_scales)
     torch.cuda.synchronize()
     rng = np.random.default_rng(8)
@@ -899,8 +1170,6 @@ def test_c5_herm16_eight_sets_sampled(row_scales):
         Q_o, s_o = O.herm16_quantize(G[int(r):int(r) + 1].cpu().numpy(), rows=row_scales)
         assert np.array_equal(sc[int(r):int(r) + 1].cpu().numpy().view(np.uint32), s_o.view(np.uint32)), r
         assert np.array_equal(Q[int(r):int(r) + 1].cpu().numpy(), Q_o), r
-    del G
-    torch.cuda.empty_cache()
     sets = ssb_sets(w, 8)
     ent = np.argwhere(O.band_mask(w.n_scan, w.step, w.band))
     pick = ent[np.sort(rng.choice(len(ent), size=64, replace=False))]
