@@ -502,7 +502,7 @@ def test_prepared_cache_new_tensor_same_address():
     """A model handed out by the cache stays valid after its slot is
     replaced and after the cache is gone; a new G at a reused address, and
     G rewritten in place, are misses whose models match a fresh prepare."""
-    w = _tiny()
+    w = _tiny(method="complex")   # at most 6 aliases: both methods prepare
     pix, k = bf_pixels(w)
     G_np = data_stack_numpy(w, pix)
     kw = dict(step=w.step, upsampling=w.upsampling, smoothness=w.smoothness)
