@@ -19,6 +19,16 @@ exp(-2 pi i q.r_p) keeps the fine frequencies K = q (mod N dq):
             + N^2 sum_{K = q} [ c^(K) conj A(k) A(k - K)
                                + conj(c^(-K)) A(k) conj A(k + K) ].
 With c sampled on the u N fine grid, N^2 c^(K) = fft2(c)[K] / u^2.
+
+The probe here is written from the physics on its own, sharing nothing with
+the oracle's aperture and aberration functions, so the simulation pins them
+too: the objective aperture is a disc of semi-angle alpha (a hard stop, or a
+stop whose transmission falls linearly to zero over one detector pixel
+centred on the edge, the antialiased stop of "Tilt-corrected SSB on CUDA"
+Changes), and the aberration phase is the Krivanek series written with the
+complex beam angle w = theta_x + i theta_y, in which the term C_nm of radial
+order n and azimuthal order m is |w|^(n+1-m) Re[w^m e^(-i m phi_nm)] /
+(n + 1), times 2 pi / lambda.
 """
 from __future__ import annotations
 
@@ -26,12 +36,44 @@ import math
 
 import numpy as np
 
-from .dsp_oracle import aperture, chi, scan_frequency_step, signed_index
+
+def _signed(i, n: int):
+    """Signed frequency index of stored row i of an n-point FFT axis."""
+    i = np.asarray(i)
+    return np.where(i < n // 2, i, i - n)
+
+
+def objective_aperture(ky, kx, optics):
+    """Transmission of the objective stop at scattering vector k (1/A): the
+    beam angle lambda |k| against the semi-angle alpha.  Hard stop: 1 inside
+    the disc, its rim included, 0 outside.  Antialiased stop: the
+    transmission falls linearly from 1 to 0 across one detector pixel dk
+    centred on the rim, 1 - (|k| - alpha/lambda + dk/2) / dk clipped to
+    [0, 1]."""
+    r = np.hypot(np.asarray(ky, dtype=np.float64), np.asarray(kx, dtype=np.float64))
+    rim = optics.semiangle / optics.wavelength
+    if not optics.soft:
+        return np.where(r <= rim, 1.0, 0.0)
+    return np.minimum(1.0, np.maximum(0.0, 1.0 - (r - rim + 0.5 * optics.det_step) / optics.det_step))
+
+
+def aberration_phase(ky, kx, optics):
+    """Aberration phase (rad) of the beam at scattering vector k: with the
+    complex beam angle w = theta_x + i theta_y, theta = lambda k + tilt,
+    chi = (2 pi / lambda) sum_nm C_nm |w|^(n+1-m) Re[w^m e^(-i m phi_nm)] / (n+1)."""
+    lam = optics.wavelength
+    w = (lam * np.asarray(kx, dtype=np.float64) + optics.tilt[1]) + 1j * (
+        lam * np.asarray(ky, dtype=np.float64) + optics.tilt[0])
+    aw = np.abs(w)
+    acc = np.zeros(w.shape, dtype=np.float64)
+    for (n, m, c, phi) in optics.aberrations:
+        acc = acc + c * aw ** (n + 1 - m) * np.real(w ** m * np.exp(-1j * m * phi)) / (n + 1)
+    return acc * (2.0 * math.pi / lam)
 
 
 def probe_amplitude(ky, kx, optics):
-    """A(k) = a(k) exp(-i chi(k))."""
-    return aperture(np.hypot(ky, kx), optics) * np.exp(-1j * chi(ky, kx, optics))
+    """Probe wave in the far field, A(k) = aperture(k) exp(-i chi(k))."""
+    return objective_aperture(ky, kx, optics) * np.exp(-1j * aberration_phase(ky, kx, optics))
 
 
 def fine_spectrum(field: np.ndarray, upsampling: int) -> np.ndarray:
@@ -47,14 +89,14 @@ def first_order_G(k: np.ndarray, c_fine: np.ndarray, n_scan: int, step: float, u
     every stored frequency is summed (no alias rule applied)."""
     n = n_scan
     nf = upsampling * n
-    dq = scan_frequency_step(n, step)
+    dq = 1.0 / (n * step)
     F = np.fft.fft2(c_fine) / float(upsampling * upsampling)
     ky, kx = k[:, 0], k[:, 1]
     A0 = probe_amplitude(ky, kx, optics)
     G = np.zeros((k.shape[0], n, n // 2 + 1), dtype=np.complex128)
     half = nf // 2
     for iy in range(n):
-        yh = int(signed_index(iy, n))
+        yh = int(_signed(iy, n))
         for ix in range(n // 2 + 1):
             acc = np.zeros(k.shape[0], dtype=np.complex128)
             for jy in range(-upsampling, upsampling + 1):
@@ -121,7 +163,7 @@ def wave_optics_G(n_scan: int, step: float, m_sim: int, optics, c_fine: np.ndarr
     psi = np.fft.ifft2(probe_amplitude(KY, KX, optics))
     F = np.fft.fft2(c_fine)
     Fs = np.zeros((m, m), dtype=np.complex128)
-    idx = signed_index(np.arange(nf), nf)
+    idx = _signed(np.arange(nf), nf)
     Fs[np.ix_(idx % m, idx % m)] = F
     c_sim = np.fft.ifft2(Fs) * (m / nf) ** 2
     t = float(getattr(optics, "depth", 0.0))

@@ -226,16 +226,78 @@ def _wave_optics_residual(sigma, opt, n=16, step=0.5, u=3, m=96, seed=5):
     return math.sqrt(num / den), counts
 
 
-def test_transfer_matches_wave_optics():
-    """The first-order transfer (all alias, lobe, sign and tilt conventions)
-    reproduces a brute-force wave-optics simulation to O(sigma)."""
+@pytest.mark.parametrize("soft", [True, False])
+def test_transfer_matches_wave_optics(soft):
+    """The first-order transfer (all alias, lobe, sign and tilt conventions,
+    and the aperture, soft or hard) reproduces a brute-force wave-optics
+    simulation to O(sigma).  The simulation's probe has its own aperture and
+    aberration phase, written from the physics apart from the oracle's."""
     n, step = 16, 0.5
-    opt = tiny_optics(O.scan_frequency_step(n, step))
+    opt = tiny_optics(O.scan_frequency_step(n, step), soft=soft)
     r1, counts = _wave_optics_residual(1e-3, opt)
     r2, _ = _wave_optics_residual(5e-4, opt)
     assert r1 < 1e-2
     assert 0.4 < r2 / r1 < 0.6           # second-order remainder halves with sigma
     assert len(set(counts.tolist())) > 1  # the tiny case exercises several alias counts
+
+
+def test_simulator_probe_is_its_own():
+    """The simulator imports nothing from the oracle, and its aperture and
+    aberration phase agree with the oracle's (two independent codings of the
+    same definitions) at scattered points, edge ring and rim included."""
+    import inspect
+
+    src = inspect.getsource(S)
+    assert "dsp_oracle" not in src and "from ." not in src
+    rng = np.random.default_rng(3)
+    kc = ALPHA / LAM
+    r = np.concatenate([rng.uniform(0, 1.2 * kc, 400), kc + np.array([-0.06, -0.03, 0.0, 0.01, 0.03, 0.06])])
+    t = rng.uniform(0, 2 * np.pi, r.size)
+    ky, kx = r * np.sin(t), r * np.cos(t)
+    for soft in (True, False):
+        o = tiny_optics(0.12, soft=soft)
+        assert np.array_equal(S.objective_aperture(ky, kx, o) > 0, O.aperture(r, o) > 0)
+        assert np.allclose(S.objective_aperture(ky, kx, o), O.aperture(np.hypot(ky, kx), o), rtol=0, atol=1e-12)
+        assert np.allclose(S.aberration_phase(ky, kx, o), O.chi(ky, kx, o), rtol=1e-12, atol=1e-9)
+
+
+def test_hard_aperture_radius_is_pinned(monkeypatch):
+    """A hard stop of radius alpha/lambda + dk/2 (the soft support's radius)
+    in place of alpha/lambda fails the wave-optics pin and the tiny
+    configuration's bright-field count (planted on the CPU only)."""
+    n, step = 16, 0.5
+    opt = tiny_optics(O.scan_frequency_step(n, step), soft=False)
+    true_aperture = O.aperture
+
+    def wide(kabs, optics):
+        if optics.soft:
+            return true_aperture(kabs, optics)
+        return (np.asarray(kabs) <= optics.semiangle / optics.wavelength + 0.5 * optics.det_step).astype(float)
+
+    monkeypatch.setattr(O, "aperture", wide)
+    r_bad, _ = _wave_optics_residual(1e-3, opt)
+    assert r_bad > 0.05
+    assert _c1_bright_field_count() != 113
+
+
+def _c1_bright_field_count():
+    """Active pixels of the tiny SSB configuration's whole 24 x 24 detector
+    (hard 30 mrad stop, detector pitch alpha/lambda / 6.04)."""
+    w = workload("c1")
+    nd = w.n_det
+    iy, ix = np.mgrid[0:nd, 0:nd]
+    d = np.stack([(iy.ravel() - nd // 2), (ix.ravel() - nd // 2)], axis=1).astype(float) * w.optics.det_step
+    return len(O.active_pixels(d, w.optics))
+
+
+def test_c1_bright_field_count(golden):
+    """The tiny SSB configuration's hard stop keeps about 113 of the 24 x 24
+    detector pixels (tests/golden/bright_field_counts.txt); brute force over
+    the lattice: the integer offsets with dy^2 + dx^2 <= 6.04^2 are 113."""
+    want = int(golden("bright_field_counts.txt")["c1_hard_30mrad_24px"][0][0])
+    brute = sum(1 for a in range(-12, 12) for b in range(-12, 12) if a * a + b * b <= 6.04 ** 2)
+    assert brute == want
+    assert _c1_bright_field_count() == want
 
 
 def test_wave_optics_pin_catches_planted_mistakes(monkeypatch):
@@ -745,6 +807,80 @@ def test_planted_transpose_breaks_minimality(monkeypatch):
     reg = prep.scale * 0.05 * np.concatenate([prep.p[i][:A], prep.p[i][A:]])
     x_true = np.linalg.solve(T.conj().T @ (w[:, None] * T) + np.diag(reg), T.conj().T @ (w * cols[i]))
     assert np.linalg.norm(xs[i] - x_true) > 1e-6 * np.linalg.norm(x_true)
+
+
+def _prior_deviation(method):
+    """The prior as the solve applies it, read back from the solution: with
+    x = (M + mu D)^-1 r (mu = strength x scale, per component for complex),
+    D x = (r - M x) / mu, so p_j = (r - M x)_j / (mu_j x_j) at every unknown.
+    Returns the largest relative deviation of p from the pages' printed prior
+    (1 + q^2/s^2)^2 ("Where the 9 s of regularized preparation goes", Raw
+    numbers, the prior stage; tests/golden/prior.txt) taken at each alias's
+    own fine frequency |Q| = |K| dq, over a three-times upsampled tiny scan
+    whose aliases of one scan frequency lie at different |Q|."""
+    n, step, u = 12, 0.45, 3
+    opt = tiny_optics(0.1)
+    rng = np.random.default_rng(31)
+    w = workload("c2")
+    _, k = bf_pixels(w)
+    k = k[O.active_pixels(k, opt)]
+    q = O.unique_frequencies(n)
+    cols = [rng.standard_normal(len(k)) + 1j * rng.standard_normal(len(k)) for _ in q]
+    wts = rng.uniform(0.5, 1.5, len(k))
+    s_p = 1.3                         # |Q| / s_p spans about 0 to 3 over the aliases
+    prep = O.prepare(q, cols, k, wts, n, step, u, opt, method, smoothness=s_p)
+    dq = O.scan_frequency_step(n, step)
+    st = 0.2 if method == "phase" else (0.2, 0.35)
+    xs = O.solve(prep, st)
+    worst, n_diff = 0.0, 0
+    for i, x in enumerate(xs):
+        A = int(prep.A[i])
+        if A == 0:
+            continue
+        Q = prep.K[i] * dq
+        t2 = (Q[:, 0] ** 2 + Q[:, 1] ** 2) / s_p ** 2
+        printed = (1.0 + t2) ** 2
+        if method == "phase":
+            mu = st * prep.scale * np.ones(A)
+            want = printed
+        else:
+            mu = prep.scale * np.concatenate([st[0] * np.ones(A), st[1] * np.ones(A)])
+            want = np.concatenate([printed, printed])
+        p_back = (prep.r[i] - prep.M[i] @ x) / (mu * x)
+        assert np.abs(p_back.imag).max() <= 1e-6 * np.abs(p_back.real).max()
+        worst = max(worst, float(np.abs(p_back.real - want).max() / want.max()))
+        n_diff += int(np.ptp(printed) > 0.1)
+    assert n_diff > 10                # aliases of one frequency see different priors
+    return worst
+
+
+@pytest.mark.parametrize("method", ["phase", "complex"])
+def test_prior_through_the_solve(method, golden):
+    """The prior the solve applies, recovered from its solutions, is the
+    printed (1 + q^2/s^2)^2 at each alias's fine |Q|."""
+    assert golden("prior.txt")["exponent"][0][0] == "2"
+    assert _prior_deviation(method) <= 1e-6
+
+
+def test_prior_mistakes_are_caught(monkeypatch):
+    """Planted on the CPU: a prior of power 1, or one taken at the coarse scan
+    frequency instead of the alias's fine |Q|, fails the solve pin."""
+    true_prior = O.prior
+
+    def power_one(Q, s):
+        return np.sqrt(true_prior(Q, s))
+
+    monkeypatch.setattr(O, "prior", power_one)
+    assert _prior_deviation("phase") > 1e-2
+    n, step = 12, 0.45
+    period = n * O.scan_frequency_step(n, step)
+
+    def coarse(Q, s):
+        Qc = (np.asarray(Q) / period + 0.5) % 1.0 - 0.5
+        return true_prior(Qc * period, s)
+
+    monkeypatch.setattr(O, "prior", coarse)
+    assert _prior_deviation("complex") > 1e-2
 
 
 # ----------------------------------------------------------------------------
