@@ -230,6 +230,30 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
                    double *agreement_out_host, void *hip_stream);
 
 /*
+ * dsp_ssb for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, outputs and errors as dsp_ssb; the results agree with dsp_ssb's
+ * to rounding (its stream-K plan may cut the pixel sums into fewer pieces).
+ * The call allocates no device memory: no hipMalloc, hipFree or allocating
+ * library routine.  Every device buffer of the pass (the layout's pixel,
+ * tile and plan tables, copied from host tables the library builds and
+ * caches on the host, and the per-call tables and partial sums) is carved
+ * from one fixed array of DSP_NOALLOC_SCRATCH_BYTES per device, part of the
+ * library's code object: each GPU the library runs on holds it from load
+ * until the process ends.  A pass that needs more returns DSP_ENOMEM (with the
+ * sizes in dsp_last_error) before any device work; the plan first takes
+ * fewer stream-K waves to fit (about 8 sets over 9,000 pixels of a
+ * 512 x 512 scan's 0.2-0.9 1/A band fit).  All calls on one GPU share that
+ * array, which keeps the last call's contents: calls that overlap on one GPU
+ * (other streams, other threads) race and must be serialized by the caller.
+ */
+#define DSP_NOALLOC_SCRATCH_BYTES (64ull << 20)
+dsp_status dsp_ssb_noalloc(const void *G_c64_dev, int n_bf, const double *bf_coords_host,
+                           const double *weights_host, const dsp_scan *scan, const dsp_optics *sets_host,
+                           int B, const double *band_invA, void *S_out_c128_dev, double *norm_out_dev,
+                           double *agreement_out_host, void *hip_stream);
+
+/*
  * Phase model derived from a prepared complex model, without a pass over G
  * ("Where the 9 s of regularized preparation goes", section "Code path":
  * the complex system contains the phase one).  For every frequency the phase

@@ -373,13 +373,19 @@ def _check_Q(Q, scale):
 
 def ssb(G, bf_coords, optics_sets: Sequence, step: float, band: Optional[Tuple[float, float]] = None,
         weights=None, want_S: bool = True, want_N: bool = True, agreement: bool = True, stream=None,
-        herm16=None):
+        herm16=None, no_alloc: bool = False, out=None):
     """SSB sums for up to 8 optics sets in one pass over G.
 
     ``herm16=(Q, scale)`` from quantize_herm16 runs the pass over the compact
-    copy instead (G may then be None).  Returns (S (B, N, N/2+1) complex128
-    or None, N (B, N, N/2+1) float64 or None, E (B,) numpy float64 or None)."""
+    copy instead (G may then be None).  ``no_alloc=True`` runs the
+    allocation-free pass (dsp_ssb_noalloc: the library allocates no device
+    memory); with ``out=(S, N)`` (either may be None) the outputs are written
+    into those tensors instead of new ones.  Returns (S (B, N, N/2+1)
+    complex128 or None, N (B, N, N/2+1) float64 or None, E (B,) numpy float64
+    or None)."""
     torch = _torch()
+    if no_alloc and herm16 is not None:
+        raise DspError(_lib.DSP_EINVAL, "the allocation-free pass reads complex64 G")
     if herm16 is not None:
         Q, sc = herm16
         n = _check_Q(Q, sc)
@@ -397,8 +403,15 @@ def ssb(G, bf_coords, optics_sets: Sequence, step: float, band: Optional[Tuple[f
         arr[i] = _optics(o)
     scan = _lib.ScanC(n, float(step))
     nh = n // 2 + 1
-    S = torch.empty((B, n, nh), dtype=torch.complex128, device=device) if want_S else None
-    Nn = torch.empty((B, n, nh), dtype=torch.float64, device=device) if want_N else None
+    if out is not None:
+        S, Nn = out
+        for t, dt in ((S, torch.complex128), (Nn, torch.float64)):
+            if t is not None and (t.dtype != dt or tuple(t.shape) != (B, n, nh) or not t.is_contiguous()
+                                  or t.device != device):
+                raise DspError(_lib.DSP_EINVAL, f"out tensors must be contiguous {(B, n, nh)} on {device}")
+    else:
+        S = torch.empty((B, n, nh), dtype=torch.complex128, device=device) if want_S else None
+        Nn = torch.empty((B, n, nh), dtype=torch.float64, device=device) if want_N else None
     E = np.zeros(max(1, B), dtype=np.float64) if agreement else None
     bd = np.asarray(band, dtype=np.float64) if band is not None else None
     outs = (_dptr(bd), ctypes.c_void_p(S.data_ptr()) if S is not None else None,
@@ -409,8 +422,8 @@ def ssb(G, bf_coords, optics_sets: Sequence, step: float, band: Optional[Tuple[f
                                  1 if sc.dim() == 2 else 0, k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan), arr,
                                  B, *outs))
     else:
-        _check(_L.dsp_ssb(ctypes.c_void_p(G.data_ptr()), k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan), arr, B,
-                          *outs))
+        fn = _L.dsp_ssb_noalloc if no_alloc else _L.dsp_ssb
+        _check(fn(ctypes.c_void_p(G.data_ptr()), k.shape[0], _dptr(k), _dptr(w), ctypes.byref(scan), arr, B, *outs))
     return S, Nn, (E[:B] if E is not None else None)
 
 

@@ -64,7 +64,10 @@ EXPORTS = (
     "dsp_destroy", "dsp_last_error", "dsp_geometry_counts", "dsp_alias_geometry", "dsp_active_bf",
     "dsp_band_count", "dsp_chi_host", "dsp_chi_shift_host", "dsp_sincos_host", "dsp_derive_phase", "dsp_quantize_herm16",
     "dsp_ssb_herm16", "dsp_preview", "dsp_loss", "dsp_cache_create", "dsp_cache_destroy", "dsp_cache_get",
+    "dsp_ssb_noalloc",
 )
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DSP_NOALLOC_SCRATCH_BYTES
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -97,6 +100,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsp_ssb.restype = _I
     lib.dsp_ssb.argtypes = [_P, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _I, _DP, _P, _P,
                             _DP, _P]
+    lib.dsp_ssb_noalloc.restype = _I
+    lib.dsp_ssb_noalloc.argtypes = [_P, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _I, _DP, _P,
+                                    _P, _DP, _P]
     lib.dsp_ssb_herm16.restype = _I
     lib.dsp_ssb_herm16.argtypes = [_P, _P, _I, _I, _DP, _DP, ctypes.POINTER(ScanC), ctypes.POINTER(OpticsC), _I,
                                    _DP, _P, _P, _DP, _P]

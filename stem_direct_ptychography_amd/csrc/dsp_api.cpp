@@ -35,6 +35,7 @@ using namespace dsp;
 // eight the partial-sum fixup costs more than the launches gain (whole
 // full-frame step: 27.6 ms at 4, 27.2 at 8, 27.3 at 12 and at 16).
 constexpr int GRAM_ROUNDS = 8;
+static_assert(NOALLOC_SCRATCH_BYTES == DSP_NOALLOC_SCRATCH_BYTES, "one scratch size in the ABI and the kernels");
 
 namespace {
 
@@ -1010,12 +1011,14 @@ struct SsbKey {
     int device = 0, n_scan = 0, soft = 0, n_bf = 0, has_band = 0;
     int up = 1;         // lanes on the u-times finer grid (previews)
     int preview = 0;    // lanes: every fine K != 0 that some lobe can reach (else the stored band)
+    int noalloc = 0;    // host tables only, plans sized to the fixed scratch (dsp_ssb_noalloc)
     double step = 0, lam = 0, alpha = 0, dk = 0, lo = 0, hi = 0;
     std::vector<double> coords, weights;
     bool operator==(const SsbKey &o) const {
         return device == o.device && n_scan == o.n_scan && soft == o.soft && n_bf == o.n_bf && has_band == o.has_band &&
-               up == o.up && preview == o.preview && step == o.step && lam == o.lam && alpha == o.alpha &&
-               dk == o.dk && lo == o.lo && hi == o.hi && coords == o.coords && weights == o.weights;
+               up == o.up && preview == o.preview && noalloc == o.noalloc && step == o.step && lam == o.lam &&
+               alpha == o.alpha && dk == o.dk && lo == o.lo && hi == o.hi && coords == o.coords &&
+               weights == o.weights;
     }
 };
 
@@ -1034,6 +1037,7 @@ struct SsbLayout {
     long long *d_wbegin[4] = {nullptr, nullptr, nullptr, nullptr};
     int *d_seg_off[4] = {nullptr, nullptr, nullptr, nullptr};
     int *d_seg_first[4] = {nullptr, nullptr, nullptr, nullptr};
+    size_t scratch_need[4] = {0, 0, 0, 0};   // noalloc: scratch bytes of a pass (0: does not fit)
     double host_ms = 0.0;
     ~SsbLayout() {
         hipSetDevice(key.device);
@@ -1049,6 +1053,20 @@ struct SsbLayout {
 };
 
 int maxb_index(int maxb) { return maxb == 1 ? 0 : (maxb == 2 ? 1 : (maxb == 4 ? 2 : 3)); }
+
+// Scratch bytes of one allocation-free pass of up to maxb sets: the
+// layout's device tables (trig table, pixels, plane offsets, tiles, stream-K
+// tables), the per-call tables and the partial sums, each piece 256-byte
+// aligned in the order ssb_impl carves them.
+size_t noalloc_need(size_t n_pix, size_t n_tiles, int maxb, size_t W, size_t n_segs) {
+    return carve_size(TRIG_N, sizeof(double2)) + carve_size(n_pix, sizeof(PixelBase)) +
+           carve_size(n_pix, sizeof(long long)) + carve_size(n_tiles, sizeof(SsbTile)) +
+           carve_size(W + 1, sizeof(long long)) + carve_size(W, sizeof(int)) + carve_size(n_tiles + 1, sizeof(int)) +
+           carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) +
+           carve_size(n_segs * (size_t)ssb_nacc(maxb) * 64, sizeof(double)) +
+           carve_size(n_tiles * (size_t)(maxb + 1), sizeof(double)) + carve_size(maxb + 1, sizeof(double)) +
+           carve_size(std::max<size_t>(1, (size_t)maxb * n_pix * TAY_N), sizeof(double));
+}
 
 dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const double *coords,
                             const double *weights, std::shared_ptr<SsbLayout> &out) {
@@ -1095,12 +1113,15 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
     }
     const int n_tiles = (int)L->tiles.size();
     const int n_pix = (int)L->act.pix.size();
-    if ((st = dev_alloc(&L->d_pixbase, (size_t)n_pix)) || (st = dev_alloc(&L->d_goff, (size_t)n_pix)) ||
-        (st = dev_alloc(&L->d_tiles, (size_t)std::max(1, n_tiles))))
-        return st;
-    HIP_TRY(hipMemcpy(L->d_pixbase, L->act.pix.data(), sizeof(PixelBase) * n_pix, hipMemcpyHostToDevice));
-    HIP_TRY(hipMemcpy(L->d_goff, L->act.goff.data(), sizeof(long long) * n_pix, hipMemcpyHostToDevice));
-    if (n_tiles) HIP_TRY(hipMemcpy(L->d_tiles, L->tiles.data(), sizeof(SsbTile) * n_tiles, hipMemcpyHostToDevice));
+    const bool dev_tables = !key.noalloc;   // noalloc: the call copies the host tables into its scratch
+    if (dev_tables) {
+        if ((st = dev_alloc(&L->d_pixbase, (size_t)n_pix)) || (st = dev_alloc(&L->d_goff, (size_t)n_pix)) ||
+            (st = dev_alloc(&L->d_tiles, (size_t)std::max(1, n_tiles))))
+            return st;
+        HIP_TRY(hipMemcpy(L->d_pixbase, L->act.pix.data(), sizeof(PixelBase) * n_pix, hipMemcpyHostToDevice));
+        HIP_TRY(hipMemcpy(L->d_goff, L->act.goff.data(), sizeof(long long) * n_pix, hipMemcpyHostToDevice));
+        if (n_tiles) HIP_TRY(hipMemcpy(L->d_tiles, L->tiles.data(), sizeof(SsbTile) * n_tiles, hipMemcpyHostToDevice));
+    }
     if (n_tiles) {
         int n_cu = 0;
         HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, key.device));
@@ -1128,7 +1149,19 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
             HIP_TRY(ssb_occupancy(maxb, &bpc));
             bpc = std::max(1, bpc);
             const long long total_it = (long long)n_tiles * n_pix;
-            const int W = (int)std::max(1LL, std::min((long long)bpc * n_cu * GRAM_ROUNDS, total_it / 64));
+            int W = (int)std::max(1LL, std::min((long long)bpc * n_cu * GRAM_ROUNDS, total_it / 64));
+            if (key.noalloc) {
+                // the most waves (down from the device path's count, halving)
+                // whose tables and partial sums (at most W + n_tiles segments)
+                // fit the fixed scratch; none: the pass does not fit
+                while (W > 1 && noalloc_need(n_pix, n_tiles, maxb, W, (size_t)W + n_tiles) > NOALLOC_SCRATCH_BYTES)
+                    W = std::max(1, W / 2);
+                if (noalloc_need(n_pix, n_tiles, maxb, W, (size_t)W + n_tiles) > NOALLOC_SCRATCH_BYTES) {
+                    L->scratch_need[mi] = 0;
+                    L->waves[mi] = 0;
+                    continue;
+                }
+            }
             StreamKPlan plan;
             plan_stream_k_iter(cost, n_tiles, n_pix, W, plan);
             L->waves[mi] = W;
@@ -1136,6 +1169,10 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
             L->wbegin[mi] = plan.wbegin;
             L->seg_off[mi] = plan.seg_off;
             L->seg_first[mi] = plan.seg_first;
+            if (key.noalloc) {
+                L->scratch_need[mi] = noalloc_need(n_pix, n_tiles, maxb, W, plan.n_segs);
+                continue;
+            }
             if ((st = dev_alloc(&L->d_wbegin[mi], plan.wbegin.size())) ||
                 (st = dev_alloc(&L->d_seg_off[mi], plan.seg_off.size())) ||
                 (st = dev_alloc(&L->d_seg_first[mi], plan.seg_first.size())))
@@ -1857,7 +1894,7 @@ dsp_status dsp_alias_table(const dsp_handle *h, int32_t *q_host, int32_t *count_
 }  // extern "C"
 
 // The SSB pass over complex64 G (GQ null) or herm16 G (GQ, gscale).
-// Scratch of one SSB pass (the stream's arena).
+// Scratch of one SSB pass (the stream's arena, or the fixed scratch).
 struct SsbPassBufs {
     PixelRec *pix;
     double *chi;        // [n_pix][MAX_SETS_DEV]
@@ -1866,16 +1903,37 @@ struct SsbPassBufs {
     double *tay;        // [n_pix][TAY_N] for a Taylor pass, else null
 };
 
+// Device copies of a pass's layout tables: the layout's own, or copies in
+// the fixed scratch of the allocation-free pass.
+struct SsbDevTables {
+    const PixelBase *pixbase = nullptr;
+    const long long *goff = nullptr;
+    const SsbTile *tiles = nullptr;
+    const long long *wbegin = nullptr;   // of the pass's compiled set count
+    const int *seg_off = nullptr;
+    const int *seg_first = nullptr;
+    const double2 *trig = nullptr;
+};
+
+static dsp_status layout_tables(const SsbLayout &L, int mi, int device, SsbDevTables &t) {
+    t.pixbase = L.d_pixbase;
+    t.goff = L.d_goff;
+    t.tiles = L.d_tiles;
+    t.wbegin = L.d_wbegin[mi];
+    t.seg_off = L.d_seg_off[mi];
+    t.seg_first = L.d_seg_first[mi];
+    return trig_table_device(device, &t.trig);
+}
+
 // One pass over G for B sets on layout L: pixel terms, then the SSB kernel
 // with lanes on the (M, M/2 + 1) grid writing S and N there.  With bufs.tay
 // (B tables of [n_pix][TAY_N]), the kernel takes both lobes' phases from each
 // set's chi Taylor coefficients about theta(k) (one evaluation of the even and
 // odd parts in lambda q per pixel and set instead of the polynomial at both
 // displaced points).
-static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int B, const void *G_c64_dev,
-                           const void *GQ_dev, const float *gscale_dev, int h16_rows, int N, int M, double2 *S_out,
-                           double *N_out, const SsbPassBufs &bufs, int device, hipStream_t stream) {
-    dsp_status st;
+static dsp_status ssb_pass(const SsbLayout &L, const SsbDevTables &dt, const dsp_optics *sets_host, int B,
+                           const void *G_c64_dev, const void *GQ_dev, const float *gscale_dev, int h16_rows, int N,
+                           int M, double2 *S_out, double *N_out, const SsbPassBufs &bufs, hipStream_t stream) {
     const int n_tiles = (int)L.tiles.size();
     const int n_pix = (int)L.act.pix.size();
     const int mi = maxb_index(ssb_maxb(B));
@@ -1887,9 +1945,9 @@ static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int 
         const OpticsDev od = make_optics_dev(sets_host + b);
         // a(k) once (set 0 writes it), chi(k) per set
         double *tb = bufs.tay ? bufs.tay + (size_t)b * n_pix * TAY_N : nullptr;   // set b's Taylor table
-        if (b == 0) HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, nullptr, 0, tb, stream));
-        else if (tb) HIP_TRY(launch_pixel_terms(L.d_pixbase, nullptr, n_pix, apd, od, nullptr, 0, tb, stream));
-        HIP_TRY(launch_pixel_terms(L.d_pixbase, bufs.pix, n_pix, apd, od, bufs.chi + b, MAX_SETS_DEV, nullptr, stream));
+        if (b == 0) HIP_TRY(launch_pixel_terms(dt.pixbase, bufs.pix, n_pix, apd, od, nullptr, 0, tb, stream));
+        else if (tb) HIP_TRY(launch_pixel_terms(dt.pixbase, nullptr, n_pix, apd, od, nullptr, 0, tb, stream));
+        HIP_TRY(launch_pixel_terms(dt.pixbase, bufs.pix, n_pix, apd, od, bufs.chi + b, MAX_SETS_DEV, nullptr, stream));
         sp.tau_y[b] = od.tau_y;
         sp.tau_x[b] = od.tau_x;
         sp.pt2[b] = od.pt2;
@@ -1901,11 +1959,11 @@ static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int 
     sp.h16_rows = h16_rows;
     sp.plane = (long long)N * (N / 2 + 1);
     sp.pix = bufs.pix;
-    sp.goff = L.d_goff;
+    sp.goff = dt.goff;
     sp.chi_tab = bufs.chi;
     sp.tay = bufs.tay;
     sp.n_pix = n_pix;
-    sp.tiles = L.d_tiles;
+    sp.tiles = dt.tiles;
     sp.N = N;
     sp.nh = N / 2 + 1;
     sp.M = M;
@@ -1917,11 +1975,11 @@ static dsp_status ssb_pass(const SsbLayout &L, const dsp_optics *sets_host, int 
     sp.lam = sets_host[0].wavelength_A;
     sp.S_out = S_out;
     sp.N_out = N_out;
-    sp.wbegin = L.d_wbegin[mi];
-    sp.seg_off = L.d_seg_off[mi];
-    sp.seg_first = L.d_seg_first[mi];
+    sp.wbegin = dt.wbegin;
+    sp.seg_off = dt.seg_off;
+    sp.seg_first = dt.seg_first;
     sp.partial = bufs.part;
-    if ((st = trig_table_device(device, &sp.trig))) return st;
+    sp.trig = dt.trig;
     HIP_TRY(launch_ssb(sp, L.waves[mi], n_tiles, bufs.tile_part, stream));
     return DSP_OK;
 }
@@ -1989,10 +2047,13 @@ static SsbKey pass_key(int device, const dsp_scan *scan, const dsp_optics *o, in
     return key;
 }
 
+// noalloc: every device buffer of the pass, layout tables included, comes
+// from the fixed scratch (no device allocation); the plan is the one sized
+// to it.
 static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const float *gscale_dev, int h16_rows, int n_bf,
                            const double *bf_coords_host, const double *weights_host, const dsp_scan *scan,
                            const dsp_optics *sets_host, int B, const double *band_invA, void *S_out_c128_dev,
-                           double *norm_out_dev, double *agreement_out_host, void *hip_stream) {
+                           double *norm_out_dev, double *agreement_out_host, void *hip_stream, bool noalloc = false) {
     dsp_status st;
     if ((st = check_scan(scan))) return st;
     if (!sets_host || B < 1 || B > MAX_SETS) return fail(DSP_EINVAL, "need 1 <= B <= %d optics sets", MAX_SETS);
@@ -2031,6 +2092,7 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
     key.lo = band_invA ? band_invA[0] : 0.0;
     key.hi = band_invA ? band_invA[1] : 0.0;
     key.n_bf = n_bf;
+    key.noalloc = noalloc ? 1 : 0;
     key.coords.assign(bf_coords_host, bf_coords_host + 2 * (size_t)n_bf);
     if (weights_host) key.weights.assign(weights_host, weights_host + n_bf);
     std::shared_ptr<SsbLayout> lay;
@@ -2042,6 +2104,11 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
     const int mi = maxb_index(maxb);
     const int stride = ssb_partial_stride(B);
     const size_t plane = (size_t)N * nh;
+    if (noalloc && n_tiles > 0 && L.waves[mi] == 0)
+        return fail(DSP_ENOMEM,
+                    "the allocation-free SSB pass of %d sets over %d pixels and %d frequency tiles needs more than "
+                    "its fixed %zu-byte scratch",
+                    B, n_pix, n_tiles, NOALLOC_SCRATCH_BYTES);
     if (S_out_c128_dev && band_invA) HIP_TRY(launch_fill_zero((double *)S_out_c128_dev, (size_t)B * plane * 2, stream));
     if (norm_out_dev && band_invA) HIP_TRY(launch_fill_zero(norm_out_dev, (size_t)B * plane, stream));
     if (n_tiles == 0) {
@@ -2052,14 +2119,60 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
         return DSP_OK;
     }
 
-    // per-call tables in the stream's scratch arena
+    // per-call tables: the stream's scratch arena, or (noalloc) the fixed
+    // scratch, which also takes copies of the layout's tables
     const size_t n_part = (size_t)L.n_segs[mi] * ssb_nacc(maxb) * 64;
     const size_t n_tay = (size_t)B * n_pix * TAY_N;
-    const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) +
-                        carve_size(n_part, sizeof(double)) + carve_size((size_t)n_tiles * stride, sizeof(double)) +
-                        carve_size(B + 1, sizeof(double)) + carve_size(std::max<size_t>(1, n_tay), sizeof(double));
+    SsbDevTables dt;
     char *scr = nullptr;
-    if ((st = arena_get(device, stream, need, &scr))) return st;
+    if (noalloc) {
+        HIP_TRY(noalloc_scratch(&scr));
+        // every piece must lie inside the scratch: the plan was sized to it
+        // (noalloc_need carves the same pieces in the same order)
+        const size_t total = noalloc_need(n_pix, n_tiles, maxb, L.waves[mi], L.n_segs[mi]);
+        if (total != L.scratch_need[mi] || total > NOALLOC_SCRATCH_BYTES)
+            return fail(DSP_ENOMEM, "allocation-free SSB pass: %zu bytes of scratch planned, %zu held", total,
+                        NOALLOC_SCRATCH_BYTES);
+        Carve tv{scr};
+        double2 *d_trig = tv.take<double2>(TRIG_N);
+        PixelBase *d_pb = tv.take<PixelBase>(n_pix);
+        long long *d_go = tv.take<long long>(n_pix);
+        SsbTile *d_ti = tv.take<SsbTile>(n_tiles);
+        long long *d_wb = tv.take<long long>(L.wbegin[mi].size());
+        int *d_so = tv.take<int>(L.seg_off[mi].size());
+        int *d_sf = tv.take<int>(L.seg_first[mi].size());
+        static const std::vector<double2> trig_host = [] {
+            std::vector<double2> t(TRIG_N);
+            trig_table_host(t.data());
+            return t;
+        }();
+        // pageable host sources: each copy has consumed its source when the call returns
+        HIP_TRY(hipMemcpyAsync(d_trig, trig_host.data(), TRIG_N * sizeof(double2), hipMemcpyHostToDevice, stream));
+        HIP_TRY(hipMemcpyAsync(d_pb, L.act.pix.data(), n_pix * sizeof(PixelBase), hipMemcpyHostToDevice, stream));
+        HIP_TRY(hipMemcpyAsync(d_go, L.act.goff.data(), n_pix * sizeof(long long), hipMemcpyHostToDevice, stream));
+        HIP_TRY(hipMemcpyAsync(d_ti, L.tiles.data(), n_tiles * sizeof(SsbTile), hipMemcpyHostToDevice, stream));
+        HIP_TRY(hipMemcpyAsync(d_wb, L.wbegin[mi].data(), L.wbegin[mi].size() * sizeof(long long),
+                               hipMemcpyHostToDevice, stream));
+        HIP_TRY(hipMemcpyAsync(d_so, L.seg_off[mi].data(), L.seg_off[mi].size() * sizeof(int), hipMemcpyHostToDevice,
+                               stream));
+        HIP_TRY(hipMemcpyAsync(d_sf, L.seg_first[mi].data(), L.seg_first[mi].size() * sizeof(int),
+                               hipMemcpyHostToDevice, stream));
+        dt.trig = d_trig;
+        dt.pixbase = d_pb;
+        dt.goff = d_go;
+        dt.tiles = d_ti;
+        dt.wbegin = d_wb;
+        dt.seg_off = d_so;
+        dt.seg_first = d_sf;
+        scr += tv.off;
+    } else {
+        const size_t need = carve_size(n_pix, sizeof(PixelRec)) +
+                            carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) + carve_size(n_part, sizeof(double)) +
+                            carve_size((size_t)n_tiles * stride, sizeof(double)) + carve_size(B + 1, sizeof(double)) +
+                            carve_size(std::max<size_t>(1, n_tay), sizeof(double));
+        if ((st = arena_get(device, stream, need, &scr))) return st;
+        if ((st = layout_tables(L, mi, device, dt))) return st;
+    }
     Carve cv{scr};
     PixelRec *d_pix = cv.take<PixelRec>(n_pix);
     double *d_chi = cv.take<double>((size_t)MAX_SETS_DEV * n_pix);
@@ -2069,8 +2182,8 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
     double *d_tay = cv.take<double>(std::max<size_t>(1, n_tay));
 
     SsbPassBufs bufs{d_pix, d_chi, d_part, d_tile_part, d_tay};
-    if ((st = ssb_pass(L, sets_host, B, G_c64_dev, GQ_dev, gscale_dev, h16_rows, N, N, (double2 *)S_out_c128_dev,
-                       norm_out_dev, bufs, device, stream)))
+    if ((st = ssb_pass(L, dt, sets_host, B, G_c64_dev, GQ_dev, gscale_dev, h16_rows, N, N, (double2 *)S_out_c128_dev,
+                       norm_out_dev, bufs, stream)))
         return st;
     std::vector<double> E(B + 1, 0.0);
     if (agreement_out_host) {
@@ -2092,6 +2205,14 @@ dsp_status dsp_ssb(const void *G_c64_dev, int n_bf, const double *bf_coords_host
     if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
     return ssb_impl(G_c64_dev, nullptr, nullptr, 0, n_bf, bf_coords_host, weights_host, scan, sets_host, B, band_invA,
                     S_out_c128_dev, norm_out_dev, agreement_out_host, hip_stream);
+}
+
+dsp_status dsp_ssb_noalloc(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
+                           const dsp_scan *scan, const dsp_optics *sets_host, int B, const double *band_invA,
+                           void *S_out_c128_dev, double *norm_out_dev, double *agreement_out_host, void *hip_stream) {
+    if (!G_c64_dev) return fail(DSP_EINVAL, "G is NULL");
+    return ssb_impl(G_c64_dev, nullptr, nullptr, 0, n_bf, bf_coords_host, weights_host, scan, sets_host, B, band_invA,
+                    S_out_c128_dev, norm_out_dev, agreement_out_host, hip_stream, true);
 }
 
 dsp_status dsp_ssb_herm16(const void *Q_i16_dev, const float *scale_dev, int row_scales, int n_bf,
@@ -2143,8 +2264,9 @@ dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_
     double2 *d_dc = cv.take<double2>(1);
     // S on the fine half plane (zero where no lane runs: K = 0 and beyond reach)
     HIP_TRY(launch_fill_zero((double *)d_S, (size_t)n_half * 2, stream));
-    if (n_tiles > 0 &&
-        (st = ssb_pass(L, optics, 1, G_c64_dev, nullptr, nullptr, 0, N, M, d_S, nullptr, bufs, device, stream)))
+    SsbDevTables dt;
+    if ((st = layout_tables(L, mi, device, dt))) return st;
+    if (n_tiles > 0 && (st = ssb_pass(L, dt, optics, 1, G_c64_dev, nullptr, nullptr, 0, N, M, d_S, nullptr, bufs, stream)))
         return st;
     HIP_TRY(launch_preview_dc(L.d_pixbase, L.d_goff, n_pix, (const float2 *)G_c64_dev, d_dc, stream));
     if (spec_out_c128_dev) HIP_TRY(launch_preview_spectrum(d_S, d_dc, n_half, (double2 *)spec_out_c128_dev, stream));

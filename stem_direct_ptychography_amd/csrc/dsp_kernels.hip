@@ -27,6 +27,7 @@
 
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace dsp {
@@ -2029,6 +2030,37 @@ hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *ti
 }
 
 int ssb_partial_stride(int B) { return ssb_maxb(B) + 1; }
+
+// ---------------------------------------------------------------------------
+// fixed scratch of the allocation-free SSB pass
+// ---------------------------------------------------------------------------
+// One array per device, part of the library's code object: each GPU the
+// library runs on holds its own copy at its own address until the process
+// ends.  In host code the name `scratch` is only a host-side stand-in, never
+// a device address: host code uses the pointer hipGetSymbolAddress returns
+// for the current device (kept per device below), in kernel arguments and
+// copies alike.
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(char **out) {
+    static std::mutex mu;
+    static char *ptrs[64] = {nullptr};
+    *out = nullptr;
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return e;
+    if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[device]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // the current device's copy
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptrs[device] = (char *)p;
+    }
+    *out = ptrs[device];
+    return hipSuccess;
+}
 
 hipError_t launch_agreement(const double *partial, int n_tiles, int B, double *E, hipStream_t st) {
     agreement_kernel<<<1, 64, 0, st>>>(partial, n_tiles, ssb_partial_stride(B), B, E);

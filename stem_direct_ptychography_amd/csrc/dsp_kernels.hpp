@@ -76,6 +76,12 @@ hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *ti
 int ssb_partial_stride(int B);
 hipError_t launch_agreement(const double *partial, int n_tiles, int B, double *E, hipStream_t st);
 
+// Fixed per-device scratch of the allocation-free SSB pass (dsp_ssb_noalloc):
+// *out receives the current device's copy (hipGetSymbolAddress, once per
+// device; no allocation).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+hipError_t noalloc_scratch(char **out);
+
 constexpr int MAX_NJ_PHASE = 8;
 constexpr int MAX_NJ_COMPLEX = 6;
 constexpr int MAX_A_SOLVE_COMPLEX = 6;
