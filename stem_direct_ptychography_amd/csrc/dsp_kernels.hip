@@ -53,6 +53,50 @@ __device__ __forceinline__ double aperture_at(const ApertureDev &ap, double d2) 
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
+// Sine and cosine of a phase x (rad) for the SSB passes, whose contract is
+// 1e-5 relative: the table method of sincos_tab with a one-step reduction
+// and shorter polynomials.  n = rint(128 x / pi), r = x - n pi/128 in one FMA
+// (|r| <= pi/256; the constant's rounding, 1e-18 per step of pi/128, stays
+// below 1e-14 rad for |x| < 1e3), sin r = r - r^3/6 (truncation below
+// 2.4e-12) and cos r = 1 - r^2/2 + r^4/24 (below 5e-15), then the angle
+// addition with T[n mod 256].  The Gram kernels, held to 1e-9, keep
+// sincos_tab.  (The hardware's FP32 sine of the phase in revolutions is
+// cheaper, but its 1e-7 rad errors, amplified where a frequency's pixel sum
+// cancels, exceed the per-frequency bound.)
+__device__ __forceinline__ void sincos_ssb(double x, const double2 *__restrict__ T, double &s, double &c) {
+    const double n = rint(x * 40.74366543152521);          // 128 / pi
+    const double r = fma(-n, 0.02454369260617026, x);      // pi / 128
+    const double z = r * r;
+    const double sr = fma(r * z, -1.6666666666666666667e-01, r);
+    const double cr = fma(z, fma(z, 4.1666666666666666667e-02, -0.5), 1.0);
+    const double2 t = T[((int)n) & (TRIG_N - 1)];
+    s = fma(t.y, cr, t.x * sr);
+    c = fma(t.x, cr, -(t.y * sr));
+}
+
+// sinc(h) = sin(h) / h of a lobe's depth term in the SSB passes: the sine of
+// sincos_ssb and the hardware reciprocal refined by two Newton steps (in
+// place of a correctly rounded division); the series below |h| = 1e-4.
+__device__ __forceinline__ double sinc_ssb(double h, const double2 *__restrict__ T) {
+    double sn, cs;
+    sincos_ssb(h, T, sn, cs);
+    double r = __builtin_amdgcn_rcp(h);
+    r = fma(r, fma(-h, r, 1.0), r);
+    r = fma(r, fma(-h, r, 1.0), r);
+    const double h2 = h * h;
+    const double series = fma(h2, fma(h2, 1.0 / 120.0, -1.0 / 6.0), 1.0);
+    return fabs(h) < 1e-4 ? series : sn * r;
+}
+
+// sqrt(d2) for the aperture's soft edge in the SSB passes: the FP32
+// reciprocal square root (measured relative error 1e-7) refined by one
+// Newton step in FP64, relative error about 1e-14.
+__device__ __forceinline__ double sqrt_fast(double d2) {
+    const double r = (double)__builtin_amdgcn_rsqf((float)d2);
+    const double s0 = d2 * r;
+    return fma(0.5 * r, fma(-s0, s0, d2), s0);
+}
+
 // ---------------------------------------------------------------------------
 // pixel terms: a(k) and chi(k) once per pixel and optics set
 // ---------------------------------------------------------------------------
@@ -1139,10 +1183,8 @@ struct SsbWaves {
 // H16: G comes as herm16 snorm16 pairs, unpacked as max(q / 32767, -1) s in
 // FP64 at use; H16 = 1: one scale per pixel (staged with the pixel record);
 // H16 = 2: one scale per stored row, fetched with G for the lane's row.
-// The eight-set Taylor pass is held to three waves per SIMD: a few spilled
-// registers cost less than the third wave gains (13.9 -> 13.2 ms).
 template <int MAXB, bool DEPTH, int H16, bool TAYS>
-__global__ __launch_bounds__(64, ((TAYS && MAXB == 8) ? 3 : SsbWaves<MAXB>::value)) void ssb_kernel(SsbParams prm) {
+__global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParams prm) {
     constexpr int NACC = 3 * MAXB + 1;
     constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
     using GT = typename std::conditional<H16 != 0, short2, float2>::type;
@@ -1283,9 +1325,73 @@ __global__ __launch_bounds__(64, ((TAYS && MAXB == 8) ? 3 : SsbWaves<MAXB>::valu
                         gre = (double)ga[k].x;
                         gim = (double)ga[k].y;
                     }
-                    if (cj) gim = -gim;
-                    if (r >= cn) gre = gim = 0.0;
+                    if (!TAYS && cj) gim = -gim;   // band passes (TAYS) read stored entries only
+                    // (the chunk's tail, r >= cn, runs on zero records: sw = amp0 = 0
+                    // zero its terms)
                     const double *chi0s = schi + r;
+                    if (TAYS) {
+                        // Band pass, straight-line: nearly every pixel has both lobes in
+                        // reach of some lane of the tile, so both are always evaluated
+                        // for every set and a lane's lobe outside the support gets
+                        // amplitude 0 by select (no per-lane branches, whose joins cost
+                        // register copies, and no exec-mask bookkeeping).
+                        const double lrlim2 = prm.ap.lrlim2, lrin2 = prm.ap.lrin2, lkc = prm.ap.lkc;
+                        const double inv_ldk = prm.ap.inv_ldk;
+                        const int B = prm.B;
+                        const double lk2 = fma(lky, lky, lkx * lkx);
+                        const double gr = gre * sw, gi = gim * sw;
+                        acc[NACC - 1] = fma(gr, gr, fma(gi, gi, acc[NACC - 1]));
+                        const double kq = fma(lky, qy, lkx * qx);
+                        const double base = lk2 + q2;
+                        const double dm2 = fma(-2.0, kq, base), dp2 = fma(2.0, kq, base);
+                        const bool zl = valid && dm2 < lrlim2;
+                        const bool zr = valid && dp2 < lrlim2;
+                        double aml = zl ? amp0 : 0.0, amr = zr ? amp0 : 0.0;
+                        const bool rl = zl && dm2 > lrin2, rr = zr && dp2 > lrin2;
+                        if (wave_any(rl || rr)) {
+                            const double fl = fma(lkc - sqrt_fast(dm2), inv_ldk, 0.5);
+                            const double fr = fma(lkc - sqrt_fast(dp2), inv_ldk, 0.5);
+                            aml = rl ? aml * fl : aml;
+                            amr = rr ? amr * fr : amr;
+                        }
+#pragma unroll
+                        for (int b = 0; b < MAXB; ++b) {
+                            if (b >= B) continue;   // uniform; keeps the loop fully unrolled
+                            int zb = 0;
+                            if (MAXB > 1) asm volatile("" : "+s"(zb));   // see the per-set loop below
+                            const double *cb = &prm.chi_c[b][zb];
+                            // the even part's 8 coefficients, then the odd part's 12: the
+                            // empty asm keeps the second group's LDS reads after the first
+                            // evaluation, so fewer coefficients are live at once
+                            const double *ts = stay + (b * CHK + r) * TAY_N;
+                            double te[8], to[12];
+#pragma unroll
+                            for (int m = 0; m < 8; ++m) te[m] = ts[m];
+                            const double E = chi_even(te, cb, qX, qY, qZ);
+                            asm volatile("" ::: "memory");
+#pragma unroll
+                            for (int m = 0; m < 12; ++m) to[m] = ts[8 + m];
+                            const double O = chi_odd(to, qx, qy, qX, qY);
+                            double hl = 0.0, hr = 0.0, al = aml, ar = amr;
+                            if (DEPTH) {
+                                const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
+                                const double td2 = 2.0 * fma(py, qy, px * qx);
+                                hl = prm.pt2[b] * (td2 - q2);
+                                hr = prm.pt2[b] * (td2 + q2);
+                                al *= sinc_ssb(hl, T);
+                                ar *= sinc_ssb(hr, T);
+                            }
+                            double sl, cl, sr, cr;
+                            sincos_ssb((O - E) + hl, T, sl, cl);
+                            sincos_ssb((O + E) + hr, T, sr, cr);
+                            // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
+                            const double gmr = fma(ar, sr, -(al * sl)), gmi = fma(al, cl, -(ar * cr));
+                            acc[3 * b] = fma(gmr, gr, fma(gmi, gi, acc[3 * b]));
+                            acc[3 * b + 1] = fma(gmr, gi, fma(-gmi, gr, acc[3 * b + 1]));
+                            acc[3 * b + 2] = fma(gmr, gmr, fma(gmi, gmi, acc[3 * b + 2]));
+                        }
+                        continue;
+                    }
                     // (one set only: with more, the branch costs registers, spills or
                     // a wave per SIMD)
                     if (MAXB == 1 && __builtin_amdgcn_readfirstlane(smask[r]) == 0u) {
@@ -1310,8 +1416,8 @@ __global__ __launch_bounds__(64, ((TAYS && MAXB == 8) ? 3 : SsbWaves<MAXB>::valu
                     const bool rl = zl && dm2 > lrin2, rr = zr && dp2 > lrin2;
                     if (wave_any(rl || rr)) {
                         asm volatile("");
-                        if (rl) aml *= fma(lkc - sqrt(dm2), inv_ldk, 0.5);
-                        if (rr) amr *= fma(lkc - sqrt(dp2), inv_ldk, 0.5);
+                        if (rl) aml *= fma(lkc - sqrt_fast(dm2), inv_ldk, 0.5);
+                        if (rr) amr *= fma(lkc - sqrt_fast(dp2), inv_ldk, 0.5);
                     }
                 #pragma unroll
                     for (int b = 0; b < MAXB; ++b) {
@@ -1328,39 +1434,7 @@ __global__ __launch_bounds__(64, ((TAYS && MAXB == 8) ? 3 : SsbWaves<MAXB>::valu
                         const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
                         const double th0 = DEPTH ? fma(px, px, py * py) : 0.0;
                         double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
-                        if (TAYS) {
-                            if (zl || zr) {
-                                // chi(theta -/+ d) - chi(theta) = E -/+ O with d = lambda q:
-                                // L = O - E (+ hl), R = O + E (+ hr); X, Y, Z are the lane's
-                                double tc[TAY_N];
-#pragma unroll
-                                for (int m = 0; m < TAY_N; ++m) tc[m] = stay[(b * CHK + r) * TAY_N + m];
-                                const double E = chi_even(tc, cb, qX, qY, qZ);
-                                const double O = chi_odd(tc + 8, qx, qy, qX, qY);
-                                double hl = 0.0, hr = 0.0;
-                                if (DEPTH) {
-                                    const double td2 = 2.0 * fma(py, qy, px * qx);
-                                    hl = prm.pt2[b] * (td2 - q2);
-                                    hr = prm.pt2[b] * (td2 + q2);
-                                }
-                                if (zl) {
-                                    double a = aml;
-                                    if (DEPTH) a *= sinc_tab(hl, T);
-                                    double sn, cs;
-                                    sincos_tab((O - E) + hl, T, sn, cs);
-                                    Lr = a * cs;
-                                    Li = a * sn;
-                                }
-                                if (zr) {
-                                    double a = amr;
-                                    if (DEPTH) a *= sinc_tab(hr, T);
-                                    double sn, cs;
-                                    sincos_tab((O + E) + hr, T, sn, cs);
-                                    Rr = a * cs;
-                                    Ri = a * sn;
-                                }
-                            }
-                        } else {
+                        {
                         if (zl) {
                             const double ty = py - qy, tx = px - qx;
                             const double c1 = chi_poly(cb, tx, ty);
@@ -1368,10 +1442,10 @@ __global__ __launch_bounds__(64, ((TAYS && MAXB == 8) ? 3 : SsbWaves<MAXB>::valu
                             if (DEPTH) {   // depth term: phase + h, amplitude sinc(h)
                                 const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
                                 arg += h;
-                                a *= sinc_tab(h, T);
+                                a *= sinc_ssb(h, T);
                             }
                             double sn, cs;
-                            sincos_tab(arg, T, sn, cs);
+                            sincos_ssb(arg, T, sn, cs);
                             Lr = a * cs;
                             Li = a * sn;
                         }
@@ -1382,10 +1456,10 @@ __global__ __launch_bounds__(64, ((TAYS && MAXB == 8) ? 3 : SsbWaves<MAXB>::valu
                             if (DEPTH) {
                                 const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
                                 arg += h;
-                                a *= sinc_tab(h, T);
+                                a *= sinc_ssb(h, T);
                             }
                             double sn, cs;
-                            sincos_tab(-arg, T, sn, cs);
+                            sincos_ssb(-arg, T, sn, cs);
                             Rr = a * cs;
                             Ri = a * sn;
                         }
