@@ -986,15 +986,48 @@ __global__ __launch_bounds__(64) void solve_empty_kernel(SolveParams prm, int n_
 }
 
 // complex method: Cholesky of M + scale diag(lambda_A p, lambda_phi p), d = 2A
+// Cholesky factor of one complex system (lower triangle, row i, col j <= i):
+// in registers, or, for the 12 x 12 systems of six aliases (78 complex
+// entries, more than the registers hold without spilling), in LDS, one
+// column of entries per thread of a SOLVE_LDS_THREADS-thread block.
+constexpr int SOLVE_LDS_THREADS = 32;
+template <int A>
+struct SolveInLds {
+    static constexpr bool value = 2 * A >= 12;
+};
+
+template <int d, bool LDS>
+struct CholFactor;
+template <int d>
+struct CholFactor<d, false> {
+    double r[d][d], i[d][d];
+    __device__ __forceinline__ void set(int a, int b, double x, double y) {
+        r[a][b] = x;
+        i[a][b] = y;
+    }
+    __device__ __forceinline__ double re(int a, int b) const { return r[a][b]; }
+    __device__ __forceinline__ double im(int a, int b) const { return i[a][b]; }
+};
+template <int d>
+struct CholFactor<d, true> {
+    double2 *col;   // this thread's entries: col[e * SOLVE_LDS_THREADS]
+    __device__ __forceinline__ static int e(int a, int b) { return (a * (a + 1) / 2 + b) * SOLVE_LDS_THREADS; }
+    __device__ __forceinline__ void set(int a, int b, double x, double y) { col[e(a, b)] = make_double2(x, y); }
+    __device__ __forceinline__ double re(int a, int b) const { return col[e(a, b)].x; }
+    __device__ __forceinline__ double im(int a, int b) const { return col[e(a, b)].y; }
+};
+
 template <int A>
 __global__ __launch_bounds__(64) void solve_complex_kernel(SolveParams prm) {
     constexpr int d = 2 * A;
+    constexpr bool LDSF = SolveInLds<A>::value;
+    __shared__ double2 lsh[LDSF ? d * (d + 1) / 2 * SOLVE_LDS_THREADS : 1];
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= prm.n) return;
     const int q = prm.qlist[t];
     const int am = prm.a_max;
     const int D = prm.D;
-    const double2 *S = prm.sys + (size_t)q * (size_t)tri_size(D);
+    const double2 *S0 = prm.sys + (size_t)q * (size_t)tri_size(D);
     int slot[d];
 #pragma unroll
     for (int i = 0; i < A; ++i) {
@@ -1010,65 +1043,95 @@ __global__ __launch_bounds__(64) void solve_complex_kernel(SolveParams prm) {
     double rr[d], ri[d];
 #pragma unroll
     for (int i = 0; i < d; ++i) {
-        const double2 e = S[tri_idx(slot[i], D - 1, D)];
+        const double2 e = S0[tri_idx(slot[i], D - 1, D)];
         rr[i] = e.x;
         ri[i] = e.y;
     }
-    const double P = S[tri_idx(D - 1, D - 1, D)].x;
+    const double P = S0[tri_idx(D - 1, D - 1, D)].x;
     for (int s = 0; s < prm.S; ++s) {
         const double la = prm.strengths[2 * s] * prm.scale, lp = prm.strengths[2 * s + 1] * prm.scale;
+        // With the factor in LDS, the system is re-read for each strength: an
+        // opaque zero offset keeps the compiler from hoisting its 78 entries
+        // out of the strength loop into registers (which would spill).
+        const double2 *S = S0;
+        if constexpr (LDSF) {
+            long long zo = 0;
+            asm volatile("" : "+v"(zo));
+            S = S0 + zo;
+        }
         // lower triangle L (row i, col j <= i) of the Cholesky factor
-        double lr[d][d], li[d][d];
+        CholFactor<d, LDSF> L;
+        if constexpr (LDSF) {
+            // the regularized system H (lower triangle, H_ij = conj(M[slot j][slot
+            // i])) copied into the factor's storage by a rolled loop, one entry
+            // at a time, then factored in place
+            L.col = lsh + threadIdx.x;
+#pragma unroll 1
+            for (int i = 0; i < d; ++i) {
+                const int si = i < A ? i : am + i - A;
+#pragma unroll 1
+                for (int j = 0; j <= i; ++j) {
+                    const int sj = j < A ? j : am + j - A;
+                    const double2 e = S[tri_idx(sj, si, D)];
+                    const double dg = i == j ? (j < A ? la : lp) * prm.prior[(size_t)q * am + (j < A ? j : j - A)] : 0.0;
+                    L.col[(i * (i + 1) / 2 + j) * SOLVE_LDS_THREADS] = make_double2(e.x + dg, i == j ? 0.0 : -e.y);
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < d; ++j) {
             // H_jj - sum_k |L_jk|^2
-            double hjj = S[tri_idx(slot[j], slot[j], D)].x + (j < A ? la : lp) * pr[j];
+            double hjj = LDSF ? L.re(j, j) : S[tri_idx(slot[j], slot[j], D)].x + (j < A ? la : lp) * pr[j];
 #pragma unroll
-            for (int k = 0; k < j; ++k) hjj -= lr[j][k] * lr[j][k] + li[j][k] * li[j][k];
+            for (int k = 0; k < j; ++k) hjj -= L.re(j, k) * L.re(j, k) + L.im(j, k) * L.im(j, k);
             const double ljj = sqrt(hjj);
             const double inv = 1.0 / ljj;
-            lr[j][j] = ljj;
-            li[j][j] = 0.0;
+            L.set(j, j, ljj, 0.0);
 #pragma unroll
             for (int i = j + 1; i < d; ++i) {
                 // H_ij (i > j) = conj(M[slot j][slot i])
-                const double2 e = S[tri_idx(slot[j], slot[i], D)];
-                double zr = e.x, zi = -e.y;
+                double zr, zi;
+                if constexpr (LDSF) {
+                    zr = L.re(i, j);
+                    zi = L.im(i, j);
+                } else {
+                    const double2 e = S[tri_idx(slot[j], slot[i], D)];
+                    zr = e.x;
+                    zi = -e.y;
+                }
 #pragma unroll
                 for (int k = 0; k < j; ++k) {
                     // L_ik conj(L_jk)
-                    zr -= lr[i][k] * lr[j][k] + li[i][k] * li[j][k];
-                    zi -= li[i][k] * lr[j][k] - lr[i][k] * li[j][k];
+                    zr -= L.re(i, k) * L.re(j, k) + L.im(i, k) * L.im(j, k);
+                    zi -= L.im(i, k) * L.re(j, k) - L.re(i, k) * L.im(j, k);
                 }
-                lr[i][j] = zr * inv;
-                li[i][j] = zi * inv;
+                L.set(i, j, zr * inv, zi * inv);
             }
         }
-        // forward L z = r, backward L^H x = z
-        double zr[d], zi[d];
+        // forward L z = r, backward L^H x = z, x overwriting z in place
+        double xr[d], xi[d];
 #pragma unroll
         for (int i = 0; i < d; ++i) {
             double ar = rr[i], ai = ri[i];
 #pragma unroll
             for (int k = 0; k < i; ++k) {
-                ar -= lr[i][k] * zr[k] - li[i][k] * zi[k];
-                ai -= lr[i][k] * zi[k] + li[i][k] * zr[k];
+                ar -= L.re(i, k) * xr[k] - L.im(i, k) * xi[k];
+                ai -= L.re(i, k) * xi[k] + L.im(i, k) * xr[k];
             }
-            zr[i] = ar / lr[i][i];
-            zi[i] = ai / lr[i][i];
+            xr[i] = ar / L.re(i, i);
+            xi[i] = ai / L.re(i, i);
         }
-        double xr[d], xi[d];
 #pragma unroll
         for (int i = d - 1; i >= 0; --i) {
-            double ar = zr[i], ai = zi[i];
+            double ar = xr[i], ai = xi[i];
 #pragma unroll
             for (int k = i + 1; k < d; ++k) {
                 // conj(L_ki) x_k
-                ar -= lr[k][i] * xr[k] + li[k][i] * xi[k];
-                ai -= lr[k][i] * xi[k] - li[k][i] * xr[k];
+                ar -= L.re(k, i) * xr[k] + L.im(k, i) * xi[k];
+                ai -= L.re(k, i) * xi[k] - L.im(k, i) * xr[k];
             }
-            xr[i] = ar / lr[i][i];
-            xi[i] = ai / lr[i][i];
+            xr[i] = ar / L.re(i, i);
+            xi[i] = ai / L.re(i, i);
         }
         double2 *xo = prm.x + ((size_t)(2 * s) * prm.n_q + q) * am;
         double2 *xo2 = prm.x + ((size_t)(2 * s + 1) * prm.n_q + q) * am;
@@ -1937,7 +2000,11 @@ hipError_t launch_solve(const SolveParams &prm, int A, int method, hipStream_t s
             case 3: solve_complex_kernel<3><<<blocks, 64, 0, st>>>(prm); break;
             case 4: solve_complex_kernel<4><<<blocks, 64, 0, st>>>(prm); break;
             case 5: solve_complex_kernel<5><<<blocks, 64, 0, st>>>(prm); break;
-            case 6: solve_complex_kernel<6><<<blocks, 64, 0, st>>>(prm); break;
+            case 6:   // factor in LDS: SOLVE_LDS_THREADS threads per block
+                static_assert(SolveInLds<6>::value, "the six-alias factor lives in LDS");
+                solve_complex_kernel<6><<<(prm.n + SOLVE_LDS_THREADS - 1) / SOLVE_LDS_THREADS, SOLVE_LDS_THREADS,
+                                          0, st>>>(prm);
+                break;
             default: return hipErrorInvalidValue;
         }
     }
