@@ -265,7 +265,7 @@ __device__ __forceinline__ void write_system(const double *acc, unsigned mask, i
 // to two, went 8.43 -> 9.23 ms).
 template <int NJ, int METHOD>
 struct GramTaylor {
-    static constexpr bool value = (METHOD == 0 && NJ == 5) || (METHOD == 1 && NJ >= 5);
+    static constexpr bool value = (METHOD == 1 && NJ >= 5);
 };
 
 // Pixels whose records (and, with the Taylor scheme, chi's coefficients
