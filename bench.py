@@ -31,6 +31,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -46,14 +48,15 @@ FP64_VECTOR_PEAK_TFLOPS = 78.6   # 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x 2
 #   support test (pixel, alias, lobe): k -/+ Q (2), squared length (3)      = 5
 #   non-zero lobe: theta = lambda k' + tau (2 FMA = 4), chi(theta) as a
 #     degree-6 bivariate polynomial of 28 coefficients by Horner (27 FMA = 54),
-#     phase difference (1), sincos counted as one Cody-Waite reduction and two
-#     minimax polynomials to double precision (18 FMA = 36), aperture product
-#     (1), amplitude times cos and sin (2)                                   = 98
+#     phase difference (1), sine and cosine by the table method (reduction 1
+#     FMA = 2, r^2 1, sine r - r^3/6 3, cosine to r^4 2 FMA = 4, angle
+#     addition 2 MUL + 2 FMA = 6: 16), aperture product (1), amplitude times
+#     cos and sin (2)                                                        = 78
 #   non-zero column per pixel: weight times column (2), diagonal |t|^2 w
 #     (2 FMA = 4), right side conj(t) w g (4 FMA = 8)                        = 14
 #   non-zero column pair c < d per pixel: conj(t_c) w t_d (4 FMA)           = 8
 #   (pixel, frequency) term: w g (2), power w |g|^2 (2 FMA = 4)              = 6
-FLOP_TEST, FLOP_LOBE, FLOP_COL, FLOP_PAIR, FLOP_TERM = 5.0, 98.0, 14.0, 8.0, 6.0
+FLOP_TEST, FLOP_LOBE, FLOP_COL, FLOP_PAIR, FLOP_TERM = 5.0, 78.0, 14.0, 8.0, 6.0
 
 KERNEL_SOURCES = ("stem_direct_ptychography_amd/csrc/dsp_kernels.hip",
                   "stem_direct_ptychography_amd/csrc/dsp_internal.hpp")
@@ -140,75 +143,171 @@ class Step:
 
 
 # ----------------------------------------------------------------------------
-# CPU baseline: the oracle as it stands on a bounded sample
+# CPU baseline: the oracle as it stands, on every host core
 # ----------------------------------------------------------------------------
+#
+# A pool of spawned worker processes (the bench process holds a GPU context,
+# so no fork), one BLAS thread each, runs the oracle's prepare + solve or SSB
+# sum over chunks of frequencies whose G columns the parent has gathered.
+# Wall clock of each pool run, data generation and gathering excluded.
 
 
-def cpu_baseline(w, k, G, n_q: int, n_band: int, budget_s: float, strength: float):
-    import numpy as np
+def _oracle_prepare_chunk(args):
+    """Worker: the oracle's prepare + solve of one chunk (compute seconds)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dsp_oracle as O
+    from synthetic import workload
+
+    name, method, q, cols, ka, wa, strengths = args
+    w = workload(name)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        pr = O.prepare(q, [cols[:, i].astype(np.complex128) for i in range(cols.shape[1])], ka, wa, w.n_scan,
+                       w.step, w.upsampling, w.optics, method, w.smoothness)
+        for st in strengths:
+            O.solve(pr, st)
+        return time.perf_counter() - t0
+
+
+def _oracle_ssb_chunk(args):
+    """Worker: the oracle's SSB sums of one chunk of band entries."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dsp_oracle as O
+    from synthetic import ssb_sets, workload
+
+    name, B, ent, cols, ka, wa = args
+    w = workload(name)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.ssb(ent, [cols[:, i].astype(np.complex128) for i in range(cols.shape[1])], ka, wa, w.n_scan, w.step,
+              ssb_sets(w, B))
+        return time.perf_counter() - t0
+
+
+def _gather(G, act_t, idx, dev):
+    """complex64 (n_act, n) columns of G at stored indices idx (n, 2)."""
+    import torch
+
+    g = G[:, torch.as_tensor(idx[:, 0], device=dev), torch.as_tensor(idx[:, 1], device=dev)]
+    return g[act_t].cpu().numpy()
+
+
+def cpu_baseline(dsp, dev, w4, k4, G4, n_q: int, n_band: int, strength: float, workers: int):
+    """The oracle on all host cores: C1-C3 in full, a seeded 4096-frequency
+    subset of the full frame stratified by alias count (extrapolated per
+    stratum), and the SSB sum on the band at 1 and 8 sets (sampled,
+    extrapolated).  value = the full frame's step rate in scan frequencies/s
+    (phase prepare + solve, complex prepare + solve, one-set SSB pass)."""
+    import multiprocessing as mp
+
     import torch
 
     from oracle import dsp_oracle as O
+    from synthetic import bf_pixels, data_stack_numpy, data_stack_torch, workload
 
-    from threadpoolctl import threadpool_limits
-
-    with threadpool_limits(limits=1):
-        act = O.active_pixels(k, w.optics)
-        ka = k[act]
-        wa = np.ones(len(act))
-        uq = O.unique_frequencies(w.n_scan)
-        bm = O.band_mask(w.n_scan, w.step, (0.2, 0.9))
-        ent = np.argwhere(bm)
-        rng = np.random.default_rng(12345)
-        qsel = uq[np.sort(rng.choice(len(uq), size=256, replace=False))]
-        esel = ent[np.sort(rng.choice(len(ent), size=256, replace=False))]
-        dev = G.device
-        act_t = torch.as_tensor(act, device=dev)
-
-        def cols(idx):
-            g = G[:, torch.as_tensor(idx[:, 0], device=dev), torch.as_tensor(idx[:, 1], device=dev)]
-            g = g[act_t].cpu().numpy().astype(np.complex128)
-            return [g[:, i] for i in range(len(idx))]
-
-        qcols, ecols = cols(qsel), cols(esel)
-        t_phase = t_cplx = t_ssb = 0.0
-        nq_done = ne_done = 0
-        t_all = time.perf_counter()
-        i = 0
-        while i < len(qsel) and time.perf_counter() - t_all < budget_s:
-            sl = slice(i, i + 8)
+    ctx = mp.get_context("spawn")
+    out = {"kind": "oracle", "unit": UNIT, "cores": workers, "cpu_model": _cpu_model(),
+           "affinity_cores": len(os.sched_getaffinity(0)), "configs": {}}
+    pool = ctx.Pool(workers)
+    try:
+        pool.map(abs, range(4 * workers))   # the workers have started before any timing
+        def run_prepare(name, G, k, method, strengths, q_idx, chunk):
+            w = workload(name)
+            act = O.active_pixels(k, w.optics)
+            ka, wa = k[act], np.ones(len(act))
+            act_t = torch.as_tensor(act, device=dev)
+            Ga = None if isinstance(G, torch.Tensor) else G[act]
+            jobs = []
+            for c0 in range(0, len(q_idx), chunk):
+                qc = q_idx[c0:c0 + chunk]
+                cols = _gather(G, act_t, qc, dev) if Ga is None else Ga[:, qc[:, 0], qc[:, 1]]
+                jobs.append((name, method, qc, cols, ka, wa, strengths))
             t0 = time.perf_counter()
-            pr = O.prepare(qsel[sl], qcols[sl], ka, wa, w.n_scan, w.step, w.upsampling, w.optics, "phase",
-                           w.smoothness)
-            O.solve(pr, strength)
-            t1 = time.perf_counter()
-            pr = O.prepare(qsel[sl], qcols[sl], ka, wa, w.n_scan, w.step, w.upsampling, w.optics, "complex",
-                           w.smoothness)
-            O.solve(pr, (strength, strength))
-            t2 = time.perf_counter()
-            O.ssb(esel[sl], ecols[sl], ka, wa, w.n_scan, w.step, [w.optics])
-            t3 = time.perf_counter()
-            t_phase += t1 - t0
-            t_cplx += t2 - t1
-            t_ssb += t3 - t2
-            nq_done += len(qsel[sl])
-            ne_done += len(esel[sl])
-            i += 8
-        per_q = (t_phase + t_cplx) / nq_done
-        per_e = t_ssb / ne_done
-        est_step = n_q * per_q + n_band * per_e
-        return {
-            "value": n_q / est_step,
-            "unit": UNIT,
-            "cores": 1,
-            "kind": "oracle",
-            "sample": (f"{nq_done} of {n_q} solved frequencies (seeded uniform) through phase prepare+solve and "
-                       f"complex prepare+solve, and {ne_done} of {n_band} band entries through the SSB sum, "
-                       f"{t_phase + t_cplx + t_ssb:.1f} s of CPU work on one thread; value = frequencies per "
-                       f"second of the whole step extrapolated from the per-item times"),
-            "phase_prepare_q_per_s": nq_done / t_phase,
-            "cpu_model": _cpu_model(),
-        }
+            busy = pool.map(_oracle_prepare_chunk, jobs, chunksize=1)
+            return time.perf_counter() - t0, busy, len(act)
+
+        # C1-C3 in full (the configurations' own methods and strength sweeps)
+        for name, strengths in (("c1", None), ("c2", None), ("c3", None)):
+            w = workload(name)
+            pix, k = bf_pixels(w)
+            if name == "c3":
+                G = data_stack_torch(w, pix, dev)
+                torch.cuda.synchronize()
+            else:
+                G = data_stack_numpy(w, pix)
+            q = O.unique_frequencies(w.n_scan)
+            sts = list(w.strengths)
+            wall, busy, n_act = run_prepare(name, G, k, w.method, sts, q, 64)
+            out["configs"][name] = {"method": w.method, "n_q": len(q), "strengths": len(sts), "wall_s": wall,
+                                    "q_per_s": len(q) / wall, "g_GBps": len(q) * n_act * 8 / wall / 1e9}
+            log(f"cpu baseline {name}: {len(q)} frequencies ({w.method}, {len(sts)} strengths) in {wall:.1f} s")
+            del G
+
+        # full frame: 4096 frequencies stratified by alias count, per method
+        _, counts, _ = O.alias_table(w4.n_scan, w4.step, w4.upsampling, w4.optics)
+        uq = O.unique_frequencies(w4.n_scan)
+        rng = np.random.default_rng(4096)
+        strata = {}
+        for A in np.unique(counts):
+            idx = np.nonzero(counts == A)[0]
+            take = max(32, int(round(4096 * len(idx) / len(uq))))
+            strata[int(A)] = (len(idx), np.sort(rng.choice(idx, size=min(take, len(idx)), replace=False)))
+        est = {}
+        sample_n = sum(len(v[1]) for v in strata.values())
+        for method in ("phase", "complex"):
+            st = strength if method == "phase" else (strength, strength)
+            cpu_full = 0.0
+            wall_tot = 0.0
+            for A, (n_all, idx) in strata.items():
+                wall, busy, n_act = run_prepare("c4", G4, k4, method, [st], uq[idx], 32)
+                cpu_full += sum(busy) * n_all / len(idx)
+                wall_tot += wall
+            est[method] = cpu_full / workers
+            out["configs"]["c4_" + method] = {
+                "sample": f"{sample_n} of {n_q} frequencies, stratified by alias count "
+                          + ", ".join(f"{A}: {len(v[1])}" for A, v in strata.items()),
+                "sample_wall_s": wall_tot, "extrapolated_s": est[method], "q_per_s": n_q / est[method],
+                "g_GBps": n_q * n_act * 8 / est[method] / 1e9}
+            log(f"cpu baseline c4 {method}: {sample_n} frequencies in {wall_tot:.1f} s, "
+                f"full frame extrapolated {est[method]:.1f} s")
+
+        # SSB on the band: 1 and 8 sets over a seeded sample of band entries
+        w5 = workload("c5")
+        pix5, k5 = bf_pixels(w5)
+        G5 = data_stack_torch(w5, pix5, dev)
+        torch.cuda.synchronize()
+        act5 = O.active_pixels(k5, w5.optics)
+        act5_t = torch.as_tensor(act5, device=dev)
+        ent = np.argwhere(O.band_mask(w5.n_scan, w5.step, w5.band))
+        for B, n_s in ((1, 2048), (8, 512)):
+            sel = ent[np.sort(np.random.default_rng(B).choice(len(ent), size=n_s, replace=False))]
+            jobs = [("c5", B, sel[c0:c0 + 32], _gather(G5, act5_t, sel[c0:c0 + 32], dev), k5[act5],
+                     np.ones(len(act5))) for c0 in range(0, n_s, 32)]
+            t0 = time.perf_counter()
+            busy = pool.map(_oracle_ssb_chunk, jobs, chunksize=1)
+            wall = time.perf_counter() - t0
+            full = sum(busy) * len(ent) / n_s / workers
+            est[f"ssb{B}"] = full
+            out["configs"][f"c5_ssb_{B}"] = {
+                "sample": f"{n_s} of {len(ent)} band entries (seeded uniform)", "sample_wall_s": wall,
+                "extrapolated_s": full, "q_sets_per_s": len(ent) * B / full,
+                "g_GBps": len(ent) * len(act5) * 8 / full / 1e9}
+            log(f"cpu baseline ssb B={B}: {n_s} entries in {wall:.1f} s, band pass extrapolated {full:.2f} s")
+        del G5
+        torch.cuda.empty_cache()
+    finally:
+        pool.close()
+        pool.join()
+    step_s = est["phase"] + est["complex"] + est["ssb1"]
+    out["value"] = n_q / step_s
+    out["sample"] = (f"oracle on {workers} worker processes: c1, c2, c3 prepare + solve in full; the full frame's "
+                     f"phase and complex prepare + solve on {sample_n} of {n_q} frequencies stratified by alias "
+                     f"count and the one-set SSB sum on 2048 of {n_band} band entries, each extrapolated to the "
+                     f"whole workload; value = full-frame step rate (phase + complex + SSB)")
+    out["phase_prepare_q_per_s"] = n_q / est["phase"]
+    return out
 
 
 def _cpu_model() -> str:
@@ -302,7 +401,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (default: every core of this process's affinity set)")
     ap.add_argument("--no-ssb-sweep", action="store_true")
     ap.add_argument("--copy-probe", type=float, default=0.0,
                     help="only run a plain device copy of this many GiB (counter calibration) and exit")
@@ -520,8 +620,9 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
-        log(f"timing the oracle on a bounded sample ({args.cpu_budget:.0f} s budget)")
-        result["cpu_baseline"] = cpu_baseline(w, k, G, n_q, n_band, args.cpu_budget, step.strength)
+        workers = args.cpu_workers or len(os.sched_getaffinity(0))
+        log(f"timing the oracle on {workers} host cores")
+        result["cpu_baseline"] = cpu_baseline(dsp, dev, w, k, G, n_q, n_band, step.strength, workers)
     else:
         result["cpu_baseline"] = None
     del G, step

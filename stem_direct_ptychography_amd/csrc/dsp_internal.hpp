@@ -152,29 +152,26 @@ struct alignas(16) PixelRec {
 // FP64 sine and cosine for the transfer's phase factors
 // ---------------------------------------------------------------------------
 // Table-driven: x = n pi/128 + r with n = rint(128 x / pi) and |r| <= pi/256,
-// by a Cody-Waite reduction (W. J. Cody and W. Waite, "Software Manual for
-// the Elementary Functions", 1980) with a two-part constant P1 + P2 = pi/128
-// (P1 = double(pi)/128, P2 the rest to 1e-34).  The first step x - n P1 is
-// exact in one FMA for |x| < 2^30: both terms are multiples of 2^-58 (or x
-// is below 2^-6 and n is 0 or +-1, with x a multiple of 2^-59) and the
-// difference is below 2^-6.  Then the Taylor series of sin r to r^5 and
-// cos r to r^6 (truncation below 1e-17 at |r| = pi/256) and the angle
-// addition with T[n mod 256] = (cos, sin)(n pi/128).  Absolute error about
-// 3e-16.  Branch-free; T is 256 double2 (4 KB).
+// by one Cody-Waite step (W. J. Cody and W. Waite, "Software Manual for the
+// Elementary Functions", 1980) with the constant P1 = double(pi)/128: x - n P1
+// is exact in one FMA for |x| < 2^30 (both terms are multiples of 2^-58, or x
+// is below 2^-6 and n is 0 or +-1, with x a multiple of 2^-59, and the
+// difference is below 2^-6); the constant's own error, 1e-18 per step of
+// pi/128, adds at most 4e-17 |x| rad (4e-14 at |x| = 1e3).  Then sin r = r - r^3/6
+// (truncation below r^5/120 = 2.4e-12 at |r| = pi/256) and cos r = 1 - r^2/2
+// + r^4/24 (below 5e-15), and the angle addition with T[n mod 256] = (cos,
+// sin)(n pi/128).  Absolute error about 2.4e-12: a lobe's value moves by that
+// fraction of its amplitude, a Gram entry by at most 5e-12 of the system's
+// largest and an SSB sum term likewise, within the 1e-9 and 1e-5 bounds.
+// Branch-free; T is 256 double2 (4 KB).
 constexpr int TRIG_N = 256;
 
 __host__ __device__ inline void sincos_tab(double x, const double2 *__restrict__ T, double &s, double &c) {
-    const double n = rint(x * 40.74366543152521);              // 128 / pi
-    double r = fma(-n, 0.02454369260617026, x);                // P1
-    r = fma(-n, 9.567553118338697e-19, r);                     // P2
+    const double n = rint(x * 40.74366543152521);          // 128 / pi
+    const double r = fma(-n, 0.02454369260617026, x);      // P1 = pi / 128
     const double z = r * r;
-    // sin r = r + r z (-1/3! + z (1/5!))
-    const double ps = fma(8.3333333333333333333e-03, z, -1.6666666666666666667e-01);
-    const double sr = fma(r * z, ps, r);
-    // cos r = 1 + z (-1/2! + z (1/4! + z (-1/6!)))
-    double pc = fma(-1.3888888888888888889e-03, z, 4.1666666666666666667e-02);
-    pc = fma(pc, z, -0.5);
-    const double cr = fma(z, pc, 1.0);
+    const double sr = fma(r * z, -1.6666666666666666667e-01, r);
+    const double cr = fma(z, fma(z, 4.1666666666666666667e-02, -0.5), 1.0);
     const double2 t = T[((int)n) & (TRIG_N - 1)];
     s = fma(t.y, cr, t.x * sr);
     c = fma(t.x, cr, -(t.y * sr));

@@ -53,33 +53,13 @@ __device__ __forceinline__ double aperture_at(const ApertureDev &ap, double d2) 
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0ull; }
 
-// Sine and cosine of a phase x (rad) for the SSB passes, whose contract is
-// 1e-5 relative: the table method of sincos_tab with a one-step reduction
-// and shorter polynomials.  n = rint(128 x / pi), r = x - n pi/128 in one FMA
-// (|r| <= pi/256; the constant's rounding, 1e-18 per step of pi/128, stays
-// below 1e-14 rad for |x| < 1e3), sin r = r - r^3/6 (truncation below
-// 2.4e-12) and cos r = 1 - r^2/2 + r^4/24 (below 5e-15), then the angle
-// addition with T[n mod 256].  The Gram kernels, held to 1e-9, keep
-// sincos_tab.  (The hardware's FP32 sine of the phase in revolutions is
-// cheaper, but its 1e-7 rad errors, amplified where a frequency's pixel sum
-// cancels, exceed the per-frequency bound.)
-__device__ __forceinline__ void sincos_ssb(double x, const double2 *__restrict__ T, double &s, double &c) {
-    const double n = rint(x * 40.74366543152521);          // 128 / pi
-    const double r = fma(-n, 0.02454369260617026, x);      // pi / 128
-    const double z = r * r;
-    const double sr = fma(r * z, -1.6666666666666666667e-01, r);
-    const double cr = fma(z, fma(z, 4.1666666666666666667e-02, -0.5), 1.0);
-    const double2 t = T[((int)n) & (TRIG_N - 1)];
-    s = fma(t.y, cr, t.x * sr);
-    c = fma(t.x, cr, -(t.y * sr));
-}
-
-// sinc(h) = sin(h) / h of a lobe's depth term in the SSB passes: the sine of
-// sincos_ssb and the hardware reciprocal refined by two Newton steps (in
-// place of a correctly rounded division); the series below |h| = 1e-4.
-__device__ __forceinline__ double sinc_ssb(double h, const double2 *__restrict__ T) {
+// sinc(h) = sin(h) / h of a lobe's depth term: the sine of sincos_tab and the
+// hardware reciprocal refined by two Newton steps (relative error about
+// 1e-16, in place of a correctly rounded division); the series below |h| =
+// 1e-4 (error below 1e-28).
+__device__ __forceinline__ double sinc_tab(double h, const double2 *__restrict__ T) {
     double sn, cs;
-    sincos_ssb(h, T, sn, cs);
+    sincos_tab(h, T, sn, cs);
     double r = __builtin_amdgcn_rcp(h);
     r = fma(r, fma(-h, r, 1.0), r);
     r = fma(r, fma(-h, r, 1.0), r);
@@ -88,7 +68,7 @@ __device__ __forceinline__ double sinc_ssb(double h, const double2 *__restrict__
     return fabs(h) < 1e-4 ? series : sn * r;
 }
 
-// sqrt(d2) for the aperture's soft edge in the SSB passes: the FP32
+// sqrt(d2) for the aperture's soft edge (Gram and SSB kernels): the FP32
 // reciprocal square root (measured relative error 1e-7) refined by one
 // Newton step in FP64, relative error about 1e-14.
 __device__ __forceinline__ double sqrt_fast(double d2) {
@@ -305,15 +285,8 @@ typedef const long long ConstLong;
 // below the plane chi refers to; "Where the 9 s of regularized preparation
 // goes", What changed 2: "chi, sinc and phase factor"): with
 // h = pi t (|theta_k|^2 - |theta'|^2) / (2 lambda) the lobe's phase argument
-// chi(k) - chi(k') gains h and its amplitude is multiplied by sinc(h).
-// sinc(h) = sin(h) / h, from its series below |h| = 1e-4 (error < 1e-28).
-__device__ __forceinline__ double sinc_tab(double h, const double2 *T) {
-    double sn, cs;
-    sincos_tab(h, T, sn, cs);
-    const double h2 = h * h;
-    const double series = fma(h2, fma(h2, 1.0 / 120.0, -1.0 / 6.0), 1.0);
-    return fabs(h) < 1e-4 ? series : sn / h;
-}
+// chi(k) - chi(k') gains h and its amplitude is multiplied by sinc(h)
+// (sinc_tab above).
 
 // One lobe of the transfer at the pixel (amp0 = sqrt(w) a(k)) and the
 // displaced point k' = k -/+ Q with d2 = |lambda k'|^2 (inside the support):
@@ -333,7 +306,7 @@ __device__ __forceinline__ void lobe(const GramParams &prm, const double2 *T, do
     const bool ring = d2 > prm.ap.lrin2;
     if (wave_any(ring)) {
         asm volatile("");
-        if (ring) amp *= fma(prm.ap.lkc - sqrt(d2), prm.ap.inv_ldk, 0.5);
+        if (ring) amp *= fma(prm.ap.lkc - sqrt_fast(d2), prm.ap.inv_ldk, 0.5);
     }
     re = amp * cs;
     im = amp * sn;
@@ -1441,12 +1414,12 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
                                 const double td2 = 2.0 * fma(py, qy, px * qx);
                                 hl = prm.pt2[b] * (td2 - q2);
                                 hr = prm.pt2[b] * (td2 + q2);
-                                al *= sinc_ssb(hl, T);
-                                ar *= sinc_ssb(hr, T);
+                                al *= sinc_tab(hl, T);
+                                ar *= sinc_tab(hr, T);
                             }
                             double sl, cl, sr, cr;
-                            sincos_ssb((O - E) + hl, T, sl, cl);
-                            sincos_ssb((O + E) + hr, T, sr, cr);
+                            sincos_tab((O - E) + hl, T, sl, cl);
+                            sincos_tab((O + E) + hr, T, sr, cr);
                             // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
                             const double gmr = fma(ar, sr, -(al * sl)), gmi = fma(al, cl, -(ar * cr));
                             acc[3 * b] = fma(gmr, gr, fma(gmi, gi, acc[3 * b]));
@@ -1505,10 +1478,10 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
                             if (DEPTH) {   // depth term: phase + h, amplitude sinc(h)
                                 const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
                                 arg += h;
-                                a *= sinc_ssb(h, T);
+                                a *= sinc_tab(h, T);
                             }
                             double sn, cs;
-                            sincos_ssb(arg, T, sn, cs);
+                            sincos_tab(arg, T, sn, cs);
                             Lr = a * cs;
                             Li = a * sn;
                         }
@@ -1519,10 +1492,10 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
                             if (DEPTH) {
                                 const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
                                 arg += h;
-                                a *= sinc_ssb(h, T);
+                                a *= sinc_tab(h, T);
                             }
                             double sn, cs;
-                            sincos_ssb(-arg, T, sn, cs);
+                            sincos_tab(-arg, T, sn, cs);
                             Rr = a * cs;
                             Ri = a * sn;
                         }

