@@ -1009,8 +1009,8 @@ dsp_status get_layout(const LayoutKey &key, const dsp_scan *scan, const dsp_opti
 // ---------------------------------------------------------------------------
 struct SsbKey {
     int device = 0, n_scan = 0, soft = 0, n_bf = 0, has_band = 0;
-    int up = 1;         // lanes on the u-times finer grid (previews)
-    int preview = 0;    // lanes: every fine K != 0 that some lobe can reach (else the stored band)
+    int up = 1;         // preview layouts: the upsampling u
+    int preview = 0;    // 1: a preview layout (the key of its own cache)
     int noalloc = 0;    // host tables only, plans sized to the fixed scratch (dsp_ssb_noalloc)
     double step = 0, lam = 0, alpha = 0, dk = 0, lo = 0, hi = 0;
     std::vector<double> coords, weights;
@@ -1062,8 +1062,7 @@ size_t noalloc_need(size_t n_pix, size_t n_tiles, int maxb, size_t W, size_t n_s
     return carve_size(TRIG_N, sizeof(double2)) + carve_size(n_pix, sizeof(PixelBase)) +
            carve_size(n_pix, sizeof(long long)) + carve_size(n_tiles, sizeof(SsbTile)) +
            carve_size(W + 1, sizeof(long long)) + carve_size(W, sizeof(int)) + carve_size(n_tiles + 1, sizeof(int)) +
-           carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) +
-           carve_size(n_segs * (size_t)ssb_nacc(maxb) * 64, sizeof(double)) +
+           carve_size(n_pix, sizeof(PixelRec)) + carve_size(n_segs * (size_t)ssb_nacc(maxb) * 64, sizeof(double)) +
            carve_size(n_tiles * (size_t)(maxb + 1), sizeof(double)) + carve_size(maxb + 1, sizeof(double)) +
            carve_size(std::max<size_t>(1, (size_t)maxb * n_pix * TAY_N), sizeof(double));
 }
@@ -1078,19 +1077,14 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
     const double dq = 1.0 / (N * key.step);
     if ((st = build_active(coords, weights, key.n_bf, optics, N, L->act))) return st;
     if (L->act.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
-    // lane groups over every stored entry inside the band; for a preview,
-    // over the fine half plane's K != 0 within reach of two overlapping
-    // apertures (|K| < 2 r_lim) and off the fine Nyquist row and column
-    // (index M/2 stands for +-M/2 dq, whose corrections differ); the rest of
-    // the plane is zero
-    const int M = key.up * N, mh = M / 2 + 1;
-    const double reach = 2.0 * std::sqrt(make_aperture_dev(optics).rlim2) * (1.0 + 1e-9);
+    // lane groups over every stored entry inside the band (all of them
+    // without one); the rest of the plane is zero
+    const int nh = N / 2 + 1;
     auto keep = [&](int yh, int ix) {
         const double f = std::hypot((double)yh * dq, (double)ix * dq);
-        if (key.preview) return !(yh == 0 && ix == 0) && yh != -M / 2 && ix != M / 2 && f < reach;
         return !key.has_band || (f >= key.lo && f <= key.hi);
     };
-    for (const Lanes &grp : pack_line_runs(M, mh, -M / 2, M / 2 - 1, mh, 16, keep)) {
+    for (const Lanes &grp : pack_line_runs(N, nh, -N / 2, (N - 1) / 2, nh, 16, keep)) {
         SsbTile t;
         std::memset(&t, 0, sizeof t);
         double sy = 0.0, sx = 0.0;
@@ -1208,6 +1202,247 @@ dsp_status get_ssb_layout(const SsbKey &key, const dsp_optics *optics, const dou
     if (st) return st;
     g_ssb_layouts.insert(g_ssb_layouts.begin(), out);
     if (g_ssb_layouts.size() > LAYOUT_CACHE_SIZE) g_ssb_layouts.pop_back();
+    return DSP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Preview layout, cached: the object fast path's corrected sum on the u-times
+// finer grid ("Tilt-corrected SSB on CUDA: fit and preview speed", Changes:
+// the 1x and 3x drag previews; "Where the 9 s of regularized preparation
+// goes", Object-redraw fast path).  Fine frequency K reads G at K mod N, so
+// every stored entry q feeds the fine K = q + j N: a lane holds one stored
+// entry and its alias slots are those K (the Gram kernels' slot scheme with
+// right sides only), so each G value is read once per pixel for all of its
+// fine images.  A slot is written either directly (K in the fine half plane,
+// Kx >= 0) or, where the half plane's K' = -K reads G through the Hermitian
+// mirror (K'x mod N > N/2), as the conjugate at K'.
+// ---------------------------------------------------------------------------
+struct PreviewLayout {
+    SsbKey key;
+    ActiveSet act;
+    TileGroups tg;
+    std::vector<int> sk_waves;
+    std::vector<size_t> wb_off, so_off, sf_off;
+    std::vector<long long> sk_wbegin;
+    std::vector<int> sk_int;
+    size_t max_partial = 0;   // doubles of the largest group's partial sums
+    PixelBase *d_pixbase = nullptr;
+    long long *d_goff = nullptr;
+    GramTile *d_tiles = nullptr;
+    long long *d_sk_wbegin = nullptr;
+    int *d_sk_int = nullptr;
+    double host_ms = 0.0;
+    ~PreviewLayout() {
+        hipSetDevice(key.device);
+        hipFree(d_pixbase);
+        hipFree(d_goff);
+        hipFree(d_tiles);
+        hipFree(d_sk_wbegin);
+        hipFree(d_sk_int);
+    }
+};
+
+// The slots of stored entry (yh, ix): the offsets j whose fine K = (yh + jy N,
+// ix + jx N) is within reach of two overlapping apertures (beyond it every
+// lobe is exactly zero) and either lies in the computed part of the fine half
+// plane itself (Kx >= 0; written at K) or has -K there with G read through
+// the mirror, (-Kx) mod N > N/2 (written, conjugated, at -K).  The computed
+// part: rows -(M/2)+1 .. (M-1)/2, columns 0 .. M/2-1, K != 0 (the Nyquist
+// row and column stay zero; K = 0 is the uncorrected DC term).  Every
+// computed fine K is the image of exactly one (entry, slot).
+JSet preview_slots(int yh, int ix, int N, int u, double dq, double reach) {
+    JSet js;
+    const int M = u * N;
+    auto computed = [M](int Ky, int Kx) {
+        return Ky > -(M / 2) && Ky <= (M - 1) / 2 && Kx >= 0 && Kx < M / 2 && !(Ky == 0 && Kx == 0);
+    };
+    for (int jy = -u; jy <= u; ++jy) {
+        const int Ky = yh + jy * N;
+        for (int jx = -u; jx <= u; ++jx) {
+            const int Kx = ix + jx * N;
+            if (Kx >= 0 ? !computed(Ky, Kx) : (!computed(-Ky, -Kx) || (-Kx) % N <= N / 2)) continue;
+            if (!(std::hypot((double)Ky * dq, (double)Kx * dq) < reach)) continue;
+            js.emplace_back(jy, jx);
+        }
+    }
+    return js;
+}
+
+void preview_finish_tile(GramTile &t, const JSet &js, const JSet (&lane_js)[64],
+                         std::map<int, std::vector<std::pair<long long, GramTile>>> &by_nj) {
+    t.nj = (int)js.size();
+    for (int s = 0; s < t.nj; ++s) {
+        t.jy[s] = (int8_t)js[s].first;
+        t.jx[s] = (int8_t)js[s].second;
+    }
+    double sy = 0.0, sx = 0.0;
+    int nv = 0;
+    long long cost = 0;
+    for (int l = 0; l < 64; ++l) {
+        t.mask[l] = 0;
+        if (t.qidx[l] < 0) continue;
+        unsigned msk = 0;
+        for (const auto &j : lane_js[l])
+            msk |= 1u << (int)(std::lower_bound(js.begin(), js.end(), j) - js.begin());
+        t.mask[l] = (uint16_t)msk;
+        sy += t.lyh[l];
+        sx += t.lix[l];
+        ++nv;
+        cost += (long long)lane_js[l].size();
+    }
+    t.cy = (float)(nv ? sy / nv : 0.0);
+    t.cx = (float)(nv ? sx / nv : 0.0);
+    double rad = 0.0;
+    for (int l = 0; l < 64; ++l) {
+        if (t.qidx[l] < 0) continue;
+        rad = std::max(rad, std::hypot((double)t.lyh[l] - (double)t.cy, (double)t.lix[l] - (double)t.cx));
+    }
+    t.rad = std::nextafter((float)(rad * (1.0 + 1e-6)), INFINITY);
+    by_nj[t.nj].emplace_back(-cost, t);
+}
+
+dsp_status build_preview_layout(const SsbKey &key, const dsp_optics *optics, const double *coords,
+                                const double *weights, std::shared_ptr<PreviewLayout> &out) {
+    const double t0 = now_ms();
+    dsp_status st;
+    auto L = std::make_shared<PreviewLayout>();
+    L->key = key;
+    const int N = key.n_scan, u = key.up, nh = N / 2 + 1;
+    const double dq = 1.0 / (N * key.step);
+    if ((st = build_active(coords, weights, key.n_bf, optics, N, L->act))) return st;
+    if (L->act.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
+    const double reach = 2.0 * std::sqrt(make_aperture_dev(optics).rlim2) * (1.0 + 1e-9);
+
+    // slots of every stored entry (rows -N/2 .. N/2-1, columns 0 .. N/2)
+    std::vector<JSet> ent((size_t)N * nh);
+    auto at = [&](int yh, int ix) -> JSet & { return ent[(size_t)(yh < 0 ? yh + N : yh) * nh + ix]; };
+    for (int yh = -N / 2; yh <= (N - 1) / 2; ++yh)
+        for (int ix = 0; ix < nh; ++ix) at(yh, ix) = preview_slots(yh, ix, N, u, dq, reach);
+    auto has = [&](int yh, int ix) { return !at(yh, ix).empty(); };
+
+    // lane groups cut along G's lines; a group whose slot union exceeds
+    // MAX_SLOTS splits into sub-tiles, greedily by lane, and a lane with more
+    // slots than that alone spreads its slots over several sub-tiles
+    std::map<int, std::vector<std::pair<long long, GramTile>>> by_nj;
+    for (const Lanes &grp : pack_line_runs(N, nh, -N / 2, (N - 1) / 2, nh, 8, has)) {
+        GramTile base;
+        std::memset(&base, 0, sizeof base);
+        JSet left[64];
+        for (int l = 0; l < 64; ++l) {
+            base.qidx[l] = -1;
+            if (l >= (int)grp.size()) continue;
+            base.lyh[l] = grp[l].first;
+            base.lix[l] = grp[l].second;
+            left[l] = at(grp[l].first, grp[l].second);
+        }
+        for (;;) {
+            GramTile t = base;
+            JSet js, lane_js[64];
+            for (int l = 0; l < 64; ++l) {
+                if (left[l].empty()) continue;
+                JSet tryu = js;
+                tryu.insert(tryu.end(), left[l].begin(), left[l].end());
+                std::sort(tryu.begin(), tryu.end());
+                tryu.erase(std::unique(tryu.begin(), tryu.end()), tryu.end());
+                if ((int)tryu.size() <= MAX_SLOTS) {
+                    js.swap(tryu);
+                    lane_js[l].swap(left[l]);
+                } else if (js.empty()) {
+                    // one lane above the maximum: its first MAX_SLOTS slots
+                    lane_js[l].assign(left[l].begin(), left[l].begin() + MAX_SLOTS);
+                    left[l].erase(left[l].begin(), left[l].begin() + MAX_SLOTS);
+                    js = lane_js[l];
+                } else {
+                    continue;
+                }
+                t.qidx[l] = 0;
+            }
+            if (js.empty()) break;
+            preview_finish_tile(t, js, lane_js, by_nj);
+        }
+    }
+    for (auto &kv : by_nj) {
+        auto &v = kv.second;
+        std::stable_sort(v.begin(), v.end(), [](const std::pair<long long, GramTile> &a,
+                                                const std::pair<long long, GramTile> &b) { return a.first < b.first; });
+        L->tg.group_nj.push_back(kv.first);
+        L->tg.group_off.push_back((int)L->tg.tiles.size());
+        L->tg.group_n.push_back((int)v.size());
+        for (auto &p : v) L->tg.tiles.push_back(p.second);
+    }
+
+    // stream-K plan per group, as for the prepare's Gram launches
+    const int n_groups = (int)L->tg.group_nj.size();
+    const int n_pix = (int)L->act.pix.size();
+    int n_cu = 0;
+    HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, key.device));
+    const double ra = std::sqrt(make_aperture_dev(optics).rlim2);
+    Geometry g;
+    g.N = N;
+    g.u = u;
+    g.dq = dq;
+    L->sk_waves.assign(n_groups, 0);
+    L->wb_off.assign(n_groups, 0);
+    L->so_off.assign(n_groups, 0);
+    L->sf_off.assign(n_groups, 0);
+    for (int gi = 0; gi < n_groups; ++gi) {
+        const int nj = L->tg.group_nj[gi], nt = L->tg.group_n[gi];
+        int bpc = 0;
+        HIP_TRY(gram_occupancy(nj, GRAM_PREVIEW, &bpc));
+        bpc = std::max(1, bpc);
+        const long long total_it = (long long)nt * n_pix;
+        const int W = (int)std::max(1LL, std::min((long long)bpc * n_cu * GRAM_ROUNDS, total_it / 64));
+        std::vector<uint16_t> cost;
+        gram_iteration_costs(L->tg.tiles.data() + L->tg.group_off[gi], nt, L->act.pix, g, ra, cost);
+        StreamKPlan plan;
+        plan_stream_k_iter(cost, nt, n_pix, W, plan);
+        L->sk_waves[gi] = W;
+        L->max_partial = std::max(L->max_partial, (size_t)plan.n_segs * gram_nacc(nj, GRAM_PREVIEW) * 64);
+        L->wb_off[gi] = L->sk_wbegin.size();
+        L->sk_wbegin.insert(L->sk_wbegin.end(), plan.wbegin.begin(), plan.wbegin.end());
+        L->so_off[gi] = L->sk_int.size();
+        L->sk_int.insert(L->sk_int.end(), plan.seg_off.begin(), plan.seg_off.end());
+        L->sf_off[gi] = L->sk_int.size();
+        L->sk_int.insert(L->sk_int.end(), plan.seg_first.begin(), plan.seg_first.end());
+    }
+    if ((st = dev_alloc(&L->d_pixbase, (size_t)n_pix)) || (st = dev_alloc(&L->d_goff, (size_t)n_pix)) ||
+        (st = dev_alloc(&L->d_tiles, std::max<size_t>(1, L->tg.tiles.size()))) ||
+        (st = dev_alloc(&L->d_sk_wbegin, std::max<size_t>(1, L->sk_wbegin.size()))) ||
+        (st = dev_alloc(&L->d_sk_int, std::max<size_t>(1, L->sk_int.size()))))
+        return st;
+    HIP_TRY(hipMemcpy(L->d_pixbase, L->act.pix.data(), sizeof(PixelBase) * n_pix, hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpy(L->d_goff, L->act.goff.data(), sizeof(long long) * n_pix, hipMemcpyHostToDevice));
+    if (!L->tg.tiles.empty())
+        HIP_TRY(hipMemcpy(L->d_tiles, L->tg.tiles.data(), L->tg.tiles.size() * sizeof(GramTile),
+                          hipMemcpyHostToDevice));
+    if (!L->sk_wbegin.empty())
+        HIP_TRY(hipMemcpy(L->d_sk_wbegin, L->sk_wbegin.data(), L->sk_wbegin.size() * sizeof(long long),
+                          hipMemcpyHostToDevice));
+    if (!L->sk_int.empty())
+        HIP_TRY(hipMemcpy(L->d_sk_int, L->sk_int.data(), L->sk_int.size() * sizeof(int), hipMemcpyHostToDevice));
+    L->host_ms = now_ms() - t0;
+    out = L;
+    return DSP_OK;
+}
+
+// front = most recent (under g_layout_mu); never destroyed, like g_layouts
+std::vector<std::shared_ptr<PreviewLayout>> &g_preview_layouts = *new std::vector<std::shared_ptr<PreviewLayout>>();
+
+dsp_status get_preview_layout(const SsbKey &key, const dsp_optics *optics, const double *coords,
+                              const double *weights, std::shared_ptr<PreviewLayout> &out) {
+    std::lock_guard<std::mutex> lock(g_layout_mu);
+    for (size_t i = 0; i < g_preview_layouts.size(); ++i) {
+        if (g_preview_layouts[i]->key == key) {
+            out = g_preview_layouts[i];
+            g_preview_layouts.erase(g_preview_layouts.begin() + i);
+            g_preview_layouts.insert(g_preview_layouts.begin(), out);
+            return DSP_OK;
+        }
+    }
+    dsp_status st = build_preview_layout(key, optics, coords, weights, out);
+    if (st) return st;
+    g_preview_layouts.insert(g_preview_layouts.begin(), out);
+    if (g_preview_layouts.size() > LAYOUT_CACHE_SIZE) g_preview_layouts.pop_back();
     return DSP_OK;
 }
 
@@ -1897,10 +2132,9 @@ dsp_status dsp_alias_table(const dsp_handle *h, int32_t *q_host, int32_t *count_
 // Scratch of one SSB pass (the stream's arena, or the fixed scratch).
 struct SsbPassBufs {
     PixelRec *pix;
-    double *chi;        // [n_pix][MAX_SETS_DEV]
     double *part;       // stream-K partial sums
     double *tile_part;  // [n_tiles][partial stride]
-    double *tay;        // [n_pix][TAY_N] for a Taylor pass, else null
+    double *tay;        // B tables [n_pix][TAY_N]
 };
 
 // Device copies of a pass's layout tables: the layout's own, or copies in
@@ -1926,14 +2160,14 @@ static dsp_status layout_tables(const SsbLayout &L, int mi, int device, SsbDevTa
 }
 
 // One pass over G for B sets on layout L: pixel terms, then the SSB kernel
-// with lanes on the (M, M/2 + 1) grid writing S and N there.  With bufs.tay
-// (B tables of [n_pix][TAY_N]), the kernel takes both lobes' phases from each
-// set's chi Taylor coefficients about theta(k) (one evaluation of the even and
-// odd parts in lambda q per pixel and set instead of the polynomial at both
-// displaced points).
+// with lanes on the stored (N, N/2 + 1) half plane writing S and N there.  The
+// kernel takes both lobes' phases from each set's chi Taylor coefficients
+// about theta(k) (bufs.tay: one evaluation of the even and odd parts in
+// lambda q per pixel and set instead of the polynomial at both displaced
+// points).
 static dsp_status ssb_pass(const SsbLayout &L, const SsbDevTables &dt, const dsp_optics *sets_host, int B,
                            const void *G_c64_dev, const void *GQ_dev, const float *gscale_dev, int h16_rows, int N,
-                           int M, double2 *S_out, double *N_out, const SsbPassBufs &bufs, hipStream_t stream) {
+                           double2 *S_out, double *N_out, const SsbPassBufs &bufs, hipStream_t stream) {
     const int n_tiles = (int)L.tiles.size();
     const int n_pix = (int)L.act.pix.size();
     const int mi = maxb_index(ssb_maxb(B));
@@ -1943,11 +2177,9 @@ static dsp_status ssb_pass(const SsbLayout &L, const SsbDevTables &dt, const dsp
     std::memset(&sp, 0, sizeof sp);
     for (int b = 0; b < B; ++b) {
         const OpticsDev od = make_optics_dev(sets_host + b);
-        // a(k) once (set 0 writes it), chi(k) per set
-        double *tb = bufs.tay ? bufs.tay + (size_t)b * n_pix * TAY_N : nullptr;   // set b's Taylor table
-        if (b == 0) HIP_TRY(launch_pixel_terms(dt.pixbase, bufs.pix, n_pix, apd, od, nullptr, 0, tb, stream));
-        else if (tb) HIP_TRY(launch_pixel_terms(dt.pixbase, nullptr, n_pix, apd, od, nullptr, 0, tb, stream));
-        HIP_TRY(launch_pixel_terms(dt.pixbase, bufs.pix, n_pix, apd, od, bufs.chi + b, MAX_SETS_DEV, nullptr, stream));
+        // the pixel records once (set 0 writes them), the Taylor table per set
+        double *tb = bufs.tay + (size_t)b * n_pix * TAY_N;
+        HIP_TRY(launch_pixel_terms(dt.pixbase, b == 0 ? bufs.pix : nullptr, n_pix, apd, od, nullptr, 0, tb, stream));
         sp.tau_y[b] = od.tau_y;
         sp.tau_x[b] = od.tau_x;
         sp.pt2[b] = od.pt2;
@@ -1960,14 +2192,11 @@ static dsp_status ssb_pass(const SsbLayout &L, const SsbDevTables &dt, const dsp
     sp.plane = (long long)N * (N / 2 + 1);
     sp.pix = bufs.pix;
     sp.goff = dt.goff;
-    sp.chi_tab = bufs.chi;
     sp.tay = bufs.tay;
     sp.n_pix = n_pix;
     sp.tiles = dt.tiles;
     sp.N = N;
     sp.nh = N / 2 + 1;
-    sp.M = M;
-    sp.mh = M / 2 + 1;
     sp.dq = dq;
     sp.ldq = sets_host[0].wavelength_A * dq;
     sp.B = B;
@@ -2166,8 +2395,7 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
         dt.seg_first = d_sf;
         scr += tv.off;
     } else {
-        const size_t need = carve_size(n_pix, sizeof(PixelRec)) +
-                            carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) + carve_size(n_part, sizeof(double)) +
+        const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size(n_part, sizeof(double)) +
                             carve_size((size_t)n_tiles * stride, sizeof(double)) + carve_size(B + 1, sizeof(double)) +
                             carve_size(std::max<size_t>(1, n_tay), sizeof(double));
         if ((st = arena_get(device, stream, need, &scr))) return st;
@@ -2175,14 +2403,13 @@ static dsp_status ssb_impl(const void *G_c64_dev, const void *GQ_dev, const floa
     }
     Carve cv{scr};
     PixelRec *d_pix = cv.take<PixelRec>(n_pix);
-    double *d_chi = cv.take<double>((size_t)MAX_SETS_DEV * n_pix);
     double *d_part = cv.take<double>(n_part);
     double *d_tile_part = cv.take<double>((size_t)n_tiles * stride);
     double *d_E = cv.take<double>(B + 1);
     double *d_tay = cv.take<double>(std::max<size_t>(1, n_tay));
 
-    SsbPassBufs bufs{d_pix, d_chi, d_part, d_tile_part, d_tay};
-    if ((st = ssb_pass(L, dt, sets_host, B, G_c64_dev, GQ_dev, gscale_dev, h16_rows, N, N, (double2 *)S_out_c128_dev,
+    SsbPassBufs bufs{d_pix, d_part, d_tile_part, d_tay};
+    if ((st = ssb_pass(L, dt, sets_host, B, G_c64_dev, GQ_dev, gscale_dev, h16_rows, N, (double2 *)S_out_c128_dev,
                        norm_out_dev, bufs, stream)))
         return st;
     std::vector<double> E(B + 1, 0.0);
@@ -2240,34 +2467,52 @@ dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_
     SsbKey key = pass_key(device, scan, optics, n_bf, bf_coords_host, weights_host);
     key.up = upsampling;
     key.preview = 1;
-    std::shared_ptr<SsbLayout> lay;
-    if ((st = get_ssb_layout(key, optics, bf_coords_host, weights_host, lay))) return st;
-    const SsbLayout &L = *lay;
-    const int n_tiles = (int)L.tiles.size();
+    std::shared_ptr<PreviewLayout> lay;
+    if ((st = get_preview_layout(key, optics, bf_coords_host, weights_host, lay))) return st;
+    const PreviewLayout &L = *lay;
     const int n_pix = (int)L.act.pix.size();
-    const int mi = maxb_index(ssb_maxb(1));
-    const size_t n_part = (size_t)L.n_segs[mi] * ssb_nacc(1) * 64;
-    const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)MAX_SETS_DEV * n_pix, sizeof(double)) +
-                        carve_size(n_part, sizeof(double)) +
-                        carve_size((size_t)std::max(1, n_tiles) * ssb_partial_stride(1), sizeof(double)) +
+    const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size(std::max<size_t>(1, L.max_partial), sizeof(double)) +
                         carve_size((size_t)n_half, sizeof(double2)) + carve_size(1, sizeof(double2));
     char *scr = nullptr;
     if ((st = arena_get(device, stream, need, &scr))) return st;
     Carve cv{scr};
-    SsbPassBufs bufs;
-    bufs.tay = nullptr;   // previews keep the direct polynomial (mostly one lobe per pixel)
-    bufs.pix = cv.take<PixelRec>(n_pix);
-    bufs.chi = cv.take<double>((size_t)MAX_SETS_DEV * n_pix);
-    bufs.part = cv.take<double>(n_part);
-    bufs.tile_part = cv.take<double>((size_t)std::max(1, n_tiles) * ssb_partial_stride(1));
+    PixelRec *d_pix = cv.take<PixelRec>(n_pix);
+    double *d_partial = cv.take<double>(std::max<size_t>(1, L.max_partial));
     double2 *d_S = cv.take<double2>((size_t)n_half);
     double2 *d_dc = cv.take<double2>(1);
-    // S on the fine half plane (zero where no lane runs: K = 0 and beyond reach)
+    // S on the fine half plane (zero where no slot writes: K = 0, the Nyquist
+    // lines and beyond reach)
     HIP_TRY(launch_fill_zero((double *)d_S, (size_t)n_half * 2, stream));
-    SsbDevTables dt;
-    if ((st = layout_tables(L, mi, device, dt))) return st;
-    if (n_tiles > 0 && (st = ssb_pass(L, dt, optics, 1, G_c64_dev, nullptr, nullptr, 0, N, M, d_S, nullptr, bufs, stream)))
-        return st;
+    const ApertureDev apd = make_aperture_dev(optics);
+    const OpticsDev opd = make_optics_dev(optics);
+    HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, opd, nullptr, 0, nullptr, stream));
+    GramParams gp;
+    std::memset(&gp, 0, sizeof gp);
+    gp.G = (const float2 *)G_c64_dev;
+    gp.pix = d_pix;
+    gp.goff = L.d_goff;
+    gp.n_pix = n_pix;
+    gp.N = N;
+    gp.nh = N / 2 + 1;
+    gp.dq = 1.0 / (N * scan->step_A);
+    gp.ldq = optics->wavelength_A * gp.dq;
+    gp.ap = apd;
+    gp.op = opd;
+    gp.sys = d_S;
+    gp.slot_test = 1;
+    gp.fine_M = M;
+    gp.fine_mh = mh;
+    gp.partial = d_partial;
+    if ((st = trig_table_device(device, &gp.trig))) return st;
+    for (size_t gi = 0; gi < L.tg.group_nj.size(); ++gi) {
+        gp.tiles = L.d_tiles + L.tg.group_off[gi];
+        gp.wbegin = L.d_sk_wbegin + L.wb_off[gi];
+        gp.seg_off = L.d_sk_int + L.so_off[gi];
+        gp.seg_first = L.d_sk_int + L.sf_off[gi];
+        gp.n_waves = L.sk_waves[gi];
+        HIP_TRY(launch_gram(gp, L.tg.group_nj[gi], GRAM_PREVIEW, gp.n_waves, stream));
+        HIP_TRY(launch_gram_fixup(gp, L.tg.group_nj[gi], GRAM_PREVIEW, L.tg.group_n[gi], stream));
+    }
     HIP_TRY(launch_preview_dc(L.d_pixbase, L.d_goff, n_pix, (const float2 *)G_c64_dev, d_dc, stream));
     if (spec_out_c128_dev) HIP_TRY(launch_preview_spectrum(d_S, d_dc, n_half, (double2 *)spec_out_c128_dev, stream));
     if (phase_out_dev) {

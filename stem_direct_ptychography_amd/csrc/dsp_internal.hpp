@@ -258,6 +258,7 @@ struct GramParams {
     int n_waves;
     const double2 *trig;       // [TRIG_N] (cos, sin)(j pi / 128)
     int slot_test;             // 1: skip slots the per-pixel bound puts out of reach; 0: run all
+    int fine_M, fine_mh;       // preview (right sides only): the fine grid M = u N and M / 2 + 1
 };
 
 constexpr int MAX_SETS_DEV = 8;   // optics sets of one SSB pass
@@ -272,12 +273,10 @@ struct SsbParams {
     long long plane;         // N (N/2 + 1): plane offset -> pixel index
     const PixelRec *pix;
     const long long *goff;   // [n_pix]
-    const double *chi_tab;   // [n_pix][MAX_SETS_DEV] chi(k) per set
-    const double *tay;       // band pass: B tables [n_pix][TAY_N] of chi Taylor coefficients about theta(k), else null
+    const double *tay;       // B tables [n_pix][TAY_N] of chi Taylor coefficients about theta(k)
     int n_pix;
     const SsbTile *tiles;
     int N, nh;
-    int M, mh;               // output grid: lanes hold fine frequencies K of the (M, mh) half plane, M = u N
     double dq;
     double ldq;              // lambda dq
     int B;

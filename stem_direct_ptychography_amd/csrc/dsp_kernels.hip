@@ -135,6 +135,18 @@ struct GramShape {
     static constexpr int im(int c, int d) { return D + 2 * off(c, d) + 1; }
 };
 
+// METHOD 2 (the upsampled preview): columns T_phi(slot 0..NJ-1), right
+// sides only, conj(T_phi) w g per slot: two doubles per slot.
+template <int NJ>
+struct GramShape<NJ, 2> {
+    static constexpr int NC = NJ;
+    static constexpr int D = NC + 1;
+    static constexpr int NOFF = 0;
+    static constexpr int NACC = 2 * NJ;
+    static constexpr int re(int c, int) { return 2 * c; }
+    static constexpr int im(int c, int) { return 2 * c + 1; }
+};
+
 // Complex method: the sums of column pairs within one side (L x L and R x R,
 // both columns below NJ or both in NJ .. 2 NJ - 1) live in LDS, one double2
 // per pair and lane; they are updated least often, and keeping them out of
@@ -263,14 +275,15 @@ constexpr int SSB_CHUNK = 64;
 // kernel within three waves per SIMD without spills), four for complex.
 template <int NJ, int METHOD>
 struct GramPrefetch {
-    static constexpr int value = METHOD == 0 ? 2 : 4;
+    static constexpr int value = METHOD == 1 ? 4 : 2;
 };
 
 // Waves per SIMD the compiler must fit (caps the registers per lane).
 template <int NJ, int METHOD>
 struct GramWaves {
-    static constexpr int value = METHOD == 0 ? (NJ <= 2 ? 4 : (NJ <= 4 ? 3 : (NJ <= 6 ? 2 : 1)))
-                                             : (NJ <= 1 ? 4 : (NJ <= 2 ? 3 : (NJ <= 4 ? 2 : 1)));
+    static constexpr int value = METHOD == 2   ? (NJ <= 6 ? 4 : 3)
+                                 : METHOD == 0 ? (NJ <= 2 ? 4 : (NJ <= 4 ? 3 : (NJ <= 6 ? 2 : 1)))
+                                               : (NJ <= 1 ? 4 : (NJ <= 2 ? 3 : (NJ <= 4 ? 2 : 1)));
 };
 
 // Pixel records and plane offsets are written by earlier kernels or copies,
@@ -342,7 +355,7 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
     }
 
     const double gr = (double)gv.x * sw, gi = (double)gv.y * sw;
-    acc[NC] = fma(gr, gr, fma(gi, gi, acc[NC]));   // signal power w |g|^2
+    if (METHOD != 2) acc[NC] = fma(gr, gr, fma(gi, gi, acc[NC]));   // signal power w |g|^2
 
     double tr[NC], ti[NC];
     unsigned long long bal[NC];   // lanes whose column is non-zero
@@ -407,7 +420,13 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
                 lobe<DEPTH>(prm, T, -arg, h, dp2, amp0, Rr, Ri);
             }
         }
-        if (METHOD == 0) {
+        if (METHOD == 2) {
+            // right side only, added as soon as the slot's column is known
+            // (no column is kept for pairs): <col s, g> = conj(T_phi) g
+            const double t_r = Ri - Li, t_i = Lr - Rr;
+            acc[Sh::re(s, NC)] = fma(t_r, gr, fma(t_i, gi, acc[Sh::re(s, NC)]));
+            acc[Sh::im(s, NC)] = fma(t_r, gi, fma(-t_i, gr, acc[Sh::im(s, NC)]));
+        } else if (METHOD == 0) {
             tr[s] = Ri - Li;   // T_phi = i (L - R)
             ti[s] = Lr - Rr;
             bal[s] = __ballot(zl || zr);
@@ -427,6 +446,7 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
     // exact zeros.  Pairs held in registers then run without a test (a
     // branch costs more than their FMAs); pairs held in LDS, whose atomics
     // are dearer, run when some lane has both columns.
+    if (METHOD == 2) return;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const unsigned bits = METHOD == 0 ? (pm >> (2 * c)) & 3u : (pm >> (c < NJ ? 2 * c : 2 * (c - NJ) + 1)) & 1u;
@@ -662,7 +682,33 @@ __global__ __launch_bounds__(64) void gram_write_kernel(GramParams prm) {
     const double *pi = prm.partial + (size_t)prm.seg_first[t] * (NACC * 64);
 #pragma unroll
     for (int i = 0; i < NACC; ++i) acc[i] = pi[i * 64 + lane];
-    write_system<NJ, METHOD>(acc, (unsigned)tile->mask[lane], qi, prm);
+    if constexpr (METHOD == 2) {
+        // preview: slot s of stored entry (yh, ix) is the fine frequency
+        // K = (yh + jy N, ix + jx N); its sum goes to S(K) when Kx >= 0 and,
+        // conjugated, to S(-K) otherwise (-K then reads G through the mirror
+        // G(-q) = conj G(q)).  The host admits only slots whose target lies
+        // in the computed part of the fine half plane; the range test here
+        // keeps every store inside the plane regardless.
+        const int M = prm.fine_M, mh = prm.fine_mh;
+        const unsigned mask = (unsigned)tile->mask[lane];
+#pragma unroll
+        for (int s = 0; s < NJ; ++s) {
+            if (!((mask >> s) & 1u)) continue;
+            int Ky = (int)tile->lyh[lane] + (int)tile->jy[s] * prm.N;
+            int Kx = (int)tile->lix[lane] + (int)tile->jx[s] * prm.N;
+            double re = acc[GramShape<NJ, 2>::re(s, 0)], im = acc[GramShape<NJ, 2>::im(s, 0)];
+            if (Kx < 0) {
+                Ky = -Ky;
+                Kx = -Kx;
+                im = -im;
+            }
+            const int row = Ky < 0 ? Ky + M : Ky;
+            if (row < 0 || row >= M || Kx >= mh) continue;
+            prm.sys[(size_t)row * mh + Kx] = make_double2(re, im);
+        }
+    } else {
+        write_system<NJ, METHOD>(acc, (unsigned)tile->mask[lane], qi, prm);
+    }
 }
 
 // Work a Gram launch does per frequency, counted exactly per lane (not the
@@ -1219,24 +1265,20 @@ struct SsbWaves {
 // H16: G comes as herm16 snorm16 pairs, unpacked as max(q / 32767, -1) s in
 // FP64 at use; H16 = 1: one scale per pixel (staged with the pixel record);
 // H16 = 2: one scale per stored row, fetched with G for the lane's row.
-template <int MAXB, bool DEPTH, int H16, bool TAYS>
+template <int MAXB, bool DEPTH, int H16>
 __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParams prm) {
     constexpr int NACC = 3 * MAXB + 1;
     constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
     using GT = typename std::conditional<H16 != 0, short2, float2>::type;
     __shared__ double2 T[TRIG_N];
-    // TAYS: both lobes' phases from each set's chi Taylor coefficients about
+    // both lobes' phases come from each set's chi Taylor coefficients about
     // theta(k), staged per chunk (chunks of 16 or 8 pixels keep the LDS within
     // the kernel's waves per SIMD)
-    constexpr int CHK = TAYS ? (MAXB <= 2 ? 16 : 8) : SSB_CHUNK;
+    constexpr int CHK = MAXB <= 2 ? 16 : 8;
     __shared__ PixelRec srec[CHK];
     __shared__ long long sgoff[CHK + PF];
     __shared__ long long sgrow[H16 == 2 ? CHK + PF : 1];   // pixel index x N (row scales)
-    __shared__ double schi[MAXB * CHK];   // [set][pixel of the chunk] chi(k)
-    __shared__ unsigned smask[CHK];        // per pixel of the chunk: the reach test's L/R bits
-    __shared__ double stay[TAYS ? MAXB * CHK * TAY_N : 1];   // [set][pixel][TAY_N]
-    __shared__ double2 scent;                    // lambda c, c the tile centre
-    __shared__ double sthr;                      // the reach test's squared bound
+    __shared__ double stay[MAXB * CHK * TAY_N];   // [set][pixel][TAY_N]
     const int lane = threadIdx.x;
     for (int i = lane; i < TRIG_N; i += 64) T[i] = prm.trig[i];
 
@@ -1247,7 +1289,6 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
     int seg = prm.seg_off[wv];
     ConstPixel *pix = (ConstPixel *)prm.pix;
     ConstLong *goffs = (ConstLong *)prm.goff;
-    const double *__restrict__ chi_tab = prm.chi_tab;
     const GT *__restrict__ G = H16 ? (const GT *)prm.GQ : (const GT *)prm.G;
     const float *__restrict__ gsc = prm.gscale;
 
@@ -1256,40 +1297,22 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
         const int p0 = (int)(it - (long long)t * n_pix);
         const int p1 = (int)((end - it) < (n_pix - p0) ? p0 + (end - it) : n_pix);
         const SsbTile *tile = prm.tiles + t;
-        const int yh = tile->lyh[lane];   // the lane's frequency K (fine grid; the stored q when M = N)
+        const int yh = tile->lyh[lane];   // the lane's stored frequency q (signed row, column)
         const int ix = tile->lix[lane];
         const bool valid = (tile->valid >> lane) & 1ull;
-        // G at q = K mod N from the stored half plane: G(-q) = conj G(q) where
-        // q's column exceeds N/2 (never when M = N)
-        int iyq = yh % prm.N;
-        if (iyq < 0) iyq += prm.N;
-        int ixq = ix % prm.N;
-        const bool cj = ixq > prm.N / 2;
-        if (cj) {
-            iyq = iyq == 0 ? 0 : prm.N - iyq;
-            ixq = prm.N - ixq;
-        }
-        const long long lane_off = valid ? (long long)iyq * prm.nh + ixq : 0;
-        const double qy = (double)yh * prm.ldq, qx = (double)ix * prm.ldq;   // lambda K
+        const int iyq = yh < 0 ? yh + prm.N : yh;   // its row in the stored half plane
+        const long long lane_off = valid ? (long long)iyq * prm.nh + ix : 0;
+        const double qy = (double)yh * prm.ldq, qx = (double)ix * prm.ldq;   // lambda q
         const double q2 = fma(qy, qy, qx * qx);
-        const double qX = qx * qx, qY = qy * qy, qZ = qx * qy;   // Taylor pass: powers of d = lambda q
+        const double qX = qx * qx, qY = qy * qy, qZ = qx * qy;   // powers of d = lambda q
 
         double acc[NACC];
 #pragma unroll
         for (int i = 0; i < NACC; ++i) acc[i] = 0.0;
-        // Reach test: the lanes' frequencies lie within rad of the tile
-        // centre c, so a lobe can be in support at pixel k only if
-        // |lambda k -/+ lambda c| < lambda r + rad lambda dq; sthr is that
-        // bound squared, widened by a part in 1e9 against rounding.  Pixels
-        // failing both tests add only their signal power.
-        if (lane == 0) {
-            scent = make_double2((double)tile->cy * prm.ldq, (double)tile->cx * prm.ldq);
-            const double rr = sqrt(prm.ap.lrlim2) + (double)tile->rad * prm.ldq;
-            sthr = rr * rr * (1.0 + 1e-9);
-        }
 
-        // records, plane offsets and the sets' chi(k) staged in LDS per chunk;
-        // G a group of PF pixels ahead; the chunk's tail runs on zero records
+        // records, plane offsets and the sets' Taylor coefficients staged in
+        // LDS per chunk; G a group of PF pixels ahead; the chunk's tail runs on
+        // zero records
         GT ga[PF];
         float sa[PF];   // row scales of the group (H16 == 2)
 #pragma unroll
@@ -1308,24 +1331,12 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
                 // herm16: the pixel's scale rides in the record's spare field
                 if (H16 == 1) rec.pad = (double)gsc[goffs[c0 + lane] / prm.plane];
                 srec[lane] = rec;
-                const double2 c = scent;
-                const double thr = sthr;
-                const double ly = rec.lky - c.x, lx = rec.lkx - c.y;
-                const double ry = rec.lky + c.x, rx = rec.lkx + c.y;
-                smask[lane] = (fma(ly, ly, lx * lx) < thr ? 1u : 0u) | (fma(ry, ry, rx * rx) < thr ? 2u : 0u);
             } else {
                 PixelRec z;
                 z.lky = z.lkx = z.amp0 = z.sw = z.chi0 = z.pad = 0.0;
                 srec[lane] = z;
-                smask[lane] = 0u;
             }
-            if (lane < CHK) {
-#pragma unroll
-                for (int b = 0; b < MAXB; ++b)
-                    schi[b * CHK + lane] =
-                        (lane < cn && b < prm.B) ? chi_tab[(size_t)(c0 + lane) * MAX_SETS_DEV + b] : 0.0;
-            }
-            if (TAYS) {
+            {
                 // set b's table starts at b n_pix TAY_N
 #pragma unroll
                 for (int b = 0; b < MAXB; ++b) {
@@ -1361,84 +1372,15 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
                         gre = (double)ga[k].x;
                         gim = (double)ga[k].y;
                     }
-                    if (!TAYS && cj) gim = -gim;   // band passes (TAYS) read stored entries only
                     // (the chunk's tail, r >= cn, runs on zero records: sw = amp0 = 0
                     // zero its terms)
-                    const double *chi0s = schi + r;
-                    if (TAYS) {
-                        // Band pass, straight-line: nearly every pixel has both lobes in
-                        // reach of some lane of the tile, so both are always evaluated
-                        // for every set and a lane's lobe outside the support gets
-                        // amplitude 0 by select (no per-lane branches, whose joins cost
-                        // register copies, and no exec-mask bookkeeping).
-                        const double lrlim2 = prm.ap.lrlim2, lrin2 = prm.ap.lrin2, lkc = prm.ap.lkc;
-                        const double inv_ldk = prm.ap.inv_ldk;
-                        const int B = prm.B;
-                        const double lk2 = fma(lky, lky, lkx * lkx);
-                        const double gr = gre * sw, gi = gim * sw;
-                        acc[NACC - 1] = fma(gr, gr, fma(gi, gi, acc[NACC - 1]));
-                        const double kq = fma(lky, qy, lkx * qx);
-                        const double base = lk2 + q2;
-                        const double dm2 = fma(-2.0, kq, base), dp2 = fma(2.0, kq, base);
-                        const bool zl = valid && dm2 < lrlim2;
-                        const bool zr = valid && dp2 < lrlim2;
-                        double aml = zl ? amp0 : 0.0, amr = zr ? amp0 : 0.0;
-                        const bool rl = zl && dm2 > lrin2, rr = zr && dp2 > lrin2;
-                        if (wave_any(rl || rr)) {
-                            const double fl = fma(lkc - sqrt_fast(dm2), inv_ldk, 0.5);
-                            const double fr = fma(lkc - sqrt_fast(dp2), inv_ldk, 0.5);
-                            aml = rl ? aml * fl : aml;
-                            amr = rr ? amr * fr : amr;
-                        }
-#pragma unroll
-                        for (int b = 0; b < MAXB; ++b) {
-                            if (b >= B) continue;   // uniform; keeps the loop fully unrolled
-                            int zb = 0;
-                            if (MAXB > 1) asm volatile("" : "+s"(zb));   // see the per-set loop below
-                            const double *cb = &prm.chi_c[b][zb];
-                            // the even part's 8 coefficients, then the odd part's 12: the
-                            // empty asm keeps the second group's LDS reads after the first
-                            // evaluation, so fewer coefficients are live at once
-                            const double *ts = stay + (b * CHK + r) * TAY_N;
-                            double te[8], to[12];
-#pragma unroll
-                            for (int m = 0; m < 8; ++m) te[m] = ts[m];
-                            const double E = chi_even(te, cb, qX, qY, qZ);
-                            asm volatile("" ::: "memory");
-#pragma unroll
-                            for (int m = 0; m < 12; ++m) to[m] = ts[8 + m];
-                            const double O = chi_odd(to, qx, qy, qX, qY);
-                            double hl = 0.0, hr = 0.0, al = aml, ar = amr;
-                            if (DEPTH) {
-                                const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
-                                const double td2 = 2.0 * fma(py, qy, px * qx);
-                                hl = prm.pt2[b] * (td2 - q2);
-                                hr = prm.pt2[b] * (td2 + q2);
-                                al *= sinc_tab(hl, T);
-                                ar *= sinc_tab(hr, T);
-                            }
-                            double sl, cl, sr, cr;
-                            sincos_tab((O - E) + hl, T, sl, cl);
-                            sincos_tab((O + E) + hr, T, sr, cr);
-                            // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
-                            const double gmr = fma(ar, sr, -(al * sl)), gmi = fma(al, cl, -(ar * cr));
-                            acc[3 * b] = fma(gmr, gr, fma(gmi, gi, acc[3 * b]));
-                            acc[3 * b + 1] = fma(gmr, gi, fma(-gmi, gr, acc[3 * b + 1]));
-                            acc[3 * b + 2] = fma(gmr, gmr, fma(gmi, gmi, acc[3 * b + 2]));
-                        }
-                        continue;
-                    }
-                    // (one set only: with more, the branch costs registers, spills or
-                    // a wave per SIMD)
-                    if (MAXB == 1 && __builtin_amdgcn_readfirstlane(smask[r]) == 0u) {
-                        // no lane can have a lobe in support: signal power only
-                        const double gr = gre * sw, gi = gim * sw;
-                        acc[NACC - 1] = fma(gr, gr, fma(gi, gi, acc[NACC - 1]));
-                        continue;
-                    }
-                    // one pixel's update (kept in the kernel body: the sets' chi
-                    // coefficients are read straight from the kernel arguments)
-                    const double lrlim2 = prm.ap.lrlim2, lrin2 = prm.ap.lrin2, lkc = prm.ap.lkc, inv_ldk = prm.ap.inv_ldk;
+                    // Straight-line: nearly every pixel has both lobes in
+                    // reach of some lane of the tile, so both are always evaluated
+                    // for every set and a lane's lobe outside the support gets
+                    // amplitude 0 by select (no per-lane branches, whose joins cost
+                    // register copies, and no exec-mask bookkeeping).
+                    const double lrlim2 = prm.ap.lrlim2, lrin2 = prm.ap.lrin2, lkc = prm.ap.lkc;
+                    const double inv_ldk = prm.ap.inv_ldk;
                     const int B = prm.B;
                     const double lk2 = fma(lky, lky, lkx * lkx);
                     const double gr = gre * sw, gi = gim * sw;
@@ -1448,60 +1390,50 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
                     const double dm2 = fma(-2.0, kq, base), dp2 = fma(2.0, kq, base);
                     const bool zl = valid && dm2 < lrlim2;
                     const bool zr = valid && dp2 < lrlim2;
-                    double aml = amp0, amr = amp0;
+                    double aml = zl ? amp0 : 0.0, amr = zr ? amp0 : 0.0;
                     const bool rl = zl && dm2 > lrin2, rr = zr && dp2 > lrin2;
                     if (wave_any(rl || rr)) {
-                        asm volatile("");
-                        if (rl) aml *= fma(lkc - sqrt_fast(dm2), inv_ldk, 0.5);
-                        if (rr) amr *= fma(lkc - sqrt_fast(dp2), inv_ldk, 0.5);
+                        const double fl = fma(lkc - sqrt_fast(dm2), inv_ldk, 0.5);
+                        const double fr = fma(lkc - sqrt_fast(dp2), inv_ldk, 0.5);
+                        aml = rl ? aml * fl : aml;
+                        amr = rr ? amr * fr : amr;
                     }
-                #pragma unroll
+#pragma unroll
                     for (int b = 0; b < MAXB; ++b) {
                         if (b >= B) continue;   // uniform; keeps the loop fully unrolled
-                        const double chi0 = chi0s[b * CHK];   // this pixel's chi(k) of set b (LDS)
+                        int zb = 0;
                         // The set's coefficients are read from the kernel arguments
                         // per use (scalar loads, constant cache): an opaque zero
                         // offset keeps the compiler from hoisting all sets' values
                         // into scalar registers, which would spill.
-                        int zb = 0;
                         if (MAXB > 1) asm volatile("" : "+s"(zb));
                         const double *cb = &prm.chi_c[b][zb];
-                        // theta(k) = lambda k + tau_b exactly as chi0 was formed, then -/+ lambda q
-                        const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
-                        const double th0 = DEPTH ? fma(px, px, py * py) : 0.0;
-                        double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
-                        {
-                        if (zl) {
-                            const double ty = py - qy, tx = px - qx;
-                            const double c1 = chi_poly(cb, tx, ty);
-                            double arg = chi0 - c1, a = aml;
-                            if (DEPTH) {   // depth term: phase + h, amplitude sinc(h)
-                                const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
-                                arg += h;
-                                a *= sinc_tab(h, T);
-                            }
-                            double sn, cs;
-                            sincos_tab(arg, T, sn, cs);
-                            Lr = a * cs;
-                            Li = a * sn;
+                        // the even part's 8 coefficients, then the odd part's 12: the
+                        // empty asm keeps the second group's LDS reads after the first
+                        // evaluation, so fewer coefficients are live at once
+                        const double *ts = stay + (b * CHK + r) * TAY_N;
+                        double te[8], to[12];
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) te[m] = ts[m];
+                        const double E = chi_even(te, cb, qX, qY, qZ);
+                        asm volatile("" ::: "memory");
+#pragma unroll
+                        for (int m = 0; m < 12; ++m) to[m] = ts[8 + m];
+                        const double O = chi_odd(to, qx, qy, qX, qY);
+                        double hl = 0.0, hr = 0.0, al = aml, ar = amr;
+                        if (DEPTH) {
+                            const double py = lky + prm.tau_y[b], px = lkx + prm.tau_x[b];
+                            const double td2 = 2.0 * fma(py, qy, px * qx);
+                            hl = prm.pt2[b] * (td2 - q2);
+                            hr = prm.pt2[b] * (td2 + q2);
+                            al *= sinc_tab(hl, T);
+                            ar *= sinc_tab(hr, T);
                         }
-                        if (zr) {
-                            const double ty = py + qy, tx = px + qx;
-                            const double c1 = chi_poly(cb, tx, ty);
-                            double arg = chi0 - c1, a = amr;
-                            if (DEPTH) {
-                                const double h = prm.pt2[b] * (th0 - fma(tx, tx, ty * ty));
-                                arg += h;
-                                a *= sinc_tab(h, T);
-                            }
-                            double sn, cs;
-                            sincos_tab(-arg, T, sn, cs);
-                            Rr = a * cs;
-                            Ri = a * sn;
-                        }
-                        }
+                        double sl, cl, sr, cr;
+                        sincos_tab((O - E) + hl, T, sl, cl);
+                        sincos_tab((O + E) + hr, T, sr, cr);
                         // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
-                        const double gmr = Ri - Li, gmi = Lr - Rr;
+                        const double gmr = fma(ar, sr, -(al * sl)), gmi = fma(al, cl, -(ar * cr));
                         acc[3 * b] = fma(gmr, gr, fma(gmi, gi, acc[3 * b]));
                         acc[3 * b + 1] = fma(gmr, gi, fma(-gmi, gr, acc[3 * b + 1]));
                         acc[3 * b + 2] = fma(gmr, gmr, fma(gmi, gmi, acc[3 * b + 2]));
@@ -1772,10 +1704,10 @@ __global__ __launch_bounds__(64) void ssb_write_kernel(SsbParams prm, double *ti
     const int yh = tile->lyh[lane];
     const int ix = tile->lix[lane];
     const bool valid = (tile->valid >> lane) & 1ull;
-    const int iy = yh < 0 ? yh + prm.M : yh;
-    const long long lane_off = valid ? (long long)iy * prm.mh + ix : 0;
+    const int iy = yh < 0 ? yh + prm.N : yh;
+    const long long lane_off = valid ? (long long)iy * prm.nh + ix : 0;
     const double *pi = prm.partial + (size_t)prm.seg_first[t] * (NACC * 64);
-    const size_t plane = (size_t)prm.M * prm.mh;
+    const size_t plane = (size_t)prm.N * prm.nh;
     double part[MAXB + 1];
 #pragma unroll
     for (int b = 0; b < MAXB; ++b) {
@@ -1851,6 +1783,20 @@ static hipError_t gram_dispatch(int nj, int method, Args &&...args) {
             default: return hipErrorInvalidValue;
         }
     }
+    if (method == 2) {
+        switch (nj) {
+            case 1: return F<1, 2>::run(args...);
+            case 2: return F<2, 2>::run(args...);
+            case 3: return F<3, 2>::run(args...);
+            case 4: return F<4, 2>::run(args...);
+            case 5: return F<5, 2>::run(args...);
+            case 6: return F<6, 2>::run(args...);
+            case 7: return F<7, 2>::run(args...);
+            case 8: return F<8, 2>::run(args...);
+            case 9: return F<9, 2>::run(args...);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (nj) {
         case 1: return F<1, 1>::run(args...);
         case 2: return F<2, 1>::run(args...);
@@ -1892,6 +1838,7 @@ struct GramOccupancy {
 };
 
 int gram_nacc(int nj, int method) {
+    if (method == 2) return 2 * nj;
     const int nc = method == 0 ? nj : 2 * nj;
     const int d = nc + 1;
     return d + d * (d - 1);
@@ -2016,25 +1963,19 @@ int ssb_nacc(int maxb) { return 3 * maxb + 1; }
 
 hipError_t ssb_occupancy(int maxb, int *blocks_per_cu) {
     switch (maxb) {
-        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1, false, 0, false>, 64, 0);
-        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2, false, 0, false>, 64, 0);
-        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4, false, 0, false>, 64, 0);
-        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8, false, 0, false>, 64, 0);
+        case 1: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<1, false, 0>, 64, 0);
+        case 2: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<2, false, 0>, 64, 0);
+        case 4: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<4, false, 0>, 64, 0);
+        case 8: return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, ssb_kernel<8, false, 0>, 64, 0);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int MAXB, bool DEPTH>
 static void ssb_dispatch_h(const SsbParams &prm, int h16, int n_waves, hipStream_t st) {
-    if (prm.tay) {
-        if (h16 == 2) ssb_kernel<MAXB, DEPTH, 2, true><<<n_waves, 64, 0, st>>>(prm);
-        else if (h16 == 1) ssb_kernel<MAXB, DEPTH, 1, true><<<n_waves, 64, 0, st>>>(prm);
-        else ssb_kernel<MAXB, DEPTH, 0, true><<<n_waves, 64, 0, st>>>(prm);
-        return;
-    }
-    if (h16 == 2) ssb_kernel<MAXB, DEPTH, 2, false><<<n_waves, 64, 0, st>>>(prm);
-    else if (h16 == 1) ssb_kernel<MAXB, DEPTH, 1, false><<<n_waves, 64, 0, st>>>(prm);
-    else ssb_kernel<MAXB, DEPTH, 0, false><<<n_waves, 64, 0, st>>>(prm);
+    if (h16 == 2) ssb_kernel<MAXB, DEPTH, 2><<<n_waves, 64, 0, st>>>(prm);
+    else if (h16 == 1) ssb_kernel<MAXB, DEPTH, 1><<<n_waves, 64, 0, st>>>(prm);
+    else ssb_kernel<MAXB, DEPTH, 0><<<n_waves, 64, 0, st>>>(prm);
 }
 
 template <int MAXB>

@@ -43,6 +43,11 @@ struct ScatterParams {
 
 hipError_t launch_pixel_terms(const PixelBase *in, PixelRec *out, int n_pix, const ApertureDev &ap, const OpticsDev &op,
                               double *chi_tab, int chi_stride, double *tay, hipStream_t st);
+// Gram launches: method DSP_PHASE (0), DSP_COMPLEX (1), or GRAM_PREVIEW (2):
+// right sides only, one per alias slot, written into the preview's fine half
+// plane (GramParams::sys then points at it; fine_M, fine_mh give its shape).
+constexpr int GRAM_PREVIEW = 2;
+constexpr int MAX_NJ_PREVIEW = 9;
 int gram_nacc(int nj, int method);   // doubles per lane of one partial sum
 hipError_t gram_occupancy(int nj, int method, int *blocks_per_cu);
 hipError_t launch_gram(const GramParams &prm, int nj, int method, int n_waves, hipStream_t st);

@@ -750,6 +750,17 @@ def test_preview_tiny_full(u):
     _preview_case(w, G, k, random_weights(len(k), 5 + u), opt, u)
 
 
+@pytest.mark.parametrize("u", [3, 4])
+def test_preview_tiny_coarse_step(u):
+    """A coarse scan step (N dq small against the aperture): at 4x most
+    stored entries have 12 to 16 fine images, more than one tile's alias
+    slots hold, so their slots are spread over several tiles."""
+    w = _tiny(n=12, step=0.8)
+    pix, k = bf_pixels(w)
+    G = data_stack_numpy(w, pix)
+    _preview_case(w, G, k, random_weights(len(k), 11 + u), w.optics, u)
+
+
 def test_preview_c1_and_c2():
     w = workload("c1")
     pix, k = bf_pixels(w)
