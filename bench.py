@@ -195,10 +195,10 @@ def _gather(G, act_t, idx, dev):
 
 
 def cpu_baseline(dsp, dev, w4, k4, G4, n_q: int, n_band: int, strength: float, workers: int):
-    """The oracle on all host cores: C1-C3 in full, a seeded 4096-frequency
-    subset of the full frame stratified by alias count (extrapolated per
-    stratum), and the SSB sum on the band at 1 and 8 sets (sampled,
-    extrapolated).  value = the full frame's step rate in scan frequencies/s
+    """The oracle on all host cores: C1 and C2 in full, seeded 2048-frequency
+    samples of C3's sweep and of the full frame stratified by alias count
+    (extrapolated per stratum), and the SSB sum on the band at 1 and 8 sets
+    (sampled, extrapolated).  value = the full frame's step rate in scan frequencies/s
     (phase prepare + solve, complex prepare + solve, one-set SSB pass)."""
     import multiprocessing as mp
 
@@ -228,15 +228,24 @@ def cpu_baseline(dsp, dev, w4, k4, G4, n_q: int, n_band: int, strength: float, w
             busy = pool.map(_oracle_prepare_chunk, jobs, chunksize=1)
             return time.perf_counter() - t0, busy, len(act)
 
-        # C1-C3 in full (the configurations' own methods and strength sweeps)
-        for name, strengths in (("c1", None), ("c2", None), ("c3", None)):
+        def stratified(w, n_take, seed):
+            # a seeded sample of the unique frequencies, stratified by alias
+            # count: {A: (frequencies with A aliases, sampled indices)}
+            _, counts, _ = O.alias_table(w.n_scan, w.step, w.upsampling, w.optics)
+            uq = O.unique_frequencies(w.n_scan)
+            rng = np.random.default_rng(seed)
+            strata = {}
+            for A in np.unique(counts):
+                idx = np.nonzero(counts == A)[0]
+                take = max(16, int(round(n_take * len(idx) / len(uq))))
+                strata[int(A)] = (len(idx), np.sort(rng.choice(idx, size=min(take, len(idx)), replace=False)))
+            return uq, strata
+
+        # C1 and C2 in full (their own methods and strength sweeps)
+        for name in ("c1", "c2"):
             w = workload(name)
             pix, k = bf_pixels(w)
-            if name == "c3":
-                G = data_stack_torch(w, pix, dev)
-                torch.cuda.synchronize()
-            else:
-                G = data_stack_numpy(w, pix)
+            G = data_stack_numpy(w, pix)
             q = O.unique_frequencies(w.n_scan)
             sts = list(w.strengths)
             wall, busy, n_act = run_prepare(name, G, k, w.method, sts, q, 64)
@@ -245,15 +254,28 @@ def cpu_baseline(dsp, dev, w4, k4, G4, n_q: int, n_band: int, strength: float, w
             log(f"cpu baseline {name}: {len(q)} frequencies ({w.method}, {len(sts)} strengths) in {wall:.1f} s")
             del G
 
-        # full frame: 4096 frequencies stratified by alias count, per method
-        _, counts, _ = O.alias_table(w4.n_scan, w4.step, w4.upsampling, w4.optics)
-        uq = O.unique_frequencies(w4.n_scan)
-        rng = np.random.default_rng(4096)
-        strata = {}
-        for A in np.unique(counts):
-            idx = np.nonzero(counts == A)[0]
-            take = max(32, int(round(4096 * len(idx) / len(uq))))
-            strata[int(A)] = (len(idx), np.sort(rng.choice(idx, size=min(take, len(idx)), replace=False)))
+        # C3: its 32-strength sweep on 2048 frequencies stratified by alias count
+        w3 = workload("c3")
+        pix3, k3 = bf_pixels(w3)
+        G3 = data_stack_torch(w3, pix3, dev)
+        torch.cuda.synchronize()
+        uq3, strata3 = stratified(w3, 2048, 2048)
+        cpu_full = wall_tot = 0.0
+        for A, (n_all, idx) in strata3.items():
+            wall, busy, n_act = run_prepare("c3", G3, k3, w3.method, list(w3.strengths), uq3[idx], 32)
+            cpu_full += sum(busy) * n_all / len(idx)
+            wall_tot += wall
+        n3 = sum(len(v[1]) for v in strata3.values())
+        out["configs"]["c3"] = {
+            "method": w3.method, "n_q": len(uq3), "strengths": len(w3.strengths),
+            "sample": f"{n3} of {len(uq3)} frequencies, stratified by alias count", "sample_wall_s": wall_tot,
+            "extrapolated_s": cpu_full / workers, "q_per_s": len(uq3) / (cpu_full / workers)}
+        log(f"cpu baseline c3: {n3} frequencies x {len(w3.strengths)} strengths in {wall_tot:.1f} s, "
+            f"extrapolated {cpu_full / workers:.1f} s")
+        del G3
+
+        # full frame: 2048 frequencies stratified by alias count, per method
+        uq, strata = stratified(w4, 2048, 4096)
         est = {}
         sample_n = sum(len(v[1]) for v in strata.values())
         for method in ("phase", "complex"):
@@ -281,7 +303,7 @@ def cpu_baseline(dsp, dev, w4, k4, G4, n_q: int, n_band: int, strength: float, w
         act5 = O.active_pixels(k5, w5.optics)
         act5_t = torch.as_tensor(act5, device=dev)
         ent = np.argwhere(O.band_mask(w5.n_scan, w5.step, w5.band))
-        for B, n_s in ((1, 2048), (8, 512)):
+        for B, n_s in ((1, 1024), (8, 256)):
             sel = ent[np.sort(np.random.default_rng(B).choice(len(ent), size=n_s, replace=False))]
             jobs = [("c5", B, sel[c0:c0 + 32], _gather(G5, act5_t, sel[c0:c0 + 32], dev), k5[act5],
                      np.ones(len(act5))) for c0 in range(0, n_s, 32)]
@@ -302,10 +324,11 @@ def cpu_baseline(dsp, dev, w4, k4, G4, n_q: int, n_band: int, strength: float, w
         pool.join()
     step_s = est["phase"] + est["complex"] + est["ssb1"]
     out["value"] = n_q / step_s
-    out["sample"] = (f"oracle on {workers} worker processes: c1, c2, c3 prepare + solve in full; the full frame's "
-                     f"phase and complex prepare + solve on {sample_n} of {n_q} frequencies stratified by alias "
-                     f"count and the one-set SSB sum on 2048 of {n_band} band entries, each extrapolated to the "
-                     f"whole workload; value = full-frame step rate (phase + complex + SSB)")
+    out["sample"] = (f"oracle on {workers} worker processes: c1 and c2 prepare + solve in full; c3's 32-strength "
+                     f"sweep and the full frame's phase and complex prepare + solve on samples of 2048 frequencies "
+                     f"stratified by alias count ({sample_n} of {n_q} for the full frame) and the SSB sum on 1024 "
+                     f"(one set) and 256 (eight sets) of {n_band} band entries, each extrapolated to the whole "
+                     f"workload; value = full-frame step rate (phase + complex + one-set SSB)")
     out["phase_prepare_q_per_s"] = n_q / est["phase"]
     return out
 
@@ -386,6 +409,50 @@ def ssb_sweep(dsp, dev, reps: int = 5):
         out["passes"][name] = {"ms": m, "q_sets_per_s": n_band * B / (m / 1e3), "g_GBps": gb / (m / 1e3) / 1e9}
         log(f"ssb B={name}: {m:.3f} ms")
     del G, h16
+    torch.cuda.empty_cache()
+    return out
+
+
+def c3_sweep(dsp, dev, reps: int = 3):
+    """The 256 x 256 strength sweep (phase method, upsampling 3): one prepare,
+    then solve + scatter at each of its 32 strengths; stream time per stage,
+    median over reps after one untimed call (layout built)."""
+    import numpy as np
+    import torch
+
+    from synthetic import bf_pixels, data_stack_torch, workload
+
+    w = workload("c3")
+    pix, k = bf_pixels(w)
+    log(f"generating sweep G {(len(k), w.n_scan, w.n_half)} on {dev}")
+    G = data_stack_torch(w, pix, dev)
+    sts = list(w.strengths)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    rows = []
+    for r in range(reps + 1):
+        ev[0].record(stream)
+        p = dsp.prepare(G, k, w.optics, step=w.step, upsampling=w.upsampling, method="phase",
+                        smoothness=w.smoothness)
+        ev[1].record(stream)
+        x = p.solve(sts)
+        ev[2].record(stream)
+        sc = p.scatter(x)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if r:
+            rows.append([ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3])])
+        n_q = p.info["n_q"]
+        del p, x, sc
+    med = np.median(np.asarray(rows), axis=0)
+    total = float(med.sum())
+    out = {"workload": f"256x256 scan, 0.373 A step, {len(k)} BF px, upsampling 3, phase method, "
+                       f"{len(sts)} strengths (1e-3 .. 10)",
+           "n_q": int(n_q), "strengths": len(sts), "prepare_ms": float(med[0]),
+           "solve_all_strengths_ms": float(med[1]), "scatter_all_strengths_ms": float(med[2]),
+           "total_ms": total, "q_per_s": n_q / (total / 1e3)}
+    log(f"c3 sweep: {out}")
+    del G
     torch.cuda.empty_cache()
     return out
 
@@ -629,6 +696,7 @@ def main(argv=None) -> int:
     torch.cuda.empty_cache()
     if not args.no_ssb_sweep:
         result["ssb_sweep"] = ssb_sweep(dsp, dev)
+        result["c3_sweep"] = c3_sweep(dsp, dev)
     print(json.dumps(result), flush=True)
     return 0
 

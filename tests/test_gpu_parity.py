@@ -1126,9 +1126,9 @@ def test_c5_ssb_eight_sets_sampled(c5_data):
     del Sg, Ng
 
 
-@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("B", [1, 2, 4])
 def test_c5_band_pass_sampled(c5_data, B):
-    """The one- and two-set band passes at full-frame size (the bench's timed
+X
     SSB pass is the one-set one) on sampled band entries, and each set's sums
     equal to the same set's in the eight-set pass (nested sets)."""
     w, k, G = c5_data
