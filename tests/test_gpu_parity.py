@@ -1128,8 +1128,8 @@ def test_c5_ssb_eight_sets_sampled(c5_data):
 
 @pytest.mark.parametrize("B", [1, 2, 4])
 def test_c5_band_pass_sampled(c5_data, B):
-X
-    SSB pass is the one-set one) on sampled band entries, and each set's sums
+    """The one-, two- and four-set band passes at full-frame size (the bench's
+    timed SSB pass is the one-set one) on sampled band entries, and each set's sums
     equal to the same set's in the eight-set pass (nested sets)."""
     w, k, G = c5_data
     sets = ssb_sets(w, B)
