@@ -19,18 +19,29 @@ constexpr int CHI_NCOEF = 28;
 
 __host__ __device__ constexpr int chi_off(int j) { return j * (2 * CHI_DEG + 3 - j) / 2; }
 
-// Horner in theta_x inside Horner in theta_y: 27 FMAs.
-__host__ __device__ inline double chi_poly(const double *__restrict__ c, double tx, double ty) {
-    double acc = c[chi_off(6)];
+// Horner in theta_x inside Horner in theta_y: 27 FMAs.  top[j] is row j's
+// leading coefficient, c[chi_off(j) + 6 - j] (chi_poly passes c's own; the
+// Gram kernels pass copies held in vector registers, so that no row's first
+// FMA has two scalar operands).
+__host__ __device__ inline double chi_poly_top(const double *__restrict__ c, const double *__restrict__ top,
+                                               double tx, double ty) {
+    double acc = top[6];
 #pragma unroll
     for (int j = 5; j >= 0; --j) {
         const double *cj = c + chi_off(j);
-        double h = cj[6 - j];
+        double h = top[j];
 #pragma unroll
         for (int i = 5 - j; i >= 0; --i) h = fma(h, tx, cj[i]);
         acc = fma(acc, ty, h);
     }
     return acc;
+}
+
+__host__ __device__ inline double chi_poly(const double *__restrict__ c, double tx, double ty) {
+    double top[CHI_DEG + 1];
+#pragma unroll
+    for (int j = 0; j <= CHI_DEG; ++j) top[j] = c[chi_off(j) + CHI_DEG - j];
+    return chi_poly_top(c, top, tx, ty);
 }
 
 // ---------------------------------------------------------------------------

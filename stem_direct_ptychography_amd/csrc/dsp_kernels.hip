@@ -281,7 +281,7 @@ struct GramPrefetch {
 // Waves per SIMD the compiler must fit (caps the registers per lane).
 template <int NJ, int METHOD>
 struct GramWaves {
-    static constexpr int value = METHOD == 2   ? (NJ <= 6 ? 4 : 3)
+    static constexpr int value = METHOD == 2   ? (NJ <= 5 ? 4 : 3)
                                  : METHOD == 0 ? (NJ <= 2 ? 4 : (NJ <= 4 ? 3 : (NJ <= 6 ? 2 : 1)))
                                                : (NJ <= 1 ? 4 : (NJ <= 2 ? 3 : (NJ <= 4 ? 2 : 1)));
 };
@@ -340,7 +340,7 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
                                            double (&acc)[GramShape<NJ, METHOD>::NACC], double2 *lpair, int yh, int ix,
                                            const int (&jyN)[NJ], const int (&jxN)[NJ], const bool (&act)[NJ],
                                            unsigned pm, double lky, double lkx, double amp0, double sw,
-                                           double chi0, const double *tay, float2 gv) {
+                                           double chi0, const double *tay, float2 gv, const double *ctop) {
     using Sh = GramShape<NJ, METHOD>;
     constexpr int NC = Sh::NC;
     const double ldq = prm.ldq, lrlim2 = prm.ap.lrlim2;
@@ -403,7 +403,7 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
             // L: chi(k) - chi(k - Q) (+ h); R: the negation of chi(k) - chi(k + Q) (+ h)
             if (zl) {
                 const double ty = py - Qy_s, tx = px - Qx_s;
-                double arg = chi0 - chi_poly(prm.op.chi_c, tx, ty), h = 0.0;
+                double arg = chi0 - chi_poly_top(prm.op.chi_c, ctop, tx, ty), h = 0.0;
                 if (DEPTH) {
                     h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
                     arg += h;
@@ -412,7 +412,7 @@ __device__ __forceinline__ void gram_pixel(const GramParams &prm, const double2 
             }
             if (zr) {
                 const double ty = py + Qy_s, tx = px + Qx_s;
-                double arg = chi0 - chi_poly(prm.op.chi_c, tx, ty), h = 0.0;
+                double arg = chi0 - chi_poly_top(prm.op.chi_c, ctop, tx, ty), h = 0.0;
                 if (DEPTH) {
                     h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
                     arg += h;
@@ -513,6 +513,20 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
     ConstPixel *pix = (ConstPixel *)prm.pix;
     ConstLong *goffs = (ConstLong *)prm.goff;
     const float2 *__restrict__ G = prm.G;
+    // the leading chi coefficients of rows 0..5 in VGPRs: from scalar
+    // registers each such row's first Horner FMA would have two scalar
+    // operands and need a copy (the empty asm hides that the values are
+    // uniform); row 6's single coefficient enters an FMA beside two VGPRs
+    // (not with the Taylor scheme, which does not evaluate the polynomial,
+    // nor in the three depth kernels where the 12 VGPRs would spill)
+    constexpr bool TOPV = !TAY && !(DEPTH && ((METHOD == 1 && NJ == 4) || (METHOD == 2 && (NJ == 5 || NJ == 9))));
+    double ctop[CHI_DEG + 1];
+#pragma unroll
+    for (int j = 0; j <= CHI_DEG; ++j) {
+        double v = prm.op.chi_c[chi_off(j) + CHI_DEG - j];
+        if (TOPV && j < CHI_DEG) asm volatile("" : "+v"(v));
+        ctop[j] = v;
+    }
     while (it < end) {
         const int t = (int)(it / n_pix);
         const int p0 = (int)(it - (long long)t * n_pix);
@@ -616,7 +630,7 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
                     const unsigned pm = prm.slot_test ? __builtin_amdgcn_readfirstlane(smask[r]) : ~0u;
                     gram_pixel<NJ, METHOD, DEPTH, TAY>(prm, T, acc, lpair, yh, ix, jyN, jxN, act, pm, srec[r].lky,
                                                        srec[r].lkx, srec[r].amp0, srec[r].sw, srec[r].chi0,
-                                                       stay + (TAY ? r * TAY_N : 0), gv);
+                                                       stay + (TAY ? r * TAY_N : 0), gv, ctop);
                 }
 #pragma unroll
                 for (int k = 0; k < PF; ++k) ga[k] = gb[k];
