@@ -316,8 +316,10 @@ dsp_status dsp_cache_get(dsp_cache *c, const void *G_c64_dev, unsigned long long
  *   G is read back as max(Q / 32767, -1) * s.
  * G_c64_dev: complex64 [n_bf][n_scan][n_scan/2+1]; Q_i16_dev: int16
  * [n_bf][n_scan][n_scan/2+1][2]; scale_dev: float [n_bf], or [n_bf][n_scan]
- * with row_scales; all device, caller-owned.  Runs on hip_stream.
- * DSP_EINVAL for NULL pointers, n_bf <= 0, odd or too small n_scan.
+ * with row_scales; all device, caller-owned, G 16-byte and Q 8-byte aligned
+ * (as any device allocation is).  Runs on hip_stream.
+ * DSP_EINVAL for NULL or misaligned pointers, n_bf <= 0, odd or too small
+ * n_scan.
  */
 dsp_status dsp_quantize_herm16(const void *G_c64_dev, int n_bf, int n_scan, int row_scales, void *Q_i16_dev,
                                float *scale_dev, void *hip_stream);

@@ -2600,6 +2600,9 @@ dsp_status dsp_quantize_herm16(const void *G_c64_dev, int n_bf, int n_scan, int 
     if (!G_c64_dev || !Q_i16_dev || !scale_dev) return fail(DSP_EINVAL, "G, Q and scale must be non-NULL");
     if (n_bf <= 0) return fail(DSP_EINVAL, "n_bf must be > 0");
     if (n_scan < 4 || (n_scan & 1)) return fail(DSP_EINVAL, "n_scan must be even and >= 4");
+    // the pack kernel reads two entries per 16-byte load and writes them in one 8-byte store
+    if ((uintptr_t)G_c64_dev % 16 || (uintptr_t)Q_i16_dev % 8)
+        return fail(DSP_EINVAL, "G must be 16-byte and Q 8-byte aligned");
     HIP_TRY(launch_herm16((const float2 *)G_c64_dev, n_bf, n_scan, n_scan / 2 + 1, row_scales != 0,
                           (short2 *)Q_i16_dev, scale_dev, (hipStream_t)hip_stream));
     return DSP_OK;

@@ -1511,22 +1511,40 @@ __global__ __launch_bounds__(256) void herm16_row_scale_kernel(const float2 *G, 
     if (lane == 0) scale[row] = (float)sqrt(m);
 }
 
-// grid-stride over the n_bf planes' entries; entry i uses scale[i / per]
-// (per = the plane, or the row for row scales)
-__global__ __launch_bounds__(256) void herm16_pack_kernel(const float2 *G, long long per, long long n,
-                                                          const float *scale, short2 *Q) {
+// One entry's codes (the reading the oracle fixes: FP64 quotient, clamp,
+// floor(0.5 + 32767 x); a zero scale packs zeros).
+__device__ __forceinline__ unsigned herm16_code(float re, float im, double s) {
 #pragma clang fp contract(off)
+    if (!(s > 0.0)) return 0u;
+    const double x = fmin(fmax((double)re / s, -1.0), 1.0), y = fmin(fmax((double)im / s, -1.0), 1.0);
+    const short qx = (short)floor(0.5 + 32767.0 * x), qy = (short)floor(0.5 + 32767.0 * y);
+    return (unsigned)(unsigned short)qx | ((unsigned)(unsigned short)qy << 16);
+}
+
+// Block row y (grid-stride) takes pixel plane p; its threads take pairs of
+// entries (one 16-byte load, one 8-byte store: a plane holds N (N/2 + 1)
+// entries, an even count, so pairs never straddle planes and stay aligned).
+// With row scales an entry e of the plane uses row e / nh's scale.
+template <bool ROWS>
+__global__ __launch_bounds__(256) void herm16_pack_kernel(const float2 *G, long long plane, int N, int nh, int n_bf,
+                                                          const float *scale, short2 *Q) {
+    const long long npair = plane / 2;
     const long long stride = (long long)gridDim.x * blockDim.x;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const double s = scale[i / per];
-        const float2 v = G[i];
-        short2 q = make_short2(0, 0);
-        if (s > 0.0) {
-            const double x = fmin(fmax((double)v.x / s, -1.0), 1.0), y = fmin(fmax((double)v.y / s, -1.0), 1.0);
-            q.x = (short)floor(0.5 + 32767.0 * x);
-            q.y = (short)floor(0.5 + 32767.0 * y);
+    for (int p = blockIdx.y; p < n_bf; p += gridDim.y) {
+        const float4 *Gp = (const float4 *)(G + (size_t)p * plane);
+        uint2 *Qp = (uint2 *)(Q + (size_t)p * plane);
+        const double sp = ROWS ? 0.0 : (double)scale[p];
+        const float *srow = scale + (size_t)p * N;
+        for (long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x; j < npair; j += stride) {
+            const float4 v = Gp[j];
+            double s0 = sp, s1 = sp;
+            if (ROWS) {
+                const unsigned e = (unsigned)(2 * j);
+                s0 = (double)srow[e / (unsigned)nh];
+                s1 = (double)srow[(e + 1u) / (unsigned)nh];
+            }
+            Qp[j] = make_uint2(herm16_code(v.x, v.y, s0), herm16_code(v.z, v.w, s1));
         }
-        Q[i] = q;
     }
 }
 
@@ -2009,10 +2027,12 @@ hipError_t launch_herm16(const float2 *G, int n_bf, int N, int nh, bool rows, sh
         herm16_scale_kernel<<<n_bf, 256, 0, st>>>(G, plane, scale);
     }
     DSP_CHECK_LAUNCH();
-    const long long n = (long long)n_bf * plane;
-    const long long blocks = (n + 255) / 256;
-    herm16_pack_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, st>>>(G, rows ? nh : plane, n, scale,
-                                                                                     Q);
+    // pairs per plane over blocks of 256 threads, about 8 pairs per thread
+    const long long npair = plane / 2;
+    const unsigned bx = (unsigned)std::max<long long>(1, std::min<long long>((npair + 2047) / 2048, 4096));
+    const dim3 grid(bx, (unsigned)std::min(n_bf, 65535));
+    if (rows) herm16_pack_kernel<true><<<grid, 256, 0, st>>>(G, plane, N, nh, n_bf, scale, Q);
+    else herm16_pack_kernel<false><<<grid, 256, 0, st>>>(G, plane, N, nh, n_bf, scale, Q);
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }
