@@ -2178,8 +2178,11 @@ static dsp_status ssb_pass(const SsbLayout &L, const SsbDevTables &dt, const dsp
     for (int b = 0; b < B; ++b) {
         const OpticsDev od = make_optics_dev(sets_host + b);
         // the pixel records once (set 0 writes them), the Taylor table per set
-        double *tb = bufs.tay + (size_t)b * n_pix * TAY_N;
-        HIP_TRY(launch_pixel_terms(dt.pixbase, b == 0 ? bufs.pix : nullptr, n_pix, apd, od, nullptr, 0, tb, stream));
+        // (the eight-set kernel computes its own: no tables)
+        double *tb = ssb_maxb(B) >= 8 ? nullptr : bufs.tay + (size_t)b * n_pix * TAY_N;
+        if (b == 0 || tb)
+            HIP_TRY(launch_pixel_terms(dt.pixbase, b == 0 ? bufs.pix : nullptr, n_pix, apd, od, nullptr, 0, tb,
+                                       stream));
         sp.tau_y[b] = od.tau_y;
         sp.tau_x[b] = od.tau_x;
         sp.pt2[b] = od.pt2;

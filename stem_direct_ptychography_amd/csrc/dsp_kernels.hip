@@ -1293,8 +1293,26 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
     __shared__ long long sgoff[CHK + PF];
     __shared__ long long sgrow[H16 == 2 ? CHK + PF : 1];   // pixel index x N (row scales)
     __shared__ double stay[MAXB * CHK * TAY_N];   // [set][pixel][TAY_N]
+    // With eight sets the chunk's Taylor coefficients are computed in the
+    // staging step, one lane per (set, pixel), from the sets' chi and tilt
+    // copied to LDS here: reading them from the tables made every tile's wave
+    // fetch 1280 bytes per pixel and wait for them at each chunk (12.3 ->
+    // 11.1 ms on the 512 x 512 band).  With four, the shift's registers cost
+    // a wave per SIMD (5.3 -> 5.7 ms), so fewer sets read the tables.
+    constexpr bool TAYIN = MAXB >= 8;
+    constexpr int CSTR = CHI_NCOEF + 2;
+    __shared__ double schi[TAYIN ? MAXB * CSTR : 1];   // [set]: chi's coefficients, tau_y, tau_x
     const int lane = threadIdx.x;
     for (int i = lane; i < TRIG_N; i += 64) T[i] = prm.trig[i];
+    if (TAYIN && lane == 0) {
+#pragma unroll
+        for (int b = 0; b < MAXB; ++b) {
+#pragma unroll
+            for (int i = 0; i < CHI_NCOEF; ++i) schi[b * CSTR + i] = prm.chi_c[b][i];
+            schi[b * CSTR + CHI_NCOEF] = prm.tau_y[b];
+            schi[b * CSTR + CHI_NCOEF + 1] = prm.tau_x[b];
+        }
+    }
 
     const int wv = blockIdx.x;
     const long long n_pix = prm.n_pix;
@@ -1350,7 +1368,24 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
                 z.lky = z.lkx = z.amp0 = z.sw = z.chi0 = z.pad = 0.0;
                 srec[lane] = z;
             }
-            {
+            if (TAYIN) {
+                // lane = (set b, pixel c) of the chunk; theta(k) = lambda k + tau
+                // formed as in the pixel-terms kernel (a rounded add)
+                if (lane < MAXB * CHK) {
+                    const int b = lane / CHK, c = lane - b * CHK;
+                    double t[TAY_N];
+                    if (b < prm.B && c < cn) {
+                        const double *cb = schi + b * CSTR;
+                        const double lky = pix[c0 + c].lky, lkx = pix[c0 + c].lkx;
+                        chi_taylor(cb, lkx + cb[CHI_NCOEF + 1], lky + cb[CHI_NCOEF], t);
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < TAY_N; ++m) t[m] = 0.0;
+                    }
+#pragma unroll
+                    for (int m = 0; m < TAY_N; ++m) stay[(b * CHK + c) * TAY_N + m] = t[m];
+                }
+            } else {
                 // set b's table starts at b n_pix TAY_N
 #pragma unroll
                 for (int b = 0; b < MAXB; ++b) {
