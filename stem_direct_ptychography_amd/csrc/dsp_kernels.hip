@@ -16,9 +16,11 @@
 // almost never diverge because neighbouring frequencies see nearly the same
 // lens; each lane keeps its own frequency's sums, so there is no cross-lane
 // reduction.  While a chunk of pixels is staged, a wave-uniform test against
-// the tile's centre and radius marks the alias slots (and, in the one-set SSB
-// kernel, the pixels) that no lane can have in support; they are skipped
-// with scalar branches.  The tiles x pixels of a launch are split into
+// the tile's centre and radius marks the alias slots that no lane can have
+// in support; they are skipped with scalar branches.  The upsampled preview
+// runs the same kernel with right sides only: a lane's slots are the fine
+// frequencies that read its stored G value ("Historical WebGPU G(q,k) memory
+// experiment", section "Object-redraw fast path").  The tiles x pixels of a launch are split into
 // equal-cost contiguous ranges (stream-K, costed per iteration by the same
 // test on the host), eight per resident wave slot; partial sums are added
 // per tile in a fixed order afterwards (deterministic).
@@ -1373,17 +1375,15 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
                 // formed as in the pixel-terms kernel (a rounded add)
                 if (lane < MAXB * CHK) {
                     const int b = lane / CHK, c = lane - b * CHK;
-                    double t[TAY_N];
+                    double *ts = stay + (b * CHK + c) * TAY_N;   // written in place
                     if (b < prm.B && c < cn) {
                         const double *cb = schi + b * CSTR;
                         const double lky = pix[c0 + c].lky, lkx = pix[c0 + c].lkx;
-                        chi_taylor(cb, lkx + cb[CHI_NCOEF + 1], lky + cb[CHI_NCOEF], t);
+                        chi_taylor(cb, lkx + cb[CHI_NCOEF + 1], lky + cb[CHI_NCOEF], ts);
                     } else {
 #pragma unroll
-                        for (int m = 0; m < TAY_N; ++m) t[m] = 0.0;
+                        for (int m = 0; m < TAY_N; ++m) ts[m] = 0.0;
                     }
-#pragma unroll
-                    for (int m = 0; m < TAY_N; ++m) stay[(b * CHK + c) * TAY_N + m] = t[m];
                 }
             } else {
                 // set b's table starts at b n_pix TAY_N
