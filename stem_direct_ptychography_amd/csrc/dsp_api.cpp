@@ -627,6 +627,32 @@ dsp_status trig_table_device(int device, const double2 **out) {
     return DSP_OK;
 }
 
+// e^{+2 pi i m / N} for m < N/2 (the fused loss transforms), from long
+// double on the host, one device table per (device, N) kept for the process.
+dsp_status twiddle_table_device(int device, int N, const double2 **out) {
+    static std::mutex mu;
+    static std::map<std::pair<int, int>, double2 *> tables;
+    std::lock_guard<std::mutex> lock(mu);
+    const auto key = std::make_pair(device, N);
+    auto f = tables.find(key);
+    if (f != tables.end()) {
+        *out = f->second;
+        return DSP_OK;
+    }
+    std::vector<double2> host((size_t)N / 2);
+    const long double two_pi = 6.283185307179586476925286766559005768L;
+    for (int m = 0; m < N / 2; ++m) {
+        const long double a = two_pi * (long double)m / (long double)N;
+        host[(size_t)m] = make_double2((double)cosl(a), (double)sinl(a));
+    }
+    double2 *d = nullptr;
+    HIP_TRY(hipMalloc((void **)&d, host.size() * sizeof(double2)));
+    HIP_TRY(hipMemcpy(d, host.data(), host.size() * sizeof(double2), hipMemcpyHostToDevice));
+    tables[key] = d;
+    *out = d;
+    return DSP_OK;
+}
+
 // Scratch memory per (device, stream) for temporaries that live within one
 // call (Gram partial sums, SSB per-call tables).  Work on one stream runs in
 // order, so consecutive calls can reuse the same bytes; the arena only grows
@@ -2546,25 +2572,36 @@ dsp_status dsp_loss(const void *G_c64_dev, int n_bf, const double *bf_coords_hos
     double W = 0.0;
     for (const PixelBase &p : L.act.pix) W += p.w;
     if (!(W > 0.0)) return fail(DSP_EINVAL, "the active pixels' weights sum to zero");
-    // chunk of pixels per inverse-FFT batch: about 1 GB of planes
-    const size_t per_pix = (size_t)plane * sizeof(double2) + (size_t)nn * sizeof(double);
+    // power-of-two N up to 1024: the fused transforms (the column pass
+    // computes the corrected values, the row pass the phase moments); else
+    // the corrected planes, hipFFT's inverse real transform and the moments
+    const bool fused = N >= 8 && N <= 1024 && (N & (N - 1)) == 0;
+    // chunk of pixels per batch: about 1 GB of planes (and real images)
+    const size_t per_pix = (size_t)plane * sizeof(double2) + (fused ? 0 : (size_t)nn * sizeof(double));
     const int CH = (int)std::max<size_t>(1, std::min<size_t>(256, ((size_t)1 << 30) / per_pix));
+    // fused: pixel groups of the row pass (about 4096 blocks of rows), each
+    // with partial moment planes
+    const int NG = fused ? std::max(1, std::min(CH, 4096 / (N / 2))) : 0;
     const int nb = loss_blocks(nn);
     const size_t need = carve_size(n_pix, sizeof(PixelRec)) + carve_size((size_t)CH * plane, sizeof(double2)) +
-                        carve_size((size_t)CH * nn, sizeof(double)) + carve_size(CH, sizeof(double2)) +
+                        carve_size(fused ? 1 : (size_t)CH * nn, sizeof(double)) + carve_size(CH, sizeof(double2)) +
                         2 * carve_size((size_t)nn, sizeof(double)) + carve_size(nb, sizeof(double)) +
-                        carve_size(1, sizeof(double));
+                        carve_size(1, sizeof(double)) + 2 * carve_size(std::max<size_t>(1, (size_t)NG * nn), sizeof(double));
     char *scr = nullptr;
     if ((st = arena_get(device, stream, need, &scr))) return st;
     Carve cv{scr};
     PixelRec *d_pix = cv.take<PixelRec>(n_pix);
     double2 *d_H = cv.take<double2>((size_t)CH * plane);
-    double *d_img = cv.take<double>((size_t)CH * nn);
+    double *d_img = cv.take<double>(fused ? 1 : (size_t)CH * nn);
     double2 *d_D = cv.take<double2>(CH);
     double *d_s1 = cv.take<double>((size_t)nn);
     double *d_s2 = cv.take<double>((size_t)nn);
     double *d_part = cv.take<double>(nb);
     double *d_loss = cv.take<double>(1);
+    double *d_s1p = cv.take<double>(std::max<size_t>(1, (size_t)NG * nn));
+    double *d_s2p = cv.take<double>(std::max<size_t>(1, (size_t)NG * nn));
+    const double2 *d_tw = nullptr;
+    if (fused && (st = twiddle_table_device(device, N, &d_tw))) return st;
     const ApertureDev apd = make_aperture_dev(optics);
     const OpticsDev opd = make_optics_dev(optics);
     HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, opd, nullptr, 0, nullptr, stream));
@@ -2586,6 +2623,11 @@ dsp_status dsp_loss(const void *G_c64_dev, int n_bf, const double *bf_coords_hos
         cp.pix = d_pix + c0;
         cp.goff = L.d_goff + c0;
         cp.n_valid = cn;
+        if (fused) {
+            HIP_TRY(launch_loss_fused(cp, d_tw, cn, L.d_pixbase + c0, std::min(NG, cn), d_s1p, d_s2p, d_s1, d_s2,
+                                      stream));
+            continue;
+        }
         HIP_TRY(launch_corrected_half(cp, CH, stream));
         if ((st = fft_z2d(device, N, CH, d_H, d_img, stream))) return st;
         HIP_TRY(launch_phase_moments(d_img, d_D, L.d_pixbase + c0, cn, nn, d_s1, d_s2, stream));

@@ -1638,29 +1638,11 @@ __global__ __launch_bounds__(256) void preview_phase_kernel(double *img, long lo
 // sqrt(w_k), which the phase does not see: H_k(q) = conj(Gamma'(q, k)) G(q, k)
 // with Gamma' = sqrt(w) Gamma = i (L - R) built on amp0 = sqrt(w) a(k), and
 // D_k = sqrt(w) G(0, k).  H is 0 at DC and on the Nyquist row and column.
-__global__ __launch_bounds__(256) void corrected_half_kernel(CorrParams prm) {
-    __shared__ double2 T[TRIG_N];
-    if (threadIdx.x < TRIG_N) T[threadIdx.x] = prm.trig[threadIdx.x];
-    __syncthreads();
-    const int j = blockIdx.y;
-    const int N = prm.N, nh = prm.nh;
-    const long long plane = (long long)N * nh;
-    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (e >= plane) return;
-    double2 *Hj = prm.H + (size_t)j * plane;
-    if (j >= prm.n_valid) {
-        Hj[e] = make_double2(0.0, 0.0);
-        if (e == 0) prm.D[j] = make_double2(0.0, 0.0);
-        return;
-    }
-    const PixelRec rec = prm.pix[j];
-    const float2 gv = prm.G[prm.goff[j] + e];
-    const int iy = (int)(e / nh), ix = (int)(e - (long long)iy * nh);
-    if (e == 0) prm.D[j] = make_double2(rec.sw * (double)gv.x, rec.sw * (double)gv.y);
-    if (e == 0 || iy == N / 2 || ix == N / 2) {
-        Hj[e] = make_double2(0.0, 0.0);
-        return;
-    }
+// H_k(q) at stored entry (iy, ix) != DC, off the Nyquist row and column,
+// for the pixel record rec and its stored value gv.
+__device__ __forceinline__ double2 corrected_value(const CorrParams &prm, const double2 *T, const PixelRec &rec,
+                                                   float2 gv, int iy, int ix) {
+    const int N = prm.N;
     const int yh = iy < N / 2 ? iy : iy - N;
     const double qy = (double)yh * prm.ldq, qx = (double)ix * prm.ldq;   // lambda q
     const double lky = rec.lky, lkx = rec.lkx;
@@ -1706,7 +1688,186 @@ __global__ __launch_bounds__(256) void corrected_half_kernel(CorrParams prm) {
     }
     const double gmr = Ri - Li, gmi = Lr - Rr;   // Gamma' = i (L - R)
     const double gr = gv.x, gi = gv.y;
-    Hj[e] = make_double2(fma(gmr, gr, gmi * gi), fma(gmr, gi, -(gmi * gr)));
+    return make_double2(fma(gmr, gr, gmi * gi), fma(gmr, gi, -(gmi * gr)));
+}
+
+__global__ __launch_bounds__(256) void corrected_half_kernel(CorrParams prm) {
+    __shared__ double2 T[TRIG_N];
+    if (threadIdx.x < TRIG_N) T[threadIdx.x] = prm.trig[threadIdx.x];
+    __syncthreads();
+    const int j = blockIdx.y;
+    const int N = prm.N, nh = prm.nh;
+    const long long plane = (long long)N * nh;
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= plane) return;
+    double2 *Hj = prm.H + (size_t)j * plane;
+    if (j >= prm.n_valid) {
+        Hj[e] = make_double2(0.0, 0.0);
+        if (e == 0) prm.D[j] = make_double2(0.0, 0.0);
+        return;
+    }
+    const PixelRec rec = prm.pix[j];
+    const float2 gv = prm.G[prm.goff[j] + e];
+    const int iy = (int)(e / nh), ix = (int)(e - (long long)iy * nh);
+    if (e == 0) prm.D[j] = make_double2(rec.sw * (double)gv.x, rec.sw * (double)gv.y);
+    if (e == 0 || iy == N / 2 || ix == N / 2) {
+        Hj[e] = make_double2(0.0, 0.0);
+        return;
+    }
+    Hj[e] = corrected_value(prm, T, rec, gv, iy, ix);
+}
+
+// ---------------------------------------------------------------------------
+// loss path, fused form for power-of-two N <= 1024: the inverse real 2D
+// transform split into a column pass (complex, along iy, for each stored
+// column ix) that computes the corrected values itself, and a row pass (the
+// real transform of each row's half spectrum) that goes straight on to the
+// phases and their moments; neither the corrected planes nor the real images
+// make a round trip through HBM.  Both passes are in-place iterative radix-2
+// transforms in LDS (bit-reversed load, natural-order result) with the
+// twiddles e^{+2 pi i m / N}, m < N/2, from a host table in long double.
+// ---------------------------------------------------------------------------
+constexpr int LOSS_E = 2048;   // complex values a column-pass block holds (N x columns)
+
+__device__ __forceinline__ void fft_inverse_inplace(double2 *A, int ncol, int N, int logN, const double2 *tw) {
+    // ncol independent length-N columns at A + c N, already in bit-reversed order
+    const int nb = ncol * (N >> 1);   // butterflies per stage
+    for (int s = 1; s <= logN; ++s) {
+        const int half = 1 << (s - 1);
+        const int tstep = N >> s;     // twiddle index step: e^{2 pi i pos / len} = tw[pos N / len]
+        for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+            const int c = b >> (logN - 1);
+            const int bb = b & ((N >> 1) - 1);
+            const int pos = bb & (half - 1);
+            const int i = c * N + ((bb - pos) << 1) + pos;
+            const int k = i + half;
+            const double2 w = tw[pos * tstep];
+            const double2 u = A[i], x = A[k];
+            const double2 v = make_double2(fma(x.x, w.x, -(x.y * w.y)), fma(x.x, w.y, x.y * w.x));
+            A[i] = make_double2(u.x + v.x, u.y + v.y);
+            A[k] = make_double2(u.x - v.x, u.y - v.y);
+        }
+        __syncthreads();
+    }
+}
+
+// Block (column block, pixel j of the chunk): columns ix0 .. ix0 + cw - 1 of
+// H_j over all N rows, transformed along iy: Y_j(y, ix) = sum_iy H_j(iy, ix)
+// e^{+2 pi i iy y / N}.  The block at ix0 = 0 also writes D_j.
+__global__ __launch_bounds__(256) void loss_column_kernel(CorrParams prm, const double2 *tw, int logN, int cw) {
+    extern __shared__ double2 lds[];
+    double2 *T = lds;                         // [TRIG_N]
+    double2 *W = T + TRIG_N;                  // [N/2]
+    double2 *A = W + (prm.N >> 1);            // [cw][N]
+    const int N = prm.N, nh = prm.nh;
+    for (int i = threadIdx.x; i < TRIG_N; i += blockDim.x) T[i] = prm.trig[i];
+    for (int i = threadIdx.x; i < (N >> 1); i += blockDim.x) W[i] = tw[i];
+    const int j = blockIdx.y;
+    const int ix0 = blockIdx.x * cw;
+    const PixelRec rec = prm.pix[j];
+    const float2 *Gj = prm.G + prm.goff[j];
+    if (ix0 == 0 && threadIdx.x == 0) {
+        const float2 g0 = Gj[0];
+        prm.D[j] = make_double2(rec.sw * (double)g0.x, rec.sw * (double)g0.y);
+    }
+    __syncthreads();
+    const int n = N * cw;
+    for (int e = threadIdx.x; e < n; e += blockDim.x) {
+        const int iy = e / cw, c = e - iy * cw, ix = ix0 + c;
+        double2 h = make_double2(0.0, 0.0);
+        if (ix < nh && !(iy == 0 && ix == 0) && iy != N / 2 && ix != N / 2)
+            h = corrected_value(prm, T, rec, Gj[(size_t)iy * nh + ix], iy, ix);
+        A[c * N + (int)(__brev((unsigned)iy) >> (32 - logN))] = h;
+    }
+    __syncthreads();
+    fft_inverse_inplace(A, cw, N, logN, W);
+    double2 *Yj = prm.H + (size_t)j * N * nh;
+    for (int e = threadIdx.x; e < n; e += blockDim.x) {
+        const int y = e / cw, c = e - y * cw, ix = ix0 + c;
+        if (ix < nh) Yj[(size_t)y * nh + ix] = A[c * N + y];
+    }
+}
+
+// Block (row pair p, pixel group g): rows p and p + N/2 of every pixel j = g,
+// g + ng, ... of the chunk.  The two rows' half spectra, each extended by
+// X(N - kx) = conj X(kx), go into one complex transform as a + i b (both
+// images are real), so its real part is row p's image and its imaginary part
+// row p + N/2's.  theta = atan2(img + Im D_j, Re D_j); the block adds
+// w_j theta and w_j theta^2 per position over its pixels in order and writes
+// them to its group's partial planes.
+__global__ __launch_bounds__(256) void loss_row_kernel(const double2 *Y, const double2 *D, const PixelBase *pb,
+                                                       int cn, int N, int nh, const double2 *tw, int logN, int ng,
+                                                       double *s1p, double *s2p) {
+    extern __shared__ double2 lds[];
+    double2 *W = lds;              // [N/2]
+    double2 *Z = W + (N >> 1);     // [N]
+    for (int i = threadIdx.x; i < (N >> 1); i += blockDim.x) W[i] = tw[i];
+    const int p = blockIdx.x, g = blockIdx.y;
+    const int ya = p, yb = p + (N >> 1);
+    constexpr int MAXP = 1024 / 256;   // positions per thread and row (N <= 1024)
+    double a1[2 * MAXP], a2[2 * MAXP];
+#pragma unroll
+    for (int m = 0; m < 2 * MAXP; ++m) a1[m] = a2[m] = 0.0;
+    const size_t plane = (size_t)N * nh;
+    for (int j = g; j < cn; j += ng) {
+        const double2 *Ya = Y + (size_t)j * plane + (size_t)ya * nh, *Yb = Y + (size_t)j * plane + (size_t)yb * nh;
+        __syncthreads();   // the previous pixel's transform is read
+        for (int kx = threadIdx.x; kx < N; kx += blockDim.x) {
+            double2 a, b;
+            if (kx <= (N >> 1)) {
+                a = Ya[kx];
+                b = Yb[kx];
+            } else {
+                a = Ya[N - kx];
+                b = Yb[N - kx];
+                a.y = -a.y;
+                b.y = -b.y;
+            }
+            Z[(int)(__brev((unsigned)kx) >> (32 - logN))] = make_double2(a.x - b.y, a.y + b.x);
+        }
+        __syncthreads();
+        fft_inverse_inplace(Z, 1, N, logN, W);
+        const double2 d = D[j];
+        const double w = pb[j].w;
+#pragma unroll
+        for (int m = 0; m < MAXP; ++m) {
+            const int x = threadIdx.x + m * 256;
+            if (x < N) {
+                const double2 z = Z[x];
+                const double ta = atan2(z.x + d.y, d.x), tb = atan2(z.y + d.y, d.x);
+                a1[m] = fma(w, ta, a1[m]);
+                a2[m] = fma(w * ta, ta, a2[m]);
+                a1[MAXP + m] = fma(w, tb, a1[MAXP + m]);
+                a2[MAXP + m] = fma(w * tb, tb, a2[MAXP + m]);
+            }
+        }
+    }
+    const size_t nn = (size_t)N * N;
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+        const int x = threadIdx.x + m * 256;
+        if (x < N) {
+            s1p[(size_t)g * nn + (size_t)ya * N + x] = a1[m];
+            s2p[(size_t)g * nn + (size_t)ya * N + x] = a2[m];
+            s1p[(size_t)g * nn + (size_t)yb * N + x] = a1[MAXP + m];
+            s2p[(size_t)g * nn + (size_t)yb * N + x] = a2[MAXP + m];
+        }
+    }
+}
+
+// s1 += the groups' partials, in group order (deterministic)
+__global__ __launch_bounds__(256) void loss_groups_kernel(const double *s1p, const double *s2p, int ng, long long nn,
+                                                          double *s1, double *s2) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long r = (long long)blockIdx.x * blockDim.x + threadIdx.x; r < nn; r += stride) {
+        double a = s1[r], b = s2[r];
+        for (int g = 0; g < ng; ++g) {
+            a += s1p[(size_t)g * nn + r];
+            b += s2p[(size_t)g * nn + r];
+        }
+        s1[r] = a;
+        s2[r] = b;
+    }
 }
 
 // r over the N^2 scan positions: theta_j = atan2(img_j[r] + Im D_j, Re D_j)
@@ -2099,6 +2260,28 @@ hipError_t launch_preview_phase(double *img, long long n, const double2 *dc, hip
 hipError_t launch_corrected_half(const CorrParams &prm, int n_planes, hipStream_t st) {
     const long long plane = (long long)prm.N * prm.nh;
     corrected_half_kernel<<<dim3((unsigned)((plane + 255) / 256), (unsigned)n_planes), 256, 0, st>>>(prm);
+    DSP_CHECK_LAUNCH();
+    return hipSuccess;
+}
+
+int loss_fused_cols(int N) { return std::max(1, std::min(LOSS_E / N, N / 2 + 1)); }
+
+hipError_t launch_loss_fused(const CorrParams &prm, const double2 *tw, int cn, const PixelBase *pb, int ng,
+                             double *s1p, double *s2p, double *s1, double *s2, hipStream_t st) {
+    const int N = prm.N, nh = prm.nh;
+    int logN = 0;
+    while ((1 << logN) < N) ++logN;
+    if ((1 << logN) != N || N < 8 || N > 1024 || cn <= 0 || ng <= 0) return hipErrorInvalidValue;
+    const int cw = loss_fused_cols(N);
+    const size_t lds_a = (size_t)(TRIG_N + N / 2 + cw * N) * sizeof(double2);
+    loss_column_kernel<<<dim3((unsigned)((nh + cw - 1) / cw), (unsigned)cn), 256, lds_a, st>>>(prm, tw, logN, cw);
+    DSP_CHECK_LAUNCH();
+    const size_t lds_b = (size_t)(N / 2 + N) * sizeof(double2);
+    loss_row_kernel<<<dim3((unsigned)(N / 2), (unsigned)ng), 256, lds_b, st>>>(prm.H, prm.D, pb, cn, N, nh, tw, logN,
+                                                                                ng, s1p, s2p);
+    DSP_CHECK_LAUNCH();
+    const long long nn = (long long)N * N;
+    loss_groups_kernel<<<grid_blocks(nn), 256, 0, st>>>(s1p, s2p, ng, nn, s1, s2);
     DSP_CHECK_LAUNCH();
     return hipSuccess;
 }
