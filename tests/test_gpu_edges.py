@@ -1,6 +1,7 @@
 """GPU tests at the limits: the alias-slot maximum, a bright-field set with no
-active pixel, and the largest supported scan (N = 8192) against the oracle on
-sampled outputs and exact properties."""
+active pixel, the largest supported scan (N = 8192) against the oracle on
+sampled outputs and exact properties, and the loss path's fused transforms
+at their smallest and largest scans."""
 import math
 
 import numpy as np
@@ -168,3 +169,24 @@ def test_largest_scan():
     assert float(torch.max(torch.abs(m3 - want))) <= 1e-12
     del G, m3, ms
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n", [8, 1024])
+def test_loss_fused_transform_limits(n):
+    """The loss path's fused transforms at their smallest and largest
+    power-of-two scans (N = 8 and 1024; other N take hipFFT's transform),
+    three pixels of real intensity traces with a bright mean, against the
+    oracle's mean phase image and loss."""
+    step = 0.373 if n > 8 else 0.9
+    opt = _optics(soft=True, det_step=0.02819)
+    k = _pixels(opt, 3, 11)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(12 + n)
+    G = torch.fft.rfft2(50.0 + torch.randn((3, n, n), generator=gen, device=DEV)).contiguous()
+    _say(f"loss at N = {n}: three pixels against the oracle")
+    mp, loss = dsp.loss(G, k, opt, step=step)
+    torch.cuda.synchronize()
+    mp_o, loss_o = O.loss_path(G.cpu().numpy().astype(np.complex128), k, None, n, step, opt)
+    assert np.max(np.abs(mp.cpu().numpy() - mp_o)) <= 1e-9
+    assert loss == pytest.approx(loss_o, rel=1e-9, abs=1e-15)
+    assert np.std(mp_o) > 1e-4
