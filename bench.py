@@ -333,6 +333,52 @@ def cpu_baseline(dsp, dev, w4, k4, G4, n_q: int, n_band: int, strength: float, w
     return out
 
 
+def cpu_full_frame(dev, workers: int):
+    """The oracle's phase and complex prepare + solve over all 130,560
+    frequencies of the full frame (not a sample), in batches of 8192 over the
+    same worker pool; checks the stratified extrapolation that cpu_baseline
+    reports.  One JSON line; minutes of host time, so not part of a default
+    run."""
+    import multiprocessing as mp
+
+    import torch
+
+    from oracle import dsp_oracle as O
+    from synthetic import bf_pixels, data_stack_torch, workload
+
+    w = workload("c4")
+    pix, k = bf_pixels(w)
+    log(f"generating G {(len(k), w.n_scan, w.n_half)} on {dev}")
+    G = data_stack_torch(w, pix, dev)
+    torch.cuda.synchronize()
+    act = O.active_pixels(k, w.optics)
+    ka, wa = k[act], np.ones(len(act))
+    act_t = torch.as_tensor(act, device=dev)
+    uq = O.unique_frequencies(w.n_scan)
+    out = {"kind": "oracle", "workload": "c4 full frame, every frequency", "cores": workers,
+           "cpu_model": _cpu_model(), "n_q": len(uq), "methods": {}}
+    ctx = mp.get_context("spawn")
+    pool = ctx.Pool(workers)
+    try:
+        pool.map(abs, range(4 * workers))
+        for method, st in (("phase", 1e-2), ("complex", (1e-2, 1e-2))):
+            busy_tot, t0 = 0.0, time.perf_counter()
+            for b0 in range(0, len(uq), 8192):
+                qb = uq[b0:b0 + 8192]
+                jobs = [("c4", method, qb[c0:c0 + 32], _gather(G, act_t, qb[c0:c0 + 32], dev), ka, wa, [st])
+                        for c0 in range(0, len(qb), 32)]
+                busy_tot += sum(pool.map(_oracle_prepare_chunk, jobs, chunksize=1))
+                log(f"oracle {method}: {b0 + len(qb)} of {len(uq)} frequencies")
+            wall = time.perf_counter() - t0
+            out["methods"][method] = {"wall_s": wall, "busy_per_worker_s": busy_tot / workers,
+                                      "q_per_s": len(uq) / (busy_tot / workers)}
+    finally:
+        pool.close()
+        pool.join()
+    del G
+    return out
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -471,6 +517,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-workers", type=int, default=0,
                     help="oracle worker processes (default: every core of this process's affinity set)")
     ap.add_argument("--no-ssb-sweep", action="store_true")
+    ap.add_argument("--cpu-full-frame", action="store_true",
+                    help="only time the oracle over every full-frame frequency (minutes of host time) and exit")
     ap.add_argument("--copy-probe", type=float, default=0.0,
                     help="only run a plain device copy of this many GiB (counter calibration) and exit")
     args = ap.parse_args(argv)
@@ -496,6 +544,11 @@ def main(argv=None) -> int:
         b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4}))
+        return 0
+
+    if args.cpu_full_frame:
+        workers = args.cpu_workers or len(os.sched_getaffinity(0))
+        print(json.dumps(cpu_full_frame(dev, workers)), flush=True)
         return 0
 
     import stem_direct_ptychography_amd as dsp
