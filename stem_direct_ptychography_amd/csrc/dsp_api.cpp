@@ -1066,6 +1066,8 @@ struct SsbLayout {
     size_t scratch_need[4] = {0, 0, 0, 0};   // noalloc: scratch bytes of a pass (0: does not fit)
     double host_ms = 0.0;
     ~SsbLayout() {
+        // an allocation-free pass's layout holds no device memory: no HIP call
+        if (key.noalloc) return;
         hipSetDevice(key.device);
         hipFree(d_pixbase);
         hipFree(d_goff);
@@ -1213,21 +1215,27 @@ dsp_status build_ssb_layout(const SsbKey &key, const dsp_optics *optics, const d
 // front = most recent (under g_layout_mu); never destroyed, like g_layouts
 std::vector<std::shared_ptr<SsbLayout>> &g_ssb_layouts = *new std::vector<std::shared_ptr<SsbLayout>>();
 
+// The allocation-free pass's layouts (host tables only) have a cache of
+// their own: inserting one never evicts, and so never frees, a layout that
+// holds device memory.
+std::vector<std::shared_ptr<SsbLayout>> &g_ssb_noalloc_layouts = *new std::vector<std::shared_ptr<SsbLayout>>();
+
 dsp_status get_ssb_layout(const SsbKey &key, const dsp_optics *optics, const double *coords, const double *weights,
                           std::shared_ptr<SsbLayout> &out) {
     std::lock_guard<std::mutex> lock(g_layout_mu);
-    for (size_t i = 0; i < g_ssb_layouts.size(); ++i) {
-        if (g_ssb_layouts[i]->key == key) {
-            out = g_ssb_layouts[i];
-            g_ssb_layouts.erase(g_ssb_layouts.begin() + i);
-            g_ssb_layouts.insert(g_ssb_layouts.begin(), out);
+    std::vector<std::shared_ptr<SsbLayout>> &cache = key.noalloc ? g_ssb_noalloc_layouts : g_ssb_layouts;
+    for (size_t i = 0; i < cache.size(); ++i) {
+        if (cache[i]->key == key) {
+            out = cache[i];
+            cache.erase(cache.begin() + i);
+            cache.insert(cache.begin(), out);
             return DSP_OK;
         }
     }
     dsp_status st = build_ssb_layout(key, optics, coords, weights, out);
     if (st) return st;
-    g_ssb_layouts.insert(g_ssb_layouts.begin(), out);
-    if (g_ssb_layouts.size() > LAYOUT_CACHE_SIZE) g_ssb_layouts.pop_back();
+    cache.insert(cache.begin(), out);
+    if (cache.size() > LAYOUT_CACHE_SIZE) cache.pop_back();
     return DSP_OK;
 }
 

@@ -106,6 +106,21 @@ def test_noalloc_matches_ssb_on_shrinking_inputs():
     _compare("128 x 128 again", G2, k2, sets2[:2], w2.step, (0.2, 1.5))
 
 
+def test_noalloc_frees_nothing_with_full_layout_caches():
+    """After more allocating passes than the layout caches hold (each band a
+    new layout), allocation-free passes with new bands evict no layout that
+    holds device memory: the device's free memory does not move and the sums
+    match dsp_ssb."""
+    w1 = workload("c1")
+    pix, k1 = bf_pixels(w1)
+    G1 = torch.as_tensor(data_stack_numpy(w1, pix), device=DEV)
+    for i in range(6):
+        dsp.ssb(G1, k1, [w1.optics], step=w1.step, band=(0.1 + 0.05 * i, 2.9))
+    torch.cuda.synchronize()
+    for i in range(6):
+        _compare(f"32 x 32 band {i}", G1, k1, [w1.optics], w1.step, (0.12 + 0.05 * i, 2.8))
+
+
 def test_noalloc_rejects_a_pass_beyond_its_scratch():
     """A pass whose tables alone exceed the fixed scratch (8 sets over 60,000
     pixels: 8 x 60,000 x 160 bytes of Taylor tables) returns DSP_ENOMEM with a
