@@ -1347,12 +1347,10 @@ dsp_status build_preview_layout(const SsbKey &key, const dsp_optics *optics, con
     if (L->act.pix.empty()) return fail(DSP_EINVAL, "no bright-field pixel has a non-zero aperture weight");
     const double reach = 2.0 * std::sqrt(make_aperture_dev(optics).rlim2) * (1.0 + 1e-9);
 
-    // slots of every stored entry (rows -N/2 .. N/2-1, columns 0 .. N/2)
-    std::vector<JSet> ent((size_t)N * nh);
-    auto at = [&](int yh, int ix) -> JSet & { return ent[(size_t)(yh < 0 ? yh + N : yh) * nh + ix]; };
-    for (int yh = -N / 2; yh <= (N - 1) / 2; ++yh)
-        for (int ix = 0; ix < nh; ++ix) at(yh, ix) = preview_slots(yh, ix, N, u, dq, reach);
-    auto has = [&](int yh, int ix) { return !at(yh, ix).empty(); };
+    // the stored entries (rows -N/2 .. N/2-1, columns 0 .. N/2) with at least
+    // one slot; each entry's slots are worked out again where its tile is
+    // built (cheap, and no per-entry storage at N = 8192)
+    auto has = [&](int yh, int ix) { return !preview_slots(yh, ix, N, u, dq, reach).empty(); };
 
     // lane groups cut along G's lines; a group whose slot union exceeds
     // MAX_SLOTS splits into sub-tiles, greedily by lane, and a lane with more
@@ -1367,7 +1365,7 @@ dsp_status build_preview_layout(const SsbKey &key, const dsp_optics *optics, con
             if (l >= (int)grp.size()) continue;
             base.lyh[l] = grp[l].first;
             base.lix[l] = grp[l].second;
-            left[l] = at(grp[l].first, grp[l].second);
+            left[l] = preview_slots(grp[l].first, grp[l].second, N, u, dq, reach);
         }
         for (;;) {
             GramTile t = base;
