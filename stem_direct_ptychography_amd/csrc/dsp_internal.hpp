@@ -208,6 +208,7 @@ struct alignas(64) GramTile {
     int8_t jy[12], jx[12];
     uint16_t mask[64];   // per lane: bit s set when slot s is an alias of the lane's frequency
     int32_t qidx[64];    // per lane: index of the frequency in the solved list, -1 if none
+                         // (preview tiles: 0 for a lane in use; its slots are its fine images)
     int16_t lyh[64];     // per lane: signed row
     int16_t lix[64];     // per lane: column
 };
