@@ -1265,10 +1265,12 @@ __global__ void export_kernel(const double2 *sys, int n_q, int D, double2 *dense
 // SSB / agreement pass
 // ---------------------------------------------------------------------------
 
-// Waves per SIMD the SSB kernel must fit.
-template <int MAXB>
+// Waves per SIMD the SSB kernel must fit.  Eight sets fit three in 168
+// registers with 4-pixel chunks (11 KB of LDS), except the per-row herm16
+// scales, which would spill there.
+template <int MAXB, int H16>
 struct SsbWaves {
-    static constexpr int value = MAXB <= 2 ? 4 : 2;
+    static constexpr int value = MAXB <= 2 ? 4 : (MAXB <= 4 ? 2 : (H16 == 2 ? 2 : 3));
 };
 
 // SSB sums over one wave's stream-K range of (band tile, pixel) iterations;
@@ -1282,7 +1284,7 @@ struct SsbWaves {
 // FP64 at use; H16 = 1: one scale per pixel (staged with the pixel record);
 // H16 = 2: one scale per stored row, fetched with G for the lane's row.
 template <int MAXB, bool DEPTH, int H16>
-__global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParams prm) {
+__global__ __launch_bounds__(64, (SsbWaves<MAXB, H16>::value)) void ssb_kernel(SsbParams prm) {
     constexpr int NACC = 3 * MAXB + 1;
     constexpr int PF = 2;   // G fetched one group of PF pixels ahead (as in gram_kernel)
     using GT = typename std::conditional<H16 != 0, short2, float2>::type;
@@ -1290,7 +1292,7 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
     // both lobes' phases come from each set's chi Taylor coefficients about
     // theta(k), staged per chunk (chunks of 16 or 8 pixels keep the LDS within
     // the kernel's waves per SIMD)
-    constexpr int CHK = MAXB <= 2 ? 16 : 8;
+    constexpr int CHK = MAXB <= 2 ? 16 : (MAXB <= 4 ? 8 : 4);
     __shared__ PixelRec srec[CHK];
     __shared__ long long sgoff[CHK + PF];
     __shared__ long long sgrow[H16 == 2 ? CHK + PF : 1];   // pixel index x N (row scales)
@@ -1320,15 +1322,18 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
     const long long n_pix = prm.n_pix;
     long long it = prm.wbegin[wv];
     const long long end = prm.wbegin[wv + 1];
-    int seg = prm.seg_off[wv];
+    // wave-uniform: the partial sums' base stays in scalar registers
+    int seg = __builtin_amdgcn_readfirstlane(prm.seg_off[wv]);
     ConstPixel *pix = (ConstPixel *)prm.pix;
     ConstLong *goffs = (ConstLong *)prm.goff;
     const GT *__restrict__ G = H16 ? (const GT *)prm.GQ : (const GT *)prm.G;
     const float *__restrict__ gsc = prm.gscale;
 
+    // the range's first tile and pixel; every later segment starts the next
+    // tile at its first pixel (one division per wave, none held in registers)
+    int t = (int)(it / n_pix);
+    int p0 = (int)(it - (long long)t * n_pix);
     while (it < end) {
-        const int t = (int)(it / n_pix);
-        const int p0 = (int)(it - (long long)t * n_pix);
         const int p1 = (int)((end - it) < (n_pix - p0) ? p0 + (end - it) : n_pix);
         const SsbTile *tile = prm.tiles + t;
         const int yh = tile->lyh[lane];   // the lane's stored frequency q (signed row, column)
@@ -1495,11 +1500,17 @@ __global__ __launch_bounds__(64, SsbWaves<MAXB>::value) void ssb_kernel(SsbParam
                 }
             }
         }
+        // the lane's offset is formed here (the empty asm keeps the compiler
+        // from holding a 64-bit address across the pixel loop)
         double *po = prm.partial + (size_t)seg * (NACC * 64);
+        int lo = lane;
+        asm volatile("" : "+v"(lo));
 #pragma unroll
-        for (int i = 0; i < NACC; ++i) po[i * 64 + lane] = acc[i];
+        for (int i = 0; i < NACC; ++i) po[i * 64 + lo] = acc[i];
         ++seg;
         it += p1 - p0;
+        ++t;
+        p0 = 0;
     }
 }
 
