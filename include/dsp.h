@@ -459,6 +459,13 @@ dsp_status dsp_chi_shift_host(const dsp_optics *optics, const double *k_host, co
  * x_host double[n] -> sin_out, cos_out double[n]. */
 dsp_status dsp_sincos_host(const double *x_host, int n, double *sin_out, double *cos_out);
 
+/* The loss path's FP64 atan2 (table-reduced, for phases whose x is fixed per
+ * pixel; the same source the kernels compile, with the host's division in
+ * place of the hardware reciprocal estimate) at n points: y_host, x_host
+ * double[n] -> out double[n]; x = 0 takes the C library's atan2, as the
+ * kernels do.  DSP_EINVAL for n < 0 or NULL arrays with n > 0. */
+dsp_status dsp_atan2_host(const double *y_host, const double *x_host, int n, double *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -483,6 +483,15 @@ def sincos_host(x) -> Tuple[np.ndarray, np.ndarray]:
     return s, c
 
 
+def atan2_host(y, x) -> np.ndarray:
+    """The loss path's FP64 atan2 (the kernels' source) on the host."""
+    yy = np.ascontiguousarray(np.asarray(y, dtype=np.float64).reshape(-1))
+    xx = np.ascontiguousarray(np.broadcast_to(np.asarray(x, dtype=np.float64), yy.shape).reshape(-1))
+    out = np.zeros_like(yy)
+    _check(_L.dsp_atan2_host(_dptr(yy), _dptr(xx), yy.shape[0], _dptr(out)))
+    return out
+
+
 def chi_host(optics, k) -> np.ndarray:
     """The library's aberration polynomial chi(k) evaluated on the host."""
     kk = _coords(k)

@@ -62,7 +62,7 @@ class InfoC(ctypes.Structure):
 EXPORTS = (
     "dsp_prepare", "dsp_solve", "dsp_scatter", "dsp_ssb", "dsp_info", "dsp_export_system", "dsp_alias_table",
     "dsp_destroy", "dsp_last_error", "dsp_geometry_counts", "dsp_alias_geometry", "dsp_active_bf",
-    "dsp_band_count", "dsp_chi_host", "dsp_chi_shift_host", "dsp_sincos_host", "dsp_derive_phase", "dsp_quantize_herm16",
+    "dsp_band_count", "dsp_chi_host", "dsp_chi_shift_host", "dsp_sincos_host", "dsp_atan2_host", "dsp_derive_phase", "dsp_quantize_herm16",
     "dsp_ssb_herm16", "dsp_preview", "dsp_loss", "dsp_cache_create", "dsp_cache_destroy", "dsp_cache_get",
     "dsp_ssb_noalloc",
 )
@@ -141,4 +141,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dsp_chi_shift_host.argtypes = [ctypes.POINTER(OpticsC), _DP, _DP, _I, _DP]
     lib.dsp_sincos_host.restype = _I
     lib.dsp_sincos_host.argtypes = [_DP, _I, _DP, _DP]
+    lib.dsp_atan2_host.restype = _I
+    lib.dsp_atan2_host.argtypes = [_DP, _DP, _I, _DP]
     return lib

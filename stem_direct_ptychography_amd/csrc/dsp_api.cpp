@@ -627,6 +627,32 @@ dsp_status trig_table_device(int device, const double2 **out) {
     return DSP_OK;
 }
 
+// atan(i/64), i = 0..ATAN_N - 1 (atan2_tab), rounded from long double.
+void atan_table_host(double *A) {
+    for (int i = 0; i < ATAN_N; ++i) A[i] = (double)atanl((long double)i / 64.0L);
+}
+
+// The atan table on a device: uploaded once per device, kept until the
+// process ends.
+dsp_status atan_table_device(int device, const double **out) {
+    static std::mutex mu;
+    static std::map<int, double *> tables;
+    std::lock_guard<std::mutex> lock(mu);
+    auto f = tables.find(device);
+    if (f != tables.end()) {
+        *out = f->second;
+        return DSP_OK;
+    }
+    double host[ATAN_N];
+    atan_table_host(host);
+    double *d = nullptr;
+    HIP_TRY(hipMalloc((void **)&d, sizeof host));
+    HIP_TRY(hipMemcpy(d, host, sizeof host, hipMemcpyHostToDevice));
+    tables[device] = d;
+    *out = d;
+    return DSP_OK;
+}
+
 // e^{+2 pi i m / N} for m < N/2 (the fused loss transforms), from long
 // double on the host, one device table per (device, N) kept for the process.
 dsp_status twiddle_table_device(int device, int N, const double2 **out) {
@@ -1707,6 +1733,17 @@ dsp_status dsp_chi_shift_host(const dsp_optics *optics, const double *k_host, co
     return DSP_OK;
 }
 
+dsp_status dsp_atan2_host(const double *y_host, const double *x_host, int n, double *out) {
+    if (n < 0 || (n > 0 && (!y_host || !x_host || !out))) return fail(DSP_EINVAL, "bad arguments");
+    double A[ATAN_N];
+    atan_table_host(A);
+    for (int i = 0; i < n; ++i) {
+        const double x = x_host[i];
+        out[i] = x == 0.0 ? std::atan2(y_host[i], x) : atan2_tab(y_host[i], x, 1.0 / x, A);
+    }
+    return DSP_OK;
+}
+
 dsp_status dsp_sincos_host(const double *x_host, int n, double *sin_out, double *cos_out) {
     if (n < 0 || (n > 0 && (!x_host || !sin_out || !cos_out))) return fail(DSP_EINVAL, "bad arguments");
     double2 T[TRIG_N];
@@ -2607,7 +2644,9 @@ dsp_status dsp_loss(const void *G_c64_dev, int n_bf, const double *bf_coords_hos
     double *d_s1p = cv.take<double>(std::max<size_t>(1, (size_t)NG * nn));
     double *d_s2p = cv.take<double>(std::max<size_t>(1, (size_t)NG * nn));
     const double2 *d_tw = nullptr;
-    if (fused && (st = twiddle_table_device(device, N, &d_tw))) return st;
+    const double *d_atan = nullptr;
+    if (fused && ((st = twiddle_table_device(device, N, &d_tw)) || (st = atan_table_device(device, &d_atan))))
+        return st;
     const ApertureDev apd = make_aperture_dev(optics);
     const OpticsDev opd = make_optics_dev(optics);
     HIP_TRY(launch_pixel_terms(L.d_pixbase, d_pix, n_pix, apd, opd, nullptr, 0, nullptr, stream));
@@ -2630,7 +2669,7 @@ dsp_status dsp_loss(const void *G_c64_dev, int n_bf, const double *bf_coords_hos
         cp.goff = L.d_goff + c0;
         cp.n_valid = cn;
         if (fused) {
-            HIP_TRY(launch_loss_fused(cp, d_tw, cn, L.d_pixbase + c0, std::min(NG, cn), d_s1p, d_s2p, d_s1, d_s2,
+            HIP_TRY(launch_loss_fused(cp, d_tw, d_atan, cn, L.d_pixbase + c0, std::min(NG, cn), d_s1p, d_s2p, d_s1, d_s2,
                                       stream));
             continue;
         }

@@ -188,6 +188,55 @@ __host__ __device__ inline void sincos_tab(double x, const double2 *__restrict__
     c = fma(t.x, cr, -(t.y * sr));
 }
 
+// ---------------------------------------------------------------------------
+// FP64 atan2 of the loss path's phases
+// ---------------------------------------------------------------------------
+// theta = atan2(y, x) where x (a pixel's Re D) is the same at every scan
+// position, so t = y (1/x) with 1/x formed once per pixel.  |t| > 1 folds by
+// atan |t| = pi/2 - atan(1/|t|); u in [0, 1] is reduced against c = i/64, i =
+// rint(64 u), by atan u = atan c + atan v with v = (u - c) / (1 + u c), |v| <=
+// 1/128, and atan v = v - v^3/3 + v^5/5 - v^7/7 (truncation below |v|^9 / 9
+// = 1.2e-20); x < 0 adds pi with the sign of y (so y = -0 gives -pi, as
+// atan2 does).  A[i] = atan(i/64), i = 0..64, rounded from long double.  The
+// reciprocals are the hardware estimate refined by Newton steps: two for
+// 1/|t|, one for 1/(1 + u c), whose quotient v is below 1/128.  Within 3 ulp
+// of atan2 (4.4e-16 rad) where the host's division stands in for the
+// estimate; x = 0 is left to the caller.
+constexpr int ATAN_N = 65;
+
+__host__ __device__ inline double rcp_estimate(double b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_rcp(b);
+#else
+    return 1.0 / b;
+#endif
+}
+
+__host__ __device__ inline double atan2_tab(double y, double x, double rx, const double *__restrict__ A) {
+    const double t = y * rx;
+    const double a = fabs(t);
+    const bool flip = a > 1.0;
+    const double b = fmax(a, 1.0);
+    double r = rcp_estimate(b);
+    r = fma(r, fma(-b, r, 1.0), r);
+    r = fma(r, fma(-b, r, 1.0), r);
+    const double u = flip ? r : a;
+    int i = (int)fma(u, 64.0, 0.5);
+    i = i < 0 ? 0 : (i > ATAN_N - 1 ? ATAN_N - 1 : i);   // keeps a NaN's index inside the table
+    const double c = (double)i * 0.015625;
+    const double den = fma(u, c, 1.0);
+    double rd = rcp_estimate(den);
+    rd = fma(rd, fma(-den, rd, 1.0), rd);
+    const double v = (u - c) * rd;
+    const double v2 = v * v;
+    const double p = v2 * fma(v2, fma(v2, -1.0 / 7.0, 0.2), -1.0 / 3.0);
+    const double s = A[i] + fma(v, p, v);
+    double res = flip ? (1.5707963267948966 - s) + 6.123233995736766e-17 : s;   // pi/2 as hi + lo
+    res = copysign(res, t);
+    if (x < 0.0) res = (res + copysign(1.2246467991473532e-16, y)) + copysign(3.141592653589793, y);
+    return res;
+}
+
 // A tile is a group of up to 64 scan frequencies, one per lane, with
 // explicit coordinates (signed row yh, column ix).  The host cuts every
 // stored row of G into the runs that fill one 128-byte line (LINE_X = 16

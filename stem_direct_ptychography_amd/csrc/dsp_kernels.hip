@@ -79,6 +79,19 @@ __device__ __forceinline__ double sqrt_fast(double d2) {
     return fma(0.5 * r, fma(-s0, s0, d2), s0);
 }
 
+// The leading coefficients of chi's Horner rows (chi_poly_top) held in VGPRs:
+// from scalar registers each row's first FMA would have two scalar operands
+// and take a register copy per evaluation (the empty asm hides that the
+// values are uniform).  Row 6's single coefficient stays scalar.
+__device__ __forceinline__ void chi_tops(const double *c, double (&top)[CHI_DEG + 1]) {
+#pragma unroll
+    for (int j = 0; j <= CHI_DEG; ++j) {
+        double v = c[chi_off(j) + CHI_DEG - j];
+        if (j < CHI_DEG) asm volatile("" : "+v"(v));
+        top[j] = v;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // pixel terms: a(k) and chi(k) once per pixel and optics set
 // ---------------------------------------------------------------------------
@@ -1651,8 +1664,8 @@ __global__ __launch_bounds__(256) void preview_phase_kernel(double *img, long lo
 // D_k = sqrt(w) G(0, k).  H is 0 at DC and on the Nyquist row and column.
 // H_k(q) at stored entry (iy, ix) != DC, off the Nyquist row and column,
 // for the pixel record rec and its stored value gv.
-__device__ __forceinline__ double2 corrected_value(const CorrParams &prm, const double2 *T, const PixelRec &rec,
-                                                   float2 gv, int iy, int ix) {
+__device__ __forceinline__ double2 corrected_value(const CorrParams &prm, const double2 *T, const double *ctop,
+                                                   const PixelRec &rec, float2 gv, int iy, int ix) {
     const int N = prm.N;
     const int yh = iy < N / 2 ? iy : iy - N;
     const double qy = (double)yh * prm.ldq, qx = (double)ix * prm.ldq;   // lambda q
@@ -1669,9 +1682,9 @@ __device__ __forceinline__ double2 corrected_value(const CorrParams &prm, const 
     double Lr = 0.0, Li = 0.0, Rr = 0.0, Ri = 0.0;
     if (zl) {
         double a = rec.amp0;
-        if (dm2 > prm.ap.lrin2) a *= fma(prm.ap.lkc - sqrt(dm2), prm.ap.inv_ldk, 0.5);
+        if (dm2 > prm.ap.lrin2) a *= fma(prm.ap.lkc - sqrt_fast(dm2), prm.ap.inv_ldk, 0.5);
         const double ty = py - qy, tx = px - qx;
-        double arg = rec.chi0 - chi_poly(prm.op.chi_c, tx, ty);
+        double arg = rec.chi0 - chi_poly_top(prm.op.chi_c, ctop, tx, ty);
         if (depth) {
             const double h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
             arg += h;
@@ -1684,9 +1697,9 @@ __device__ __forceinline__ double2 corrected_value(const CorrParams &prm, const 
     }
     if (zr) {
         double a = rec.amp0;
-        if (dp2 > prm.ap.lrin2) a *= fma(prm.ap.lkc - sqrt(dp2), prm.ap.inv_ldk, 0.5);
+        if (dp2 > prm.ap.lrin2) a *= fma(prm.ap.lkc - sqrt_fast(dp2), prm.ap.inv_ldk, 0.5);
         const double ty = py + qy, tx = px + qx;
-        double arg = rec.chi0 - chi_poly(prm.op.chi_c, tx, ty);
+        double arg = rec.chi0 - chi_poly_top(prm.op.chi_c, ctop, tx, ty);
         if (depth) {
             const double h = prm.op.pt2 * (th0 - fma(tx, tx, ty * ty));
             arg += h;
@@ -1725,7 +1738,9 @@ __global__ __launch_bounds__(256) void corrected_half_kernel(CorrParams prm) {
         Hj[e] = make_double2(0.0, 0.0);
         return;
     }
-    Hj[e] = corrected_value(prm, T, rec, gv, iy, ix);
+    double ctop[CHI_DEG + 1];
+    chi_tops(prm.op.chi_c, ctop);
+    Hj[e] = corrected_value(prm, T, ctop, rec, gv, iy, ix);
 }
 
 // ---------------------------------------------------------------------------
@@ -1734,122 +1749,331 @@ __global__ __launch_bounds__(256) void corrected_half_kernel(CorrParams prm) {
 // column ix) that computes the corrected values itself, and a row pass (the
 // real transform of each row's half spectrum) that goes straight on to the
 // phases and their moments; neither the corrected planes nor the real images
-// make a round trip through HBM.  Both passes are in-place iterative radix-2
-// transforms in LDS (bit-reversed load, natural-order result) with the
-// twiddles e^{+2 pi i m / N}, m < N/2, from a host table in long double.
+// make a round trip through HBM.  Both passes run self-sorting (Stockham)
+// transforms in LDS, radix 8 in registers (one radix-4 or radix-2 pass first
+// when log2 N is not a multiple of 3), with the twiddles e^{+2 pi i m / N},
+// m < N/2, from a host table in long double.
 // ---------------------------------------------------------------------------
-constexpr int LOSS_E = 2048;   // complex values a column-pass block holds (N x columns)
+constexpr int LOSS_E = 2048;                     // complex values a block transforms at once
+constexpr int LOSS_EP = LOSS_E + LOSS_E / 8;     // the same, padded (loss_pad)
 
-__device__ __forceinline__ void fft_inverse_inplace(double2 *A, int ncol, int N, int logN, const double2 *tw) {
-    // ncol independent length-N columns at A + c N, already in bit-reversed order
-    const int nb = ncol * (N >> 1);   // butterflies per stage
-    for (int s = 1; s <= logN; ++s) {
-        const int half = 1 << (s - 1);
-        const int tstep = N >> s;     // twiddle index step: e^{2 pi i pos / len} = tw[pos N / len]
-        for (int b = threadIdx.x; b < nb; b += blockDim.x) {
-            const int c = b >> (logN - 1);
-            const int bb = b & ((N >> 1) - 1);
-            const int pos = bb & (half - 1);
-            const int i = c * N + ((bb - pos) << 1) + pos;
-            const int k = i + half;
-            const double2 w = tw[pos * tstep];
-            const double2 u = A[i], x = A[k];
-            const double2 v = make_double2(fma(x.x, w.x, -(x.y * w.y)), fma(x.x, w.y, x.y * w.x));
-            A[i] = make_double2(u.x + v.x, u.y + v.y);
-            A[k] = make_double2(u.x - v.x, u.y - v.y);
-        }
-        __syncthreads();
+// LDS slot of sequence element i: one spare slot per 8, so the first pass's
+// stride-8 stores of a wave's lanes fall in distinct banks
+__device__ __forceinline__ int loss_pad(int i) { return i + (i >> 3); }
+
+__device__ __forceinline__ double2 c_mul(double2 a, double2 b) {
+    return make_double2(fma(a.x, b.x, -(a.y * b.y)), fma(a.x, b.y, a.y * b.x));
+}
+__device__ __forceinline__ double2 c_add(double2 a, double2 b) { return make_double2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ double2 c_sub(double2 a, double2 b) { return make_double2(a.x - b.x, a.y - b.y); }
+
+// In-register DFT of length R in {2, 4, 8} with e^{+2 pi i r k / R}; the
+// length-8 one from two length-4 ones (even and odd r) and the factors
+// e^{i pi k / 4}.
+template <int R>
+__device__ __forceinline__ void dft_small(double2 (&v)[R]) {
+    if constexpr (R == 2) {
+        const double2 t = v[0];
+        v[0] = c_add(t, v[1]);
+        v[1] = c_sub(t, v[1]);
+    } else if constexpr (R == 4) {
+        const double2 a = c_add(v[0], v[2]), b = c_sub(v[0], v[2]);
+        const double2 c = c_add(v[1], v[3]), d = c_sub(v[1], v[3]);
+        const double2 id = make_double2(-d.y, d.x);   // i d
+        v[0] = c_add(a, c);
+        v[1] = c_add(b, id);
+        v[2] = c_sub(a, c);
+        v[3] = c_sub(b, id);
+    } else {
+        double2 e[4] = {v[0], v[2], v[4], v[6]};
+        double2 o[4] = {v[1], v[3], v[5], v[7]};
+        dft_small<4>(e);
+        dft_small<4>(o);
+        const double h = 0.70710678118654752440;   // 1 / sqrt 2
+        const double2 t1 = make_double2((o[1].x - o[1].y) * h, (o[1].x + o[1].y) * h);    // e^{i pi/4} o1
+        const double2 t2 = make_double2(-o[2].y, o[2].x);                                // i o2
+        const double2 t3 = make_double2(-(o[3].x + o[3].y) * h, (o[3].x - o[3].y) * h);  // e^{3 i pi/4} o3
+        v[0] = c_add(e[0], o[0]);
+        v[4] = c_sub(e[0], o[0]);
+        v[1] = c_add(e[1], t1);
+        v[5] = c_sub(e[1], t1);
+        v[2] = c_add(e[2], t2);
+        v[6] = c_sub(e[2], t2);
+        v[3] = c_add(e[3], t3);
+        v[7] = c_sub(e[3], t3);
     }
 }
 
-// Block (column block, pixel j of the chunk): columns ix0 .. ix0 + cw - 1 of
+// One Stockham pass of radix R over nt length-N sequences (sequence t at
+// elements t N .. t N + N - 1, slots loss_pad of those): sub-transforms of
+// length Ns are done; butterfly j of a sequence reads elements j + r N/R,
+// applies e^{+2 pi i k r / (Ns R)} (k = j mod Ns) and writes its R outputs
+// to (j - k) R + k + r Ns.  A 256-thread block holds at most LOSS_E values,
+// so a thread has 8 / R butterflies; all are read before the barrier and
+// written after it (in place).
+template <int R>
+__device__ __forceinline__ void stockham_pass(double2 *A, int nt, int N, int logN, int Ns, const double2 *tw) {
+    constexpr int BPT = 8 / R;
+    const int NR = N / R;
+    const int lognr = logN - (R == 8 ? 3 : (R == 4 ? 2 : 1));
+    const int nbut = nt * NR;
+    const int step = N / (Ns * R);   // twiddle index per unit of k r
+    double2 v[BPT][R];
+    int obase[BPT];
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+        const int b = threadIdx.x + u * 256;
+        obase[u] = -1;
+        if (b < nbut) {
+            const int c = b >> lognr, j = b - (c << lognr);
+            const int k = j & (Ns - 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r) v[u][r] = A[loss_pad(c * N + j + r * NR)];
+#pragma unroll
+            for (int r = 1; r < R; ++r) {
+                const int idx = k * r * step;   // < N
+                double2 w;
+                if (idx < (N >> 1)) {
+                    w = tw[idx];
+                } else {
+                    w = tw[idx - (N >> 1)];
+                    w.x = -w.x;
+                    w.y = -w.y;
+                }
+                v[u][r] = c_mul(v[u][r], w);
+            }
+            obase[u] = c * N + (j - k) * R + k;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+        if (obase[u] < 0) continue;
+        dft_small<R>(v[u]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) A[loss_pad(obase[u] + r * Ns)] = v[u][r];
+    }
+    __syncthreads();
+}
+
+// Unnormalized inverse DFT of nt length-N sequences in place (natural order
+// in and out); nt N <= LOSS_E.  Every thread of the 256-thread block calls it
+// after the input is in LDS and visible (a barrier).
+__device__ __forceinline__ void fft_inverse_stockham(double2 *A, int nt, int N, int logN, const double2 *tw) {
+    int Ns = 1;
+    const int lead = logN % 3;
+    if (lead == 1) {
+        stockham_pass<2>(A, nt, N, logN, Ns, tw);
+        Ns = 2;
+    } else if (lead == 2) {
+        stockham_pass<4>(A, nt, N, logN, Ns, tw);
+        Ns = 4;
+    }
+    for (; Ns < N; Ns *= 8) stockham_pass<8>(A, nt, N, logN, Ns, tw);
+}
+
+// Item (column block, pixel j of the chunk): columns ix0 .. ix0 + cw - 1 of
 // H_j over all N rows, transformed along iy: Y_j(y, ix) = sum_iy H_j(iy, ix)
-// e^{+2 pi i iy y / N}.  The block at ix0 = 0 also writes D_j.
-__global__ __launch_bounds__(256) void loss_column_kernel(CorrParams prm, const double2 *tw, int logN, int cw) {
+// e^{+2 pi i iy y / N}.  The item at ix0 = 0 also writes D_j.
+// The n_items = ncb cn items are spread over a grid of 8 m blocks that loop:
+// block b takes virtual items v = b, b + grid, ...  Workgroups go to the 8
+// XCDs in turn, so v maps to item (v mod 8) per + v/8 (per = n_items / 8;
+// the last n_items mod 8 map to themselves): each XCD runs a contiguous
+// stretch of items, and the column blocks that share G's 128-byte lines meet
+// them in that XCD's L2.  A block loads the next item's G values while it
+// transforms the current one.
+struct LossColItem {
+    int j, ix0;
+};
+
+__device__ __forceinline__ LossColItem loss_col_item(int v, int per, int ncb, int cw) {
+    const int item = v < (per << 3) ? (v & 7) * per + (v >> 3) : v;
+    LossColItem it;
+    it.j = item / ncb;
+    it.ix0 = (item - it.j * ncb) * cw;
+    return it;
+}
+
+__global__ __launch_bounds__(256, 3) void loss_column_kernel(CorrParams prm, const double2 *tw, int logN, int cw,
+                                                             int ncb, int n_items) {
     extern __shared__ double2 lds[];
     double2 *T = lds;                         // [TRIG_N]
     double2 *W = T + TRIG_N;                  // [N/2]
-    double2 *A = W + (prm.N >> 1);            // [cw][N]
+    double2 *A = W + (prm.N >> 1);            // [LOSS_EP]: cw columns of N, padded
     const int N = prm.N, nh = prm.nh;
     for (int i = threadIdx.x; i < TRIG_N; i += blockDim.x) T[i] = prm.trig[i];
     for (int i = threadIdx.x; i < (N >> 1); i += blockDim.x) W[i] = tw[i];
-    const int j = blockIdx.y;
-    const int ix0 = blockIdx.x * cw;
-    const PixelRec rec = prm.pix[j];
-    const float2 *Gj = prm.G + prm.goff[j];
-    if (ix0 == 0 && threadIdx.x == 0) {
-        const float2 g0 = Gj[0];
-        prm.D[j] = make_double2(rec.sw * (double)g0.x, rec.sw * (double)g0.y);
-    }
-    __syncthreads();
+    double ctop[CHI_DEG + 1];
+    chi_tops(prm.op.chi_c, ctop);
+    // element e = iy cw + c, the thread's elements e = tid + 256 s; with cw a
+    // power of two (N >= 64) its column c stays fixed, with no division
+    constexpr int EPT = LOSS_E / 256;
     const int n = N * cw;
-    for (int e = threadIdx.x; e < n; e += blockDim.x) {
-        const int iy = e / cw, c = e - iy * cw, ix = ix0 + c;
-        double2 h = make_double2(0.0, 0.0);
-        if (ix < nh && !(iy == 0 && ix == 0) && iy != N / 2 && ix != N / 2)
-            h = corrected_value(prm, T, rec, Gj[(size_t)iy * nh + ix], iy, ix);
-        A[c * N + (int)(__brev((unsigned)iy) >> (32 - logN))] = h;
+    const bool pow2 = (cw & (cw - 1)) == 0;
+    const int lc = pow2 ? __ffs(cw) - 1 : 0;
+    // (row, column) of the thread's element s
+    auto rc = [&](int s, int &iy, int &c) {
+        const int e = (int)threadIdx.x + 256 * s;
+        if (pow2) {
+            iy = e >> lc;
+            c = e & (cw - 1);
+        } else {
+            iy = e / cw;
+            c = e - iy * cw;
+        }
+    };
+    const int per = n_items >> 3;
+    const int stride = gridDim.x;
+    int v = blockIdx.x;
+    if (v >= n_items) return;
+    // the first item's G values
+    LossColItem it = loss_col_item(v, per, ncb, cw);
+    float2 gv[EPT];
+    {
+        const float2 *Gj = prm.G + prm.goff[it.j];
+#pragma unroll
+        for (int s = 0; s < EPT; ++s) {
+            const int e = threadIdx.x + 256 * s;
+            int iy, c;
+            rc(s, iy, c);
+            gv[s] = make_float2(0.0f, 0.0f);
+            if (e < n && it.ix0 + c < nh) gv[s] = Gj[(size_t)iy * nh + it.ix0 + c];
+        }
     }
-    __syncthreads();
-    fft_inverse_inplace(A, cw, N, logN, W);
-    double2 *Yj = prm.H + (size_t)j * N * nh;
-    for (int e = threadIdx.x; e < n; e += blockDim.x) {
-        const int y = e / cw, c = e - y * cw, ix = ix0 + c;
-        if (ix < nh) Yj[(size_t)y * nh + ix] = A[c * N + y];
+    while (true) {
+        const int j = it.j, ix0 = it.ix0;
+        const PixelRec rec = prm.pix[j];
+        if (ix0 == 0 && threadIdx.x == 0) {
+            const float2 g0 = prm.G[prm.goff[j]];
+            prm.D[j] = make_double2(rec.sw * (double)g0.x, rec.sw * (double)g0.y);
+        }
+        __syncthreads();   // tables loaded; the previous item's transform is read
+#pragma unroll
+        for (int s = 0; s < EPT; ++s) {
+            const int e = threadIdx.x + 256 * s;
+            if (e >= n) continue;
+            int iy, c;
+            rc(s, iy, c);
+            const int ix = ix0 + c;
+            double2 h = make_double2(0.0, 0.0);
+            if (ix < nh && !(iy == 0 && ix == 0) && iy != N / 2 && ix != N / 2)
+                h = corrected_value(prm, T, ctop, rec, gv[s], iy, ix);
+            A[loss_pad(c * N + iy)] = h;
+        }
+        // the next item's G values go out before this item's transform
+        const int vn = v + stride;
+        LossColItem nx = it;
+        if (vn < n_items) {
+            nx = loss_col_item(vn, per, ncb, cw);
+            const float2 *Gn = prm.G + prm.goff[nx.j];
+#pragma unroll
+            for (int s = 0; s < EPT; ++s) {
+                const int e = threadIdx.x + 256 * s;
+                int iy, c;
+                rc(s, iy, c);
+                gv[s] = make_float2(0.0f, 0.0f);
+                if (e < n && nx.ix0 + c < nh) gv[s] = Gn[(size_t)iy * nh + nx.ix0 + c];
+            }
+        }
+        __syncthreads();
+        fft_inverse_stockham(A, cw, N, logN, W);
+        double2 *Yj = prm.H + (size_t)j * N * nh;
+#pragma unroll
+        for (int s = 0; s < EPT; ++s) {
+            const int e = threadIdx.x + 256 * s;
+            int y, c;
+            rc(s, y, c);
+            const int ix = ix0 + c;
+            if (e < n && ix < nh) Yj[(size_t)y * nh + ix] = A[loss_pad(c * N + y)];
+        }
+        if (vn >= n_items) break;
+        v = vn;
+        it = nx;
     }
 }
 
 // Block (row pair p, pixel group g): rows p and p + N/2 of every pixel j = g,
-// g + ng, ... of the chunk.  The two rows' half spectra, each extended by
-// X(N - kx) = conj X(kx), go into one complex transform as a + i b (both
-// images are real), so its real part is row p's image and its imaginary part
-// row p + N/2's.  theta = atan2(img + Im D_j, Re D_j); the block adds
-// w_j theta and w_j theta^2 per position over its pixels in order and writes
-// them to its group's partial planes.
-__global__ __launch_bounds__(256) void loss_row_kernel(const double2 *Y, const double2 *D, const PixelBase *pb,
+// g + ng, ... of the chunk, LOSS_E / N pixels at a time.  The two rows' half
+// spectra, each extended by X(N - kx) = conj X(kx), go into one complex
+// transform as a + i b (both images are real), so its real part is row p's
+// image and its imaginary part row p + N/2's.  theta = atan2(img + Im D_j,
+// Re D_j); each thread adds w_j theta and w_j theta^2 for its positions over
+// the group's pixels in order and writes them to the group's partial planes.
+// MAXP = max(1, N / 256) positions per thread and row.
+template <int MAXP>
+__global__ __launch_bounds__(256, (MAXP >= 4 ? 2 : 3)) void loss_row_kernel(const double2 *Y, const double2 *D, const PixelBase *pb,
                                                        int cn, int N, int nh, const double2 *tw, int logN, int ng,
-                                                       double *s1p, double *s2p) {
+                                                       const double *atab, double *s1p, double *s2p) {
     extern __shared__ double2 lds[];
     double2 *W = lds;              // [N/2]
-    double2 *Z = W + (N >> 1);     // [N]
+    double2 *Z = W + (N >> 1);     // [LOSS_EP]: P transforms of N, padded
+    double *AT = (double *)(Z + LOSS_EP);   // [ATAN_N] atan(i/64)
     for (int i = threadIdx.x; i < (N >> 1); i += blockDim.x) W[i] = tw[i];
+    for (int i = threadIdx.x; i < ATAN_N; i += blockDim.x) AT[i] = atab[i];
     const int p = blockIdx.x, g = blockIdx.y;
     const int ya = p, yb = p + (N >> 1);
-    constexpr int MAXP = 1024 / 256;   // positions per thread and row (N <= 1024)
+    const int P = LOSS_E >> logN;            // pixels per batch
+    const int npx = (cn - g + ng - 1) / ng;  // the group's pixels g + ng m, m < npx
     double a1[2 * MAXP], a2[2 * MAXP];
 #pragma unroll
     for (int m = 0; m < 2 * MAXP; ++m) a1[m] = a2[m] = 0.0;
     const size_t plane = (size_t)N * nh;
-    for (int j = g; j < cn; j += ng) {
-        const double2 *Ya = Y + (size_t)j * plane + (size_t)ya * nh, *Yb = Y + (size_t)j * plane + (size_t)yb * nh;
-        __syncthreads();   // the previous pixel's transform is read
-        for (int kx = threadIdx.x; kx < N; kx += blockDim.x) {
-            double2 a, b;
-            if (kx <= (N >> 1)) {
-                a = Ya[kx];
-                b = Yb[kx];
-            } else {
-                a = Ya[N - kx];
-                b = Yb[N - kx];
-                a.y = -a.y;
-                b.y = -b.y;
+    for (int m0 = 0; m0 < npx; m0 += P) {
+        const int nb = (npx - m0) < P ? (npx - m0) : P;
+        // the batch's row values, all loaded before the first is used
+        constexpr int EPT = LOSS_E / 256;
+        double2 va[EPT], vb[EPT];
+#pragma unroll
+        for (int s = 0; s < EPT; ++s) {
+            const int e = threadIdx.x + 256 * s;
+            va[s] = vb[s] = make_double2(0.0, 0.0);
+            if (e < (nb << logN)) {
+                const int t = e >> logN, kx = e & (N - 1);
+                const size_t jo = (size_t)(g + ng * (m0 + t)) * plane;
+                const int kk = kx <= (N >> 1) ? kx : N - kx;
+                va[s] = Y[jo + (size_t)ya * nh + kk];
+                vb[s] = Y[jo + (size_t)yb * nh + kk];
             }
-            Z[(int)(__brev((unsigned)kx) >> (32 - logN))] = make_double2(a.x - b.y, a.y + b.x);
+        }
+        __syncthreads();   // the previous batch's transforms are read
+#pragma unroll
+        for (int s = 0; s < EPT; ++s) {
+            const int e = threadIdx.x + 256 * s;
+            if (e < (nb << logN)) {
+                double2 a = va[s], b = vb[s];
+                if ((e & (N - 1)) > (N >> 1)) {
+                    a.y = -a.y;
+                    b.y = -b.y;
+                }
+                Z[loss_pad(e)] = make_double2(a.x - b.y, a.y + b.x);
+            }
         }
         __syncthreads();
-        fft_inverse_inplace(Z, 1, N, logN, W);
-        const double2 d = D[j];
-        const double w = pb[j].w;
+        fft_inverse_stockham(Z, nb, N, logN, W);
+        for (int t = 0; t < nb; ++t) {
+            const int j = g + ng * (m0 + t);
+            const double2 d = D[j];
+            const double w = pb[j].w;
+            const bool x0 = d.x == 0.0;   // atan2(y, 0): the library's (uniform per pixel)
+            const double rx = x0 ? 0.0 : 1.0 / d.x;
 #pragma unroll
-        for (int m = 0; m < MAXP; ++m) {
-            const int x = threadIdx.x + m * 256;
-            if (x < N) {
-                const double2 z = Z[x];
-                const double ta = atan2(z.x + d.y, d.x), tb = atan2(z.y + d.y, d.x);
-                a1[m] = fma(w, ta, a1[m]);
-                a2[m] = fma(w * ta, ta, a2[m]);
-                a1[MAXP + m] = fma(w, tb, a1[MAXP + m]);
-                a2[MAXP + m] = fma(w * tb, tb, a2[MAXP + m]);
+            for (int m = 0; m < MAXP; ++m) {
+                const int x = threadIdx.x + m * 256;
+                if (x < N) {
+                    const double2 z = Z[loss_pad((t << logN) + x)];
+                    double ta, tb;
+                    if (x0) {
+                        ta = atan2(z.x + d.y, d.x);
+                        tb = atan2(z.y + d.y, d.x);
+                    } else {
+                        ta = atan2_tab(z.x + d.y, d.x, rx, AT);
+                        tb = atan2_tab(z.y + d.y, d.x, rx, AT);
+                    }
+                    a1[m] = fma(w, ta, a1[m]);
+                    a2[m] = fma(w * ta, ta, a2[m]);
+                    a1[MAXP + m] = fma(w, tb, a1[MAXP + m]);
+                    a2[MAXP + m] = fma(w * tb, tb, a2[MAXP + m]);
+                }
             }
         }
     }
@@ -2277,19 +2501,27 @@ hipError_t launch_corrected_half(const CorrParams &prm, int n_planes, hipStream_
 
 int loss_fused_cols(int N) { return std::max(1, std::min(LOSS_E / N, N / 2 + 1)); }
 
-hipError_t launch_loss_fused(const CorrParams &prm, const double2 *tw, int cn, const PixelBase *pb, int ng,
-                             double *s1p, double *s2p, double *s1, double *s2, hipStream_t st) {
+hipError_t launch_loss_fused(const CorrParams &prm, const double2 *tw, const double *atab, int cn, const PixelBase *pb,
+                             int ng, double *s1p, double *s2p, double *s1, double *s2, hipStream_t st) {
     const int N = prm.N, nh = prm.nh;
     int logN = 0;
     while ((1 << logN) < N) ++logN;
     if ((1 << logN) != N || N < 8 || N > 1024 || cn <= 0 || ng <= 0) return hipErrorInvalidValue;
     const int cw = loss_fused_cols(N);
-    const size_t lds_a = (size_t)(TRIG_N + N / 2 + cw * N) * sizeof(double2);
-    loss_column_kernel<<<dim3((unsigned)((nh + cw - 1) / cw), (unsigned)cn), 256, lds_a, st>>>(prm, tw, logN, cw);
+    const size_t lds_a = (size_t)(TRIG_N + N / 2 + LOSS_EP) * sizeof(double2);
+    // looping blocks: about eight items each, a multiple of 8 blocks (XCDs)
+    const int ncb = (nh + cw - 1) / cw, n_items = ncb * cn;
+    const int grid_a = std::max(8, (n_items / 8 + 7) / 8 * 8);
+    loss_column_kernel<<<(unsigned)grid_a, 256, lds_a, st>>>(prm, tw, logN, cw, ncb, n_items);
     DSP_CHECK_LAUNCH();
-    const size_t lds_b = (size_t)(N / 2 + N) * sizeof(double2);
-    loss_row_kernel<<<dim3((unsigned)(N / 2), (unsigned)ng), 256, lds_b, st>>>(prm.H, prm.D, pb, cn, N, nh, tw, logN,
-                                                                                ng, s1p, s2p);
+    const size_t lds_b = (size_t)(N / 2 + LOSS_EP) * sizeof(double2) + ATAN_N * sizeof(double);
+    const dim3 grid_b((unsigned)(N / 2), (unsigned)ng);
+    if (N <= 256)
+        loss_row_kernel<1><<<grid_b, 256, lds_b, st>>>(prm.H, prm.D, pb, cn, N, nh, tw, logN, ng, atab, s1p, s2p);
+    else if (N == 512)
+        loss_row_kernel<2><<<grid_b, 256, lds_b, st>>>(prm.H, prm.D, pb, cn, N, nh, tw, logN, ng, atab, s1p, s2p);
+    else
+        loss_row_kernel<4><<<grid_b, 256, lds_b, st>>>(prm.H, prm.D, pb, cn, N, nh, tw, logN, ng, atab, s1p, s2p);
     DSP_CHECK_LAUNCH();
     const long long nn = (long long)N * N;
     loss_groups_kernel<<<grid_blocks(nn), 256, 0, st>>>(s1p, s2p, ng, nn, s1, s2);

@@ -78,10 +78,11 @@ int loss_blocks(long long nn);
 // Fused loss pass over one chunk of cn pixels (power-of-two N, 8 <= N <= 1024):
 // column transform with the corrected values (Y into prm.H, D into prm.D),
 // row transform with the phase moments into ng group partials, then
-// s1/s2 += the partials.  tw: e^{+2 pi i m / N}, m < N/2.
+// s1/s2 += the partials.  tw: e^{+2 pi i m / N}, m < N/2; atab: atan(i/64),
+// i = 0..ATAN_N - 1 (atan2_tab).
 int loss_fused_cols(int N);
-hipError_t launch_loss_fused(const CorrParams &prm, const double2 *tw, int cn, const PixelBase *pb, int ng,
-                             double *s1p, double *s2p, double *s1, double *s2, hipStream_t st);
+hipError_t launch_loss_fused(const CorrParams &prm, const double2 *tw, const double *atab, int cn, const PixelBase *pb,
+                             int ng, double *s1p, double *s2p, double *s1, double *s2, hipStream_t st);
 hipError_t launch_loss(const double *s1, const double *s2, long long nn, double W, double *mean_out, double *part,
                        double *loss, hipStream_t st);
 hipError_t launch_ssb(const SsbParams &prm, int n_waves, int n_tiles, double *tile_part, hipStream_t st);

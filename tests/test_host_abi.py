@@ -127,6 +127,24 @@ def test_sincos_matches_libm():
     assert np.max(np.abs(s * s + c * c - 1.0)) <= 2 * bound
 
 
+def test_atan2_matches_libm():
+    """The loss path's table-reduced atan2 against the C library's: both
+    signs of x (x < 0 takes the +-pi branch), |y/x| across 16 decades, the
+    fold at |y/x| = 1, the table's nodes i/64 and the signed zeros."""
+    rng = np.random.default_rng(3)
+    n = 200000
+    y = rng.standard_normal(n) * np.exp(rng.uniform(-18.0, 18.0, n))
+    x = rng.choice([1.0, -1.0, 37.5, -0.01, 2.5e4], n)
+    nodes = np.arange(65) / 64.0
+    y = np.concatenate([y, nodes, -nodes, nodes + 1e-9, 1.0 / np.maximum(nodes, 1e-3), [0.0, -0.0, 0.0, -0.0, 1.0]])
+    x = np.concatenate([x, np.ones(65), -np.ones(65), np.ones(65), np.ones(65), [1.0, 1.0, -1.0, -1.0, 0.0]])
+    got = dsp.atan2_host(y, x)
+    ref = np.arctan2(y, x)
+    # 3 ulp of the result: the reduction's rounding and t = y (1/x)
+    assert np.all(np.abs(got - ref) <= 3 * np.spacing(np.abs(ref)) + 1e-300)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
 def _status(fn, *args):
     return fn(*args)
 
