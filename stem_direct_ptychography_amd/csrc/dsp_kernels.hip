@@ -604,16 +604,31 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
         for (int i = 0; i < PF; ++i) ga[i] = G[goffs[p0 + i < p1 ? p0 + i : p1 - 1] + lane_off];
         for (int c0 = p0; c0 < p1; c0 += GRAM_CHUNK) {
             const int cn = (p1 - c0) < GRAM_CHUNK ? (p1 - c0) : GRAM_CHUNK;
+            // the chunk's loads all go out before the first is used (a wait
+            // per load would expose each one's latency): lane = pixel of the
+            // chunk (zero records past the end), then the Taylor coefficients
+            // and plane offsets, coalesced
+            PixelRec rec;
+            rec.lky = rec.lkx = rec.amp0 = rec.sw = rec.chi0 = rec.pad = 0.0;
+            if (lane < cn) rec = pix[c0 + lane];
+            constexpr int NTV = TAY ? (GRAM_CHUNK * TAY_N + 63) / 64 : 1;
+            double tv[NTV];
+            if (TAY) {
+#pragma unroll
+                for (int u = 0; u < NTV; ++u) {
+                    const int i = lane + 64 * u;
+                    tv[u] = i < cn * TAY_N ? prm.tay[(size_t)c0 * TAY_N + i] : 0.0;
+                }
+            }
+            constexpr int NGO = (GRAM_CHUNK + PF + 63) / 64;
+            long long gov[NGO];
+#pragma unroll
+            for (int u = 0; u < NGO; ++u) {
+                const int i = lane + 64 * u;
+                gov[u] = i < GRAM_CHUNK + PF ? goffs[c0 + i < p1 ? c0 + i : p1 - 1] : 0;
+            }
             __syncthreads();   // the previous chunk's records are no longer read
             if (lane < GRAM_CHUNK) {
-                // lane = pixel of the chunk (zero records past the end); then
-                // the chunk's Taylor coefficients, coalesced
-                PixelRec rec;
-                if (lane < cn) {
-                    rec = pix[c0 + lane];
-                } else {
-                    rec.lky = rec.lkx = rec.amp0 = rec.sw = rec.chi0 = rec.pad = 0.0;
-                }
                 srec[lane] = rec;
                 const double thr = sthr;
                 unsigned m = 0;
@@ -629,10 +644,17 @@ __global__ __launch_bounds__(64, (GramWaves<NJ, METHOD>::value)) void gram_kerne
                 smask[lane] = m;
             }
             if (TAY) {
-                for (int i = lane; i < GRAM_CHUNK * TAY_N; i += 64)
-                    stay[i] = i < cn * TAY_N ? prm.tay[(size_t)c0 * TAY_N + i] : 0.0;
+#pragma unroll
+                for (int u = 0; u < NTV; ++u) {
+                    const int i = lane + 64 * u;
+                    if (i < GRAM_CHUNK * TAY_N) stay[i] = tv[u];
+                }
             }
-            for (int i = lane; i < GRAM_CHUNK + PF; i += 64) sgoff[i] = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
+#pragma unroll
+            for (int u = 0; u < NGO; ++u) {
+                const int i = lane + 64 * u;
+                if (i < GRAM_CHUNK + PF) sgoff[i] = gov[u];
+            }
             __syncthreads();
             for (int r0 = 0; r0 < cn; r0 += PF) {
                 float2 gb[PF];
@@ -1279,11 +1301,10 @@ __global__ void export_kernel(const double2 *sys, int n_q, int D, double2 *dense
 // ---------------------------------------------------------------------------
 
 // Waves per SIMD the SSB kernel must fit.  Eight sets fit three in 168
-// registers with 4-pixel chunks (11 KB of LDS), except the per-row herm16
-// scales, which would spill there.
+// registers with 4-pixel chunks (11 KB of LDS).
 template <int MAXB, int H16>
 struct SsbWaves {
-    static constexpr int value = MAXB <= 2 ? 4 : (MAXB <= 4 ? 2 : (H16 == 2 ? 2 : 3));
+    static constexpr int value = MAXB <= 2 ? 4 : (MAXB <= 4 ? 2 : 3);
 };
 
 // SSB sums over one wave's stream-K range of (band tile, pixel) iterations;
@@ -1375,47 +1396,69 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB, H16>::value)) void ssb_kernel(S
         }
         for (int c0 = p0; c0 < p1; c0 += CHK) {
             const int cn = (p1 - c0) < CHK ? (p1 - c0) : CHK;
-            __syncthreads();
-            if (lane >= CHK) {
-                // lanes past the chunk stage nothing
-            } else if (lane < cn) {
-                PixelRec rec = pix[c0 + lane];
-                // herm16: the pixel's scale rides in the record's spare field
-                if (H16 == 1) rec.pad = (double)gsc[goffs[c0 + lane] / prm.plane];
-                srec[lane] = rec;
-            } else {
-                PixelRec z;
-                z.lky = z.lkx = z.amp0 = z.sw = z.chi0 = z.pad = 0.0;
-                srec[lane] = z;
-            }
+            // the chunk's loads all go out before the first is used (a wait
+            // per load would expose each one's latency): lane = pixel of the
+            // chunk (zero records past the end; herm16: the pixel's scale
+            // rides in the record's spare field), the sets' Taylor tables or,
+            // with TAYIN, lane (set b, pixel c)'s lambda k, and the plane
+            // offsets (CHK + PF <= 64: one per lane)
+            PixelRec rec;
+            rec.lky = rec.lkx = rec.amp0 = rec.sw = rec.chi0 = rec.pad = 0.0;
+            if (lane < cn) rec = pix[c0 + lane];
+            const long long go = goffs[c0 + lane < p1 ? c0 + lane : p1 - 1];
+            float sc1 = 0.0f;
+            if (H16 == 1 && lane < cn) sc1 = gsc[go / prm.plane];
+            constexpr int NTV = TAYIN ? 1 : (CHK * TAY_N + 63) / 64;
+            double tv[MAXB][NTV];
+            double tky = 0.0, tkx = 0.0;
+            const int tb_ = lane / CHK, tc_ = lane - tb_ * CHK;   // TAYIN: lane = (set, pixel)
+            const bool tin = TAYIN && lane < MAXB * CHK && tb_ < prm.B && tc_ < cn;
             if (TAYIN) {
-                // lane = (set b, pixel c) of the chunk; theta(k) = lambda k + tau
-                // formed as in the pixel-terms kernel (a rounded add)
+                if (tin) {
+                    tky = pix[c0 + tc_].lky;
+                    tkx = pix[c0 + tc_].lkx;
+                }
+            } else {
+                // set b's table starts at b n_pix TAY_N
+#pragma unroll
+                for (int b = 0; b < MAXB; ++b) {
+                    const double *tb = prm.tay + ((size_t)b * prm.n_pix + c0) * TAY_N;
+#pragma unroll
+                    for (int u = 0; u < NTV; ++u) {
+                        const int i = lane + 64 * u;
+                        tv[b][u] = (b < prm.B && i < cn * TAY_N) ? tb[i] : 0.0;
+                    }
+                }
+            }
+            __syncthreads();   // the previous chunk's LDS is no longer read
+            if (H16 == 1) rec.pad = (double)sc1;
+            if (lane < CHK) srec[lane] = rec;
+            if (TAYIN) {
+                // theta(k) = lambda k + tau formed as in the pixel-terms kernel
+                // (a rounded add)
                 if (lane < MAXB * CHK) {
-                    const int b = lane / CHK, c = lane - b * CHK;
-                    double *ts = stay + (b * CHK + c) * TAY_N;   // written in place
-                    if (b < prm.B && c < cn) {
-                        const double *cb = schi + b * CSTR;
-                        const double lky = pix[c0 + c].lky, lkx = pix[c0 + c].lkx;
-                        chi_taylor(cb, lkx + cb[CHI_NCOEF + 1], lky + cb[CHI_NCOEF], ts);
+                    double *ts = stay + (tb_ * CHK + tc_) * TAY_N;   // written in place
+                    if (tin) {
+                        const double *cb = schi + tb_ * CSTR;
+                        chi_taylor(cb, tkx + cb[CHI_NCOEF + 1], tky + cb[CHI_NCOEF], ts);
                     } else {
 #pragma unroll
                         for (int m = 0; m < TAY_N; ++m) ts[m] = 0.0;
                     }
                 }
             } else {
-                // set b's table starts at b n_pix TAY_N
 #pragma unroll
                 for (int b = 0; b < MAXB; ++b) {
-                    if (b >= prm.B) continue;
-                    const double *tb = prm.tay + ((size_t)b * prm.n_pix + c0) * TAY_N;
-                    for (int i = lane; i < CHK * TAY_N; i += 64) stay[b * CHK * TAY_N + i] = i < cn * TAY_N ? tb[i] : 0.0;
+#pragma unroll
+                    for (int u = 0; u < NTV; ++u) {
+                        const int i = lane + 64 * u;
+                        if (i < CHK * TAY_N) stay[b * CHK * TAY_N + i] = tv[b][u];
+                    }
                 }
             }
-            for (int i = lane; i < CHK + PF; i += 64) {
-                const long long go = goffs[c0 + i < p1 ? c0 + i : p1 - 1];
-                sgoff[i] = go;
-                if (H16 == 2) sgrow[i] = (go / prm.plane) * prm.N;
+            if (lane < CHK + PF) {
+                sgoff[lane] = go;
+                if (H16 == 2) sgrow[lane] = (go / prm.plane) * prm.N;
             }
             __syncthreads();
             for (int r0 = 0; r0 < cn; r0 += PF) {
