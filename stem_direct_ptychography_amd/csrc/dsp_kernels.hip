@@ -1578,13 +1578,26 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB, H16>::value)) void ssb_kernel(S
 
 // Block = one pixel's plane: |G|^2 as a rounded sum of rounded squares in
 // FP64, an exact max tree, the root rounded to float.
+__device__ __forceinline__ double herm16_mag2(float re, float im) {
+    const double r = re, i = im;
+    return __dadd_rn(__dmul_rn(r, r), __dmul_rn(i, i));
+}
+
+// One scale per pixel plane (a block per plane): pairs of entries per 16-byte
+// load (a plane holds N (N/2 + 1) entries, an even count, so pairs never
+// straddle planes and stay aligned), four loads in flight per thread; the
+// maximum is order-independent.
 __global__ __launch_bounds__(256) void herm16_scale_kernel(const float2 *G, long long plane, float *scale) {
     __shared__ double red[256];
-    const float2 *Gp = G + (size_t)blockIdx.x * plane;
+    const float4 *Gp = (const float4 *)(G + (size_t)blockIdx.x * plane);
+    const long long npair = plane / 2;
     double m = 0.0;
-    for (long long e = threadIdx.x; e < plane; e += 256) {
-        const double re = Gp[e].x, im = Gp[e].y;
-        m = fmax(m, __dadd_rn(__dmul_rn(re, re), __dmul_rn(im, im)));
+    for (long long j = threadIdx.x; j < npair; j += 4 * 256) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = j + u * 256 < npair ? Gp[j + u * 256] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m = fmax(m, fmax(herm16_mag2(v[u].x, v[u].y), herm16_mag2(v[u].z, v[u].w)));
     }
     red[threadIdx.x] = m;
     __syncthreads();
@@ -1604,9 +1617,12 @@ __global__ __launch_bounds__(256) void herm16_row_scale_kernel(const float2 *G, 
     if (row >= n_rows) return;
     const float2 *Gr = G + (size_t)row * nh;
     double m = 0.0;
-    for (int e = lane; e < nh; e += 64) {
-        const double re = Gr[e].x, im = Gr[e].y;
-        m = fmax(m, __dadd_rn(__dmul_rn(re, re), __dmul_rn(im, im)));
+    for (int e = lane; e < nh; e += 4 * 64) {
+        float2 v[4];   // four loads in flight per lane
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = e + u * 64 < nh ? Gr[e + u * 64] : make_float2(0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m = fmax(m, herm16_mag2(v[u].x, v[u].y));
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
@@ -1637,15 +1653,26 @@ __global__ __launch_bounds__(256) void herm16_pack_kernel(const float2 *G, long 
         uint2 *Qp = (uint2 *)(Q + (size_t)p * plane);
         const double sp = ROWS ? 0.0 : (double)scale[p];
         const float *srow = scale + (size_t)p * N;
-        for (long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x; j < npair; j += stride) {
-            const float4 v = Gp[j];
-            double s0 = sp, s1 = sp;
-            if (ROWS) {
-                const unsigned e = (unsigned)(2 * j);
-                s0 = (double)srow[e / (unsigned)nh];
-                s1 = (double)srow[(e + 1u) / (unsigned)nh];
+        // two pairs per thread and step, both loaded before either is coded
+        for (long long j = (long long)blockIdx.x * blockDim.x + threadIdx.x; j < npair; j += 2 * stride) {
+            float4 v[2];
+            double s0[2], s1[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const long long jj = j + u * stride;
+                v[u] = jj < npair ? Gp[jj] : make_float4(0.f, 0.f, 0.f, 0.f);
+                s0[u] = s1[u] = sp;
+                if (ROWS && jj < npair) {
+                    const unsigned e = (unsigned)(2 * jj);
+                    s0[u] = (double)srow[e / (unsigned)nh];
+                    s1[u] = (double)srow[(e + 1u) / (unsigned)nh];
+                }
             }
-            Qp[j] = make_uint2(herm16_code(v.x, v.y, s0), herm16_code(v.z, v.w, s1));
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const long long jj = j + u * stride;
+                if (jj < npair) Qp[jj] = make_uint2(herm16_code(v[u].x, v[u].y, s0[u]), herm16_code(v[u].z, v[u].w, s1[u]));
+            }
         }
     }
 }
@@ -2502,6 +2529,7 @@ hipError_t launch_herm16(const float2 *G, int n_bf, int N, int nh, bool rows, sh
     }
     DSP_CHECK_LAUNCH();
     // pairs per plane over blocks of 256 threads, about 8 pairs per thread
+    // (two per step)
     const long long npair = plane / 2;
     const unsigned bx = (unsigned)std::max<long long>(1, std::min<long long>((npair + 2047) / 2048, 4096));
     const dim3 grid(bx, (unsigned)std::min(n_bf, 65535));
