@@ -171,12 +171,16 @@ def test_largest_scan():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("n", [8, 1024])
+@pytest.mark.parametrize("n", [8, 16, 64, 256, 1024])
 def test_loss_fused_transform_limits(n):
     """The loss path's fused transforms at their smallest and largest
-    power-of-two scans (N = 8 and 1024; other N take hipFFT's transform),
-    three pixels of real intensity traces with a bright mean, against the
-    oracle's mean phase image and loss."""
+    power-of-two scans (N = 8 and 1024; other N take hipFFT's transform) and
+    at N = 16, 64 and 256, which with the full-frame and the 32 and 128 scans
+    of the other loss tests run every pass sequence of the transforms (a
+    radix-2 or radix-4 pass first, or radix 8 only) and both column layouts
+    (N >= 64 keeps a power-of-two column count per block), three pixels of
+    real intensity traces with a bright mean, against the oracle's mean
+    phase image and loss."""
     step = 0.373 if n > 8 else 0.9
     opt = _optics(soft=True, det_step=0.02819)
     k = _pixels(opt, 3, 11)
