@@ -20,10 +20,18 @@
 // in support; they are skipped with scalar branches.  The upsampled preview
 // runs the same kernel with right sides only: a lane's slots are the fine
 // frequencies that read its stored G value ("Historical WebGPU G(q,k) memory
-// experiment", section "Object-redraw fast path").  The tiles x pixels of a launch are split into
-// equal-cost contiguous ranges (stream-K, costed per iteration by the same
-// test on the host), eight per resident wave slot; partial sums are added
-// per tile in a fixed order afterwards (deterministic).
+// experiment", section "Object-redraw fast path").  The tiles x pixels of a
+// launch are split into equal-cost contiguous ranges (stream-K, costed per
+// iteration by the same test on the host), eight per resident wave slot;
+// partial sums are added per tile in a fixed order afterwards
+// (deterministic).  A chunk's staging issues all of its loads before the
+// first is used: vector loads complete in issue order, and a wait per load
+// would expose each one's latency.
+//
+// The loss path takes each pixel's corrected half plane through an inverse
+// real 2D transform in two fused passes, self-sorting radix-8 transforms in
+// LDS: the column pass computes the corrected values itself, the row pass
+// goes straight on to the phases and their moments.
 #include "dsp_internal.hpp"
 #include "dsp_kernels.hpp"
 
