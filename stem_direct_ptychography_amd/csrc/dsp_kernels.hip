@@ -1548,8 +1548,10 @@ __global__ __launch_bounds__(64, (SsbWaves<MAXB, H16>::value)) void ssb_kernel(S
                             ar *= sinc_tab(hr, T);
                         }
                         double sl, cl, sr, cr;
-                        sincos_tab((O - E) + hl, T, sl, cl);
-                        sincos_tab((O + E) + hr, T, sr, cr);
+                        // (without depth no + 0.0: IEEE's signed zero keeps the
+                        // compiler from dropping it)
+                        sincos_tab(DEPTH ? (O - E) + hl : O - E, T, sl, cl);
+                        sincos_tab(DEPTH ? (O + E) + hr : O + E, T, sr, cr);
                         // Gamma = i (L - R); S += conj(Gamma) g'; N += |Gamma|^2
                         const double gmr = fma(ar, sr, -(al * sl)), gmi = fma(al, cl, -(ar * cr));
                         acc[3 * b] = fma(gmr, gr, fma(gmi, gi, acc[3 * b]));
