@@ -1649,6 +1649,39 @@ __device__ __forceinline__ unsigned herm16_code(float re, float im, double s) {
     return (unsigned)(unsigned short)qx | ((unsigned)(unsigned short)qy << 16);
 }
 
+// Per-row scales and codes in one pass over G, for rows of at most 64
+// HERM16_RPL entries: wave w of the block takes row 4 b + w, its lanes the
+// row's entries, loaded once into registers; the row's largest |G|^2 by a
+// wave reduction (the maximum is order-independent), then each lane's codes
+// from its registers.  The same scale and codes as the two-pass form.
+constexpr int HERM16_RPL = 9;   // entries per lane: rows of up to 576 entries (N <= 1024)
+__global__ __launch_bounds__(256) void herm16_rows_fused_kernel(const float2 *G, long long n_rows, int nh,
+                                                                float *scale, short2 *Q) {
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= n_rows) return;   // whole waves
+    const float2 *Gr = G + (size_t)row * nh;
+    float2 v[HERM16_RPL];
+    double m = 0.0;
+#pragma unroll
+    for (int u = 0; u < HERM16_RPL; ++u) {
+        const int e = lane + 64 * u;
+        v[u] = e < nh ? Gr[e] : make_float2(0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < HERM16_RPL; ++u) m = fmax(m, herm16_mag2(v[u].x, v[u].y));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    const float sc = (float)sqrt(m);
+    if (lane == 0) scale[row] = sc;
+    unsigned *Qr = (unsigned *)(Q + (size_t)row * nh);
+#pragma unroll
+    for (int u = 0; u < HERM16_RPL; ++u) {
+        const int e = lane + 64 * u;
+        if (e < nh) Qr[e] = herm16_code(v[u].x, v[u].y, (double)sc);
+    }
+}
+
 // Block row y (grid-stride) takes pixel plane p; its threads take pairs of
 // entries (one 16-byte load, one 8-byte store: a plane holds N (N/2 + 1)
 // entries, an even count, so pairs never straddle planes and stay aligned).
@@ -2531,6 +2564,12 @@ hipError_t launch_herm16(const float2 *G, int n_bf, int N, int nh, bool rows, sh
                          hipStream_t st) {
     const long long plane = (long long)N * nh;
     if (n_bf <= 0 || plane <= 0) return hipSuccess;
+    if (rows && nh <= 64 * HERM16_RPL) {
+        const long long n_rows = (long long)n_bf * N;
+        herm16_rows_fused_kernel<<<(unsigned)((n_rows + 3) / 4), 256, 0, st>>>(G, n_rows, nh, scale, Q);
+        DSP_CHECK_LAUNCH();
+        return hipSuccess;
+    }
     if (rows) {
         const long long n_rows = (long long)n_bf * N;
         herm16_row_scale_kernel<<<(unsigned)((n_rows + 3) / 4), 256, 0, st>>>(G, n_rows, nh, scale);

@@ -671,6 +671,22 @@ def test_herm16_quantize_bit_exact():
         assert Q_o[5, 7, 9, 0] == -32767 and not np.any(Q_o[3])
 
 
+def test_herm16_quantize_long_rows_bit_exact():
+    """Rows longer than one wave holds in registers (N = 1280: 641 stored
+    entries per row) take the two-pass per-row form; scales and codes match
+    the oracle's to the bit, as do the per-pixel ones."""
+    rng = np.random.default_rng(41)
+    n = 1280
+    G = (rng.standard_normal((2, n, n // 2 + 1)) + 1j * rng.standard_normal((2, n, n // 2 + 1))).astype(np.complex64)
+    G[1, 5] *= 1e3   # one row far above the others
+    for rows in (False, True):
+        Q, sc = dsp.quantize_herm16(torch.as_tensor(G, device=DEV), rows=rows)
+        torch.cuda.synchronize()
+        Q_o, s_o = O.herm16_quantize(G, rows=rows)
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), s_o.view(np.uint32)), rows
+        assert np.array_equal(Q.cpu().numpy(), Q_o), rows
+
+
 @pytest.mark.parametrize("rows", [False, True])
 @pytest.mark.parametrize("depth", [0.0, 136.0])
 def test_ssb_herm16_c1_full(depth, rows):
