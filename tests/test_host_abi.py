@@ -228,3 +228,16 @@ def test_python_binding_rejects_cpu_tensors():
     G = torch.zeros((len(k), 32, 17), dtype=torch.complex64)
     with pytest.raises(dsp.DspError):
         dsp.prepare(G, k, w.optics, step=w.step, upsampling=1)
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: any --gpus other than 1 exits with status 2
+    and a message before touching a device."""
+    import subprocess
+    import sys as _sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([_sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU only" in res.stderr
+    assert res.stdout.strip() == ""
