@@ -433,12 +433,17 @@ dsp_status dsp_preview(const void *G_c64_dev, int n_bf, const double *bf_coords_
  *   loss_out_host: the mean over the scan of sum_k w_k (theta_k - mean)^2 /
  *       sum_k w_k, or NULL (non-NULL synchronizes the stream).
  * Arguments as dsp_preview (u = 1).  G's self-conjugate column (ix = 0)
- * should hold conjugate pairs G(-q) = conj G(q), as a real transform gives;
- * where rounding breaks them, the inverse real FFT uses their Hermitian
- * part.  The inverse FFTs are hipFFT's batched
- * Z2D over chunks of pixels (about 1 GB of planes per batch, from the
- * stream's arena; plans kept until the process ends).  DSP_EINVAL for bad
- * arguments or weights summing to zero, DSP_EDEVICE for a hipFFT failure. */
+ * should hold conjugate pairs G(-q) = conj G(q), as a real transform gives.
+ * For power-of-two N from 8 to 1024 two fused passes take the planes through
+ * the inverse real transform (self-sorting radix-8 transforms in LDS: a
+ * column pass that computes the corrected values, a row pass that goes on
+ * to the phases and their moments), and neither the corrected planes' second
+ * read nor the real images reach memory; they read the self-conjugate
+ * columns as given.  Other N write the corrected planes for chunks of pixels
+ * (about 1 GB per batch, from the stream's arena), run hipFFT's batched Z2D
+ * (plans kept until the process ends; it uses those columns' Hermitian
+ * part) and reduce the moments.  DSP_EINVAL for bad arguments or weights
+ * summing to zero, DSP_EDEVICE for a hipFFT failure. */
 dsp_status dsp_loss(const void *G_c64_dev, int n_bf, const double *bf_coords_host, const double *weights_host,
                     const dsp_scan *scan, const dsp_optics *optics, double *mean_phase_out_dev, double *loss_out_host,
                     void *hip_stream);
