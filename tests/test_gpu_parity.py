@@ -846,7 +846,9 @@ def _loss_case(w, G_np, k, wts, optics):
 
 
 def test_loss_tiny_and_c1():
-    """Ragged N = 12 with zero weights and depth, and c1 (hard aperture)."""
+    """Ragged N = 12 (hipFFT's transform) with zero weights and depth, and c1
+    (hard aperture, N = 32: the fused transforms), also with zero weights and
+    depth."""
     w = _tiny()
     pix, k = bf_pixels(w)
     G = data_stack_numpy(w, pix)
@@ -857,7 +859,11 @@ def test_loss_tiny_and_c1():
     assert l1 > 0 and l2 > 0
     w = workload("c1")
     pix, k = bf_pixels(w)
-    _loss_case(w, data_stack_numpy(w, pix), k, None, w.optics)
+    G = data_stack_numpy(w, pix)
+    _loss_case(w, G, k, None, w.optics)
+    wts = random_weights(len(k), 23)
+    wts[::4] = 0.0
+    _loss_case(w, G, k, wts, w.optics.replace(depth=70.0))
 
 
 def test_loss_c2():
