@@ -765,7 +765,7 @@ void pool_sweep(DevicePool &P) {
     size_t j = 0;
     for (size_t i = 0; i < P.retired.size(); ++i) {
         if (hipEventQuery(P.retired[i]) == hipSuccess)
-            hipEventDestroy(P.retired[i]);
+            (void)hipEventDestroy(P.retired[i]);
         else
             P.retired[j++] = P.retired[i];
     }
@@ -777,10 +777,10 @@ void pool_sweep(DevicePool &P) {
 void pool_drain(DevicePool &P) {
     for (auto &b : P.kept) {
         for (auto e : b.ev) {
-            hipEventSynchronize(e);
-            hipEventDestroy(e);
+            (void)hipEventSynchronize(e);
+            (void)hipEventDestroy(e);
         }
-        hipFree(b.ptr);
+        (void)hipFree(b.ptr);
     }
     P.kept.clear();
     P.bytes = 0;
@@ -808,7 +808,7 @@ dsp_status pool_alloc(int device, hipStream_t stream, size_t bytes, void **out) 
                 const hipError_t err = hipStreamWaitEvent(stream, e, 0);
                 P.retired.push_back(e);
                 if (err != hipSuccess) {
-                    hipFree(blk.ptr);
+                    (void)hipFree(blk.ptr);
                     return fail(DSP_EDEVICE, "hipStreamWaitEvent: %s", hipGetErrorString(err));
                 }
             }
@@ -838,7 +838,7 @@ dsp_status pool_alloc(int device, hipStream_t stream, size_t bytes, void **out) 
 // device must be current.
 void pool_release(int device, void *ptr, size_t bytes, std::vector<hipEvent_t> ev) {
     if (!ptr) {
-        for (auto e : ev) hipEventDestroy(e);
+        for (auto e : ev) (void)hipEventDestroy(e);
         return;
     }
     bytes = (std::max<size_t>(bytes, 1) + kPoolGrain - 1) / kPoolGrain * kPoolGrain;
@@ -851,10 +851,10 @@ void pool_release(int device, void *ptr, size_t bytes, std::vector<hipEvent_t> e
         P.kept.erase(P.kept.begin());
         P.bytes -= b.bytes;
         for (auto e : b.ev) {
-            hipEventSynchronize(e);
-            hipEventDestroy(e);
+            (void)hipEventSynchronize(e);
+            (void)hipEventDestroy(e);
         }
-        hipFree(b.ptr);
+        (void)hipFree(b.ptr);
     }
 }
 
@@ -920,16 +920,16 @@ struct Layout {
     int *d_sk_int = nullptr;
 
     ~Layout() {
-        hipSetDevice(key.device);
-        hipFree(d_pixbase);
-        hipFree(d_goff);
-        hipFree(d_tiles);
-        hipFree(d_prior);
-        hipFree(d_count);
-        hipFree(d_K);
-        hipFree(d_bucket);
-        hipFree(d_sk_wbegin);
-        hipFree(d_sk_int);
+        (void)hipSetDevice(key.device);
+        (void)hipFree(d_pixbase);
+        (void)hipFree(d_goff);
+        (void)hipFree(d_tiles);
+        (void)hipFree(d_prior);
+        (void)hipFree(d_count);
+        (void)hipFree(d_K);
+        (void)hipFree(d_bucket);
+        (void)hipFree(d_sk_wbegin);
+        (void)hipFree(d_sk_int);
     }
 };
 
@@ -1094,14 +1094,14 @@ struct SsbLayout {
     ~SsbLayout() {
         // an allocation-free pass's layout holds no device memory: no HIP call
         if (key.noalloc) return;
-        hipSetDevice(key.device);
-        hipFree(d_pixbase);
-        hipFree(d_goff);
-        hipFree(d_tiles);
+        (void)hipSetDevice(key.device);
+        (void)hipFree(d_pixbase);
+        (void)hipFree(d_goff);
+        (void)hipFree(d_tiles);
         for (int i = 0; i < 4; ++i) {
-            hipFree(d_wbegin[i]);
-            hipFree(d_seg_off[i]);
-            hipFree(d_seg_first[i]);
+            (void)hipFree(d_wbegin[i]);
+            (void)hipFree(d_seg_off[i]);
+            (void)hipFree(d_seg_first[i]);
         }
     }
 };
@@ -1293,12 +1293,12 @@ struct PreviewLayout {
     int *d_sk_int = nullptr;
     double host_ms = 0.0;
     ~PreviewLayout() {
-        hipSetDevice(key.device);
-        hipFree(d_pixbase);
-        hipFree(d_goff);
-        hipFree(d_tiles);
-        hipFree(d_sk_wbegin);
-        hipFree(d_sk_int);
+        (void)hipSetDevice(key.device);
+        (void)hipFree(d_pixbase);
+        (void)hipFree(d_goff);
+        (void)hipFree(d_tiles);
+        (void)hipFree(d_sk_wbegin);
+        (void)hipFree(d_sk_int);
     }
 };
 
@@ -1543,21 +1543,26 @@ struct dsp_handle {
     std::vector<hipEvent_t> gram_ev;          // three per launch: start, Gram done, fixup done (timing)
     unsigned long long *d_work = nullptr;     // [tile][5] (DSP_FLAG_COUNT_WORK)
 
-    // Records that work using the buffers has been queued on s.
+    // Records that work using the buffers has been queued on s.  Where no
+    // event can be recorded, it waits for s here instead, so that the block
+    // is free to reuse once the handle is destroyed.
     void mark(hipStream_t s) const {
         for (auto &u : uses) {
             if (u.first == s) {
-                hipEventRecord(u.second, s);
+                if (hipEventRecord(u.second, s) != hipSuccess) (void)hipStreamSynchronize(s);
                 return;
             }
         }
         hipEvent_t e = nullptr;
         if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
-            // no event: wait here instead, so the block is free to reuse
-            hipStreamSynchronize(s);
+            (void)hipStreamSynchronize(s);
             return;
         }
-        hipEventRecord(e, s);
+        if (hipEventRecord(e, s) != hipSuccess) {
+            (void)hipEventDestroy(e);
+            (void)hipStreamSynchronize(s);
+            return;
+        }
         uses.emplace_back(s, e);
     }
 
@@ -1581,15 +1586,15 @@ struct dsp_handle {
     }
 
     ~dsp_handle() {
-        hipSetDevice(device);
+        (void)hipSetDevice(device);
         std::vector<hipEvent_t> evs;
         for (auto &u : uses) evs.push_back(u.second);
         pool_release(device, block, block_bytes, std::move(evs));
         for (auto &e : ev)
-            if (e) hipEventDestroy(e);
+            if (e) (void)hipEventDestroy(e);
         for (auto &e : gram_ev)
-            if (e) hipEventDestroy(e);
-        hipFree(d_work);
+            if (e) (void)hipEventDestroy(e);
+        (void)hipFree(d_work);
     }
 };
 
