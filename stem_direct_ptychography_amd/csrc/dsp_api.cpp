@@ -804,13 +804,15 @@ dsp_status pool_alloc(int device, hipStream_t stream, size_t bytes, void **out) 
             blk = P.kept[best];
             P.kept.erase(P.kept.begin() + best);
             P.bytes -= blk.bytes;
+            // every event is retired, also those after a failed wait
+            hipError_t err = hipSuccess;
             for (auto e : blk.ev) {
-                const hipError_t err = hipStreamWaitEvent(stream, e, 0);
+                if (err == hipSuccess) err = hipStreamWaitEvent(stream, e, 0);
                 P.retired.push_back(e);
-                if (err != hipSuccess) {
-                    (void)hipFree(blk.ptr);
-                    return fail(DSP_EDEVICE, "hipStreamWaitEvent: %s", hipGetErrorString(err));
-                }
+            }
+            if (err != hipSuccess) {
+                (void)hipFree(blk.ptr);
+                return fail(DSP_EDEVICE, "hipStreamWaitEvent: %s", hipGetErrorString(err));
             }
             *out = blk.ptr;
             return DSP_OK;
